@@ -1,0 +1,328 @@
+"""Pins of the fp64 CPU oracle to facts that do not come from the oracle itself.
+
+Each check is chosen so that a plausible slip (a dropped term, a wrong sign or
+index, a transposed operand, the gate on the wrong side of the delta update)
+fails at least one of them:
+
+* delta-rule read-back: with b=1 and a unit key, kᵀS_t = v_t whatever the
+  previous state and gate; this fixes the order gate -> erase -> write;
+* b = 0 closed forms (pure decay of h0) for the forward and every gradient;
+* one token from a zero state, expanded by hand;
+* central finite differences of L = Σ<dO,o> + <dht,S_T> for all six outputs
+  (dense, GQA, varlen, h0 and dht non-zero) and of the KDA-stage functional;
+* the chunked WY derivation equals the token recurrence for several BT,
+  including partial last chunks (BT invariance);
+* linearity in the cotangents; varlen == per-sequence runs; GQA == repeated
+  heads summed; an independent fp64 torch-autograd derivation.
+"""
+import numpy as np
+import pytest
+import torch
+
+RTOL_FD = 2e-7
+
+
+def _rand_problem(rng, T, HK, HV, K, V, N=1, gate=1.0, beta=None):
+    q = rng.standard_normal((N * T, HK, K))
+    k = rng.standard_normal((N * T, HK, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N * T, HV, V))
+    g = -gate * rng.random((N * T, HV))
+    b = rng.random((N * T, HV)) if beta is None else np.full((N * T, HV), beta)
+    h0 = rng.standard_normal((N, HV, K, V))
+    dO = rng.standard_normal((N * T, HV, V))
+    dht = rng.standard_normal((N, HV, K, V))
+    return q, k, v, g, b, h0, dO, dht
+
+
+def test_delta_rule_readback(oracle):
+    """b=1, unit key, query = key: o_t = scale * v_t for any history and gate."""
+    rng = np.random.default_rng(3)
+    T, K, V = 9, 5, 4
+    p = oracle.Problem(1, T, 1, 1, K, V, scale=0.7)
+    q, k, v, g, b, h0, _, _ = _rand_problem(rng, T, 1, 1, K, V, beta=1.0)
+    q = k.copy()
+    out = oracle.gdr_fwd_token(p, 0, q, k, v, g, b, h0)
+    np.testing.assert_allclose(out["o"], 0.7 * v, rtol=1e-12, atol=1e-12)
+
+
+def test_beta_zero_forward_closed_form(oracle):
+    rng = np.random.default_rng(4)
+    T, K, V = 11, 4, 3
+    p = oracle.Problem(1, T, 1, 1, K, V)
+    q, k, v, g, b, h0, _, _ = _rand_problem(rng, T, 1, 1, K, V, beta=0.0)
+    lam = np.exp(np.cumsum(g[:, 0]))
+    out = oracle.gdr_fwd_token(p, 0, q, k, v, g, b, h0)
+    o_ref = p.scale * lam[:, None] * np.einsum("kv,tk->tv", h0[0, 0], q[:, 0])
+    np.testing.assert_allclose(out["o"][:, 0], o_ref, rtol=1e-12)
+    np.testing.assert_allclose(out["ht"][0, 0], lam[-1] * h0[0, 0], rtol=1e-12)
+
+
+def test_single_token_by_hand(oracle):
+    """S_1 = b k vᵀ from a zero state; o = scale b (q·k) v; hand-expanded gradients."""
+    rng = np.random.default_rng(5)
+    K, V = 3, 2
+    p = oracle.Problem(1, 1, 1, 1, K, V, scale=0.5)
+    q, k, v = rng.standard_normal((1, 1, K)), rng.standard_normal((1, 1, K)), rng.standard_normal((1, 1, V))
+    g, b, dO = np.array([[-0.3]]), np.array([[0.6]]), rng.standard_normal((1, 1, V))
+    out = oracle.gdr_fwd_token(p, 0, q, k, v, g, b, None)
+    qk, vdo = float(q.ravel() @ k.ravel()), float(v.ravel() @ dO.ravel())
+    np.testing.assert_allclose(out["o"].ravel(), 0.5 * 0.6 * qk * v.ravel(), rtol=1e-13)
+    gr = oracle.gdr_bwd_token(p, q, k, v, g, b, None, dO, None)
+    # L = 0.5 * b * (q·k) * (v·dO)
+    np.testing.assert_allclose(gr["dq"].ravel(), 0.5 * 0.6 * vdo * k.ravel(), rtol=1e-13)
+    np.testing.assert_allclose(gr["dk"].ravel(), 0.5 * 0.6 * vdo * q.ravel(), rtol=1e-13)
+    np.testing.assert_allclose(gr["dv"].ravel(), 0.5 * 0.6 * qk * dO.ravel(), rtol=1e-13)
+    np.testing.assert_allclose(gr["dbeta"].ravel(), [0.5 * qk * vdo], rtol=1e-13)
+    np.testing.assert_allclose(gr["dg"].ravel(), [0.0], atol=1e-15)  # zero state: the gate acts on nothing
+    # dL/dh0 = a (I - b k kᵀ) (scale q dOᵀ), even at h0 = 0
+    kk = k.ravel()
+    dh0_ref = np.exp(-0.3) * (np.eye(K) - 0.6 * np.outer(kk, kk)) @ (0.5 * np.outer(q.ravel(), dO.ravel()))
+    np.testing.assert_allclose(gr["dh0"][0, 0], dh0_ref, rtol=1e-13)
+
+
+def test_beta_zero_backward_closed_form(oracle):
+    """b=0: L = Σ_t scale Λ_t q_tᵀ h0 dO_t + Λ_T <dht, h0>, Λ_t = exp(Σ_{s<=t} ĝ_s)."""
+    rng = np.random.default_rng(6)
+    T, K, V = 10, 4, 3
+    p = oracle.Problem(1, T, 1, 1, K, V)
+    q, k, v, g, b, h0, dO, dht = _rand_problem(rng, T, 1, 1, K, V, beta=0.0)
+    gr = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    lam = np.exp(np.cumsum(g[:, 0]))
+    H0, sc = h0[0, 0], p.scale
+    terms = sc * lam * np.einsum("tk,kv,tv->t", q[:, 0], H0, dO[:, 0])
+    final = lam[-1] * float((dht[0, 0] * H0).sum())
+    dg_ref = np.array([terms[s:].sum() + final for s in range(T)])
+    np.testing.assert_allclose(gr["dg"][:, 0], dg_ref, rtol=1e-11)
+    np.testing.assert_allclose(gr["dq"][:, 0], sc * lam[:, None] * (dO[:, 0] @ H0.T), rtol=1e-11)
+    dh0_ref = sc * np.einsum("t,tk,tv->kv", lam, q[:, 0], dO[:, 0]) + lam[-1] * dht[0, 0]
+    np.testing.assert_allclose(gr["dh0"][0, 0], dh0_ref, rtol=1e-11)
+    np.testing.assert_allclose(gr["dv"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(gr["dk"], 0.0, atol=1e-15)
+    # db_t = kᵀ dS_t v_t - a_t kᵀ dS_t S_{t-1}ᵀ k_t with S_{t-1} = Λ_{t-1} h0 and
+    # dS_t = Σ_{s>=t} scale (Λ_s/Λ_t) q_s dO_sᵀ + (Λ_T/Λ_t) dht
+    db_ref = []
+    for t in range(T):
+        dS = sum(sc * lam[s] / lam[t] * np.outer(q[s, 0], dO[s, 0]) for s in range(t, T)) + lam[-1] / lam[t] * dht[0, 0]
+        Sp = (lam[t - 1] if t > 0 else 1.0) * H0
+        kk = k[t, 0]
+        db_ref.append(kk @ dS @ v[t, 0] - np.exp(g[t, 0]) * kk @ dS @ Sp.T @ kk)
+    np.testing.assert_allclose(gr["dbeta"][:, 0], db_ref, rtol=1e-10)
+
+
+def _loss(oracle, p, dO, dht, q, k, v, g, b, h0):
+    f = oracle.gdr_fwd_token(p, 0, q, k, v, g, b, h0)
+    return float((f["o"] * dO).sum() + (f["ht"] * dht).sum())
+
+
+@pytest.mark.parametrize("case", ["dense", "gqa", "varlen"])
+def test_finite_differences(oracle, case):
+    rng = np.random.default_rng({"dense": 1, "gqa": 2, "varlen": 7}[case])
+    if case == "dense":
+        T, HK, HV, K, V, cu = 8, 1, 1, 4, 3, None
+    elif case == "gqa":
+        T, HK, HV, K, V, cu = 6, 1, 2, 3, 4, None
+    else:
+        T, HK, HV, K, V, cu = 9, 1, 1, 3, 3, [0, 4, 9]
+    N = 1 if cu is None else len(cu) - 1
+    p = oracle.Problem(1, T, HK, HV, K, V, cu_seqlens=cu)
+    q, k, v, g, b, _, dO, _ = _rand_problem(rng, T, HK, HV, K, V)
+    h0 = rng.standard_normal((N, HV, K, V))
+    dht = rng.standard_normal((N, HV, K, V))
+    gr = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    args = {"q": q, "k": k, "v": v, "g": g, "b": b, "h0": h0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "b": "dbeta", "h0": "dh0"}
+    eps = 1e-6
+    for nm, a in args.items():
+        num = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            vals = []
+            for s in (1, -1):
+                x = a.copy()
+                x[idx] += s * eps
+                kw = dict(args)
+                kw[nm] = x
+                vals.append(_loss(oracle, p, dO, dht, **kw))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        err = np.abs(num - gr[names[nm]]).max() / np.abs(num).max()
+        assert err < RTOL_FD, (nm, err)
+
+
+@pytest.mark.parametrize("BT", [1, 2, 3, 5, 16, 64])
+def test_chunked_equals_token(oracle, BT):
+    """BT invariance: the chunked WY derivation reproduces the token recurrence,
+    including partial last chunks and per-chunk states."""
+    rng = np.random.default_rng(11)
+    T, HK, HV, K, V, cu = 23, 1, 2, 4, 3, [0, 10, 23]
+    p = oracle.Problem(1, T, HK, HV, K, V, cu_seqlens=cu)
+    q, k, v, g, b, _, dO, _ = _rand_problem(rng, T, HK, HV, K, V)
+    h0 = rng.standard_normal((2, HV, K, V))
+    dht = rng.standard_normal((2, HV, K, V))
+    tok = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    ch = oracle.gdr_bwd_chunked(p, BT, q, k, v, g, b, h0, dO, dht)
+    for nm in tok:
+        np.testing.assert_allclose(ch[nm], tok[nm], rtol=1e-11, atol=1e-12 * np.abs(tok[nm]).max(), err_msg=nm)
+    fw = oracle.gdr_fwd_token(p, BT, q, k, v, g, b, h0, want_o=False, want_hc=True)
+    np.testing.assert_allclose(ch["hc"], fw["hc"], rtol=1e-11, atol=1e-12)
+
+
+def test_linearity_in_cotangents(oracle):
+    rng = np.random.default_rng(12)
+    T, K, V = 7, 3, 3
+    p = oracle.Problem(1, T, 1, 1, K, V)
+    q, k, v, g, b, h0, dO, dht = _rand_problem(rng, T, 1, 1, K, V)
+    full = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    a = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, None)
+    c = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, np.zeros_like(dO), dht)
+    for nm in full:
+        np.testing.assert_allclose(full[nm], a[nm] + c[nm], rtol=1e-11, atol=1e-13)
+
+
+def test_varlen_equals_separate_sequences(oracle):
+    rng = np.random.default_rng(13)
+    lens = [5, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    HK, HV, K, V = 1, 2, 3, 4
+    T = int(cu[-1])
+    p = oracle.Problem(1, T, HK, HV, K, V, cu_seqlens=cu)
+    q, k, v, g, b, _, dO, _ = _rand_problem(rng, T, HK, HV, K, V)
+    h0 = rng.standard_normal((3, HV, K, V))
+    dht = rng.standard_normal((3, HV, K, V))
+    packed = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    for n, (s, e) in enumerate(zip(cu[:-1], cu[1:])):
+        pn = oracle.Problem(1, e - s, HK, HV, K, V)
+        one = oracle.gdr_bwd_token(pn, q[s:e], k[s:e], v[s:e], g[s:e], b[s:e], h0[n:n + 1], dO[s:e], dht[n:n + 1])
+        for nm in ("dq", "dk", "dv", "dg", "dbeta"):
+            np.testing.assert_allclose(packed[nm][s:e], one[nm], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(packed["dh0"][n], one["dh0"][0], rtol=1e-12)
+
+
+def test_gqa_equals_repeated_heads(oracle):
+    rng = np.random.default_rng(14)
+    T, HK, HV, K, V = 6, 2, 4, 3, 3
+    p = oracle.Problem(1, T, HK, HV, K, V)
+    q, k, v, g, b, h0, dO, dht = _rand_problem(rng, T, HK, HV, K, V)
+    gq = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    rep = HV // HK
+    qr, kr = np.repeat(q, rep, axis=1), np.repeat(k, rep, axis=1)
+    pr = oracle.Problem(1, T, HV, HV, K, V)
+    full = oracle.gdr_bwd_token(pr, qr, kr, v, g, b, h0, dO, dht)
+    np.testing.assert_allclose(gq["dq"], full["dq"].reshape(T, HK, rep, K).sum(2), rtol=1e-12)
+    np.testing.assert_allclose(gq["dk"], full["dk"].reshape(T, HK, rep, K).sum(2), rtol=1e-12)
+    for nm in ("dv", "dg", "dbeta", "dh0"):
+        np.testing.assert_allclose(gq[nm], full[nm], rtol=1e-12)
+
+
+def test_torch_autograd_cross_check(oracle):
+    """An independent derivation: torch fp64 autograd through a naive loop."""
+    rng = np.random.default_rng(15)
+    T, K, V = 7, 4, 3
+    p = oracle.Problem(1, T, 1, 1, K, V)
+    q, k, v, g, b, h0, dO, dht = _rand_problem(rng, T, 1, 1, K, V)
+    ref = oracle.gdr_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    tq, tk, tv, tg, tb, th = (torch.tensor(x[:, 0] if x.ndim > 2 and x.shape[0] == T else x, dtype=torch.float64,
+                                           requires_grad=True) for x in (q, k, v, g, b, h0[0, 0]))
+    S = th
+    loss = 0.0
+    for t in range(T):
+        a = torch.exp(tg[t, 0])
+        kk = tk[t]
+        S = a * (S - tb[t, 0] * torch.outer(kk, kk @ S)) + tb[t, 0] * torch.outer(kk, tv[t])
+        loss = loss + (p.scale * (S.T @ tq[t]) * torch.tensor(dO[t, 0])).sum()
+    loss = loss + (S * torch.tensor(dht[0, 0])).sum()
+    loss.backward()
+    np.testing.assert_allclose(tq.grad.numpy(), ref["dq"][:, 0], rtol=1e-11)
+    np.testing.assert_allclose(tk.grad.numpy(), ref["dk"][:, 0], rtol=1e-11)
+    np.testing.assert_allclose(tv.grad.numpy(), ref["dv"][:, 0], rtol=1e-11)
+    np.testing.assert_allclose(tg.grad.numpy(), ref["dg"], rtol=1e-11)
+    np.testing.assert_allclose(tb.grad.numpy(), ref["dbeta"], rtol=1e-11)
+    np.testing.assert_allclose(th.grad.numpy(), ref["dh0"][0, 0], rtol=1e-11)
+
+
+def test_gcum_roundtrip(oracle):
+    """The raw gate is recovered from its fp32 in-chunk cumulative sum."""
+    from chunked_gated_delta_08_amd.workloads import in_chunk_cumsum
+    rng = np.random.default_rng(16)
+    lens = [70, 5, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    graw = (-rng.random((int(cu[-1]), 2))).astype(np.float32)
+    gc = in_chunk_cumsum(graw, 64, cu=cu)
+    p = oracle.Problem(1, int(cu[-1]), 1, 2, 4, 4, cu_seqlens=cu)
+    back = oracle.gcum_to_graw(p, 64, gc)
+    np.testing.assert_allclose(back, graw, rtol=0, atol=2e-6)
+    # chunk starts hold the raw value itself
+    for s in (0, 64, 70, 75, 139, 203):
+        np.testing.assert_array_equal(gc[s], graw[s])
+
+
+# ---------------------------------------------------------------- KDA stage
+def _kda_phi(q, k, v, vn, g, b, A, h, dO, dh, dv, scale):
+    """The chunk-local functional whose VJP is the KDA WY stage (one chunk, one head)."""
+    gm = np.exp(g)
+    gC = gm[-1]
+    W = A @ (b[:, None] * gm * k)
+    U = A @ (b[:, None] * v)
+    return (scale * (dO * ((q * gm) @ h)).sum() + (dh * ((k * gC / gm).T @ vn)).sum()
+            + (dh * (gC[:, None] * h)).sum() + (dv * (U - W @ h)).sum())
+
+
+@pytest.mark.parametrize("C", [6, 4])
+def test_kda_finite_differences(oracle, C):
+    """O-K against finite differences of its functional, including dA through A=(I+L)^{-1}."""
+    rng = np.random.default_rng(21 + C)
+    BT, K, V = 6, 3, 4  # C=4 exercises a partial chunk
+    T = C
+    p = oracle.Problem(1, T, 1, 1, K, V, scale=0.6)
+    q, k, v, vn, dO, dv = (rng.standard_normal((T, 1, d)) for d in (K, K, V, V, V, V))
+    g = -rng.random((T, 1, K)) * 0.8
+    b = rng.random((T, 1))
+    Lm = np.tril(rng.standard_normal((C, C)) * 0.3, -1)
+    Am = np.linalg.inv(np.eye(C) + Lm)
+    A = np.zeros((T, 1, BT))
+    A[:, 0, :C] = Am
+    h, dh = rng.standard_normal((1, 1, K, V)), rng.standard_normal((1, 1, K, V))
+    out = oracle.kda_wy_bwd(p, BT, q, k, v, vn, g, b, A, h, dO, dh, dv)
+
+    def phi(q=q, k=k, v=v, g=g, b=b, Lm=Lm):
+        Ax = np.linalg.inv(np.eye(C) + Lm)
+        return _kda_phi(q[:, 0], k[:, 0], v[:, 0], vn[:, 0], g[:, 0], b[:, 0], Ax, h[0, 0], dO[:, 0], dh[0, 0],
+                        dv[:, 0], 0.6)
+
+    eps = 1e-6
+    for nm, arr, key in (("q", q, "dq"), ("k", k, "dk"), ("v", v, "dv"), ("g", g, "dg"), ("b", b, "db")):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            xp, xm = arr.copy(), arr.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num[idx] = (phi(**{nm: xp}) - phi(**{nm: xm})) / (2 * eps)
+        err = np.abs(num - out[key]).max() / np.abs(num).max()
+        assert err < RTOL_FD, (nm, err)
+    numL = np.zeros((C, C))
+    for r in range(C):
+        for s in range(r):
+            xp, xm = Lm.copy(), Lm.copy()
+            xp[r, s] += eps
+            xm[r, s] -= eps
+            numL[r, s] = (phi(Lm=xp) - phi(Lm=xm)) / (2 * eps)
+    got = out["dA"][:, 0, :C]
+    assert np.abs(got - numL).max() / np.abs(numL).max() < RTOL_FD
+    assert np.all(out["dA"][:, 0, :][np.triu_indices(BT)[0][np.triu_indices(BT)[0] < C],
+                                     np.triu_indices(BT)[1][np.triu_indices(BT)[0] < C]] == 0)
+
+
+def test_kda_ignores_upper_triangle_of_A(oracle):
+    rng = np.random.default_rng(31)
+    T, BT, K, V = 8, 8, 3, 3
+    p = oracle.Problem(1, T, 1, 1, K, V)
+    args = [rng.standard_normal((T, 1, d)) for d in (K, K, V, V)]
+    g = -rng.random((T, 1, K))
+    b = rng.random((T, 1))
+    A = np.tril(rng.standard_normal((T, 1, BT)).transpose(1, 0, 2)[0]).reshape(T, 1, BT)
+    A2 = A + np.triu(rng.standard_normal((T, BT)), 1).reshape(T, 1, BT)
+    h, dh = rng.standard_normal((1, 1, K, V)), rng.standard_normal((1, 1, K, V))
+    dO, dv = rng.standard_normal((T, 1, V)), rng.standard_normal((T, 1, V))
+    o1 = oracle.kda_wy_bwd(p, BT, *args, g, b, A, h, dO, dh, dv)
+    o2 = oracle.kda_wy_bwd(p, BT, *args, g, b, A2, h, dO, dh, dv)
+    for nm in o1:
+        np.testing.assert_array_equal(o1[nm], o2[nm])
