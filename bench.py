@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule chunked backward on one MI355X.
+
+One step = one gdr_chunk_bwd call (chunk table + WY factors, the forward state
+scan and the reverse dh scan, the per-chunk gradient kernel with the dg
+reverse cumsum and GQA sums) over one batch of synthetic inputs already
+resident in HBM.  Default workload: B=1, T=32768, 16 key / 16 value heads,
+K=V=128, BT=64, bf16 inputs with fp32 gate, dht present.
+
+Prints one JSON line: the headline metric (effective TFLOP/s under the FLOP
+model below, with ms per call), a roofline entry for the dominant kernel
+(timed with HIP events recorded by the library between its stages during the
+timed steps), and the fp64 CPU oracle timed on a bounded sample.
+
+FLOP model per (chunk of C rows, value head), dense tiles, recompute not
+counted:  F(C) = 16 C K V + 18 C^2 K + 10 C^2 V + 13/3 C^3  (32.59 MFLOP at
+C=64, K=V=128).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "c2": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None,
+               name="gdn_bwd_T32768_hk16_hv16_K128_V128_BT64_bf16"),
+    "c3": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None,
+               name="gdn_bwd_T32768_hk32_hv32_K128_V128_BT64_bf16"),
+    "c5": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12",
+               name="gdn_bwd_varlen12_65536tok_hk16_hv32_K128_V128_BT64_bf16"),
+}
+
+
+def flop_model(C, K, V):
+    return 16 * C * K * V + 18 * C * C * K + 10 * C * C * V + 13.0 / 3.0 * C ** 3
+
+
+def chunk_lengths(lengths, T, B, BT):
+    seqs = [T] * B if lengths is None else lengths
+    out = []
+    for L in seqs:
+        out += [BT] * (L // BT) + ([L % BT] if L % BT else [])
+    return out
+
+
+def kernel_bytes(cfg, chunks, es=2):
+    """Algorithmic bytes of each stage (inputs read once, outputs written once)."""
+    HK, HV, K, V = cfg["HK"], cfg["HV"], cfg["K"], cfg["V"]
+    ntok, nunits, nkunits = sum(chunks), len(chunks) * HV, len(chunks) * HK
+    tok_k, tok_v = ntok * K * es, ntok * V * es
+    st = 64 * K * es              # one [64, K] workspace tile
+    state = K * V * es            # one K x V state in the workspace
+    gb = ntok * HV * (4 + es)     # gate (fp32) and beta
+    prep = HK * (2 * tok_k) + HV * tok_v + gb + nunits * (3 * st + 64 * 64 * es)
+    scans = nunits * (3 * st) + HK * tok_k + nunits * state + \
+        nunits * (3 * st) + HK * tok_k + HV * tok_v + nunits * state
+    grad = HK * 2 * tok_k + HV * 2 * tok_v + nunits * (2 * state + 64 * 64 * es) + gb + \
+        HK * 2 * tok_k + HV * tok_v + ntok * HV * 8
+    return {"prep": prep, "scans": scans, "grad": grad}
+
+
+def hip_events(n):
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        assert hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))) == 0
+    return hip, evs
+
+
+def elapsed_ms(hip, a, b):
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+    return ms.value
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(inp, cfg, seconds_hint=20.0):
+    """The fp64 oracle, unchanged, on a bounded sample of the same inputs:
+    all heads, the first T_s tokens of the (first) sequence."""
+    from oracle import oracle as O
+    HK, HV, K, V = cfg["HK"], cfg["HV"], cfg["K"], cfg["V"]
+    T_s = 8192
+    f = lambda t: t[:T_s].double().numpy()  # noqa: E731
+    p = O.Problem(1, T_s, HK, HV, K, V)
+    graw = O.gcum_to_graw(p, 64, inp["gcum"][:T_s].numpy())
+    dht = inp["dht"][:1].double().numpy()
+    t0 = time.perf_counter()
+    O.gdr_bwd_token(p, f(inp["q"]), f(inp["k"]), f(inp["v"]), graw, f(inp["beta"]), None, f(inp["dO"]), dht)
+    dt = time.perf_counter() - t0
+    flops = (T_s // 64) * HV * flop_model(64, K, V)
+    threads = min(O.num_threads(), HK)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T_s} tokens x {HV} value heads of the same workload ({dt:.1f} s, fp64 token "
+                      f"recurrence + hand-derived backward, OpenMP over key heads)",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=list(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the backward of one GPU's share); "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunked_gated_delta_08_amd import binding, workloads
+
+    cfg = dict(WORKLOADS[args.workload])
+    lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
+    inp = workloads.gdr_inputs(cfg["B"], cfg["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], dtype="bf16", seed=0,
+                               lengths=lengths, dht=True)
+    dev = {k: inp[k].cuda() for k in ("q", "k", "v", "beta", "dO", "gcum", "dht")}
+    cu = None if inp["cu"] is None else torch.tensor(inp["cu"], dtype=torch.int32, device="cuda")
+    T = inp["T"]
+    prob, keep = binding.make_problem(cfg["B"], T, cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], torch.bfloat16, 64, cu)
+    N = inp["N"]
+    ws = torch.empty(binding.workspace_size(prob), dtype=torch.uint8, device="cuda")
+    out = {"dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]), "dv": torch.empty_like(dev["v"]),
+           "dg": torch.empty(dev["gcum"].shape, dtype=torch.float32, device="cuda"),
+           "dbeta": torch.empty(dev["beta"].shape, dtype=torch.float32, device="cuda"),
+           "dh0": torch.empty((N, cfg["HV"], cfg["K"], cfg["V"]), dtype=torch.float32, device="cuda")}
+    P = binding._ptr
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    args_c = [ctypes.byref(prob), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["gcum"]), P(dev["beta"]), None,
+              P(dev["dO"]), P(dev["dht"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]), P(out["dbeta"]),
+              P(out["dh0"]), P(ws), ws.numel(), sp]
+    hip, evs = hip_events(4 * args.steps)
+
+    def call(i=None):
+        ev = None if i is None else ctypes.byref(evs, 4 * i * ctypes.sizeof(ctypes.c_void_p))
+        rc = binding.lib.gdr_chunk_bwd_events(*args_c, ev)
+        if rc != 0:
+            raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stage = {"prep": 0.0, "scans": 0.0, "grad": 0.0}
+    for i in range(args.steps):
+        e = [evs[4 * i + j] for j in range(4)]
+        stage["prep"] += elapsed_ms(hip, e[0], e[1]) / args.steps
+        stage["scans"] += elapsed_ms(hip, e[1], e[2]) / args.steps
+        stage["grad"] += elapsed_ms(hip, e[2], e[3]) / args.steps
+    chunks = chunk_lengths(lengths, cfg["T"], cfg["B"], 64)
+    F = sum(flop_model(c, cfg["K"], cfg["V"]) for c in chunks) * cfg["HV"]
+    tflops = F / (ms_per_step * 1e-3) / 1e12
+    kb = kernel_bytes(cfg, chunks)
+    dom = max(stage, key=stage.get)
+    achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
+    kernel_name = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}[dom]
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{args.workload}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            t = json.load(fh)
+        if t.get("source_digest") == source_digest(t.get("sources", [])):
+            traffic = t.get("bytes_per_launch")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel_name,
+            "kernel_ms": round(stage[dom], 4), "algorithmic_bytes": kb[dom],
+            "stage_ms": {k: round(v, 4) for k, v in stage.items()}}
+
+    res = {"metric": "GDN chunked bwd eff. TFLOP/s (ms/call in ms_per_step) at T=32k, H=16, K=V=128, BT=64",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
+           "config": {"workload": cfg["name"], "B": cfg["B"], "T": T, "HK": cfg["HK"], "HV": cfg["HV"],
+                      "K": cfg["K"], "V": cfg["V"], "BT": 64, "global_batch": cfg["B"], "seq_len": T,
+                      "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2)},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+    del keep
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+"""Thin ctypes binding of libgdr.so (include/gdr.h) over torch tensors.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, output tensors and the workspace are allocated with torch, and the
+pointers and the current HIP stream are handed to the C ABI.  Every step of the
+computation runs in the library's gfx950 kernels; if the library is missing the
+import fails (there is no fallback).
+
+Layouts (token axis flattened over the batch, as in include/gdr.h):
+  q, k [B*T, HK, K]   v, dO [B*T, HV, V]   beta [B*T, HV]   g_cum [B*T, HV] fp32
+  h0, dht, dh0 [N, HV, K, V] fp32
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_F32, GDR_F16, GDR_BF16 = 0, 1, 2
+_DT = {torch.float32: GDR_F32, torch.float16: GDR_F16, torch.bfloat16: GDR_BF16}
+STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED", -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_LAUNCH"}
+
+
+class GdrError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("HK", ctypes.c_int), ("HV", ctypes.c_int),
+                ("K", ctypes.c_int), ("V", ctypes.c_int), ("BT", ctypes.c_int), ("N", ctypes.c_int),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run chunked_gated_delta_08_amd/build.py (hipcc, gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+lib.gdr_strerror.restype = ctypes.c_char_p
+lib.gdr_strerror.argtypes = [ctypes.c_int]
+lib.gdr_num_chunks.restype = ctypes.c_int64
+lib.gdr_num_chunks.argtypes = [ctypes.POINTER(Problem)]
+lib.gdr_workspace_size.restype = _sz
+lib.gdr_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+lib.gdr_fwd_states.restype = ctypes.c_int
+lib.gdr_fwd_states.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp]
+lib.gdr_chunk_bwd.restype = ctypes.c_int
+lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp]
+lib.gdr_chunk_bwd_events.restype = ctypes.c_int
+lib.gdr_chunk_bwd_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp, _vp]
+lib.kda_chunk_bwd.restype = ctypes.c_int
+lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
+
+EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_chunk_bwd",
+            "gdr_chunk_bwd_events", "kda_chunk_bwd"]
+
+
+def _check(code):
+    if code != 0:
+        raise GdrError(code, lib.gdr_strerror(code).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_problem(B, T, HK, HV, K, V, dtype, BT=64, cu_seqlens=None, scale=None):
+    """Builds the gdr_problem struct.  cu_seqlens: int32 CUDA tensor [N+1] or None.
+    Returns (problem, keepalive) -- keep `keepalive` referenced while the struct is used."""
+    p = Problem(B, T, HK, HV, K, V, BT, 0, None, None, float(scale or 0.0), _DT[dtype])
+    keep = []
+    if cu_seqlens is not None:
+        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+        host = cu_seqlens.detach().to("cpu").contiguous()
+        keep += [cu_seqlens, host]
+        p.N = host.numel() - 1
+        p.cu_seqlens = cu_seqlens.data_ptr()
+        p.cu_seqlens_host = host.data_ptr()
+    return p, keep
+
+
+def num_chunks(p):
+    return int(lib.gdr_num_chunks(ctypes.byref(p)))
+
+
+def workspace_size(p):
+    return int(lib.gdr_workspace_size(ctypes.byref(p)))
+
+
+def _dims(q_or_k, v, cu_seqlens, B):
+    ntok, HK, K = q_or_k.shape
+    _, HV, V = v.shape
+    if cu_seqlens is None:
+        assert ntok % B == 0
+        return B, ntok // B, HK, HV, K, V
+    return 1, ntok, HK, HV, K, V
+
+
+def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, scale=None, BT=64,
+                  want_dh0=True, out=None, workspace=None, stream=None):
+    """Backward of the chunkwise gated delta rule.  Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
+    for t in (q, k, v, g_cum, beta, dO):
+        assert t.is_cuda and t.is_contiguous()
+    assert g_cum.dtype == torch.float32
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale)
+    N = B if cu_seqlens is None else p.N
+    dev = v.device
+    if out is None:
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "dg": torch.empty(g_cum.shape, dtype=torch.float32, device=dev),
+               "dbeta": torch.empty(beta.shape, dtype=torch.float32, device=dev),
+               "dh0": torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if want_dh0 else None}
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g_cum), _ptr(beta), _ptr(h0),
+                             _ptr(dO), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                             _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
+    del keep
+    return out
+
+
+def gdr_fwd_states(k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, BT=64, want_v_new=True, want_ht=True,
+                   workspace=None, stream=None):
+    """Per-chunk forward states h [NT, HV, K, V] fp32 (state entering each chunk), v_new, ht."""
+    B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, None)
+    N = B if cu_seqlens is None else p.N
+    dev = v.device
+    NT = num_chunks(p)
+    h = torch.empty((max(NT, 0), HV, K, V), dtype=torch.float32, device=dev)
+    vn = torch.empty_like(v) if want_v_new else None
+    ht = torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if want_ht else None
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_fwd_states(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g_cum), _ptr(beta), _ptr(h0), _ptr(h),
+                              _ptr(vn), _ptr(ht), _ptr(workspace), workspace.numel(), _stream(stream)))
+    del keep
+    return {"h": h, "v_new": vn, "ht": ht}
+
+
+def kda_chunk_bwd(q, k, v, v_new, g, beta, A, h, dO, dh, dv, scale=None, cu_seqlens=None, B=1, BT=64,
+                  out=None, stream=None):
+    """KDA WY backward stage.  Returns dict dq, dk, dv, db, dg, dA (the page's order)."""
+    ntok, H, K = k.shape
+    V = v.shape[-1]
+    T = ntok // B if cu_seqlens is None else ntok
+    p, keep = make_problem(B if cu_seqlens is None else 1, T, H, H, K, V, v.dtype, BT, cu_seqlens, scale)
+    dev = v.device
+    if out is None:
+        out = {"dq": torch.empty((ntok, H, K), dtype=torch.float32, device=dev),
+               "dk": torch.empty((ntok, H, K), dtype=torch.float32, device=dev),
+               "dv": torch.empty_like(v),
+               "db": torch.empty((ntok, H), dtype=torch.float32, device=dev),
+               "dg": torch.empty((ntok, H, K), dtype=torch.float32, device=dev),
+               "dA": torch.empty((ntok, H, BT), dtype=torch.float32, device=dev)}
+    _check(lib.kda_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(v_new), _ptr(g), _ptr(beta), _ptr(A),
+                             _ptr(h), _ptr(dO), _ptr(dh), _ptr(dv), _ptr(out["dq"]), _ptr(out["dk"]),
+                             _ptr(out["dv"]), _ptr(out["db"]), _ptr(out["dg"]), _ptr(out["dA"]), _stream(stream)))
+    del keep
+    return out

@@ -1,0 +1,58 @@
+"""Builds csrc/ into chunked_gated_delta_08_amd/libgdr.so for gfx950 with hipcc.
+
+Every HIP source is compiled with packed-fp32 instructions disabled
+(-Xclang -target-feature -Xclang -packed-fp32-ops); objects are built in
+parallel and linked into one shared library exporting the C ABI of
+include/gdr.h.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libgdr.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip"]
+HOST_SOURCES = ["gdr_api.cpp"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("command failed: " + " ".join(cmd))
+    return r
+
+
+def build(verbose=False, jobs=None):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cmds, objs = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([HIPCC] + COMMON + DEVICE + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = OUT + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp], verbose)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)

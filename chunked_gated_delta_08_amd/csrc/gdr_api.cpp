@@ -1,0 +1,202 @@
+// gdr_api.cpp -- the C ABI (include/gdr.h): host-side validation, workspace
+// plan and the launch sequence.  Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/gdr.h"
+#include "gdr_launch.hpp"
+
+namespace {
+
+using gdr::Problem;
+using gdr::WsPlan;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t elem_size(int dtype) { return dtype == GDR_F32 ? 4 : 2; }
+
+// Host-side checks shared by every entry point.  Fills `q` on success.
+int check_problem(const gdr_problem* p, Problem* q) {
+    if (!p) return GDR_ERR_INVALID;
+    if (p->B < 1 || p->T < 0 || p->HK < 1 || p->HV < 1 || p->K < 1 || p->V < 1 || p->BT < 1) return GDR_ERR_INVALID;
+    if (p->HV % p->HK != 0) return GDR_ERR_INVALID;
+    if (p->dtype != GDR_F32 && p->dtype != GDR_F16 && p->dtype != GDR_BF16) return GDR_ERR_INVALID;
+    int64_t nt = 0;
+    int nseq;
+    if (p->cu_seqlens) {
+        if (!p->cu_seqlens_host || p->B != 1 || p->N < 1) return GDR_ERR_INVALID;
+        const int32_t* cu = p->cu_seqlens_host;
+        if (cu[0] != 0) return GDR_ERR_INVALID;
+        for (int n = 0; n < p->N; n++) {
+            if (cu[n + 1] < cu[n]) return GDR_ERR_INVALID;
+            nt += (cu[n + 1] - cu[n] + p->BT - 1) / p->BT;
+        }
+        if (cu[p->N] != p->T) return GDR_ERR_INVALID;
+        nseq = p->N;
+    } else {
+        nt = (int64_t)p->B * ((p->T + p->BT - 1) / p->BT);
+        nseq = p->B;
+    }
+    if ((int64_t)p->B * p->T > INT32_MAX / 2) return GDR_ERR_UNSUPPORTED;
+    q->B = p->B; q->T = p->T; q->HK = p->HK; q->HV = p->HV; q->K = p->K; q->V = p->V; q->BT = p->BT;
+    q->N = nseq; q->NT = nt;
+    q->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
+    q->dtype = p->dtype;
+    q->cu = p->cu_seqlens;
+    return GDR_OK;
+}
+
+int check_supported(const Problem& q) {
+    if (q.BT != 64) return GDR_ERR_UNSUPPORTED;
+    if (q.K != q.V || (q.K != 64 && q.K != 128)) return GDR_ERR_UNSUPPORTED;
+    if (q.dtype == GDR_F32 && q.K != 64) return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH; }
+
+}  // namespace
+
+namespace gdr {
+
+WsPlan plan_workspace(const Problem& p) {
+    WsPlan w{};
+    const size_t es = elem_size(p.dtype);       // input type and scan operand type share a width
+    const size_t units = (size_t)p.NT * p.HV;
+    size_t off = 0;
+    w.chunk_info = off; off = align256(off + (size_t)(p.NT > 0 ? p.NT : 1) * sizeof(ChunkInfo));
+    w.seq_chunk0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
+    w.W = off; off = align256(off + units * 64 * p.K * es);
+    w.U = off; off = align256(off + units * 64 * p.V * es);
+    w.R = off; off = align256(off + units * 64 * p.K * es);
+    w.A = off; off = align256(off + units * 64 * 64 * es);
+    w.h = off; off = align256(off + units * (size_t)p.K * p.V * es);
+    w.dh = off; off = align256(off + units * (size_t)p.K * p.V * es);
+    w.total = off;
+    return w;
+}
+
+}  // namespace gdr
+
+extern "C" {
+
+const char* gdr_strerror(int status) {
+    switch (status) {
+        case GDR_OK: return "ok";
+        case GDR_ERR_INVALID: return "invalid argument (shape, dtype, null pointer or cu_seqlens)";
+        case GDR_ERR_UNSUPPORTED: return "unsupported configuration (this build handles BT=64, K=V in {64,128}; fp32 only at K=64)";
+        case GDR_ERR_WORKSPACE: return "workspace missing or smaller than gdr_workspace_size()";
+        case GDR_ERR_LAUNCH: return "HIP error at kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int64_t gdr_num_chunks(const gdr_problem* p) {
+    Problem q;
+    if (check_problem(p, &q) != GDR_OK) return -1;
+    return q.NT;
+}
+
+size_t gdr_workspace_size(const gdr_problem* p) {
+    Problem q;
+    if (check_problem(p, &q) != GDR_OK) return 0;
+    return gdr::plan_workspace(q).total;
+}
+
+int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const float* g_cum, const void* beta,
+                   const float* h0, float* h_out, void* v_new_out, float* ht_out, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    Problem q;
+    int st = check_problem(p, &q);
+    if (st != GDR_OK) return st;
+    if ((st = check_supported(q)) != GDR_OK) return st;
+    if (q.NT > 0 && (!k || !v || !g_cum || !beta || !h_out)) return GDR_ERR_INVALID;
+    const WsPlan w = gdr::plan_workspace(q);
+    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
+    auto* sc0 = (int32_t*)(base + w.seq_chunk0);
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
+    if (q.NT > 0) {
+        st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
+                                            nullptr, stream));
+        if (st != GDR_OK) return st;
+    }
+    gdr::ScanArgs a{};
+    a.k = k; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
+    a.W = base + w.W; a.U = base + w.U; a.h0 = h0;
+    a.h32 = h_out; a.v_new = v_new_out; a.ht = ht_out;
+    a.do_fwd = true; a.do_rev = false;
+    return launch_status(gdr::launch_scans(q, a, stream));
+}
+
+int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                         const void* beta, const float* h0, const void* dO, const float* dht, void* dq, void* dk,
+                         void* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t* ev) {
+    Problem q;
+    int st = check_problem(p, &q);
+    if (st != GDR_OK) return st;
+    if ((st = check_supported(q)) != GDR_OK) return st;
+    if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
+        return GDR_ERR_INVALID;
+    const WsPlan w = gdr::plan_workspace(q);
+    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
+    auto* sc0 = (int32_t*)(base + w.seq_chunk0);
+    auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
+    if ((st = mark(0)) != GDR_OK) return st;
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
+    if (q.NT > 0) {
+        st = launch_status(gdr::launch_prep(q, qp, k, v, g_cum, beta, info, base + w.W, base + w.U, base + w.R,
+                                            base + w.A, stream));
+        if (st != GDR_OK) return st;
+    }
+    if ((st = mark(1)) != GDR_OK) return st;
+    gdr::ScanArgs a{};
+    a.k = k; a.dO = dO; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
+    a.W = base + w.W; a.U = base + w.U; a.R = base + w.R;
+    a.h0 = h0; a.dht = dht;
+    a.hT = base + w.h; a.dhT = base + w.dh; a.dh0 = dh0;
+    a.do_fwd = q.NT > 0; a.do_rev = true;
+    if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
+    if ((st = mark(2)) != GDR_OK) return st;
+    if (q.NT > 0) {
+        gdr::GradArgs g{};
+        g.q = qp; g.k = k; g.v = v; g.gcum = g_cum; g.beta = beta; g.dO = dO;
+        g.hT = base + w.h; g.dhT = base + w.dh; g.A = base + w.A; g.info = info;
+        g.dq = dq; g.dk = dk; g.dv = dv; g.dg = dg; g.dbeta = dbeta;
+        st = launch_status(gdr::launch_grad(q, g, stream));
+        if (st != GDR_OK) return st;
+    }
+    return mark(3);
+}
+
+int gdr_chunk_bwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                  const void* beta, const float* h0, const void* dO, const float* dht, void* dq, void* dk, void* dv,
+                  float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return gdr_chunk_bwd_events(p, qp, k, v, g_cum, beta, h0, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes,
+                                stream, nullptr);
+}
+
+int kda_chunk_bwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const void* v_new,
+                  const float* g, const void* beta, const void* A, const float* h, const void* dO, const float* dh,
+                  const void* dv_in, float* dq, float* dk, void* dv_out, float* db, float* dg, float* dA,
+                  hipStream_t stream) {
+    Problem q;
+    int st = check_problem(p, &q);
+    if (st != GDR_OK) return st;
+    if (q.HK != q.HV) return GDR_ERR_INVALID;
+    if (q.dtype == GDR_BF16) return GDR_ERR_UNSUPPORTED;
+    if (q.BT != 64 || q.K != q.V || (q.K != 64 && q.K != 128)) return GDR_ERR_UNSUPPORTED;
+    if (q.NT == 0) return GDR_OK;
+    if (!qp || !k || !v || !v_new || !g || !beta || !A || !h || !dO || !dh || !dv_in || !dq || !dk || !dv_out ||
+        !db || !dg || !dA)
+        return GDR_ERR_INVALID;
+    gdr::KdaArgs a{};
+    a.q = qp; a.k = k; a.v = v; a.v_new = v_new; a.g = g; a.beta = beta; a.A = A; a.h = h; a.dO = dO; a.dh = dh;
+    a.dv_in = dv_in; a.dq = dq; a.dk = dk; a.dv_out = dv_out; a.db = db; a.dg = dg; a.dA = dA;
+    return launch_status(gdr::launch_kda(q, a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// gdr_device.hpp -- device-side building blocks for the gfx950 kernels.
+//
+// MFMA operand layouts (16x16 output tile, wave64; verified on gfx950):
+//   16-bit (v_mfma_f32_16x16x32_{bf16,f16}): lane l = 16*g + r holds
+//       A[r][8g+i], B[8g+i][r] for i = 0..7, and D[4g+j][r] for j = 0..3.
+//   fp32   (v_mfma_f32_16x16x4_f32):        lane l holds A[r][g], B[g][r],
+//       and the same D layout.
+// Operands come from LDS in one of two orientations:
+//   "direct": the matrix is stored with its reduction index k contiguous
+//             (A as [m][k], B as [n][k]) -> one 16-byte read per fragment;
+//   "trans":  the matrix is stored with k strided (A as [k][m], B as [k][n])
+//             -> two ds_read_b64_tr_b16 transposing reads per fragment.
+//   ds_read_b64_tr_b16: within each 16-lane group, lane r addresses 8 bytes at
+//   row (k0 + r/4), column (mn0 + 4*(r%4)); lane i then receives
+//   X[k0 + j][mn0 + i] for j = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+using bf16 = __bf16;
+using f16 = _Float16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef WG_KUNROLL
+#define WG_KUNROLL 2
+#endif
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <class E> __device__ __forceinline__ E to_e(float x) { return (E)x; }
+template <class E> __device__ __forceinline__ float to_f(E x) { return (float)x; }
+
+// --------------------------------------------------------------------------
+// MFMA traits
+template <class E> struct Mma;
+template <> struct Mma<bf16> {
+    static constexpr int KS = 32;
+    using frag = bf16x8;
+    __device__ __forceinline__ static f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<f16> {
+    static constexpr int KS = 32;
+    using frag = f16x8;
+    __device__ __forceinline__ static f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<float> {
+    static constexpr int KS = 4;
+    using frag = float;
+    __device__ __forceinline__ static f32x4 run(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// --------------------------------------------------------------------------
+// Fragment loads from LDS (padded row-major tiles, leading dimension ld).
+// Requirements (16-bit): ld % 8 == 0, k0 % 8 == 0 for direct; ld % 4 == 0,
+// mn0 % 4 == 0 for trans.
+template <class E>
+__device__ __forceinline__ typename Mma<E>::frag ld_direct(const E* X, int ld, int mn0, int k0) {
+    const int l = lane_id();
+    if constexpr (sizeof(E) == 2) {
+        return *(const typename Mma<E>::frag*)(X + (mn0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+    } else {
+        return X[(mn0 + (l & 15)) * ld + k0 + (l >> 4)];
+    }
+}
+
+template <class E>
+__device__ __forceinline__ typename Mma<E>::frag ld_trans(const E* X, int ld, int mn0, int k0) {
+    const int l = lane_id();
+    const int r = l & 15, g = l >> 4;
+    if constexpr (sizeof(E) == 2) {
+        const E* p = X + (k0 + 8 * g + (r >> 2)) * ld + mn0 + 4 * (r & 3);
+        i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+        i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 4 * ld));
+        i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        return __builtin_bit_cast(typename Mma<E>::frag, c);
+    } else {
+        return X[(k0 + g) * ld + mn0 + r];
+    }
+}
+
+// Transposing read of 4 consecutive k (rows k0 + 4*g_sel .. +3 chosen by the
+// caller through `krow`) for column mn0 + r of a [k][mn] tile: the building
+// block for fragments whose k order is permuted (see the scans).
+template <class E>
+__device__ __forceinline__ i16x4 ld_trans4(const E* X, int ld, int mn0, int krow) {
+    const int r = lane_id() & 15;
+    const E* p = X + (krow + (r >> 2)) * ld + mn0 + 4 * (r & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+}
+
+// --------------------------------------------------------------------------
+// Wave-level GEMM: acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD.
+// AT: A stored [k][m] (else [m][k]).  BT_: B stored [k][n] (else [n][k]).
+template <class E, int TM, int TN, int KD, bool AT, bool BT_>
+__device__ __forceinline__ void wgemm(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0,
+                                      int n0) {
+    using M = Mma<E>;
+#pragma unroll WG_KUNROLL
+    for (int k0 = 0; k0 < KD; k0 += M::KS) {
+        typename M::frag a[TM], b[TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++) a[i] = AT ? ld_trans<E>(A, lda, m0 + 16 * i, k0) : ld_direct<E>(A, lda, m0 + 16 * i, k0);
+#pragma unroll
+        for (int j = 0; j < TN; j++) b[j] = BT_ ? ld_trans<E>(B, ldb, n0 + 16 * j, k0) : ld_direct<E>(B, ldb, n0 + 16 * j, k0);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) acc[i][j] = M::run(a[i], b[j], acc[i][j]);
+    }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = zero4();
+}
+
+// Row / column of accumulator element e of tile (i, j) for this lane.
+__device__ __forceinline__ int acc_row(int m0, int i, int e) { return m0 + 16 * i + 4 * (lane_id() >> 4) + e; }
+__device__ __forceinline__ int acc_col(int n0, int j) { return n0 + 16 * j + (lane_id() & 15); }
+
+// Global <-> register helpers
+template <class E> struct Vec16;  // 16-byte vector of E
+template <> struct Vec16<bf16> { using t = bf16x8; static constexpr int n = 8; };
+template <> struct Vec16<f16> { using t = f16x8; static constexpr int n = 8; };
+template <> struct Vec16<float> { using t = f32x4; static constexpr int n = 4; };
+
+}  // namespace gdr

@@ -1,0 +1,488 @@
+// gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
+//
+// One workgroup (8 waves) per (chunk, key head); it loops over the value heads
+// that share the key head and keeps the dq/dk group sums in registers (the
+// GQA reduction the FlashQLA backward explainer, §一 step ④, does in Python).
+// Given h = h[c] (state entering the chunk) and dh = dh[c] (gradient of the
+// state leaving it) from the scans, and recomputing the chunk's WY factors:
+//   L = strictly-lower(diag(β)(K Kᵀ) ⊙ Γ),  A = (I+L)^{-1} (read from the prep kernel),
+//   Pm = scale·lower(Γ ⊙ Q Kᵀ),  V_new = A·diag(β)(V − diag(γ) K h)
+//   dV_new = Pmᵀ dO + diag(γ_C/γ) K dh
+//   dPm = lower(dO V_newᵀ)                    T1 = dPm ⊙ Γ · scale
+//   dq  = scale·diag(γ) dO hᵀ + T1 K
+//   dW  = −dV_new hᵀ,   dv = diag(β) Aᵀ dV_new
+//   dA  = dV_new (diag(β)V)ᵀ + dW (diag(βγ)K)ᵀ,   dL = −strictlower(Aᵀ dA Aᵀ)
+//   E   = dL ⊙ Γ,  Eb = diag(β) E
+//   dk  = T1ᵀ Q + diag(γ_C/γ) V_new dhᵀ + diag(βγ) Aᵀ dW + Eb K + Ebᵀ K
+//   dβ  = rowsum(Aᵀ dV_new ⊙ V) + γ ⊙ rowsum(Aᵀ dW ⊙ K) + rowsum(dL ⊙ Γ ⊙ KKᵀ)
+//   dG  = rowsum(Q ⊙ scale γ dO hᵀ) + rowsum(F) − colsum(F)          F  = dPm ⊙ Pm
+//         − z + βγ ⊙ rowsum(Aᵀ dW ⊙ K) + rowsum(F2) − colsum(F2)      F2 = dL ⊙ L
+//         with z = rowsum(K ⊙ diag(γ_C/γ) V_new dhᵀ);  the last row also
+//         gains Σz + γ_C <dh, h>;
+//   dg  = in-chunk reverse cumsum of dG  (same page, §一: the gate arrives as
+//         its in-chunk cumsum and its gradient is reverse-cumsummed at the end).
+// All contractions run on MFMA (16-bit operands for 16-bit inputs, fp32 for
+// fp32 inputs) with fp32 accumulation; the state-dependent products are taken
+// over V in 64-column slices so the LDS footprint stays under 140 KB.
+// Every output tile of a wave uses rows 32*(w&1) .. +31, so the per-row
+// reductions (dG, dβ) accumulate in registers and are reduced once, in a
+// fixed order (deterministic, no atomics).
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 8 : 4; }
+
+template <class E, int KD, int VD>
+struct GradCfg {
+    static constexpr int C = 64, VH = 64, NVH = VD / VH;
+    static constexpr int LK = KD + gpad<E>(), LA = 64 + gpad<E>(), LS = VH + gpad<E>(), LF = 68;
+    static constexpr int TNK = KD / 64;      // 16-col tiles per wave for [64][KD] outputs
+    // byte offsets.  The V slice lives in Q's buffer during the V loop (Q is
+    // reloaded afterwards); after the loop the slice region holds dW, dA_pre,
+    // M1 and Eb.
+    static constexpr size_t oQ = 0;
+    static constexpr size_t oK = oQ + (size_t)C * LK * sizeof(E);
+    static constexpr size_t oA = oK + (size_t)C * LK * sizeof(E);
+    static constexpr size_t oPm = oA + (size_t)C * LA * sizeof(E);
+    static constexpr size_t oH = oPm + (size_t)C * LA * sizeof(E);
+    static constexpr size_t odH = oH + (size_t)VH * LK * sizeof(E);
+    static constexpr size_t odO = odH + (size_t)VH * LK * sizeof(E);
+    static constexpr size_t oVn = odO + (size_t)C * LS * sizeof(E);
+    static constexpr size_t odVn = oVn + (size_t)C * LS * sizeof(E);
+    static constexpr size_t oSm = odVn + (size_t)C * LS * sizeof(E);
+    // small arrays: G, β, γ, row partials 2x[4][64], col partials [2][64], misc [80]
+    static constexpr size_t smem = oSm + (size_t)(3 * 64 + 8 * 64 + 2 * 64 + 80) * 4;
+    static constexpr size_t oV = oQ;                                    // [64][LS] inside the V loop
+    static constexpr size_t odW = oH;                                   // [64][LK]
+    static constexpr size_t odA = odH;                                  // [64][LA]
+    static constexpr size_t oM1 = odO;                                  // [64][LA]
+    static constexpr size_t oEb = oVn;                                  // [64][LA]
+    static_assert(LS <= LK && LA <= LK, "alias size");
+    static_assert(LA == LS, "alias size");
+};
+
+template <class Ein, class E, int D, int LD>
+__device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, long rs, int C, int rows = 64) {
+    constexpr int EPV = 16 / sizeof(Ein);
+    constexpr int VPR = D / EPV;
+    for (int idx = threadIdx.x; idx < rows * VPR; idx += 512) {
+        const int r = idx / VPR, c = idx % VPR;
+        typename Vec16<Ein>::t v;
+        if (r < C) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
+        else v = typename Vec16<Ein>::t{};
+        *(typename Vec16<E>::t*)(s + r * LD + c * EPV) = v;
+    }
+}
+
+// sum over the 16 lanes that share a row group (lane bits 0..3)
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+// sum over the 4 row groups (lane bits 4..5)
+__device__ __forceinline__ float sum4g(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// GT: value heads per key head as a compile-time constant (0 = runtime); the
+// head and slice loops are unrolled so no addressing is hoisted across them.
+template <class E, int KD, int VD, int GT>
+__global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, float scale) {
+    using Cf = GradCfg<E, KD, VD>;
+    constexpr int C = 64, TNK = Cf::TNK, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, LF = Cf::LF;
+    extern __shared__ __align__(16) unsigned char smem[];
+    E* sQ = (E*)(smem + Cf::oQ);
+    E* sK = (E*)(smem + Cf::oK);
+    E* sA = (E*)(smem + Cf::oA);
+    E* sPm = (E*)(smem + Cf::oPm);
+    E* sH = (E*)(smem + Cf::oH);
+    E* sdH = (E*)(smem + Cf::odH);
+    E* sdO = (E*)(smem + Cf::odO);
+    E* sV = (E*)(smem + Cf::oV);
+    E* sVn = (E*)(smem + Cf::oVn);
+    E* sdVn = (E*)(smem + Cf::odVn);
+    E* sdW = (E*)(smem + Cf::odW);
+    E* sdA = (E*)(smem + Cf::odA);
+    E* sM1 = (E*)(smem + Cf::oM1);
+    E* sEb = (E*)(smem + Cf::oEb);
+    float* sG = (float*)(smem + Cf::oSm);
+    float* sB = sG + 64;
+    float* sGam = sB + 64;
+    float* sRowG = sGam + 64;      // [4][64] row partials of dG per column block
+    float* sRowB = sRowG + 4 * 64; // [4][64] row partials of dβ
+    float* sCol = sRowB + 4 * 64;  // [2][64] column partials of dG per row half
+    float* sMisc = sCol + 2 * 64;  // [16 + 64]
+
+    const int ci = blockIdx.x, hk = blockIdx.y, G = GT ? GT : HV / HK;
+    const ChunkInfo ch = a.info[ci];
+    const int Cn = ch.len;
+    const long t0 = ch.t0;
+    const int w = wave_id(), l = lane_id(), r16 = l & 15, g4 = l >> 4;
+    const int m0 = 32 * (w & 1);           // every output block of this wave starts at this row
+    const int n0s = 16 * (w >> 1);         // column block for [64][64] outputs
+    const int n0k = (KD / 4) * (w >> 1);   // column block for [64][KD] outputs
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const E* v = (const E*)a.v;
+    const E* dO = (const E*)a.dO;
+    const E* hT = (const E*)a.hT;
+    const E* dhT = (const E*)a.dhT;
+    const E* beta = (const E*)a.beta;
+
+    g_load_rows<E, E, KD, LK>(sQ, q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+    g_load_rows<E, E, KD, LK>(sK, k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+
+    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];
+    zero_acc(dq_tot);
+    zero_acc(dk_tot);
+
+#pragma unroll
+    for (int hi = 0; hi < G; hi++) {
+        const int hv = hk * G + hi;
+        const long unit = (long)ci * HV + hv;
+        if (threadIdx.x < C) {
+            const int r = threadIdx.x;
+            const float gg = a.gcum[(t0 + min(r, Cn - 1)) * HV + hv];
+            sG[r] = gg;
+            sGam[r] = __expf(gg);
+            sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
+        }
+        __syncthreads();
+        const float gl = sG[C - 1], gC = sGam[C - 1];
+
+        // per-lane partial row sums (rows m0 + 16i + 4g4 + e) and column sums
+        float rowG[2][4], rowB[2][4], colG[1];
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) rowG[i][e] = rowB[i][e] = 0.f;
+        colG[0] = 0.f;
+        float hdh = 0.f;   // partial <dh, h>
+
+        // ---- S_qk -> Pm = scale · lower(Γ ⊙ Q Kᵀ)
+        {
+            f32x4 aqk[2][1];
+            zero_acc(aqk);
+            wgemm<E, 2, 1, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                    const float gm = (cc <= rr) ? __expf(sG[rr] - sG[cc]) : 0.f;
+                    sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][0][e] : 0.f);
+                }
+        }
+        // ---- A = (I+L)^{-1} from the prep kernel
+        g_load_rows<E, E, 64, LA>(sA, (const E*)a.A + unit * C * C, C, C);
+        __syncthreads();
+
+        // persistent accumulators over the V slices
+        f32x4 dPm[2][1], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][1];
+        zero_acc(dPm);
+        zero_acc(dqi);
+        zero_acc(dWa);
+        zero_acc(dks);
+        zero_acc(dAp);
+
+#pragma unroll
+        for (int vh = 0; vh < Cf::NVH; vh++) {
+            // h / dh slices are stored transposed: [V][K] per chunk -> rows v
+            g_load_rows<E, E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD, KD, 64);
+            g_load_rows<E, E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD, KD, 64);
+            g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+            g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+            __syncthreads();
+            // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
+            {
+                f32x4 kh[2][1], kdh[2][1], pdo[2][1];
+                zero_acc(kh);
+                zero_acc(kdh);
+                zero_acc(pdo);
+                wgemm<E, 2, 1, KD, false, false>(kh, sK, LK, sH, LK, m0, n0s);
+                wgemm<E, 2, 1, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0s);
+                wgemm<E, 2, 1, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0s);
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                        const float z = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]);
+                        sVn[rr * LS + cc] = to_e<E>(z);
+                        sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + __expf(gl - sG[rr]) * kdh[i][0][e]);
+                    }
+            }
+            // <dh, h> over this slice
+            for (int idx = threadIdx.x; idx < 64 * KD; idx += 512) {
+                const int rr = idx / KD, cc = idx % KD;
+                hdh += (float)sH[rr * LK + cc] * (float)sdH[rr * LK + cc];
+            }
+            __syncthreads();
+            // ---- V_new = A Z
+            {
+                f32x4 vn[2][1];
+                zero_acc(vn);
+                wgemm<E, 2, 1, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) sVn[acc_row(m0, i, e) * LS + acc_col(n0s, 0)] = to_e<E>(vn[i][0][e]);
+            }
+            __syncthreads();
+            // ---- accumulate the state products and the V-separable outputs
+            wgemm<E, 2, 1, 64, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);     // dO V_newᵀ
+            wgemm<E, 2, TNK, 64, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);    // dO hᵀ
+            wgemm<E, 2, TNK, 64, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);   // dV_new hᵀ
+            wgemm<E, 2, TNK, 64, false, true>(dks, sVn, LS, sdH, LK, m0, n0k);   // V_new dhᵀ
+            wgemm<E, 2, 1, 64, false, false>(dAp, sdVn, LS, sV, LS, m0, n0s);     // dV_new Vᵀ
+            {
+                f32x4 adv[2][1];
+                zero_acc(adv);
+                wgemm<E, 2, 1, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0s);    // Aᵀ dV_new
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                        rowB[i][e] += adv[i][0][e] * (float)sV[rr * LS + cc];
+                        if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
+                    }
+            }
+            __syncthreads();
+        }
+
+        // ---- Q back into its buffer (it held the V slices)
+        g_load_rows<E, E, KD, LK>(sQ, q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        // ---- F = dPm ⊙ Pm -> dG; T1 = dPm ⊙ Γ · scale (over Pm); dW -> LDS
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                const bool lo = cc <= rr;
+                const float dp = lo ? dPm[i][0][e] : 0.f;
+                const float f = dp * (float)sPm[rr * LA + cc];
+                rowG[i][e] += f;
+                colG[0] += f;
+                sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
+            }
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < TNK; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sdW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = to_e<E>(-dWa[i][j][e]);
+        __syncthreads();
+        E* sT1 = sPm;
+
+        // ---- dq = scale γ dO hᵀ + T1 K ;  dG += rowsum(Q ⊙ scale γ dO hᵀ)
+        {
+            f32x4 t1k[2][TNK];
+            zero_acc(t1k);
+            wgemm<E, 2, TNK, 64, false, true>(t1k, sT1, LA, sK, LK, m0, n0k);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < TNK; j++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
+                        const float di = scale * sGam[rr] * dqi[i][j][e];
+                        rowG[i][e] += di * (float)sQ[rr * LK + cc];
+                        dq_tot[i][j][e] += di + t1k[i][j][e];
+                    }
+        }
+        // ---- dk: T1ᵀ Q + diag(γ_C/γ) V_new dhᵀ (z terms) + diag(βγ) Aᵀ dW
+        float zsum = 0.f;
+        {
+            f32x4 acc[2][TNK];
+            zero_acc(acc);
+            wgemm<E, 2, TNK, 64, true, true>(acc, sT1, LA, sQ, LK, m0, n0k);
+            f32x4 adw[2][TNK];
+            zero_acc(adw);
+            wgemm<E, 2, TNK, 64, true, true>(adw, sA, LA, sdW, LK, m0, n0k);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < TNK; j++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
+                        const float kv = (float)sK[rr * LK + cc];
+                        const float ds = __expf(gl - sG[rr]) * dks[i][j][e];
+                        const float z = ds * kv;
+                        rowG[i][e] -= z;
+                        zsum += z;
+                        const float aw = adw[i][j][e] * kv;
+                        rowB[i][e] += sGam[rr] * aw;
+                        rowG[i][e] += sB[rr] * sGam[rr] * aw;
+                        dk_tot[i][j][e] += acc[i][j][e] + ds + sB[rr] * sGam[rr] * adw[i][j][e];
+                    }
+        }
+        // ---- dA_pre = dV_new (diag(β)V)ᵀ + dW (diag(βγ)K)ᵀ  -> LDS
+        {
+            f32x4 dwk[2][1];
+            zero_acc(dwk);
+            wgemm<E, 2, 1, KD, false, false>(dwk, sdW, LK, sK, LK, m0, n0s);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                    sdA[rr * LA + cc] = to_e<E>(sB[cc] * (dAp[i][0][e] + sGam[cc] * dwk[i][0][e]));
+                }
+        }
+        __syncthreads();
+        // ---- M1 = Aᵀ dA_pre
+        {
+            f32x4 m1[2][1];
+            zero_acc(m1);
+            wgemm<E, 2, 1, 64, true, true>(m1, sA, LA, sdA, LA, m0, n0s);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sM1[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = to_e<E>(m1[i][0][e]);
+        }
+        __syncthreads();
+        // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ
+        {
+            f32x4 dl[2][1], akk[2][1];
+            zero_acc(dl);
+            zero_acc(akk);
+            wgemm<E, 2, 1, 64, false, false>(dl, sM1, LA, sA, LA, m0, n0s);
+            wgemm<E, 2, 1, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                    const bool lo = cc < rr;
+                    const float d = lo ? -dl[i][0][e] : 0.f;
+                    const float lg = lo ? __expf(sG[rr] - sG[cc]) * akk[i][0][e] : 0.f;   // Γ ⊙ KKᵀ
+                    rowB[i][e] += d * lg;
+                    const float f2 = d * sB[rr] * lg;
+                    rowG[i][e] += f2;
+                    colG[0] += f2;
+                    sEb[rr * LA + cc] = to_e<E>(lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f);
+                }
+        }
+        __syncthreads();
+        // ---- dk += Eb K + Ebᵀ K
+        {
+            f32x4 acc[2][TNK];
+            zero_acc(acc);
+            wgemm<E, 2, TNK, 64, false, true>(acc, sEb, LA, sK, LK, m0, n0k);
+            wgemm<E, 2, TNK, 64, true, true>(acc, sEb, LA, sK, LK, m0, n0k);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < TNK; j++) dk_tot[i][j] += acc[i][j];
+        }
+
+        // ---- reductions (fixed order): rows over the 16 lanes of a group and
+        // the four column blocks; columns over the 4 row groups and 2 row halves
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float rg = sum16(rowG[i][e]);
+                const float rb = sum16(rowB[i][e]);
+                if (r16 == 0) {
+                    const int rr = acc_row(m0, i, e);
+                    sRowG[(w >> 1) * 64 + rr] = rg;
+                    sRowB[(w >> 1) * 64 + rr] = rb;
+                }
+            }
+        {
+            const float cs = sum4g(colG[0]);
+            if (g4 == 0) sCol[(w & 1) * 64 + acc_col(n0s, 0)] = cs;
+        }
+        {
+            float hz = hdh, zz = zsum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                hz += __shfl_xor(hz, off, 64);
+                zz += __shfl_xor(zz, off, 64);
+            }
+            if (l == 0) { sMisc[w] = hz; sMisc[8 + w] = zz; }
+        }
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            const int rr = threadIdx.x;
+            float dG = (sRowG[rr] + sRowG[64 + rr] + sRowG[128 + rr] + sRowG[192 + rr]) - (sCol[rr] + sCol[64 + rr]);
+            const float db = sRowB[rr] + sRowB[64 + rr] + sRowB[128 + rr] + sRowB[192 + rr];
+            if (rr == C - 1) {
+                float hd = 0.f, zs = 0.f;
+                for (int i = 0; i < 8; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
+                dG += zs + gC * hd;
+            }
+            sMisc[16 + rr] = dG;
+            if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {   // in-chunk reverse cumulative sum
+            float acc = 0.f;
+            for (int rr = C - 1; rr >= 0; rr--) {
+                acc += sMisc[16 + rr];
+                if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = acc;
+            }
+        }
+        __syncthreads();
+    }
+    // ---- write the group sums dq, dk for this key head
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < TNK; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
+                if (rr < Cn) {
+                    ((E*)a.dq)[((t0 + rr) * HK + hk) * KD + cc] = to_e<E>(dq_tot[i][j][e]);
+                    ((E*)a.dk)[((t0 + rr) * HK + hk) * KD + cc] = to_e<E>(dk_tot[i][j][e]);
+                }
+            }
+}
+
+template <class E, int KD, int VD, int GT>
+static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
+    using Cf = GradCfg<E, KD, VD>;
+    static_assert(Cf::smem <= 160 * 1024, "LDS budget");
+    auto kern = grad_kernel<E, KD, VD, GT>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(512), Cf::smem, s, a, p.HK, p.HV, p.scale);
+    return hipGetLastError();
+}
+
+template <class E, int KD, int VD>
+static hipError_t grad_go(const Problem& p, const GradArgs& a, hipStream_t s) {
+    const int G = p.HV / p.HK;
+    if (G == 1) return grad_go1<E, KD, VD, 1>(p, a, s);
+    if (G == 2) return grad_go1<E, KD, VD, 2>(p, a, s);
+    return grad_go1<E, KD, VD, 0>(p, a, s);
+}
+
+hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s) {
+    if (p.K == 128 && p.V == 128) {
+        if (p.dtype == 2) return grad_go<bf16, 128, 128>(p, a, s);
+        if (p.dtype == 1) return grad_go<f16, 128, 128>(p, a, s);
+        return hipErrorInvalidValue;   // fp32 at 128 exceeds the LDS budget
+    }
+    if (p.K == 64 && p.V == 64) {
+        if (p.dtype == 2) return grad_go<bf16, 64, 64>(p, a, s);
+        if (p.dtype == 1) return grad_go<f16, 64, 64>(p, a, s);
+        return grad_go<float, 64, 64>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

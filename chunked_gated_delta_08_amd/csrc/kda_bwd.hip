@@ -1,0 +1,330 @@
+// kda_bwd.hip -- the KDA (per-channel gate) WY backward stage.
+//
+// Page: "chunk_kda_bwd_wy_dqkg_fused 算子" (MindSpeed-Ops).  Its 实现原理
+// section splits the work per (chunk, batch·head) and names the intermediates
+// dq = do·hᵀ, dk = v_new·dhᵀ, dw = −dv·hᵀ, then the gate/β/A corrections; its
+// 多阶段 kernel table adds the A·dw corrections of dk/dg/db, a masked dA_pre
+// and dA = −A(dA_pre·A).  Read with A as the chunk's lower-triangular WY
+// inverse (the page's A being its transpose), these are the exact gradients of
+//   Φ = scale<dO,(Q⊙γ)h> + <dh,(K⊙γ_C/γ)ᵀV_new> + <dh,diag(γ_C)h>
+//       + <dv, A(β⊙V) − A(β⊙γ⊙K)h>,        γ = e^g (per channel)
+// with respect to q, k, v, β, g and the strictly-lower L of A = (I+L)^{-1}:
+//   dq  = scale (dO hᵀ) ⊙ γ,   dks = (V_new dhᵀ) ⊙ γ_C/γ,   dw = −dv hᵀ
+//   dv' = β ⊙ Aᵀ dv,   dk = dks + βγ ⊙ Aᵀdw
+//   db  = rowsum(Aᵀdv ⊙ V) + rowsum(Aᵀdw ⊙ γ ⊙ K)
+//   dg  = Q⊙dq − K⊙dks + βγ⊙K⊙Aᵀdw,  last row + colsum(K⊙dks) + γ_C⊙rowsum(h⊙dh)
+//   dA  = −strictlower(Aᵀ dA_pre Aᵀ),  dA_pre = dv(β⊙V)ᵀ + dw(β⊙γ⊙K)ᵀ
+// The page runs this as six Ascend kernels to avoid the BT x BT post-processing
+// in one kernel; with 160 KB of LDS per CU it is one gfx950 kernel here.
+// One workgroup (8 waves) per (chunk, head); operands in the input type
+// (fp16 MFMA for fp16, fp32 MFMA for fp32) with fp32 accumulation.
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+template <class E> constexpr int kpad() { return sizeof(E) == 2 ? 8 : 4; }
+
+template <class E, int KD, int VD>
+struct KdaCfg {
+    static constexpr int C = 64;
+    static constexpr int LK = KD + kpad<E>(), LV = VD + kpad<E>(), LA = 64 + kpad<E>();
+    static constexpr int TN = KD / 64;       // [64][KD] outputs: 2 row tiles x TN col tiles per wave
+    static constexpr size_t oH = 0;                                          // h  [KD][LV]  (later dh)
+    static constexpr size_t oX = oH + (size_t)KD * LV * sizeof(E);           // dO [64][LV]  (later V_new)
+    static constexpr size_t oDV = oX + (size_t)C * LV * sizeof(E);           // dv_in [64][LV]
+    static constexpr size_t oA = oDV + (size_t)C * LV * sizeof(E);           // A [64][LA]
+    static constexpr size_t oDW = oA + (size_t)C * LA * sizeof(E);           // dw [64][LK]
+    static constexpr size_t oKb = oDW + (size_t)C * LK * sizeof(E);          // β γ K [64][LK]
+    static constexpr size_t oVb = oKb + (size_t)C * LK * sizeof(E);          // β V [64][LV]
+    static constexpr size_t oP = oVb + (size_t)C * LV * sizeof(E);           // dA_pre, then M1 [64][LA]
+    static constexpr size_t oSm = oP + (size_t)C * LA * sizeof(E);
+    static constexpr int NCS = 2 * KD > 256 ? 2 * KD : 256;   // column partials [2][KD], later db partials [4][64]
+    static constexpr size_t smem = oSm + (size_t)(64 + KD + NCS) * 4;
+};
+
+__device__ __forceinline__ void kda_find_chunk(const int32_t* __restrict__ cu, int N, int T, int BT, int ci, int& t0,
+                                               int& len) {
+    if (!cu) {
+        const int ncs = (T + BT - 1) / BT, b = ci / ncs, c = ci % ncs;
+        t0 = b * T + c * BT;
+        len = min(BT, T - c * BT);
+        return;
+    }
+    int base = 0;
+    for (int n = 0; n < N; n++) {
+        const int l = cu[n + 1] - cu[n], nc = (l + BT - 1) / BT;
+        if (ci < base + nc) {
+            const int c = ci - base;
+            t0 = cu[n] + c * BT;
+            len = min(BT, l - c * BT);
+            return;
+        }
+        base += nc;
+    }
+    t0 = 0;
+    len = 0;
+}
+
+template <class Ein, class E, int D, int LD>
+__device__ __forceinline__ void kda_load(E* s, const Ein* __restrict__ g, long rs, int rows_valid, int rows) {
+    constexpr int EPV = 16 / sizeof(Ein);
+    constexpr int VPR = D / EPV;
+    for (int idx = threadIdx.x; idx < rows * VPR; idx += 512) {
+        const int r = idx / VPR, c = idx % VPR;
+        typename Vec16<Ein>::t v;
+        if (r < rows_valid) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
+        else v = typename Vec16<Ein>::t{};
+#pragma unroll
+        for (int e = 0; e < EPV; e++) s[r * LD + c * EPV + e] = (E)(float)v[e];
+    }
+}
+
+template <class E, int KD, int VD>
+__global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H,
+                                                  float scale) {
+    using Cf = KdaCfg<E, KD, VD>;
+    constexpr int C = 64, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, TN = Cf::TN;
+    extern __shared__ __align__(16) unsigned char smem[];
+    E* sH = (E*)(smem + Cf::oH);
+    E* sX = (E*)(smem + Cf::oX);
+    E* sDV = (E*)(smem + Cf::oDV);
+    E* sA = (E*)(smem + Cf::oA);
+    E* sDW = (E*)(smem + Cf::oDW);
+    E* sKb = (E*)(smem + Cf::oKb);
+    E* sVb = (E*)(smem + Cf::oVb);
+    E* sP = (E*)(smem + Cf::oP);
+    float* sB = (float*)(smem + Cf::oSm);
+    float* sHD = sB + 64;        // rowsum_V(h ⊙ dh), per key
+    float* sCS = sHD + KD;       // [2][KD] column partials of K ⊙ dks
+
+    const int ci = blockIdx.x, hh = blockIdx.y;
+    int t0i, Cn;
+    kda_find_chunk(cu, N, T, 64, ci, t0i, Cn);
+    const long t0 = t0i;
+    const int w = wave_id(), l = lane_id(), g4 = l >> 4;
+    const int m0 = 32 * (w & 1), n0k = (KD / 4) * (w >> 1), n0s = 16 * (w >> 1);
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const E* v = (const E*)a.v;
+    const E* vn = (const E*)a.v_new;
+    const E* dO = (const E*)a.dO;
+    const E* dvi = (const E*)a.dv_in;
+    const E* Ain = (const E*)a.A;
+    const E* beta = (const E*)a.beta;
+    const long unit = (long)ci * H + hh;
+    const float* hg = a.h + unit * KD * VD;
+    const float* dhg = a.dh + unit * KD * VD;
+    auto gidx = [&](int r, int c) { return ((t0 + r) * H + hh) * (long)KD + c; };   // [.,H,KD] element
+
+    // ---- stage h, dO, dv_in, A (lower triangle), β, β γ K, β V
+    kda_load<float, E, VD, LV>(sH, hg, VD, KD, KD);
+    kda_load<E, E, VD, LV>(sX, dO + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
+    kda_load<E, E, VD, LV>(sDV, dvi + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
+    for (int idx = threadIdx.x; idx < C * 64; idx += 512) {
+        const int r = idx / 64, c = idx % 64;
+        const float x = (r < Cn && c <= r) ? (float)Ain[((t0 + r) * H + hh) * 64 + c] : 0.f;
+        sA[r * LA + c] = (E)x;
+    }
+    if (threadIdx.x < C) sB[threadIdx.x] = threadIdx.x < Cn ? (float)beta[(t0 + threadIdx.x) * H + hh] : 0.f;
+    // rowsum_V(h ⊙ dh) in fp32 straight from memory: 4 threads per key
+    {
+        const int key = threadIdx.x >> 2, part = threadIdx.x & 3;
+        float s = 0.f;
+        if (key < KD)
+            for (int c = part; c < VD; c += 4) s += hg[key * VD + c] * dhg[key * VD + c];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (part == 0 && key < KD) sHD[key] = s;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < C * KD; idx += 512) {
+        const int r = idx / KD, c = idx % KD;
+        float x = 0.f;
+        if (r < Cn) x = sB[r] * __expf(a.g[gidx(r, c)]) * (float)k[gidx(r, c)];
+        sKb[r * LK + c] = (E)x;
+    }
+    for (int idx = threadIdx.x; idx < C * VD; idx += 512) {
+        const int r = idx / VD, c = idx % VD;
+        float x = 0.f;
+        if (r < Cn) x = sB[r] * (float)v[((t0 + r) * H + hh) * VD + c];
+        sVb[r * LV + c] = (E)x;
+    }
+
+    // ---- dq_acc = dO hᵀ,  dw = −dv hᵀ      (B = hᵀ: h stored [key][v] = [n][k])
+    f32x4 dqa[2][TN], dwa[2][TN];
+    zero_acc(dqa);
+    zero_acc(dwa);
+    wgemm<E, 2, TN, VD, false, false>(dqa, sX, LV, sH, LV, m0, n0k);
+    wgemm<E, 2, TN, VD, false, false>(dwa, sDV, LV, sH, LV, m0, n0k);
+    __syncthreads();
+    // ---- swap in dh and V_new; dw -> LDS
+    kda_load<float, E, VD, LV>(sH, dhg, VD, KD, KD);
+    kda_load<E, E, VD, LV>(sX, vn + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) sDW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = (E)(-dwa[i][j][e]);
+    __syncthreads();
+    // ---- dks_acc = V_new dhᵀ ; AdW = Aᵀ dw ; AdV = Aᵀ dv (V-tiles)
+    f32x4 dka[2][TN], adw[2][TN];
+    zero_acc(dka);
+    zero_acc(adw);
+    wgemm<E, 2, TN, VD, false, false>(dka, sX, LV, sH, LV, m0, n0k);
+    wgemm<E, 2, TN, 64, true, true>(adw, sA, LA, sDW, LK, m0, n0k);
+    // dv_out = β Aᵀ dv, db part 1 = rowsum(Aᵀdv ⊙ V)
+    float dbr[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) dbr[i][e] = 0.f;
+    {
+        constexpr int TNV = VD / 64;
+        const int n0v = (VD / 4) * (w >> 1);
+        f32x4 adv[2][TNV];
+        zero_acc(adv);
+        wgemm<E, 2, TNV, 64, true, true>(adv, sA, LA, sDV, LV, m0, n0v);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < TNV; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0v, j);
+                    if (rr < Cn) {
+                        const long o = ((t0 + rr) * H + hh) * VD + cc;
+                        ((E*)a.dv_out)[o] = (E)(sB[rr] * adv[i][j][e]);
+                        dbr[i][e] += adv[i][j][e] * (float)v[o];
+                    }
+                }
+    }
+    // ---- per-element outputs dq, dk and dg (last-row terms after the column sums)
+    float csum[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) csum[j] = 0.f;
+    float dgl[2][TN][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
+                dgl[i][j][e] = 0.f;
+                if (rr < Cn) {
+                    const long o = gidx(rr, cc);
+                    const float gg = a.g[o], gm = __expf(gg);
+                    const float glast = a.g[gidx(Cn - 1, cc)];
+                    const float kk = (float)k[o], qq = (float)q[o];
+                    const float dqv = scale * dqa[i][j][e] * gm;
+                    const float dks = dka[i][j][e] * __expf(glast - gg);
+                    const float bgw = sB[rr] * gm * adw[i][j][e];
+                    a.dq[o] = dqv;
+                    a.dk[o] = dks + bgw;
+                    dgl[i][j][e] = qq * dqv - kk * dks + kk * bgw;
+                    csum[j] += kk * dks;
+                    dbr[i][e] += adw[i][j][e] * gm * kk;
+                }
+            }
+    // column sums over this wave's 32 rows -> sCS[row half][key]
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        float x = csum[j];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (g4 == 0) sCS[(w & 1) * KD + acc_col(n0k, j)] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
+                if (rr < Cn) {
+                    float x = dgl[i][j][e];
+                    if (rr == Cn - 1) x += sCS[cc] + sCS[KD + cc] + __expf(a.g[gidx(rr, cc)]) * sHD[cc];
+                    a.dg[gidx(rr, cc)] = x;
+                }
+            }
+    // ---- dA_pre = dv (βV)ᵀ + dw (βγK)ᵀ -> LDS (B operands stored [s][.] = [n][k])
+    {
+        f32x4 dap[2][1];
+        zero_acc(dap);
+        wgemm<E, 2, 1, VD, false, false>(dap, sDV, LV, sVb, LV, m0, n0s);
+        wgemm<E, 2, 1, KD, false, false>(dap, sDW, LK, sKb, LK, m0, n0s);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) sP[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = (E)dap[i][0][e];
+    }
+    // db: reduce over the 16 lanes of each row group, then over the 4 column blocks
+    float* sDB = sCS;   // reuse [4][64] (column sums already consumed above)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float x = dbr[i][e];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            x += __shfl_xor(x, 8, 64);
+            if ((l & 15) == 0) sDB[(w >> 1) * 64 + acc_row(m0, i, e)] = x;
+        }
+    // ---- M1 = Aᵀ dA_pre
+    f32x4 m1[2][1];
+    zero_acc(m1);
+    wgemm<E, 2, 1, 64, true, true>(m1, sA, LA, sP, LA, m0, n0s);
+    __syncthreads();
+    if (threadIdx.x < Cn) {
+        const int rr = threadIdx.x;
+        a.db[(t0 + rr) * H + hh] = sDB[rr] + sDB[64 + rr] + sDB[128 + rr] + sDB[192 + rr];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) sP[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = (E)m1[i][0][e];
+    __syncthreads();
+    // ---- dA = −strictlower(M1 Aᵀ)   (B = Aᵀ: A stored [s][j] = [n][k])
+    {
+        f32x4 da[2][1];
+        zero_acc(da);
+        wgemm<E, 2, 1, 64, false, false>(da, sP, LA, sA, LA, m0, n0s);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                if (rr < Cn) a.dA[((t0 + rr) * H + hh) * 64 + cc] = (cc < rr) ? -da[i][0][e] : 0.f;
+            }
+    }
+}
+
+template <class E, int KD, int VD>
+static hipError_t kda_go(const Problem& p, const KdaArgs& a, hipStream_t s) {
+    using Cf = KdaCfg<E, KD, VD>;
+    auto kern = kda_kernel<E, KD, VD>;
+    static_assert(Cf::smem <= 160 * 1024, "LDS budget");
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(512), Cf::smem, s, a, p.cu, p.N, p.T, p.HV, p.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_kda(const Problem& p, const KdaArgs& a, hipStream_t s) {
+    if (p.K == 128 && p.V == 128) {
+        if (p.dtype == 1) return kda_go<f16, 128, 128>(p, a, s);
+        return hipErrorInvalidValue;
+    }
+    if (p.K == 64 && p.V == 64) {
+        if (p.dtype == 1) return kda_go<f16, 64, 64>(p, a, s);
+        return kda_go<float, 64, 64>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -149,7 +149,7 @@ def kda_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0):
     beta = _sigmoid(randn(ntok, H).astype(np.float64)).astype(np.float32)
     A = randn(ntok, H, BT)
     r = (np.arange(ntok) % T) % BT
-    A[np.arange(BT)[None, None, :] > r[:, None, None]] = 0.0
+    A *= (np.arange(BT)[None, None, :] <= r[:, None, None]).astype(np.float32)
     h = randn(B * NT, H, K, V)
     dO, dh, dv = randn(ntok, H, V), randn(B * NT, H, K, V), randn(ntok, H, V)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)  # noqa: E731

@@ -1,0 +1,160 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) gated-delta-rule backward library.
+ *
+ * Method (gated delta rule, state S_t is K x V per sequence and value head):
+ *     S_t = a_t (I - b_t k_t k_tᵀ) S_{t-1} + b_t k_t v_tᵀ ,  a_t = exp(ĝ_t)
+ *     o_t = scale * S_tᵀ q_t
+ * The backward returns the gradients of  L = Σ_t <dO_t, o_t> + <dht, S_T>.
+ *
+ * Page references (by title and section):
+ *  [P1] "FlashQLA 反向传播全解：fused_gdr_bwd 与 dh 梯度 Kernel 的设计取舍"
+ *       -- §一: entry point, the gate arrives as its in-chunk cumulative sum and
+ *       the gate gradient is reverse-cumsummed at the end, dh0 accumulated and
+ *       returned in fp32, dq/dk/dv stored in the 16-bit input type, dht optional
+ *       (absent == zero); step ② recomputes the per-chunk states h; §二: one
+ *       backward produces dq, dk, dv, dg, db, dh0 walking chunks last-to-first.
+ *  [P2] "chunk_kda_bwd_wy_dqkg_fused 算子" -- 函数签名 / 参数说明: argument list,
+ *       shapes and dtypes of the KDA WY backward stage; 实现原理: its intermediates.
+ *
+ * Conventions for every call:
+ *  - Tensors are caller-owned, contiguous, row-major DEVICE pointers unless a
+ *    parameter says "host".  The library keeps no pointer after a call returns
+ *    and never allocates device memory; scratch comes from a caller-provided
+ *    workspace whose size is given by gdr_workspace_size().
+ *  - The token axis is flattened over the batch: a [B,T,H,D] tensor is passed as
+ *    [B*T,H,D].  With varlen (cu_seqlens != NULL) B must be 1 and sequence n is
+ *    tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *  - Value head hv reads key head hv / (HV/HK) (grouped-query layout).
+ *  - Calls are asynchronous on the given stream (NULL = default stream); inputs
+ *    must stay valid and outputs untouched until the stream reaches the call.
+ *  - Return value: GDR_OK (0) or a negative gdr_status.  Validation happens on
+ *    the host before anything is launched; on error nothing is launched and no
+ *    output is written.  gdr_strerror() maps a status to a string.
+ *  - Reentrant: no global mutable state (a per-device attribute cache only).
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDR_F32 = 0, GDR_F16 = 1, GDR_BF16 = 2 } gdr_dtype;
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID = -1,     /* bad shape, dtype, null required pointer, bad cu_seqlens */
+    GDR_ERR_UNSUPPORTED = -2, /* valid but not built: K != V, K not in {64,128}, BT != 64 */
+    GDR_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than gdr_workspace_size() */
+    GDR_ERR_LAUNCH = -4       /* a HIP error was reported at launch */
+} gdr_status;
+
+typedef struct gdr_problem {
+    int B, T;      /* batch and tokens per sequence (dense); varlen: B = 1, T = total tokens */
+    int HK, HV;    /* key/query heads and value heads; HV % HK == 0 */
+    int K, V;      /* key and value head dims */
+    int BT;        /* chunk size */
+    int N;         /* number of sequences when varlen; ignored when cu_seqlens == NULL */
+    const int32_t *cu_seqlens;      /* device [N+1] or NULL (dense) */
+    const int32_t *cu_seqlens_host; /* host mirror of cu_seqlens [N+1]; required iff cu_seqlens != NULL.
+                                       It must hold the same values; it is read during the call only. */
+    float scale;   /* output scale; <= 0 selects 1/sqrt(K) */
+    gdr_dtype dtype; /* type of q, k, v, beta, dO and of dq, dk, dv */
+} gdr_problem;
+
+/* Human-readable text for a gdr_status (static storage). */
+const char *gdr_strerror(int status);
+
+/* Number of chunks NT = sum over sequences of ceil(len / BT); -1 if invalid. */
+int64_t gdr_num_chunks(const gdr_problem *p);
+
+/* Workspace bytes needed by gdr_fwd_states / gdr_chunk_bwd for this problem
+ * (0 if the problem is invalid).  The same workspace may be reused by later
+ * calls on the same stream. */
+size_t gdr_workspace_size(const gdr_problem *p);
+
+/*
+ * gdr_fwd_states -- recompute the per-chunk forward states ([P1] §一 step ②).
+ *   k [B*T,HK,K], v [B*T,HV,V], beta [B*T,HV]    dtype
+ *   g_cum [B*T,HV] fp32    in-chunk cumulative log-gate (restarts every BT tokens
+ *                          and at every sequence start)
+ *   h0 [N,HV,K,V] fp32     initial states, NULL = zero
+ * Outputs:
+ *   h_out  [NT,HV,K,V] fp32   state ENTERING each chunk (chunk-major over sequences)
+ *   v_new_out [B*T,HV,V] dtype or NULL   the chunk's corrected values U - W h
+ *   ht_out [N,HV,K,V] fp32 or NULL       final state of each sequence
+ * ws/ws_bytes: workspace (>= gdr_workspace_size(p)).
+ */
+int gdr_fwd_states(const gdr_problem *p, const void *k, const void *v, const float *g_cum, const void *beta,
+                   const float *h0, float *h_out, void *v_new_out, float *ht_out,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gdr_chunk_bwd -- the backward of the chunkwise gated delta rule ([P1] §一, §二).
+ * Inputs:
+ *   q, k [B*T,HK,K]  v, dO [B*T,HV,V]  beta [B*T,HV]   dtype
+ *   g_cum [B*T,HV] fp32     in-chunk cumulative log-gate, as for gdr_fwd_states
+ *   h0  [N,HV,K,V] fp32     initial states, NULL = zero
+ *   dht [N,HV,K,V] fp32     gradient of the final states, NULL = zero (identical
+ *                           to passing zeros)
+ * Outputs (all written in full):
+ *   dq, dk [B*T,HK,K] dtype   summed over the value heads of each key head
+ *   dv [B*T,HV,V] dtype
+ *   dg [B*T,HV] fp32          gradient w.r.t. the RAW per-token log-gate ĝ_t
+ *                             (already reverse-cumsummed inside each chunk)
+ *   dbeta [B*T,HV] fp32
+ *   dh0 [N,HV,K,V] fp32 or NULL (skip)
+ * ws/ws_bytes: workspace (>= gdr_workspace_size(p)).
+ * Precision: matrix products run on MFMA with fp32 accumulation; 16-bit inputs
+ * use 16-bit operands (the scans use fp16 operands, so 16-bit inputs must lie
+ * within the fp16 range), fp32 inputs use fp32 operands throughout.
+ */
+int gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                  const void *beta, const float *h0, const void *dO, const float *dht,
+                  void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gdr_chunk_bwd_events -- gdr_chunk_bwd for measurement tools.  Identical
+ * computation and arguments; `events` (NULL or 4 caller-created hipEvent_t)
+ * are recorded on `stream` before the first launch and after each of the three
+ * stages: [0] start, [1] after the chunk table and WY-factor kernel, [2] after
+ * the two chunk scans, [3] after the gradient kernel.  hipEventElapsedTime on
+ * consecutive pairs gives the per-stage GPU time of this call.
+ */
+int gdr_chunk_bwd_events(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                         const void *beta, const float *h0, const void *dO, const float *dht,
+                         void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                         void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *events);
+
+/*
+ * kda_chunk_bwd -- the KDA (per-channel gate) WY backward stage ([P2] 函数签名,
+ * 参数说明, 实现原理).  Requires HK == HV == H; dtype F16 or F32 (the page
+ * validates fp16/fp32 only).  Per chunk of C <= BT rows, with γ = exp(g):
+ * returns the gradients of
+ *   scale<dO,(Q⊙γ)h> + <dh,(K⊙γ_C/γ)ᵀV_new> + <dh,diag(γ_C)h> + <dv,A(β⊙V) - A(β⊙γ⊙K)h>
+ * with respect to q, k, v, beta, g and the strictly-lower L of A = (I+L)^{-1}.
+ * Inputs:
+ *   q, k [B*T,H,K]   v, v_new, dO, dv_in [B*T,H,V]   beta [B*T,H]   dtype
+ *   g [B*T,H,K] fp32 (per-channel in-chunk log-gate, used as given)
+ *   A [B*T,H,BT] dtype (row r of a chunk holds that chunk's lower-triangular
+ *                       matrix row; entries above the diagonal are ignored)
+ *   h, dh [NT,H,K,V] fp32 (state entering / gradient of state leaving each chunk)
+ * Outputs: dq, dk, dg [B*T,H,K] fp32; dv_out [B*T,H,V] dtype; db [B*T,H] fp32;
+ *   dA [B*T,H,BT] fp32 (strictly-lower part; zeros on and above the diagonal
+ *   and in columns beyond a partial chunk's length).
+ * No workspace.
+ */
+int kda_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v, const void *v_new,
+                  const float *g, const void *beta, const void *A, const float *h, const void *dO,
+                  const float *dh, const void *dv_in, float *dq, float *dk, void *dv_out, float *db,
+                  float *dg, float *dA, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H_ */
