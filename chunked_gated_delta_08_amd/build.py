@@ -21,7 +21,8 @@ ARCH = "gfx950"
 HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip"]
 HOST_SOURCES = ["gdr_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _run(cmd, verbose):

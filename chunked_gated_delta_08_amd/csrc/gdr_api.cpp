@@ -69,6 +69,7 @@ WsPlan plan_workspace(const Problem& p) {
     w.U = off; off = align256(off + units * 64 * p.V * es);
     w.R = off; off = align256(off + units * 64 * p.K * es);
     w.A = off; off = align256(off + units * 64 * 64 * es);
+    w.KT = off; off = align256(off + units * 64 * p.K * es);
     w.h = off; off = align256(off + units * (size_t)p.K * p.V * es);
     w.dh = off; off = align256(off + units * (size_t)p.K * p.V * es);
     w.total = off;
@@ -118,13 +119,14 @@ int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const flo
     if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
-                                            nullptr, stream));
+                                            nullptr, base + w.KT, stream));
         if (st != GDR_OK) return st;
     }
     gdr::ScanArgs a{};
     a.k = k; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
-    a.W = base + w.W; a.U = base + w.U; a.h0 = h0;
+    a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.h0 = h0;
     a.h32 = h_out; a.v_new = v_new_out; a.ht = ht_out;
+    a.cu = q.cu; a.T = q.T;
     a.do_fwd = true; a.do_rev = false;
     return launch_status(gdr::launch_scans(q, a, stream));
 }
@@ -149,15 +151,16 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, qp, k, v, g_cum, beta, info, base + w.W, base + w.U, base + w.R,
-                                            base + w.A, stream));
+                                            base + w.A, base + w.KT, stream));
         if (st != GDR_OK) return st;
     }
     if ((st = mark(1)) != GDR_OK) return st;
     gdr::ScanArgs a{};
     a.k = k; a.dO = dO; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
-    a.W = base + w.W; a.U = base + w.U; a.R = base + w.R;
+    a.W = base + w.W; a.U = base + w.U; a.R = base + w.R; a.KT = base + w.KT;
     a.h0 = h0; a.dht = dht;
     a.hT = base + w.h; a.dhT = base + w.dh; a.dh0 = dh0;
+    a.cu = q.cu; a.T = q.T;
     a.do_fwd = q.NT > 0; a.do_rev = true;
     if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
     if ((st = mark(2)) != GDR_OK) return st;

@@ -30,12 +30,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef WG_KUNROLL
-#define WG_KUNROLL 2
-#endif
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Workgroup barrier for LDS exchange only: waits for this wave's LDS traffic
+// and meets the other waves, without the release fence of __syncthreads()
+// (which makes every barrier wait for all outstanding global loads and
+// stores).  No kernel here exchanges data through global memory inside a
+// workgroup.  The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 template <class E> __device__ __forceinline__ E to_e(float x) { return (E)x; }
@@ -110,21 +115,30 @@ __device__ __forceinline__ i16x4 ld_trans4(const E* X, int ld, int mn0, int krow
 // --------------------------------------------------------------------------
 // Wave-level GEMM: acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD.
 // AT: A stored [k][m] (else [m][k]).  BT_: B stored [k][n] (else [n][k]).
+// The fragments of k-step s+1 are read from LDS before the MFMAs of k-step s
+// are issued (register double buffer), so LDS latency overlaps the MFMAs.
 template <class E, int TM, int TN, int KD, bool AT, bool BT_>
 __device__ __forceinline__ void wgemm(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0,
                                       int n0) {
     using M = Mma<E>;
-#pragma unroll WG_KUNROLL
-    for (int k0 = 0; k0 < KD; k0 += M::KS) {
-        typename M::frag a[TM], b[TN];
+    constexpr int NS = KD / M::KS;
+    typename M::frag a[2][TM], b[2][TN];
+    auto load = [&](int buf, int k0) {
 #pragma unroll
-        for (int i = 0; i < TM; i++) a[i] = AT ? ld_trans<E>(A, lda, m0 + 16 * i, k0) : ld_direct<E>(A, lda, m0 + 16 * i, k0);
+        for (int i = 0; i < TM; i++)
+            a[buf][i] = AT ? ld_trans<E>(A, lda, m0 + 16 * i, k0) : ld_direct<E>(A, lda, m0 + 16 * i, k0);
 #pragma unroll
-        for (int j = 0; j < TN; j++) b[j] = BT_ ? ld_trans<E>(B, ldb, n0 + 16 * j, k0) : ld_direct<E>(B, ldb, n0 + 16 * j, k0);
+        for (int j = 0; j < TN; j++)
+            b[buf][j] = BT_ ? ld_trans<E>(B, ldb, n0 + 16 * j, k0) : ld_direct<E>(B, ldb, n0 + 16 * j, k0);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        if (s + 1 < NS) load((s + 1) & 1, (s + 1) * M::KS);
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < TN; j++) acc[i][j] = M::run(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < TN; j++) acc[i][j] = M::run(a[s & 1][i], b[s & 1][j], acc[i][j]);
     }
 }
 

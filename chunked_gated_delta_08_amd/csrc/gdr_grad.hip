@@ -76,6 +76,25 @@ __device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, lon
     }
 }
 
+// Load 64 rows of a per-chunk state stored transposed ([V][K]) with keys in
+// the scan's lane order key' = (K/4)g + 4t + e (key = 16t + 4g + e): each
+// 16-byte vector holds runs of 4 consecutive real keys.
+template <class E, int KD, int LD>
+__device__ __forceinline__ void g_load_state_rows(E* s, const E* __restrict__ g) {
+    constexpr int EPV = 16 / sizeof(E);
+    constexpr int VPR = KD / EPV;
+    for (int idx = threadIdx.x; idx < 64 * VPR; idx += 512) {
+        const int r = idx / VPR, c = idx % VPR;
+        const typename Vec16<E>::t v = *(const typename Vec16<E>::t*)(g + (long)r * KD + c * EPV);
+#pragma unroll
+        for (int e = 0; e < EPV; e++) {
+            const int kp = c * EPV + e;                       // key' = (K/4)g + 4t + q
+            const int gg = kp / (KD / 4), t = (kp % (KD / 4)) >> 2, q = kp & 3;
+            s[r * LD + 16 * t + 4 * gg + q] = v[e];
+        }
+    }
+}
+
 // sum over the 16 lanes that share a row group (lane bits 0..3)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1, 64);
@@ -154,7 +173,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
             sGam[r] = __expf(gg);
             sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         const float gl = sG[C - 1], gC = sGam[C - 1];
 
         // per-lane partial row sums (rows m0 + 16i + 4g4 + e) and column sums
@@ -182,7 +201,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         }
         // ---- A = (I+L)^{-1} from the prep kernel
         g_load_rows<E, E, 64, LA>(sA, (const E*)a.A + unit * C * C, C, C);
-        __syncthreads();
+        lds_barrier();
 
         // persistent accumulators over the V slices
         f32x4 dPm[2][1], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][1];
@@ -195,11 +214,11 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
             // h / dh slices are stored transposed: [V][K] per chunk -> rows v
-            g_load_rows<E, E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD, KD, 64);
-            g_load_rows<E, E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD, KD, 64);
+            g_load_state_rows<E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD);
+            g_load_state_rows<E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD);
             g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
             g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
-            __syncthreads();
+            lds_barrier();
             // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
             {
                 f32x4 kh[2][1], kdh[2][1], pdo[2][1];
@@ -224,19 +243,19 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                 const int rr = idx / KD, cc = idx % KD;
                 hdh += (float)sH[rr * LK + cc] * (float)sdH[rr * LK + cc];
             }
-            __syncthreads();
+            lds_barrier();
             // ---- V_new = A Z
             {
                 f32x4 vn[2][1];
                 zero_acc(vn);
                 wgemm<E, 2, 1, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
-                __syncthreads();
+                lds_barrier();
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) sVn[acc_row(m0, i, e) * LS + acc_col(n0s, 0)] = to_e<E>(vn[i][0][e]);
             }
-            __syncthreads();
+            lds_barrier();
             // ---- accumulate the state products and the V-separable outputs
             wgemm<E, 2, 1, 64, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);     // dO V_newᵀ
             wgemm<E, 2, TNK, 64, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);    // dO hᵀ
@@ -256,7 +275,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                         if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
                     }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- Q back into its buffer (it held the V slices)
@@ -280,7 +299,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
             for (int j = 0; j < TNK; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) sdW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = to_e<E>(-dWa[i][j][e]);
-        __syncthreads();
+        lds_barrier();
         E* sT1 = sPm;
 
         // ---- dq = scale γ dO hᵀ + T1 K ;  dG += rowsum(Q ⊙ scale γ dO hᵀ)
@@ -340,7 +359,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                     sdA[rr * LA + cc] = to_e<E>(sB[cc] * (dAp[i][0][e] + sGam[cc] * dwk[i][0][e]));
                 }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- M1 = Aᵀ dA_pre
         {
             f32x4 m1[2][1];
@@ -351,7 +370,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
                 for (int e = 0; e < 4; e++) sM1[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = to_e<E>(m1[i][0][e]);
         }
-        __syncthreads();
+        lds_barrier();
         // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ
         {
             f32x4 dl[2][1], akk[2][1];
@@ -374,7 +393,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                     sEb[rr * LA + cc] = to_e<E>(lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f);
                 }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- dk += Eb K + Ebᵀ K
         {
             f32x4 acc[2][TNK];
@@ -414,7 +433,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
             }
             if (l == 0) { sMisc[w] = hz; sMisc[8 + w] = zz; }
         }
-        __syncthreads();
+        lds_barrier();
         if (threadIdx.x < 64) {
             const int rr = threadIdx.x;
             float dG = (sRowG[rr] + sRowG[64 + rr] + sRowG[128 + rr] + sRowG[192 + rr]) - (sCol[rr] + sCol[64 + rr]);
@@ -427,7 +446,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
             sMisc[16 + rr] = dG;
             if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
         }
-        __syncthreads();
+        lds_barrier();
         if (threadIdx.x == 0) {   // in-chunk reverse cumulative sum
             float acc = 0.f;
             for (int rr = C - 1; rr >= 0; rr--) {
@@ -435,7 +454,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                 if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     // ---- write the group sums dq, dk for this key head
 #pragma unroll

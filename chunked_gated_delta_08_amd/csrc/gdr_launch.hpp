@@ -25,16 +25,17 @@ struct Problem {
 
 // Workspace carve-up (byte offsets from the workspace base).
 struct WsPlan {
-    size_t chunk_info, seq_chunk0, W, U, R, A, h, dh, total;
+    size_t chunk_info, seq_chunk0, W, U, R, A, KT, h, dh, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
 hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, hipStream_t s);
 
-// K1a: per-chunk WY factors.  W, U (and R when q != NULL) in the scan operand
-// type; A = (I+L)^{-1} in the input type when A != NULL.
+// K1a: per-chunk WY factors.  W, U, K̃ (and R when q != NULL) in the scan
+// operand type; A = (I+L)^{-1} in the input type when A != NULL.
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const void* v, const float* gcum,
-                       const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, hipStream_t s);
+                       const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, void* KT,
+                       hipStream_t s);
 
 // K1b + K2: the forward state scan and the reverse dh scan (one launch, two roles).
 //   fwd role: writes h (state entering each chunk; transposed [NT,HV,V,K] in the
@@ -43,10 +44,11 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const voi
 //   rev role (when R != NULL): writes dh (transposed, input type) and dh0.
 struct ScanArgs {
     const void* k; const void* dO; const float* gcum; const ChunkInfo* info; const int32_t* seq_chunk0;
-    const void* W; const void* U; const void* R;
+    const void* W; const void* U; const void* R; const void* KT;
     const float* h0; const float* dht;
     void* hT; float* h32; void* v_new; float* ht;
     void* dhT; float* dh0;
+    const int32_t* cu; int T;   // sequence bounds: cu_seqlens (device) or dense length T
     bool do_fwd, do_rev;
 };
 hipError_t launch_scans(const Problem& p, const ScanArgs& a, hipStream_t s);

@@ -6,7 +6,8 @@
 //   W  = A diag(βγ) K,    U = A diag(β) V
 //   Pm = scale · lower( Γ ⊙ Q Kᵀ )   (diagonal included)
 //   R  = scale · diag(γ) Q − Pm W
-// A itself is also written out (input type) for the gradient kernel.
+// A itself is also written out (input type) for the gradient kernel, and
+// K̃ = diag(γ_C/γ) K (scan operand type) for both scans.
 // W and U drive the forward state scan (V_new = U − W h); R and W drive the
 // reverse scan in the form dh ← γ_C dh + Rᵀ dO − Wᵀ (K̃ dh) given on the
 // FlashQLA backward explainer page (§三, the dh kernel's three consumer groups:
@@ -103,7 +104,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                                                    const E* __restrict__ v, const float* __restrict__ gcum,
                                                    const E* __restrict__ beta, const ChunkInfo* __restrict__ info,
                                                    int HK, int HV, float scale, S* __restrict__ Wg,
-                                                   S* __restrict__ Ug, S* __restrict__ Rg, E* __restrict__ Ag) {
+                                                   S* __restrict__ Ug, S* __restrict__ Rg, E* __restrict__ Ag,
+                                                   S* __restrict__ KTg) {
     static_assert(sizeof(E) == sizeof(S), "input and scan types share a width");
     constexpr int C = 64, NTHR = 256;
     constexpr int LK = KD + pad_of<E>(), LV = VD + pad_of<E>(), LA = 64 + pad_of<E>(), LL = 68;
@@ -133,7 +135,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
         sG[r] = gcum[(t0 + min(r, Cn - 1)) * HV + hv];
         sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32x32 block)
     {
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                     if (WITH_R) sPm[r * LA + c] = to_e<S>((c <= r) ? scale * gm * aqk[i][j][e] : 0.f);
                 }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- A = (I+L)^{-1} (wave 0, lane j owns column j); other waves scale K, V
     if (w == 0) {
@@ -178,11 +180,13 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
             for (int r = 0; r < C; r++) Ao[r * C + l] = to_e<E>(a[r]);
         }
     } else {
-        // Kb = diag(βγ) K, Vb = diag(β) V, written in place as type S
+        // Kb = diag(βγ) K written in place as type S; K̃ = diag(γ_C/γ) K to memory
+        S* KTo = KTg + ((long)ci * HV + hv) * C * KD;
         for (int idx = threadIdx.x - 64; idx < C * KD; idx += NTHR - 64) {
             const int r = idx / KD, c = idx % KD;
             const float f = sB[r] * __expf(sG[r]);
             const float x = (float)sK[r * LK + c];
+            KTo[r * KD + c] = to_e<S>(__expf(sG[C - 1] - sG[r]) * x);
             ((S*)sK)[r * LK + c] = to_e<S>(f * x);
         }
         for (int idx = threadIdx.x - 64; idx < C * VD; idx += NTHR - 64) {
@@ -191,7 +195,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
             ((S*)sV)[r * LV + c] = to_e<S>(sB[r] * x);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- W = A Kb, U = A Vb      (wave w: all 64 rows, KD/4 resp. VD/4 columns)
     constexpr int TNK = KD / 64, TNV = VD / 64;
@@ -200,7 +204,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     zero_acc(au);
     wgemm<S, 4, TNK, 64, false, true>(aw, sA, LA, (const S*)sK, LK, 0, w * (KD / 4));
     wgemm<S, 4, TNV, 64, false, true>(au, sA, LA, (const S*)sV, LV, 0, w * (VD / 4));
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -211,7 +215,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
 #pragma unroll
             for (int j = 0; j < TNV; j++) ((S*)sV)[r * LV + acc_col(w * (VD / 4), j)] = to_e<S>(au[i][j][e]);
         }
-    __syncthreads();
+    lds_barrier();
 
     const long unit = (long)ci * HV + hv;
     if (WITH_R) {
@@ -221,7 +225,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
         wgemm<S, 4, TNK, 64, false, true>(ar, sPm, LA, sW, LK, 0, w * (KD / 4));
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
         store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, (const S*)sV);
-        __syncthreads();
+        lds_barrier();
         S* sR = (S*)sK;
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -235,7 +239,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                     sR[r * LK + c] = to_e<S>(scale * gr * (float)sQ[r * LK + c] - ar[i][j][e]);
                 }
             }
-        __syncthreads();
+        lds_barrier();
         store_tile_dense<S, KD, LK, NTHR>(Rg + unit * C * KD, sR);
     } else {
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
@@ -253,7 +257,8 @@ static size_t prep_smem() {
 
 template <class E, class S, int KD, int VD>
 static hipError_t prep_go(const Problem& p, const void* q, const void* k, const void* v, const float* gcum,
-                          const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, hipStream_t s) {
+                          const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, void* KT,
+                          hipStream_t s) {
     const size_t sm = prep_smem<E, S, KD, VD>();
     dim3 grid((unsigned)p.NT, p.HV);
     if (q) {
@@ -261,29 +266,30 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A);
+                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A, (S*)KT);
     } else {
         auto kern = prep_kernel<E, S, KD, VD, false>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A);
+                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A, (S*)KT);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const void* v, const float* gcum,
-                       const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, hipStream_t s) {
+                       const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, void* KT,
+                       hipStream_t s) {
     // dtype: 0 f32, 1 f16, 2 bf16; the scans use fp16 operands for 16-bit inputs
     if (p.K == 128 && p.V == 128) {
-        if (p.dtype == 2) return prep_go<bf16, f16, 128, 128>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
-        if (p.dtype == 1) return prep_go<f16, f16, 128, 128>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
-        return prep_go<float, float, 128, 128>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
+        if (p.dtype == 2) return prep_go<bf16, f16, 128, 128>(p, q, k, v, gcum, beta, info, W, U, R, A, KT, s);
+        if (p.dtype == 1) return prep_go<f16, f16, 128, 128>(p, q, k, v, gcum, beta, info, W, U, R, A, KT, s);
+        return hipErrorInvalidValue;   // fp32 is built at K = V = 64 only
     }
     if (p.K == 64 && p.V == 64) {
-        if (p.dtype == 2) return prep_go<bf16, f16, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
-        if (p.dtype == 1) return prep_go<f16, f16, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
-        return prep_go<float, float, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, s);
+        if (p.dtype == 2) return prep_go<bf16, f16, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, KT, s);
+        if (p.dtype == 1) return prep_go<f16, f16, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, KT, s);
+        return prep_go<float, float, 64, 64>(p, q, k, v, gcum, beta, info, W, U, R, A, KT, s);
     }
     return hipErrorInvalidValue;
 }

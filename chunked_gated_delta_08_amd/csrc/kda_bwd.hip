@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
         s += __shfl_xor(s, 2, 64);
         if (part == 0 && key < KD) sHD[key] = s;
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = threadIdx.x; idx < C * KD; idx += 512) {
         const int r = idx / KD, c = idx % KD;
         float x = 0.f;
@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     zero_acc(dwa);
     wgemm<E, 2, TN, VD, false, false>(dqa, sX, LV, sH, LV, m0, n0k);
     wgemm<E, 2, TN, VD, false, false>(dwa, sDV, LV, sH, LV, m0, n0k);
-    __syncthreads();
+    lds_barrier();
     // ---- swap in dh and V_new; dw -> LDS
     kda_load<float, E, VD, LV>(sH, dhg, VD, KD, KD);
     kda_load<E, E, VD, LV>(sX, vn + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
         for (int j = 0; j < TN; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) sDW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = (E)(-dwa[i][j][e]);
-    __syncthreads();
+    lds_barrier();
     // ---- dks_acc = V_new dhᵀ ; AdW = Aᵀ dw ; AdV = Aᵀ dv (V-tiles)
     f32x4 dka[2][TN], adw[2][TN];
     zero_acc(dka);
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
         x += __shfl_xor(x, 32, 64);
         if (g4 == 0) sCS[(w & 1) * KD + acc_col(n0k, j)] = x;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     }
     // db: reduce over the 16 lanes of each row group, then over the 4 column blocks
     float* sDB = sCS;   // reuse [4][64] (column sums already consumed above)
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     f32x4 m1[2][1];
     zero_acc(m1);
     wgemm<E, 2, 1, 64, true, true>(m1, sA, LA, sP, LA, m0, n0s);
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < Cn) {
         const int rr = threadIdx.x;
         a.db[(t0 + rr) * H + hh] = sDB[rr] + sDB[64 + rr] + sDB[128 + rr] + sDB[192 + rr];
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int e = 0; e < 4; e++) sP[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = (E)m1[i][0][e];
-    __syncthreads();
+    lds_barrier();
     // ---- dA = −strictlower(M1 Aᵀ)   (B = Aᵀ: A stored [s][j] = [n][k])
     {
         f32x4 da[2][1];
