@@ -76,25 +76,6 @@ __device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, lon
     }
 }
 
-// Load 64 rows of a per-chunk state stored transposed ([V][K]) with keys in
-// the scan's lane order key' = (K/4)g + 4t + e (key = 16t + 4g + e): each
-// 16-byte vector holds runs of 4 consecutive real keys.
-template <class E, int KD, int LD>
-__device__ __forceinline__ void g_load_state_rows(E* s, const E* __restrict__ g) {
-    constexpr int EPV = 16 / sizeof(E);
-    constexpr int VPR = KD / EPV;
-    for (int idx = threadIdx.x; idx < 64 * VPR; idx += 512) {
-        const int r = idx / VPR, c = idx % VPR;
-        const typename Vec16<E>::t v = *(const typename Vec16<E>::t*)(g + (long)r * KD + c * EPV);
-#pragma unroll
-        for (int e = 0; e < EPV; e++) {
-            const int kp = c * EPV + e;                       // key' = (K/4)g + 4t + q
-            const int gg = kp / (KD / 4), t = (kp % (KD / 4)) >> 2, q = kp & 3;
-            s[r * LD + 16 * t + 4 * gg + q] = v[e];
-        }
-    }
-}
-
 // sum over the 16 lanes that share a row group (lane bits 0..3)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1, 64);
@@ -214,8 +195,8 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
             // h / dh slices are stored transposed: [V][K] per chunk -> rows v
-            g_load_state_rows<E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD);
-            g_load_state_rows<E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD);
+            g_load_rows<E, E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD, KD, 64);
+            g_load_rows<E, E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD, KD, 64);
             g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
             g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
             lds_barrier();

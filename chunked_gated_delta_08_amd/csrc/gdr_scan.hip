@@ -1,7 +1,6 @@
 // gdr_scan.hip -- the two sequential chunk scans (K1b forward states, K2 dh).
 //
-// The per-chunk states go to the workspace transposed ([V][K] per chunk) with
-// keys in lane order (see store_state); the gradient kernel undoes that order.
+// The per-chunk states go to the workspace transposed ([V][K] per chunk).
 //
 // Forward (state entering chunk c is h[c]; FlashQLA backward explainer §一
 // step ②, "recompute h"):
@@ -121,30 +120,28 @@ __device__ __forceinline__ void transT_times_rows(f32x4 (&St)[KD / 16], const S*
     }
 }
 
-// Store a wave's K x 16 state slice: transposed [V][K] in type E for the
-// gradient kernel, with the keys of each row in the lane order
-// key' = (K/4)g + 4t + e  <->  key = 16t + 4g + e  (so every lane writes its
-// K/4 values as contiguous 16-byte vectors), and/or row-major [K][V] fp32.
-// All values are packed before the first store so that each store owns its
-// data registers (a store whose data registers are reused stalls until the
-// memory pipeline has read them).
-template <class E, int KD, int VD>
+// Store a wave's K x 16 state slice: transposed [V][K] in type E (for the
+// gradient kernel) and/or row-major [K][V] fp32.  All values are packed
+// before the first store so that each store owns its data registers (a store
+// whose data registers are reused right away stalls until the memory
+// pipeline has read them).
+template <class E, int KD, int VD, bool EST>
 __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long unit, int col, E* hT, float* h32) {
     const int g = lane_id() >> 4;
-    if (hT) {
-        E* p = hT + (unit * VD + col) * KD + (KD / 4) * g;
+    if constexpr (EST) {
+        E* p = hT + (unit * VD + col) * KD + 4 * g;
         if constexpr (sizeof(E) == 2) {
-            typedef E e8 __attribute__((ext_vector_type(8)));
-            e8 v[KD / 32];
+            typedef E e4 __attribute__((ext_vector_type(4)));
+            e4 v[KD / 16];
 #pragma unroll
-            for (int j = 0; j < KD / 32; j++)
+            for (int t = 0; t < KD / 16; t++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) { v[j][e] = (E)St[2 * j][e]; v[j][4 + e] = (E)St[2 * j + 1][e]; }
+                for (int e = 0; e < 4; e++) v[t][e] = (E)St[t][e];
 #pragma unroll
-            for (int j = 0; j < KD / 32; j++) *(e8*)(p + 8 * j) = v[j];
+            for (int t = 0; t < KD / 16; t++) *(e4*)(p + 16 * t) = v[t];
         } else {
 #pragma unroll
-            for (int t = 0; t < KD / 16; t++) *(f32x4*)(p + 4 * t) = St[t];
+            for (int t = 0; t < KD / 16; t++) *(f32x4*)(p + 16 * t) = St[t];
         }
     }
     if (h32) {
@@ -155,7 +152,7 @@ __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long uni
     }
 }
 
-template <class E, class S, int KD, int VD, bool rev>
+template <class E, class S, int KD, int VD, bool rev, bool EST>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int HV, unsigned char* smem) {
     using Cf = ScanCfg<E, S, KD, VD>;
     using St_t = Stage<E, S, KD, VD, rev>;
@@ -313,7 +310,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
                     At[t][sidx] = __builtin_bit_cast(frag, c);
                 }
             // state store (before the update) and B fragments of the state
-            store_state<E, KD, VD>(St, unit, col, rev ? (E*)a.dhT : (E*)a.hT, rev ? nullptr : a.h32);
+            store_state<E, KD, VD, EST>(St, unit, col, rev ? (E*)a.dhT : (E*)a.hT, rev ? nullptr : a.h32);
             const float sg = rev ? 1.f : -1.f;   // fwd: X = U − W h ; rev: X = K̃ dh
             frag Bs[KD / 32];
 #pragma unroll
@@ -365,7 +362,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
         } else {
             // fp32 operands (16x16x4 MFMA): small sizes only, plain order
             if constexpr (!rev) {
-                store_state<E, KD, VD>(St, unit, col, (E*)a.hT, a.h32);
+                store_state<E, KD, VD, EST>(St, unit, col, (E*)a.hT, a.h32);
 #pragma unroll
                 for (int m = 0; m < 4; m++)
 #pragma unroll
@@ -386,7 +383,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
                 for (int t = 0; t < KT; t++) St[t] *= gC;
                 transT_times_rows<S, KD, LK>(St, sK, X, 1.f);
             } else {
-                store_state<E, KD, VD>(St, unit, col, (E*)a.dhT, nullptr);
+                store_state<E, KD, VD, EST>(St, unit, col, (E*)a.dhT, nullptr);
 #pragma unroll
                 for (int m = 0; m < 4; m++) X[m] = zero4();
                 rows_times_state<S, KD, LK>(X, sK, St, 1.f);
@@ -421,9 +418,13 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
         commit(s0, slot[0]);
         glv0 = s0.gl;
         lds_barrier();
-        for (int i = 0; i < nc; i += 2) {
-            step(i, s0, s1, glv0, glv1, slot[0], slot[1]);
-            if (i + 1 < nc) step(i + 1, s1, s0, glv1, glv0, slot[1], slot[0]);
+        // The first chunk is peeled so that the loop is entered with the same
+        // outstanding loads/stores as on its back edge (the compiler's wait
+        // counts at the commits then allow two chunks of loads in flight).
+        step(0, s0, s1, glv0, glv1, slot[0], slot[1]);
+        for (int i = 1; i < nc; i += 2) {
+            step(i, s1, s0, glv1, glv0, slot[1], slot[0]);
+            if (i + 1 < nc) step(i + 1, s0, s1, glv0, glv1, slot[0], slot[1]);
         }
     }
 
@@ -437,12 +438,15 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
     }
 }
 
-template <class E, class S, int KD, int VD>
+// EST: the transposed states (hT for the forward scan, dhT for the reverse
+// one) are stored in type E.  It is a template parameter so the store is not
+// behind a runtime branch: the compiler's wait counts are then exact.
+template <class E, class S, int KD, int VD, bool EST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 scan_kernel(ScanArgs a, int nfwd, int HK, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    if ((int)blockIdx.x >= nfwd) scan_body<E, S, KD, VD, true>(a, (int)blockIdx.x - nfwd, HK, HV, smem);
-    else scan_body<E, S, KD, VD, false>(a, (int)blockIdx.x, HK, HV, smem);
+    if ((int)blockIdx.x >= nfwd) scan_body<E, S, KD, VD, true, EST>(a, (int)blockIdx.x - nfwd, HK, HV, smem);
+    else scan_body<E, S, KD, VD, false, EST>(a, (int)blockIdx.x, HK, HV, smem);
 }
 
 template <class E, class S, int KD, int VD>
@@ -452,7 +456,11 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
     const int per = nseq * p.HV * (VD / 64);
     const int nfwd = a.do_fwd ? per : 0, nrev = a.do_rev ? per : 0;
     if (nfwd + nrev == 0) return hipSuccess;
-    auto kern = scan_kernel<E, S, KD, VD>;
+    // either every launched scan stores its E-typed states or none does
+    const bool est_f = !a.do_fwd || a.hT, est_r = !a.do_rev || a.dhT;
+    const bool none_f = !a.do_fwd || !a.hT, none_r = !a.do_rev || !a.dhT;
+    if (!(est_f && est_r) && !(none_f && none_r)) return hipErrorInvalidValue;
+    auto kern = (est_f && est_r) ? scan_kernel<E, S, KD, VD, true> : scan_kernel<E, S, KD, VD, false>;
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
         return hipErrorInvalidConfiguration;
