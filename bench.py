@@ -18,7 +18,6 @@ C=64, K=V=128).
 """
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -31,11 +30,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 WORKLOADS = {
-    "c2": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None,
+    "dense_t32k_h16": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None,
                name="gdn_bwd_T32768_hk16_hv16_K128_V128_BT64_bf16"),
-    "c3": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None,
+    "dense_t32k_h32": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None,
                name="gdn_bwd_T32768_hk32_hv32_K128_V128_BT64_bf16"),
-    "c5": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12",
+    "varlen12_hk16_hv32": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12",
                name="gdn_bwd_varlen12_65536tok_hk16_hv32_K128_V128_BT64_bf16"),
 }
 
@@ -60,9 +59,11 @@ def kernel_bytes(cfg, chunks, es=2):
     st = 64 * K * es              # one [64, K] workspace tile
     state = K * V * es            # one K x V state in the workspace
     gb = ntok * HV * (4 + es)     # gate (fp32) and beta
-    prep = HK * (2 * tok_k) + HV * tok_v + gb + nunits * (3 * st + 64 * 64 * es)
-    scans = nunits * (3 * st) + HK * tok_k + nunits * state + \
-        nunits * (3 * st) + HK * tok_k + HV * tok_v + nunits * state
+    # prep: q, k, v, gate, beta in; W, U, R, K~ tiles and A out
+    prep = HK * (2 * tok_k) + HV * tok_v + gb + nunits * (4 * st + 64 * 64 * es)
+    # forward scan: W, K~, U in, h states out; reverse scan: W, K~, R, dO in, dh states out
+    scans = nunits * (3 * st) + nunits * state + nunits * (3 * st) + HV * tok_v + nunits * state
+    # grad: q, k, v, dO, h and dh states, A, gate, beta in; dq, dk, dv, dg, dbeta out
     grad = HK * 2 * tok_k + HV * 2 * tok_v + nunits * (2 * state + 64 * 64 * es) + gb + \
         HK * 2 * tok_k + HV * tok_v + ntok * HV * 8
     return {"prep": prep, "scans": scans, "grad": grad}
@@ -80,14 +81,6 @@ def elapsed_ms(hip, a, b):
     ms = ctypes.c_float()
     assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
     return ms.value
-
-
-def source_digest(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def cpu_baseline(inp, cfg, seconds_hint=20.0):
@@ -116,7 +109,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -125,7 +118,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from chunked_gated_delta_08_amd import binding, workloads
+    from chunked_gated_delta_08_amd import binding, profiling, workloads
 
     cfg = dict(WORKLOADS[args.workload])
     lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
@@ -178,12 +171,12 @@ def main():
     dom = max(stage, key=stage.get)
     achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
     kernel_name = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}[dom]
-    traffic = None
+    traffic = None   # HBM bytes per launch from the committed counter summary, while the sources match it
     tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{args.workload}.json")
     if os.path.exists(tfile):
         with open(tfile) as fh:
             t = json.load(fh)
-        if t.get("source_digest") == source_digest(t.get("sources", [])):
+        if t.get("source_digest") == profiling.source_digest(profiling.KERNEL_SOURCES[kernel_name]):
             traffic = t.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel_name,

@@ -157,9 +157,9 @@ def test_fwd_states(B, oracle):
 
 # ------------------------------------------------------------------ full sizes
 FULL = {
-    "c2_hk16_hv16_T32k": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None, heads=[0, 9]),
-    "c3_hk32_hv32_T32k": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None, heads=[5]),
-    "c5_varlen_gqa": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="c5", heads=[6, 7]),
+    "dense_T32k_hk16_hv16": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None, heads=[0, 9]),
+    "dense_T32k_hk32_hv32": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None, heads=[5]),
+    "varlen12_64k_hk16_hv32": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12", heads=[6, 7]),
 }
 
 
@@ -168,7 +168,7 @@ FULL = {
 def test_full_size_sampled_heads(B, oracle, name):
     cfg = dict(FULL[name])
     heads = cfg.pop("heads")
-    if cfg["lengths"] == "c5":
+    if cfg["lengths"] == "varlen12":
         cfg["lengths"] = W.varlen_lengths()
     _log(f"[parity] {name}: {cfg} sampled value heads {heads}")
     inp = W.gdr_inputs(cfg["B"], cfg["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], dtype="bf16", seed=0,
@@ -212,7 +212,7 @@ def test_kda_small(B, oracle):
 
 
 @pytest.mark.slow
-def test_kda_c4_sampled(B, oracle):
-    _log("[parity] kda C4 B=1 T=2048 H=32 K=V=128 fp16, sampled heads")
+def test_kda_T2048_h32_sampled(B, oracle):
+    _log("[parity] kda B=1 T=2048 H=32 K=V=128 fp16, sampled heads")
     inp = W.kda_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0)
-    _kda_compare(B, oracle, inp, heads=[0, 13, 31], label="kda_c4")
+    _kda_compare(B, oracle, inp, heads=[0, 13, 31], label="kda_T2048_h32")
