@@ -33,7 +33,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("HK", ctypes.c_int), ("HV", ctypes.c_int),
                 ("K", ctypes.c_int), ("V", ctypes.c_int), ("BT", ctypes.c_int), ("N", ctypes.c_int),
                 ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("seg_chunks", ctypes.c_int)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -74,10 +74,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def make_problem(B, T, HK, HV, K, V, dtype, BT=64, cu_seqlens=None, scale=None):
+def make_problem(B, T, HK, HV, K, V, dtype, BT=64, cu_seqlens=None, scale=None, seg_chunks=0):
     """Builds the gdr_problem struct.  cu_seqlens: int32 CUDA tensor [N+1] or None.
+    seg_chunks: chunks per scan segment (0 = automatic, < 0 = no segments).
     Returns (problem, keepalive) -- keep `keepalive` referenced while the struct is used."""
-    p = Problem(B, T, HK, HV, K, V, BT, 0, None, None, float(scale or 0.0), _DT[dtype])
+    p = Problem(B, T, HK, HV, K, V, BT, 0, None, None, float(scale or 0.0), _DT[dtype], int(seg_chunks))
     keep = []
     if cu_seqlens is not None:
         assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
@@ -107,13 +108,13 @@ def _dims(q_or_k, v, cu_seqlens, B):
 
 
 def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, scale=None, BT=64,
-                  want_dh0=True, out=None, workspace=None, stream=None):
+                  want_dh0=True, out=None, workspace=None, stream=None, seg_chunks=0):
     """Backward of the chunkwise gated delta rule.  Returns dict dq, dk, dv, dg, dbeta, dh0."""
     B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
     for t in (q, k, v, g_cum, beta, dO):
         assert t.is_cuda and t.is_contiguous()
     assert g_cum.dtype == torch.float32
-    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale)
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale, seg_chunks)
     N = B if cu_seqlens is None else p.N
     dev = v.device
     if out is None:
@@ -132,10 +133,10 @@ def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, 
 
 
 def gdr_fwd_states(k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, BT=64, want_v_new=True, want_ht=True,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, seg_chunks=0):
     """Per-chunk forward states h [NT, HV, K, V] fp32 (state entering each chunk), v_new, ht."""
     B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
-    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, None)
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, None, seg_chunks)
     N = B if cu_seqlens is None else p.N
     dev = v.device
     NT = num_chunks(p)

@@ -9,9 +9,58 @@
 namespace {
 
 using gdr::Problem;
+using gdr::SegInfo;
 using gdr::WsPlan;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Segments for the sequential state scans.  A sequence of n chunks is cut into
+// ceil(n / L) segments (at least one).  Without segments the scans take one
+// workgroup per (sequence, value head, direction) and as many sequential
+// steps as the longest sequence has chunks; with segments there are three
+// launches (local scans and transfer matrices: about 3 jobs per segment and
+// value head; the sequential combine: one step per segment; the scans proper:
+// 2 jobs per segment and value head).  L is chosen to minimise the estimated
+// number of sequential chunk steps with one workgroup per CU on 256 CUs.
+void plan_segments(const gdr_problem* p, Problem* q) {
+    const int nseq = q->N;
+    auto nch = [&](int n) -> int64_t {
+        const int64_t len = p->cu_seqlens ? (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] : p->T;
+        return (len + p->BT - 1) / p->BT;
+    };
+    int64_t maxn = 0;
+    for (int n = 0; n < nseq; n++) maxn = nch(n) > maxn ? nch(n) : maxn;
+    auto rounds = [](int64_t jobs) { return (double)((jobs + 255) / 256); };
+    struct Plan { int L; int64_t NS; int maxS; double cost; };
+    auto eval = [&](int64_t L) {
+        Plan pl{(int)L, 0, 1, 0.0};
+        int64_t multi = 0;
+        for (int n = 0; n < nseq; n++) {
+            const int64_t c = nch(n), S = c > L ? (c + L - 1) / L : 1;
+            pl.NS += S;
+            if (S > 1) multi += 3 * S - 2;
+            if (S > pl.maxS) pl.maxS = (int)S;
+        }
+        const double Ls = (double)(L < maxn ? L : maxn);
+        pl.cost = rounds(2 * q->HV * pl.NS) * Ls;
+        if (pl.maxS > 1) pl.cost += rounds(q->HV * multi) * Ls + pl.maxS + 3.0;
+        return pl;
+    };
+    Plan best = eval(maxn > 0 ? maxn : 1);   // no segments
+    if (q->dtype != GDR_F32 && p->seg_chunks >= 0 && maxn > 1) {
+        if (p->seg_chunks > 0) {
+            best = eval(p->seg_chunks);
+        } else {
+            for (int64_t L = 8; L < maxn; L *= 2) {
+                const Plan c = eval(L);
+                if (c.cost < best.cost) best = c;
+            }
+        }
+    }
+    q->L = best.L;
+    q->NS = (int)best.NS;
+    q->maxS = best.maxS;
+}
 size_t elem_size(int dtype) { return dtype == GDR_F32 ? 4 : 2; }
 
 // Host-side checks shared by every entry point.  Fills `q` on success.
@@ -42,6 +91,7 @@ int check_problem(const gdr_problem* p, Problem* q) {
     q->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
     q->dtype = p->dtype;
     q->cu = p->cu_seqlens;
+    plan_segments(p, q);
     return GDR_OK;
 }
 
@@ -54,6 +104,11 @@ int check_supported(const Problem& q) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH; }
 
+void set_seg_buffers(gdr::ScanArgs& a, char* base, const WsPlan& w) {
+    a.hloc = (float*)(base + w.hloc); a.dhloc = (float*)(base + w.dhloc); a.P = (float*)(base + w.P);
+    a.hstart = (float*)(base + w.hstart); a.dhin = (float*)(base + w.dhin);
+}
+
 }  // namespace
 
 namespace gdr {
@@ -65,6 +120,8 @@ WsPlan plan_workspace(const Problem& p) {
     size_t off = 0;
     w.chunk_info = off; off = align256(off + (size_t)(p.NT > 0 ? p.NT : 1) * sizeof(ChunkInfo));
     w.seq_chunk0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
+    w.seg_info = off; off = align256(off + (size_t)p.NS * sizeof(SegInfo));
+    w.seq_seg0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
     w.W = off; off = align256(off + units * 64 * p.K * es);
     w.U = off; off = align256(off + units * 64 * p.V * es);
     w.R = off; off = align256(off + units * 64 * p.K * es);
@@ -72,6 +129,12 @@ WsPlan plan_workspace(const Problem& p) {
     w.KT = off; off = align256(off + units * 64 * p.K * es);
     w.h = off; off = align256(off + units * (size_t)p.K * p.V * es);
     w.dh = off; off = align256(off + units * (size_t)p.K * p.V * es);
+    const size_t segbuf = p.maxS > 1 ? (size_t)p.NS * p.HV * p.K * p.V * 4 : 0;
+    w.hloc = off; off = align256(off + segbuf);
+    w.dhloc = off; off = align256(off + segbuf);
+    w.P = off; off = align256(off + segbuf);
+    w.hstart = off; off = align256(off + segbuf);
+    w.dhin = off; off = align256(off + segbuf);
     w.total = off;
     return w;
 }
@@ -116,14 +179,17 @@ int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const flo
     char* base = (char*)ws;
     auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
+    auto* seg = (SegInfo*)(base + w.seg_info);
+    auto* ss0 = (int32_t*)(base + w.seq_seg0);
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
                                             nullptr, base + w.KT, stream));
         if (st != GDR_OK) return st;
     }
     gdr::ScanArgs a{};
-    a.k = k; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
+    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    set_seg_buffers(a, base, w);
     a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.h0 = h0;
     a.h32 = h_out; a.v_new = v_new_out; a.ht = ht_out;
     a.cu = q.cu; a.T = q.T;
@@ -146,9 +212,11 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     char* base = (char*)ws;
     auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
+    auto* seg = (SegInfo*)(base + w.seg_info);
+    auto* ss0 = (int32_t*)(base + w.seq_seg0);
     auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
     if ((st = mark(0)) != GDR_OK) return st;
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, stream))) != GDR_OK) return st;
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, qp, k, v, g_cum, beta, info, base + w.W, base + w.U, base + w.R,
                                             base + w.A, base + w.KT, stream));
@@ -156,7 +224,8 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     }
     if ((st = mark(1)) != GDR_OK) return st;
     gdr::ScanArgs a{};
-    a.k = k; a.dO = dO; a.gcum = g_cum; a.info = info; a.seq_chunk0 = sc0;
+    a.dO = dO; a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    set_seg_buffers(a, base, w);
     a.W = base + w.W; a.U = base + w.U; a.R = base + w.R; a.KT = base + w.KT;
     a.h0 = h0; a.dht = dht;
     a.hT = base + w.h; a.dhT = base + w.dh; a.dh0 = dh0;

@@ -76,6 +76,28 @@ __device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, lon
     }
 }
 
+// 64 value columns (vc0 .. vc0+63) of one K x V state block from the workspace
+// state layout into LDS as [64 columns][KD keys] (row pitch LD).  16-bit types
+// read the fragment order (one contiguous 16 B per thread, two 8 B LDS
+// writes); fp32 reads the transposed [V][K] rows.
+template <class E, int KD, int LD>
+__device__ __forceinline__ void g_load_state(E* s, const E* __restrict__ blk, int vc0) {
+    if constexpr (sizeof(E) == 2) {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        typedef short s8 __attribute__((ext_vector_type(8)));
+        const E* src = blk + (long)vc0 * KD;          // 64 columns = 4 contiguous [16 x KD] blocks
+        for (int c = threadIdx.x; c < 64 * KD / 8; c += 512) {
+            const int ln = c & 63, sblk = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
+            const int row = 16 * cb + (ln & 15), key = 32 * sblk + 4 * (ln >> 4);
+            const s8 v = *(const s8*)(src + (long)c * 8);
+            *(s4*)(s + row * LD + key) = s4{v[0], v[1], v[2], v[3]};
+            *(s4*)(s + row * LD + key + 16) = s4{v[4], v[5], v[6], v[7]};
+        }
+    } else {
+        g_load_rows<E, E, KD, LD>(s, blk + (long)vc0 * KD, KD, 64);
+    }
+}
+
 // sum over the 16 lanes that share a row group (lane bits 0..3)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1, 64);
@@ -195,8 +217,8 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
             // h / dh slices are stored transposed: [V][K] per chunk -> rows v
-            g_load_rows<E, E, KD, LK>(sH, hT + (unit * VD + vh * 64) * KD, KD, 64);
-            g_load_rows<E, E, KD, LK>(sdH, dhT + (unit * VD + vh * 64) * KD, KD, 64);
+            g_load_state<E, KD, LK>(sH, hT + unit * VD * KD, vh * 64);
+            g_load_state<E, KD, LK>(sdH, dhT + unit * VD * KD, vh * 64);
             g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
             g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
             lds_barrier();

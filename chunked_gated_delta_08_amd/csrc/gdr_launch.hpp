@@ -14,6 +14,16 @@ struct ChunkInfo {
     int pad;  // chunk index within its sequence
 };
 
+// Scan segment table: the chunks of a sequence are cut into segments of L
+// chunks (the last one shorter) so that the sequential state scans can run
+// one workgroup per segment (see gdr_scan.hip).
+struct SegInfo {
+    int seq;  // sequence index
+    int c0;   // global index of the segment's first chunk
+    int nc;   // chunks in the segment
+    int lc0;  // index of its first chunk within the sequence
+};
+
 // Arguments shared by the launchers.  All pointers are device pointers.
 struct Problem {
     int B, T, HK, HV, K, V, BT, N;
@@ -21,15 +31,22 @@ struct Problem {
     float scale;
     int dtype;         // gdr_dtype
     const int32_t* cu; // device cu_seqlens or NULL
+    int L;             // scan segment length in chunks
+    int NS;            // total scan segments
+    int maxS;          // most segments in one sequence (1: no segmented scans)
 };
 
-// Workspace carve-up (byte offsets from the workspace base).
+// Workspace carve-up (byte offsets from the workspace base).  The segment
+// state buffers (hloc, dhloc, P, hstart, dhin: [NS][HV][K][V] fp32 each, in
+// the fp32 fragment order below) are empty when maxS == 1.
 struct WsPlan {
-    size_t chunk_info, seq_chunk0, W, U, R, A, KT, h, dh, total;
+    size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
+    size_t hloc, dhloc, P, hstart, dhin, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
-hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, hipStream_t s);
+hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, SegInfo* seg,
+                              int32_t* seq_seg0, hipStream_t s);
 
 // K1a: per-chunk WY factors.  W, U, K̃ (and R when q != NULL) in the scan
 // operand type; A = (I+L)^{-1} in the input type when A != NULL.
@@ -37,17 +54,44 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const voi
                        const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, void* KT,
                        hipStream_t s);
 
-// K1b + K2: the forward state scan and the reverse dh scan (one launch, two roles).
-//   fwd role: writes h (state entering each chunk; transposed [NT,HV,V,K] in the
-//   input type when hT != NULL, row-major fp32 [NT,HV,K,V] when h32 != NULL),
+// Workspace layout of the per-chunk states h[c] / dh[c] (one K x V block per
+// (chunk, value head) unit), shared by the scans (writers) and the gradient
+// kernel (reader):
+//   16-bit types: the scan's accumulator fragment order.  Element (key k,
+//     column v) sits at
+//         ((v/16 * K/32 + k/32) * 64 + 16 g + v%16) * 8 + i,
+//     with j = k % 32, g = (j % 16) / 4 and i = j % 4 + (j >= 16 ? 4 : 0);
+//     so one wave writes each [16 columns x 32 keys] block as 64 lanes x 16 B.
+//   fp32: transposed [V][K].
+__host__ __device__ constexpr long state_frag_offset(int KD, int k, int v) {
+    return ((long)((v / 16) * (KD / 32) + k / 32) * 64 + 16 * ((k % 16) / 4) + v % 16) * 8 + k % 4 +
+           ((k % 32) >= 16 ? 4 : 0);
+}
+
+// fp32 fragment order of a K x V block (segment buffers): 16 x 16 tiles,
+// tile (column block v/16, row block k/16) at ((v/16) * K/16 + k/16) * 256,
+// inside it lane 16 g + v%16 holds rows 4g .. 4g+3 (k % 16 = 4 g + e) as 4
+// consecutive floats.
+__host__ __device__ constexpr long state32_frag_offset(int KD, int k, int v) {
+    return ((long)((v / 16) * (KD / 16) + k / 16) * 64 + 16 * ((k % 16) / 4) + v % 16) * 4 + k % 4;
+}
+
+// K1b + K2: the forward state scan and the reverse dh scan.
+//   fwd role: writes h (state entering each chunk, layout above, in the input
+//   type when hT != NULL; row-major fp32 [NT,HV,K,V] when h32 != NULL),
 //   optional v_new (input type) and ht (fp32).
-//   rev role (when R != NULL): writes dh (transposed, input type) and dh0.
+//   rev role: writes dh (layout above, input type) and dh0.
+// With maxS > 1 three launches: local segment scans and transfer matrices,
+// the sequential combine over segments, then the scans proper from the exact
+// segment boundary states.
 struct ScanArgs {
-    const void* k; const void* dO; const float* gcum; const ChunkInfo* info; const int32_t* seq_chunk0;
+    const void* dO; const float* gcum; const int32_t* seq_chunk0;
+    const SegInfo* seg; const int32_t* seq_seg0;
     const void* W; const void* U; const void* R; const void* KT;
     const float* h0; const float* dht;
     void* hT; float* h32; void* v_new; float* ht;
     void* dhT; float* dh0;
+    float* hloc; float* dhloc; float* P; float* hstart; float* dhin;   // segment buffers
     const int32_t* cu; int T;   // sequence bounds: cu_seqlens (device) or dense length T
     bool do_fwd, do_rev;
 };

@@ -19,48 +19,93 @@
 
 namespace gdr {
 
-// ---------------------------------------------------------------- chunk table
+__device__ __forceinline__ int last_le(const int32_t* __restrict__ a, int n, int x) {
+    // largest i in [0, n) with a[i] <= x (a non-decreasing, a[0] <= x)
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// One workgroup: per-sequence chunk and segment counts (at least one segment
+// per sequence, so that an empty sequence still gets its dh0), their exclusive
+// prefix sums (seq_chunk0, seq_seg0, each with the total at [nseq]), then the
+// chunk table and the segment table filled in parallel (binary search of
+// each entry's sequence in the prefix arrays).
 __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* __restrict__ cu, int N, int B, int T,
-                                                           int BT, ChunkInfo* __restrict__ info,
-                                                           int32_t* __restrict__ seq_chunk0) {
-    __shared__ int part[1024];
+                                                           int BT, int L, ChunkInfo* __restrict__ info,
+                                                           int32_t* __restrict__ seq_chunk0,
+                                                           SegInfo* __restrict__ seg,
+                                                           int32_t* __restrict__ seq_seg0) {
+    __shared__ int pc[1024], ps[1024];
     const int nseq = cu ? N : B;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int per = (nseq + nt - 1) / nt;
-    const int s0 = tid * per, s1 = min(nseq, s0 + per);
-    int cnt = 0;
+    const int s0 = min(nseq, tid * per), s1 = min(nseq, s0 + per);
+    int cc = 0, cs = 0;
     for (int n = s0; n < s1; n++) {
-        int len = cu ? (cu[n + 1] - cu[n]) : T;
-        cnt += (len + BT - 1) / BT;
+        const int len = cu ? (cu[n + 1] - cu[n]) : T;
+        const int nc = (len + BT - 1) / BT;
+        cc += nc;
+        cs += nc > L ? (nc + L - 1) / L : 1;   // every sequence has a segment, empty ones too
     }
-    part[tid] = cnt;
+    pc[tid] = cc;
+    ps[tid] = cs;
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < nt; i++) { int c = part[i]; part[i] = acc; acc += c; }
-        seq_chunk0[nseq] = acc;
+    for (int off = 1; off < nt; off <<= 1) {   // inclusive scan (Hillis-Steele)
+        const int a = tid >= off ? pc[tid - off] : 0, b = tid >= off ? ps[tid - off] : 0;
+        __syncthreads();
+        pc[tid] += a;
+        ps[tid] += b;
+        __syncthreads();
     }
-    __syncthreads();
-    int base = part[tid];
+    int bc = pc[tid] - cc, bs = ps[tid] - cs;
     for (int n = s0; n < s1; n++) {
-        int bos = cu ? cu[n] : n * T;
-        int len = cu ? (cu[n + 1] - cu[n]) : T;
-        seq_chunk0[n] = base;
-        int nc = (len + BT - 1) / BT;
-        for (int c = 0; c < nc; c++) {
-            ChunkInfo ci;
-            ci.seq = n;
-            ci.t0 = bos + c * BT;
-            ci.len = min(BT, len - c * BT);
-            ci.pad = c;
-            info[base + c] = ci;
-        }
-        base += nc;
+        const int len = cu ? (cu[n + 1] - cu[n]) : T;
+        const int nc = (len + BT - 1) / BT;
+        seq_chunk0[n] = bc;
+        seq_seg0[n] = bs;
+        bc += nc;
+        bs += nc > L ? (nc + L - 1) / L : 1;
+    }
+    if (tid == nt - 1) {
+        seq_chunk0[nseq] = pc[nt - 1];
+        seq_seg0[nseq] = ps[nt - 1];
+    }
+    __syncthreads();
+    const int NT = pc[nt - 1], NS = ps[nt - 1];
+    for (int c = tid; c < NT; c += nt) {
+        const int n = last_le(seq_chunk0, nseq, c);
+        const int lc = c - seq_chunk0[n];
+        const int bos = cu ? cu[n] : n * T;
+        const int len = cu ? (cu[n + 1] - cu[n]) : T;
+        ChunkInfo ci;
+        ci.seq = n;
+        ci.t0 = bos + lc * BT;
+        ci.len = min(BT, len - lc * BT);
+        ci.pad = lc;
+        info[c] = ci;
+    }
+    for (int j = tid; j < NS; j += nt) {
+        const int n = last_le(seq_seg0, nseq, j);
+        const int ls = j - seq_seg0[n];
+        const int nc = seq_chunk0[n + 1] - seq_chunk0[n];
+        SegInfo si;
+        si.seq = n;
+        si.lc0 = ls * L;
+        si.c0 = seq_chunk0[n] + si.lc0;
+        si.nc = min(L, nc - si.lc0);
+        seg[j] = si;
     }
 }
 
-hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, hipStream_t s) {
-    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.B, p.T, p.BT, info, seq_chunk0);
+hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, SegInfo* seg,
+                              int32_t* seq_seg0, hipStream_t s) {
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.B, p.T, p.BT, p.L, info,
+                       seq_chunk0, seg, seq_seg0);
     return hipGetLastError();
 }
 

@@ -10,10 +10,12 @@
 //     dh[c−1] = γ_C dh[c] + Rᵀ dO − Wᵀ (K̃ dh[c]),   dh0 = dh[−1]
 //
 // Parallel decomposition: every column of the K x V state evolves on its own
-// (all updates multiply the state from the left), so a wave owns a K x 16
-// column slice for the whole sequence, in fp32 accumulator registers.  A
-// workgroup (4 waves) covers 64 columns; a grid row is (sequence, value head,
-// 64-column group).  The state doubles as the MFMA B operand without any data
+// (all updates multiply the state from the left), so a wave owns a K x V/4
+// column slice (V/64 blocks of 16 columns) for the whole sequence, in fp32
+// accumulator registers.  A workgroup (4 waves) covers all V columns of one
+// (sequence, value head, direction), so each operand tile is read from HBM
+// once per direction and every fragment read from LDS feeds V/64 MFMAs.
+// The state doubles as the MFMA B operand without any data
 // movement: the accumulator holds rows {4g..4g+3} of every 16-row tile, so two
 // tiles form one 32-deep k block in the permuted order
 //     π(8g+i) = 32s + (i < 4 ? 4g + i : 16 + 4g + i − 4),
@@ -32,12 +34,14 @@ template <class E, class S, int KD, int VD>
 struct ScanCfg {
     static constexpr int C = 64;
     static constexpr int LK = KD + spad<S>();   // [64][KD] tiles
-    static constexpr int LS = 64 + spad<S>();   // [64][64] column-group tiles
+    static constexpr int LS = VD + spad<S>();   // [64][VD] tiles (U or dO)
     static constexpr int EPV = 16 / (int)sizeof(S);
     static constexpr int NK = C * KD / (EPV * 256);   // 16-byte vectors per thread, [64][KD]
-    static constexpr int NX = C * 64 / (EPV * 256);   // per thread, [64][64]
-    static constexpr int KT = KD / 16;                // state tiles per wave
-    // one LDS slot: K̃, W, R [64][LK] and the U / dO column slice [64][LS]
+    static constexpr int NX = C * VD / (EPV * 256);   // per thread, [64][VD]
+    static constexpr int KT = KD / 16;                // state row tiles
+    static constexpr int NB = VD / 64;                // 16-column blocks per wave
+    static constexpr int CW = VD / 4;                 // state columns per wave
+    // one LDS slot: K̃, W, R [64][LK] and U / dO [64][LS]
     static constexpr size_t slot_elems = (size_t)3 * C * LK + (size_t)C * LS;
     static constexpr size_t smem = 2 * slot_elems * sizeof(S);
 };
@@ -50,8 +54,8 @@ struct Stage {
     typename Vec16<S>::t k[Cf::NK];
     typename Vec16<S>::t w[Cf::NK];
     typename Vec16<S>::t r[REV ? Cf::NK : 1];
-    typename Vec16<E>::t x[REV ? Cf::NX : 1];   // dO slice (reverse)
-    typename Vec16<S>::t u[REV ? 1 : Cf::NX];   // U slice (forward)
+    typename Vec16<E>::t x[REV ? Cf::NX : 1];   // dO tile (reverse)
+    typename Vec16<S>::t u[REV ? 1 : Cf::NX];   // U tile (forward)
     float gl;
     int cn;                                      // rows in the chunk (dO rows past it are zeroed at commit)
 };
@@ -120,26 +124,30 @@ __device__ __forceinline__ void transT_times_rows(f32x4 (&St)[KD / 16], const S*
     }
 }
 
-// Store a wave's K x 16 state slice: transposed [V][K] in type E (for the
-// gradient kernel) and/or row-major [K][V] fp32.  All values are packed
-// before the first store so that each store owns its data registers (a store
-// whose data registers are reused right away stalls until the memory
-// pipeline has read them).
+// Store a wave's K x 16 state block (columns col - r .. col - r + 15): in type
+// E in the workspace state layout (fragment order, 16 B per lane and 1 KB per
+// wave instruction; fp32: transposed [V][K]) and/or row-major [K][V] fp32.
+// All values are packed before the first store so that each store owns its
+// data registers.
 template <class E, int KD, int VD, bool EST>
 __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long unit, int col, E* hT, float* h32) {
     const int g = lane_id() >> 4;
     if constexpr (EST) {
-        E* p = hT + (unit * VD + col) * KD + 4 * g;
         if constexpr (sizeof(E) == 2) {
-            typedef E e4 __attribute__((ext_vector_type(4)));
-            e4 v[KD / 16];
+            typedef E e8 __attribute__((ext_vector_type(8)));
+            E* p = hT + unit * VD * KD + ((long)(col / 16) * (KD / 32) * 64 + lane_id()) * 8;
+            e8 v[KD / 32];
 #pragma unroll
-            for (int t = 0; t < KD / 16; t++)
+            for (int s = 0; s < KD / 32; s++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[t][e] = (E)St[t][e];
+                for (int e = 0; e < 4; e++) {
+                    v[s][e] = (E)St[2 * s][e];
+                    v[s][4 + e] = (E)St[2 * s + 1][e];
+                }
 #pragma unroll
-            for (int t = 0; t < KD / 16; t++) *(e4*)(p + 16 * t) = v[t];
+            for (int s = 0; s < KD / 32; s++) *(e8*)(p + 512 * s) = v[s];
         } else {
+            E* p = hT + (unit * VD + col) * KD + 4 * g;
 #pragma unroll
             for (int t = 0; t < KD / 16; t++) *(f32x4*)(p + 16 * t) = St[t];
         }
@@ -152,19 +160,33 @@ __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long uni
     }
 }
 
-template <class E, class S, int KD, int VD, bool rev, bool EST>
-__device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int HV, unsigned char* smem) {
+// Initial / final state forms of one scan job.
+enum StateForm { ST_NONE = 0, ST_ZERO = 0, ST_IDENT = 1, ST_NAT = 2, ST_FRAG = 3 };
+
+// One scan job: a run of chunks of one sequence and value head.
+struct ScanJob {
+    int n, hv;          // sequence, value head
+    int c0, nc, lc0;    // first chunk (global index), chunk count, first chunk's index in the sequence
+    int init_form;      // ST_ZERO, ST_IDENT (transfer matrix), ST_NAT ([K][V] fp32), ST_FRAG (fp32 fragment order)
+    const float* init;  // K x V block of the initial state
+    int out_form;       // ST_NONE, ST_NAT or ST_FRAG
+    float* out;         // K x V block of the final state
+};
+
+// rev: reverse (dh) recursion, else forward.  EST: per-chunk states stored in
+// type E.  ZU: U is taken as zero (the transfer-matrix role).
+template <class E, class S, int KD, int VD, bool rev, bool EST, bool ZU>
+__device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, int HV, unsigned char* smem) {
     using Cf = ScanCfg<E, S, KD, VD>;
     using St_t = Stage<E, S, KD, VD, rev>;
-    constexpr int NVG = VD / 64, KT = KD / 16, C = 64, EPV = Cf::EPV, LK = Cf::LK, LS = Cf::LS;
-    constexpr int VPR = KD / EPV, XPR = 64 / EPV;
+    constexpr int KT = KD / 16, C = 64, EPV = Cf::EPV, LK = Cf::LK, LS = Cf::LS, NB = Cf::NB, CW = Cf::CW;
+    constexpr int VPR = KD / EPV, XPR = VD / EPV;
     S* slot[2] = {(S*)smem, (S*)smem + Cf::slot_elems};
 
-    const int vg = b % NVG, hv = (b / NVG) % HV, n = b / (NVG * HV);
-    const int hk = hv / (HV / HK);
+    const int hv = jb.hv, n = jb.n;
     const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-    const int col = vg * 64 + 16 * w + r;       // this lane's state column
-    const int c0 = a.seq_chunk0[n], nc = a.seq_chunk0[n + 1] - c0;
+    const int col0 = CW * w + r;                // this lane's state column in block 0 (block nb: + 16 nb)
+    const int c0 = jb.c0, nc = jb.nc;
     const long bos = a.cu ? a.cu[n] : (long)n * a.T;            // first token of the sequence
     const int slen = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;        // its length
     const E* dO = (const E*)a.dO;
@@ -172,7 +194,6 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
     const S* U = (const S*)a.U;
     const S* R = (const S*)a.R;
     const S* KTl = (const S*)a.KT;
-    (void)hk;
 
     // loop-invariant per-thread element offsets of the staged vectors
     int offK[Cf::NK], rowX[Cf::NX], offX[Cf::NX];
@@ -188,17 +209,27 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
         offX[i] = (idx % XPR) * EPV;
     }
 
-    // state tiles: St[t][e] = state[16t + 4g + e][col]
-    f32x4 St[KT];
-    const float* init = rev ? a.dht : a.h0;
+    // state tiles: St[nb][t][e] = state[16t + 4g + e][col0 + 16 nb]
+    f32x4 St[NB][KT];
 #pragma unroll
-    for (int t = 0; t < KT; t++)
+    for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-        for (int e = 0; e < 4; e++)
-            St[t][e] = init ? init[(((long)n * HV + hv) * KD + 16 * t + 4 * g + e) * VD + col] : 0.f;
+        for (int t = 0; t < KT; t++) {
+            const int cb = CW * w / 16 + nb;
+            if (jb.init_form == ST_FRAG) {
+                St[nb][t] = *(const f32x4*)(jb.init + ((cb * KT + t) * 64 + l) * 4);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = 16 * t + 4 * g + e, col = col0 + 16 * nb;
+                    St[nb][t][e] = jb.init_form == ST_NAT ? jb.init[row * VD + col]
+                                 : jb.init_form == ST_IDENT ? (row == col ? 1.f : 0.f) : 0.f;
+                }
+            }
+        }
 
     auto chunk_of = [&](int i) { return rev ? c0 + nc - 1 - i : c0 + i; };
-    auto local_of = [&](int i) { return rev ? nc - 1 - i : i; };   // chunk index within the sequence
+    auto local_of = [&](int i) { return jb.lc0 + (rev ? nc - 1 - i : i); };   // chunk index within the sequence
 
     auto issue = [&](St_t& st, int i) {
         const int ci = chunk_of(i), lc = local_of(i);
@@ -222,9 +253,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
                 // commit, where the data is needed anyway (a select here would
                 // make the wave wait for the load it just issued)
                 const int rowc = min(rowX[j], Cn - 1);
-                st.x[j] = *(const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + vg * 64 + offX[j]);
-            } else {
-                st.u[j] = *(const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + vg * 64 + offX[j]);
+                st.x[j] = *(const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]);
+            } else if constexpr (!ZU) {
+                st.u[j] = *(const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]);
             }
         }
         st.gl = a.gcum[(t0 + Cn - 1) * HV + hv];
@@ -249,6 +280,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
 #pragma unroll
                 for (int e = 0; e < EPV; e++) xv[e] = valid ? (S)(float)st.x[j][e] : (S)0.f;
             } else {
+                if constexpr (ZU) continue;
                 xv = st.u[j];
             }
             *(typename Vec16<S>::t*)(sX + rowX[j] * LS + offX[j]) = xv;
@@ -263,7 +295,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
         const int ci = chunk_of(i);
         const long unit = (long)ci * HV + hv;
         const float gC = __expf(gl);
-        f32x4 X[4];
+        f32x4 X[NB][4];
         if constexpr (sizeof(S) == 2) {
             // All state-independent fragments of this chunk are read from LDS
             // first; the MFMA groups then only wait on their own operands.
@@ -271,7 +303,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
             frag Ar[4][KD / 32];   // rows of W (fwd) or K̃ (rev), keys in π order
             frag At[KT][2];        // K̃ᵀ (fwd) or Wᵀ (rev), rows in π order
             frag Rt[rev ? KT : 1][2];
-            frag Db[2];
+            frag Db[NB][2];
             const S* sRow = rev ? sK : sW;
             const S* sTr = rev ? sW : sK;
 #pragma unroll
@@ -283,22 +315,27 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
                     i16x8 c = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     Ar[m][sidx] = __builtin_bit_cast(frag, c);
                 }
-            if constexpr (!rev) {
+            if constexpr (!rev && ZU) {
 #pragma unroll
-                for (int m = 0; m < 4; m++) {   // U in accumulator layout: one transposing read per tile
-                    i16x4 u = ld_trans4<S>(sX, LS, 16 * w, 16 * m + 4 * g);
-                    S uu[4];
-                    __builtin_memcpy(uu, &u, 8);
+                for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) X[m][e] = (float)uu[e];
-                }
+                    for (int m = 0; m < 4; m++) X[nb][m] = zero4();
+            } else if constexpr (!rev) {
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int m = 0; m < 4; m++) {   // U in accumulator layout: one transposing read per tile
+                        i16x4 u = ld_trans4<S>(sX, LS, CW * w + 16 * nb, 16 * m + 4 * g);
+                        S uu[4];
+                        __builtin_memcpy(uu, &u, 8);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) X[nb][m][e] = (float)uu[e];
+                    }
             } else {
 #pragma unroll
-                for (int sidx = 0; sidx < 2; sidx++) Db[sidx] = ld_trans<S>(sX, LS, 16 * w, 32 * sidx);
+                for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                for (int t = 0; t < KT; t++)
-#pragma unroll
-                    for (int sidx = 0; sidx < 2; sidx++) Rt[t][sidx] = ld_trans<S>(sR, LK, 16 * t, 32 * sidx);
+                    for (int sidx = 0; sidx < 2; sidx++) Db[nb][sidx] = ld_trans<S>(sX, LS, CW * w + 16 * nb, 32 * sidx);
             }
 #pragma unroll
             for (int t = 0; t < KT; t++)
@@ -310,64 +347,94 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
                     At[t][sidx] = __builtin_bit_cast(frag, c);
                 }
             // state store (before the update) and B fragments of the state
-            store_state<E, KD, VD, EST>(St, unit, col, rev ? (E*)a.dhT : (E*)a.hT, rev ? nullptr : a.h32);
-            const float sg = rev ? 1.f : -1.f;   // fwd: X = U − W h ; rev: X = K̃ dh
-            frag Bs[KD / 32];
 #pragma unroll
-            for (int sidx = 0; sidx < KD / 32; sidx++)
+            for (int nb = 0; nb < NB; nb++)
+                store_state<E, KD, VD, EST>(St[nb], unit, col0 + 16 * nb, rev ? (E*)a.dhT : (E*)a.hT,
+                                            rev ? nullptr : a.h32);
+            // fwd: X = U − W h ; rev: X = K̃ dh ; transfer role: X = W h (sign applied below)
+            const float sg = (rev || ZU) ? 1.f : -1.f;
+            frag Bs[NB][KD / 32];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    Bs[sidx][e] = (S)(sg * St[2 * sidx][e]);
-                    Bs[sidx][4 + e] = (S)(sg * St[2 * sidx + 1][e]);
-                }
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int sidx = 0; sidx < KD / 32; sidx++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        Bs[nb][sidx][e] = (S)(sg * St[nb][2 * sidx][e]);
+                        Bs[nb][sidx][4 + e] = (S)(sg * St[nb][2 * sidx + 1][e]);
+                    }
             if constexpr (rev) {
 #pragma unroll
-                for (int m = 0; m < 4; m++) X[m] = zero4();
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int m = 0; m < 4; m++) X[nb][m] = zero4();
             }
 #pragma unroll
             for (int sidx = 0; sidx < KD / 32; sidx++)
 #pragma unroll
-                for (int m = 0; m < 4; m++) X[m] = Mma<S>::run(Ar[m][sidx], Bs[sidx], X[m]);
+                for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int t = 0; t < KT; t++) St[t] *= gC;
+                    for (int nb = 0; nb < NB; nb++) X[nb][m] = Mma<S>::run(Ar[m][sidx], Bs[nb][sidx], X[nb][m]);
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int t = 0; t < KT; t++) St[nb][t] *= gC;
             if constexpr (rev) {
+                // Rᵀ fragments are read here, after the K̃ dh products are
+                // issued, to keep them out of the live range of the others
 #pragma unroll
                 for (int t = 0; t < KT; t++)
 #pragma unroll
-                    for (int sidx = 0; sidx < 2; sidx++) St[t] = Mma<S>::run(Rt[t][sidx], Db[sidx], St[t]);   // + Rᵀ dO
+                    for (int sidx = 0; sidx < 2; sidx++) Rt[t][sidx] = ld_trans<S>(sR, LK, 16 * t, 32 * sidx);
+#pragma unroll
+                for (int t = 0; t < KT; t++)
+#pragma unroll
+                    for (int sidx = 0; sidx < 2; sidx++)
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++)
+                            St[nb][t] = Mma<S>::run(Rt[t][sidx], Db[nb][sidx], St[nb][t]);   // + Rᵀ dO
             } else if (a.v_new) {
                 const int lc = local_of(i), clen = min(C, slen - lc * C);
                 const long ct0 = bos + (long)lc * C;
 #pragma unroll
-                for (int m = 0; m < 4; m++)
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int m = 0; m < 4; m++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int row = 16 * m + 4 * g + e;
+                            if (row < clen)
+                                ((E*)a.v_new)[((ct0 + row) * HV + hv) * VD + col0 + 16 * nb] = (E)X[nb][m][e];
+                        }
+            }
+            // fwd: + K̃ᵀ V_new ; rev: − Wᵀ (K̃ dh) ; transfer role: − K̃ᵀ (W h)
+            const float sp = (rev || ZU) ? -1.f : 1.f;
+            frag Bp[NB][2];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int sidx = 0; sidx < 2; sidx++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int row = 16 * m + 4 * g + e;
-                        if (row < clen) ((E*)a.v_new)[((ct0 + row) * HV + hv) * VD + col] = (E)X[m][e];
+                        Bp[nb][sidx][e] = (S)(sp * X[nb][2 * sidx][e]);
+                        Bp[nb][sidx][4 + e] = (S)(sp * X[nb][2 * sidx + 1][e]);
                     }
-            }
-            const float sp = rev ? -1.f : 1.f;   // fwd: + K̃ᵀ V_new ; rev: − Wᵀ (K̃ dh)
-            frag Bp[2];
-#pragma unroll
-            for (int sidx = 0; sidx < 2; sidx++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    Bp[sidx][e] = (S)(sp * X[2 * sidx][e]);
-                    Bp[sidx][4 + e] = (S)(sp * X[2 * sidx + 1][e]);
-                }
 #pragma unroll
             for (int t = 0; t < KT; t++)
 #pragma unroll
-                for (int sidx = 0; sidx < 2; sidx++) St[t] = Mma<S>::run(At[t][sidx], Bp[sidx], St[t]);
+                for (int sidx = 0; sidx < 2; sidx++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) St[nb][t] = Mma<S>::run(At[t][sidx], Bp[nb][sidx], St[nb][t]);
         } else {
-            // fp32 operands (16x16x4 MFMA): small sizes only, plain order
+            // fp32 operands (16x16x4 MFMA): K = V = 64 only (one 16-column block per wave), plain order
+            static_assert(NB == 1, "fp32 scan is built for V = 64");
             if constexpr (!rev) {
-                store_state<E, KD, VD, EST>(St, unit, col, (E*)a.hT, a.h32);
+                store_state<E, KD, VD, EST>(St[0], unit, col0, (E*)a.hT, a.h32);
 #pragma unroll
                 for (int m = 0; m < 4; m++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) X[m][e] = (float)sX[(16 * m + 4 * g + e) * LS + 16 * w + r];
-                rows_times_state<S, KD, LK>(X, sW, St, -1.f);
+                    for (int e = 0; e < 4; e++) X[0][m][e] = (float)sX[(16 * m + 4 * g + e) * LS + 16 * w + r];
+                rows_times_state<S, KD, LK>(X[0], sW, St[0], -1.f);
                 if (a.v_new) {
                     const int lc = local_of(i), clen = min(C, slen - lc * C);
                     const long ct0 = bos + (long)lc * C;
@@ -376,25 +443,26 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
                             const int row = 16 * m + 4 * g + e;
-                            if (row < clen) ((E*)a.v_new)[((ct0 + row) * HV + hv) * VD + col] = (E)X[m][e];
+                            if (row < clen) ((E*)a.v_new)[((ct0 + row) * HV + hv) * VD + col0] = (E)X[0][m][e];
                         }
                 }
 #pragma unroll
-                for (int t = 0; t < KT; t++) St[t] *= gC;
-                transT_times_rows<S, KD, LK>(St, sK, X, 1.f);
+                for (int t = 0; t < KT; t++) St[0][t] *= gC;
+                transT_times_rows<S, KD, LK>(St[0], sK, X[0], 1.f);
             } else {
-                store_state<E, KD, VD, EST>(St, unit, col, (E*)a.dhT, nullptr);
+                store_state<E, KD, VD, EST>(St[0], unit, col0, (E*)a.dhT, nullptr);
 #pragma unroll
-                for (int m = 0; m < 4; m++) X[m] = zero4();
-                rows_times_state<S, KD, LK>(X, sK, St, 1.f);
+                for (int m = 0; m < 4; m++) X[0][m] = zero4();
+                rows_times_state<S, KD, LK>(X[0], sK, St[0], 1.f);
 #pragma unroll
-                for (int t = 0; t < KT; t++) St[t] *= gC;
+                for (int t = 0; t < KT; t++) St[0][t] *= gC;
 #pragma unroll
                 for (int t = 0; t < KT; t++)
 #pragma unroll
                     for (int kb = 0; kb < 16; kb++)
-                        St[t] = Mma<float>::run(sR[(4 * kb + g) * LK + 16 * t + r], sX[(4 * kb + g) * LS + 16 * w + r], St[t]);
-                transT_times_rows<S, KD, LK>(St, sW, X, -1.f);
+                        St[0][t] = Mma<float>::run(sR[(4 * kb + g) * LK + 16 * t + r], sX[(4 * kb + g) * LS + 16 * w + r],
+                                                   St[0][t]);
+                transT_times_rows<S, KD, LK>(St[0], sW, X[0], -1.f);
             }
         }
     };
@@ -428,43 +496,265 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int HK, int 
         }
     }
 
-    // final state / dh0
-    float* out = rev ? a.dh0 : a.ht;
-    if (out) {
+    // final state
+    if (jb.out_form == ST_FRAG) {
 #pragma unroll
-        for (int t = 0; t < KT; t++)
+        for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) out[(((long)n * HV + hv) * KD + 16 * t + 4 * g + e) * VD + col] = St[t][e];
+            for (int t = 0; t < KT; t++) *(f32x4*)(jb.out + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4) = St[nb][t];
+    } else if (jb.out_form == ST_NAT) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int t = 0; t < KT; t++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) jb.out[(16 * t + 4 * g + e) * VD + col0 + 16 * nb] = St[nb][t][e];
     }
 }
 
-// EST: the transposed states (hT for the forward scan, dhT for the reverse
-// one) are stored in type E.  It is a template parameter so the store is not
-// behind a runtime branch: the compiler's wait counts are then exact.
+// Segment bookkeeping shared by the kernels below.
+struct SegView {
+    SegInfo si;
+    int j, ls, S;   // segment index, its index within the sequence, segments in the sequence
+    bool first, last;
+};
+__device__ __forceinline__ SegView seg_view(const ScanArgs& a, int j) {
+    SegView v;
+    v.si = a.seg[j];
+    v.j = j;
+    const int s0 = a.seq_seg0[v.si.seq];
+    v.ls = j - s0;
+    v.S = a.seq_seg0[v.si.seq + 1] - s0;
+    v.first = v.ls == 0;
+    v.last = v.ls == v.S - 1;
+    return v;
+}
+
+// The scans proper (one job per (segment, value head, direction)): forward
+// jobs for blocks [0, nfwd), reverse jobs after.  A job starts from h0 / dht
+// at the sequence ends and from the combined boundary states otherwise; the
+// first reverse segment writes dh0 and the last forward one ht.
+// EST: the states are stored in type E.  It is a template parameter so the
+// store is not behind a runtime branch: the compiler's wait counts are then
+// exact.
 template <class E, class S, int KD, int VD, bool EST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-scan_kernel(ScanArgs a, int nfwd, int HK, int HV) {
+scan_kernel(ScanArgs a, int nfwd, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    if ((int)blockIdx.x >= nfwd) scan_body<E, S, KD, VD, true, EST>(a, (int)blockIdx.x - nfwd, HK, HV, smem);
-    else scan_body<E, S, KD, VD, false, EST>(a, (int)blockIdx.x, HK, HV, smem);
+    const bool rev = (int)blockIdx.x >= nfwd;
+    const int b = rev ? (int)blockIdx.x - nfwd : (int)blockIdx.x;
+    const SegView v = seg_view(a, b / HV);
+    const long KV = (long)KD * VD;
+    ScanJob jb;
+    jb.n = v.si.seq;
+    jb.hv = b % HV;
+    jb.c0 = v.si.c0;
+    jb.nc = v.si.nc;
+    jb.lc0 = v.si.lc0;
+    const long nblk = ((long)jb.n * HV + jb.hv) * KV, sblk = ((long)v.j * HV + jb.hv) * KV;
+    if (rev) {
+        const bool from_end = v.last;
+        jb.init_form = from_end ? (a.dht ? ST_NAT : ST_ZERO) : ST_FRAG;
+        jb.init = from_end ? (a.dht ? a.dht + nblk : nullptr) : a.dhin + sblk;
+        jb.out_form = v.first && a.dh0 ? ST_NAT : ST_NONE;
+        jb.out = a.dh0 ? a.dh0 + nblk : nullptr;
+        scan_body<E, S, KD, VD, true, EST, false>(a, jb, HV, smem);
+    } else {
+        jb.init_form = v.first ? (a.h0 ? ST_NAT : ST_ZERO) : ST_FRAG;
+        jb.init = v.first ? (a.h0 ? a.h0 + nblk : nullptr) : a.hstart + sblk;
+        jb.out_form = v.last && a.ht ? ST_NAT : ST_NONE;
+        jb.out = a.ht ? a.ht + nblk : nullptr;
+        scan_body<E, S, KD, VD, false, EST, false>(a, jb, HV, smem);
+    }
+}
+
+// Local segment scans (16-bit operands only).  Roles, NS*HV blocks each:
+//   0: forward from zero over the segment  -> hloc  (not for a sequence's last segment)
+//   1: reverse from zero over the segment  -> dhloc (not for its first segment)
+//   2: transfer matrix P = Π (γ_C I − K̃ᵀ W) over the segment, from I -> P
+//      (only for sequences with more than one segment)
+// The caller passes arguments with no per-chunk outputs (hT, dhT, h32, v_new).
+template <class E, class S, int KD, int VD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+seg_kernel(ScanArgs a, int NS, int HV) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int per = NS * HV, role = (int)blockIdx.x / per, b = (int)blockIdx.x % per;
+    const SegView v = seg_view(a, b / HV);
+    const long KV = (long)KD * VD;
+    ScanJob jb;
+    jb.n = v.si.seq;
+    jb.hv = b % HV;
+    jb.c0 = v.si.c0;
+    jb.nc = v.si.nc;
+    jb.lc0 = v.si.lc0;
+    jb.init = nullptr;
+    jb.out_form = ST_FRAG;
+    const long sblk = ((long)v.j * HV + jb.hv) * KV;
+    if (role == 0) {
+        if (v.last || !a.do_fwd) return;
+        jb.init_form = ST_ZERO;
+        jb.out = a.hloc + sblk;
+        scan_body<E, S, KD, VD, false, false, false>(a, jb, HV, smem);
+    } else if (role == 1) {
+        if (v.first || !a.do_rev) return;
+        jb.init_form = ST_ZERO;
+        jb.out = a.dhloc + sblk;
+        scan_body<E, S, KD, VD, true, false, false>(a, jb, HV, smem);
+    } else {
+        if (v.S == 1) return;
+        jb.init_form = ST_IDENT;
+        jb.out = a.P + sblk;
+        scan_body<E, S, KD, VD, false, false, true>(a, jb, HV, smem);
+    }
+}
+
+// Sequential combine over the segments of one (sequence, value head):
+//   forward  h_start[s+1] = P_s h_start[s] + hloc_s       (h_start[0] = h0)
+//   reverse  dh_in[s-1]   = P_sᵀ dh_in[s] + dhloc_s       (dh_in[S-1] = dht)
+// writing every boundary state except the two sequence ends (which the scans
+// read from h0 / dht).  The state is kept in fp32 accumulators as in the
+// scans; P_s is staged in LDS transposed (PT[v][k] = P[k][v], operand type S)
+// and the next segment's P and hloc are prefetched into registers while the
+// current product runs.  Grid: forward jobs then reverse jobs, N*HV each.
+template <class S, int KD, int VD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+combine_kernel(ScanArgs a, int nseq, int HV) {
+    static_assert(KD == VD, "the transfer matrix multiplies the state from the left");
+    constexpr int KT = KD / 16, NB = VD / 64, CW = VD / 4, LK = KD + spad<S>();
+    constexpr int NP = KD * KD / (4 * 256);   // float4 chunks of P per thread
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sPT = (S*)smem;
+    using frag = typename Mma<S>::frag;
+    const int per = nseq * HV;
+    const bool rev = (int)blockIdx.x >= per;
+    const int b = rev ? (int)blockIdx.x - per : (int)blockIdx.x;
+    const int n = b / HV, hv = b % HV;
+    const int s0 = a.seq_seg0[n], S_n = a.seq_seg0[n + 1] - s0;
+    if (S_n < 2 || (rev ? !a.do_rev : !a.do_fwd)) return;
+    const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+    const int col0 = CW * w + r;
+    const long KV = (long)KD * VD;
+    auto blk = [&](float* base, int j) { return base + ((long)j * HV + hv) * KV; };
+
+    f32x4 St[NB][KT];
+    const float* init = rev ? a.dht : a.h0;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int t = 0; t < KT; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                St[nb][t][e] = init ? init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col0 + 16 * nb] : 0.f;
+
+    // step q uses segment j(q): forward j = s0 + q (q = 0 .. S_n-2), reverse j = s0 + S_n-1-q
+    const int nsteps = S_n - 1;
+    auto seg_of = [&](int q) { return rev ? s0 + S_n - 1 - q : s0 + q; };
+    f32x4 pr[NP], hl[NB][KT];
+    auto prefetch = [&](int q) {
+        const int j = seg_of(q);
+        const float* P = blk(a.P, j);
+        const float* H = blk(rev ? a.dhloc : a.hloc, j);
+#pragma unroll
+        for (int i = 0; i < NP; i++) pr[i] = *(const f32x4*)(P + (threadIdx.x + 256 * i) * 4);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int t = 0; t < KT; t++) hl[nb][t] = *(const f32x4*)(H + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4);
+    };
+    prefetch(0);
+    for (int q = 0; q < nsteps; q++) {
+        lds_barrier();   // the previous product has read sPT
+#pragma unroll
+        for (int i = 0; i < NP; i++) {   // fragment-order tile (cb, tt), lane (g', r'): P[16tt+4g'+e][16cb+r']
+            const int c = threadIdx.x + 256 * i, tile = c >> 6, ln = c & 63;
+            const int cb = tile / KT, tt = tile % KT;
+            typedef S s4 __attribute__((ext_vector_type(4)));
+            s4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) v4[e] = (S)pr[i][e];
+            *(s4*)(sPT + (16 * cb + (ln & 15)) * LK + 16 * tt + 4 * (ln >> 4)) = v4;
+        }
+        f32x4 X[NB][KT];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int t = 0; t < KT; t++) X[nb][t] = hl[nb][t];
+        lds_barrier();
+        if (q + 1 < nsteps) prefetch(q + 1);
+        frag Bs[NB][KD / 32];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int s = 0; s < KD / 32; s++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    Bs[nb][s][e] = (S)St[nb][2 * s][e];
+                    Bs[nb][s][4 + e] = (S)St[nb][2 * s + 1][e];
+                }
+#pragma unroll
+        for (int t = 0; t < KT; t++)
+#pragma unroll
+            for (int s = 0; s < KD / 32; s++) {
+                i16x4 lo, hi;
+                if (rev) {   // rows of Pᵀ = rows of PT
+                    const S* p = sPT + (16 * t + r) * LK + 32 * s + 4 * g;
+                    lo = *(const i16x4*)p;
+                    hi = *(const i16x4*)(p + 16);
+                } else {     // rows of P = columns of PT
+                    lo = ld_trans4<S>(sPT, LK, 16 * t, 32 * s + 4 * g);
+                    hi = ld_trans4<S>(sPT, LK, 16 * t, 32 * s + 16 + 4 * g);
+                }
+                i16x8 c8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const frag A = __builtin_bit_cast(frag, c8);
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) X[nb][t] = Mma<S>::run(A, Bs[nb][s], X[nb][t]);
+            }
+        const int jd = rev ? seg_of(q) - 1 : seg_of(q) + 1;   // the segment whose boundary state this is
+        float* out = blk(rev ? a.dhin : a.hstart, jd);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int t = 0; t < KT; t++) {
+                St[nb][t] = X[nb][t];
+                *(f32x4*)(out + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4) = X[nb][t];
+            }
+    }
 }
 
 template <class E, class S, int KD, int VD>
 static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
     using Cf = ScanCfg<E, S, KD, VD>;
     const int nseq = p.cu ? p.N : p.B;
-    const int per = nseq * p.HV * (VD / 64);
+    const int per = p.NS * p.HV;
     const int nfwd = a.do_fwd ? per : 0, nrev = a.do_rev ? per : 0;
     if (nfwd + nrev == 0) return hipSuccess;
     // either every launched scan stores its E-typed states or none does
     const bool est_f = !a.do_fwd || a.hT, est_r = !a.do_rev || a.dhT;
     const bool none_f = !a.do_fwd || !a.hT, none_r = !a.do_rev || !a.dhT;
     if (!(est_f && est_r) && !(none_f && none_r)) return hipErrorInvalidValue;
-    auto kern = (est_f && est_r) ? scan_kernel<E, S, KD, VD, true> : scan_kernel<E, S, KD, VD, false>;
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
+    if (p.maxS > 1) {
+        if constexpr (sizeof(S) == 2) {
+            ScanArgs a1 = a;   // local scans write only their final states
+            a1.hT = nullptr; a1.dhT = nullptr; a1.h32 = nullptr; a1.v_new = nullptr;
+            auto k1 = seg_kernel<E, S, KD, VD>;
+            if (hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) !=
+                hipSuccess)
+                return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL(k1, dim3(3 * per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            constexpr int csm = KD * (KD + spad<S>()) * (int)sizeof(S);
+            hipLaunchKernelGGL((combine_kernel<S, KD, VD>), dim3(2 * nseq * p.HV), dim3(256), csm, s, a, nseq, p.HV);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else {
+            return hipErrorInvalidValue;   // fp32 problems are planned without segments
+        }
+    }
+    auto kern = (est_f && est_r) ? scan_kernel<E, S, KD, VD, true> : scan_kernel<E, S, KD, VD, false>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3(nfwd + nrev), dim3(256), Cf::smem, s, a, nfwd, p.HK, p.HV);
+    hipLaunchKernelGGL(kern, dim3(nfwd + nrev), dim3(256), Cf::smem, s, a, nfwd, p.HV);
     return hipGetLastError();
 }
 

@@ -64,6 +64,11 @@ typedef struct gdr_problem {
                                        It must hold the same values; it is read during the call only. */
     float scale;   /* output scale; <= 0 selects 1/sqrt(K) */
     gdr_dtype dtype; /* type of q, k, v, beta, dO and of dq, dk, dv */
+    int seg_chunks;  /* chunks per segment of the sequential state scans (16-bit types): each
+                        sequence is cut into segments that are scanned in parallel and joined
+                        exactly by their transfer matrices.  0 = chosen from the chunk counts and
+                        the head count; < 0 = never segment.  fp32 problems are never segmented.
+                        Results agree up to rounding for every value. */
 } gdr_problem;
 
 /* Human-readable text for a gdr_status (static storage). */

@@ -27,7 +27,8 @@ def test_header_symbols_exported(B):
 def _prob(lib, **kw):
     d = dict(B=1, T=256, HK=2, HV=2, K=64, V=64, BT=64, dtype=lib.GDR_BF16)
     d.update(kw)
-    return lib.Problem(d["B"], d["T"], d["HK"], d["HV"], d["K"], d["V"], d["BT"], 0, None, None, 0.0, d["dtype"])
+    return lib.Problem(d["B"], d["T"], d["HK"], d["HV"], d["K"], d["V"], d["BT"], 0, None, None, 0.0, d["dtype"],
+                       d.get("seg_chunks", 0))
 
 
 FAKE = ctypes.c_void_p(256)   # never dereferenced: validation fails first

@@ -40,13 +40,13 @@ def _to_dev(x):
     return None if x is None else x.cuda()
 
 
-def _run_gpu(B, inp, dht_zero_tensor=False):
+def _run_gpu(B, inp, dht_zero_tensor=False, seg_chunks=0):
     dev = {k: _to_dev(inp[k]) for k in ("q", "k", "v", "beta", "dO", "gcum", "dht", "h0")}
     if dht_zero_tensor and dev["dht"] is None:
         dev["dht"] = torch.zeros((inp["N"], inp["HV"], inp["K"], inp["V"]), device="cuda")
     cu = None if inp["cu"] is None else torch.tensor(inp["cu"], dtype=torch.int32, device="cuda")
     out = B.gdr_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["gcum"], dev["beta"], dev["dO"], dht=dev["dht"],
-                          h0=dev["h0"], cu_seqlens=cu, B=inp["B"], BT=inp["BT"])
+                          h0=dev["h0"], cu_seqlens=cu, B=inp["B"], BT=inp["BT"], seg_chunks=seg_chunks)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.float().cpu().numpy()) for k, v in out.items()}
 
@@ -117,6 +117,42 @@ def test_small_parity(B, oracle, name):
     _compare(got, ref, dt, label=name)
 
 
+# Segmented state scans (local scans + transfer matrices + combine), forced at
+# small sizes so that segment boundaries fall inside short sequences, next to
+# partial chunks, one-chunk and empty sequences.
+SEG_CASES = {
+    # name: (B, T, HK, HV, K, V, dtype, lengths, extra, seg_chunks)
+    "bf16_T700_seg1": (1, 700, 2, 2, 128, 128, "bf16", None, {}, 1),
+    "bf16_slow_gate_h0_T1000_seg3": (1, 1000, 1, 1, 128, 128, "bf16", None, {"gate_scale": 1 / 64, "h0": True}, 3),
+    "bf16_gqa_varlen_seg2": (1, None, 1, 2, 128, 128, "bf16", [300, 5, 530, 0, 64, 1, 200], {"gate_scale": 1 / 16}, 2),
+    "f16_k64_batch2_seg2": (2, 600, 2, 2, 64, 64, "f16", None, {"gate_scale": 1 / 8, "h0": True}, 2),
+    "bf16_zero_gate_T640_seg4": (1, 640, 1, 1, 128, 128, "bf16", None, {"zero_gate": True}, 4),
+}
+
+
+@pytest.mark.parametrize("name", list(SEG_CASES))
+def test_segmented_parity(B, oracle, name):
+    Bb, T, HK, HV, K, V, dt, lens, extra, seg = SEG_CASES[name]
+    _log(f"[parity] {name}: B={Bb} T={T} HK={HK} HV={HV} K={K} {dt} lens={lens} {extra} seg_chunks={seg}")
+    inp = W.gdr_inputs(Bb, T, HK, HV, K, V, dtype=dt, seed=2, lengths=lens, **extra)
+    got = _run_gpu(B, inp, seg_chunks=seg)
+    ref = _run_oracle(oracle, inp)
+    _compare(got, ref, dt, label=name)
+
+
+def test_segmented_matches_unsegmented(B):
+    """Automatic segmentation (chosen at this size) against no segmentation: same
+    gradients up to rounding."""
+    _log("[parity] T=8192 H=2 bf16: automatic segments vs none")
+    inp = W.gdr_inputs(1, 8192, 2, 2, 128, 128, dtype="bf16", seed=4, gate_scale=1 / 16)
+    a = _run_gpu(B, inp, seg_chunks=0)
+    b = _run_gpu(B, inp, seg_chunks=-1)
+    for name in a:
+        e = rel_l2(a[name], b[name])
+        _log(f"  {name}: {e:.2e}")
+        assert e <= 5e-3, (name, e)
+
+
 def test_dht_null_equals_zero(B):
     _log("[parity] dht NULL vs explicit zeros")
     inp = W.gdr_inputs(1, 256, 2, 2, 64, 64, dtype="f32", seed=0, dht=False)
@@ -137,12 +173,13 @@ def test_deterministic(B):
 
 def test_fwd_states(B, oracle):
     """Per-chunk states h[c], v_new and final states against the oracle's token recurrence."""
-    for dt, K, lens, tol in (("f32", 64, [150, 64, 33], 1e-5), ("bf16", 128, [300, 64], 2e-2)):
-        _log(f"[parity] fwd_states {dt} K={K} lens={lens}")
+    for dt, K, lens, tol, seg in (("f32", 64, [150, 64, 33], 1e-5, 0), ("bf16", 128, [300, 64], 2e-2, 0),
+                                  ("bf16", 128, [300, 64, 700, 0], 2e-2, 2)):
+        _log(f"[parity] fwd_states {dt} K={K} lens={lens} seg_chunks={seg}")
         inp = W.gdr_inputs(1, None, 1, 2, K, K, dtype=dt, seed=3, lengths=lens, h0=True, gate_scale=1 / 32)
         cu = torch.tensor(inp["cu"], dtype=torch.int32, device="cuda")
         out = B.gdr_fwd_states(inp["k"].cuda(), inp["v"].cuda(), inp["gcum"].cuda(), inp["beta"].cuda(),
-                               h0=inp["h0"].cuda(), cu_seqlens=cu)
+                               h0=inp["h0"].cuda(), cu_seqlens=cu, seg_chunks=seg)
         torch.cuda.synchronize()
         p = oracle.Problem(1, inp["T"], 1, 2, K, K, cu_seqlens=inp["cu"])
         graw = oracle.gcum_to_graw(p, 64, inp["gcum"].numpy())
