@@ -53,7 +53,10 @@ struct GradCfg {
     static constexpr size_t odVn = oVn + (size_t)C * LS * sizeof(E);
     static constexpr size_t oSm = odVn + (size_t)C * LS * sizeof(E);
     // small arrays: G, β, γ, row partials 2x[4][64], col partials [2][64], misc [80]
-    static constexpr size_t smem = oSm + (size_t)(3 * 64 + 8 * 64 + 2 * 64 + 80) * 4;
+    // dv slice [64][LS] staged for coalesced stores (16-bit types; fp32 stores directly)
+    static constexpr bool DV_LDS = sizeof(E) == 2;
+    static constexpr size_t oDv = oSm + (size_t)(3 * 64 + 8 * 64 + 2 * 64 + 80) * 4;
+    static constexpr size_t smem = oDv + (DV_LDS ? (size_t)C * LS * sizeof(E) : 0);
     static constexpr size_t oV = oQ;                                    // [64][LS] inside the V loop
     static constexpr size_t odW = oH;                                   // [64][LK]
     static constexpr size_t odA = odH;                                  // [64][LA]
@@ -95,6 +98,84 @@ __device__ __forceinline__ void g_load_state(E* s, const E* __restrict__ blk, in
         }
     } else {
         g_load_rows<E, E, KD, LD>(s, blk + (long)vc0 * KD, KD, 64);
+    }
+}
+
+// Register staging of a [ROWS][D] row block (row stride rs elements): load()
+// issues the 16-byte loads (rows at or past C read row C-1, a valid row),
+// store() writes the block to LDS (row pitch LD) with rows past C zeroed.
+// Splitting the two lets several blocks' loads be in flight together.
+template <class E, int D, int LD, int ROWS = 64>
+struct RowsReg {
+    static constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV, NV = ROWS * VPR, N = (NV + 511) / 512;
+    typename Vec16<E>::t v[N];
+    int C;
+    __device__ __forceinline__ void load(const E* __restrict__ g, long rs, int Cn) {
+        C = Cn;
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = threadIdx.x + 512 * i;
+            if (NV % 512 == 0 || idx < NV) {
+                const int r = min(idx / VPR, Cn - 1), c = idx % VPR;
+                v[i] = *(const typename Vec16<E>::t*)(g + r * rs + c * EPV);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(E* s) const {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int idx = threadIdx.x + 512 * i;
+            if (NV % 512 == 0 || idx < NV) {
+                const int r = idx / VPR, c = idx % VPR;
+                typename Vec16<E>::t x = v[i];
+                if (r >= C) x = typename Vec16<E>::t{};
+                *(typename Vec16<E>::t*)(s + r * LD + c * EPV) = x;
+            }
+        }
+    }
+};
+
+// Register staging of 64 value columns (vc0 .. vc0+63) of one K x V state
+// block from the workspace state layout, written to LDS as [64 columns][KD]
+// (see g_load_state).
+template <class E, int KD, int LD>
+struct StateReg {
+    static constexpr bool FRAG = sizeof(E) == 2;
+    static constexpr int N = 64 * KD * (int)sizeof(E) / 16 / 512;
+    typename Vec16<E>::t v[N];
+    __device__ __forceinline__ void load(const E* __restrict__ blk, int vc0) {
+        const E* src = blk + (long)vc0 * KD;   // 64 columns: contiguous in both layouts
+#pragma unroll
+        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(threadIdx.x + 512 * i) * (16 / sizeof(E)));
+    }
+    __device__ __forceinline__ void store(E* s) const {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            const int c = threadIdx.x + 512 * i;
+            if constexpr (FRAG) {
+                typedef short s4 __attribute__((ext_vector_type(4)));
+                typedef short s8 __attribute__((ext_vector_type(8)));
+                const int ln = c & 63, sblk = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
+                const int row = 16 * cb + (ln & 15), key = 32 * sblk + 4 * (ln >> 4);
+                const s8 x = __builtin_bit_cast(s8, v[i]);
+                *(s4*)(s + row * LD + key) = s4{x[0], x[1], x[2], x[3]};
+                *(s4*)(s + row * LD + key + 16) = s4{x[4], x[5], x[6], x[7]};
+            } else {
+                const int row = c / (KD / 4), col = (c % (KD / 4)) * 4;
+                *(typename Vec16<E>::t*)(s + row * LD + col) = v[i];
+            }
+        }
+    }
+};
+
+// Coalesced store of a [64][D] LDS tile (row pitch LD) to rows < C of a global
+// row block (row stride rs), 16 bytes per thread and instruction.
+template <class E, int D, int LD>
+__device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* s, int C) {
+    constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV;
+    for (int idx = threadIdx.x; idx < 64 * VPR; idx += 512) {
+        const int r = idx / VPR, c = idx % VPR;
+        if (r < C) *(typename Vec16<E>::t*)(g + r * rs + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
     }
 }
 
@@ -141,6 +222,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
     float* sRowB = sRowG + 4 * 64; // [4][64] row partials of dβ
     float* sCol = sRowB + 4 * 64;  // [2][64] column partials of dG per row half
     float* sMisc = sCol + 2 * 64;  // [16 + 64]
+    E* sDv = (E*)(smem + Cf::oDv);
 
     const int ci = blockIdx.x, hk = blockIdx.y, G = GT ? GT : HV / HK;
     const ChunkInfo ch = a.info[ci];
@@ -158,8 +240,13 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
     const E* dhT = (const E*)a.dhT;
     const E* beta = (const E*)a.beta;
 
-    g_load_rows<E, E, KD, LK>(sQ, q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-    g_load_rows<E, E, KD, LK>(sK, k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+    {
+        RowsReg<E, KD, LK> rq, rk;
+        rq.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        rk.load(k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        rq.store(sQ);
+        rk.store(sK);
+    }
 
     f32x4 dq_tot[2][TNK], dk_tot[2][TNK];
     zero_acc(dq_tot);
@@ -169,6 +256,15 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
     for (int hi = 0; hi < G; hi++) {
         const int hv = hk * G + hi;
         const long unit = (long)ci * HV + hv;
+        // this head's A and first value slice: loads in flight during Pm
+        RowsReg<E, 64, LA> rA;
+        StateReg<E, KD, LK> rH, rdH;
+        RowsReg<E, 64, LS> rdO, rV;
+        rA.load((const E*)a.A + unit * C * C, C, C);
+        rH.load(hT + unit * VD * KD, 0);
+        rdH.load(dhT + unit * VD * KD, 0);
+        rdO.load(dO + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
+        rV.load(v + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
         if (threadIdx.x < C) {
             const int r = threadIdx.x;
             const float gg = a.gcum[(t0 + min(r, Cn - 1)) * HV + hv];
@@ -202,9 +298,13 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                     sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][0][e] : 0.f);
                 }
         }
-        // ---- A = (I+L)^{-1} from the prep kernel
-        g_load_rows<E, E, 64, LA>(sA, (const E*)a.A + unit * C * C, C, C);
-        lds_barrier();
+        // ---- A = (I+L)^{-1} from the prep kernel, and the first slice
+        rA.store(sA);
+        rH.store(sH);
+        rdH.store(sdH);
+        rdO.store(sdO);
+        lds_barrier();   // Pm has read Q: the V slice may take its buffer
+        rV.store(sV);
 
         // persistent accumulators over the V slices
         f32x4 dPm[2][1], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][1];
@@ -216,11 +316,12 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
-            // h / dh slices are stored transposed: [V][K] per chunk -> rows v
-            g_load_state<E, KD, LK>(sH, hT + unit * VD * KD, vh * 64);
-            g_load_state<E, KD, LK>(sdH, dhT + unit * VD * KD, vh * 64);
-            g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
-            g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+            if (vh > 0) {   // h / dh slices as rows v of [V][K]
+                g_load_state<E, KD, LK>(sH, hT + unit * VD * KD, vh * 64);
+                g_load_state<E, KD, LK>(sdH, dhT + unit * VD * KD, vh * 64);
+                g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+                g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+            }
             lds_barrier();
             // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
             {
@@ -275,10 +376,12 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                     for (int e = 0; e < 4; e++) {
                         const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
                         rowB[i][e] += adv[i][0][e] * (float)sV[rr * LS + cc];
-                        if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
+                        if constexpr (Cf::DV_LDS) sDv[rr * LS + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
+                        else if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
                     }
             }
             lds_barrier();
+            if constexpr (Cf::DV_LDS) store_rows<E, 64, LS>((E*)a.dv + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, sDv, Cn);
         }
 
         // ---- Q back into its buffer (it held the V slices)
@@ -446,20 +549,20 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                 for (int i = 0; i < 8; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
                 dG += zs + gC * hd;
             }
-            sMisc[16 + rr] = dG;
             if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
-        }
-        lds_barrier();
-        if (threadIdx.x == 0) {   // in-chunk reverse cumulative sum
-            float acc = 0.f;
-            for (int rr = C - 1; rr >= 0; rr--) {
-                acc += sMisc[16 + rr];
-                if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = acc;
+            // in-chunk reverse cumulative sum (suffix sums over the 64 rows,
+            // one row per lane; padded rows carry the chunk-end terms)
+            float x = dG;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(x, off, 64);
+                x += rr + off < 64 ? y : 0.f;
             }
+            if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
         }
         lds_barrier();
     }
-    // ---- write the group sums dq, dk for this key head
+    // ---- the group sums dq, dk for this key head, through LDS (sH, sdH are free)
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -467,11 +570,12 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                if (rr < Cn) {
-                    ((E*)a.dq)[((t0 + rr) * HK + hk) * KD + cc] = to_e<E>(dq_tot[i][j][e]);
-                    ((E*)a.dk)[((t0 + rr) * HK + hk) * KD + cc] = to_e<E>(dk_tot[i][j][e]);
-                }
+                sH[rr * LK + cc] = to_e<E>(dq_tot[i][j][e]);
+                sdH[rr * LK + cc] = to_e<E>(dk_tot[i][j][e]);
             }
+    lds_barrier();
+    store_rows<E, KD, LK>((E*)a.dq + (t0 * HK + hk) * KD, (long)HK * KD, sH, Cn);
+    store_rows<E, KD, LK>((E*)a.dk + (t0 * HK + hk) * KD, (long)HK * KD, sdH, Cn);
 }
 
 template <class E, int KD, int VD, int GT>
