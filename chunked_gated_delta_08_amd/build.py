@@ -19,10 +19,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip"]
+# per-source device flags: the scan kernels keep MFMA accumulators in VGPRs;
+# the gradient kernel is left to the compiler's heuristics (its AGPR rewrite
+# is what keeps the 4-wave kernel free of spills)
+SOURCE_FLAGS = {"gdr_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "gdr_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HOST_SOURCES = ["gdr_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _run(cmd, verbose):
@@ -40,7 +45,7 @@ def build(verbose=False, jobs=None):
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        cmds.append([HIPCC] + COMMON + DEVICE + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + COMMON + DEVICE + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")

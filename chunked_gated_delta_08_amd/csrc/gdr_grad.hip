@@ -1,6 +1,6 @@
 // gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
 //
-// One workgroup (8 waves) per (chunk, key head); it loops over the value heads
+// One workgroup (4 waves) per (chunk, key head); it loops over the value heads
 // that share the key head and keeps the dq/dk group sums in registers (the
 // GQA reduction the FlashQLA backward explainer, §一 step ④, does in Python).
 // Given h = h[c] (state entering the chunk) and dh = dh[c] (gradient of the
@@ -34,11 +34,16 @@ namespace gdr {
 
 template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 8 : 4; }
 
+// 4 waves (one per SIMD, so each wave may use the whole register file): wave w
+// owns rows 32*(w&1) .. +31 and the column half (w>>1) of every output.
+constexpr int GNT = 256;
+
 template <class E, int KD, int VD>
 struct GradCfg {
     static constexpr int C = 64, VH = 64, NVH = VD / VH;
     static constexpr int LK = KD + gpad<E>(), LA = 64 + gpad<E>(), LS = VH + gpad<E>(), LF = 68;
-    static constexpr int TNK = KD / 64;      // 16-col tiles per wave for [64][KD] outputs
+    static constexpr int TNK = KD / 32;      // 16-col tiles per wave for [64][KD] outputs
+    static constexpr int TNS = 2;            // 16-col tiles per wave for [64][64] outputs
     // byte offsets.  The V slice lives in Q's buffer during the V loop (Q is
     // reloaded afterwards); after the loop the slice region holds dW, dA_pre,
     // M1 and Eb.
@@ -70,7 +75,7 @@ template <class Ein, class E, int D, int LD>
 __device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, long rs, int C, int rows = 64) {
     constexpr int EPV = 16 / sizeof(Ein);
     constexpr int VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < rows * VPR; idx += 512) {
+    for (int idx = threadIdx.x; idx < rows * VPR; idx += GNT) {
         const int r = idx / VPR, c = idx % VPR;
         typename Vec16<Ein>::t v;
         if (r < C) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
@@ -89,7 +94,7 @@ __device__ __forceinline__ void g_load_state(E* s, const E* __restrict__ blk, in
         typedef short s4 __attribute__((ext_vector_type(4)));
         typedef short s8 __attribute__((ext_vector_type(8)));
         const E* src = blk + (long)vc0 * KD;          // 64 columns = 4 contiguous [16 x KD] blocks
-        for (int c = threadIdx.x; c < 64 * KD / 8; c += 512) {
+        for (int c = threadIdx.x; c < 64 * KD / 8; c += GNT) {
             const int ln = c & 63, sblk = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
             const int row = 16 * cb + (ln & 15), key = 32 * sblk + 4 * (ln >> 4);
             const s8 v = *(const s8*)(src + (long)c * 8);
@@ -107,15 +112,15 @@ __device__ __forceinline__ void g_load_state(E* s, const E* __restrict__ blk, in
 // Splitting the two lets several blocks' loads be in flight together.
 template <class E, int D, int LD, int ROWS = 64>
 struct RowsReg {
-    static constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV, NV = ROWS * VPR, N = (NV + 511) / 512;
+    static constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV, NV = ROWS * VPR, N = (NV + GNT - 1) / GNT;
     typename Vec16<E>::t v[N];
     int C;
     __device__ __forceinline__ void load(const E* __restrict__ g, long rs, int Cn) {
         C = Cn;
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int idx = threadIdx.x + 512 * i;
-            if (NV % 512 == 0 || idx < NV) {
+            const int idx = threadIdx.x + GNT * i;
+            if (NV % GNT == 0 || idx < NV) {
                 const int r = min(idx / VPR, Cn - 1), c = idx % VPR;
                 v[i] = *(const typename Vec16<E>::t*)(g + r * rs + c * EPV);
             }
@@ -124,8 +129,8 @@ struct RowsReg {
     __device__ __forceinline__ void store(E* s) const {
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int idx = threadIdx.x + 512 * i;
-            if (NV % 512 == 0 || idx < NV) {
+            const int idx = threadIdx.x + GNT * i;
+            if (NV % GNT == 0 || idx < NV) {
                 const int r = idx / VPR, c = idx % VPR;
                 typename Vec16<E>::t x = v[i];
                 if (r >= C) x = typename Vec16<E>::t{};
@@ -141,17 +146,17 @@ struct RowsReg {
 template <class E, int KD, int LD>
 struct StateReg {
     static constexpr bool FRAG = sizeof(E) == 2;
-    static constexpr int N = 64 * KD * (int)sizeof(E) / 16 / 512;
+    static constexpr int N = 64 * KD * (int)sizeof(E) / 16 / GNT;
     typename Vec16<E>::t v[N];
     __device__ __forceinline__ void load(const E* __restrict__ blk, int vc0) {
         const E* src = blk + (long)vc0 * KD;   // 64 columns: contiguous in both layouts
 #pragma unroll
-        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(threadIdx.x + 512 * i) * (16 / sizeof(E)));
+        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(threadIdx.x + GNT * i) * (16 / sizeof(E)));
     }
     __device__ __forceinline__ void store(E* s) const {
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int c = threadIdx.x + 512 * i;
+            const int c = threadIdx.x + GNT * i;
             if constexpr (FRAG) {
                 typedef short s4 __attribute__((ext_vector_type(4)));
                 typedef short s8 __attribute__((ext_vector_type(8)));
@@ -173,7 +178,7 @@ struct StateReg {
 template <class E, int D, int LD>
 __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* s, int C) {
     constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < 64 * VPR; idx += 512) {
+    for (int idx = threadIdx.x; idx < 64 * VPR; idx += GNT) {
         const int r = idx / VPR, c = idx % VPR;
         if (r < C) *(typename Vec16<E>::t*)(g + r * rs + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
     }
@@ -194,12 +199,16 @@ __device__ __forceinline__ float sum4g(float x) {
     return x;
 }
 
-// GT: value heads per key head as a compile-time constant (0 = runtime); the
-// head and slice loops are unrolled so no addressing is hoisted across them.
+// GT: value heads per key head as a compile-time constant (1 or 2; the head
+// loop is then unrolled), or 0 for a runtime count.  With G > 1 the running group sums of dq and dk are not
+// kept in registers across value heads: after each head the workgroup adds
+// its fp32 partials into a private workspace block (fragment order, read back
+// and rewritten only by the lane that owns it), so the order of the sum is
+// fixed and the heavy per-head phases keep their registers.
 template <class E, int KD, int VD, int GT>
-__global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, float scale) {
+__global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, float scale) {
     using Cf = GradCfg<E, KD, VD>;
-    constexpr int C = 64, TNK = Cf::TNK, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, LF = Cf::LF;
+    constexpr int C = 64, TNK = Cf::TNK, TNS = Cf::TNS, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, LF = Cf::LF;
     extern __shared__ __align__(16) unsigned char smem[];
     E* sQ = (E*)(smem + Cf::oQ);
     E* sK = (E*)(smem + Cf::oK);
@@ -218,8 +227,8 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
     float* sG = (float*)(smem + Cf::oSm);
     float* sB = sG + 64;
     float* sGam = sB + 64;
-    float* sRowG = sGam + 64;      // [4][64] row partials of dG per column block
-    float* sRowB = sRowG + 4 * 64; // [4][64] row partials of dβ
+    float* sRowG = sGam + 64;      // [2][64] row partials of dG per column block (4 x 64 reserved)
+    float* sRowB = sRowG + 4 * 64; // [2][64] row partials of dβ
     float* sCol = sRowB + 4 * 64;  // [2][64] column partials of dG per row half
     float* sMisc = sCol + 2 * 64;  // [16 + 64]
     E* sDv = (E*)(smem + Cf::oDv);
@@ -230,8 +239,8 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
     const long t0 = ch.t0;
     const int w = wave_id(), l = lane_id(), r16 = l & 15, g4 = l >> 4;
     const int m0 = 32 * (w & 1);           // every output block of this wave starts at this row
-    const int n0s = 16 * (w >> 1);         // column block for [64][64] outputs
-    const int n0k = (KD / 4) * (w >> 1);   // column block for [64][KD] outputs
+    const int n0s = 32 * (w >> 1);         // column block for [64][64] outputs
+    const int n0k = (KD / 2) * (w >> 1);   // column block for [64][KD] outputs
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
@@ -248,9 +257,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         rk.store(sK);
     }
 
-    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];
-    zero_acc(dq_tot);
-    zero_acc(dk_tot);
+    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];   // this head's dq, dk (after the loop: the group sums)
 
 #pragma unroll
     for (int hi = 0; hi < G; hi++) {
@@ -276,26 +283,29 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         const float gl = sG[C - 1], gC = sGam[C - 1];
 
         // per-lane partial row sums (rows m0 + 16i + 4g4 + e) and column sums
-        float rowG[2][4], rowB[2][4], colG[1];
+        float rowG[2][4], rowB[2][4], colG[TNS];
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) rowG[i][e] = rowB[i][e] = 0.f;
-        colG[0] = 0.f;
+#pragma unroll
+        for (int j = 0; j < TNS; j++) colG[j] = 0.f;
         float hdh = 0.f;   // partial <dh, h>
 
         // ---- S_qk -> Pm = scale · lower(Γ ⊙ Q Kᵀ)
         {
-            f32x4 aqk[2][1];
+            f32x4 aqk[2][TNS];
             zero_acc(aqk);
-            wgemm<E, 2, 1, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
+            wgemm<E, 2, TNS, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
+                for (int j = 0; j < TNS; j++)
+#pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
                     const float gm = (cc <= rr) ? __expf(sG[rr] - sG[cc]) : 0.f;
-                    sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][0][e] : 0.f);
+                    sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][j][e] : 0.f);
                 }
         }
         // ---- A = (I+L)^{-1} from the prep kernel, and the first slice
@@ -307,7 +317,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         rV.store(sV);
 
         // persistent accumulators over the V slices
-        f32x4 dPm[2][1], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][1];
+        f32x4 dPm[2][TNS], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][TNS];
         zero_acc(dPm);
         zero_acc(dqi);
         zero_acc(dWa);
@@ -325,59 +335,65 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
             lds_barrier();
             // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
             {
-                f32x4 kh[2][1], kdh[2][1], pdo[2][1];
+                f32x4 kh[2][TNS], kdh[2][TNS], pdo[2][TNS];
                 zero_acc(kh);
                 zero_acc(kdh);
                 zero_acc(pdo);
-                wgemm<E, 2, 1, KD, false, false>(kh, sK, LK, sH, LK, m0, n0s);
-                wgemm<E, 2, 1, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0s);
-                wgemm<E, 2, 1, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0s);
+                wgemm<E, 2, TNS, KD, false, false>(kh, sK, LK, sH, LK, m0, n0s);
+                wgemm<E, 2, TNS, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0s);
+                wgemm<E, 2, TNS, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0s);
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
+                    for (int j = 0; j < TNS; j++)
+#pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
-                        const float z = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]);
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
+                        const float z = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][j][e]);
                         sVn[rr * LS + cc] = to_e<E>(z);
-                        sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + __expf(gl - sG[rr]) * kdh[i][0][e]);
+                        sdVn[rr * LS + cc] = to_e<E>(pdo[i][j][e] + __expf(gl - sG[rr]) * kdh[i][j][e]);
                     }
             }
             // <dh, h> over this slice
-            for (int idx = threadIdx.x; idx < 64 * KD; idx += 512) {
+            for (int idx = threadIdx.x; idx < 64 * KD; idx += GNT) {
                 const int rr = idx / KD, cc = idx % KD;
                 hdh += (float)sH[rr * LK + cc] * (float)sdH[rr * LK + cc];
             }
             lds_barrier();
             // ---- V_new = A Z
             {
-                f32x4 vn[2][1];
+                f32x4 vn[2][TNS];
                 zero_acc(vn);
-                wgemm<E, 2, 1, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
+                wgemm<E, 2, TNS, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
                 lds_barrier();
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) sVn[acc_row(m0, i, e) * LS + acc_col(n0s, 0)] = to_e<E>(vn[i][0][e]);
+                    for (int j = 0; j < TNS; j++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) sVn[acc_row(m0, i, e) * LS + acc_col(n0s, j)] = to_e<E>(vn[i][j][e]);
             }
             lds_barrier();
             // ---- accumulate the state products and the V-separable outputs
-            wgemm<E, 2, 1, 64, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);     // dO V_newᵀ
+            wgemm<E, 2, TNS, 64, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);     // dO V_newᵀ
             wgemm<E, 2, TNK, 64, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);    // dO hᵀ
             wgemm<E, 2, TNK, 64, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);   // dV_new hᵀ
             wgemm<E, 2, TNK, 64, false, true>(dks, sVn, LS, sdH, LK, m0, n0k);   // V_new dhᵀ
-            wgemm<E, 2, 1, 64, false, false>(dAp, sdVn, LS, sV, LS, m0, n0s);     // dV_new Vᵀ
+            wgemm<E, 2, TNS, 64, false, false>(dAp, sdVn, LS, sV, LS, m0, n0s);     // dV_new Vᵀ
             {
-                f32x4 adv[2][1];
+                f32x4 adv[2][TNS];
                 zero_acc(adv);
-                wgemm<E, 2, 1, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0s);    // Aᵀ dV_new
+                wgemm<E, 2, TNS, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0s);    // Aᵀ dV_new
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
+                    for (int j = 0; j < TNS; j++)
+#pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
-                        rowB[i][e] += adv[i][0][e] * (float)sV[rr * LS + cc];
-                        if constexpr (Cf::DV_LDS) sDv[rr * LS + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
-                        else if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][0][e]);
+                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
+                        rowB[i][e] += adv[i][j][e] * (float)sV[rr * LS + cc];
+                        if constexpr (Cf::DV_LDS) sDv[rr * LS + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
+                        else if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
                     }
             }
             lds_barrier();
@@ -390,13 +406,15 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
+            for (int j = 0; j < TNS; j++)
+#pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
                 const bool lo = cc <= rr;
-                const float dp = lo ? dPm[i][0][e] : 0.f;
+                const float dp = lo ? dPm[i][j][e] : 0.f;
                 const float f = dp * (float)sPm[rr * LA + cc];
                 rowG[i][e] += f;
-                colG[0] += f;
+                colG[j] += f;
                 sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
             }
 #pragma unroll
@@ -422,7 +440,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                         const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
                         const float di = scale * sGam[rr] * dqi[i][j][e];
                         rowG[i][e] += di * (float)sQ[rr * LK + cc];
-                        dq_tot[i][j][e] += di + t1k[i][j][e];
+                        dq_tot[i][j][e] = di + t1k[i][j][e];
                     }
         }
         // ---- dk: T1ᵀ Q + diag(γ_C/γ) V_new dhᵀ (z terms) + diag(βγ) Aᵀ dW
@@ -449,53 +467,59 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                         const float aw = adw[i][j][e] * kv;
                         rowB[i][e] += sGam[rr] * aw;
                         rowG[i][e] += sB[rr] * sGam[rr] * aw;
-                        dk_tot[i][j][e] += acc[i][j][e] + ds + sB[rr] * sGam[rr] * adw[i][j][e];
+                        dk_tot[i][j][e] = acc[i][j][e] + ds + sB[rr] * sGam[rr] * adw[i][j][e];
                     }
         }
         // ---- dA_pre = dV_new (diag(β)V)ᵀ + dW (diag(βγ)K)ᵀ  -> LDS
         {
-            f32x4 dwk[2][1];
+            f32x4 dwk[2][TNS];
             zero_acc(dwk);
-            wgemm<E, 2, 1, KD, false, false>(dwk, sdW, LK, sK, LK, m0, n0s);
+            wgemm<E, 2, TNS, KD, false, false>(dwk, sdW, LK, sK, LK, m0, n0s);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
+                for (int j = 0; j < TNS; j++)
+#pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
-                    sdA[rr * LA + cc] = to_e<E>(sB[cc] * (dAp[i][0][e] + sGam[cc] * dwk[i][0][e]));
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
+                    sdA[rr * LA + cc] = to_e<E>(sB[cc] * (dAp[i][j][e] + sGam[cc] * dwk[i][j][e]));
                 }
         }
         lds_barrier();
         // ---- M1 = Aᵀ dA_pre
         {
-            f32x4 m1[2][1];
+            f32x4 m1[2][TNS];
             zero_acc(m1);
-            wgemm<E, 2, 1, 64, true, true>(m1, sA, LA, sdA, LA, m0, n0s);
+            wgemm<E, 2, TNS, 64, true, true>(m1, sA, LA, sdA, LA, m0, n0s);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) sM1[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = to_e<E>(m1[i][0][e]);
+                for (int j = 0; j < TNS; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sM1[acc_row(m0, i, e) * LA + acc_col(n0s, j)] = to_e<E>(m1[i][j][e]);
         }
         lds_barrier();
         // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ
         {
-            f32x4 dl[2][1], akk[2][1];
+            f32x4 dl[2][TNS], akk[2][TNS];
             zero_acc(dl);
             zero_acc(akk);
-            wgemm<E, 2, 1, 64, false, false>(dl, sM1, LA, sA, LA, m0, n0s);
-            wgemm<E, 2, 1, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
+            wgemm<E, 2, TNS, 64, false, false>(dl, sM1, LA, sA, LA, m0, n0s);
+            wgemm<E, 2, TNS, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
+                for (int j = 0; j < TNS; j++)
+#pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
+                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
                     const bool lo = cc < rr;
-                    const float d = lo ? -dl[i][0][e] : 0.f;
-                    const float lg = lo ? __expf(sG[rr] - sG[cc]) * akk[i][0][e] : 0.f;   // Γ ⊙ KKᵀ
+                    const float d = lo ? -dl[i][j][e] : 0.f;
+                    const float lg = lo ? __expf(sG[rr] - sG[cc]) * akk[i][j][e] : 0.f;   // Γ ⊙ KKᵀ
                     rowB[i][e] += d * lg;
                     const float f2 = d * sB[rr] * lg;
                     rowG[i][e] += f2;
-                    colG[0] += f2;
+                    colG[j] += f2;
                     sEb[rr * LA + cc] = to_e<E>(lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f);
                 }
         }
@@ -513,7 +537,7 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         }
 
         // ---- reductions (fixed order): rows over the 16 lanes of a group and
-        // the four column blocks; columns over the 4 row groups and 2 row halves
+        // the two column blocks; columns over the 4 row groups and 2 row halves
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -526,9 +550,10 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                     sRowB[(w >> 1) * 64 + rr] = rb;
                 }
             }
-        {
-            const float cs = sum4g(colG[0]);
-            if (g4 == 0) sCol[(w & 1) * 64 + acc_col(n0s, 0)] = cs;
+#pragma unroll
+        for (int j = 0; j < TNS; j++) {
+            const float cs = sum4g(colG[j]);
+            if (g4 == 0) sCol[(w & 1) * 64 + acc_col(n0s, j)] = cs;
         }
         {
             float hz = hdh, zz = zsum;
@@ -542,11 +567,11 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
         lds_barrier();
         if (threadIdx.x < 64) {
             const int rr = threadIdx.x;
-            float dG = (sRowG[rr] + sRowG[64 + rr] + sRowG[128 + rr] + sRowG[192 + rr]) - (sCol[rr] + sCol[64 + rr]);
-            const float db = sRowB[rr] + sRowB[64 + rr] + sRowB[128 + rr] + sRowB[192 + rr];
+            float dG = (sRowG[rr] + sRowG[64 + rr]) - (sCol[rr] + sCol[64 + rr]);
+            const float db = sRowB[rr] + sRowB[64 + rr];
             if (rr == C - 1) {
                 float hd = 0.f, zs = 0.f;
-                for (int i = 0; i < 8; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
+                for (int i = 0; i < GNT / 64; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
                 dG += zs + gC * hd;
             }
             if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
@@ -559,6 +584,25 @@ __global__ void __launch_bounds__(512) grad_kernel(GradArgs a, int HK, int HV, f
                 x += rr + off < 64 ? y : 0.f;
             }
             if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
+        }
+        if (GT != 1) {   // group sums through the workspace block of this (chunk, key head)
+            float* st = a.gsum + ((long)ci * HK + hk) * 2 * 64 * KD;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < TNK; j++) {
+                    const int tl = (w * 2 + i) * TNK + j;
+                    f32x4* pq = (f32x4*)(st + (tl * 64 + l) * 4);
+                    f32x4* pk = (f32x4*)(st + 64 * KD + (tl * 64 + l) * 4);
+                    if (hi > 0) {
+                        dq_tot[i][j] += *pq;
+                        dk_tot[i][j] += *pk;
+                    }
+                    if (hi + 1 < G) {
+                        *pq = dq_tot[i][j];
+                        *pk = dk_tot[i][j];
+                    }
+                }
         }
         lds_barrier();
     }
@@ -585,15 +629,15 @@ static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
     auto kern = grad_kernel<E, KD, VD, GT>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(512), Cf::smem, s, a, p.HK, p.HV, p.scale);
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale);
     return hipGetLastError();
 }
 
 template <class E, int KD, int VD>
 static hipError_t grad_go(const Problem& p, const GradArgs& a, hipStream_t s) {
-    const int G = p.HV / p.HK;
-    if (G == 1) return grad_go1<E, KD, VD, 1>(p, a, s);
-    if (G == 2) return grad_go1<E, KD, VD, 2>(p, a, s);
+    if (p.HV == p.HK) return grad_go1<E, KD, VD, 1>(p, a, s);
+    if (!a.gsum) return hipErrorInvalidValue;
+    if (p.HV == 2 * p.HK) return grad_go1<E, KD, VD, 2>(p, a, s);
     return grad_go1<E, KD, VD, 0>(p, a, s);
 }
 

@@ -41,7 +41,7 @@ struct Problem {
 // the fp32 fragment order below) are empty when maxS == 1.
 struct WsPlan {
     size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
-    size_t hloc, dhloc, P, hstart, dhin, total;
+    size_t hloc, dhloc, P, hstart, dhin, gsum, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
@@ -102,6 +102,7 @@ struct GradArgs {
     const void* q; const void* k; const void* v; const float* gcum; const void* beta; const void* dO;
     const void* hT; const void* dhT; const void* A; const ChunkInfo* info;
     void* dq; void* dk; void* dv; float* dg; float* dbeta;
+    float* gsum;   // HV > HK: fp32 group-sum blocks, [NT][HK][2][64*K] (fragment order)
 };
 hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s);
 
