@@ -110,22 +110,6 @@ hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_ch
 }
 
 // ---------------------------------------------------------------- helpers
-// Cooperative copy of a [C][D] row block (row stride `rs` elements) into a
-// zero-padded [64][LD] LDS tile, converting element type Ein -> Eout.
-template <class Ein, class Eout, int D, int LD, int NTHR>
-__device__ __forceinline__ void load_rows(Eout* s, const Ein* __restrict__ g, long rs, int C) {
-    constexpr int EPV = 16 / sizeof(Ein);  // elements per 16-byte vector
-    constexpr int VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < 64 * VPR; idx += NTHR) {
-        const int r = idx / VPR, c = idx % VPR;
-        typename Vec16<Ein>::t v;
-        if (r < C) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
-        else v = typename Vec16<Ein>::t{};
-#pragma unroll
-        for (int e = 0; e < EPV; e++) s[r * LD + c * EPV + e] = (Eout)(float)v[e];
-    }
-}
-
 // Copy a [64][D] LDS tile (rows < C) out to a dense row-major [64][D] block.
 template <class E, int D, int LD, int NTHR>
 __device__ __forceinline__ void store_tile_dense(E* __restrict__ g, const E* s) {
@@ -143,6 +127,132 @@ __device__ __forceinline__ void store_tile_dense(E* __restrict__ g, const E* s) 
 template <class E> constexpr int pad_of() { return sizeof(E) == 2 ? 8 : 4; }
 
 // ---------------------------------------------------------------- K1a
+// LDS carve-up of the WY-factor kernel (byte offsets).
+template <class E, class S, int KD, int VD>
+struct PrepCfg {
+    static constexpr int C = 64;
+    static constexpr int LK = KD + pad_of<S>(), LV = VD + pad_of<S>(), LA = 64 + pad_of<S>(), LL = 68;
+    static constexpr size_t oK = 0;                                          // K     [64][LK] S (later R)
+    static constexpr size_t oV = oK + (size_t)C * LK * sizeof(S);            // V     [64][LV] S (later U)
+    static constexpr size_t oQ = oV + (size_t)C * LV * sizeof(S);            // Q     [64][LK] S
+    static constexpr size_t oL = oQ + (size_t)C * LK * sizeof(S);            // L     [64][LL] fp32 (later W [64][LK] S)
+    static constexpr size_t oAf = oL + (size_t)C * LL * 4;                   // A     [64][LL] fp32
+    static constexpr size_t oAw = oAf + (size_t)C * LL * 4;                  // A diag(βγ) [64][LA] S
+    static constexpr size_t oAu = oAw + (size_t)C * LA * sizeof(S);          // A diag(β)  [64][LA] S
+    static constexpr size_t oPm = oAu + (size_t)C * LA * sizeof(S);          // Pm    [64][LA] S
+    static constexpr size_t oT = oPm + (size_t)C * LA * sizeof(S);           // 4 waves x 2 blocks [16][17] fp32
+    static constexpr size_t oG = oT + (size_t)4 * 2 * 16 * 17 * 4;           // G, β [64] fp32
+    static constexpr size_t smem = oG + (size_t)2 * C * 4;
+    static_assert((size_t)C * LK * sizeof(S) <= (size_t)C * LL * 4, "W aliases L");
+    static_assert(smem <= 160 * 1024, "LDS budget");
+};
+
+// acc += X · Y for 16 x 16 fp32 blocks held row-major in LDS (fp32 MFMA, exact
+// products): lane (r, g) feeds X[r][4s+g] and Y[4s+g][r] and holds
+// (X·Y)[4g+j][r] in acc[j].
+__device__ __forceinline__ void mm16(f32x4& acc, const float* X, int ldx, const float* Y, int ldy) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; s++) acc = Mma<float>::run(X[r * ldx + 4 * s + g], Y[(4 * s + g) * ldy + r], acc);
+}
+__device__ __forceinline__ void put16(float* Z, int ldz, const f32x4& acc, float sgn) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; j++) Z[(4 * g + j) * ldz + r] = sgn * acc[j];
+}
+
+// A = (I + L)^{-1} for the strictly lower 64 x 64 L in sL (fp32, pitch LL),
+// written to sAf (fp32, pitch LL) by the four waves together.  With 16 x 16
+// blocks, D_i = (I + L_ii)^{-1} and A_ij = −D_i Σ_{j<=k<i} L_ik A_kj:
+//   step 1: wave w inverts D_w by forward substitution (one lane per column);
+//   step 2: A_10 = −D_1 L_10 D_0 and A_32 = −D_3 L_32 D_2; meanwhile
+//           Y01 = L_21 D_1 and Y11 = L_31 D_1;
+//   step 3: with Y00 = L_20 D_0 + L_21 A_10 and Y10 = L_30 D_0 + L_31 A_10,
+//           A_20 = −D_2 Y00, A_21 = −D_2 Y01, A_30 = −(A_32 Y00 + D_3 Y10),
+//           A_31 = −(A_32 Y01 + D_3 Y11)   (one block per wave).
+// The block products are fp32 MFMAs on LDS operands; sT holds two [16][17]
+// scratch blocks per wave.
+template <int LL>
+__device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float* sT) {
+    const int w = wave_id(), l = lane_id();
+    constexpr int LT = 17;
+    float* t0 = sT + w * 2 * 16 * LT;
+    float* t1 = t0 + 16 * LT;
+    auto Lb = [&](int i, int j) { return sL + 16 * i * LL + 16 * j; };
+    auto Ab = [&](int i, int j) { return sAf + 16 * i * LL + 16 * j; };
+    // step 1 (+ zero the blocks above the diagonal)
+    if (l < 16) {
+        const float* L = Lb(w, w);
+        float a[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float acc = r == l ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; s++) acc -= L[r * LL + s] * a[s];
+            a[r] = acc;
+        }
+        float* D = Ab(w, w);
+#pragma unroll
+        for (int r = 0; r < 16; r++) D[r * LL + l] = a[r];
+    }
+    for (int idx = threadIdx.x; idx < 6 * 256; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2), bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        Ab(bi, bj)[(e >> 4) * LL + (e & 15)] = 0.f;
+    }
+    lds_barrier();
+    // step 2
+    {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (w < 2) {
+            const int i = 2 * w + 1, j = 2 * w;            // (1,0) or (3,2)
+            mm16(acc, Lb(i, j), LL, Ab(j, j), LL);
+            put16(t0, LT, acc, 1.f);
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            mm16(acc, Ab(i, i), LL, t0, LT);
+            put16(Ab(i, j), LL, acc, -1.f);
+        } else {
+            mm16(acc, Lb(w, 1), LL, Ab(1, 1), LL);         // Y01 = L_21 D_1 or Y11 = L_31 D_1
+            put16(t0, LT, acc, 1.f);
+        }
+    }
+    lds_barrier();
+    // step 3: wave w -> block (2 + (w >> 1), w & 1).  LDS operations of one
+    // wave execute in order, so a wave may rewrite its own scratch block right
+    // after reading it.
+    {
+        const float* Y01 = sT + 2 * 2 * 16 * LT;   // wave 2's first block
+        const float* Y11 = sT + 3 * 2 * 16 * LT;   // wave 3's first block
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (w == 0 || w == 2) {
+            mm16(acc, Lb(2, 0), LL, Ab(0, 0), LL);   // Y00 = L_20 D_0 + L_21 A_10
+            mm16(acc, Lb(2, 1), LL, Ab(1, 0), LL);
+            put16(t1, LT, acc, 1.f);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (w == 0) {
+                mm16(x, Ab(2, 2), LL, t1, LT);       // A_20 = −D_2 Y00
+                put16(Ab(2, 0), LL, x, -1.f);
+            } else {
+                mm16(x, Ab(3, 2), LL, t1, LT);       // A_32 Y00
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                mm16(acc, Lb(3, 0), LL, Ab(0, 0), LL);   // Y10 = L_30 D_0 + L_31 A_10
+                mm16(acc, Lb(3, 1), LL, Ab(1, 0), LL);
+                put16(t1, LT, acc, 1.f);
+                mm16(x, Ab(3, 3), LL, t1, LT);       // + D_3 Y10
+                put16(Ab(3, 0), LL, x, -1.f);        // A_30
+            }
+        } else if (w == 1) {
+            mm16(acc, Ab(2, 2), LL, Y01, LT);        // A_21 = −D_2 Y01
+            put16(Ab(2, 1), LL, acc, -1.f);
+        } else {
+            mm16(acc, Ab(3, 2), LL, Y01, LT);        // A_31 = −(A_32 Y01 + D_3 Y11)
+            mm16(acc, Ab(3, 3), LL, Y11, LT);
+            put16(Ab(3, 1), LL, acc, -1.f);
+        }
+    }
+    lds_barrier();
+}
+
 // Grid (NT, HV), 256 threads.  E: input type; S: scan operand type.
 template <class E, class S, int KD, int VD, bool WITH_R>
 __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
@@ -152,45 +262,89 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                                                    S* __restrict__ Ug, S* __restrict__ Rg, E* __restrict__ Ag,
                                                    S* __restrict__ KTg) {
     static_assert(sizeof(E) == sizeof(S), "input and scan types share a width");
-    constexpr int C = 64, NTHR = 256;
-    constexpr int LK = KD + pad_of<E>(), LV = VD + pad_of<E>(), LA = 64 + pad_of<E>(), LL = 68;
+    using Cf = PrepCfg<E, S, KD, VD>;
+    constexpr int C = 64, NTHR = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
+    constexpr int EPV = 16 / (int)sizeof(E);
     extern __shared__ __align__(16) unsigned char smem[];
-    E* sK = (E*)smem;                       // K, later Kb = diag(βγ)K (type S)
-    E* sV = sK + C * LK;                    // V, later Vb = diag(β)V (type S), later U
-    E* sQ = sV + C * LV;                    // Q
-    float* sL = (float*)(sQ + C * LK);      // L (fp32), later W (type S)
-    constexpr int LW_BYTES = (C * LL * 4 > C * LK * (int)sizeof(S)) ? C * LL * 4 : C * LK * (int)sizeof(S);
-    S* sA = (S*)((unsigned char*)sL + LW_BYTES);
-    S* sPm = sA + C * LA;
-    float* sG = (float*)(sPm + C * LA);
+    S* sK = (S*)(smem + Cf::oK);
+    S* sV = (S*)(smem + Cf::oV);
+    S* sQ = (S*)(smem + Cf::oQ);
+    float* sL = (float*)(smem + Cf::oL);
+    S* sW = (S*)(smem + Cf::oL);
+    float* sAf = (float*)(smem + Cf::oAf);
+    S* sAw = (S*)(smem + Cf::oAw);
+    S* sAu = (S*)(smem + Cf::oAu);
+    S* sPm = (S*)(smem + Cf::oPm);
+    float* sT = (float*)(smem + Cf::oT);
+    float* sG = (float*)(smem + Cf::oG);
     float* sB = sG + C;
-    S* sW = (S*)sL;
 
     const int ci = blockIdx.x, hv = blockIdx.y, hk = hv / (HV / HK);
     const ChunkInfo ch = info[ci];
     const int Cn = ch.len;
     const long t0 = ch.t0;
-    const int w = wave_id(), l = lane_id();
+    const int w = wave_id();
+    const long unit = (long)ci * HV + hv;
 
-    load_rows<E, E, KD, LK, NTHR>(sK, k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-    load_rows<E, E, VD, LV, NTHR>(sV, v + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
-    if (WITH_R) load_rows<E, E, KD, LK, NTHR>(sQ, q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+    // ---- loads: every 16-byte vector of K, V, Q in flight together (rows past
+    // the chunk read its last row and are zeroed when staged)
+    constexpr int NKV = C * KD / EPV / NTHR, NVV = C * VD / EPV / NTHR;
+    typename Vec16<E>::t rk[NKV], rv[NVV], rq[WITH_R ? NKV : 1];
+#pragma unroll
+    for (int i = 0; i < NKV; i++) {
+        const int idx = threadIdx.x + NTHR * i, r = min(idx / (KD / EPV), Cn - 1), c = idx % (KD / EPV);
+        rk[i] = *(const typename Vec16<E>::t*)(k + ((t0 + r) * HK + hk) * KD + c * EPV);
+        if constexpr (WITH_R) rq[i] = *(const typename Vec16<E>::t*)(q + ((t0 + r) * HK + hk) * KD + c * EPV);
+    }
+#pragma unroll
+    for (int i = 0; i < NVV; i++) {
+        const int idx = threadIdx.x + NTHR * i, r = min(idx / (VD / EPV), Cn - 1), c = idx % (VD / EPV);
+        rv[i] = *(const typename Vec16<E>::t*)(v + ((t0 + r) * HV + hv) * VD + c * EPV);
+    }
     if (threadIdx.x < C) {
         const int r = threadIdx.x;
         sG[r] = gcum[(t0 + min(r, Cn - 1)) * HV + hv];
         sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
     }
+    auto to_s = [](const typename Vec16<E>::t& x, float f, bool keep) {
+        typename Vec16<S>::t y;
+#pragma unroll
+        for (int e = 0; e < EPV; e++) y[e] = keep ? (S)(f * (float)x[e]) : (S)0.f;
+        return y;
+    };
+#pragma unroll
+    for (int i = 0; i < NKV; i++) {
+        const int idx = threadIdx.x + NTHR * i, r = idx / (KD / EPV), c = idx % (KD / EPV);
+        *(typename Vec16<S>::t*)(sK + r * LK + c * EPV) = to_s(rk[i], 1.f, r < Cn);
+        if constexpr (WITH_R) *(typename Vec16<S>::t*)(sQ + r * LK + c * EPV) = to_s(rq[i], 1.f, r < Cn);
+    }
+#pragma unroll
+    for (int i = 0; i < NVV; i++) {
+        const int idx = threadIdx.x + NTHR * i, r = idx / (VD / EPV), c = idx % (VD / EPV);
+        *(typename Vec16<S>::t*)(sV + r * LV + c * EPV) = to_s(rv[i], 1.f, r < Cn);
+    }
     lds_barrier();
+
+    // ---- K̃ = diag(γ_C/γ) K straight from the registers
+    {
+        const float gl = sG[C - 1];
+        S* KTo = KTg + unit * C * KD;
+#pragma unroll
+        for (int i = 0; i < NKV; i++) {
+            const int idx = threadIdx.x + NTHR * i, r = idx / (KD / EPV), c = idx % (KD / EPV);
+            *(typename Vec16<S>::t*)(KTo + r * KD + c * EPV) = to_s(rk[i], __expf(gl - sG[r]), r < Cn);
+        }
+    }
 
     // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32x32 block)
     {
         const int m0 = 32 * (w & 1), n0 = 32 * (w >> 1);
         f32x4 akk[2][2], aqk[2][2];
         zero_acc(akk);
-        wgemm<E, 2, 2, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
+        wgemm<S, 2, 2, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
         if (WITH_R) {
             zero_acc(aqk);
-            wgemm<E, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+            wgemm<S, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
         }
 #pragma unroll
         for (int i = 0; i < 2; i++)
@@ -206,50 +360,38 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     }
     lds_barrier();
 
-    // ---- A = (I+L)^{-1} (wave 0, lane j owns column j); other waves scale K, V
-    if (w == 0) {
-        float a[C];
+    // ---- A = (I+L)^{-1}
+    tri_inverse64<LL>(sL, sAf, sT);
+
+    // ---- A diag(βγ), A diag(β) as MFMA operands; A itself to memory (input type)
+    {
+        E* Ao = Ag ? Ag + unit * C * C : nullptr;
+        for (int idx = threadIdx.x; idx < C * C / EPV; idx += NTHR) {
+            const int r = idx / (C / EPV), c0 = (idx % (C / EPV)) * EPV;
+            typename Vec16<S>::t aw, au;
+            typename Vec16<E>::t ao;
 #pragma unroll
-        for (int r = 0; r < C; r++) {
-            float acc = (r == l) ? 1.f : 0.f;
-            const float* Lr = sL + r * LL;
-#pragma unroll
-            for (int s = 0; s < r; s++) acc -= Lr[s] * a[s];
-            a[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < C; r++) sA[r * LA + l] = to_e<S>(a[r]);
-        if (Ag) {
-            E* Ao = Ag + ((long)ci * HV + hv) * C * C;
-#pragma unroll
-            for (int r = 0; r < C; r++) Ao[r * C + l] = to_e<E>(a[r]);
-        }
-    } else {
-        // Kb = diag(βγ) K written in place as type S; K̃ = diag(γ_C/γ) K to memory
-        S* KTo = KTg + ((long)ci * HV + hv) * C * KD;
-        for (int idx = threadIdx.x - 64; idx < C * KD; idx += NTHR - 64) {
-            const int r = idx / KD, c = idx % KD;
-            const float f = sB[r] * __expf(sG[r]);
-            const float x = (float)sK[r * LK + c];
-            KTo[r * KD + c] = to_e<S>(__expf(sG[C - 1] - sG[r]) * x);
-            ((S*)sK)[r * LK + c] = to_e<S>(f * x);
-        }
-        for (int idx = threadIdx.x - 64; idx < C * VD; idx += NTHR - 64) {
-            const int r = idx / VD, c = idx % VD;
-            const float x = (float)sV[r * LV + c];
-            ((S*)sV)[r * LV + c] = to_e<S>(sB[r] * x);
+            for (int e = 0; e < EPV; e++) {
+                const float x = sAf[r * LL + c0 + e], b = sB[c0 + e];
+                aw[e] = (S)(x * b * __expf(sG[c0 + e]));
+                au[e] = (S)(x * b);
+                ao[e] = (E)x;
+            }
+            *(typename Vec16<S>::t*)(sAw + r * LA + c0) = aw;
+            *(typename Vec16<S>::t*)(sAu + r * LA + c0) = au;
+            if (Ao) *(typename Vec16<E>::t*)(Ao + r * C + c0) = ao;
         }
     }
     lds_barrier();
 
-    // ---- W = A Kb, U = A Vb      (wave w: all 64 rows, KD/4 resp. VD/4 columns)
+    // ---- W = A diag(βγ) K, U = A diag(β) V     (wave w: all 64 rows, KD/4 resp. VD/4 columns)
     constexpr int TNK = KD / 64, TNV = VD / 64;
     f32x4 aw[4][TNK], au[4][TNV];
     zero_acc(aw);
     zero_acc(au);
-    wgemm<S, 4, TNK, 64, false, true>(aw, sA, LA, (const S*)sK, LK, 0, w * (KD / 4));
-    wgemm<S, 4, TNV, 64, false, true>(au, sA, LA, (const S*)sV, LV, 0, w * (VD / 4));
-    lds_barrier();
+    wgemm<S, 4, TNK, 64, false, true>(aw, sAw, LA, sK, LK, 0, w * (KD / 4));
+    wgemm<S, 4, TNV, 64, false, true>(au, sAu, LA, sV, LV, 0, w * (VD / 4));
+    lds_barrier();   // V is overwritten by U below
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -258,20 +400,18 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
 #pragma unroll
             for (int j = 0; j < TNK; j++) sW[r * LK + acc_col(w * (KD / 4), j)] = to_e<S>(aw[i][j][e]);
 #pragma unroll
-            for (int j = 0; j < TNV; j++) ((S*)sV)[r * LV + acc_col(w * (VD / 4), j)] = to_e<S>(au[i][j][e]);
+            for (int j = 0; j < TNV; j++) sV[r * LV + acc_col(w * (VD / 4), j)] = to_e<S>(au[i][j][e]);
         }
     lds_barrier();
 
-    const long unit = (long)ci * HV + hv;
     if (WITH_R) {
         // ---- R = scale diag(γ) Q − Pm W
         f32x4 ar[4][TNK];
         zero_acc(ar);
         wgemm<S, 4, TNK, 64, false, true>(ar, sPm, LA, sW, LK, 0, w * (KD / 4));
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
-        store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, (const S*)sV);
-        lds_barrier();
-        S* sR = (S*)sK;
+        store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, sV);
+        S* sR = sK;   // K is no longer read
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -288,16 +428,13 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
         store_tile_dense<S, KD, LK, NTHR>(Rg + unit * C * KD, sR);
     } else {
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
-        store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, (const S*)sV);
+        store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, sV);
     }
 }
 
 template <class E, class S, int KD, int VD>
 static size_t prep_smem() {
-    constexpr int C = 64, LK = KD + pad_of<E>(), LV = VD + pad_of<E>(), LA = 64 + pad_of<E>(), LL = 68;
-    constexpr int LW_BYTES = (C * LL * 4 > C * LK * (int)sizeof(S)) ? C * LL * 4 : C * LK * (int)sizeof(S);
-    return (size_t)C * LK * sizeof(E) * 2 + (size_t)C * LV * sizeof(E) + LW_BYTES + 2 * (size_t)C * LA * sizeof(S) +
-           2 * C * sizeof(float);
+    return PrepCfg<E, S, KD, VD>::smem;
 }
 
 template <class E, class S, int KD, int VD>
