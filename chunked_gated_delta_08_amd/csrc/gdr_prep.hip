@@ -110,12 +110,17 @@ hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_ch
 }
 
 // ---------------------------------------------------------------- helpers
-// Copy a [64][D] LDS tile (rows < C) out to a dense row-major [64][D] block.
+// Copy a [64][D] LDS tile out to a dense row-major [64][D] block.  Every
+// thread issues the same fixed number of 16-byte stores, so the compiler can
+// count them and later waits on loads need not wait for these stores.
 template <class E, int D, int LD, int NTHR>
 __device__ __forceinline__ void store_tile_dense(E* __restrict__ g, const E* s) {
     constexpr int EPV = 16 / sizeof(E);
     constexpr int VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < 64 * VPR; idx += NTHR) {
+    static_assert(64 * VPR % NTHR == 0, "whole vectors per thread");
+#pragma unroll
+    for (int it = 0; it < 64 * VPR / NTHR; it++) {
+        const int idx = threadIdx.x + NTHR * it;
         const int r = idx / VPR, c = idx % VPR;
         typename Vec16<E>::t v;
 #pragma unroll
@@ -253,14 +258,17 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
     lds_barrier();
 }
 
-// Grid (NT, HV), 256 threads.  E: input type; S: scan operand type.
+// Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...;
+// 256 threads.  The next unit's K, V, Q, gate and β are loaded into registers
+// right after the current ones are staged in LDS, so those loads are in flight
+// while the current unit is computed.  E: input type; S: scan operand type.
 template <class E, class S, int KD, int VD, bool WITH_R>
 __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const float* __restrict__ gcum,
                                                    const E* __restrict__ beta, const ChunkInfo* __restrict__ info,
                                                    int HK, int HV, float scale, S* __restrict__ Wg,
                                                    S* __restrict__ Ug, S* __restrict__ Rg, E* __restrict__ Ag,
-                                                   S* __restrict__ KTg) {
+                                                   S* __restrict__ KTg, int nunits) {
     static_assert(sizeof(E) == sizeof(S), "input and scan types share a width");
     using Cf = PrepCfg<E, S, KD, VD>;
     constexpr int C = 64, NTHR = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
@@ -279,39 +287,57 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     float* sG = (float*)(smem + Cf::oG);
     float* sB = sG + C;
 
-    const int ci = blockIdx.x, hv = blockIdx.y, hk = hv / (HV / HK);
-    const ChunkInfo ch = info[ci];
-    const int Cn = ch.len;
-    const long t0 = ch.t0;
     const int w = wave_id();
-    const long unit = (long)ci * HV + hv;
-
-    // ---- loads: every 16-byte vector of K, V, Q in flight together (rows past
-    // the chunk read its last row and are zeroed when staged)
     constexpr int NKV = C * KD / EPV / NTHR, NVV = C * VD / EPV / NTHR;
     typename Vec16<E>::t rk[NKV], rv[NVV], rq[WITH_R ? NKV : 1];
+    float rg = 0.f;
+    E rb = E(0.f);   // raw β: converted and masked when staged (a conversion here would wait for the loads)
+    // issue the loads of unit u (rows past the chunk read its last row; they
+    // are zeroed when staged)
+    auto issue = [&](int u, int Cu, int tu) {
+        const int hvu = u % HV, hku = hvu / (HV / HK);
+        if (threadIdx.x < C) {   // first, so that waiting for them leaves the vectors in flight
+            const int r = min((int)threadIdx.x, Cu - 1);
+            rg = gcum[(tu + r) * HV + hvu];
+            rb = beta[(tu + r) * HV + hvu];
+        }
 #pragma unroll
-    for (int i = 0; i < NKV; i++) {
-        const int idx = threadIdx.x + NTHR * i, r = min(idx / (KD / EPV), Cn - 1), c = idx % (KD / EPV);
-        rk[i] = *(const typename Vec16<E>::t*)(k + ((t0 + r) * HK + hk) * KD + c * EPV);
-        if constexpr (WITH_R) rq[i] = *(const typename Vec16<E>::t*)(q + ((t0 + r) * HK + hk) * KD + c * EPV);
-    }
+        for (int i = 0; i < NKV; i++) {
+            const int idx = threadIdx.x + NTHR * i, r = min(idx / (KD / EPV), Cu - 1), cc = idx % (KD / EPV);
+            rk[i] = *(const typename Vec16<E>::t*)(k + ((tu + r) * HK + hku) * KD + cc * EPV);
+            if constexpr (WITH_R) rq[i] = *(const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV);
+        }
 #pragma unroll
-    for (int i = 0; i < NVV; i++) {
-        const int idx = threadIdx.x + NTHR * i, r = min(idx / (VD / EPV), Cn - 1), c = idx % (VD / EPV);
-        rv[i] = *(const typename Vec16<E>::t*)(v + ((t0 + r) * HV + hv) * VD + c * EPV);
-    }
-    if (threadIdx.x < C) {
-        const int r = threadIdx.x;
-        sG[r] = gcum[(t0 + min(r, Cn - 1)) * HV + hv];
-        sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
-    }
+        for (int i = 0; i < NVV; i++) {
+            const int idx = threadIdx.x + NTHR * i, r = min(idx / (VD / EPV), Cu - 1), cc = idx % (VD / EPV);
+            rv[i] = *(const typename Vec16<E>::t*)(v + ((tu + r) * HV + hvu) * VD + cc * EPV);
+        }
+    };
     auto to_s = [](const typename Vec16<E>::t& x, float f, bool keep) {
         typename Vec16<S>::t y;
 #pragma unroll
         for (int e = 0; e < EPV; e++) y[e] = keep ? (S)(f * (float)x[e]) : (S)0.f;
         return y;
     };
+
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    int cur_len = info[u / HV].len, cur_t0 = info[u / HV].t0;
+    issue(u, cur_len, cur_t0);
+    for (; u < nunits; u += gridDim.x) {
+    const int ci = u / HV, hv = u % HV;
+    const int Cn = cur_len;
+    const long t0 = cur_t0;
+    const long unit = (long)ci * HV + hv;
+    const int un = u + (int)gridDim.x;
+    // read early: used for the prefetch below
+    const int nxt_len = un < nunits ? info[un / HV].len : 1, nxt_t0 = un < nunits ? info[un / HV].t0 : 0;
+
+    // ---- stage this unit
+    if (threadIdx.x < C) {
+        sG[threadIdx.x] = rg;
+        sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)rb : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < NKV; i++) {
         const int idx = threadIdx.x + NTHR * i, r = idx / (KD / EPV), c = idx % (KD / EPV);
@@ -335,6 +361,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
             *(typename Vec16<S>::t*)(KTo + r * KD + c * EPV) = to_s(rk[i], __expf(gl - sG[r]), r < Cn);
         }
     }
+    // ---- the next unit's loads fly during this unit's compute
+    if (un < nunits) issue(un, nxt_len, nxt_t0);
 
     // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32x32 block)
     {
@@ -346,6 +374,17 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
             zero_acc(aqk);
             wgemm<S, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
         }
+        // branch-free: Γ_rc = exp(min(G_r − G_c, 0)), then masked by a select
+        float gr[2][4], br[2][4], gc[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                gr[i][e] = sG[acc_row(m0, i, e)];
+                br[i][e] = sB[acc_row(m0, i, e)];
+            }
+#pragma unroll
+        for (int j = 0; j < 2; j++) gc[j] = sG[acc_col(n0, j)];
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -353,9 +392,10 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = acc_row(m0, i, e), c = acc_col(n0, j);
-                    const float gm = (c <= r) ? __expf(sG[r] - sG[c]) : 0.f;
-                    sL[r * LL + c] = (c < r) ? sB[r] * gm * akk[i][j][e] : 0.f;
-                    if (WITH_R) sPm[r * LA + c] = to_e<S>((c <= r) ? scale * gm * aqk[i][j][e] : 0.f);
+                    const float gm = __expf(fminf(gr[i][e] - gc[j], 0.f));
+                    const float lv = br[i][e] * gm * akk[i][j][e];
+                    sL[r * LL + c] = c < r ? lv : 0.f;
+                    if (WITH_R) sPm[r * LA + c] = to_e<S>(c <= r ? scale * gm * aqk[i][j][e] : 0.f);
                 }
     }
     lds_barrier();
@@ -430,6 +470,10 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
         store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, sV);
     }
+    lds_barrier();   // the next unit is staged over this one's LDS
+    cur_len = nxt_len;
+    cur_t0 = nxt_t0;
+    }
 }
 
 template <class E, class S, int KD, int VD>
@@ -442,19 +486,22 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
                           const void* beta, const ChunkInfo* info, void* W, void* U, void* R, void* A, void* KT,
                           hipStream_t s) {
     const size_t sm = prep_smem<E, S, KD, VD>();
-    dim3 grid((unsigned)p.NT, p.HV);
+    const long nunits = p.NT * p.HV;
+    if (nunits > INT32_MAX) return hipErrorInvalidValue;
+    // one persistent workgroup per CU (the LDS carve-up allows one), 256 CUs
+    dim3 grid((unsigned)(nunits < 256 ? nunits : 256));
     if (q) {
         auto kern = prep_kernel<E, S, KD, VD, true>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A, (S*)KT);
+                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A, (S*)KT, (int)nunits);
     } else {
         auto kern = prep_kernel<E, S, KD, VD, false>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A, (S*)KT);
+                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A, (S*)KT, (int)nunits);
     }
     return hipGetLastError();
 }
