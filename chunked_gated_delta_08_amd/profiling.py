@@ -33,6 +33,8 @@ KERNEL_SOURCES = {
     "chunk_table_kernel": [_CS + "gdr_prep.hip"] + _COMMON,
     "prep_kernel": [_CS + "gdr_prep.hip"] + _COMMON,
     "scan_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
+    "seg_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
+    "combine_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
     "grad_kernel": [_CS + "gdr_grad.hip"] + _COMMON,
     "kda_kernel": [_CS + "kda_bwd.hip"] + _COMMON,
 }
