@@ -324,13 +324,23 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         zero_acc(dks);
         zero_acc(dAp);
 
+        // the next value slice (h, dh as rows v of [V][K]; dO, V) is loaded into
+        // registers while the current one is computed
+        StateReg<E, KD, LK> nH, ndH;
+        RowsReg<E, 64, LS> ndO, nV;
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
-            if (vh > 0) {   // h / dh slices as rows v of [V][K]
-                g_load_state<E, KD, LK>(sH, hT + unit * VD * KD, vh * 64);
-                g_load_state<E, KD, LK>(sdH, dhT + unit * VD * KD, vh * 64);
-                g_load_rows<E, E, 64, LS>(sdO, dO + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
-                g_load_rows<E, E, 64, LS>(sV, v + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, Cn);
+            if (vh > 0) {
+                nH.store(sH);
+                ndH.store(sdH);
+                ndO.store(sdO);
+                nV.store(sV);
+            }
+            if (vh + 1 < Cf::NVH) {
+                nH.load(hT + unit * VD * KD, (vh + 1) * 64);
+                ndH.load(dhT + unit * VD * KD, (vh + 1) * 64);
+                ndO.load(dO + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
+                nV.load(v + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
             }
             lds_barrier();
             // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
