@@ -328,6 +328,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         // registers while the current one is computed
         StateReg<E, KD, LK> nH, ndH;
         RowsReg<E, 64, LS> ndO, nV;
+        RowsReg<E, KD, LK> nQ;   // Q returns to its buffer (which holds V during the loop)
 #pragma unroll
         for (int vh = 0; vh < Cf::NVH; vh++) {
             if (vh > 0) {
@@ -341,6 +342,8 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 ndH.load(dhT + unit * VD * KD, (vh + 1) * 64);
                 ndO.load(dO + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
                 nV.load(v + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
+            } else {
+                nQ.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
             }
             lds_barrier();
             // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
@@ -411,7 +414,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         }
 
         // ---- Q back into its buffer (it held the V slices)
-        g_load_rows<E, E, KD, LK>(sQ, q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        nQ.store(sQ);
         // ---- F = dPm ⊙ Pm -> dG; T1 = dPm ⊙ Γ · scale (over Pm); dW -> LDS
 #pragma unroll
         for (int i = 0; i < 2; i++)
