@@ -153,6 +153,15 @@ struct StateReg {
 #pragma unroll
         for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(threadIdx.x + GNT * i) * (16 / sizeof(E)));
     }
+    // partial <this, o> over the elements this thread holds (same layout)
+    __device__ __forceinline__ float dot(const StateReg& o) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; i++)
+#pragma unroll
+            for (int e = 0; e < (int)(16 / sizeof(E)); e++) acc += (float)v[i][e] * (float)o.v[i][e];
+        return acc;
+    }
     __device__ __forceinline__ void store(E* s) const {
 #pragma unroll
         for (int i = 0; i < N; i++) {
@@ -184,12 +193,18 @@ __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* 
     }
 }
 
-// sum over the 16 lanes that share a row group (lane bits 0..3)
-__device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+// Sum over the 16 lanes that share a row group (lane bits 0..3), valid in the
+// group's last lane (r16 == 15): four DPP row_shr adds (lanes shifted in from
+// outside the row read 0), no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum16_last(float x) {
+    x = dpp_shr_add<0x111>(x);   // row_shr:1
+    x = dpp_shr_add<0x112>(x);   // row_shr:2
+    x = dpp_shr_add<0x114>(x);   // row_shr:4
+    x = dpp_shr_add<0x118>(x);   // row_shr:8
     return x;
 }
 // sum over the 4 row groups (lane bits 4..5)
@@ -555,9 +570,9 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float rg = sum16(rowG[i][e]);
-                const float rb = sum16(rowB[i][e]);
-                if (r16 == 0) {
+                const float rg = sum16_last(rowG[i][e]);
+                const float rb = sum16_last(rowB[i][e]);
+                if (r16 == 15) {
                     const int rr = acc_row(m0, i, e);
                     sRowG[(w >> 1) * 64 + rr] = rg;
                     sRowB[(w >> 1) * 64 + rr] = rb;
