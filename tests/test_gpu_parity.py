@@ -104,6 +104,9 @@ SMALL_CASES = {
     "f16_slow_gate_h0": (1, 200, 1, 2, 128, 128, "f16", None, {"gate_scale": 1 / 64, "h0": True}),
     "bf16_k64_batch2": (2, 130, 2, 2, 64, 64, "bf16", None, {"gate_scale": 1 / 8}),
     "bf16_beta0": (1, 128, 1, 1, 128, 128, "bf16", None, {"beta_zero": True, "h0": True, "gate_scale": 1 / 64}),
+    # GQA ratios other than 1 and 2 take the runtime head-count path
+    "bf16_gqa4_varlen": (1, None, 2, 8, 128, 128, "bf16", [150, 64, 1, 90], {"gate_scale": 1 / 16, "h0": True}),
+    "f16_gqa3_k64": (2, 100, 1, 3, 64, 64, "f16", None, {"gate_scale": 1 / 8}),
 }
 
 
