@@ -1,6 +1,6 @@
 // gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
 //
-// One workgroup (4 waves) per (chunk, key head); it loops over the value heads
+// One workgroup (8 waves) per (chunk, key head); it loops over the value heads
 // that share the key head and keeps the dq/dk group sums in registers (the
 // GQA reduction the FlashQLA backward explainer, §一 step ④, does in Python).
 // Given h = h[c] (state entering the chunk) and dh = dh[c] (gradient of the
@@ -34,16 +34,23 @@ namespace gdr {
 
 template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 8 : 4; }
 
-// 4 waves (one per SIMD, so each wave may use the whole register file): wave w
-// owns rows 32*(w&1) .. +31 and the column half (w>>1) of every output.
-constexpr int GNT = 256;
+// Wave w owns rows 32*(w&1) .. +31 and the column block (w>>1) of every
+// output; 8 waves (two per SIMD, so one wave's element-wise work overlaps the
+// other's LDS and MFMA latency) measured faster than 4 at every workload.
+// Cross-lane results (DPP and permute reductions) are written by every lane
+// that holds them, never under a lane-dependent branch.
+#ifndef GDR_GRAD_WAVES
+#define GDR_GRAD_WAVES 8
+#endif
+constexpr int GNT = 64 * GDR_GRAD_WAVES;
+constexpr int GNCB = GDR_GRAD_WAVES / 2;   // column blocks (waves w and w^1 share one)
 
 template <class E, int KD, int VD>
 struct GradCfg {
     static constexpr int C = 64, VH = 64, NVH = VD / VH;
     static constexpr int LK = KD + gpad<E>(), LA = 64 + gpad<E>(), LS = VH + gpad<E>(), LF = 68;
-    static constexpr int TNK = KD / 32;      // 16-col tiles per wave for [64][KD] outputs
-    static constexpr int TNS = 2;            // 16-col tiles per wave for [64][64] outputs
+    static constexpr int TNK = KD / 16 / GNCB;   // 16-col tiles per wave for [64][KD] outputs
+    static constexpr int TNS = 4 / GNCB;         // 16-col tiles per wave for [64][64] outputs
     // byte offsets.  The V slice lives in Q's buffer during the V loop (Q is
     // reloaded afterwards); after the loop the slice region holds dW, dA_pre,
     // M1 and Eb.
@@ -193,18 +200,19 @@ __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* 
     }
 }
 
-// Sum over the 16 lanes that share a row group (lane bits 0..3), valid in the
-// group's last lane (r16 == 15): four DPP row_shr adds (lanes shifted in from
-// outside the row read 0), no LDS round trips.
+// Sum over the 16 lanes that share a row group (lane bits 0..3), in every lane
+// of the group: four DPP adds (swap neighbours, swap pairs, mirror within
+// each half row, mirror the row), no LDS round trips.  Every lane of the
+// wave must be active.
 template <int CTRL>
-__device__ __forceinline__ float dpp_shr_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float sum16_last(float x) {
-    x = dpp_shr_add<0x111>(x);   // row_shr:1
-    x = dpp_shr_add<0x112>(x);   // row_shr:2
-    x = dpp_shr_add<0x114>(x);   // row_shr:4
-    x = dpp_shr_add<0x118>(x);   // row_shr:8
+__device__ __forceinline__ float sum16(float x) {
+    x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]
+    x = dpp_add<0x141>(x);   // row_half_mirror
+    x = dpp_add<0x140>(x);   // row_mirror
     return x;
 }
 // sum over the 4 row groups (lane bits 4..5)
@@ -254,8 +262,8 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
     const long t0 = ch.t0;
     const int w = wave_id(), l = lane_id(), r16 = l & 15, g4 = l >> 4;
     const int m0 = 32 * (w & 1);           // every output block of this wave starts at this row
-    const int n0s = 32 * (w >> 1);         // column block for [64][64] outputs
-    const int n0k = (KD / 2) * (w >> 1);   // column block for [64][KD] outputs
+    const int n0s = (64 / GNCB) * (w >> 1);   // column block for [64][64] outputs
+    const int n0k = (KD / GNCB) * (w >> 1);   // column block for [64][KD] outputs
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
@@ -570,18 +578,17 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float rg = sum16_last(rowG[i][e]);
-                const float rb = sum16_last(rowB[i][e]);
-                if (r16 == 15) {
-                    const int rr = acc_row(m0, i, e);
-                    sRowG[(w >> 1) * 64 + rr] = rg;
-                    sRowB[(w >> 1) * 64 + rr] = rb;
-                }
+                const float rg = sum16(rowG[i][e]);
+                const float rb = sum16(rowB[i][e]);
+                // every lane of the group holds the sum: all write the same value (no branch)
+                const int rr = acc_row(m0, i, e);
+                sRowG[(w >> 1) * 64 + rr] = rg;
+                sRowB[(w >> 1) * 64 + rr] = rb;
             }
 #pragma unroll
-        for (int j = 0; j < TNS; j++) {
+        for (int j = 0; j < TNS; j++) {   // all four row groups hold the sum and write it (no branch)
             const float cs = sum4g(colG[j]);
-            if (g4 == 0) sCol[(w & 1) * 64 + acc_col(n0s, j)] = cs;
+            sCol[(w & 1) * 64 + acc_col(n0s, j)] = cs;
         }
         {
             float hz = hdh, zz = zsum;
@@ -590,13 +597,18 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 hz += __shfl_xor(hz, off, 64);
                 zz += __shfl_xor(zz, off, 64);
             }
-            if (l == 0) { sMisc[w] = hz; sMisc[8 + w] = zz; }
+            sMisc[w] = hz;   // every lane holds the sum (no branch)
+            sMisc[8 + w] = zz;
         }
         lds_barrier();
         if (threadIdx.x < 64) {
             const int rr = threadIdx.x;
-            float dG = (sRowG[rr] + sRowG[64 + rr]) - (sCol[rr] + sCol[64 + rr]);
-            const float db = sRowB[rr] + sRowB[64 + rr];
+            float dG = -(sCol[rr] + sCol[64 + rr]), db = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < GNCB; cb++) {
+                dG += sRowG[cb * 64 + rr];
+                db += sRowB[cb * 64 + rr];
+            }
             if (rr == C - 1) {
                 float hd = 0.f, zs = 0.f;
                 for (int i = 0; i < GNT / 64; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
