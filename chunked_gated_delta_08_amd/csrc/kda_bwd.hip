@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     int t0i, Cn;
     kda_find_chunk(cu, N, T, 64, ci, t0i, Cn);
     const long t0 = t0i;
-    const int w = wave_id(), l = lane_id(), g4 = l >> 4;
+    const int w = wave_id();
     const int m0 = 32 * (w & 1), n0k = (KD / 4) * (w >> 1), n0s = 16 * (w >> 1);
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
@@ -135,7 +135,8 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
             for (int c = part; c < VD; c += 4) s += hg[key * VD + c] * dhg[key * VD + c];
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
-        if (part == 0 && key < KD) sHD[key] = s;
+        // all four lanes of a key hold the sum and write it (key < KD is uniform per wave)
+        if (key < KD) sHD[key] = s;
     }
     lds_barrier();
     for (int idx = threadIdx.x; idx < C * KD; idx += 512) {
@@ -234,7 +235,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
         float x = csum[j];
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
-        if (g4 == 0) sCS[(w & 1) * KD + acc_col(n0k, j)] = x;
+        sCS[(w & 1) * KD + acc_col(n0k, j)] = x;   // every row group holds the sum (no branch)
     }
     lds_barrier();
 #pragma unroll
@@ -273,7 +274,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
             x += __shfl_xor(x, 2, 64);
             x += __shfl_xor(x, 4, 64);
             x += __shfl_xor(x, 8, 64);
-            if ((l & 15) == 0) sDB[(w >> 1) * 64 + acc_row(m0, i, e)] = x;
+            sDB[(w >> 1) * 64 + acc_row(m0, i, e)] = x;   // every lane of the group holds the sum
         }
     // ---- M1 = Aᵀ dA_pre
     f32x4 m1[2][1];
