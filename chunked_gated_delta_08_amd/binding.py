@@ -52,11 +52,15 @@ lib.gdr_chunk_bwd.restype = ctypes.c_int
 lib.gdr_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp]
 lib.gdr_chunk_bwd_events.restype = ctypes.c_int
 lib.gdr_chunk_bwd_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp, _vp]
+lib.gdr_gate_cumsum.restype = ctypes.c_int
+lib.gdr_gate_cumsum.argtypes = [ctypes.POINTER(Problem), _vp, _vp, _vp]
+lib.gdr_chunk_fwd.restype = ctypes.c_int
+lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp]
 lib.kda_chunk_bwd.restype = ctypes.c_int
 lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
 
-EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_chunk_bwd",
-            "gdr_chunk_bwd_events", "kda_chunk_bwd"]
+EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_gate_cumsum",
+            "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd"]
 
 
 def _check(code):
@@ -128,6 +132,43 @@ def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, 
                              _ptr(dO), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
+    del keep
+    return out
+
+
+def gdr_gate_cumsum(g, cu_seqlens=None, B=1, BT=64, out=None, stream=None):
+    """In-chunk cumulative sum of the raw gate g [B*T, HV] fp32 (restarting every BT
+    tokens and at every sequence start).  Returns g_cum, same shape, fp32."""
+    assert g.is_cuda and g.is_contiguous() and g.dtype == torch.float32 and g.dim() == 2
+    ntok, HV = g.shape
+    T = ntok // B if cu_seqlens is None else ntok
+    assert cu_seqlens is not None or ntok % B == 0
+    p, keep = make_problem(B if cu_seqlens is None else 1, T, 1, HV, 1, 1, torch.float32, BT, cu_seqlens)
+    if out is None:
+        out = torch.empty_like(g)
+    _check(lib.gdr_gate_cumsum(ctypes.byref(p), _ptr(g), _ptr(out), _stream(stream)))
+    del keep
+    return out
+
+
+def gdr_chunk_fwd(q, k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, scale=None, BT=64, want_ht=True,
+                  out=None, workspace=None, stream=None, seg_chunks=0):
+    """Chunked forward of the gated delta rule.  Returns dict o [B*T, HV, V] (input
+    dtype) and ht [N, HV, K, V] fp32 (or None)."""
+    B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
+    for t in (q, k, v, g_cum, beta):
+        assert t.is_cuda and t.is_contiguous()
+    assert g_cum.dtype == torch.float32
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale, seg_chunks)
+    N = B if cu_seqlens is None else p.N
+    dev = v.device
+    if out is None:
+        out = {"o": torch.empty_like(v),
+               "ht": torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if want_ht else None}
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g_cum), _ptr(beta), _ptr(h0),
+                             _ptr(out["o"]), _ptr(out["ht"]), _ptr(workspace), workspace.numel(), _stream(stream)))
     del keep
     return out
 

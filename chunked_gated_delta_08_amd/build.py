@@ -18,10 +18,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip"]
-# per-source device flags: the scan kernels keep MFMA accumulators in VGPRs;
-# the gradient kernel is left to the compiler's heuristics (its AGPR rewrite
-# is what keeps the 4-wave kernel free of spills)
+HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip", "gdr_fwd.hip"]
+# per-source device flags: the WY-factor, scan and KDA kernels keep MFMA
+# accumulators in VGPRs; the gradient and forward-output kernels are left to
+# the compiler's register-class heuristics
 SOURCE_FLAGS = {"gdr_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "gdr_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -198,6 +198,53 @@ int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const flo
     return launch_status(gdr::launch_scans(q, a, stream));
 }
 
+int gdr_gate_cumsum(const gdr_problem* p, const float* g, float* g_cum, hipStream_t stream) {
+    Problem q;
+    int st = check_problem(p, &q);
+    if (st != GDR_OK) return st;
+    const int64_t n = (p->cu_seqlens ? (int64_t)p->T : (int64_t)p->B * p->T) * p->HV;
+    if (n == 0) return GDR_OK;
+    if (!g || !g_cum) return GDR_ERR_INVALID;
+    if ((const char*)g < (const char*)(g_cum + n) && (const char*)g_cum < (const char*)(g + n)) return GDR_ERR_INVALID;
+    return launch_status(gdr::launch_gate_cumsum(q, g, g_cum, stream));
+}
+
+int gdr_chunk_fwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                  const void* beta, const float* h0, void* o, float* ht_out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    Problem q;
+    int st = check_problem(p, &q);
+    if (st != GDR_OK) return st;
+    if ((st = check_supported(q)) != GDR_OK) return st;
+    if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !o)) return GDR_ERR_INVALID;
+    const WsPlan w = gdr::plan_workspace(q);
+    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
+    auto* sc0 = (int32_t*)(base + w.seq_chunk0);
+    auto* seg = (SegInfo*)(base + w.seg_info);
+    auto* ss0 = (int32_t*)(base + w.seq_seg0);
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
+    if (q.NT > 0) {
+        st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
+                                            nullptr, base + w.KT, stream));
+        if (st != GDR_OK) return st;
+    }
+    gdr::ScanArgs a{};
+    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    set_seg_buffers(a, base, w);
+    a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.h0 = h0;
+    a.hT = base + w.h; a.ht = ht_out;
+    a.cu = q.cu; a.T = q.T;
+    a.do_fwd = true; a.do_rev = false;
+    if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
+    if (q.NT == 0) return GDR_OK;
+    gdr::FwdArgs f{};
+    f.q = qp; f.k = k; f.gcum = g_cum; f.info = info;
+    f.W = base + w.W; f.U = base + w.U; f.hT = base + w.h; f.o = o;
+    return launch_status(gdr::launch_fwd_out(q, f, stream));
+}
+
 int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
                          const void* beta, const float* h0, const void* dO, const float* dht, void* dq, void* dk,
                          void* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,

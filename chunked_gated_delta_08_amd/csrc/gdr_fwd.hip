@@ -1,0 +1,235 @@
+// gdr_fwd.hip -- the chunked forward output and the gate's in-chunk cumsum.
+//
+// FlashQLA backward explainer §一: the gate is carried as its in-chunk
+// cumulative sum (restarting at every chunk and sequence start) and the
+// forward state h[c] (entering chunk c) is what the chunked form runs on.
+// With V_new = U − W h[c] (W, U from the WY-factor kernel) the chunk output is
+//     o = scale · diag(γ) Q h[c] + Pm V_new,   Pm = scale · lower(Γ ⊙ Q Kᵀ)
+// (the same decomposition the backward differentiates).
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+// ---------------------------------------------------------------- gate cumsum
+// One thread per (token, value head): the in-chunk prefix sum of the raw gate
+// up to this token, accumulated in fp32 in token order from the chunk's first
+// token (so every element is the same sequence of fp32 additions a serial
+// in-chunk scan performs).
+__global__ void gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, const int32_t* __restrict__ cu,
+                                   int nseq, int T, int HV, int BT, long ntok) {
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= ntok * HV) return;
+    const long t = idx / HV;
+    const int hv = (int)(idx % HV);
+    long bos;
+    if (cu) {   // sequence of token t: largest n with cu[n] <= t
+        int lo = 0, hi = nseq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        bos = cu[lo];
+    } else {
+        bos = (t / T) * (long)T;
+    }
+    const long c0 = bos + ((t - bos) / BT) * BT;
+    float acc = g[c0 * HV + hv];
+    for (long s = c0 + 1; s <= t; s++) acc += g[s * HV + hv];
+    gc[idx] = acc;
+}
+
+hipError_t launch_gate_cumsum(const Problem& p, const float* g, float* gc, hipStream_t s) {
+    const long ntok = p.cu ? p.T : (long)p.B * p.T;
+    const long n = ntok * p.HV;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, gc, p.cu,
+                       p.cu ? p.N : p.B, p.T, p.HV, p.BT, ntok);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- output
+template <class T, int N> using vec_t = T __attribute__((ext_vector_type(N)));
+
+template <class S, int KD, int VD>
+struct FwdCfg {
+    static constexpr int C = 64, PAD = 16 / (int)sizeof(S);
+    static constexpr int LK = KD + PAD, LV = VD + PAD, LA = 64 + PAD;
+    static constexpr size_t oQ = 0;                                     // Q [64][LK]
+    static constexpr size_t oK = oQ + (size_t)C * LK * sizeof(S);       // K [64][LK], later the o tile
+    static constexpr size_t oW = oK + (size_t)C * LK * sizeof(S);       // W [64][LK]
+    static constexpr size_t oH = oW + (size_t)C * LK * sizeof(S);       // h[c] as [V][LK]
+    static constexpr size_t oVn = oH + (size_t)VD * LK * sizeof(S);     // U, then V_new [64][LV]
+    static constexpr size_t oPm = oVn + (size_t)C * LV * sizeof(S);     // Pm [64][LA]
+    static constexpr size_t oG = oPm + (size_t)C * LA * sizeof(S);      // G [64]
+    static constexpr size_t smem = oG + C * 4;
+    static_assert(smem <= 160 * 1024, "LDS budget");
+};
+
+// Grid (chunks, HV), 256 threads (4 waves).  E: input type; S: operand type of
+// the workspace tiles and of the MFMAs (fp16 for 16-bit inputs, fp32 for fp32).
+template <class E, class S, int KD, int VD>
+__global__ void __launch_bounds__(256) fwd_out_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                      const float* __restrict__ gcum, const ChunkInfo* __restrict__ info,
+                                                      const S* __restrict__ Wg, const S* __restrict__ Ug,
+                                                      const E* __restrict__ hT, E* __restrict__ o, int HK, int HV,
+                                                      float scale) {
+    using Cf = FwdCfg<S, KD, VD>;
+    constexpr int C = 64, NT = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA;
+    constexpr int EPE = 16 / (int)sizeof(E), EPS = 16 / (int)sizeof(S);
+    static_assert(C * LV * sizeof(E) <= C * LK * sizeof(S), "o tile fits in the K buffer");
+    using VE = vec_t<E, EPE>;
+    using VS = vec_t<S, EPE>;   // EPE elements of S (the 16-byte input vector, converted)
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sQ = (S*)(smem + Cf::oQ);
+    S* sK = (S*)(smem + Cf::oK);
+    S* sW = (S*)(smem + Cf::oW);
+    S* sH = (S*)(smem + Cf::oH);
+    S* sVn = (S*)(smem + Cf::oVn);
+    S* sPm = (S*)(smem + Cf::oPm);
+    float* sG = (float*)(smem + Cf::oG);
+    E* sO = (E*)(smem + Cf::oK);
+
+    const int ci = blockIdx.x, hv = blockIdx.y, hk = hv / (HV / HK);
+    const int Cn = info[ci].len;
+    const long t0 = info[ci].t0;
+    const long unit = (long)ci * HV + hv;
+    const int w = wave_id();
+
+    // ---- stage Q, K (rows past the chunk are zero), W, U, h[c], G
+    for (int idx = threadIdx.x; idx < C * KD / EPE; idx += NT) {
+        const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
+        const VE xq = *(const VE*)(q + ((t0 + rc) * HK + hk) * KD + c);
+        const VE xk = *(const VE*)(k + ((t0 + rc) * HK + hk) * KD + c);
+        VS yq, yk;
+#pragma unroll
+        for (int e = 0; e < EPE; e++) {
+            yq[e] = r < Cn ? (S)(float)xq[e] : (S)0.f;
+            yk[e] = r < Cn ? (S)(float)xk[e] : (S)0.f;
+        }
+        *(VS*)(sQ + r * LK + c) = yq;
+        *(VS*)(sK + r * LK + c) = yk;
+    }
+    for (int idx = threadIdx.x; idx < C * KD / EPS; idx += NT) {
+        const int r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
+        *(vec_t<S, EPS>*)(sW + r * LK + c) = *(const vec_t<S, EPS>*)(Wg + (unit * C + r) * KD + c);
+    }
+    for (int idx = threadIdx.x; idx < C * VD / EPS; idx += NT) {
+        const int r = idx / (VD / EPS), c = (idx % (VD / EPS)) * EPS;
+        *(vec_t<S, EPS>*)(sVn + r * LV + c) = *(const vec_t<S, EPS>*)(Ug + (unit * C + r) * VD + c);
+    }
+    {
+        const E* blk = hT + unit * KD * VD;
+        if constexpr (sizeof(E) == 2) {
+            // 16-byte piece c of the state block: column 16 cb + (c % 16) of the
+            // key block sb, keys 32 sb + 4 g + {0..3} and 32 sb + 16 + 4 g + {0..3}
+            // with g = (c % 64) / 16, cb = (c / 64) / (KD / 32), sb = (c / 64) % (KD / 32)
+            for (int c = threadIdx.x; c < KD * VD / 8; c += NT) {
+                const int ln = c & 63, sb = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
+                const int row = 16 * cb + (ln & 15), key = 32 * sb + 4 * (ln >> 4);
+                const vec_t<E, 8> x = *(const vec_t<E, 8>*)(blk + (long)c * 8);
+                vec_t<S, 4> lo, hi;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    lo[e] = (S)(float)x[e];
+                    hi[e] = (S)(float)x[4 + e];
+                }
+                *(vec_t<S, 4>*)(sH + row * LK + key) = lo;
+                *(vec_t<S, 4>*)(sH + row * LK + key + 16) = hi;
+            }
+        } else {   // fp32 states are stored [V][K]
+            for (int c = threadIdx.x; c < KD * VD / 4; c += NT) {
+                const int row = (c * 4) / KD, key = (c * 4) % KD;
+                *(vec_t<S, 4>*)(sH + row * LK + key) = *(const vec_t<S, 4>*)(blk + (long)row * KD + key);
+            }
+        }
+    }
+    if (threadIdx.x < C) sG[threadIdx.x] = gcum[(t0 + min((int)threadIdx.x, Cn - 1)) * HV + hv];
+    lds_barrier();
+
+    // ---- Pm = scale · lower(Γ ⊙ Q Kᵀ), Γ[r][c] = exp(G_r − G_c)   (wave w: a 32 x 32 block)
+    {
+        const int m0 = 32 * (w & 1), n0 = 32 * (w >> 1);
+        f32x4 aqk[2][2];
+        zero_acc(aqk);
+        wgemm<S, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = acc_row(m0, i, e), c = acc_col(n0, j);
+                    const float x = scale * __expf(sG[r] - sG[c]) * aqk[i][j][e];
+                    sPm[r * LA + c] = (S)(c <= r ? x : 0.f);
+                }
+    }
+    // ---- W h and Q h   (wave w: 32 rows x VD/2 columns); V_new = U − W h in place
+    constexpr int TN = VD / 32;
+    const int m0 = 32 * (w & 1), n0 = (VD / 2) * (w >> 1);
+    f32x4 qh[2][TN];
+    {
+        f32x4 wh[2][TN];
+        zero_acc(wh);
+        zero_acc(qh);
+        wgemm<S, 2, TN, KD, false, false>(wh, sW, LK, sH, LK, m0, n0);
+        wgemm<S, 2, TN, KD, false, false>(qh, sQ, LK, sH, LK, m0, n0);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = acc_row(m0, i, e), c = acc_col(n0, j);
+                    sVn[r * LV + c] = (S)((float)sVn[r * LV + c] - wh[i][j][e]);
+                }
+    }
+    lds_barrier();   // Pm and V_new complete; K is no longer read
+    // ---- o = scale · diag(γ) Q h + Pm V_new
+    f32x4 ov[2][TN];
+    zero_acc(ov);
+    wgemm<S, 2, TN, 64, false, true>(ov, sPm, LA, sVn, LV, m0, n0);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r = acc_row(m0, i, 0) + e;
+            const float gq = scale * __expf(sG[r]);
+#pragma unroll
+            for (int j = 0; j < TN; j++) sO[r * LV + acc_col(n0, j)] = (E)(ov[i][j][e] + gq * qh[i][j][e]);
+        }
+    }
+    lds_barrier();
+    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
+        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
+        if (r < Cn) *(VE*)(o + ((t0 + r) * HV + hv) * VD + c) = *(const VE*)(sO + r * LV + c);
+    }
+}
+
+template <class E, class S, int KD, int VD>
+static hipError_t fwd_out_go(const Problem& p, const FwdArgs& a, hipStream_t s) {
+    using Cf = FwdCfg<S, KD, VD>;
+    auto kern = fwd_out_kernel<E, S, KD, VD>;
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), Cf::smem, s, (const E*)a.q, (const E*)a.k, a.gcum,
+                       a.info, (const S*)a.W, (const S*)a.U, (const E*)a.hT, (E*)a.o, p.HK, p.HV, p.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_out(const Problem& p, const FwdArgs& a, hipStream_t s) {
+    if (p.K == 128 && p.V == 128) {
+        if (p.dtype == 2) return fwd_out_go<bf16, f16, 128, 128>(p, a, s);
+        if (p.dtype == 1) return fwd_out_go<f16, f16, 128, 128>(p, a, s);
+        return hipErrorInvalidValue;
+    }
+    if (p.K == 64 && p.V == 64) {
+        if (p.dtype == 2) return fwd_out_go<bf16, f16, 64, 64>(p, a, s);
+        if (p.dtype == 1) return fwd_out_go<f16, f16, 64, 64>(p, a, s);
+        return fwd_out_go<float, float, 64, 64>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

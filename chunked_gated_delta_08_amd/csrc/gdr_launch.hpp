@@ -106,6 +106,18 @@ struct GradArgs {
 };
 hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s);
 
+// Chunked forward output: o = scale·diag(γ)Q h[c] + scale·lower(Γ⊙QKᵀ)(U − W h[c])
+// per (chunk, value head), from the WY factors W, U (scan operand type) and the
+// states h[c] written by the forward scan (workspace layout above).
+struct FwdArgs {
+    const void* q; const void* k; const float* gcum; const ChunkInfo* info;
+    const void* W; const void* U; const void* hT; void* o;
+};
+hipError_t launch_fwd_out(const Problem& p, const FwdArgs& a, hipStream_t s);
+
+// In-chunk cumulative sum of the raw gate (fp32, token order).
+hipError_t launch_gate_cumsum(const Problem& p, const float* g, float* gc, hipStream_t s);
+
 // KDA WY backward stage.
 struct KdaArgs {
     const void* q; const void* k; const void* v; const void* v_new; const float* g; const void* beta;

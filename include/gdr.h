@@ -1,5 +1,6 @@
 /*
- * gdr.h -- C ABI of the MI355X (gfx950) gated-delta-rule backward library.
+ * gdr.h -- C ABI of the MI355X (gfx950) gated-delta-rule library: the chunked
+ * backward, and the chunked forward it differentiates.
  *
  * Method (gated delta rule, state S_t is K x V per sequence and value head):
  *     S_t = a_t (I - b_t k_t k_tᵀ) S_{t-1} + b_t k_t v_tᵀ ,  a_t = exp(ĝ_t)
@@ -77,7 +78,7 @@ const char *gdr_strerror(int status);
 /* Number of chunks NT = sum over sequences of ceil(len / BT); -1 if invalid. */
 int64_t gdr_num_chunks(const gdr_problem *p);
 
-/* Workspace bytes needed by gdr_fwd_states / gdr_chunk_bwd for this problem
+/* Workspace bytes needed by gdr_fwd_states / gdr_chunk_fwd / gdr_chunk_bwd for this problem
  * (0 if the problem is invalid).  The same workspace may be reused by later
  * calls on the same stream. */
 size_t gdr_workspace_size(const gdr_problem *p);
@@ -97,6 +98,41 @@ size_t gdr_workspace_size(const gdr_problem *p);
 int gdr_fwd_states(const gdr_problem *p, const void *k, const void *v, const float *g_cum, const void *beta,
                    const float *h0, float *h_out, void *v_new_out, float *ht_out,
                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gdr_gate_cumsum -- the gate in the form the chunked forward saves for the
+ * backward ([P1] §一: in-chunk cumulative sum of the raw log-gate).
+ *   g     [B*T,HV] fp32   raw per-token log-gate ĝ_t
+ *   g_cum [B*T,HV] fp32   output: Σ ĝ_s over the tokens s <= t of t's chunk
+ *                         (chunks of BT tokens, restarting at every sequence start)
+ * Each element is accumulated in fp32 in token order starting from the chunk's
+ * first token, so the result is bit-identical to a serial fp32 in-chunk scan.
+ * g and g_cum must not overlap.  No workspace; errors as for every call.
+ */
+int gdr_gate_cumsum(const gdr_problem *p, const float *g, float *g_cum, hipStream_t stream);
+
+/*
+ * gdr_chunk_fwd -- the chunked forward of the gated delta rule: outputs o_t and
+ * the final states S_T of the recurrence above ([P1] §一: the forward whose
+ * saved gate and states the backward consumes).
+ * Inputs:
+ *   q, k [B*T,HK,K]  v [B*T,HV,V]  beta [B*T,HV]   dtype
+ *   g_cum [B*T,HV] fp32     in-chunk cumulative log-gate (gdr_gate_cumsum)
+ *   h0 [N,HV,K,V] fp32      initial states, NULL = zero
+ * Outputs:
+ *   o [B*T,HV,V] dtype      written in full
+ *   ht_out [N,HV,K,V] fp32 or NULL (skip)
+ * ws/ws_bytes: workspace (>= gdr_workspace_size(p)); it holds the per-chunk
+ * states afterwards but nothing in it is part of the contract.
+ * Per chunk, with W, U from the WY factors and h[c] the state entering it:
+ *   o = scale·diag(γ) Q h[c] + scale·lower(Γ ⊙ Q Kᵀ) (U − W h[c]).
+ * Precision as for gdr_chunk_bwd (16-bit inputs: fp16 operands, fp32 accumulate;
+ * the per-chunk states are held in the input type between the scan and the
+ * output kernel).
+ */
+int gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                  const void *beta, const float *h0, void *o, float *ht_out, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
 
 /*
  * gdr_chunk_bwd -- the backward of the chunkwise gated delta rule ([P1] §一, §二).

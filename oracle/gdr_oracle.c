@@ -35,6 +35,7 @@
  *                       the per-chunk states h[c] / dh[c].          [pinned]
  *   orc_kda_wy_bwd      exact VJP of the KDA WY-stage functional (O-K). [pinned]
  *   orc_gcum_to_graw    recovers the raw gate from its in-chunk cumsum.
+ *   orc_gate_cumsum     the in-chunk cumulative sum itself, in fp64. [pinned]
  * "Pinned" = checked by tests/test_oracle_*.py against finite differences,
  * closed forms and invariants that do not reuse the code below.
  *
@@ -93,6 +94,25 @@ void orc_gcum_to_graw(const orc_problem *p, int BT, const float *gcum, double *g
                 double prev = (t % BT == 0) ? 0.0 : (double)gcum[i - p->HV];
                 graw[i] = (double)gcum[i] - prev;
             }
+    }
+}
+
+/* The in-chunk cumulative sum of the raw gate ([P1] §一: the forward saves
+ * the gate as this sum; chunks are BT tokens long and restart at every
+ * sequence start):  out[t] = Σ_{s in t's chunk, s <= t} graw[s], in fp64. */
+void orc_gate_cumsum(const orc_problem *p, int BT, const double *graw, double *out) {
+    int NS = orc_num_seqs(p);
+    for (int n = 0; n < NS; n++) {
+        int64_t bos, len; seq_range(p, n, &bos, &len);
+        for (int h = 0; h < p->HV; h++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < len; t++) {
+                int64_t i = (bos + t) * p->HV + h;
+                if (t % BT == 0) acc = 0.0;
+                acc += graw[i];
+                out[i] = acc;
+            }
+        }
     }
 }
 

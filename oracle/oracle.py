@@ -84,6 +84,15 @@ def gcum_to_graw(prob, BT, gcum):
     return out
 
 
+def gate_cumsum(prob, BT, graw):
+    """fp64 in-chunk cumulative sum of the raw gate (restarts every BT tokens and
+    at every sequence start)."""
+    g = _f64(graw)
+    out = np.zeros(g.shape, dtype=np.float64)
+    _lib().orc_gate_cumsum(ctypes.byref(prob._c()), int(BT), _ptr(g), _ptr(out))
+    return out
+
+
 def gdr_fwd_token(prob, BT, q, k, v, graw, beta, h0=None, want_o=True, want_hc=False):
     q, k, v, graw, beta, h0 = map(_f64, (q, k, v, graw, beta, h0))
     o = np.zeros((prob.ntok, prob.HV, prob.V)) if want_o else None

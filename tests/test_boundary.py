@@ -109,3 +109,31 @@ def test_kda_validation(B):
 def test_strerror(B):
     for c in (0, -1, -2, -3, -4):
         assert B.lib.gdr_strerror(c)
+
+
+def _fwd(B, p, ws_bytes=1 << 40, **null):
+    args = {n: FAKE for n in ("q", "k", "v", "g", "beta", "h0", "o", "ht")}
+    args.update(null)
+    return B.lib.gdr_chunk_fwd(ctypes.byref(p), args["q"], args["k"], args["v"], args["g"], args["beta"],
+                               args["h0"], args["o"], args["ht"], FAKE, ws_bytes, None)
+
+
+def test_fwd_validation(B):
+    assert _fwd(B, _prob(B, HK=2, HV=3)) == -1
+    assert _fwd(B, _prob(B, BT=32)) == -2
+    assert _fwd(B, _prob(B, K=128, V=128, dtype=0)) == -2
+    p = _prob(B)
+    assert _fwd(B, p, ws_bytes=B.workspace_size(p) - 1) == -3
+    for missing in ("q", "k", "v", "g", "beta", "o"):
+        assert _fwd(B, p, **{missing: None}) == -1, missing
+
+
+def test_gate_cumsum_validation(B):
+    p = _prob(B)
+    assert B.lib.gdr_gate_cumsum(ctypes.byref(p), None, FAKE, None) == -1
+    assert B.lib.gdr_gate_cumsum(ctypes.byref(p), FAKE, None, None) == -1
+    # overlapping input and output
+    assert B.lib.gdr_gate_cumsum(ctypes.byref(p), ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 64), None) == -1
+    assert B.lib.gdr_gate_cumsum(ctypes.byref(_prob(B, HK=2, HV=3)), FAKE, FAKE, None) == -1
+    # nothing to do: no tokens
+    assert B.lib.gdr_gate_cumsum(ctypes.byref(_prob(B, T=0)), None, None, None) == 0

@@ -13,7 +13,9 @@ fails at least one of them:
 * the chunked WY derivation equals the token recurrence for several BT,
   including partial last chunks (BT invariance);
 * linearity in the cotangents; varlen == per-sequence runs; GQA == repeated
-  heads summed; an independent fp64 torch-autograd derivation.
+  heads summed; an independent fp64 torch-autograd derivation;
+* the in-chunk gate cumsum: a case worked by hand, its inverse, and the plain
+  cumsum when one chunk covers each sequence.
 """
 import numpy as np
 import pytest
@@ -253,6 +255,35 @@ def test_gcum_roundtrip(oracle):
     # chunk starts hold the raw value itself
     for s in (0, 64, 70, 75, 139, 203):
         np.testing.assert_array_equal(gc[s], graw[s])
+
+
+def test_gate_cumsum_by_hand(oracle):
+    """In-chunk cumsum worked by hand: BT=3, varlen lengths 4 and 5, and the
+    dense layout B=2, T=4 (restart at each chunk and each sequence)."""
+    g = np.arange(1, 10, dtype=np.float64)[:, None] * np.array([[1.0, -0.5]])
+    p = oracle.Problem(1, 9, 1, 2, 4, 4, cu_seqlens=[0, 4, 9])
+    want = np.array([1, 3, 6, 4, 5, 11, 18, 8, 17], dtype=np.float64)
+    out = oracle.gate_cumsum(p, 3, g)
+    np.testing.assert_array_equal(out[:, 0], want)
+    np.testing.assert_array_equal(out[:, 1], -0.5 * want)
+    pd = oracle.Problem(2, 4, 1, 2, 4, 4)
+    want_d = np.array([1, 3, 6, 4, 5, 11, 18, 8], dtype=np.float64)
+    np.testing.assert_array_equal(oracle.gate_cumsum(pd, 3, g[:8])[:, 0], want_d)
+
+
+def test_gate_cumsum_inverse(oracle):
+    """gcum_to_graw undoes gate_cumsum (fp32 rounding of the sums aside), and a
+    chunk size longer than every sequence gives the plain per-sequence cumsum."""
+    rng = np.random.default_rng(17)
+    lens = [70, 5, 130, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    g = -rng.random((int(cu[-1]), 3))
+    p = oracle.Problem(1, int(cu[-1]), 1, 3, 4, 4, cu_seqlens=cu)
+    gc = oracle.gate_cumsum(p, 64, g)
+    np.testing.assert_allclose(oracle.gcum_to_graw(p, 64, gc.astype(np.float32)), g, rtol=0, atol=4e-5)
+    whole = oracle.gate_cumsum(p, 1 << 20, g)
+    for a, b in zip(cu[:-1], cu[1:]):
+        np.testing.assert_allclose(whole[a:b], np.cumsum(g[a:b], axis=0), rtol=1e-14, atol=1e-13)
 
 
 # ---------------------------------------------------------------- KDA stage
