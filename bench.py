@@ -7,6 +7,10 @@ reverse cumsum and GQA sums) over one batch of synthetic inputs already
 resident in HBM.  Default workload: B=1, T=32768, 16 key / 16 value heads,
 K=V=128, BT=64, bf16 inputs with fp32 gate, dht present.
 
+With --path fwd a step is instead the chunked forward: gdr_gate_cumsum on the
+raw gate, then gdr_chunk_fwd (chunk table + WY factors, the forward state
+scan, the output kernel), on the same inputs.
+
 Prints one JSON line: the headline metric (effective TFLOP/s under the FLOP
 model below, with ms per call), a roofline entry for the dominant kernel
 (timed with HIP events recorded by the library between its stages during the
@@ -14,7 +18,10 @@ timed steps), and the fp64 CPU oracle timed on a bounded sample.
 
 FLOP model per (chunk of C rows, value head), dense tiles, recompute not
 counted:  F(C) = 16 C K V + 18 C^2 K + 10 C^2 V + 13/3 C^3  (32.59 MFLOP at
-C=64, K=V=128).
+C=64, K=V=128).  Forward: K Kᵀ, W = A(βγK), Q Kᵀ (2 C^2 K each), U = A(βV) and
+Pm V_new (2 C^2 V each), W h, K̃ᵀ V_new and Q h (2 C K V each), the triangular
+inverse (C^3 / 3):  F_fwd(C) = 6 C K V + 6 C^2 K + 4 C^2 V + C^3 / 3
+(11.62 MFLOP at C=64, K=V=128).
 """
 import argparse
 import ctypes
@@ -43,6 +50,10 @@ def flop_model(C, K, V):
     return 16 * C * K * V + 18 * C * C * K + 10 * C * C * V + 13.0 / 3.0 * C ** 3
 
 
+def flop_model_fwd(C, K, V):
+    return 6 * C * K * V + 6 * C * C * K + 4 * C * C * V + C ** 3 / 3.0
+
+
 def chunk_lengths(lengths, T, B, BT):
     seqs = [T] * B if lengths is None else lengths
     out = []
@@ -69,6 +80,22 @@ def kernel_bytes(cfg, chunks, es=2):
     return {"prep": prep, "scans": scans, "grad": grad}
 
 
+def kernel_bytes_fwd(cfg, chunks, es=2):
+    """Algorithmic bytes of each forward stage (inputs read once, outputs written once)."""
+    HK, HV, K, V = cfg["HK"], cfg["HV"], cfg["K"], cfg["V"]
+    ntok, nunits = sum(chunks), len(chunks) * HV
+    tok_k, tok_v = ntok * K * es, ntok * V * es
+    st, state = 64 * K * es, K * V * es
+    gate = ntok * HV * 8                       # raw gate in, cumulative gate out (fp32)
+    # prep: k, v, gate, beta in; W, U, K~ tiles out
+    prep = HK * tok_k + HV * tok_v + ntok * HV * (4 + es) + nunits * 3 * st
+    # forward scan: W, K~, U in; h states out
+    scans = nunits * (3 * st + state)
+    # output: q, k, W, U, h states and gate in; o out
+    out = HK * 2 * tok_k + nunits * (2 * st + state) + ntok * HV * 4 + HV * tok_v
+    return {"gate": gate, "prep": prep, "scans": scans, "out": out}
+
+
 def hip_events(n):
     hip = ctypes.CDLL("libamdhip64.so")
     evs = (ctypes.c_void_p * n)()
@@ -83,7 +110,7 @@ def elapsed_ms(hip, a, b):
     return ms.value
 
 
-def cpu_baseline(inp, cfg, chunks, min_seconds=10.0):
+def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
     """The fp64 oracle, unchanged, on the same inputs: full passes over every
     sequence and head of the workload, repeated until at least `min_seconds`
     of CPU time have elapsed (a bounded sample of the timed work)."""
@@ -96,16 +123,39 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0):
     passes, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
-        O.gdr_bwd_token(p, *args)
+        if path == "fwd":
+            O.gdr_fwd_token(p, 64, args[0], args[1], args[2], args[3], args[4], None)
+        else:
+            O.gdr_bwd_token(p, *args)
         dt += time.perf_counter() - t0
         passes += 1
-    flops = passes * sum(flop_model(c, K, V) for c in chunks) * HV
+    model = flop_model_fwd if path == "fwd" else flop_model
+    flops = passes * sum(model(c, K, V) for c in chunks) * HV
     nseq = B if inp["cu"] is None else len(inp["cu"]) - 1
-    threads = min(O.num_threads(), nseq * HK)
+    threads = min(O.num_threads(), nseq * (HV if path == "fwd" else HK))
+    what = ("token recurrence (forward), OpenMP over (sequence, value head)" if path == "fwd" else
+            "token recurrence with the hand-derived backward, OpenMP over (sequence, key head)")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 token recurrence with the "
-                      f"hand-derived backward, OpenMP over (sequence, key head)",
+            "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 {what}",
             "seconds": round(dt, 2)}
+
+
+def _roofline(stage, kb, names, workload, profiling):
+    """Roofline entry of the slowest stage's kernel (HBM-bound)."""
+    dom = max(stage, key=stage.get)
+    achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
+    kernel_name = names[dom]
+    traffic = None   # HBM bytes per launch from the committed counter summary, while the sources match it
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            t = json.load(fh)
+        if t.get("source_digest") == profiling.source_digest(profiling.KERNEL_SOURCES[kernel_name]):
+            traffic = t.get("bytes_per_launch")
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel_name,
+            "kernel_ms": round(stage[dom], 4), "algorithmic_bytes": kb[dom],
+            "stage_ms": {k: round(v, 4) for k, v in stage.items()}}
 
 
 def main():
@@ -114,6 +164,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
+    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd"],
+                    help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -124,33 +176,53 @@ def main():
     import torch
     from chunked_gated_delta_08_amd import binding, profiling, workloads
 
+    fwd = args.path == "fwd"
     cfg = dict(WORKLOADS[args.workload])
     lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
     inp = workloads.gdr_inputs(cfg["B"], cfg["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], dtype="bf16", seed=0,
                                lengths=lengths, dht=True)
-    dev = {k: inp[k].cuda() for k in ("q", "k", "v", "beta", "dO", "gcum", "dht")}
+    dev = {k: inp[k].cuda() for k in ("q", "k", "v", "beta", "dO", "gcum", "graw", "dht")}
     cu = None if inp["cu"] is None else torch.tensor(inp["cu"], dtype=torch.int32, device="cuda")
     T = inp["T"]
     prob, keep = binding.make_problem(cfg["B"], T, cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], torch.bfloat16, 64, cu)
     N = inp["N"]
     ws = torch.empty(binding.workspace_size(prob), dtype=torch.uint8, device="cuda")
-    out = {"dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]), "dv": torch.empty_like(dev["v"]),
-           "dg": torch.empty(dev["gcum"].shape, dtype=torch.float32, device="cuda"),
-           "dbeta": torch.empty(dev["beta"].shape, dtype=torch.float32, device="cuda"),
-           "dh0": torch.empty((N, cfg["HV"], cfg["K"], cfg["V"]), dtype=torch.float32, device="cuda")}
     P = binding._ptr
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    args_c = [ctypes.byref(prob), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["gcum"]), P(dev["beta"]), None,
-              P(dev["dO"]), P(dev["dht"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]), P(out["dbeta"]),
-              P(out["dh0"]), P(ws), ws.numel(), sp]
-    hip, evs = hip_events(4 * args.steps)
+    nev = 5 if fwd else 4
+    hip, evs = hip_events(nev * args.steps)
+    evsz = ctypes.sizeof(ctypes.c_void_p)
+    if fwd:
+        gprob, gkeep = binding.make_problem(cfg["B"], T, 1, cfg["HV"], 1, 1, torch.float32, 64, cu)
+        gc = torch.empty_like(dev["graw"])
+        out = {"o": torch.empty_like(dev["v"]),
+               "ht": torch.empty((N, cfg["HV"], cfg["K"], cfg["V"]), dtype=torch.float32, device="cuda")}
+        args_c = [ctypes.byref(prob), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(gc), P(dev["beta"]), None,
+                  P(out["o"]), P(out["ht"]), P(ws), ws.numel(), sp]
+    else:
+        out = {"dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]), "dv": torch.empty_like(dev["v"]),
+               "dg": torch.empty(dev["gcum"].shape, dtype=torch.float32, device="cuda"),
+               "dbeta": torch.empty(dev["beta"].shape, dtype=torch.float32, device="cuda"),
+               "dh0": torch.empty((N, cfg["HV"], cfg["K"], cfg["V"]), dtype=torch.float32, device="cuda")}
+        args_c = [ctypes.byref(prob), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["gcum"]), P(dev["beta"]), None,
+                  P(dev["dO"]), P(dev["dht"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]),
+                  P(out["dbeta"]), P(out["dh0"]), P(ws), ws.numel(), sp]
 
-    def call(i=None):
-        ev = None if i is None else ctypes.byref(evs, 4 * i * ctypes.sizeof(ctypes.c_void_p))
-        rc = binding.lib.gdr_chunk_bwd_events(*args_c, ev)
+    def check(rc):
         if rc != 0:
             raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
+
+    def call(i=None):
+        if fwd:
+            if i is not None:
+                assert hip.hipEventRecord(ctypes.c_void_p(evs[nev * i]), sp) == 0
+            check(binding.lib.gdr_gate_cumsum(ctypes.byref(gprob), P(dev["graw"]), P(gc), sp))
+            ev = None if i is None else ctypes.byref(evs, (nev * i + 1) * evsz)
+            check(binding.lib.gdr_chunk_fwd_events(*args_c, ev))
+        else:
+            ev = None if i is None else ctypes.byref(evs, nev * i * evsz)
+            check(binding.lib.gdr_chunk_bwd_events(*args_c, ev))
 
     for _ in range(args.warmup):
         call()
@@ -162,41 +234,36 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    stage = {"prep": 0.0, "scans": 0.0, "grad": 0.0}
+    names = (["gate", "prep", "scans", "out"] if fwd else ["prep", "scans", "grad"])
+    stage = {k: 0.0 for k in names}
     for i in range(args.steps):
-        e = [evs[4 * i + j] for j in range(4)]
-        stage["prep"] += elapsed_ms(hip, e[0], e[1]) / args.steps
-        stage["scans"] += elapsed_ms(hip, e[1], e[2]) / args.steps
-        stage["grad"] += elapsed_ms(hip, e[2], e[3]) / args.steps
+        e = [evs[nev * i + j] for j in range(nev)]
+        for j, k in enumerate(names):
+            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
     chunks = chunk_lengths(lengths, cfg["T"], cfg["B"], 64)
-    F = sum(flop_model(c, cfg["K"], cfg["V"]) for c in chunks) * cfg["HV"]
+    model = flop_model_fwd if fwd else flop_model
+    F = sum(model(c, cfg["K"], cfg["V"]) for c in chunks) * cfg["HV"]
     tflops = F / (ms_per_step * 1e-3) / 1e12
-    kb = kernel_bytes(cfg, chunks)
-    dom = max(stage, key=stage.get)
-    achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
-    kernel_name = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}[dom]
-    traffic = None   # HBM bytes per launch from the committed counter summary, while the sources match it
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{args.workload}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as fh:
-            t = json.load(fh)
-        if t.get("source_digest") == profiling.source_digest(profiling.KERNEL_SOURCES[kernel_name]):
-            traffic = t.get("bytes_per_launch")
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel_name,
-            "kernel_ms": round(stage[dom], 4), "algorithmic_bytes": kb[dom],
-            "stage_ms": {k: round(v, 4) for k, v in stage.items()}}
+    if fwd:
+        kb = kernel_bytes_fwd(cfg, chunks)
+        kn = {"gate": "gate_cumsum_kernel", "prep": "prep_kernel", "scans": "scan_kernel", "out": "fwd_out_kernel"}
+    else:
+        kb = kernel_bytes(cfg, chunks)
+        kn = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}
+    roof = _roofline(stage, kb, kn, ("fwd_" if fwd else "") + args.workload, profiling)
 
-    res = {"metric": "GDN chunked bwd eff. TFLOP/s (ms/call in ms_per_step) at T=32k, H=16, K=V=128, BT=64",
+    wname = cfg["name"].replace("gdn_bwd", "gdn_fwd") if fwd else cfg["name"]
+    what = "fwd" if fwd else "bwd"
+    res = {"metric": f"GDN chunked {what} ms/call + eff. TFLOP/s at T=32k, H=16/32, K=V=128, BT=64",
            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
-           "config": {"workload": cfg["name"], "B": cfg["B"], "T": T, "HK": cfg["HK"], "HV": cfg["HV"],
+           "config": {"workload": wname, "B": cfg["B"], "T": T, "HK": cfg["HK"], "HV": cfg["HV"],
                       "K": cfg["K"], "V": cfg["V"], "BT": 64, "global_batch": cfg["B"], "seq_len": T,
                       "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2)},
            "roofline": roof}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path=args.path)
     del keep
     print(json.dumps(res), flush=True)
 

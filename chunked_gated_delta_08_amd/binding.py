@@ -56,11 +56,13 @@ lib.gdr_gate_cumsum.restype = ctypes.c_int
 lib.gdr_gate_cumsum.argtypes = [ctypes.POINTER(Problem), _vp, _vp, _vp]
 lib.gdr_chunk_fwd.restype = ctypes.c_int
 lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp]
+lib.gdr_chunk_fwd_events.restype = ctypes.c_int
+lib.gdr_chunk_fwd_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp, _vp]
 lib.kda_chunk_bwd.restype = ctypes.c_int
 lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
 
 EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_gate_cumsum",
-            "gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd"]
+            "gdr_chunk_fwd", "gdr_chunk_fwd_events", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd"]
 
 
 def _check(code):

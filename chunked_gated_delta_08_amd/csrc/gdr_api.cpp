@@ -209,9 +209,9 @@ int gdr_gate_cumsum(const gdr_problem* p, const float* g, float* g_cum, hipStrea
     return launch_status(gdr::launch_gate_cumsum(q, g, g_cum, stream));
 }
 
-int gdr_chunk_fwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
-                  const void* beta, const float* h0, void* o, float* ht_out, void* ws, size_t ws_bytes,
-                  hipStream_t stream) {
+int gdr_chunk_fwd_events(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                         const void* beta, const float* h0, void* o, float* ht_out, void* ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t* ev) {
     Problem q;
     int st = check_problem(p, &q);
     if (st != GDR_OK) return st;
@@ -224,12 +224,15 @@ int gdr_chunk_fwd(const gdr_problem* p, const void* qp, const void* k, const voi
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
     auto* seg = (SegInfo*)(base + w.seg_info);
     auto* ss0 = (int32_t*)(base + w.seq_seg0);
+    auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
+    if ((st = mark(0)) != GDR_OK) return st;
     if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
                                             nullptr, base + w.KT, stream));
         if (st != GDR_OK) return st;
     }
+    if ((st = mark(1)) != GDR_OK) return st;
     gdr::ScanArgs a{};
     a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
     set_seg_buffers(a, base, w);
@@ -238,11 +241,20 @@ int gdr_chunk_fwd(const gdr_problem* p, const void* qp, const void* k, const voi
     a.cu = q.cu; a.T = q.T;
     a.do_fwd = true; a.do_rev = false;
     if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
-    if (q.NT == 0) return GDR_OK;
-    gdr::FwdArgs f{};
-    f.q = qp; f.k = k; f.gcum = g_cum; f.info = info;
-    f.W = base + w.W; f.U = base + w.U; f.hT = base + w.h; f.o = o;
-    return launch_status(gdr::launch_fwd_out(q, f, stream));
+    if ((st = mark(2)) != GDR_OK) return st;
+    if (q.NT > 0) {
+        gdr::FwdArgs f{};
+        f.q = qp; f.k = k; f.gcum = g_cum; f.info = info;
+        f.W = base + w.W; f.U = base + w.U; f.hT = base + w.h; f.o = o;
+        if ((st = launch_status(gdr::launch_fwd_out(q, f, stream))) != GDR_OK) return st;
+    }
+    return mark(3);
+}
+
+int gdr_chunk_fwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                  const void* beta, const float* h0, void* o, float* ht_out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    return gdr_chunk_fwd_events(p, qp, k, v, g_cum, beta, h0, o, ht_out, ws, ws_bytes, stream, nullptr);
 }
 
 int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,

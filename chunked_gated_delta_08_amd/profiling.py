@@ -37,6 +37,8 @@ KERNEL_SOURCES = {
     "combine_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
     "grad_kernel": [_CS + "gdr_grad.hip"] + _COMMON,
     "kda_kernel": [_CS + "kda_bwd.hip"] + _COMMON,
+    "fwd_out_kernel": [_CS + "gdr_fwd.hip"] + _COMMON,
+    "gate_cumsum_kernel": [_CS + "gdr_fwd.hip"] + _COMMON,
 }
 
 

@@ -135,6 +135,17 @@ int gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void
                   hipStream_t stream);
 
 /*
+ * gdr_chunk_fwd_events -- gdr_chunk_fwd for measurement tools.  Identical
+ * computation and arguments; `events` (NULL or 4 caller-created hipEvent_t)
+ * are recorded on `stream` before the first launch and after each of the three
+ * stages: [0] start, [1] after the chunk table and WY-factor kernel, [2] after
+ * the forward state scan, [3] after the output kernel.
+ */
+int gdr_chunk_fwd_events(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                         const void *beta, const float *h0, void *o, float *ht_out, void *ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t *events);
+
+/*
  * gdr_chunk_bwd -- the backward of the chunkwise gated delta rule ([P1] §一, §二).
  * Inputs:
  *   q, k [B*T,HK,K]  v, dO [B*T,HV,V]  beta [B*T,HV]   dtype
