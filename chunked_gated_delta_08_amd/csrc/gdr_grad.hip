@@ -1,8 +1,9 @@
 // gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
 //
-// One workgroup (8 waves) per (chunk, key head); it loops over the value heads
-// that share the key head and keeps the dq/dk group sums in registers (the
-// GQA reduction the FlashQLA backward explainer, §一 step ④, does in Python).
+// One workgroup (8 waves) per (chunk, key head) and launch; with G value heads
+// per key head there are G launches, one per head of the group, that add up
+// the dq/dk group sums in a fixed order (the GQA reduction the FlashQLA
+// backward explainer, §一 step ④, does in Python).
 // Given h = h[c] (state entering the chunk) and dh = dh[c] (gradient of the
 // state leaving it) from the scans, and recomputing the chunk's WY factors:
 //   L = strictly-lower(diag(β)(K Kᵀ) ⊙ Γ),  A = (I+L)^{-1} (read from the prep kernel),
@@ -215,6 +216,10 @@ __device__ __forceinline__ float sum16(float x) {
     x = dpp_add<0x140>(x);   // row_mirror
     return x;
 }
+// Keeps a value in a register at this point: the arithmetic that produced it
+// is not deferred to a later phase (where its operands would be kept live).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // sum over the 4 row groups (lane bits 4..5)
 __device__ __forceinline__ float sum4g(float x) {
     x += __shfl_xor(x, 16, 64);
@@ -222,14 +227,15 @@ __device__ __forceinline__ float sum4g(float x) {
     return x;
 }
 
-// GT: value heads per key head as a compile-time constant (1 or 2; the head
-// loop is then unrolled), or 0 for a runtime count.  With G > 1 the running group sums of dq and dk are not
-// kept in registers across value heads: after each head the workgroup adds
-// its fp32 partials into a private workspace block (fragment order, read back
-// and rewritten only by the lane that owns it), so the order of the sum is
-// fixed and the heavy per-head phases keep their registers.
-template <class E, int KD, int VD, int GT>
-__global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, float scale) {
+// One launch handles value head hv = hk * G + hi of every (chunk, key head).
+// GRP (G > 1): the launches for hi = 0 .. G-1 run in order on one stream and
+// carry the group sums of dq and dk in an fp32 workspace block per (chunk,
+// key head) (fragment order, each element read back and rewritten only by the
+// lane that owns it): the first launch writes its partials, later ones add
+// theirs, and the last one stores the 16-bit sums.  The order of the sum is
+// fixed, and every launch has the register footprint of a single head.
+template <class E, int KD, int VD, bool GRP>
+__global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     using Cf = GradCfg<E, KD, VD>;
     constexpr int C = 64, TNK = Cf::TNK, TNS = Cf::TNS, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, LF = Cf::LF;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -256,7 +262,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
     float* sMisc = sCol + 2 * 64;  // [16 + 64]
     E* sDv = (E*)(smem + Cf::oDv);
 
-    const int ci = blockIdx.x, hk = blockIdx.y, G = GT ? GT : HV / HK;
+    const int ci = blockIdx.x, hk = blockIdx.y, G = GRP ? HV / HK : 1;
     const ChunkInfo ch = a.info[ci];
     const int Cn = ch.len;
     const long t0 = ch.t0;
@@ -280,11 +286,10 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         rk.store(sK);
     }
 
-    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];   // this head's dq, dk (after the loop: the group sums)
+    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];   // this head's dq, dk (then the group sums)
 
-#pragma unroll
-    for (int hi = 0; hi < G; hi++) {
-        const int hv = hk * G + hi;
+    {
+        const int hv = GRP ? hk * G + hi : hk;
         const long unit = (long)ci * HV + hv;
         // this head's A and first value slice: loads in flight during Pm
         RowsReg<E, 64, LA> rA;
@@ -395,6 +400,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 const int rr = idx / KD, cc = idx % KD;
                 hdh += (float)sH[rr * LK + cc] * (float)sdH[rr * LK + cc];
             }
+            pin(hdh);
             lds_barrier();
             // ---- V_new = A Z
             {
@@ -431,6 +437,10 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                         if constexpr (Cf::DV_LDS) sDv[rr * LS + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
                         else if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
                     }
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) pin(rowB[i][e]);
             }
             lds_barrier();
             if constexpr (Cf::DV_LDS) store_rows<E, 64, LS>((E*)a.dv + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, sDv, Cn);
@@ -453,6 +463,12 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 colG[j] += f;
                 sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
             }
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) pin(rowG[i][e]);
+#pragma unroll
+        for (int j = 0; j < TNS; j++) pin(colG[j]);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -625,7 +641,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
             }
             if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
         }
-        if (GT != 1) {   // group sums through the workspace block of this (chunk, key head)
+        if constexpr (GRP) {   // group sums through the workspace block of this (chunk, key head)
             float* st = a.gsum + ((long)ci * HK + hk) * 2 * 64 * KD;
 #pragma unroll
             for (int i = 0; i < 2; i++)
@@ -643,6 +659,7 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                         *pk = dk_tot[i][j];
                     }
                 }
+            if (hi + 1 < G) return;   // uniform: only the last head of the group stores dq, dk
         }
         lds_barrier();
     }
@@ -662,23 +679,26 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
     store_rows<E, KD, LK>((E*)a.dk + (t0 * HK + hk) * KD, (long)HK * KD, sdH, Cn);
 }
 
-template <class E, int KD, int VD, int GT>
+template <class E, int KD, int VD, bool GRP>
 static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
     using Cf = GradCfg<E, KD, VD>;
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
-    auto kern = grad_kernel<E, KD, VD, GT>;
+    auto kern = grad_kernel<E, KD, VD, GRP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale);
-    return hipGetLastError();
+    const int G = GRP ? p.HV / p.HK : 1;
+    for (int hi = 0; hi < G; hi++) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale, hi);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <class E, int KD, int VD>
 static hipError_t grad_go(const Problem& p, const GradArgs& a, hipStream_t s) {
-    if (p.HV == p.HK) return grad_go1<E, KD, VD, 1>(p, a, s);
+    if (p.HV == p.HK) return grad_go1<E, KD, VD, false>(p, a, s);
     if (!a.gsum) return hipErrorInvalidValue;
-    if (p.HV == 2 * p.HK) return grad_go1<E, KD, VD, 2>(p, a, s);
-    return grad_go1<E, KD, VD, 0>(p, a, s);
+    return grad_go1<E, KD, VD, true>(p, a, s);
 }
 
 hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s) {
