@@ -167,7 +167,8 @@ __device__ __forceinline__ void put16(float* Z, int ldz, const f32x4& acc, float
 }
 
 // A = (I + L)^{-1} for the strictly lower 64 x 64 L in sL (fp32, pitch LL),
-// written to sAf (fp32, pitch LL) by the four waves together.  With 16 x 16
+// written to sAf (fp32, pitch LL) by waves 0..3 together (the others only help
+// to zero the blocks above the diagonal).  With 16 x 16
 // blocks, D_i = (I + L_ii)^{-1} and A_ij = −D_i Σ_{j<=k<i} L_ik A_kj:
 //   step 1: wave w inverts D_w by forward substitution (one lane per column);
 //   step 2: A_10 = −D_1 L_10 D_0 and A_32 = −D_3 L_32 D_2; meanwhile
@@ -177,7 +178,7 @@ __device__ __forceinline__ void put16(float* Z, int ldz, const f32x4& acc, float
 //           A_31 = −(A_32 Y01 + D_3 Y11)   (one block per wave).
 // The block products are fp32 MFMAs on LDS operands; sT holds two [16][17]
 // scratch blocks per wave.
-template <int LL>
+template <int LL, int NTHR>
 __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float* sT) {
     const int w = wave_id(), l = lane_id();
     constexpr int LT = 17;
@@ -186,7 +187,7 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
     auto Lb = [&](int i, int j) { return sL + 16 * i * LL + 16 * j; };
     auto Ab = [&](int i, int j) { return sAf + 16 * i * LL + 16 * j; };
     // step 1 (+ zero the blocks above the diagonal)
-    if (l < 16) {
+    if (w < 4 && l < 16) {
         const float* L = Lb(w, w);
         float a[16];
 #pragma unroll
@@ -200,7 +201,7 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
 #pragma unroll
         for (int r = 0; r < 16; r++) D[r * LL + l] = a[r];
     }
-    for (int idx = threadIdx.x; idx < 6 * 256; idx += 256) {
+    for (int idx = threadIdx.x; idx < 6 * 256; idx += NTHR) {
         const int blk = idx >> 8, e = idx & 255;
         const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2), bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
         Ab(bi, bj)[(e >> 4) * LL + (e & 15)] = 0.f;
@@ -209,7 +210,8 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
     // step 2
     {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (w < 2) {
+        if (w >= 4) {
+        } else if (w < 2) {
             const int i = 2 * w + 1, j = 2 * w;            // (1,0) or (3,2)
             mm16(acc, Lb(i, j), LL, Ab(j, j), LL);
             put16(t0, LT, acc, 1.f);
@@ -249,7 +251,7 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
         } else if (w == 1) {
             mm16(acc, Ab(2, 2), LL, Y01, LT);        // A_21 = −D_2 Y01
             put16(Ab(2, 1), LL, acc, -1.f);
-        } else {
+        } else if (w == 3) {
             mm16(acc, Ab(3, 2), LL, Y01, LT);        // A_31 = −(A_32 Y01 + D_3 Y11)
             mm16(acc, Ab(3, 3), LL, Y11, LT);
             put16(Ab(3, 1), LL, acc, -1.f);
@@ -258,12 +260,18 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
     lds_barrier();
 }
 
-// Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...;
-// 256 threads.  The next unit's K, V, Q, gate and β are loaded into registers
+// Waves per workgroup: 8 for 16-bit inputs (two per SIMD, so one wave's
+// element-wise and LDS work overlaps the other's), 4 for fp32 (whose fp32 MFMA
+// operands need the larger register share of one wave per SIMD).
+template <class E> constexpr int prep_waves() { return sizeof(E) == 2 ? 8 : 4; }
+
+// Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...
+// Every 64-row product is tiled over the waves as two row halves x (waves / 2)
+// column blocks.  The next unit's K, V, Q, gate and β are loaded into registers
 // right after the current ones are staged in LDS, so those loads are in flight
 // while the current unit is computed.  E: input type; S: scan operand type.
 template <class E, class S, int KD, int VD, bool WITH_R>
-__global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const float* __restrict__ gcum,
                                                    const E* __restrict__ beta, const ChunkInfo* __restrict__ info,
                                                    int HK, int HV, float scale, S* __restrict__ Wg,
@@ -271,7 +279,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                                                    S* __restrict__ KTg, int nunits) {
     static_assert(sizeof(E) == sizeof(S), "input and scan types share a width");
     using Cf = PrepCfg<E, S, KD, VD>;
-    constexpr int C = 64, NTHR = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
+    constexpr int C = 64, NTHR = 64 * prep_waves<E>(), NCB = prep_waves<E>() / 2;
+    constexpr int LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
     constexpr int EPV = 16 / (int)sizeof(E);
     extern __shared__ __align__(16) unsigned char smem[];
     S* sK = (S*)(smem + Cf::oK);
@@ -288,6 +297,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     float* sB = sG + C;
 
     const int w = wave_id();
+    const int m0 = 32 * (w & 1);                // row half of every 64-row output
+    static_assert(C * KD / EPV % NTHR == 0 && C * VD / EPV % NTHR == 0, "whole vectors per thread");
     constexpr int NKV = C * KD / EPV / NTHR, NVV = C * VD / EPV / NTHR;
     typename Vec16<E>::t rk[NKV], rv[NVV], rq[WITH_R ? NKV : 1];
     float rg = 0.f;
@@ -364,18 +375,19 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     // ---- the next unit's loads fly during this unit's compute
     if (un < nunits) issue(un, nxt_len, nxt_t0);
 
-    // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32x32 block)
+    // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32 rows x 64/NCB columns)
     {
-        const int m0 = 32 * (w & 1), n0 = 32 * (w >> 1);
-        f32x4 akk[2][2], aqk[2][2];
+        constexpr int TN = 4 / NCB;
+        const int n0 = (64 / NCB) * (w >> 1);
+        f32x4 akk[2][TN], aqk[2][TN];
         zero_acc(akk);
-        wgemm<S, 2, 2, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
+        wgemm<S, 2, TN, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
         if (WITH_R) {
             zero_acc(aqk);
-            wgemm<S, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+            wgemm<S, 2, TN, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
         }
         // branch-free: Γ_rc = exp(min(G_r − G_c, 0)), then masked by a select
-        float gr[2][4], br[2][4], gc[2];
+        float gr[2][4], br[2][4], gc[TN];
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -384,11 +396,11 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
                 br[i][e] = sB[acc_row(m0, i, e)];
             }
 #pragma unroll
-        for (int j = 0; j < 2; j++) gc[j] = sG[acc_col(n0, j)];
+        for (int j = 0; j < TN; j++) gc[j] = sG[acc_col(n0, j)];
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < TN; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = acc_row(m0, i, e), c = acc_col(n0, j);
@@ -401,7 +413,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     lds_barrier();
 
     // ---- A = (I+L)^{-1}
-    tri_inverse64<LL>(sL, sAf, sT);
+    tri_inverse64<LL, NTHR>(sL, sAf, sT);
 
     // ---- A diag(βγ), A diag(β) as MFMA operands; A itself to memory (input type)
     {
@@ -424,43 +436,44 @@ __global__ void __launch_bounds__(256) prep_kernel(const E* __restrict__ q, cons
     }
     lds_barrier();
 
-    // ---- W = A diag(βγ) K, U = A diag(β) V     (wave w: all 64 rows, KD/4 resp. VD/4 columns)
-    constexpr int TNK = KD / 64, TNV = VD / 64;
-    f32x4 aw[4][TNK], au[4][TNV];
+    // ---- W = A diag(βγ) K, U = A diag(β) V     (wave w: 32 rows, KD/NCB resp. VD/NCB columns)
+    constexpr int TNK = KD / 16 / NCB, TNV = VD / 16 / NCB;
+    const int n0k = (KD / NCB) * (w >> 1), n0v = (VD / NCB) * (w >> 1);
+    f32x4 aw[2][TNK], au[2][TNV];
     zero_acc(aw);
     zero_acc(au);
-    wgemm<S, 4, TNK, 64, false, true>(aw, sAw, LA, sK, LK, 0, w * (KD / 4));
-    wgemm<S, 4, TNV, 64, false, true>(au, sAu, LA, sV, LV, 0, w * (VD / 4));
+    wgemm<S, 2, TNK, 64, false, true>(aw, sAw, LA, sK, LK, m0, n0k);
+    wgemm<S, 2, TNV, 64, false, true>(au, sAu, LA, sV, LV, m0, n0v);
     lds_barrier();   // V is overwritten by U below
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int r = acc_row(0, i, e);
+            const int r = acc_row(m0, i, e);
 #pragma unroll
-            for (int j = 0; j < TNK; j++) sW[r * LK + acc_col(w * (KD / 4), j)] = to_e<S>(aw[i][j][e]);
+            for (int j = 0; j < TNK; j++) sW[r * LK + acc_col(n0k, j)] = to_e<S>(aw[i][j][e]);
 #pragma unroll
-            for (int j = 0; j < TNV; j++) sV[r * LV + acc_col(w * (VD / 4), j)] = to_e<S>(au[i][j][e]);
+            for (int j = 0; j < TNV; j++) sV[r * LV + acc_col(n0v, j)] = to_e<S>(au[i][j][e]);
         }
     lds_barrier();
 
     if (WITH_R) {
         // ---- R = scale diag(γ) Q − Pm W
-        f32x4 ar[4][TNK];
+        f32x4 ar[2][TNK];
         zero_acc(ar);
-        wgemm<S, 4, TNK, 64, false, true>(ar, sPm, LA, sW, LK, 0, w * (KD / 4));
+        wgemm<S, 2, TNK, 64, false, true>(ar, sPm, LA, sW, LK, m0, n0k);
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
         store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, sV);
         S* sR = sK;   // K is no longer read
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int r = acc_row(0, i, e);
+                const int r = acc_row(m0, i, e);
                 const float gr = __expf(sG[r]);
 #pragma unroll
                 for (int j = 0; j < TNK; j++) {
-                    const int c = acc_col(w * (KD / 4), j);
+                    const int c = acc_col(n0k, j);
                     sR[r * LK + c] = to_e<S>(scale * gr * (float)sQ[r * LK + c] - ar[i][j][e]);
                 }
             }
@@ -494,13 +507,13 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
         auto kern = prep_kernel<E, S, KD, VD, true>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
+        hipLaunchKernelGGL(kern, grid, dim3(64 * prep_waves<E>()), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
                            info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A, (S*)KT, (int)nunits);
     } else {
         auto kern = prep_kernel<E, S, KD, VD, false>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kern, grid, dim3(256), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
+        hipLaunchKernelGGL(kern, grid, dim3(64 * prep_waves<E>()), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
                            info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A, (S*)KT, (int)nunits);
     }
     return hipGetLastError();
