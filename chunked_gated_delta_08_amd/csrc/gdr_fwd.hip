@@ -67,20 +67,27 @@ struct FwdCfg {
     static_assert(smem <= 160 * 1024, "LDS budget");
 };
 
-// Grid (chunks, HV), 256 threads (4 waves).  E: input type; S: operand type of
-// the workspace tiles and of the MFMAs (fp16 for 16-bit inputs, fp32 for fp32).
+// Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...;
+// 512 threads (8 waves, two per SIMD); wave w computes rows 32 (w & 1) .. +31
+// and column block w >> 1 of every output.  The next unit's Q, K, W, U, h and
+// gate are loaded into registers while the current unit is computed.
+// E: input type; S: operand type of the workspace tiles and of the MFMAs (fp16
+// for 16-bit inputs, fp32 for fp32).
 template <class E, class S, int KD, int VD>
-__global__ void __launch_bounds__(256) fwd_out_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                       const float* __restrict__ gcum, const ChunkInfo* __restrict__ info,
                                                       const S* __restrict__ Wg, const S* __restrict__ Ug,
                                                       const E* __restrict__ hT, E* __restrict__ o, int HK, int HV,
-                                                      float scale) {
+                                                      float scale, int nunits) {
+    static_assert(sizeof(E) == sizeof(S), "input and operand types share a width");
     using Cf = FwdCfg<S, KD, VD>;
-    constexpr int C = 64, NT = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA;
-    constexpr int EPE = 16 / (int)sizeof(E), EPS = 16 / (int)sizeof(S);
+    constexpr int C = 64, NT = 512, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA;
+    constexpr int EPE = 16 / (int)sizeof(E);
     static_assert(C * LV * sizeof(E) <= C * LK * sizeof(S), "o tile fits in the K buffer");
+    static_assert(C * KD / EPE % NT == 0 && C * VD / EPE % NT == 0 && KD * VD / EPE % NT == 0, "whole vectors");
+    constexpr int NQ = C * KD / EPE / NT, NU = C * VD / EPE / NT, NH = KD * VD / EPE / NT;
     using VE = vec_t<E, EPE>;
-    using VS = vec_t<S, EPE>;   // EPE elements of S (the 16-byte input vector, converted)
+    using VS = vec_t<S, EPE>;
     extern __shared__ __align__(16) unsigned char smem[];
     S* sQ = (S*)(smem + Cf::oQ);
     S* sK = (S*)(smem + Cf::oK);
@@ -90,120 +97,147 @@ __global__ void __launch_bounds__(256) fwd_out_kernel(const E* __restrict__ q, c
     S* sPm = (S*)(smem + Cf::oPm);
     float* sG = (float*)(smem + Cf::oG);
     E* sO = (E*)(smem + Cf::oK);
-
-    const int ci = blockIdx.x, hv = blockIdx.y, hk = hv / (HV / HK);
-    const int Cn = info[ci].len;
-    const long t0 = info[ci].t0;
-    const long unit = (long)ci * HV + hv;
     const int w = wave_id();
+    const int m0 = 32 * (w & 1);
 
-    // ---- stage Q, K (rows past the chunk are zero), W, U, h[c], G
-    for (int idx = threadIdx.x; idx < C * KD / EPE; idx += NT) {
-        const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
-        const VE xq = *(const VE*)(q + ((t0 + rc) * HK + hk) * KD + c);
-        const VE xk = *(const VE*)(k + ((t0 + rc) * HK + hk) * KD + c);
-        VS yq, yk;
+    VE rq[NQ], rk[NQ], rh[NH];
+    VS rw[NQ], ru[NU];
+    float rg = 0.f;
+    // loads of unit u (rows past the chunk read its last row; zeroed when staged)
+    auto issue = [&](int u, int Cu, long tu) {
+        const int hvu = u % HV, hku = hvu / (HV / HK);
+        const long unit = (long)(u / HV) * HV + hvu;
+        if (threadIdx.x < C) rg = gcum[(tu + min((int)threadIdx.x, Cu - 1)) * HV + hvu];
 #pragma unroll
-        for (int e = 0; e < EPE; e++) {
-            yq[e] = r < Cn ? (S)(float)xq[e] : (S)0.f;
-            yk[e] = r < Cn ? (S)(float)xk[e] : (S)0.f;
+        for (int i = 0; i < NQ; i++) {
+            const int idx = threadIdx.x + NT * i, r = min(idx / (KD / EPE), Cu - 1), c = (idx % (KD / EPE)) * EPE;
+            rq[i] = *(const VE*)(q + ((tu + r) * HK + hku) * KD + c);
+            rk[i] = *(const VE*)(k + ((tu + r) * HK + hku) * KD + c);
+            rw[i] = *(const VS*)(Wg + unit * C * KD + (long)idx * EPE);
         }
-        *(VS*)(sQ + r * LK + c) = yq;
-        *(VS*)(sK + r * LK + c) = yk;
-    }
-    for (int idx = threadIdx.x; idx < C * KD / EPS; idx += NT) {
-        const int r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
-        *(vec_t<S, EPS>*)(sW + r * LK + c) = *(const vec_t<S, EPS>*)(Wg + (unit * C + r) * KD + c);
-    }
-    for (int idx = threadIdx.x; idx < C * VD / EPS; idx += NT) {
-        const int r = idx / (VD / EPS), c = (idx % (VD / EPS)) * EPS;
-        *(vec_t<S, EPS>*)(sVn + r * LV + c) = *(const vec_t<S, EPS>*)(Ug + (unit * C + r) * VD + c);
-    }
-    {
-        const E* blk = hT + unit * KD * VD;
-        if constexpr (sizeof(E) == 2) {
-            // 16-byte piece c of the state block: column 16 cb + (c % 16) of the
-            // key block sb, keys 32 sb + 4 g + {0..3} and 32 sb + 16 + 4 g + {0..3}
-            // with g = (c % 64) / 16, cb = (c / 64) / (KD / 32), sb = (c / 64) % (KD / 32)
-            for (int c = threadIdx.x; c < KD * VD / 8; c += NT) {
+#pragma unroll
+        for (int i = 0; i < NU; i++) ru[i] = *(const VS*)(Ug + unit * C * VD + (long)(threadIdx.x + NT * i) * EPE);
+#pragma unroll
+        for (int i = 0; i < NH; i++) rh[i] = *(const VE*)(hT + unit * KD * VD + (long)(threadIdx.x + NT * i) * EPE);
+    };
+
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    int cur_len = info[u / HV].len;
+    long cur_t0 = info[u / HV].t0;
+    issue(u, cur_len, cur_t0);
+    for (; u < nunits; u += gridDim.x) {
+        const int hv = u % HV, Cn = cur_len;
+        const long t0 = cur_t0;
+        const int un = u + (int)gridDim.x;
+        const int nxt_len = un < nunits ? info[un / HV].len : 1;
+        const long nxt_t0 = un < nunits ? info[un / HV].t0 : 0;
+
+        // ---- stage Q, K (rows past the chunk zero), W, U, h[c] (as [V][K] rows), G
+        if (threadIdx.x < C) sG[threadIdx.x] = rg;
+#pragma unroll
+        for (int i = 0; i < NQ; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE;
+            VS yq, yk;
+#pragma unroll
+            for (int e = 0; e < EPE; e++) {
+                yq[e] = r < Cn ? (S)(float)rq[i][e] : (S)0.f;
+                yk[e] = r < Cn ? (S)(float)rk[i][e] : (S)0.f;
+            }
+            *(VS*)(sQ + r * LK + c) = yq;
+            *(VS*)(sK + r * LK + c) = yk;
+            *(VS*)(sW + r * LK + c) = rw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NU; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
+            *(VS*)(sVn + r * LV + c) = ru[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NH; i++) {
+            const int c = threadIdx.x + NT * i;
+            if constexpr (sizeof(E) == 2) {
+                // 16-byte piece c of the state block: column 16 cb + (c % 16) of the
+                // key block sb, keys 32 sb + 4 g + {0..3} and 32 sb + 16 + 4 g + {0..3}
+                // with g = (c % 64) / 16, cb = (c / 64) / (KD / 32), sb = (c / 64) % (KD / 32)
                 const int ln = c & 63, sb = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
                 const int row = 16 * cb + (ln & 15), key = 32 * sb + 4 * (ln >> 4);
-                const vec_t<E, 8> x = *(const vec_t<E, 8>*)(blk + (long)c * 8);
                 vec_t<S, 4> lo, hi;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    lo[e] = (S)(float)x[e];
-                    hi[e] = (S)(float)x[4 + e];
+                    lo[e] = (S)(float)rh[i][e];
+                    hi[e] = (S)(float)rh[i][4 + e];
                 }
                 *(vec_t<S, 4>*)(sH + row * LK + key) = lo;
                 *(vec_t<S, 4>*)(sH + row * LK + key + 16) = hi;
-            }
-        } else {   // fp32 states are stored [V][K]
-            for (int c = threadIdx.x; c < KD * VD / 4; c += NT) {
+            } else {   // fp32 states are stored [V][K]
                 const int row = (c * 4) / KD, key = (c * 4) % KD;
-                *(vec_t<S, 4>*)(sH + row * LK + key) = *(const vec_t<S, 4>*)(blk + (long)row * KD + key);
+                *(VS*)(sH + row * LK + key) = rh[i];
             }
         }
-    }
-    if (threadIdx.x < C) sG[threadIdx.x] = gcum[(t0 + min((int)threadIdx.x, Cn - 1)) * HV + hv];
-    lds_barrier();
+        lds_barrier();
+        // ---- the next unit's loads fly during this unit's compute
+        if (un < nunits) issue(un, nxt_len, nxt_t0);
 
-    // ---- Pm = scale · lower(Γ ⊙ Q Kᵀ), Γ[r][c] = exp(G_r − G_c)   (wave w: a 32 x 32 block)
-    {
-        const int m0 = 32 * (w & 1), n0 = 32 * (w >> 1);
-        f32x4 aqk[2][2];
-        zero_acc(aqk);
-        wgemm<S, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+        // ---- Pm = scale · lower(Γ ⊙ Q Kᵀ), Γ[r][c] = exp(G_r − G_c)   (wave w: a 32 x 16 block)
+        {
+            const int n0 = 16 * (w >> 1);
+            f32x4 aqk[2][1];
+            zero_acc(aqk);
+            wgemm<S, 2, 1, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int r = acc_row(m0, i, e), c = acc_col(n0, j);
-                    const float x = scale * __expf(sG[r] - sG[c]) * aqk[i][j][e];
+                    const int r = acc_row(m0, i, e), c = acc_col(n0, 0);
+                    const float x = scale * __expf(sG[r] - sG[c]) * aqk[i][0][e];
                     sPm[r * LA + c] = (S)(c <= r ? x : 0.f);
                 }
-    }
-    // ---- W h and Q h   (wave w: 32 rows x VD/2 columns); V_new = U − W h in place
-    constexpr int TN = VD / 32;
-    const int m0 = 32 * (w & 1), n0 = (VD / 2) * (w >> 1);
-    f32x4 qh[2][TN];
-    {
-        f32x4 wh[2][TN];
-        zero_acc(wh);
-        zero_acc(qh);
-        wgemm<S, 2, TN, KD, false, false>(wh, sW, LK, sH, LK, m0, n0);
-        wgemm<S, 2, TN, KD, false, false>(qh, sQ, LK, sH, LK, m0, n0);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = acc_row(m0, i, e), c = acc_col(n0, j);
-                    sVn[r * LV + c] = (S)((float)sVn[r * LV + c] - wh[i][j][e]);
-                }
-    }
-    lds_barrier();   // Pm and V_new complete; K is no longer read
-    // ---- o = scale · diag(γ) Q h + Pm V_new
-    f32x4 ov[2][TN];
-    zero_acc(ov);
-    wgemm<S, 2, TN, 64, false, true>(ov, sPm, LA, sVn, LV, m0, n0);
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int r = acc_row(m0, i, 0) + e;
-            const float gq = scale * __expf(sG[r]);
-#pragma unroll
-            for (int j = 0; j < TN; j++) sO[r * LV + acc_col(n0, j)] = (E)(ov[i][j][e] + gq * qh[i][j][e]);
         }
-    }
-    lds_barrier();
-    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
-        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
-        if (r < Cn) *(VE*)(o + ((t0 + r) * HV + hv) * VD + c) = *(const VE*)(sO + r * LV + c);
+        // ---- W h and Q h   (wave w: 32 rows x VD/4 columns); V_new = U − W h in place
+        constexpr int TN = VD / 64;
+        const int n0 = (VD / 4) * (w >> 1);
+        f32x4 qh[2][TN];
+        {
+            f32x4 wh[2][TN];
+            zero_acc(wh);
+            zero_acc(qh);
+            wgemm<S, 2, TN, KD, false, false>(wh, sW, LK, sH, LK, m0, n0);
+            wgemm<S, 2, TN, KD, false, false>(qh, sQ, LK, sH, LK, m0, n0);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int r = acc_row(m0, i, e), c = acc_col(n0, j);
+                        sVn[r * LV + c] = (S)((float)sVn[r * LV + c] - wh[i][j][e]);
+                    }
+        }
+        lds_barrier();   // Pm and V_new complete; K is no longer read
+        // ---- o = scale · diag(γ) Q h + Pm V_new
+        f32x4 ov[2][TN];
+        zero_acc(ov);
+        wgemm<S, 2, TN, 64, false, true>(ov, sPm, LA, sVn, LV, m0, n0);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = acc_row(m0, i, 0) + e;
+                const float gq = scale * __expf(sG[r]);
+#pragma unroll
+                for (int j = 0; j < TN; j++) sO[r * LV + acc_col(n0, j)] = (E)(ov[i][j][e] + gq * qh[i][j][e]);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < NU; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
+            if (r < Cn) *(VE*)(o + ((t0 + r) * HV + hv) * VD + c) = *(const VE*)(sO + r * LV + c);
+        }
+        lds_barrier();   // the next unit is staged over this one's LDS
+        cur_len = nxt_len;
+        cur_t0 = nxt_t0;
     }
 }
 
@@ -213,8 +247,12 @@ static hipError_t fwd_out_go(const Problem& p, const FwdArgs& a, hipStream_t s) 
     auto kern = fwd_out_kernel<E, S, KD, VD>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), Cf::smem, s, (const E*)a.q, (const E*)a.k, a.gcum,
-                       a.info, (const S*)a.W, (const S*)a.U, (const E*)a.hT, (E*)a.o, p.HK, p.HV, p.scale);
+    const long nunits = p.NT * p.HV;
+    if (nunits > INT32_MAX) return hipErrorInvalidValue;
+    // one persistent workgroup per CU (the LDS carve-up allows one), 256 CUs
+    const unsigned grid = (unsigned)(nunits < 256 ? nunits : 256);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), Cf::smem, s, (const E*)a.q, (const E*)a.k, a.gcum, a.info,
+                       (const S*)a.W, (const S*)a.U, (const E*)a.hT, (E*)a.o, p.HK, p.HV, p.scale, (int)nunits);
     return hipGetLastError();
 }
 
