@@ -34,6 +34,8 @@
  *                       independent derivation used for self-checks and for
  *                       the per-chunk states h[c] / dh[c].          [pinned]
  *   orc_kda_wy_bwd      exact VJP of the KDA WY-stage functional (O-K). [pinned]
+ *   orc_kda_fwd_token   KDA (per-channel gate) token recurrence, forward. [pinned]
+ *   orc_kda_bwd_token   its hand-derived reverse-time gradients (O-KF).   [pinned]
  *   orc_gcum_to_graw    recovers the raw gate from its in-chunk cumsum.
  *   orc_gate_cumsum     the in-chunk cumulative sum itself, in fp64. [pinned]
  * "Pinned" = checked by tests/test_oracle_*.py against finite differences,
@@ -673,6 +675,166 @@ int orc_kda_wy_bwd(const orc_problem *p, int BT, const double *q, const double *
 #undef BB_
             }
             free(A); free(X); free(dw); free(AdW); free(AdV); free(dks); free(dAp); free(T);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KDA: the gated delta rule with a per-channel gate ([P2] 概述: the operator
+ * is one stage of the KDA chunk backward).  State S (K x V) per sequence and
+ * head (HK == HV == H), gate a_t = exp(ĝ_t) in R^K applied before the delta
+ * update:
+ *   X = diag(a_t) S_{t−1},  u_t = v_t − Xᵀ k_t,  S_t = X + b_t k_t u_tᵀ
+ *   (= (I − b_t k_t k_tᵀ) diag(a_t) S_{t−1} + b_t k_t v_tᵀ),
+ *   o_t = scale S_tᵀ q_t.
+ * Layouts: q, k, ĝ [NTOK,H,K]; v, dO [NTOK,H,V]; b [NTOK,H]; states [N,H,K,V]. */
+static void kda_step(double *S, int K, int V, const double *kk, const double *vv, const double *ga, double b,
+                     double *u) {
+    for (int i = 0; i < K; i++) {
+        const double a = exp(ga[i]);
+        for (int j = 0; j < V; j++) S[i * V + j] *= a;
+    }
+    for (int j = 0; j < V; j++) {
+        double s = 0;
+        for (int i = 0; i < K; i++) s += S[i * V + j] * kk[i];
+        u[j] = vv[j] - s;
+    }
+    for (int i = 0; i < K; i++)
+        for (int j = 0; j < V; j++) S[i * V + j] += b * kk[i] * u[j];
+}
+
+int orc_kda_fwd_token(const orc_problem *p, const double *q, const double *k, const double *v, const double *graw,
+                      const double *beta, const double *h0, double *o, double *ht) {
+    const int K = p->K, V = p->V, H = p->HV;
+    const int NS = orc_num_seqs(p);
+    if (p->HK != p->HV) return -1;
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int n = 0; n < NS; n++)
+        for (int h = 0; h < H; h++) {
+            int64_t bos, len; seq_range(p, n, &bos, &len);
+            double *S = (double *)calloc((size_t)K * V, sizeof(double));
+            double *u = (double *)malloc(sizeof(double) * V);
+            if (h0) memcpy(S, h0 + ((size_t)n * H + h) * K * V, sizeof(double) * K * V);
+            for (int64_t t = 0; t < len; t++) {
+                const int64_t tok = bos + t;
+                kda_step(S, K, V, k + ((size_t)tok * H + h) * K, v + ((size_t)tok * H + h) * V,
+                         graw + ((size_t)tok * H + h) * K, beta[tok * H + h], u);
+                if (o) {
+                    const double *qq = q + ((size_t)tok * H + h) * K;
+                    double *oo = o + ((size_t)tok * H + h) * V;
+                    for (int j = 0; j < V; j++) {
+                        double s = 0;
+                        for (int i = 0; i < K; i++) s += S[i * V + j] * qq[i];
+                        oo[j] = p->scale * s;
+                    }
+                }
+            }
+            if (ht) memcpy(ht + ((size_t)n * H + h) * K * V, S, sizeof(double) * K * V);
+            free(u);
+            free(S);
+        }
+    return 0;
+}
+
+/* O-KF: reverse-time gradients of L = Σ_t <dO_t, o_t> + <dht, S_T> for the KDA
+ * recurrence, derived by hand from the step above (X, u as there):
+ *   dS_t += scale q_t dO_tᵀ,        dq_t = scale S_t dO_t
+ *   du = b dS_tᵀ k,  dv_t = du,     db_t = kᵀ dS_t u
+ *   dk_t = b dS_t u − X du,         dX = dS_t − k duᵀ
+ *   dĝ_t = rowsum(dX ⊙ X),          dS_{t−1} = diag(a_t) dX
+ * States are checkpointed every CKPT tokens and recomputed per segment.      */
+int orc_kda_bwd_token(const orc_problem *p, const double *q, const double *k, const double *v, const double *graw,
+                      const double *beta, const double *h0, const double *dO, const double *dht,
+                      double *dq, double *dk, double *dv, double *dg, double *dbeta, double *dh0) {
+    const int K = p->K, V = p->V, H = p->HV;
+    const int NS = orc_num_seqs(p);
+    if (p->HK != p->HV) return -1;
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int n = 0; n < NS; n++)
+        for (int h = 0; h < H; h++) {
+            int64_t bos, len; seq_range(p, n, &bos, &len);
+            const size_t KV = (size_t)K * V;
+            const int64_t nck = (len + CKPT - 1) / CKPT;
+            double *ck = (double *)malloc(sizeof(double) * KV * (nck > 0 ? nck : 1));
+            double *seg = (double *)malloc(sizeof(double) * KV * (CKPT + 1));
+            double *dS = (double *)malloc(sizeof(double) * KV);
+            double *X = (double *)malloc(sizeof(double) * KV);
+            double *u = (double *)malloc(sizeof(double) * V);
+            double *du = (double *)malloc(sizeof(double) * V);
+            double *w = (double *)malloc(sizeof(double) * V);
+            double *S = seg;
+            if (h0) memcpy(S, h0 + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+            else memset(S, 0, sizeof(double) * KV);
+            for (int64_t t = 0; t < len; t++) {
+                if (t % CKPT == 0) memcpy(ck + (t / CKPT) * KV, S, sizeof(double) * KV);
+                const int64_t tok = bos + t;
+                kda_step(S, K, V, k + ((size_t)tok * H + h) * K, v + ((size_t)tok * H + h) * V,
+                         graw + ((size_t)tok * H + h) * K, beta[tok * H + h], w);
+            }
+            if (dht) memcpy(dS, dht + ((size_t)n * H + h) * KV, sizeof(double) * KV);
+            else memset(dS, 0, sizeof(double) * KV);
+            for (int64_t sgi = nck - 1; sgi >= 0; sgi--) {
+                const int64_t t0 = sgi * CKPT, t1 = t0 + CKPT < len ? t0 + CKPT : len;
+                memcpy(seg, ck + sgi * KV, sizeof(double) * KV);
+                for (int64_t t = t0; t < t1; t++) {
+                    const int64_t tok = bos + t;
+                    double *Sn = seg + (t - t0 + 1) * KV;
+                    memcpy(Sn, seg + (t - t0) * KV, sizeof(double) * KV);
+                    kda_step(Sn, K, V, k + ((size_t)tok * H + h) * K, v + ((size_t)tok * H + h) * V,
+                             graw + ((size_t)tok * H + h) * K, beta[tok * H + h], w);
+                }
+                for (int64_t t = t1 - 1; t >= t0; t--) {
+                    const int64_t tok = bos + t;
+                    const double *St = seg + (t - t0 + 1) * KV, *Sp = seg + (t - t0) * KV;
+                    const double *qq = q + ((size_t)tok * H + h) * K, *kk = k + ((size_t)tok * H + h) * K;
+                    const double *vv = v + ((size_t)tok * H + h) * V, *dd = dO + ((size_t)tok * H + h) * V;
+                    const double *ga = graw + ((size_t)tok * H + h) * K;
+                    const double b = beta[tok * H + h];
+                    for (int i = 0; i < K; i++)
+                        for (int j = 0; j < V; j++) dS[i * V + j] += p->scale * qq[i] * dd[j];
+                    double *dqq = dq + ((size_t)tok * H + h) * K;
+                    for (int i = 0; i < K; i++) {
+                        double s = 0;
+                        for (int j = 0; j < V; j++) s += St[i * V + j] * dd[j];
+                        dqq[i] = p->scale * s;
+                    }
+                    /* X = diag(a) S_{t−1}, u = v − Xᵀk */
+                    for (int i = 0; i < K; i++) {
+                        const double a = exp(ga[i]);
+                        for (int j = 0; j < V; j++) X[i * V + j] = a * Sp[i * V + j];
+                    }
+                    for (int j = 0; j < V; j++) {
+                        double s = 0, s2 = 0;
+                        for (int i = 0; i < K; i++) { s += X[i * V + j] * kk[i]; s2 += dS[i * V + j] * kk[i]; }
+                        u[j] = vv[j] - s;
+                        du[j] = b * s2;
+                    }
+                    double *dvv = dv + ((size_t)tok * H + h) * V;
+                    for (int j = 0; j < V; j++) dvv[j] = du[j];
+                    double db = 0;
+                    double *dkk = dk + ((size_t)tok * H + h) * K;
+                    for (int i = 0; i < K; i++) {
+                        double su = 0, xd = 0;
+                        for (int j = 0; j < V; j++) { su += dS[i * V + j] * u[j]; xd += X[i * V + j] * du[j]; }
+                        db += kk[i] * su;
+                        dkk[i] = b * su - xd;
+                    }
+                    dbeta[tok * H + h] = db;
+                    double *dgg = dg + ((size_t)tok * H + h) * K;
+                    for (int i = 0; i < K; i++) {
+                        const double a = exp(ga[i]);
+                        double s = 0;
+                        for (int j = 0; j < V; j++) {
+                            const double dx = dS[i * V + j] - kk[i] * du[j];
+                            s += dx * X[i * V + j];
+                            dS[i * V + j] = a * dx;
+                        }
+                        dgg[i] = s;
+                    }
+                }
+            }
+            if (dh0) memcpy(dh0 + ((size_t)n * H + h) * KV, dS, sizeof(double) * KV);
+            free(w); free(du); free(u); free(X); free(dS); free(seg); free(ck);
         }
     return 0;
 }

@@ -148,3 +148,29 @@ def kda_wy_bwd(prob, BT, q, k, v, v_new, g, beta, A, h, dO, dh, dv):
                                _ptr(o["dA"]))
     assert rc == 0
     return o
+
+
+def kda_fwd_token(prob, q, k, v, graw, beta, h0=None):
+    """KDA (per-channel gate) token recurrence: o [NTOK,H,V], ht [N,H,K,V].
+    graw is the raw per-channel log-gate [NTOK,H,K]; HK == HV == H."""
+    q, k, v, graw, beta, h0 = map(_f64, (q, k, v, graw, beta, h0))
+    o = np.zeros((prob.ntok, prob.HV, prob.V))
+    ht = np.zeros((prob.N, prob.HV, prob.K, prob.V))
+    rc = _lib().orc_kda_fwd_token(ctypes.byref(prob._c()), _ptr(q), _ptr(k), _ptr(v), _ptr(graw), _ptr(beta),
+                                  _ptr(h0), _ptr(o), _ptr(ht))
+    assert rc == 0
+    return {"o": o, "ht": ht}
+
+
+def kda_bwd_token(prob, q, k, v, graw, beta, h0, dO, dht):
+    """O-KF: gradients of sum<dO,o> + <dht,S_T> for the KDA recurrence.
+    Returns dq, dk, dg [NTOK,H,K]; dv [NTOK,H,V]; dbeta [NTOK,H]; dh0 [N,H,K,V]."""
+    q, k, v, graw, beta, h0, dO, dht = map(_f64, (q, k, v, graw, beta, h0, dO, dht))
+    n, H, K, V = prob.ntok, prob.HV, prob.K, prob.V
+    o = {"dq": np.zeros((n, H, K)), "dk": np.zeros((n, H, K)), "dv": np.zeros((n, H, V)),
+         "dg": np.zeros((n, H, K)), "dbeta": np.zeros((n, H)), "dh0": np.zeros((prob.N, H, K, V))}
+    rc = _lib().orc_kda_bwd_token(ctypes.byref(prob._c()), _ptr(q), _ptr(k), _ptr(v), _ptr(graw), _ptr(beta),
+                                  _ptr(h0), _ptr(dO), _ptr(dht), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]),
+                                  _ptr(o["dg"]), _ptr(o["dbeta"]), _ptr(o["dh0"]))
+    assert rc == 0
+    return o

@@ -15,7 +15,10 @@ fails at least one of them:
 * linearity in the cotangents; varlen == per-sequence runs; GQA == repeated
   heads summed; an independent fp64 torch-autograd derivation;
 * the in-chunk gate cumsum: a case worked by hand, its inverse, and the plain
-  cumsum when one chunk covers each sequence.
+  cumsum when one chunk covers each sequence;
+* the full KDA recurrence (per-channel gate): finite differences of every
+  gradient, the channel-constant gate reproducing the GDN oracle, and the
+  b = 0 closed form.
 """
 import numpy as np
 import pytest
@@ -357,3 +360,89 @@ def test_kda_ignores_upper_triangle_of_A(oracle):
     o2 = oracle.kda_wy_bwd(p, BT, *args, g, b, A2, h, dO, dh, dv)
     for nm in o1:
         np.testing.assert_array_equal(o1[nm], o2[nm])
+
+
+# ---------------------------------------------------------------- full KDA (per-channel gate)
+def _kda_rand(rng, T, H, K, V, N=1):
+    q = rng.standard_normal((T, H, K))
+    k = rng.standard_normal((T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, V))
+    g = -rng.random((T, H, K))
+    b = rng.random((T, H))
+    h0 = rng.standard_normal((N, H, K, V))
+    dO = rng.standard_normal((T, H, V))
+    dht = rng.standard_normal((N, H, K, V))
+    return q, k, v, g, b, h0, dO, dht
+
+
+def _kda_loss(oracle, p, dO, dht, q, k, v, g, b, h0):
+    f = oracle.kda_fwd_token(p, q, k, v, g, b, h0)
+    return float((f["o"] * dO).sum() + (f["ht"] * dht).sum())
+
+
+@pytest.mark.parametrize("case", ["dense", "varlen"])
+def test_kda_full_finite_differences(oracle, case):
+    """Central finite differences of L = Σ<dO,o> + <dht,S_T> for every KDA gradient,
+    including the per-channel gate."""
+    rng = np.random.default_rng({"dense": 31, "varlen": 32}[case])
+    if case == "dense":
+        T, H, K, V, cu = 7, 1, 4, 3, None
+    else:
+        T, H, K, V, cu = 9, 2, 3, 3, [0, 4, 4, 9]
+    N = 1 if cu is None else len(cu) - 1
+    p = oracle.Problem(1, T, H, H, K, V, cu_seqlens=cu)
+    q, k, v, g, b, h0, dO, dht = _kda_rand(rng, T, H, K, V, N)
+    gr = oracle.kda_bwd_token(p, q, k, v, g, b, h0, dO, dht)
+    args = {"q": q, "k": k, "v": v, "g": g, "b": b, "h0": h0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "b": "dbeta", "h0": "dh0"}
+    eps = 1e-6
+    for nm, a in args.items():
+        num = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            vals = []
+            for s in (1, -1):
+                x = a.copy()
+                x[idx] += s * eps
+                kw = dict(args)
+                kw[nm] = x
+                vals.append(_kda_loss(oracle, p, dO, dht, **kw))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        err = np.abs(num - gr[names[nm]]).max() / np.abs(num).max()
+        assert err < RTOL_FD, (nm, err)
+
+
+def test_kda_full_channel_constant_gate_is_gdn(oracle):
+    """With the same gate on every channel the KDA recurrence is the gated delta
+    rule: forward outputs and gradients equal the (independently pinned) GDN
+    oracle's, the gate gradient summed over channels."""
+    rng = np.random.default_rng(33)
+    T, H, K, V = 150, 2, 5, 4
+    cu = [0, 70, 75, 150]
+    p = oracle.Problem(1, T, H, H, K, V, cu_seqlens=cu)
+    q, k, v, _, b, h0, dO, dht = _kda_rand(rng, T, H, K, V, N=3)
+    g1 = -0.3 * rng.random((T, H))
+    gk = np.repeat(g1[:, :, None], K, axis=2)
+    fk = oracle.kda_fwd_token(p, q, k, v, gk, b, h0)
+    fg = oracle.gdr_fwd_token(p, 0, q, k, v, g1, b, h0)
+    np.testing.assert_allclose(fk["o"], fg["o"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(fk["ht"], fg["ht"], rtol=1e-11, atol=1e-12)
+    bk = oracle.kda_bwd_token(p, q, k, v, gk, b, h0, dO, dht)
+    bg = oracle.gdr_bwd_token(p, q, k, v, g1, b, h0, dO, dht)
+    for n in ("dq", "dk", "dv", "dbeta", "dh0"):
+        np.testing.assert_allclose(bk[n], bg[n], rtol=1e-10, atol=1e-10, err_msg=n)
+    np.testing.assert_allclose(bk["dg"].sum(-1), bg["dg"], rtol=1e-10, atol=1e-10)
+
+
+def test_kda_full_beta_zero_closed_form(oracle):
+    """b = 0: S_t = diag(exp(Σ_{s<=t} ĝ_s)) h0, so o_t = scale q_tᵀ diag(Λ_t) h0."""
+    rng = np.random.default_rng(34)
+    T, H, K, V = 9, 1, 4, 3
+    p = oracle.Problem(1, T, H, H, K, V)
+    q, k, v, g, _, h0, _, _ = _kda_rand(rng, T, H, K, V)
+    b = np.zeros((T, H))
+    lam = np.exp(np.cumsum(g[:, 0], axis=0))          # [T, K]
+    f = oracle.kda_fwd_token(p, q, k, v, g, b, h0)
+    o_ref = p.scale * np.einsum("tk,tk,kv->tv", q[:, 0], lam, h0[0, 0])
+    np.testing.assert_allclose(f["o"][:, 0], o_ref, rtol=1e-12)
+    np.testing.assert_allclose(f["ht"][0, 0], lam[-1][:, None] * h0[0, 0], rtol=1e-12)
