@@ -58,11 +58,18 @@ lib.gdr_chunk_fwd.restype = ctypes.c_int
 lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp]
 lib.gdr_chunk_fwd_events.restype = ctypes.c_int
 lib.gdr_chunk_fwd_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 8 + [_vp, _sz, _vp, _vp]
+lib.kda_workspace_size.restype = _sz
+lib.kda_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+lib.kda_chunk_bwd_full.restype = ctypes.c_int
+lib.kda_chunk_bwd_full.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp]
+lib.kda_chunk_bwd_full_events.restype = ctypes.c_int
+lib.kda_chunk_bwd_full_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp, _vp]
 lib.kda_chunk_bwd.restype = ctypes.c_int
 lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
 
 EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_gate_cumsum",
-            "gdr_chunk_fwd", "gdr_chunk_fwd_events", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd"]
+            "gdr_chunk_fwd", "gdr_chunk_fwd_events", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd",
+            "kda_workspace_size", "kda_chunk_bwd_full", "kda_chunk_bwd_full_events"]
 
 
 def _check(code):
@@ -212,5 +219,34 @@ def kda_chunk_bwd(q, k, v, v_new, g, beta, A, h, dO, dh, dv, scale=None, cu_seql
     _check(lib.kda_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(v_new), _ptr(g), _ptr(beta), _ptr(A),
                              _ptr(h), _ptr(dO), _ptr(dh), _ptr(dv), _ptr(out["dq"]), _ptr(out["dk"]),
                              _ptr(out["dv"]), _ptr(out["db"]), _ptr(out["dg"]), _ptr(out["dA"]), _stream(stream)))
+    del keep
+    return out
+
+
+def kda_chunk_bwd_full(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, scale=None, BT=64,
+                       want_dh0=True, out=None, workspace=None, stream=None):
+    """Full chunked KDA backward (per-channel gate).  g_cum [B*T, H, K] fp32 in-chunk
+    cumulative log-gate.  Returns dict dq, dk, dv (input dtype), dg [B*T,H,K],
+    dbeta [B*T,H], dh0 [N,H,K,V] (fp32)."""
+    ntok, H, K = k.shape
+    V = v.shape[-1]
+    for t in (q, k, v, g_cum, beta, dO):
+        assert t.is_cuda and t.is_contiguous()
+    assert g_cum.dtype == torch.float32 and g_cum.shape == k.shape
+    T = ntok // B if cu_seqlens is None else ntok
+    p, keep = make_problem(B if cu_seqlens is None else 1, T, H, H, K, V, v.dtype, BT, cu_seqlens, scale)
+    N = B if cu_seqlens is None else p.N
+    dev = v.device
+    if out is None:
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "dg": torch.empty(g_cum.shape, dtype=torch.float32, device=dev),
+               "dbeta": torch.empty(beta.shape, dtype=torch.float32, device=dev),
+               "dh0": torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_dh0 else None}
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.kda_workspace_size(ctypes.byref(p))), 1), dtype=torch.uint8, device=dev)
+    _check(lib.kda_chunk_bwd_full(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g_cum), _ptr(beta), _ptr(h0),
+                                  _ptr(dO), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                  _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
     del keep
     return out

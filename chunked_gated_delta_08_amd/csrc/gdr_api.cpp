@@ -142,6 +142,60 @@ WsPlan plan_workspace(const Problem& p) {
 
 }  // namespace gdr
 
+namespace {
+
+// Workspace carve-up of the full KDA backward (byte offsets).
+struct KdaWsPlan {
+    size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, KT, QG, Aqk, A, hs, dhs, vn, dvn, dqs, dks, dgs, dbs,
+        dA, total;
+};
+
+KdaWsPlan plan_kda_workspace(const Problem& p) {
+    KdaWsPlan w{};
+    const size_t es = elem_size(p.dtype);
+    const size_t units = (size_t)p.NT * p.HV;
+    const size_t ntok = p.cu ? (size_t)p.T : (size_t)p.B * p.T;
+    const size_t H = p.HV;
+    size_t off = 0;
+    w.chunk_info = off; off = align256(off + (size_t)(p.NT > 0 ? p.NT : 1) * sizeof(gdr::ChunkInfo));
+    w.seq_chunk0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
+    w.seg_info = off; off = align256(off + (size_t)p.NS * sizeof(SegInfo));
+    w.seq_seg0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
+    w.W = off; off = align256(off + units * 64 * p.K * es);
+    w.U = off; off = align256(off + units * 64 * p.V * es);
+    w.KT = off; off = align256(off + units * 64 * p.K * es);
+    w.QG = off; off = align256(off + units * 64 * p.K * es);
+    w.Aqk = off; off = align256(off + units * 64 * 64 * es);
+    w.A = off; off = align256(off + ntok * H * 64 * es);
+    w.hs = off; off = align256(off + units * (size_t)p.K * p.V * 4);
+    w.dhs = off; off = align256(off + units * (size_t)p.K * p.V * 4);
+    w.vn = off; off = align256(off + ntok * H * p.V * es);
+    w.dvn = off; off = align256(off + ntok * H * p.V * es);
+    w.dqs = off; off = align256(off + ntok * H * p.K * 4);
+    w.dks = off; off = align256(off + ntok * H * p.K * 4);
+    w.dgs = off; off = align256(off + ntok * H * p.K * 4);
+    w.dbs = off; off = align256(off + ntok * H * 4);
+    w.dA = off; off = align256(off + ntok * H * 64 * 4);
+    w.total = off;
+    return w;
+}
+
+// Validation of the full KDA backward: one head count, K = V in {64, 128},
+// fp16 (or fp32 at K = 64), BT = 64; the scans are never segmented.
+int check_kda_full(const gdr_problem* p, Problem* q) {
+    if (!p) return GDR_ERR_INVALID;
+    gdr_problem pp = *p;
+    pp.seg_chunks = -1;
+    int st = check_problem(&pp, q);
+    if (st != GDR_OK) return st;
+    if (q->HK != q->HV) return GDR_ERR_INVALID;
+    if (q->BT != 64 || q->K != q->V || (q->K != 64 && q->K != 128)) return GDR_ERR_UNSUPPORTED;
+    if (q->dtype == GDR_BF16 || (q->dtype == GDR_F32 && q->K != 64)) return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* gdr_strerror(int status) {
@@ -310,6 +364,60 @@ int gdr_chunk_bwd(const gdr_problem* p, const void* qp, const void* k, const voi
                   float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes, hipStream_t stream) {
     return gdr_chunk_bwd_events(p, qp, k, v, g_cum, beta, h0, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes,
                                 stream, nullptr);
+}
+
+size_t kda_workspace_size(const gdr_problem* p) {
+    Problem q;
+    if (check_kda_full(p, &q) != GDR_OK) return 0;
+    return plan_kda_workspace(q).total;
+}
+
+int kda_chunk_bwd_full_events(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                              const void* beta, const float* h0, const void* dO, const float* dht, void* dq, void* dk,
+                              void* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t* ev) {
+    Problem q;
+    int st = check_kda_full(p, &q);
+    if (st != GDR_OK) return st;
+    if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
+        return GDR_ERR_INVALID;
+    const KdaWsPlan w = plan_kda_workspace(q);
+    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    char* base = (char*)ws;
+    auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
+    auto* sc0 = (int32_t*)(base + w.seq_chunk0);
+    if (ev && (st = launch_status(hipEventRecord(ev[0], stream))) != GDR_OK) return st;
+    st = launch_status(gdr::launch_chunk_table(q, info, sc0, (SegInfo*)(base + w.seg_info),
+                                               (int32_t*)(base + w.seq_seg0), stream));
+    if (st != GDR_OK) return st;
+    gdr::KdaFullArgs a{};
+    a.q = qp; a.k = k; a.v = v; a.gcum = g_cum; a.beta = beta; a.dO = dO; a.h0 = h0; a.dht = dht;
+    a.info = info; a.seq_chunk0 = sc0;
+    a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.QG = base + w.QG; a.Aqk = base + w.Aqk;
+    a.A = base + w.A; a.hs = (float*)(base + w.hs); a.dhs = (float*)(base + w.dhs);
+    a.vn = base + w.vn; a.dvn = base + w.dvn;
+    a.dqs = (float*)(base + w.dqs); a.dks = (float*)(base + w.dks); a.dgs = (float*)(base + w.dgs);
+    a.dbs = (float*)(base + w.dbs); a.dA = (float*)(base + w.dA);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    if (q.NT == 0) {   // no tokens: dh0 = dht (or zero) through the reverse scan alone is not launched
+        if (dh0) {
+            const size_t bytes = (size_t)q.N * q.HV * q.K * q.V * 4;
+            hipError_t e = dht ? hipMemcpyAsync(dh0, dht, bytes, hipMemcpyDeviceToDevice, stream)
+                               : hipMemsetAsync(dh0, 0, bytes, stream);
+            if ((st = launch_status(e)) != GDR_OK) return st;
+        }
+        for (int i = 1; ev && i < 5; i++)
+            if ((st = launch_status(hipEventRecord(ev[i], stream))) != GDR_OK) return st;
+        return GDR_OK;
+    }
+    return launch_status(gdr::launch_kda_full(q, a, stream, ev));
+}
+
+int kda_chunk_bwd_full(const gdr_problem* p, const void* qp, const void* k, const void* v, const float* g_cum,
+                       const void* beta, const float* h0, const void* dO, const float* dht, void* dq, void* dk,
+                       void* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return kda_chunk_bwd_full_events(p, qp, k, v, g_cum, beta, h0, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes,
+                                     stream, nullptr);
 }
 
 int kda_chunk_bwd(const gdr_problem* p, const void* qp, const void* k, const void* v, const void* v_new,

@@ -127,4 +127,22 @@ struct KdaArgs {
 };
 hipError_t launch_kda(const Problem& p, const KdaArgs& a, hipStream_t s);
 
+// Full KDA backward (kda_full.hip): arguments of all its launches.  Device
+// pointers; workspace arrays: W, K̃, Qg [NT*H][64][K] and U [NT*H][64][V] and
+// Aqk [NT*H][64][64] in the operand type; A [B*T,H,64], V_new and dV_new
+// [B*T,H,V] in the input type; h[c], dh[c] [NT,H,K,V] fp32; the WY stage's
+// partials dq, dk, dg [B*T,H,K], dβ [B*T,H], dA [B*T,H,64] fp32.
+struct KdaFullArgs {
+    const void* q; const void* k; const void* v; const float* gcum; const void* beta; const void* dO;
+    const float* h0; const float* dht;
+    const ChunkInfo* info; const int32_t* seq_chunk0;
+    void* W; void* U; void* KT; void* QG; void* Aqk; void* A;
+    float* hs; float* dhs; void* vn; void* dvn;
+    float* dqs; float* dks; float* dgs; float* dbs; float* dA;
+    void* dq; void* dk; void* dv; float* dg; float* dbeta; float* dh0;
+};
+// ev: NULL or 5 events; [1..4] are recorded after the WY factors, the scans,
+// the WY stage and the intra-chunk kernel ([0] is the caller's).
+hipError_t launch_kda_full(const Problem& p, const KdaFullArgs& a, hipStream_t s, hipEvent_t* ev);
+
 }  // namespace gdr

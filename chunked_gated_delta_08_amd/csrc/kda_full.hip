@@ -1,0 +1,602 @@
+// kda_full.hip -- the full chunked backward of KDA (the gated delta rule with a
+// per-channel gate), built around the WY stage of kda_bwd.hip.
+//
+// Page: "chunk_kda_bwd_wy_dqkg_fused 算子" (MindSpeed-Ops) -- 概述 places that
+// operator inside the KDA chunk backward ("wy representation gradient"); the
+// other steps of that backward are the state recomputation, the per-channel
+// dh scan and the intra-chunk attention / dL distribution written out here.
+//
+// Per chunk (C <= 64 rows), with G the in-chunk cumulative per-channel
+// log-gate (C x K), γ = e^G, γ_C its last row, and h the state entering it:
+//   Akk[r][s] = Σ_d k_r[d] k_s[d] e^{G_r[d] − G_s[d]},   L = strictlower(diag(β) Akk)
+//   Aqk[r][s] = scale Σ_d q_r[d] k_s[d] e^{G_r[d] − G_s[d]}  (s <= r)
+//   A = (I + L)^{-1},  W = A diag(β)(K ⊙ γ),  U = A diag(β) V,  K̃ = K ⊙ γ_C/γ
+//   V_new = U − W h,   h' = diag(γ_C) h + K̃ᵀ V_new,   o = scale (Q ⊙ γ) h + Aqk V_new
+// Backward (dh' the gradient of the state leaving the chunk):
+//   dV_new = Aqkᵀ dO + K̃ dh'
+//   dh     = diag(γ_C) dh' + scale (Q ⊙ γ)ᵀ dO − Wᵀ dV_new          (reverse scan)
+//   WY stage (kda_bwd.hip): dq, dk, dv, dβ, dG partials and dL = dA
+//   intra:  dAqk = lower(dO V_newᵀ)
+//           dq += scale e^{G−m} ⊙ (dAqk (K ⊙ e^{m−G}))
+//           dk += scale e^{m−G} ⊙ (dAqkᵀ (Q ⊙ e^{G−m}))
+//                 + β ⊙ e^{G−m} ⊙ (dL (K ⊙ e^{m−G})) + e^{m−G} ⊙ (dLᵀ (β ⊙ K ⊙ e^{G−m}))
+//           dG += Q ⊙ dq_intra − K ⊙ dk_qk + K ⊙ dk_row − K ⊙ dk_col
+//           dβ += rowsum(K ⊙ e^{G−m} ⊙ (dL (K ⊙ e^{m−G})))
+//   dg = in-chunk reverse cumsum of dG (per channel).
+// m is the gate row in the middle of the chunk: e^{G_r − G_s} is formed as
+// e^{G_r − m} e^{m − G_s}, each factor within e^{±(half the chunk's gate span)},
+// so the gated products are plain fp32 MFMA contractions (the factors exceed
+// the fp16 range).  Precondition: each channel's in-chunk gate span stays
+// below about 170 (fp32 range of the factors).
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+#include "gdr_tri.hpp"
+
+namespace gdr {
+
+namespace {
+template <class T, int N> using kvec = T __attribute__((ext_vector_type(N)));
+template <class S> constexpr int kfpad() { return sizeof(S) == 2 ? 8 : 4; }
+
+// fp32 slices of 32 channels: [64 rows][KSL + 4]
+constexpr int KSL = 32, LSL = KSL + 4;
+
+// LDS carve-up of the KDA WY-factor kernel.
+template <class S, int KD, int VD>
+struct KPrepCfg {
+    static constexpr int C = 64, LK = KD + kfpad<S>(), LV = VD + kfpad<S>(), LA = 64 + kfpad<S>(), LL = 68;
+    static constexpr size_t oK = 0;                                        // K [64][LK] S (later W)
+    static constexpr size_t oQ = oK + (size_t)C * LK * sizeof(S);          // Q [64][LK] S (later K ⊙ γ)
+    static constexpr size_t oV = oQ + (size_t)C * LK * sizeof(S);          // V [64][LV] S (later U)
+    static constexpr size_t oSl = oV + (size_t)C * LV * sizeof(S);         // 3 fp32 slices [64][LSL]
+    static constexpr size_t oL = oSl + (size_t)3 * C * LSL * 4;            // L [64][LL] fp32
+    static constexpr size_t oAf = oL + (size_t)C * LL * 4;                 // A [64][LL] fp32
+    static constexpr size_t oAb = oAf + (size_t)C * LL * 4;                // A diag(β) [64][LA] S
+    static constexpr size_t oT = oAb + (size_t)C * LA * sizeof(S);         // inverse scratch
+    static constexpr size_t oB = oT + (size_t)4 * 2 * 16 * 17 * 4;        // β [64], m [KD]
+    static constexpr size_t smem = oB + (size_t)(64 + KD) * 4;
+    static_assert(smem <= 160 * 1024, "LDS budget");
+};
+}  // namespace
+
+// ---------------------------------------------------------------- WY factors
+// Grid (chunks, H), 256 threads.  Writes, per unit u = chunk * H + head:
+// W, K̃, Qg = scale (Q ⊙ γ) as [u][64][KD], U as [u][64][VD], Aqk as
+// [u][64][64] (operand type S), and A in the input type as [B*T, H, 64].
+template <class E, class S, int KD, int VD>
+__global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, float scale) {
+    using Cf = KPrepCfg<S, KD, VD>;
+    constexpr int C = 64, NT = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
+    constexpr int EPE = 16 / (int)sizeof(E);
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sK = (S*)(smem + Cf::oK);
+    S* sQ = (S*)(smem + Cf::oQ);
+    S* sV = (S*)(smem + Cf::oV);
+    float* sKp = (float*)(smem + Cf::oSl);   // slices: K e^{G−m} (or Q e^{G−m}), K e^{m−G}
+    float* sKm = sKp + C * LSL;
+    float* sQp = sKm + C * LSL;
+    float* sL = (float*)(smem + Cf::oL);
+    float* sAf = (float*)(smem + Cf::oAf);
+    S* sAb = (S*)(smem + Cf::oAb);
+    float* sT = (float*)(smem + Cf::oT);
+    float* sB = (float*)(smem + Cf::oB);
+    float* sM = sB + 64;
+
+    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int Cn = a.info[ci].len;
+    const long t0 = a.info[ci].t0;
+    const long unit = (long)ci * H + h;
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const E* v = (const E*)a.v;
+    const float* G = a.gcum;
+    const int ref = (Cn - 1) / 2;
+
+    // ---- stage K, Q, V (rows past the chunk zero), β, m
+    for (int idx = threadIdx.x; idx < C * KD / EPE; idx += NT) {
+        const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
+        const kvec<E, EPE> xk = *(const kvec<E, EPE>*)(k + ((t0 + rc) * H + h) * KD + c);
+        const kvec<E, EPE> xq = *(const kvec<E, EPE>*)(q + ((t0 + rc) * H + h) * KD + c);
+        kvec<S, EPE> yk, yq;
+#pragma unroll
+        for (int e = 0; e < EPE; e++) {
+            yk[e] = r < Cn ? (S)(float)xk[e] : (S)0.f;
+            yq[e] = r < Cn ? (S)(float)xq[e] : (S)0.f;
+        }
+        *(kvec<S, EPE>*)(sK + r * LK + c) = yk;
+        *(kvec<S, EPE>*)(sQ + r * LK + c) = yq;
+    }
+    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
+        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
+        const kvec<E, EPE> xv = *(const kvec<E, EPE>*)(v + ((t0 + rc) * H + h) * VD + c);
+        kvec<S, EPE> yv;
+#pragma unroll
+        for (int e = 0; e < EPE; e++) yv[e] = r < Cn ? (S)(float)xv[e] : (S)0.f;
+        *(kvec<S, EPE>*)(sV + r * LV + c) = yv;
+    }
+    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)((const E*)a.beta)[(t0 + threadIdx.x) * H + h] : 0.f;
+    for (int d = threadIdx.x; d < KD; d += NT) sM[d] = G[((t0 + ref) * H + h) * KD + d];
+    lds_barrier();
+
+    // ---- K̃ = K ⊙ e^{G_C − G},  Qg = scale Q ⊙ e^G   (straight to memory)
+    {
+        S* KTo = (S*)a.KT + unit * C * KD;
+        S* QGo = (S*)a.QG + unit * C * KD;
+        for (int idx = threadIdx.x; idx < C * KD; idx += NT) {
+            const int r = idx / KD, d = idx % KD;
+            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+            const float gC = G[((t0 + Cn - 1) * H + h) * KD + d];
+            KTo[idx] = (S)((float)sK[r * LK + d] * __expf(gC - g));
+            QGo[idx] = (S)(scale * (float)sQ[r * LK + d] * __expf(g));
+        }
+    }
+
+    // ---- Akk, Aqk over 32-channel slices (fp32 MFMA)   (wave w: rows 16w, all 64 columns)
+    f32x4 akk[1][4], aqk[1][4];
+    zero_acc(akk);
+    zero_acc(aqk);
+    for (int s0 = 0; s0 < KD; s0 += KSL) {
+        for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
+            const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
+            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+            const float ep = __expf(g - sM[d]), em = __expf(sM[d] - g);
+            const float kv = (float)sK[r * LK + d], qv = (float)sQ[r * LK + d];
+            sKp[r * LSL + dd] = kv * ep;
+            sKm[r * LSL + dd] = kv * em;
+            sQp[r * LSL + dd] = qv * ep;
+        }
+        lds_barrier();
+        wgemm<float, 1, 4, KSL, false, false>(akk, sKp, LSL, sKm, LSL, 16 * w, 0);
+        wgemm<float, 1, 4, KSL, false, false>(aqk, sQp, LSL, sKm, LSL, 16 * w, 0);
+        lds_barrier();
+    }
+    // ---- L = strictlower(diag(β) Akk) -> LDS;  Aqk (scaled, lower incl. diagonal) -> memory
+    {
+        S* Ao = (S*)a.Aqk + unit * C * C;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
+                sL[r * LL + c] = c < r ? sB[r] * akk[0][j][e] : 0.f;
+                Ao[r * C + c] = (S)(c <= r ? scale * aqk[0][j][e] : 0.f);
+            }
+    }
+    lds_barrier();
+    tri_inverse64<LL, NT>(sL, sAf, sT);
+
+    // ---- A diag(β) as an MFMA operand; A itself to memory (input type, [B*T, H, 64]);
+    //      K ⊙ γ over Q's buffer
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+        const int r = idx / C, c = idx % C;
+        const float x = sAf[r * LL + c];
+        sAb[r * LA + c] = (S)(x * sB[c]);
+        if (r < Cn) ((E*)a.A)[((t0 + r) * H + h) * C + c] = (E)x;
+    }
+    for (int idx = threadIdx.x; idx < C * KD; idx += NT) {
+        const int r = idx / KD, d = idx % KD;
+        const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+        sQ[r * LK + d] = (S)((float)sK[r * LK + d] * __expf(g));
+    }
+    lds_barrier();
+    // ---- W = A diag(β) (K ⊙ γ),  U = A diag(β) V   (wave w: rows 16w, all columns)
+    {
+        f32x4 aw[1][KD / 16], au[1][VD / 16];
+        zero_acc(aw);
+        zero_acc(au);
+        wgemm<S, 1, KD / 16, 64, false, true>(aw, sAb, LA, sQ, LK, 16 * w, 0);
+        wgemm<S, 1, VD / 16, 64, false, true>(au, sAb, LA, sV, LV, 16 * w, 0);
+        lds_barrier();   // K and V are overwritten below
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r = acc_row(16 * w, 0, e);
+#pragma unroll
+            for (int j = 0; j < KD / 16; j++) sK[r * LK + acc_col(0, j)] = (S)aw[0][j][e];
+#pragma unroll
+            for (int j = 0; j < VD / 16; j++) sV[r * LV + acc_col(0, j)] = (S)au[0][j][e];
+        }
+    }
+    lds_barrier();
+    {
+        constexpr int EPS = 16 / (int)sizeof(S);
+        S* Wo = (S*)a.W + unit * C * KD;
+        S* Uo = (S*)a.U + unit * C * VD;
+        for (int idx = threadIdx.x; idx < C * KD / EPS; idx += NT) {
+            const int r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
+            *(kvec<S, EPS>*)(Wo + r * KD + c) = *(const kvec<S, EPS>*)(sK + r * LK + c);
+        }
+        for (int idx = threadIdx.x; idx < C * VD / EPS; idx += NT) {
+            const int r = idx / (VD / EPS), c = (idx % (VD / EPS)) * EPS;
+            *(kvec<S, EPS>*)(Uo + r * VD + c) = *(const kvec<S, EPS>*)(sV + r * LV + c);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- state scans
+// One workgroup (4 waves) per (sequence, head, 64-column value slice,
+// direction); the K x 64 fp32 state slice lives in MFMA accumulators (wave w:
+// state rows (KD/4) w ..), a 16-bit copy of it in LDS is the operand of the
+// per-chunk products.
+//   forward:  stores h[c] (fp32 [NT,H,K,V]) and V_new (input type)
+//   reverse:  stores dh[c] (fp32, gradient of the state leaving chunk c),
+//             dV_new (input type) and dh0
+template <class S, int KD>
+struct KScanCfg {
+    static constexpr int C = 64, LK = KD + kfpad<S>(), LS = 64 + kfpad<S>(), LA = 64 + kfpad<S>();
+    static constexpr size_t oW = 0;                                     // W [64][LK]
+    static constexpr size_t oKT = oW + (size_t)C * LK * sizeof(S);      // K̃ [64][LK]
+    static constexpr size_t oQG = oKT + (size_t)C * LK * sizeof(S);     // Qg [64][LK] (reverse)
+    static constexpr size_t oX = oQG + (size_t)C * LK * sizeof(S);      // U or dO slice [64][LS]
+    static constexpr size_t oH = oX + (size_t)C * LS * sizeof(S);       // state copy [KD][LS]
+    static constexpr size_t oVn = oH + (size_t)KD * LS * sizeof(S);     // V_new / dV_new slice [64][LS]
+    static constexpr size_t oAq = oVn + (size_t)C * LS * sizeof(S);     // Aqk [64][LA] (reverse)
+    static constexpr size_t oGC = oAq + (size_t)C * LA * sizeof(S);     // γ_C [KD] fp32
+    static constexpr size_t smem = oGC + (size_t)KD * 4;
+    static_assert(smem <= 160 * 1024, "LDS budget");
+};
+
+template <class E, class S, int KD, int VD, bool REV>
+__global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int nseq) {
+    using Cf = KScanCfg<S, KD>;
+    constexpr int C = 64, NT = 256, LK = Cf::LK, LS = Cf::LS, LA = Cf::LA;
+    constexpr int TMH = KD / 64;   // 16-row tiles of state rows per wave
+    constexpr int EPS = 16 / (int)sizeof(S);
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sW = (S*)(smem + Cf::oW);
+    S* sKT = (S*)(smem + Cf::oKT);
+    S* sQG = (S*)(smem + Cf::oQG);
+    S* sX = (S*)(smem + Cf::oX);
+    S* sH = (S*)(smem + Cf::oH);
+    S* sVn = (S*)(smem + Cf::oVn);
+    S* sAq = (S*)(smem + Cf::oAq);
+    float* sGC = (float*)(smem + Cf::oGC);
+
+    const int nvs = VD / 64;
+    const int job = blockIdx.x, vs = job % nvs, h = (job / nvs) % H, n = job / nvs / H;
+    if (n >= nseq) return;
+    const int w = wave_id();
+    const int m0 = (KD / 4) * w;      // this wave's state rows
+    const int vc0 = 64 * vs;          // this workgroup's value columns
+    const int c_first = a.seq_chunk0[n], c_end = a.seq_chunk0[n + 1];
+    const size_t KV = (size_t)KD * VD;
+
+    // state slice: rows m0 + 16 i + 4 g + e, columns 16 j + r
+    f32x4 st[TMH][4];
+    {
+        const float* init = REV ? a.dht : a.h0;
+#pragma unroll
+        for (int i = 0; i < TMH; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    st[i][j][e] = init ? init[((size_t)n * H + h) * KV + (size_t)acc_row(m0, i, e) * VD + vc0 +
+                                              acc_col(0, j)]
+                                       : 0.f;
+    }
+    const int nch = c_end - c_first;
+    for (int it = 0; it < nch; it++) {
+        const int ci = REV ? c_end - 1 - it : c_first + it;
+        const int Cn = a.info[ci].len;
+        const long t0 = a.info[ci].t0;
+        const long unit = (long)ci * H + h;
+        // ---- stage this chunk's operands and the state copy
+        for (int idx = threadIdx.x; idx < C * KD / EPS; idx += NT) {
+            const int r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
+            *(kvec<S, EPS>*)(sW + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.W + (unit * C + r) * KD + c);
+            *(kvec<S, EPS>*)(sKT + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.KT + (unit * C + r) * KD + c);
+            if (REV)
+                *(kvec<S, EPS>*)(sQG + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.QG + (unit * C + r) * KD + c);
+        }
+        for (int idx = threadIdx.x; idx < C * 64 / EPS; idx += NT) {
+            const int r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
+            kvec<S, EPS> x;
+            if (REV) {   // dO slice (rows past the chunk zero)
+                const int rc = min(r, Cn - 1);
+                constexpr int EPE = 16 / (int)sizeof(E);
+                static_assert(EPE == EPS, "input and operand types share a width");
+                const kvec<E, EPE> y = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + rc) * H + h) * VD + vc0 + c);
+#pragma unroll
+                for (int e = 0; e < EPS; e++) x[e] = r < Cn ? (S)(float)y[e] : (S)0.f;
+            } else {     // U slice
+                x = *(const kvec<S, EPS>*)((const S*)a.U + (unit * C + r) * VD + vc0 + c);
+            }
+            *(kvec<S, EPS>*)(sX + r * LS + c) = x;
+        }
+        if (REV) {
+            for (int idx = threadIdx.x; idx < C * C / EPS; idx += NT) {
+                const int r = idx / (C / EPS), c = (idx % (C / EPS)) * EPS;
+                *(kvec<S, EPS>*)(sAq + r * LA + c) = *(const kvec<S, EPS>*)((const S*)a.Aqk + (unit * C + r) * C + c);
+            }
+        }
+        for (int d = threadIdx.x; d < KD; d += NT) sGC[d] = __expf(a.gcum[((t0 + Cn - 1) * H + h) * KD + d]);
+        // state copy as [KD][64] and the fp32 state of this chunk boundary to memory
+        {
+            float* so = (REV ? a.dhs : a.hs) + unit * KV;
+#pragma unroll
+            for (int i = 0; i < TMH; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int r = acc_row(m0, i, e), c = acc_col(0, j);
+                        sH[r * LS + c] = (S)st[i][j][e];
+                        so[(size_t)r * VD + vc0 + c] = st[i][j][e];
+                    }
+        }
+        lds_barrier();
+        // ---- V_new = U − W h   or   dV_new = Aqkᵀ dO + K̃ dh      (wave w: rows 16w, 64 columns)
+        {
+            f32x4 x[1][4];
+            zero_acc(x);
+            if (REV) {
+                wgemm<S, 1, 4, 64, true, true>(x, sAq, LA, sX, LS, 16 * w, 0);
+                wgemm<S, 1, 4, KD, false, true>(x, sKT, LK, sH, LS, 16 * w, 0);
+            } else {
+                wgemm<S, 1, 4, KD, false, true>(x, sW, LK, sH, LS, 16 * w, 0);
+            }
+            E* out = (E*)(REV ? a.dvn : a.vn);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
+                    const float y = REV ? x[0][j][e] : (float)sX[r * LS + c] - x[0][j][e];
+                    const float yv = r < Cn ? y : 0.f;
+                    sVn[r * LS + c] = (S)yv;
+                    if (r < Cn) out[((t0 + r) * H + h) * VD + vc0 + c] = (E)yv;
+                }
+        }
+        lds_barrier();
+        // ---- h ← diag(γ_C) h + K̃ᵀ V_new    or    dh ← diag(γ_C) dh + Qgᵀ dO − Wᵀ dV_new
+#pragma unroll
+        for (int i = 0; i < TMH; i++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float gc = sGC[acc_row(m0, i, e)];
+#pragma unroll
+                for (int j = 0; j < 4; j++) st[i][j][e] *= gc;
+            }
+        if (REV) {
+            wgemm<S, TMH, 4, 64, true, true>(st, sQG, LK, sX, LS, m0, 0);
+            f32x4 t[TMH][4];
+            zero_acc(t);
+            wgemm<S, TMH, 4, 64, true, true>(t, sW, LK, sVn, LS, m0, 0);
+#pragma unroll
+            for (int i = 0; i < TMH; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) st[i][j] -= t[i][j];
+        } else {
+            wgemm<S, TMH, 4, 64, true, true>(st, sKT, LK, sVn, LS, m0, 0);
+        }
+        lds_barrier();   // the next chunk is staged over this one's LDS
+    }
+    if (REV && a.dh0) {
+#pragma unroll
+        for (int i = 0; i < TMH; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    a.dh0[((size_t)n * H + h) * KV + (size_t)acc_row(m0, i, e) * VD + vc0 + acc_col(0, j)] =
+                        st[i][j][e];
+    }
+}
+
+// ---------------------------------------------------------------- intra-chunk part
+// Grid (chunks, H), 256 threads.  Adds the Aqk and dL terms to the WY stage's
+// partials and writes dq, dk (input type), dg (reverse-cumsummed), dβ.
+template <class S, int VD>
+struct KIntraCfg {
+    static constexpr int C = 64, LV = VD + kfpad<S>(), LF = 68;
+    static constexpr size_t oDO = 0;                                   // dO [64][LV] S
+    static constexpr size_t oVn = oDO + (size_t)C * LV * sizeof(S);    // V_new [64][LV] S
+    static constexpr size_t oDAq = oVn + (size_t)C * LV * sizeof(S);   // dAqk [64][LF] fp32
+    static constexpr size_t oDL = oDAq + (size_t)C * LF * 4;           // dL [64][LF] fp32
+    static constexpr size_t oDG = oDL + (size_t)C * LF * 4;            // dG slice [64][LSL] fp32
+    static constexpr size_t oB = oDG + (size_t)C * LSL * 4;            // β [64], dβ row sums [64]
+    static constexpr size_t oPA = oB + (size_t)2 * 64 * 4;             // 4 fp32 slices [64][LSL]
+    static constexpr size_t smem = oPA + (size_t)4 * C * LSL * 4;
+    static_assert(smem <= 160 * 1024, "LDS budget");
+};
+
+template <class E, class S, int KD, int VD>
+__global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, float scale) {
+    using Cf = KIntraCfg<S, VD>;
+    constexpr int C = 64, NT = 256, LV = Cf::LV, LF = Cf::LF;
+    constexpr int EPE = 16 / (int)sizeof(E);
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sDO = (S*)(smem + Cf::oDO);
+    S* sVn = (S*)(smem + Cf::oVn);
+    float* sKm = (float*)(smem + Cf::oPA);   // K e^{m−G}
+    float* sQp = sKm + C * LSL;              // Q e^{G−m}
+    float* sKb = sQp + C * LSL;              // β K e^{G−m}
+    float* sEp = sKb + C * LSL;              // e^{G−m}
+    float* sDAq = (float*)(smem + Cf::oDAq);
+    float* sDL = (float*)(smem + Cf::oDL);
+    float* sDG = (float*)(smem + Cf::oDG);
+    float* sB = (float*)(smem + Cf::oB);
+    float* sRB = sB + 64;
+
+    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int Cn = a.info[ci].len;
+    const long t0 = a.info[ci].t0;
+    const E* q = (const E*)a.q;
+    const E* k = (const E*)a.k;
+    const float* G = a.gcum;
+    const int ref = (Cn - 1) / 2;
+
+    // ---- dO, V_new (rows past the chunk zero), dL, β
+    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
+        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
+        const kvec<E, EPE> xo = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + rc) * H + h) * VD + c);
+        const kvec<E, EPE> xv = *(const kvec<E, EPE>*)((const E*)a.vn + ((t0 + rc) * H + h) * VD + c);
+        kvec<S, EPE> yo, yv;
+#pragma unroll
+        for (int e = 0; e < EPE; e++) {
+            yo[e] = r < Cn ? (S)(float)xo[e] : (S)0.f;
+            yv[e] = r < Cn ? (S)(float)xv[e] : (S)0.f;
+        }
+        *(kvec<S, EPE>*)(sDO + r * LV + c) = yo;
+        *(kvec<S, EPE>*)(sVn + r * LV + c) = yv;
+    }
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+        const int r = idx / C, c = idx % C;
+        sDL[r * LF + c] = r < Cn ? a.dA[((t0 + r) * H + h) * C + c] : 0.f;
+    }
+    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)((const E*)a.beta)[(t0 + threadIdx.x) * H + h] : 0.f;
+    lds_barrier();
+    // ---- dAqk = lower(dO V_newᵀ)    (wave w: rows 16w, 64 columns)
+    {
+        f32x4 x[1][4];
+        zero_acc(x);
+        wgemm<S, 1, 4, VD, false, false>(x, sDO, LV, sVn, LV, 16 * w, 0);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
+                sDAq[r * LF + c] = c <= r ? x[0][j][e] : 0.f;
+            }
+    }
+    lds_barrier();   // dO and V_new are no longer read: the slices take their place
+
+    float rbeta[4] = {0.f, 0.f, 0.f, 0.f};   // Σ_d K e^{G−m} ⊙ (dL K e^{m−G}) for rows 16w + 4g + e
+    for (int s0 = 0; s0 < KD; s0 += KSL) {
+        for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
+            const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
+            const float m = G[((t0 + ref) * H + h) * KD + d];
+            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+            const float ep = r < Cn ? __expf(g - m) : 0.f, em = r < Cn ? __expf(m - g) : 0.f;
+            const float kv = (float)k[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+            const float qv = (float)q[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
+            sKm[r * LSL + dd] = kv * em;
+            sQp[r * LSL + dd] = qv * ep;
+            sKb[r * LSL + dd] = sB[r] * kv * ep;
+            sEp[r * LSL + dd] = ep;
+        }
+        lds_barrier();
+        // wave w: rows 16w, the 32 channels of the slice
+        f32x4 p1[1][2], p2[1][2], p3[1][2], p4[1][2];
+        zero_acc(p1);
+        zero_acc(p2);
+        zero_acc(p3);
+        zero_acc(p4);
+        wgemm<float, 1, 2, 64, false, true>(p1, sDAq, LF, sKm, LSL, 16 * w, 0);   // dAqk · K e^{m−G}
+        wgemm<float, 1, 2, 64, true, true>(p2, sDAq, LF, sQp, LSL, 16 * w, 0);    // dAqkᵀ · Q e^{G−m}
+        wgemm<float, 1, 2, 64, false, true>(p3, sDL, LF, sKm, LSL, 16 * w, 0);    // dL · K e^{m−G}
+        wgemm<float, 1, 2, 64, true, true>(p4, sDL, LF, sKb, LSL, 16 * w, 0);     // dLᵀ · β K e^{G−m}
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = acc_row(16 * w, 0, e), dd = acc_col(0, j), d = s0 + dd;
+                const float ep = sEp[r * LSL + dd];
+                const float em = ep > 0.f ? 1.f / ep : 0.f;
+                const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
+                const float kv = (float)k[o], qv = (float)q[o];
+                const float dqi = scale * ep * p1[0][j][e];
+                const float dkq = scale * em * p2[0][j][e];
+                const float dkr = sB[r] * ep * p3[0][j][e];
+                const float dkc = em * p4[0][j][e];
+                rbeta[e] += kv * ep * p3[0][j][e];
+                const float dG = qv * dqi - kv * dkq + kv * dkr - kv * dkc;
+                if (r < Cn) {
+                    ((E*)a.dq)[o] = (E)(a.dqs[o] + dqi);
+                    ((E*)a.dk)[o] = (E)(a.dks[o] + dkq + dkr + dkc);
+                    sDG[r * LSL + dd] = a.dgs[o] + dG;
+                } else {
+                    sDG[r * LSL + dd] = 0.f;
+                }
+            }
+        lds_barrier();
+        // in-chunk reverse cumsum of dG per channel: one thread per channel
+        if (threadIdx.x < KSL) {
+            const int dd = threadIdx.x;
+            float acc = 0.f;
+            for (int r = Cn - 1; r >= 0; r--) {
+                acc += sDG[r * LSL + dd];
+                a.dg[((t0 + r) * H + h) * KD + s0 + dd] = acc;
+            }
+        }
+        lds_barrier();   // the next slice is built over this one
+    }
+    // ---- dβ = dβ_stage + row sums (over the 16 lanes of each row group)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        float x = rbeta[e];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        sRB[16 * w + 4 * (lane_id() >> 4) + e] = x;   // every lane of the group holds the sum
+    }
+    lds_barrier();
+    if (threadIdx.x < Cn) {
+        const int r = threadIdx.x;
+        a.dbeta[(t0 + r) * H + h] = a.dbs[(t0 + r) * H + h] + sRB[r];
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <class E, class S, int KD, int VD>
+static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_t s, hipEvent_t* ev) {
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+    hipError_t e;
+    {
+        auto kern = kda_prep_kernel<E, S, KD, VD>;
+        const int sm = (int)KPrepCfg<S, KD, VD>::smem;
+        if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), sm, s, a, p.HV, p.scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = mark(1)) != hipSuccess) return e;
+    {
+        const int sm = (int)KScanCfg<S, KD>::smem;
+        const unsigned jobs = (unsigned)(p.N * p.HV * (VD / 64));
+        auto kf = kda_scan_kernel<E, S, KD, VD, false>;
+        auto kr = kda_scan_kernel<E, S, KD, VD, true>;
+        if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
+            return e;
+        if ((e = hipFuncSetAttribute((const void*)kr, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(kf, dim3(jobs), dim3(256), sm, s, a, p.HV, p.N);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(kr, dim3(jobs), dim3(256), sm, s, a, p.HV, p.N);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = mark(2)) != hipSuccess) return e;
+    {
+        KdaArgs k{};
+        k.q = a.q; k.k = a.k; k.v = a.v; k.v_new = a.vn; k.g = a.gcum; k.beta = a.beta; k.A = a.A;
+        k.h = a.hs; k.dO = a.dO; k.dh = a.dhs; k.dv_in = a.dvn; k.info = a.info;
+        k.dq = a.dqs; k.dk = a.dks; k.dv_out = a.dv; k.db = a.dbs; k.dg = a.dgs; k.dA = a.dA;
+        if ((e = launch_kda(p, k, s)) != hipSuccess) return e;
+    }
+    if ((e = mark(3)) != hipSuccess) return e;
+    {
+        auto kern = kda_intra_kernel<E, S, KD, VD>;
+        const int sm = (int)KIntraCfg<S, VD>::smem;
+        if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), sm, s, a, p.HV, p.scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return mark(4);
+}
+
+hipError_t launch_kda_full(const Problem& p, const KdaFullArgs& a, hipStream_t s, hipEvent_t* ev) {
+    if (p.K == 128 && p.V == 128) {
+        if (p.dtype == 1) return kda_full_go<f16, f16, 128, 128>(p, a, s, ev);
+        return hipErrorInvalidValue;
+    }
+    if (p.K == 64 && p.V == 64) {
+        if (p.dtype == 1) return kda_full_go<f16, f16, 64, 64>(p, a, s, ev);
+        if (p.dtype == 0) return kda_full_go<float, float, 64, 64>(p, a, s, ev);
+        return hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -157,3 +157,41 @@ def kda_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0):
     return {"q": t(q), "k": t(k), "v": t(v), "v_new": t(vn), "g": f(g), "beta": t(beta), "A": t(A),
             "h": f(h), "dO": t(dO), "dh": f(dh), "dv": t(dv),
             "B": B, "T": T, "H": H, "K": K, "V": V, "BT": BT, "NT": NT, "dtype": dtype}
+
+
+def kda_full_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0, lengths=None, h0=False,
+                    dht=True, gate_scale=1.0):
+    """Inputs of one full KDA backward (per-channel gate), as CPU torch tensors.
+
+    q, k [NTOK,H,K] (L2-normalised), v, dO [NTOK,H,V], beta [NTOK,H] in `dtype`;
+    graw = gate_scale * logsigmoid(randn) [NTOK,H,K] fp32 and its in-chunk
+    cumsum gcum; dht = 0.1 randn, h0 randn [N,H,K,V] fp32 or None."""
+    rng = np.random.default_rng(seed)
+    dt = DTYPES[dtype]
+    if lengths is not None:
+        assert B == 1
+        cu = cu_from_lengths(lengths)
+        ntok, N = int(cu[-1]), len(lengths)
+    else:
+        cu, ntok, N = None, B * T, B
+
+    def randn(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    q = randn(ntok, H, K)
+    k = randn(ntok, H, K)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = randn(ntok, H, V)
+    graw = (_logsigmoid(randn(ntok, H, K).astype(np.float64)) * gate_scale).astype(np.float32)
+    beta = _sigmoid(randn(ntok, H).astype(np.float64)).astype(np.float32)
+    dO = randn(ntok, H, V)
+    dht_a = (0.1 * randn(N, H, K, V)).astype(np.float32) if dht else None
+    h0_a = randn(N, H, K, V) if h0 else None
+    cu_chunks = cu if cu is not None else np.arange(0, ntok + 1, T)
+    gcum = _in_chunk_cumsum_fast(graw, BT, cu_chunks)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)  # noqa: E731
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    return {"q": t(q), "k": t(k), "v": t(v), "beta": t(beta), "dO": t(dO), "graw": f(graw), "gcum": f(gcum),
+            "dht": f(dht_a), "h0": f(h0_a), "cu": cu, "B": B, "T": T if lengths is None else ntok, "H": H, "K": K,
+            "V": V, "BT": BT, "N": N, "ntok": ntok, "dtype": dtype}

@@ -206,6 +206,48 @@ int kda_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void
                   const float *dh, const void *dv_in, float *dq, float *dk, void *dv_out, float *db,
                   float *dg, float *dA, hipStream_t stream);
 
+/*
+ * kda_chunk_bwd_full -- the whole chunked backward of KDA, the gated delta rule
+ * with a per-channel gate ([P2] 概述: the operator above is the "WY
+ * representation gradient" stage of this backward; the other steps -- state
+ * recomputation, the per-channel dh scan, the intra-chunk attention and dL
+ * distribution -- run around it here).  Recurrence, per sequence and head
+ * (HK == HV == H), gate a_t = exp(ĝ_t) in R^K:
+ *     S_t = (I - b_t k_t k_tᵀ) diag(a_t) S_{t-1} + b_t k_t v_tᵀ,   o_t = scale S_tᵀ q_t
+ * Returns the gradients of L = Σ_t <dO_t, o_t> + <dht, S_T>.
+ * Inputs:
+ *   q, k [B*T,H,K]  v, dO [B*T,H,V]  beta [B*T,H]   dtype (F16; F32 at K = 64)
+ *   g_cum [B*T,H,K] fp32   in-chunk cumulative per-channel log-gate (restarts
+ *                          every BT tokens and at every sequence start;
+ *                          gdr_gate_cumsum with HV = H*K computes it)
+ *   h0, dht [N,H,K,V] fp32 or NULL (zero)
+ * Outputs (written in full): dq, dk [B*T,H,K] and dv [B*T,H,V] in dtype;
+ *   dg [B*T,H,K] fp32 (w.r.t. the RAW per-channel gate, reverse-cumsummed in
+ *   each chunk); dbeta [B*T,H] fp32; dh0 [N,H,K,V] fp32 or NULL (skip).
+ * ws/ws_bytes: workspace (>= kda_workspace_size(p)).
+ * Errors: GDR_ERR_INVALID if HK != HV; GDR_ERR_UNSUPPORTED for bf16, BT != 64,
+ * K != V, K not in {64, 128}, fp32 at K = 128.
+ * Precision: gated intra-chunk products in fp32 (each factor e^{±(G − m)} with m
+ * the chunk's middle gate row; each channel's in-chunk gate span must stay
+ * below about 170), other products fp16 operands with fp32 accumulation.
+ */
+size_t kda_workspace_size(const gdr_problem *p);
+int kda_chunk_bwd_full(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                       const void *beta, const float *h0, const void *dO, const float *dht,
+                       void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_bwd_full_events -- kda_chunk_bwd_full for measurement tools; `events`
+ * (NULL or 5 caller-created hipEvent_t) are recorded on `stream` at the start
+ * and after the WY factors, the two state scans, the WY stage and the
+ * intra-chunk kernel.
+ */
+int kda_chunk_bwd_full_events(const gdr_problem *p, const void *q, const void *k, const void *v,
+                              const float *g_cum, const void *beta, const float *h0, const void *dO,
+                              const float *dht, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                              float *dh0, void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *events);
+
 #ifdef __cplusplus
 }
 #endif
