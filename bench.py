@@ -9,7 +9,9 @@ K=V=128, BT=64, bf16 inputs with fp32 gate, dht present.
 
 With --path fwd a step is instead the chunked forward: gdr_gate_cumsum on the
 raw gate, then gdr_chunk_fwd (chunk table + WY factors, the forward state
-scan, the output kernel), on the same inputs.
+scan, the output kernel), on the same inputs.  With --path kda a step is one
+kda_chunk_bwd_full call (the full KDA backward, per-channel gate) at B=1,
+T=2048, H=32, K=V=128, BT=64, fp16, dht present.
 
 Prints one JSON line: the headline metric (effective TFLOP/s under the FLOP
 model below, with ms per call), a roofline entry for the dominant kernel
@@ -52,6 +54,26 @@ def flop_model(C, K, V):
 
 def flop_model_fwd(C, K, V):
     return 6 * C * K * V + 6 * C * C * K + 4 * C * C * V + C ** 3 / 3.0
+
+
+def kernel_bytes_kda(H, K, V, chunks, es=2):
+    """Algorithmic bytes of each stage of the full KDA backward (inputs read
+    once, outputs written once)."""
+    ntok, nunits = sum(chunks), len(chunks) * H
+    tk, tv = ntok * H * K, ntok * H * V          # elements of [NTOK,H,K] / [NTOK,H,V]
+    st, stv, state = 64 * K * es, 64 * V * es, K * V * 4
+    tri = 64 * 64 * es
+    # WY factors: q, k, v, per-channel gate, beta in; W, U, K~, Qg, Aqk and A out
+    prep = 2 * tk * es + tv * es + tk * 4 + ntok * H * es + nunits * (3 * st + stv + 2 * tri)
+    # scans: W, K~, U in, h (fp32) and V_new out; W, K~, Qg, Aqk, dO in, dh (fp32) and dV_new out
+    scans = nunits * (2 * st + stv + state) + tv * es + nunits * (3 * st + tri + state) + 2 * tv * es
+    # WY stage: q, k, v, V_new, dO, dV_new, gate, beta, A, h, dh in; dq, dk, dg, dA (fp32), dv, db out
+    stage = (2 * tk + 4 * tv) * es + tk * 4 + ntok * H * es + nunits * tri + 2 * nunits * state + \
+        3 * tk * 4 + tv * es + ntok * H * 4 + ntok * H * 64 * 4
+    # intra: dO, V_new, dA, beta, gate, q, k, stage dq/dk/dg/db in; dq, dk, dg, dbeta out
+    intra = 2 * tv * es + ntok * H * 64 * 4 + ntok * H * es + tk * 4 + 2 * tk * es + 3 * tk * 4 + ntok * H * 4 + \
+        2 * tk * es + tk * 4 + ntok * H * 4
+    return {"prep": prep, "scans": scans, "stage": stage, "intra": intra}
 
 
 def chunk_lengths(lengths, T, B, BT):
@@ -117,7 +139,11 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
     from oracle import oracle as O
     B, T, HK, HV, K, V = cfg["B"], inp["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"]
     p = O.Problem(B if inp["cu"] is None else 1, T, HK, HV, K, V, cu_seqlens=inp["cu"])
-    graw = O.gcum_to_graw(p, 64, inp["gcum"].numpy())
+    if path == "kda":   # per-channel gate: recover it channel by channel
+        pg = O.Problem(B, T, HV * K, HV * K, 1, 1)
+        graw = O.gcum_to_graw(pg, 64, inp["gcum"].numpy().reshape(-1, HV * K)).reshape(-1, HV, K)
+    else:
+        graw = O.gcum_to_graw(p, 64, inp["gcum"].numpy())
     f = lambda t: None if t is None else t.double().numpy()  # noqa: E731
     args = (f(inp["q"]), f(inp["k"]), f(inp["v"]), graw, f(inp["beta"]), None, f(inp["dO"]), f(inp["dht"]))
     passes, dt = 0, 0.0
@@ -125,6 +151,8 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
         t0 = time.perf_counter()
         if path == "fwd":
             O.gdr_fwd_token(p, 64, args[0], args[1], args[2], args[3], args[4], None)
+        elif path == "kda":
+            O.kda_bwd_token(p, *args)
         else:
             O.gdr_bwd_token(p, *args)
         dt += time.perf_counter() - t0
@@ -132,9 +160,10 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
     model = flop_model_fwd if path == "fwd" else flop_model
     flops = passes * sum(model(c, K, V) for c in chunks) * HV
     nseq = B if inp["cu"] is None else len(inp["cu"]) - 1
-    threads = min(O.num_threads(), nseq * (HV if path == "fwd" else HK))
-    what = ("token recurrence (forward), OpenMP over (sequence, value head)" if path == "fwd" else
-            "token recurrence with the hand-derived backward, OpenMP over (sequence, key head)")
+    threads = min(O.num_threads(), nseq * (HV if path in ("fwd", "kda") else HK))
+    what = {"fwd": "token recurrence (forward), OpenMP over (sequence, value head)",
+            "kda": "KDA token recurrence with the hand-derived backward, OpenMP over (sequence, head)"}.get(
+        path, "token recurrence with the hand-derived backward, OpenMP over (sequence, key head)")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 {what}",
             "seconds": round(dt, 2)}
@@ -164,8 +193,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
-    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd"],
-                    help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward")
+    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd", "kda"],
+                    help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward; "
+                         "kda: the full KDA backward at B=1 T=2048 H=32 K=V=128 fp16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -176,6 +206,8 @@ def main():
     import torch
     from chunked_gated_delta_08_amd import binding, profiling, workloads
 
+    if args.path == "kda":
+        return bench_kda(args, torch, binding, profiling, workloads)
     fwd = args.path == "fwd"
     cfg = dict(WORKLOADS[args.workload])
     lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
@@ -264,6 +296,66 @@ def main():
            "roofline": roof}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path=args.path)
+    del keep
+    print(json.dumps(res), flush=True)
+
+
+def bench_kda(args, torch, binding, profiling, workloads):
+    """One step = one kda_chunk_bwd_full call at B=1, T=2048, H=32, K=V=128, fp16."""
+    B, T, H, K, V = 1, 2048, 32, 128, 128
+    cfg = dict(B=B, T=T, HK=H, HV=H, K=K, V=V, name="kda_bwd_T2048_h32_K128_V128_BT64_f16")
+    inp = workloads.kda_full_inputs(B, T, H, K, V, dtype="f16", seed=0)
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v", "beta", "dO", "gcum", "dht")}
+    prob, keep = binding.make_problem(B, T, H, H, K, V, torch.float16, 64, None)
+    ws = torch.empty(int(binding.lib.kda_workspace_size(ctypes.byref(prob))), dtype=torch.uint8, device="cuda")
+    out = {"dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]), "dv": torch.empty_like(dev["v"]),
+           "dg": torch.empty(dev["gcum"].shape, dtype=torch.float32, device="cuda"),
+           "dbeta": torch.empty(dev["beta"].shape, dtype=torch.float32, device="cuda"),
+           "dh0": torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")}
+    P = binding._ptr
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args_c = [ctypes.byref(prob), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["gcum"]), P(dev["beta"]), None,
+              P(dev["dO"]), P(dev["dht"]), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]), P(out["dbeta"]),
+              P(out["dh0"]), P(ws), ws.numel(), sp]
+    nev = 5
+    hip, evs = hip_events(nev * args.steps)
+    evsz = ctypes.sizeof(ctypes.c_void_p)
+
+    def call(i=None):
+        ev = None if i is None else ctypes.byref(evs, nev * i * evsz)
+        rc = binding.lib.kda_chunk_bwd_full_events(*args_c, ev)
+        if rc != 0:
+            raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = ["prep", "scans", "stage", "intra"]
+    stage = {k: 0.0 for k in names}
+    for i in range(args.steps):
+        e = [evs[nev * i + j] for j in range(nev)]
+        for j, k in enumerate(names):
+            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
+    chunks = chunk_lengths(None, T, B, 64)
+    F = sum(flop_model(c, K, V) for c in chunks) * H
+    kb = kernel_bytes_kda(H, K, V, chunks)
+    kn = {"prep": "kda_prep_kernel", "scans": "kda_scan_kernel", "stage": "kda_kernel", "intra": "kda_intra_kernel"}
+    roof = _roofline(stage, kb, kn, "kda_t2048_h32", profiling)
+    res = {"metric": "KDA chunked bwd (full, per-channel gate) ms/call + eff. TFLOP/s at T=2048, H=32, K=V=128, BT=64",
+           "value": round(F / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
+           "config": {"workload": cfg["name"], "B": B, "T": T, "HK": H, "HV": H, "K": K, "V": V, "BT": 64,
+                      "global_batch": B, "seq_len": T, "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2)},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path="kda")
     del keep
     print(json.dumps(res), flush=True)
 

@@ -214,9 +214,10 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, flo
 
 // ---------------------------------------------------------------- state scans
 // One workgroup (4 waves) per (sequence, head, 64-column value slice,
-// direction); the K x 64 fp32 state slice lives in MFMA accumulators (wave w:
-// state rows (KD/4) w ..), a 16-bit copy of it in LDS is the operand of the
-// per-chunk products.
+// direction); both directions run in one launch (the reverse scan needs
+// nothing the forward one writes).  The K x 64 fp32 state slice lives in MFMA
+// accumulators (wave w: state rows (KD/4) w ..), a 16-bit copy of it in LDS is
+// the operand of the per-chunk products.
 //   forward:  stores h[c] (fp32 [NT,H,K,V]) and V_new (input type)
 //   reverse:  stores dh[c] (fp32, gradient of the state leaving chunk c),
 //             dV_new (input type) and dh0
@@ -236,7 +237,7 @@ struct KScanCfg {
 };
 
 template <class E, class S, int KD, int VD, bool REV>
-__global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int nseq) {
+__device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int nseq, int job) {
     using Cf = KScanCfg<S, KD>;
     constexpr int C = 64, NT = 256, LK = Cf::LK, LS = Cf::LS, LA = Cf::LA;
     constexpr int TMH = KD / 64;   // 16-row tiles of state rows per wave
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int
     float* sGC = (float*)(smem + Cf::oGC);
 
     const int nvs = VD / 64;
-    const int job = blockIdx.x, vs = job % nvs, h = (job / nvs) % H, n = job / nvs / H;
+    const int vs = job % nvs, h = (job / nvs) % H, n = job / nvs / H;
     if (n >= nseq) return;
     const int w = wave_id();
     const int m0 = (KD / 4) * w;      // this wave's state rows
@@ -383,6 +384,13 @@ __global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int
     }
 }
 
+// blocks [0, jobs): forward scans; [jobs, 2 jobs): reverse scans
+template <class E, class S, int KD, int VD>
+__global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int nseq, int jobs) {
+    if ((int)blockIdx.x < jobs) kda_scan_body<E, S, KD, VD, false>(a, H, nseq, blockIdx.x);
+    else kda_scan_body<E, S, KD, VD, true>(a, H, nseq, (int)blockIdx.x - jobs);
+}
+
 // ---------------------------------------------------------------- intra-chunk part
 // Grid (chunks, H), 256 threads.  Adds the Aqk and dL terms to the WY stage's
 // partials and writes dq, dk (input type), dg (reverse-cumsummed), dβ.
@@ -476,6 +484,20 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
             sEp[r * LSL + dd] = ep;
         }
         lds_barrier();
+        // this lane's elements of q, k and the stage partials, loaded before the products
+        float pk[2][4], pq[2][4], pdq[2][4], pdk[2][4], pdg[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = acc_row(16 * w, 0, e), d = s0 + acc_col(0, j);
+                const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
+                pk[j][e] = (float)k[o];
+                pq[j][e] = (float)q[o];
+                pdq[j][e] = a.dqs[o];
+                pdk[j][e] = a.dks[o];
+                pdg[j][e] = a.dgs[o];
+            }
         // wave w: rows 16w, the 32 channels of the slice
         f32x4 p1[1][2], p2[1][2], p3[1][2], p4[1][2];
         zero_acc(p1);
@@ -494,7 +516,7 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
                 const float ep = sEp[r * LSL + dd];
                 const float em = ep > 0.f ? 1.f / ep : 0.f;
                 const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
-                const float kv = (float)k[o], qv = (float)q[o];
+                const float kv = pk[j][e], qv = pq[j][e];
                 const float dqi = scale * ep * p1[0][j][e];
                 const float dkq = scale * em * p2[0][j][e];
                 const float dkr = sB[r] * ep * p3[0][j][e];
@@ -502,21 +524,21 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
                 rbeta[e] += kv * ep * p3[0][j][e];
                 const float dG = qv * dqi - kv * dkq + kv * dkr - kv * dkc;
                 if (r < Cn) {
-                    ((E*)a.dq)[o] = (E)(a.dqs[o] + dqi);
-                    ((E*)a.dk)[o] = (E)(a.dks[o] + dkq + dkr + dkc);
-                    sDG[r * LSL + dd] = a.dgs[o] + dG;
-                } else {
-                    sDG[r * LSL + dd] = 0.f;
+                    ((E*)a.dq)[o] = (E)(pdq[j][e] + dqi);
+                    ((E*)a.dk)[o] = (E)(pdk[j][e] + dkq + dkr + dkc);
                 }
+                sDG[r * LSL + dd] = r < Cn ? pdg[j][e] + dG : 0.f;
             }
         lds_barrier();
-        // in-chunk reverse cumsum of dG per channel: one thread per channel
+        // in-chunk reverse cumsum of dG per channel: one thread per channel, all
+        // 64 rows (rows past the chunk hold zeros)
         if (threadIdx.x < KSL) {
             const int dd = threadIdx.x;
             float acc = 0.f;
-            for (int r = Cn - 1; r >= 0; r--) {
+#pragma unroll
+            for (int r = C - 1; r >= 0; r--) {
                 acc += sDG[r * LSL + dd];
-                a.dg[((t0 + r) * H + h) * KD + s0 + dd] = acc;
+                if (r < Cn) a.dg[((t0 + r) * H + h) * KD + s0 + dd] = acc;
             }
         }
         lds_barrier();   // the next slice is built over this one
@@ -554,16 +576,11 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
     if ((e = mark(1)) != hipSuccess) return e;
     {
         const int sm = (int)KScanCfg<S, KD>::smem;
-        const unsigned jobs = (unsigned)(p.N * p.HV * (VD / 64));
-        auto kf = kda_scan_kernel<E, S, KD, VD, false>;
-        auto kr = kda_scan_kernel<E, S, KD, VD, true>;
-        if ((e = hipFuncSetAttribute((const void*)kf, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
+        const int jobs = p.N * p.HV * (VD / 64);
+        auto kern = kda_scan_kernel<E, S, KD, VD>;
+        if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
-        if ((e = hipFuncSetAttribute((const void*)kr, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(kf, dim3(jobs), dim3(256), sm, s, a, p.HV, p.N);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(kr, dim3(jobs), dim3(256), sm, s, a, p.HV, p.N);
+        hipLaunchKernelGGL(kern, dim3(2 * jobs), dim3(256), sm, s, a, p.HV, p.N, jobs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(2)) != hipSuccess) return e;

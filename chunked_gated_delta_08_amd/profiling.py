@@ -22,6 +22,7 @@ import argparse
 import collections
 import csv
 import hashlib
+import re
 import json
 import os
 import sys
@@ -31,7 +32,7 @@ _CS = "chunked_gated_delta_08_amd/csrc/"
 _COMMON = [_CS + "gdr_device.hpp", _CS + "gdr_launch.hpp", "chunked_gated_delta_08_amd/build.py"]
 KERNEL_SOURCES = {
     "chunk_table_kernel": [_CS + "gdr_prep.hip"] + _COMMON,
-    "prep_kernel": [_CS + "gdr_prep.hip"] + _COMMON,
+    "prep_kernel": [_CS + "gdr_prep.hip", _CS + "gdr_tri.hpp"] + _COMMON,
     "scan_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
     "seg_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
     "combine_kernel": [_CS + "gdr_scan.hip"] + _COMMON,
@@ -39,6 +40,9 @@ KERNEL_SOURCES = {
     "kda_kernel": [_CS + "kda_bwd.hip"] + _COMMON,
     "fwd_out_kernel": [_CS + "gdr_fwd.hip"] + _COMMON,
     "gate_cumsum_kernel": [_CS + "gdr_fwd.hip"] + _COMMON,
+    "kda_prep_kernel": [_CS + "kda_full.hip", _CS + "gdr_tri.hpp"] + _COMMON,
+    "kda_scan_kernel": [_CS + "kda_full.hip"] + _COMMON,
+    "kda_intra_kernel": [_CS + "kda_full.hip"] + _COMMON,
 }
 
 
@@ -51,9 +55,11 @@ def source_digest(files):
 
 
 def short_name(full):
-    """Library kernel name (``gdr::grad_kernel<...>`` -> ``grad_kernel``), else None."""
+    """Library kernel name (``gdr::grad_kernel<...>`` or its mangled form ->
+    ``grad_kernel``), else None.  The whole identifier must match
+    (``prep_kernel`` is not ``kda_prep_kernel``)."""
     for k in KERNEL_SOURCES:
-        if k in full:
+        if f"{len(k)}{k}" in full or re.search(r"::" + k + r"[(<]", full):
             return k
     return None
 

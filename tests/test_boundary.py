@@ -137,3 +137,26 @@ def test_gate_cumsum_validation(B):
     assert B.lib.gdr_gate_cumsum(ctypes.byref(_prob(B, HK=2, HV=3)), FAKE, FAKE, None) == -1
     # nothing to do: no tokens
     assert B.lib.gdr_gate_cumsum(ctypes.byref(_prob(B, T=0)), None, None, None) == 0
+
+
+def _kda_full(B, p, ws_bytes=1 << 40, **null):
+    args = {n: FAKE for n in ("q", "k", "v", "g", "beta", "h0", "dO", "dht", "dq", "dk", "dv", "dg", "db", "dh0")}
+    args.update(null)
+    return B.lib.kda_chunk_bwd_full(ctypes.byref(p), args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                    args["h0"], args["dO"], args["dht"], args["dq"], args["dk"], args["dv"],
+                                    args["dg"], args["db"], args["dh0"], FAKE, ws_bytes, None)
+
+
+def test_kda_full_validation(B):
+    f16 = dict(dtype=B.GDR_F16)
+    assert _kda_full(B, _prob(B, HK=2, HV=4, **f16)) == -1          # one head count only
+    assert _kda_full(B, _prob(B)) == -2                              # bf16 not built
+    assert _kda_full(B, _prob(B, BT=32, **f16)) == -2
+    assert _kda_full(B, _prob(B, K=128, V=128, dtype=0)) == -2       # fp32 only at K = 64
+    assert _kda_full(B, _prob(B, K=64, V=128, **f16)) == -2
+    p = _prob(B, **f16)
+    need = B.lib.kda_workspace_size(ctypes.byref(p))
+    assert need > 0 and B.lib.kda_workspace_size(ctypes.byref(_prob(B))) == 0
+    assert _kda_full(B, p, ws_bytes=need - 1) == -3
+    for missing in ("q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "db"):
+        assert _kda_full(B, p, **{missing: None}) == -1, missing
