@@ -122,7 +122,7 @@ def gdr_inputs(B, T, HK, HV, K, V, BT=64, dtype="bf16", seed=0, lengths=None, dh
     dO = randn(ntok, HV, V)
     dht_a = (0.1 * randn(N, HV, K, V)).astype(np.float32) if dht else None
     h0_a = randn(N, HV, K, V) if h0 else None
-    cu_chunks = cu if cu is not None else np.arange(0, ntok + 1, T)
+    cu_chunks = cu if cu is not None else np.arange(B + 1) * T   # sequence starts (dense: every T tokens)
     gcum = _in_chunk_cumsum_fast(graw, BT, cu_chunks)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)  # noqa: E731
     f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
@@ -188,7 +188,7 @@ def kda_full_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0,
     dO = randn(ntok, H, V)
     dht_a = (0.1 * randn(N, H, K, V)).astype(np.float32) if dht else None
     h0_a = randn(N, H, K, V) if h0 else None
-    cu_chunks = cu if cu is not None else np.arange(0, ntok + 1, T)
+    cu_chunks = cu if cu is not None else np.arange(B + 1) * T   # sequence starts (dense: every T tokens)
     gcum = _in_chunk_cumsum_fast(graw, BT, cu_chunks)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)  # noqa: E731
     f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
