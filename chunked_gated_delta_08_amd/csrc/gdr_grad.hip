@@ -340,6 +340,8 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         rA.store(sA);
         rH.store(sH);
         rdH.store(sdH);
+        hdh += rH.dot(rdH);   // <dh, h> over the first slice, from the registers just stored
+        pin(hdh);
         rdO.store(sdO);
         lds_barrier();   // Pm has read Q: the V slice may take its buffer
         rV.store(sV);
@@ -362,6 +364,8 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
             if (vh > 0) {
                 nH.store(sH);
                 ndH.store(sdH);
+                hdh += nH.dot(ndH);   // this slice's <dh, h>, before the registers take the next one
+                pin(hdh);
                 ndO.store(sdO);
                 nV.store(sV);
             }
@@ -395,12 +399,6 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                         sdVn[rr * LS + cc] = to_e<E>(pdo[i][j][e] + __expf(gl - sG[rr]) * kdh[i][j][e]);
                     }
             }
-            // <dh, h> over this slice
-            for (int idx = threadIdx.x; idx < 64 * KD; idx += GNT) {
-                const int rr = idx / KD, cc = idx % KD;
-                hdh += (float)sH[rr * LK + cc] * (float)sdH[rr * LK + cc];
-            }
-            pin(hdh);
             lds_barrier();
             // ---- V_new = A Z
             {
