@@ -60,13 +60,15 @@ struct KPrepCfg {
 }  // namespace
 
 // ---------------------------------------------------------------- WY factors
-// Grid (chunks, H), 256 threads.  Writes, per unit u = chunk * H + head:
+// Grid (chunks, H), 512 threads (8 waves: wave w owns rows 16 (w & 3) .. +15
+// and column half w >> 2 of every product; the triangular inverse runs on
+// waves 0..3).  Writes, per unit u = chunk * H + head:
 // W, K̃, Qg = scale (Q ⊙ γ) as [u][64][KD], U as [u][64][VD], Aqk as
 // [u][64][64] (operand type S), and A in the input type as [B*T, H, 64].
 template <class E, class S, int KD, int VD>
-__global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, float scale) {
+__global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, float scale) {
     using Cf = KPrepCfg<S, KD, VD>;
-    constexpr int C = 64, NT = 256, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
+    constexpr int C = 64, NT = 512, LK = Cf::LK, LV = Cf::LV, LA = Cf::LA, LL = Cf::LL;
     constexpr int EPE = 16 / (int)sizeof(E);
     extern __shared__ __align__(16) unsigned char smem[];
     S* sK = (S*)(smem + Cf::oK);
@@ -83,6 +85,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, flo
     float* sM = sB + 64;
 
     const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int m0 = 16 * (w & 3), hc = w >> 2;   // row group, column half
     const int Cn = a.info[ci].len;
     const long t0 = a.info[ci].t0;
     const long unit = (long)ci * H + h;
@@ -131,10 +134,11 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, flo
         }
     }
 
-    // ---- Akk, Aqk over 32-channel slices (fp32 MFMA)   (wave w: rows 16w, all 64 columns)
-    f32x4 akk[1][4], aqk[1][4];
+    // ---- Akk, Aqk over 32-channel slices (fp32 MFMA)   (wave w: rows m0, columns 32 hc .. +31)
+    f32x4 akk[1][2], aqk[1][2];
     zero_acc(akk);
     zero_acc(aqk);
+#pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
         for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
             const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
@@ -146,18 +150,18 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, flo
             sQp[r * LSL + dd] = qv * ep;
         }
         lds_barrier();
-        wgemm<float, 1, 4, KSL, false, false>(akk, sKp, LSL, sKm, LSL, 16 * w, 0);
-        wgemm<float, 1, 4, KSL, false, false>(aqk, sQp, LSL, sKm, LSL, 16 * w, 0);
+        wgemm<float, 1, 2, KSL, false, false>(akk, sKp, LSL, sKm, LSL, m0, 32 * hc);
+        wgemm<float, 1, 2, KSL, false, false>(aqk, sQp, LSL, sKm, LSL, m0, 32 * hc);
         lds_barrier();
     }
     // ---- L = strictlower(diag(β) Akk) -> LDS;  Aqk (scaled, lower incl. diagonal) -> memory
     {
         S* Ao = (S*)a.Aqk + unit * C * C;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
+                const int r = acc_row(m0, 0, e), c = acc_col(32 * hc, j);
                 sL[r * LL + c] = c < r ? sB[r] * akk[0][j][e] : 0.f;
                 Ao[r * C + c] = (S)(c <= r ? scale * aqk[0][j][e] : 0.f);
             }
@@ -179,21 +183,21 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(KdaFullArgs a, int H, flo
         sQ[r * LK + d] = (S)((float)sK[r * LK + d] * __expf(g));
     }
     lds_barrier();
-    // ---- W = A diag(β) (K ⊙ γ),  U = A diag(β) V   (wave w: rows 16w, all columns)
+    // ---- W = A diag(β) (K ⊙ γ),  U = A diag(β) V   (wave w: rows m0, column half hc)
     {
-        f32x4 aw[1][KD / 16], au[1][VD / 16];
+        f32x4 aw[1][KD / 32], au[1][VD / 32];
         zero_acc(aw);
         zero_acc(au);
-        wgemm<S, 1, KD / 16, 64, false, true>(aw, sAb, LA, sQ, LK, 16 * w, 0);
-        wgemm<S, 1, VD / 16, 64, false, true>(au, sAb, LA, sV, LV, 16 * w, 0);
+        wgemm<S, 1, KD / 32, 64, false, true>(aw, sAb, LA, sQ, LK, m0, (KD / 2) * hc);
+        wgemm<S, 1, VD / 32, 64, false, true>(au, sAb, LA, sV, LV, m0, (VD / 2) * hc);
         lds_barrier();   // K and V are overwritten below
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int r = acc_row(16 * w, 0, e);
+            const int r = acc_row(m0, 0, e);
 #pragma unroll
-            for (int j = 0; j < KD / 16; j++) sK[r * LK + acc_col(0, j)] = (S)aw[0][j][e];
+            for (int j = 0; j < KD / 32; j++) sK[r * LK + acc_col((KD / 2) * hc, j)] = (S)aw[0][j][e];
 #pragma unroll
-            for (int j = 0; j < VD / 16; j++) sV[r * LV + acc_col(0, j)] = (S)au[0][j][e];
+            for (int j = 0; j < VD / 32; j++) sV[r * LV + acc_col((VD / 2) * hc, j)] = (S)au[0][j][e];
         }
     }
     lds_barrier();
@@ -402,16 +406,18 @@ struct KIntraCfg {
     static constexpr size_t oDAq = oVn + (size_t)C * LV * sizeof(S);   // dAqk [64][LF] fp32
     static constexpr size_t oDL = oDAq + (size_t)C * LF * 4;           // dL [64][LF] fp32
     static constexpr size_t oDG = oDL + (size_t)C * LF * 4;            // dG slice [64][LSL] fp32
-    static constexpr size_t oB = oDG + (size_t)C * LSL * 4;            // β [64], dβ row sums [64]
-    static constexpr size_t oPA = oB + (size_t)2 * 64 * 4;             // 4 fp32 slices [64][LSL]
+    static constexpr size_t oB = oDG + (size_t)C * LSL * 4;            // β [64], dβ row sums [2][64]
+    static constexpr size_t oPA = oB + (size_t)3 * 64 * 4;             // 4 fp32 slices [64][LSL]
     static constexpr size_t smem = oPA + (size_t)4 * C * LSL * 4;
     static_assert(smem <= 160 * 1024, "LDS budget");
 };
 
+// 512 threads: wave w owns rows 16 (w & 3) .. +15 and half w >> 2 of the
+// columns of every product.
 template <class E, class S, int KD, int VD>
-__global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, float scale) {
+__global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, float scale) {
     using Cf = KIntraCfg<S, VD>;
-    constexpr int C = 64, NT = 256, LV = Cf::LV, LF = Cf::LF;
+    constexpr int C = 64, NT = 512, LV = Cf::LV, LF = Cf::LF;
     constexpr int EPE = 16 / (int)sizeof(E);
     extern __shared__ __align__(16) unsigned char smem[];
     S* sDO = (S*)(smem + Cf::oDO);
@@ -427,6 +433,7 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
     float* sRB = sB + 64;
 
     const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int m0 = 16 * (w & 3), hc = w >> 2;   // row group, column half
     const int Cn = a.info[ci].len;
     const long t0 = a.info[ci].t0;
     const E* q = (const E*)a.q;
@@ -454,22 +461,23 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
     }
     if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)((const E*)a.beta)[(t0 + threadIdx.x) * H + h] : 0.f;
     lds_barrier();
-    // ---- dAqk = lower(dO V_newᵀ)    (wave w: rows 16w, 64 columns)
+    // ---- dAqk = lower(dO V_newᵀ)    (wave w: rows m0, columns 32 hc .. +31)
     {
-        f32x4 x[1][4];
+        f32x4 x[1][2];
         zero_acc(x);
-        wgemm<S, 1, 4, VD, false, false>(x, sDO, LV, sVn, LV, 16 * w, 0);
+        wgemm<S, 1, 2, VD, false, false>(x, sDO, LV, sVn, LV, m0, 32 * hc);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
+                const int r = acc_row(m0, 0, e), c = acc_col(32 * hc, j);
                 sDAq[r * LF + c] = c <= r ? x[0][j][e] : 0.f;
             }
     }
     lds_barrier();   // dO and V_new are no longer read: the slices take their place
 
-    float rbeta[4] = {0.f, 0.f, 0.f, 0.f};   // Σ_d K e^{G−m} ⊙ (dL K e^{m−G}) for rows 16w + 4g + e
+    float rbeta[4] = {0.f, 0.f, 0.f, 0.f};   // Σ_d K e^{G−m} ⊙ (dL K e^{m−G}) for rows m0 + 4g + e (this half)
+#pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
         for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
             const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
@@ -485,12 +493,12 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
         }
         lds_barrier();
         // this lane's elements of q, k and the stage partials, loaded before the products
-        float pk[2][4], pq[2][4], pdq[2][4], pdk[2][4], pdg[2][4];
+        float pk[1][4], pq[1][4], pdq[1][4], pdk[1][4], pdg[1][4];
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < 1; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int r = acc_row(16 * w, 0, e), d = s0 + acc_col(0, j);
+                const int r = acc_row(m0, 0, e), d = s0 + acc_col(16 * hc, j);
                 const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
                 pk[j][e] = (float)k[o];
                 pq[j][e] = (float)q[o];
@@ -498,21 +506,21 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
                 pdk[j][e] = a.dks[o];
                 pdg[j][e] = a.dgs[o];
             }
-        // wave w: rows 16w, the 32 channels of the slice
-        f32x4 p1[1][2], p2[1][2], p3[1][2], p4[1][2];
+        // wave w: rows m0, channels 16 hc .. +15 of the slice
+        f32x4 p1[1][1], p2[1][1], p3[1][1], p4[1][1];
         zero_acc(p1);
         zero_acc(p2);
         zero_acc(p3);
         zero_acc(p4);
-        wgemm<float, 1, 2, 64, false, true>(p1, sDAq, LF, sKm, LSL, 16 * w, 0);   // dAqk · K e^{m−G}
-        wgemm<float, 1, 2, 64, true, true>(p2, sDAq, LF, sQp, LSL, 16 * w, 0);    // dAqkᵀ · Q e^{G−m}
-        wgemm<float, 1, 2, 64, false, true>(p3, sDL, LF, sKm, LSL, 16 * w, 0);    // dL · K e^{m−G}
-        wgemm<float, 1, 2, 64, true, true>(p4, sDL, LF, sKb, LSL, 16 * w, 0);     // dLᵀ · β K e^{G−m}
+        wgemm<float, 1, 1, 64, false, true>(p1, sDAq, LF, sKm, LSL, m0, 16 * hc);   // dAqk · K e^{m−G}
+        wgemm<float, 1, 1, 64, true, true>(p2, sDAq, LF, sQp, LSL, m0, 16 * hc);    // dAqkᵀ · Q e^{G−m}
+        wgemm<float, 1, 1, 64, false, true>(p3, sDL, LF, sKm, LSL, m0, 16 * hc);    // dL · K e^{m−G}
+        wgemm<float, 1, 1, 64, true, true>(p4, sDL, LF, sKb, LSL, m0, 16 * hc);     // dLᵀ · β K e^{G−m}
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < 1; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int r = acc_row(16 * w, 0, e), dd = acc_col(0, j), d = s0 + dd;
+                const int r = acc_row(m0, 0, e), dd = acc_col(16 * hc, j), d = s0 + dd;
                 const float ep = sEp[r * LSL + dd];
                 const float em = ep > 0.f ? 1.f / ep : 0.f;
                 const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
@@ -535,7 +543,7 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
         if (threadIdx.x < KSL) {
             const int dd = threadIdx.x;
             float acc = 0.f;
-#pragma unroll
+#pragma unroll 8
             for (int r = C - 1; r >= 0; r--) {
                 acc += sDG[r * LSL + dd];
                 if (r < Cn) a.dg[((t0 + r) * H + h) * KD + s0 + dd] = acc;
@@ -551,12 +559,12 @@ __global__ void __launch_bounds__(256) kda_intra_kernel(KdaFullArgs a, int H, fl
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        sRB[16 * w + 4 * (lane_id() >> 4) + e] = x;   // every lane of the group holds the sum
+        sRB[64 * hc + m0 + 4 * (lane_id() >> 4) + e] = x;   // every lane of the group holds the sum
     }
     lds_barrier();
     if (threadIdx.x < Cn) {
         const int r = threadIdx.x;
-        a.dbeta[(t0 + r) * H + h] = a.dbs[(t0 + r) * H + h] + sRB[r];
+        a.dbeta[(t0 + r) * H + h] = a.dbs[(t0 + r) * H + h] + (sRB[r] + sRB[64 + r]);
     }
 }
 
@@ -570,7 +578,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
         const int sm = (int)KPrepCfg<S, KD, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), sm, s, a, p.HV, p.scale);
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(512), sm, s, a, p.HV, p.scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
@@ -597,7 +605,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
         const int sm = (int)KIntraCfg<S, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(256), sm, s, a, p.HV, p.scale);
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(512), sm, s, a, p.HV, p.scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return mark(4);
