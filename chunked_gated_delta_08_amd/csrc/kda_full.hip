@@ -280,41 +280,77 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
                                        : 0.f;
     }
     const int nch = c_end - c_first;
-    for (int it = 0; it < nch; it++) {
-        const int ci = REV ? c_end - 1 - it : c_first + it;
+    // operand registers of one chunk: the next chunk's are loaded while the
+    // current one is computed
+    constexpr int EPE = 16 / (int)sizeof(E);
+    static_assert(EPE == EPS, "input and operand types share a width");
+    static_assert(C * KD / EPS % NT == 0 && C * 64 / EPS % NT == 0 && C * C / EPS % NT == 0, "whole vectors");
+    constexpr int NKW = C * KD / EPS / NT, NXS = C * 64 / EPS / NT, NAQ = C * C / EPS / NT;
+    kvec<S, EPS> rW[NKW], rKT[NKW], rQG[REV ? NKW : 1], rU[REV ? 1 : NXS], rAq[REV ? NAQ : 1];
+    kvec<E, EPE> rO[REV ? NXS : 1];
+    float rgc = 0.f;
+    auto chunk_at = [&](int it) { return REV ? c_end - 1 - it : c_first + it; };
+    auto issue = [&](int it) {
+        const int ci = chunk_at(it);
         const int Cn = a.info[ci].len;
         const long t0 = a.info[ci].t0;
         const long unit = (long)ci * H + h;
-        // ---- stage this chunk's operands and the state copy
-        for (int idx = threadIdx.x; idx < C * KD / EPS; idx += NT) {
-            const int r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
-            *(kvec<S, EPS>*)(sW + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.W + (unit * C + r) * KD + c);
-            *(kvec<S, EPS>*)(sKT + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.KT + (unit * C + r) * KD + c);
-            if (REV)
-                *(kvec<S, EPS>*)(sQG + r * LK + c) = *(const kvec<S, EPS>*)((const S*)a.QG + (unit * C + r) * KD + c);
-        }
-        for (int idx = threadIdx.x; idx < C * 64 / EPS; idx += NT) {
-            const int r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
-            kvec<S, EPS> x;
-            if (REV) {   // dO slice (rows past the chunk zero)
-                const int rc = min(r, Cn - 1);
-                constexpr int EPE = 16 / (int)sizeof(E);
-                static_assert(EPE == EPS, "input and operand types share a width");
-                const kvec<E, EPE> y = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + rc) * H + h) * VD + vc0 + c);
 #pragma unroll
-                for (int e = 0; e < EPS; e++) x[e] = r < Cn ? (S)(float)y[e] : (S)0.f;
-            } else {     // U slice
-                x = *(const kvec<S, EPS>*)((const S*)a.U + (unit * C + r) * VD + vc0 + c);
+        for (int i = 0; i < NKW; i++) {
+            const long o = unit * C * KD + (long)(threadIdx.x + NT * i) * EPS;
+            rW[i] = *(const kvec<S, EPS>*)((const S*)a.W + o);
+            rKT[i] = *(const kvec<S, EPS>*)((const S*)a.KT + o);
+            if constexpr (REV) rQG[i] = *(const kvec<S, EPS>*)((const S*)a.QG + o);
+        }
+#pragma unroll
+        for (int i = 0; i < NXS; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
+            if constexpr (REV)   // dO slice; rows past the chunk read its last row (zeroed when staged)
+                rO[i] = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + min(r, Cn - 1)) * H + h) * VD + vc0 + c);
+            else
+                rU[i] = *(const kvec<S, EPS>*)((const S*)a.U + (unit * C + r) * VD + vc0 + c);
+        }
+        if constexpr (REV) {
+#pragma unroll
+            for (int i = 0; i < NAQ; i++)
+                rAq[i] = *(const kvec<S, EPS>*)((const S*)a.Aqk + unit * C * C + (long)(threadIdx.x + NT * i) * EPS);
+        }
+        if (threadIdx.x < KD) rgc = a.gcum[((t0 + Cn - 1) * H + h) * KD + threadIdx.x];
+    };
+    if (nch > 0) issue(0);
+    for (int it = 0; it < nch; it++) {
+        const int ci = chunk_at(it);
+        const int Cn = a.info[ci].len;
+        const long t0 = a.info[ci].t0;
+        const long unit = (long)ci * H + h;
+        // ---- stage this chunk's operands (from the registers) and the state copy
+#pragma unroll
+        for (int i = 0; i < NKW; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (KD / EPS), c = (idx % (KD / EPS)) * EPS;
+            *(kvec<S, EPS>*)(sW + r * LK + c) = rW[i];
+            *(kvec<S, EPS>*)(sKT + r * LK + c) = rKT[i];
+            if constexpr (REV) *(kvec<S, EPS>*)(sQG + r * LK + c) = rQG[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NXS; i++) {
+            const int idx = threadIdx.x + NT * i, r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
+            kvec<S, EPS> x;
+            if constexpr (REV) {
+#pragma unroll
+                for (int e = 0; e < EPS; e++) x[e] = r < Cn ? (S)(float)rO[i][e] : (S)0.f;
+            } else {
+                x = rU[i];
             }
             *(kvec<S, EPS>*)(sX + r * LS + c) = x;
         }
-        if (REV) {
-            for (int idx = threadIdx.x; idx < C * C / EPS; idx += NT) {
-                const int r = idx / (C / EPS), c = (idx % (C / EPS)) * EPS;
-                *(kvec<S, EPS>*)(sAq + r * LA + c) = *(const kvec<S, EPS>*)((const S*)a.Aqk + (unit * C + r) * C + c);
+        if constexpr (REV) {
+#pragma unroll
+            for (int i = 0; i < NAQ; i++) {
+                const int idx = threadIdx.x + NT * i, r = idx / (C / EPS), c = (idx % (C / EPS)) * EPS;
+                *(kvec<S, EPS>*)(sAq + r * LA + c) = rAq[i];
             }
         }
-        for (int d = threadIdx.x; d < KD; d += NT) sGC[d] = __expf(a.gcum[((t0 + Cn - 1) * H + h) * KD + d]);
+        if (threadIdx.x < KD) sGC[threadIdx.x] = __expf(rgc);
         // state copy as [KD][64] and the fp32 state of this chunk boundary to memory
         {
             float* so = (REV ? a.dhs : a.hs) + unit * KV;
@@ -330,6 +366,7 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
                     }
         }
         lds_barrier();
+        if (it + 1 < nch) issue(it + 1);   // the next chunk's loads fly during this one's products
         // ---- V_new = U − W h   or   dV_new = Aqkᵀ dO + K̃ dh      (wave w: rows 16w, 64 columns)
         {
             f32x4 x[1][4];
