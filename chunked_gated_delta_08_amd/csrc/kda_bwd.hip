@@ -66,6 +66,11 @@ __device__ __forceinline__ void kda_find_chunk(const int32_t* __restrict__ cu, i
     len = 0;
 }
 
+template <class T, int N> using kdv = T __attribute__((ext_vector_type(N)));
+
+// rows [0, rows) of a row-major block (row stride rs) into LDS (row pitch LD),
+// converted to E; rows at or past rows_valid are zero.  One 16-byte load and
+// one vector LDS write per step.
 template <class Ein, class E, int D, int LD>
 __device__ __forceinline__ void kda_load(E* s, const Ein* __restrict__ g, long rs, int rows_valid, int rows) {
     constexpr int EPV = 16 / sizeof(Ein);
@@ -75,10 +80,32 @@ __device__ __forceinline__ void kda_load(E* s, const Ein* __restrict__ g, long r
         typename Vec16<Ein>::t v;
         if (r < rows_valid) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
         else v = typename Vec16<Ein>::t{};
+        kdv<E, EPV> y;
 #pragma unroll
-        for (int e = 0; e < EPV; e++) s[r * LD + c * EPV + e] = (E)(float)v[e];
+        for (int e = 0; e < EPV; e++) y[e] = (E)(float)v[e];
+        *(kdv<E, EPV>*)(s + r * LD + c * EPV) = y;
     }
 }
+
+// A fp32 KD x VD state block into LDS as E (pitch LD), keeping this thread's
+// values: NS float4 per thread, element (row (tid + 512 i) / (VD/4), ...).
+template <class E, int KD, int VD, int LD>
+struct KdaStateRegs {
+    static constexpr int VPR = VD / 4, NS = KD * VPR / 512;
+    static_assert(KD * VPR % 512 == 0, "whole vectors per thread");
+    f32x4 v[NS];
+    __device__ __forceinline__ void load(E* s, const float* __restrict__ g) {
+#pragma unroll
+        for (int i = 0; i < NS; i++) {
+            const int idx = threadIdx.x + 512 * i, r = idx / VPR, c = idx % VPR;
+            v[i] = *(const f32x4*)(g + (long)r * VD + c * 4);
+            kdv<E, 4> y;
+#pragma unroll
+            for (int e = 0; e < 4; e++) y[e] = (E)v[i][e];
+            *(kdv<E, 4>*)(s + r * LD + c * 4) = y;
+        }
+    }
+};
 
 template <class E, int KD, int VD>
 __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H,
@@ -118,7 +145,8 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     auto gidx = [&](int r, int c) { return ((t0 + r) * H + hh) * (long)KD + c; };   // [.,H,KD] element
 
     // ---- stage h, dO, dv_in, A (lower triangle), β, β γ K, β V
-    kda_load<float, E, VD, LV>(sH, hg, VD, KD, KD);
+    KdaStateRegs<E, KD, VD, LV> hreg;   // h stays in registers for rowsum_V(h ⊙ dh)
+    hreg.load(sH, hg);
     kda_load<E, E, VD, LV>(sX, dO + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
     kda_load<E, E, VD, LV>(sDV, dvi + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
     for (int idx = threadIdx.x; idx < C * 64; idx += 512) {
@@ -127,29 +155,30 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
         sA[r * LA + c] = (E)x;
     }
     if (threadIdx.x < C) sB[threadIdx.x] = threadIdx.x < Cn ? (float)beta[(t0 + threadIdx.x) * H + hh] : 0.f;
-    // rowsum_V(h ⊙ dh) in fp32 straight from memory: 4 threads per key
-    {
-        const int key = threadIdx.x >> 2, part = threadIdx.x & 3;
-        float s = 0.f;
-        if (key < KD)
-            for (int c = part; c < VD; c += 4) s += hg[key * VD + c] * dhg[key * VD + c];
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        // all four lanes of a key hold the sum and write it (key < KD is uniform per wave)
-        if (key < KD) sHD[key] = s;
-    }
     lds_barrier();
-    for (int idx = threadIdx.x; idx < C * KD; idx += 512) {
-        const int r = idx / KD, c = idx % KD;
-        float x = 0.f;
-        if (r < Cn) x = sB[r] * __expf(a.g[gidx(r, c)]) * (float)k[gidx(r, c)];
-        sKb[r * LK + c] = (E)x;
-    }
-    for (int idx = threadIdx.x; idx < C * VD; idx += 512) {
-        const int r = idx / VD, c = idx % VD;
-        float x = 0.f;
-        if (r < Cn) x = sB[r] * (float)v[((t0 + r) * H + hh) * VD + c];
-        sVb[r * LV + c] = (E)x;
+    {   // β γ K and β V, one 16-byte load of k / v (and the matching gates) per step
+        constexpr int EPE = 16 / (int)sizeof(E);
+        for (int idx = threadIdx.x; idx < C * KD / EPE; idx += 512) {
+            const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
+            const kdv<E, EPE> kv = *(const kdv<E, EPE>*)(k + gidx(rc, c));
+            kdv<E, EPE> y;
+#pragma unroll
+            for (int e4 = 0; e4 < EPE; e4 += 4) {
+                const f32x4 gv = *(const f32x4*)(a.g + gidx(rc, c + e4));
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    y[e4 + e] = (E)(r < Cn ? sB[r] * __expf(gv[e]) * (float)kv[e4 + e] : 0.f);
+            }
+            *(kdv<E, EPE>*)(sKb + r * LK + c) = y;
+        }
+        for (int idx = threadIdx.x; idx < C * VD / EPE; idx += 512) {
+            const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
+            const kdv<E, EPE> vv = *(const kdv<E, EPE>*)(v + ((t0 + rc) * H + hh) * VD + c);
+            kdv<E, EPE> y;
+#pragma unroll
+            for (int e = 0; e < EPE; e++) y[e] = (E)(r < Cn ? sB[r] * (float)vv[e] : 0.f);
+            *(kdv<E, EPE>*)(sVb + r * LV + c) = y;
+        }
     }
 
     // ---- dq_acc = dO hᵀ,  dw = −dv hᵀ      (B = hᵀ: h stored [key][v] = [n][k])
@@ -159,8 +188,22 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     wgemm<E, 2, TN, VD, false, false>(dqa, sX, LV, sH, LV, m0, n0k);
     wgemm<E, 2, TN, VD, false, false>(dwa, sDV, LV, sH, LV, m0, n0k);
     lds_barrier();
-    // ---- swap in dh and V_new; dw -> LDS
-    kda_load<float, E, VD, LV>(sH, dhg, VD, KD, KD);
+    // ---- swap in dh and V_new; dw -> LDS; rowsum_V(h ⊙ dh) in fp32 from the registers
+    {
+        KdaStateRegs<E, KD, VD, LV> dhreg;
+        dhreg.load(sH, dhg);
+        constexpr int VPR = KdaStateRegs<E, KD, VD, LV>::VPR;   // lanes per key row (16 or 32)
+#pragma unroll
+        for (int i = 0; i < KdaStateRegs<E, KD, VD, LV>::NS; i++) {
+            float x = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) x += hreg.v[i][e] * dhreg.v[i][e];
+#pragma unroll
+            for (int off = 1; off < VPR; off <<= 1) x += __shfl_xor(x, off, 64);
+            // all VPR lanes of the row hold the sum and write it
+            sHD[(threadIdx.x + 512 * i) / VPR] = x;
+        }
+    }
     kda_load<E, E, VD, LV>(sX, vn + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
 #pragma unroll
     for (int i = 0; i < 2; i++)
