@@ -69,7 +69,12 @@ struct GradCfg {
     // dv slice [64][LS] staged for coalesced stores (16-bit types; fp32 stores directly)
     static constexpr bool DV_LDS = sizeof(E) == 2;
     static constexpr size_t oDv = oSm + (size_t)(3 * 64 + 8 * 64 + 2 * 64 + 80) * 4;
-    static constexpr size_t smem = oDv + (DV_LDS ? (size_t)C * LS * sizeof(E) : 0);
+    // V_new of the slice gets its own [64][LS] buffer when it fits (else it
+    // overwrites Z in place, one barrier later)
+    static constexpr size_t oEnd = oDv + (DV_LDS ? (size_t)C * LS * sizeof(E) : 0);
+    static constexpr bool VN2 = oEnd + (size_t)C * LS * sizeof(E) <= 160 * 1024;
+    static constexpr size_t oVn2 = VN2 ? oEnd : oVn;
+    static constexpr size_t smem = oEnd + (VN2 ? (size_t)C * LS * sizeof(E) : 0);
     static constexpr size_t oV = oQ;                                    // [64][LS] inside the V loop
     static constexpr size_t odW = oH;                                   // [64][LK]
     static constexpr size_t odA = odH;                                  // [64][LA]
@@ -247,7 +252,8 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
     E* sdH = (E*)(smem + Cf::odH);
     E* sdO = (E*)(smem + Cf::odO);
     E* sV = (E*)(smem + Cf::oV);
-    E* sVn = (E*)(smem + Cf::oVn);
+    E* sVn = (E*)(smem + Cf::oVn);     // Z = diag(β)(V − diag(γ) K h) of the slice
+    E* sVn2 = (E*)(smem + Cf::oVn2);   // V_new = A Z of the slice (own buffer when it fits)
     E* sdVn = (E*)(smem + Cf::odVn);
     E* sdW = (E*)(smem + Cf::odW);
     E* sdA = (E*)(smem + Cf::odA);
@@ -405,20 +411,20 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 f32x4 vn[2][TNS];
                 zero_acc(vn);
                 wgemm<E, 2, TNS, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
-                lds_barrier();
+                if constexpr (!Cf::VN2) lds_barrier();   // V_new overwrites Z
 #pragma unroll
                 for (int i = 0; i < 2; i++)
 #pragma unroll
                     for (int j = 0; j < TNS; j++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) sVn[acc_row(m0, i, e) * LS + acc_col(n0s, j)] = to_e<E>(vn[i][j][e]);
+                    for (int e = 0; e < 4; e++) sVn2[acc_row(m0, i, e) * LS + acc_col(n0s, j)] = to_e<E>(vn[i][j][e]);
             }
             lds_barrier();
             // ---- accumulate the state products and the V-separable outputs
-            wgemm<E, 2, TNS, 64, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);     // dO V_newᵀ
+            wgemm<E, 2, TNS, 64, false, false>(dPm, sdO, LS, sVn2, LS, m0, n0s);    // dO V_newᵀ
             wgemm<E, 2, TNK, 64, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);    // dO hᵀ
             wgemm<E, 2, TNK, 64, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);   // dV_new hᵀ
-            wgemm<E, 2, TNK, 64, false, true>(dks, sVn, LS, sdH, LK, m0, n0k);   // V_new dhᵀ
+            wgemm<E, 2, TNK, 64, false, true>(dks, sVn2, LS, sdH, LK, m0, n0k);  // V_new dhᵀ
             wgemm<E, 2, TNS, 64, false, false>(dAp, sdVn, LS, sV, LS, m0, n0s);     // dV_new Vᵀ
             {
                 f32x4 adv[2][TNS];
