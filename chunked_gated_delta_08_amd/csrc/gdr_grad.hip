@@ -665,9 +665,9 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                 }
             if (hi + 1 < G) return;   // uniform: only the last head of the group stores dq, dk
         }
-        lds_barrier();
     }
-    // ---- the group sums dq, dk for this key head, through LDS (sH, sdH are free)
+    // ---- the group sums dq, dk for this key head, through LDS (sH and sdH were last
+    //      read before the dA_pre and M1 barriers above)
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
