@@ -399,17 +399,6 @@ int kda_chunk_bwd_full_events(const gdr_problem* p, const void* qp, const void* 
     a.dqs = (float*)(base + w.dqs); a.dks = (float*)(base + w.dks); a.dgs = (float*)(base + w.dgs);
     a.dbs = (float*)(base + w.dbs); a.dA = (float*)(base + w.dA);
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
-    if (q.NT == 0) {   // no tokens: dh0 = dht (or zero) through the reverse scan alone is not launched
-        if (dh0) {
-            const size_t bytes = (size_t)q.N * q.HV * q.K * q.V * 4;
-            hipError_t e = dht ? hipMemcpyAsync(dh0, dht, bytes, hipMemcpyDeviceToDevice, stream)
-                               : hipMemsetAsync(dh0, 0, bytes, stream);
-            if ((st = launch_status(e)) != GDR_OK) return st;
-        }
-        for (int i = 1; ev && i < 5; i++)
-            if ((st = launch_status(hipEventRecord(ev[i], stream))) != GDR_OK) return st;
-        return GDR_OK;
-    }
     return launch_status(gdr::launch_kda_full(q, a, stream, ev));
 }
 

@@ -606,11 +606,13 @@ __global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, fl
 }
 
 // ---------------------------------------------------------------- launchers
+// With no chunks at all (T = 0) only the scans run: their zero-chunk jobs pass
+// dht (or zero) through to dh0.
 template <class E, class S, int KD, int VD>
 static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_t s, hipEvent_t* ev) {
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
     hipError_t e;
-    {
+    if (p.NT > 0) {
         auto kern = kda_prep_kernel<E, S, KD, VD>;
         const int sm = (int)KPrepCfg<S, KD, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
@@ -629,7 +631,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(2)) != hipSuccess) return e;
-    {
+    if (p.NT > 0) {
         KdaArgs k{};
         k.q = a.q; k.k = a.k; k.v = a.v; k.v_new = a.vn; k.g = a.gcum; k.beta = a.beta; k.A = a.A;
         k.h = a.hs; k.dO = a.dO; k.dh = a.dhs; k.dv_in = a.dvn; k.info = a.info;
@@ -637,7 +639,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
         if ((e = launch_kda(p, k, s)) != hipSuccess) return e;
     }
     if ((e = mark(3)) != hipSuccess) return e;
-    {
+    if (p.NT > 0) {
         auto kern = kda_intra_kernel<E, S, KD, VD>;
         const int sm = (int)KIntraCfg<S, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
