@@ -140,14 +140,22 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
     zero_acc(aqk);
 #pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
-        for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
-            const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
-            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-            const float ep = __expf(g - sM[d]), em = __expf(sM[d] - g);
-            const float kv = (float)sK[r * LK + d], qv = (float)sQ[r * LK + d];
-            sKp[r * LSL + dd] = kv * ep;
-            sKm[r * LSL + dd] = kv * em;
-            sQp[r * LSL + dd] = qv * ep;
+        for (int idx = threadIdx.x; idx < C * KSL / 4; idx += NT) {   // 4 channels per step
+            const int r = idx / (KSL / 4), dd = (idx % (KSL / 4)) * 4, d = s0 + dd;
+            const f32x4 g = *(const f32x4*)(G + ((t0 + min(r, Cn - 1)) * H + h) * KD + d);
+            const f32x4 m = *(const f32x4*)(sM + d);
+            const kvec<S, 4> kv = *(const kvec<S, 4>*)(sK + r * LK + d), qv = *(const kvec<S, 4>*)(sQ + r * LK + d);
+            f32x4 kp, km, qp;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float ep = __expf(g[e] - m[e]), em = __expf(m[e] - g[e]);
+                kp[e] = (float)kv[e] * ep;
+                km[e] = (float)kv[e] * em;
+                qp[e] = (float)qv[e] * ep;
+            }
+            *(f32x4*)(sKp + r * LSL + dd) = kp;
+            *(f32x4*)(sKm + r * LSL + dd) = km;
+            *(f32x4*)(sQp + r * LSL + dd) = qp;
         }
         lds_barrier();
         wgemm<float, 1, 2, KSL, false, false>(akk, sKp, LSL, sKm, LSL, m0, 32 * hc);
@@ -516,17 +524,25 @@ __global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, fl
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};   // Σ_d K e^{G−m} ⊙ (dL K e^{m−G}) for rows m0 + 4g + e (this half)
 #pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
-        for (int idx = threadIdx.x; idx < C * KSL; idx += NT) {
-            const int r = idx / KSL, dd = idx % KSL, d = s0 + dd;
-            const float m = G[((t0 + ref) * H + h) * KD + d];
-            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-            const float ep = r < Cn ? __expf(g - m) : 0.f, em = r < Cn ? __expf(m - g) : 0.f;
-            const float kv = (float)k[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-            const float qv = (float)q[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-            sKm[r * LSL + dd] = kv * em;
-            sQp[r * LSL + dd] = qv * ep;
-            sKb[r * LSL + dd] = sB[r] * kv * ep;
-            sEp[r * LSL + dd] = ep;
+        for (int idx = threadIdx.x; idx < C * KSL / 4; idx += NT) {   // 4 channels per step
+            const int r = idx / (KSL / 4), dd = (idx % (KSL / 4)) * 4, d = s0 + dd;
+            const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
+            const f32x4 m = *(const f32x4*)(G + ((t0 + ref) * H + h) * KD + d);
+            const f32x4 g = *(const f32x4*)(G + o);
+            const kvec<E, 4> kv = *(const kvec<E, 4>*)(k + o), qv = *(const kvec<E, 4>*)(q + o);
+            f32x4 km, qp, kb, epv;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float ep = r < Cn ? __expf(g[e] - m[e]) : 0.f, em = r < Cn ? __expf(m[e] - g[e]) : 0.f;
+                km[e] = (float)kv[e] * em;
+                qp[e] = (float)qv[e] * ep;
+                kb[e] = sB[r] * (float)kv[e] * ep;
+                epv[e] = ep;
+            }
+            *(f32x4*)(sKm + r * LSL + dd) = km;
+            *(f32x4*)(sQp + r * LSL + dd) = qp;
+            *(f32x4*)(sKb + r * LSL + dd) = kb;
+            *(f32x4*)(sEp + r * LSL + dd) = epv;
         }
         lds_barrier();
         // this lane's elements of q, k and the stage partials, loaded before the products
