@@ -568,17 +568,33 @@ scan_kernel(ScanArgs a, int nfwd, int HV) {
     }
 }
 
-// Local segment scans (16-bit operands only).  Roles, NS*HV blocks each:
+// Local segment scans (16-bit operands only).  Roles, NS*HV jobs each:
 //   0: forward from zero over the segment  -> hloc  (not for a sequence's last segment)
 //   1: reverse from zero over the segment  -> dhloc (not for its first segment)
 //   2: transfer matrix P = Π (γ_C I − K̃ᵀ W) over the segment, from I -> P
 //      (only for sequences with more than one segment)
+// Roles 0 and 2 read the same W and K̃ tiles in the same order, so their jobs
+// are interleaved in groups of 8: blocks 16 j + i and 16 j + 8 + i (i < 8) are
+// the two roles of job 8 j + i -- the same XCD under round-robin dispatch and
+// started together, so the second reader finds the tiles in that XCD's L2.
+// Role 1 follows in blocks [2 * seg_pairs(per), ...).
 // The caller passes arguments with no per-chunk outputs (hT, dhT, h32, v_new).
+__host__ __device__ constexpr int seg_pairs(int per) { return (per + 7) / 8 * 8; }
+
 template <class E, class S, int KD, int VD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 seg_kernel(ScanArgs a, int NS, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int per = NS * HV, role = (int)blockIdx.x / per, b = (int)blockIdx.x % per;
+    const int per = NS * HV, x = (int)blockIdx.x, np = seg_pairs(per);
+    int role, b;
+    if (x < 2 * np) {
+        role = (x & 8) ? 2 : 0;
+        b = (x >> 4) * 8 + (x & 7);
+    } else {
+        role = 1;
+        b = x - 2 * np;
+    }
+    if (b >= per) return;
     const SegView v = seg_view(a, b / HV);
     const long KV = (long)KD * VD;
     ScanJob jb;
@@ -741,7 +757,7 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
             if (hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) !=
                 hipSuccess)
                 return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL(k1, dim3(3 * per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
+            hipLaunchKernelGGL(k1, dim3(2 * seg_pairs(per) + per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             constexpr int csm = KD * (KD + spad<S>()) * (int)sizeof(S);
