@@ -67,9 +67,30 @@ lib.kda_chunk_bwd_full_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 
 lib.kda_chunk_bwd.restype = ctypes.c_int
 lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
 
+
+
+
+class BigdnProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("F", ctypes.c_int), ("S", ctypes.c_int), ("H", ctypes.c_int),
+                ("D", ctypes.c_int), ("k_scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("eps", ctypes.c_float)]
+
+
+lib.bigdn_workspace_size.restype = _sz
+lib.bigdn_workspace_size.argtypes = [ctypes.POINTER(BigdnProblem), ctypes.c_int]
+lib.bigdn_fwd.restype = ctypes.c_int
+lib.bigdn_fwd.argtypes = [ctypes.POINTER(BigdnProblem)] + [_vp] * 8 + [_vp, _sz, _vp]
+lib.bigdn_fwd_events.restype = ctypes.c_int
+lib.bigdn_fwd_events.argtypes = [ctypes.POINTER(BigdnProblem)] + [_vp] * 8 + [_vp, _sz, _vp, _vp]
+lib.bigdn_bwd.restype = ctypes.c_int
+lib.bigdn_bwd.argtypes = [ctypes.POINTER(BigdnProblem)] + [_vp] * 13 + [_vp, _sz, _vp]
+lib.bigdn_bwd_events.restype = ctypes.c_int
+lib.bigdn_bwd_events.argtypes = [ctypes.POINTER(BigdnProblem)] + [_vp] * 13 + [_vp, _sz, _vp, _vp]
+
 EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_gate_cumsum",
             "gdr_chunk_fwd", "gdr_chunk_fwd_events", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd",
-            "kda_workspace_size", "kda_chunk_bwd_full", "kda_chunk_bwd_full_events"]
+            "kda_workspace_size", "kda_chunk_bwd_full", "kda_chunk_bwd_full_events", "bigdn_workspace_size",
+            "bigdn_fwd", "bigdn_fwd_events", "bigdn_bwd", "bigdn_bwd_events"]
 
 
 def _check(code):
@@ -249,4 +270,72 @@ def kda_chunk_bwd_full(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=N
                                   _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
                                   workspace.numel(), _stream(stream)))
     del keep
+    return out
+
+
+# --------------------------------------------------------------------------
+# BiGDN layer (include/bigdn.h).  Layouts: qkv bf16 [B, N, 3, H, D] with
+# N = F*S; beta fp32 [B, H, F, S]; decay fp32 [B, H, F]; norm weights fp32
+# [H*D]; rope cos/sin fp32 [N, D]; out / dout bf16 [B, N, H, D].
+
+def bigdn_problem(qkv, F, S, k_scale=1.0, norm_eps=1e-5, eps=1e-6):
+    B, N, three, H, D = qkv.shape
+    assert three == 3 and N == F * S
+    return BigdnProblem(B, F, S, H, D, float(k_scale), float(norm_eps), float(eps))
+
+
+def _bigdn_inputs(qkv, beta, decay, qw, kw, cos, sin, F, S):
+    B, N, _, H, D = qkv.shape
+    assert qkv.dtype == torch.bfloat16
+    for t, shape in ((beta, (B, H, F, S)), (decay, (B, H, F)), (qw, (H * D,)), (kw, (H * D,)), (cos, (N, D)),
+                     (sin, (N, D))):
+        assert t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == shape
+    assert qkv.is_cuda and qkv.is_contiguous()
+
+
+def bigdn_workspace_size(p, bwd):
+    return int(lib.bigdn_workspace_size(ctypes.byref(p), 1 if bwd else 0))
+
+
+def bigdn_fwd(qkv, beta, decay, qw, kw, cos, sin, F, S, k_scale=1.0, norm_eps=1e-5, eps=1e-6, out=None,
+              workspace=None, stream=None, events=None):
+    """BiGDN layer output bf16 [B, N, H, D]."""
+    _bigdn_inputs(qkv, beta, decay, qw, kw, cos, sin, F, S)
+    p = bigdn_problem(qkv, F, S, k_scale, norm_eps, eps)
+    B, N, _, H, D = qkv.shape
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=qkv.device)
+    if workspace is None:
+        workspace = torch.empty(max(bigdn_workspace_size(p, False), 1), dtype=torch.uint8, device=qkv.device)
+    args = [ctypes.byref(p), _ptr(qkv), _ptr(beta), _ptr(decay), _ptr(qw), _ptr(kw), _ptr(cos), _ptr(sin),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)]
+    if events is None:
+        _check(lib.bigdn_fwd(*args))
+    else:
+        _check(lib.bigdn_fwd_events(*args, events))
+    return out
+
+
+def bigdn_bwd(qkv, beta, decay, qw, kw, cos, sin, dout, F, S, k_scale=1.0, norm_eps=1e-5, eps=1e-6, out=None,
+              workspace=None, stream=None, events=None):
+    """BiGDN layer backward.  Returns dict dqkv (bf16, qkv's shape), dbeta, ddecay,
+    dqw, dkw (fp32)."""
+    _bigdn_inputs(qkv, beta, decay, qw, kw, cos, sin, F, S)
+    B, N, _, H, D = qkv.shape
+    assert dout.is_cuda and dout.is_contiguous() and dout.dtype == torch.bfloat16
+    assert tuple(dout.shape) == (B, N, H, D)
+    p = bigdn_problem(qkv, F, S, k_scale, norm_eps, eps)
+    dev = qkv.device
+    if out is None:
+        out = {"dqkv": torch.empty_like(qkv), "dbeta": torch.empty_like(beta), "ddecay": torch.empty_like(decay),
+               "dqw": torch.empty_like(qw), "dkw": torch.empty_like(kw)}
+    if workspace is None:
+        workspace = torch.empty(max(bigdn_workspace_size(p, True), 1), dtype=torch.uint8, device=dev)
+    args = [ctypes.byref(p), _ptr(qkv), _ptr(beta), _ptr(decay), _ptr(qw), _ptr(kw), _ptr(cos), _ptr(sin),
+            _ptr(dout), _ptr(out["dqkv"]), _ptr(out["dbeta"]), _ptr(out["ddecay"]), _ptr(out["dqw"]),
+            _ptr(out["dkw"]), _ptr(workspace), workspace.numel(), _stream(stream)]
+    if events is None:
+        _check(lib.bigdn_bwd(*args))
+    else:
+        _check(lib.bigdn_bwd_events(*args, events))
     return out

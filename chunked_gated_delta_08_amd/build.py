@@ -18,14 +18,15 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip", "gdr_fwd.hip", "kda_full.hip"]
+HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip", "gdr_fwd.hip", "kda_full.hip",
+               "bigdn.hip"]
 # per-source device flags: the WY-factor, scan and KDA kernels keep MFMA
 # accumulators in VGPRs; the gradient and forward-output kernels are left to
 # the compiler's register-class heuristics
 SOURCE_FLAGS = {"gdr_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "gdr_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
-HOST_SOURCES = ["gdr_api.cpp"]
+HOST_SOURCES = ["gdr_api.cpp", "bigdn_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -195,3 +195,41 @@ def kda_full_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0,
     return {"q": t(q), "k": t(k), "v": t(v), "beta": t(beta), "dO": t(dO), "graw": f(graw), "gcum": f(gcum),
             "dht": f(dht_a), "h0": f(h0_a), "cu": cu, "B": B, "T": T if lengths is None else ntok, "H": H, "K": K,
             "V": V, "BT": BT, "N": N, "ntok": ntok, "dtype": dtype}
+
+
+def rope_tables(N, D, base=10000.0):
+    """Rotary tables [N, D] fp32 for positions 0..N-1: channel pair (2i, 2i+1)
+    turns by the angle n * base^(-2i/D); cos repeats per pair and sin carries
+    the sign pattern (-sin, +sin), so x*cos + pairflip(x)*sin is a rotation."""
+    inv = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+    ang = np.arange(N, dtype=np.float64)[:, None] * inv[None, :]
+    cos = np.repeat(np.cos(ang), 2, axis=1)
+    sin = np.stack([-np.sin(ang), np.sin(ang)], axis=-1).reshape(N, D)
+    return cos.astype(np.float32), sin.astype(np.float32)
+
+
+def bigdn_inputs(B=8, F=11, S=1024, H=16, D=128, seed=0, k_scale=None):
+    """Inputs of one BiGDN layer call (CPU torch tensors).
+
+    qkv = randn bf16 [B, N, 3, H, D] (N = F*S); beta = sigmoid(randn) fp32
+    [B, H, F, S]; decay = sigmoid(randn) fp32 [B, H, F]; q/k norm weights
+    1 + 0.1 randn fp32 [H*D]; rope tables from rope_tables(N, D); dout = randn
+    bf16 [B, N, H, D].  k_scale defaults to 2/sqrt(S*D), which keeps the
+    spectral norm of the frame sums P well below 1 at these distributions."""
+    rng = np.random.default_rng(seed)
+    N = F * S
+
+    def randn(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    qkv = randn(B, N, 3, H, D)
+    beta = _sigmoid(randn(B, H, F, S).astype(np.float64)).astype(np.float32)
+    decay = _sigmoid(randn(B, H, F).astype(np.float64)).astype(np.float32)
+    qw = (1 + 0.1 * randn(H * D)).astype(np.float32)
+    kw = (1 + 0.1 * randn(H * D)).astype(np.float32)
+    dout = randn(B, N, H, D)
+    cos, sin = rope_tables(N, D)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    return {"qkv": f(qkv).to(torch.bfloat16), "beta": f(beta), "decay": f(decay), "qw": f(qw), "kw": f(kw),
+            "cos": f(cos), "sin": f(sin), "dout": f(dout).to(torch.bfloat16), "B": B, "F": F, "S": S, "H": H, "D": D,
+            "k_scale": float(2.0 / np.sqrt(S * D)) if k_scale is None else float(k_scale)}

@@ -91,12 +91,12 @@ def _transforms(qkv, qw, kw, cos, sin, F, S, k_scale, norm_eps):
 
 def phase_a(Kr, Ku, V, beta):
     """Per-frame sums (phase Ā's forward): all [B, H, F, ...]."""
-    Kb = Kr * beta[..., None]
-    P = np.einsum("bhfsd,bhfse->bhfde", Kb, Kr)
-    A = np.einsum("bhfsd,bhfse->bhfde", Kb, V)
-    Kub = Ku * beta[..., None]
-    Pz = np.einsum("bhfsd,bhfse->bhfde", Kub, Ku)
-    Bz = Kub.sum(axis=3)
+    Kb = np.swapaxes(Kr * beta[..., None], -1, -2)
+    P = Kb @ Kr
+    A = Kb @ V
+    Kub = np.swapaxes(Ku * beta[..., None], -1, -2)
+    Pz = Kub @ Ku
+    Bz = Kub.sum(axis=-1)
     return P, A, Pz, Bz
 
 
@@ -128,8 +128,8 @@ def bigdn_fwd(qkv, beta, decay, qw, kw, cos, sin, F, S, k_scale=1.0, norm_eps=1e
     zf, zr = frame_scans(Pz, Bz[..., None], g)
     Mc = Mf + Mr
     zc = (zf + zr)[..., 0]
-    num = np.einsum("bhfsd,bhfde->bhfse", Qr, Mc)
-    den = np.einsum("bhfsd,bhfd->bhfs", Qu, zc)
+    num = Qr @ Mc
+    den = (Qu @ zc[..., None])[..., 0]
     out = num / (den[..., None] + eps)
     if not keep:
         return _bnhd(out)

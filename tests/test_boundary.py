@@ -17,7 +17,7 @@ def B():
 
 
 def test_header_symbols_exported(B):
-    hdr = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    hdr = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("gdr.h", "bigdn.h"))
     declared = set(re.findall(r"^(?:const char \*|int64_t |size_t |int )(\w+)\(", hdr, flags=re.M))
     assert declared == set(B.EXPORTED)
     for name in declared:
@@ -160,3 +160,54 @@ def test_kda_full_validation(B):
     assert _kda_full(B, p, ws_bytes=need - 1) == -3
     for missing in ("q", "k", "v", "g", "beta", "dO", "dq", "dk", "dv", "dg", "db"):
         assert _kda_full(B, p, **{missing: None}) == -1, missing
+
+
+# ---- BiGDN layer (include/bigdn.h)
+
+def _bprob(lib, **kw):
+    d = dict(B=2, F=3, S=100, H=2, D=64, k_scale=0.1, norm_eps=1e-5, eps=1e-6)
+    d.update(kw)
+    return lib.BigdnProblem(d["B"], d["F"], d["S"], d["H"], d["D"], d["k_scale"], d["norm_eps"], d["eps"])
+
+
+def _bigdn_bwd(lib, p, ws_bytes=1 << 40, **null):
+    names = ["qkv", "beta", "decay", "qw", "kw", "cos", "sin", "dout", "dqkv", "dbeta", "ddecay", "dqw", "dkw"]
+    args = [None if n in null else FAKE for n in names]
+    return lib.lib.bigdn_bwd(ctypes.byref(p), *args, FAKE, ws_bytes, None)
+
+
+def _bigdn_fwd(lib, p, ws_bytes=1 << 40, **null):
+    names = ["qkv", "beta", "decay", "qw", "kw", "cos", "sin", "out"]
+    args = [None if n in null else FAKE for n in names]
+    return lib.lib.bigdn_fwd(ctypes.byref(p), *args, FAKE, ws_bytes, None)
+
+
+def test_bigdn_workspace_size(B):
+    p = _bprob(B, B=8, F=11, S=1024, H=16, D=128)
+    fwd, bwd = B.bigdn_workspace_size(p, False), B.bigdn_workspace_size(p, True)
+    NF, DD = 8 * 16 * 11, 128 * 128
+    # forward: rms stats, P (bf16), A, Pz (fp32), both states (bf16) and vectors
+    assert fwd >= 2 * 8 * 11264 * 4 + NF * DD * (2 + 4 + 4 + 2 + 2)
+    assert bwd > fwd
+    assert B.bigdn_workspace_size(_bprob(B, D=96), True) == 0
+    assert B.bigdn_workspace_size(_bprob(B, F=0), True) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(F=0), -1), (dict(S=0), -1), (dict(H=0), -1), (dict(eps=0.0), -1),
+    (dict(norm_eps=-1.0), -1), (dict(k_scale=float("inf")), -1), (dict(D=96), -2), (dict(D=32), -2),
+    (dict(H=33, D=128), -2)])
+def test_bigdn_invalid_problem(B, kw, code):
+    assert _bigdn_bwd(B, _bprob(B, **kw)) == code
+    assert _bigdn_fwd(B, _bprob(B, **kw)) == code
+
+
+def test_bigdn_workspace_and_pointers(B):
+    p = _bprob(B)
+    need = B.bigdn_workspace_size(p, True)
+    assert _bigdn_bwd(B, p, ws_bytes=need - 1) == -3
+    assert _bigdn_fwd(B, p, ws_bytes=B.bigdn_workspace_size(p, False) - 1) == -3
+    for n in ("qkv", "beta", "decay", "qw", "kw", "cos", "sin", "dout", "dqkv", "dbeta", "ddecay", "dqw", "dkw"):
+        assert _bigdn_bwd(B, p, **{n: True}) == -1, n
+    for n in ("qkv", "beta", "decay", "qw", "kw", "cos", "sin", "out"):
+        assert _bigdn_fwd(B, p, **{n: True}) == -1, n
