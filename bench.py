@@ -7,6 +7,11 @@ reverse cumsum and GQA sums) over one batch of synthetic inputs already
 resident in HBM.  Default workload: B=1, T=32768, 16 key / 16 value heads,
 K=V=128, BT=64, bf16 inputs with fp32 gate, dht present.
 
+With --path bigdn a step is one bigdn_bwd call: the BiGDN chunkwise layer
+backward (frame-level bidirectional gated delta rule with its normaliser
+stream, RoPE/ReLU and full-channel RMSNorm, recomputing the per-frame sums and
+both frame scans) at B=8, F=11 frames of S=1024 tokens, H=16, D=128, bf16.
+
 With --path fwd a step is instead the chunked forward: gdr_gate_cumsum on the
 raw gate, then gdr_chunk_fwd (chunk table + WY factors, the forward state
 scan, the output kernel), on the same inputs.  With --path kda a step is one
@@ -193,9 +198,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
-    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd", "kda"],
+    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd", "kda", "bigdn"],
                     help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward; "
-                         "kda: the full KDA backward at B=1 T=2048 H=32 K=V=128 fp16")
+                         "kda: the full KDA backward at B=1 T=2048 H=32 K=V=128 fp16; "
+                         "bigdn: the BiGDN layer backward at B=8 F=11 S=1024 H=16 D=128 bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -208,6 +214,8 @@ def main():
 
     if args.path == "kda":
         return bench_kda(args, torch, binding, profiling, workloads)
+    if args.path == "bigdn":
+        return bench_bigdn(args, torch, binding, profiling, workloads)
     fwd = args.path == "fwd"
     cfg = dict(WORKLOADS[args.workload])
     lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
@@ -357,6 +365,122 @@ def bench_kda(args, torch, binding, profiling, workloads):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path="kda")
     del keep
+    print(json.dumps(res), flush=True)
+
+
+def flop_model_bigdn(B, F, S, H, D):
+    """Products of the page's BiGDN backward per frame (forward recompute not
+    counted): phase C-bar dQ = dO Mc^T and dMc = Q^T dO (2 x 2SD^2); phase A-bar
+    K dP, K dP^T, V dA^T, K dA (4 x 2SD^2) and K dPz, K dPz^T (2 x 2SD^2); the
+    combine's dM Mprev^T and (I - P) Mprev for both directions (4 x 2D^3) and
+    the two gradient scans' (I - P)^T dM (2 x 2D^3):  16 S D^2 + 12 D^3."""
+    return B * H * F * (16 * S * D * D + 12 * D ** 3)
+
+
+def kernel_bytes_bigdn(B, F, S, H, D, nblk):
+    """Algorithmic HBM bytes per launch of each BiGDN backward stage: tensors
+    read once and written once per launch (bf16 activations; fp32 gates, norm
+    weights and rope tables; per-frame D x D intermediates as the kernels store
+    them: P, Mf, Mr, Tf, Tr in bf16, A, Pz, dMc in fp32)."""
+    ntok, NF, C = B * F * S, B * H * F, H * D
+    act = ntok * C * 2                 # one bf16 [B, N, H, D] tensor
+    rope = 2 * F * S * D * 4
+    DDb, DDf, vec = NF * D * D * 2, NF * D * D * 4, NF * D * 4
+    beta = ntok * H * 4
+    return {
+        "stats": 2 * act + 2 * ntok * 4,
+        "phase_a": 2 * act + beta + ntok * 4 + C * 4 + rope + DDb + 2 * DDf + vec,
+        "scans": DDb + 2 * DDf + vec + 2 * DDb + 2 * vec + NF * 4,
+        "phase_c": 2 * act + ntok * 4 + C * 4 + rope + 2 * DDb + 2 * vec + act + DDf + vec,
+        "gscans": DDf + DDb + DDf + vec + 2 * DDb + 2 * vec + NF * 4,
+        "abar": 2 * act + beta + ntok * 4 + C * 4 + rope + DDb + DDf + 2 * DDb + 2 * DDb + 4 * vec + NF * 4
+                + 2 * act + beta + NF * 4,
+        "rms_bwd": 4 * act + 2 * ntok * 4 + 2 * C * 4 + 2 * act + 2 * nblk * 2 * C * 4 + 2 * C * 4,
+    }
+
+
+def cpu_baseline_bigdn(inp, flops_row):
+    """The fp64 oracle (forward recompute + hand-derived backward), unchanged,
+    on batch row 0 of the workload, repeated until at least 10 s have elapsed."""
+    from oracle import bigdn_oracle as BO
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    f = lambda n: inp[n].double().numpy()[:1] if n in ("qkv", "beta", "decay", "dout") else inp[n].double().numpy()  # noqa: E731,E501
+    args = [f(n) for n in ("qkv", "beta", "decay", "qw", "kw", "cos", "sin")]
+    passes, dt = 0, 0.0
+    while dt < 10.0:
+        t0 = time.perf_counter()
+        BO.bigdn_bwd(*args, f("dout"), inp["F"], inp["S"], k_scale=inp["k_scale"])
+        dt += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(passes * flops_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} pass(es) over batch row 0 of {inp['B']} ({dt:.1f} s): fp64 numpy forward recompute "
+                      "+ hand-derived backward, BLAS threads for the per-frame products",
+            "seconds": round(dt, 2)}
+
+
+def bench_bigdn(args, torch, binding, profiling, workloads):
+    """One step = one bigdn_bwd call at B=8, F=11, S=1024, H=16, D=128, bf16."""
+    B, F, S, H, D = 8, 11, 1024, 16, 128
+    inp = workloads.bigdn_inputs(B, F, S, H, D, seed=0)
+    dev = {n: inp[n].cuda() for n in ("qkv", "beta", "decay", "qw", "kw", "cos", "sin", "dout")}
+    prob = binding.bigdn_problem(dev["qkv"], F, S, inp["k_scale"])
+    ws = torch.empty(binding.bigdn_workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    out = {"dqkv": torch.empty_like(dev["qkv"]), "dbeta": torch.empty_like(dev["beta"]),
+           "ddecay": torch.empty_like(dev["decay"]), "dqw": torch.empty_like(dev["qw"]),
+           "dkw": torch.empty_like(dev["kw"])}
+    P = binding._ptr
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args_c = [ctypes.byref(prob), P(dev["qkv"]), P(dev["beta"]), P(dev["decay"]), P(dev["qw"]), P(dev["kw"]),
+              P(dev["cos"]), P(dev["sin"]), P(dev["dout"]), P(out["dqkv"]), P(out["dbeta"]), P(out["ddecay"]),
+              P(out["dqw"]), P(out["dkw"]), P(ws), ws.numel(), sp]
+    nev = 8
+    hip, evs = hip_events(nev * args.steps)
+    evsz = ctypes.sizeof(ctypes.c_void_p)
+
+    def call(i=None):
+        ev = None if i is None else ctypes.byref(evs, nev * i * evsz)
+        rc = binding.lib.bigdn_bwd_events(*args_c, ev)
+        if rc != 0:
+            raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = ["stats", "phase_a", "scans", "phase_c", "gscans", "abar", "rms_bwd"]
+    stage = {k: 0.0 for k in names}
+    for i in range(args.steps):
+        e = [evs[nev * i + j] for j in range(nev)]
+        for j, k in enumerate(names):
+            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
+    Fl = flop_model_bigdn(B, F, S, H, D)
+    nblk = min(1024, (B * F * S + 3) // 4)
+    kb = kernel_bytes_bigdn(B, F, S, H, D, nblk)
+    kn = {"stats": "bigdn_stats_kernel", "phase_a": "bigdn_phase_a_kernel", "scans": "bigdn_scan_kernel",
+          "phase_c": "bigdn_phase_c_kernel", "gscans": "bigdn_scan_kernel", "abar": "bigdn_abar_kernel",
+          "rms_bwd": "bigdn_rms_bwd_kernel"}
+    roof = _roofline(stage, kb, kn, "bigdn_b8_f11_s1024_h16", profiling)
+    roof["call_algorithmic_bytes"] = sum(kb.values())
+    roof["call_hbm_frac"] = round(sum(kb.values()) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    res = {"metric": "BiGDN chunkwise bwd ms/call + eff. TFLOP/s at B=8, F=11, S=1024, H=16, D=128",
+           "value": round(Fl / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded randn / sigmoid, rotary tables, as the page's layer inputs)",
+           "config": {"workload": "bigdn_bwd_B8_F11_S1024_H16_D128_bf16", "B": B, "F": F, "S": S, "H": H, "D": D,
+                      "k_scale": inp["k_scale"], "global_batch": B, "seq_len": F * S, "parallelism": "none",
+                      "flop_model_gflop": round(Fl / 1e9, 2)},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_bigdn(inp, Fl / B)
     print(json.dumps(res), flush=True)
 
 

@@ -84,7 +84,7 @@ __device__ __forceinline__ void transform8(const bf16x8& raw, float r, const flo
 // --------------------------------------------------------------------------
 // Inverse RMS over all C channels of each token, for q and k.  One wave per
 // token.
-__global__ void __launch_bounds__(256) rms_stats_kernel(const bf16* __restrict__ qkv, float* __restrict__ rq,
+__global__ void __launch_bounds__(256) bigdn_stats_kernel(const bf16* __restrict__ qkv, float* __restrict__ rq,
                                                         float* __restrict__ rk, int ntok, int C, float norm_eps) {
     const int l = lane_id();
     const int tok = blockIdx.x * 4 + wave_id();
@@ -121,7 +121,7 @@ struct ACfg {
 };
 
 template <int D>
-__global__ void __launch_bounds__(512) phase_a_kernel(const bf16* __restrict__ qkv, const float* __restrict__ beta,
+__global__ void __launch_bounds__(512) bigdn_phase_a_kernel(const bf16* __restrict__ qkv, const float* __restrict__ beta,
                                                       const float* __restrict__ rk, const float* __restrict__ kw,
                                                       const float* __restrict__ cosT, const float* __restrict__ sinT,
                                                       bf16* __restrict__ Pout, float* __restrict__ Aout,
@@ -273,7 +273,7 @@ struct SCfg {
 };
 
 template <int D>
-__global__ void __launch_bounds__(512) scan_kernel(ScanArgs a) {
+__global__ void __launch_bounds__(512) bigdn_scan_kernel(ScanArgs a) {
     using Cf = SCfg<D>;
     constexpr int LD = Cf::LD, NP = Cf::NP, EPP = D / NP;
     constexpr int TM = D / 64, TN = D / 32;
@@ -421,7 +421,7 @@ struct CCfg {
 };
 
 template <int D, bool BWD>
-__global__ void __launch_bounds__(512) phase_c_kernel(const bf16* __restrict__ qkv, const float* __restrict__ rq,
+__global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restrict__ qkv, const float* __restrict__ rq,
                                                       const float* __restrict__ qw, const float* __restrict__ cosT,
                                                       const float* __restrict__ sinT, const bf16* __restrict__ Mf,
                                                       const bf16* __restrict__ Mr, const float* __restrict__ zf,
@@ -638,7 +638,7 @@ struct BCfg {
 };
 
 template <int D>
-__global__ void __launch_bounds__(512) abar_kernel(const bf16* __restrict__ qkv, const float* __restrict__ beta,
+__global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict__ qkv, const float* __restrict__ beta,
                                                    const float* __restrict__ decay, const float* __restrict__ rk,
                                                    const float* __restrict__ kw, const float* __restrict__ cosT,
                                                    const float* __restrict__ sinT, const bf16* __restrict__ P,
@@ -914,7 +914,7 @@ __global__ void __launch_bounds__(512) abar_kernel(const bf16* __restrict__ qkv,
 // of dqkv (which hold dQn and dKn):  dx = r w dy - r^3/C x sum(w dy x);
 // per-block partial sums of dy x r for the norm weights.  One wave per token.
 template <int NCH>
-__global__ void __launch_bounds__(256) rms_bwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ dqkv,
+__global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ dqkv,
                                                       const float* __restrict__ rq, const float* __restrict__ rk,
                                                       const float* __restrict__ qw, const float* __restrict__ kw,
                                                       float* __restrict__ wpart, int ntok, int C) {
@@ -988,7 +988,7 @@ __global__ void __launch_bounds__(256) rms_bwd_kernel(const bf16* __restrict__ q
         wpart[(size_t)blockIdx.x * 2 * C + i] = red[i] + red[2 * C + i] + red[4 * C + i] + red[6 * C + i];
 }
 
-__global__ void __launch_bounds__(256) wsum_kernel(const float* __restrict__ wpart, float* __restrict__ dqw,
+__global__ void __launch_bounds__(256) bigdn_wsum_kernel(const float* __restrict__ wpart, float* __restrict__ dqw,
                                                    float* __restrict__ dkw, int nblk, int C) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= 2 * C) return;
@@ -1049,7 +1049,7 @@ static hipError_t set_smem(K kern, size_t bytes) {
 
 template <int D>
 static hipError_t run_phase_a(const Dims& d, const Inputs& in, const Ws& w, hipStream_t s) {
-    auto k = phase_a_kernel<D>;
+    auto k = bigdn_phase_a_kernel<D>;
     if (set_smem(k, ACfg<D>::smem) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(d.B * d.H * d.F), dim3(512), ACfg<D>::smem, s, (const bf16*)in.qkv, in.beta, w.rk,
                        in.kw, in.cos, in.sin, (bf16*)w.P, w.A, w.Pz, w.Bz, d.F, d.S, d.H, d.k_scale);
@@ -1058,7 +1058,7 @@ static hipError_t run_phase_a(const Dims& d, const Inputs& in, const Ws& w, hipS
 
 template <int D>
 static hipError_t run_scan(const Dims& d, const ScanArgs& a, hipStream_t s) {
-    auto k = scan_kernel<D>;
+    auto k = bigdn_scan_kernel<D>;
     if (set_smem(k, SCfg<D>::smem) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(2 * d.B * d.H), dim3(512), SCfg<D>::smem, s, a);
     return hipGetLastError();
@@ -1066,7 +1066,7 @@ static hipError_t run_scan(const Dims& d, const ScanArgs& a, hipStream_t s) {
 
 template <int D, bool BWD>
 static hipError_t run_phase_c(const Dims& d, const Inputs& in, const Outputs& out, const Ws& w, hipStream_t s) {
-    auto k = phase_c_kernel<D, BWD>;
+    auto k = bigdn_phase_c_kernel<D, BWD>;
     if (set_smem(k, CCfg<D>::smem) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(d.B * d.H * d.F), dim3(512), CCfg<D>::smem, s, (const bf16*)in.qkv, w.rq, in.qw,
                        in.cos, in.sin, (const bf16*)w.Mf, (const bf16*)w.Mr, w.zf, w.zr, (const bf16*)in.dout,
@@ -1076,7 +1076,7 @@ static hipError_t run_phase_c(const Dims& d, const Inputs& in, const Outputs& ou
 
 template <int D>
 static hipError_t run_abar(const Dims& d, const Inputs& in, const Outputs& out, const Ws& w, hipStream_t s) {
-    auto k = abar_kernel<D>;
+    auto k = bigdn_abar_kernel<D>;
     if (set_smem(k, BCfg<D>::smem) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(d.B * d.H * d.F), dim3(512), BCfg<D>::smem, s, (const bf16*)in.qkv, in.beta, in.decay,
                        w.rk, in.kw, in.cos, in.sin, (const bf16*)w.P, w.Pz, (const bf16*)w.Mf, (const bf16*)w.Mr,
@@ -1089,13 +1089,13 @@ template <int NCH>
 static hipError_t run_rms_bwd(const Dims& d, const Inputs& in, const Outputs& out, const Ws& w, hipStream_t s) {
     const int C = d.H * d.D, ntok = d.B * d.F * d.S;
     const size_t sm = (size_t)4 * 2 * C * 4;
-    auto k = rms_bwd_kernel<NCH>;
+    auto k = bigdn_rms_bwd_kernel<NCH>;
     if (set_smem(k, sm) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(w.nblk), dim3(256), sm, s, (const bf16*)in.qkv, (bf16*)out.dqkv, w.rq, w.rk, in.qw,
                        in.kw, w.wpart, ntok, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wsum_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, w.wpart, out.dqw, out.dkw, w.nblk, C);
+    hipLaunchKernelGGL(bigdn_wsum_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, w.wpart, out.dqw, out.dkw, w.nblk, C);
     return hipGetLastError();
 }
 
@@ -1112,7 +1112,7 @@ template <int D>
 static hipError_t run_states(const Dims& d, const Inputs& in, const Ws& w, hipStream_t s, hipEvent_t* ev) {
     const int ntok = d.B * d.F * d.S, C = d.H * d.D;
     BIGDN_TRY(mark(ev, 0, s));
-    hipLaunchKernelGGL(rms_stats_kernel, dim3((ntok + 3) / 4), dim3(256), 0, s, (const bf16*)in.qkv, w.rq, w.rk, ntok,
+    hipLaunchKernelGGL(bigdn_stats_kernel, dim3((ntok + 3) / 4), dim3(256), 0, s, (const bf16*)in.qkv, w.rq, w.rk, ntok,
                        C, d.norm_eps);
     BIGDN_TRY(hipGetLastError());
     BIGDN_TRY(mark(ev, 1, s));

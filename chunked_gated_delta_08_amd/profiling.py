@@ -44,6 +44,10 @@ KERNEL_SOURCES = {
     "kda_scan_kernel": [_CS + "kda_full.hip"] + _COMMON,
     "kda_intra_kernel": [_CS + "kda_full.hip"] + _COMMON,
 }
+_BIGDN = [_CS + "bigdn.hip", _CS + "bigdn_launch.hpp"] + _COMMON
+for _k in ("bigdn_stats_kernel", "bigdn_phase_a_kernel", "bigdn_scan_kernel", "bigdn_phase_c_kernel",
+           "bigdn_abar_kernel", "bigdn_rms_bwd_kernel", "bigdn_wsum_kernel"):
+    KERNEL_SOURCES[_k] = _BIGDN
 
 
 def source_digest(files):
