@@ -137,7 +137,10 @@ __global__ void __launch_bounds__(512) bigdn_phase_a_kernel(const bf16* __restri
     bf16* sUb = sV + ST * LD;
     bf16* sU = sUb + ST * LD;
 
-    const int fr = blockIdx.x, bh = fr / F, f = fr - bh * F, b = bh / H, h = bh - b * H;
+    // frame-major order: the workgroups resident at a time share a few frames,
+    // whose rope-table rows then stay in L2
+    const int BH = (int)gridDim.x / F, f = (int)blockIdx.x / BH, bh = (int)blockIdx.x - f * BH;
+    const int fr = bh * F + f, b = bh / H, h = bh - b * H;
     const int N = F * S, C = H * D;
     const int t = threadIdx.x, w = wave_id(), c = t % CPR, row0 = t / CPR;
     float wk[8];
@@ -443,7 +446,10 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
     float* sRed = (float*)(smem + Cf::oRed);
     float* sZr = (float*)(smem + Cf::oZr);
 
-    const int fr = blockIdx.x, bh = fr / F, f = fr - bh * F, b = bh / H, h = bh - b * H;
+    // frame-major order: the workgroups resident at a time share a few frames,
+    // whose rope-table rows then stay in L2
+    const int BH = (int)gridDim.x / F, f = (int)blockIdx.x / BH, bh = (int)blockIdx.x - f * BH;
+    const int fr = bh * F + f, b = bh / H, h = bh - b * H;
     const int N = F * S, C = H * D;
     const int t = threadIdx.x, w = wave_id(), c = t % CPR, row0 = t / CPR;
     const size_t DD = (size_t)D * D;
@@ -470,7 +476,31 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
     f32x4 accM[TMd][TNd];
     if constexpr (BWD) zero_acc(accM);
 
+    // the next tile's q and dout chunks are loaded into registers while the
+    // current tile is computed
+    bf16x8 pQ[NPT], pD[NPT];
+    float pR[NPT];
+    auto fetch = [&](int s0n) {
+#pragma unroll
+        for (int p = 0; p < NPT; p++) {
+            const int s = s0n + row0 + p * RSTEP;
+            if (s < S) {
+                const size_t tok = (size_t)b * N + (size_t)f * S + s;
+                pQ[p] = *(const bf16x8*)(qkv + tok * 3 * C + h * D + 8 * c);
+                pR[p] = rq[tok];
+                if constexpr (BWD) pD[p] = *(const bf16x8*)(dout + (tok * H + h) * D + 8 * c);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    pQ[p][i] = (bf16)0.f;
+                    if constexpr (BWD) pD[p][i] = (bf16)0.f;
+                }
+                pR[p] = 0.f;
+            }
+        }
+    };
     const int ntile = (S + ST - 1) / ST;
+    fetch(0);
     for (int it = 0; it < ntile; ++it) {
         const int s0 = it * ST;
         float u[NPT][8], cs[NPT][8], sn[NPT][8], inv[NPT];
@@ -481,23 +511,18 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
         for (int p = 0; p < NPT; p++) {
             const int row = row0 + p * RSTEP, s = s0 + row;
             ok[p] = s < S;
-            const size_t tok = (size_t)b * N + (size_t)f * S + (ok[p] ? s : 0);
-            bf16x8 raw;
-            float r = 0.f;
+            const bf16x8 raw = pQ[p];
+            const float r = pR[p];
+            if constexpr (BWD) rD[p] = pD[p];
             if (ok[p]) {
-                raw = *(const bf16x8*)(qkv + tok * 3 * C + h * D + 8 * c);
                 const size_t ro = ((size_t)f * S + s) * D + 8 * c;
                 ld8(cosT + ro, cs[p]);
                 ld8(sinT + ro, sn[p]);
-                r = rq[tok];
-                if constexpr (BWD) rD[p] = *(const bf16x8*)(dout + (tok * H + h) * D + 8 * c);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    raw[i] = (bf16)0.f;
                     cs[p][i] = 0.f;
                     sn[p][i] = 0.f;
-                    if constexpr (BWD) rD[p][i] = (bf16)0.f;
                 }
             }
             float y[8];
@@ -521,6 +546,7 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
                 if (c == 0) sRed[row] = inv[p];
             }
         }
+        if (it + 1 < ntile) fetch((it + 1) * ST);
         lds_barrier();
         f32x4 accN[1][TN];
         zero_acc(accN);
@@ -676,7 +702,10 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
     float* sBeta = (float*)(smem + Cf::oBeta);
     float* sG = (float*)(smem + Cf::oG);
 
-    const int fr = blockIdx.x, bh = fr / F, f = fr - bh * F, b = bh / H, h = bh - b * H;
+    // frame-major order: the workgroups resident at a time share a few frames,
+    // whose rope-table rows then stay in L2
+    const int BH = (int)gridDim.x / F, f = (int)blockIdx.x / BH, bh = (int)blockIdx.x - f * BH;
+    const int fr = bh * F + f, b = bh / H, h = bh - b * H;
     const int N = F * S, C = H * D;
     const int t = threadIdx.x, w = wave_id(), c = t % CPR, row0 = t / CPR;
     const size_t DD = (size_t)D * D, fo = (size_t)fr * DD;
@@ -797,6 +826,31 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
     const float* vTzr = sTzr + 8 * c;
     const float* vZr = sZr + 8 * c;
     const float* vDBz = sDBz + 8 * c;
+    bf16x8 pK[NPT], pV[NPT];
+    float pR[NPT], pB[NPT];
+    auto fetch = [&](int s0n) {
+#pragma unroll
+        for (int p = 0; p < NPT; p++) {
+            const int s = s0n + row0 + p * RSTEP;
+            if (s < S) {
+                const size_t tok = (size_t)b * N + (size_t)f * S + s;
+                const bf16* base = qkv + (tok * 3 + 1) * C + h * D + 8 * c;
+                pK[p] = *(const bf16x8*)base;
+                pV[p] = *(const bf16x8*)(base + C);
+                pR[p] = rk[tok];
+                pB[p] = beta[(size_t)fr * S + s];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    pK[p][i] = (bf16)0.f;
+                    pV[p][i] = (bf16)0.f;
+                }
+                pR[p] = 0.f;
+                pB[p] = 0.f;
+            }
+        }
+    };
+    fetch(0);
     for (int it = 0; it < ntile; ++it) {
         const int s0 = it * ST;
         // per row: the four Ku dot products of the rank-4 normaliser term and
@@ -808,23 +862,16 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
         for (int p = 0; p < NPT; p++) {
             const int row = row0 + p * RSTEP, s = s0 + row;
             ok[p] = s < S;
-            bf16x8 raw, rv;
-            float r = 0.f, bb = 0.f, cs[8], sn[8];
+            const bf16x8 raw = pK[p], rv = pV[p];
+            const float r = pR[p], bb = pB[p];
+            float cs[8], sn[8];
             if (ok[p]) {
-                const size_t tok = (size_t)b * N + (size_t)f * S + s;
-                const bf16* base = qkv + (tok * 3 + 1) * C + h * D + 8 * c;
-                raw = *(const bf16x8*)base;
-                rv = *(const bf16x8*)(base + C);
                 const size_t ro = ((size_t)f * S + s) * D + 8 * c;
                 ld8(cosT + ro, cs);
                 ld8(sinT + ro, sn);
-                r = rk[tok];
-                bb = beta[(size_t)fr * S + s];
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    raw[i] = (bf16)0.f;
-                    rv[i] = (bf16)0.f;
                     cs[i] = 0.f;
                     sn[i] = 0.f;
                 }
@@ -854,6 +901,7 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
             *(bf16x8*)(sV + row * LD + 8 * c) = rv;
             if (c == 0) sBeta[row] = bb;
         }
+        if (it + 1 < ntile) fetch((it + 1) * ST);
         lds_barrier();
         f32x4 acc1[1][TN], acc2[1][TN];
         zero_acc(acc1);
@@ -912,64 +960,79 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
 // --------------------------------------------------------------------------
 // RMSNorm VJP over all C channels of a token, in place on the q and k slots
 // of dqkv (which hold dQn and dKn):  dx = r w dy - r^3/C x sum(w dy x);
-// per-block partial sums of dy x r for the norm weights.  One wave per token.
+// per-block partial sums of dy x r for the norm weights.  One wave per
+// (token, slot).
 template <int NCH>
 __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ dqkv,
-                                                      const float* __restrict__ rq, const float* __restrict__ rk,
-                                                      const float* __restrict__ qw, const float* __restrict__ kw,
-                                                      float* __restrict__ wpart, int ntok, int C) {
+                                                            const float* __restrict__ rq, const float* __restrict__ rk,
+                                                            const float* __restrict__ qw, const float* __restrict__ kw,
+                                                            float* __restrict__ wpart, int ntok, int C) {
     extern __shared__ __align__(16) unsigned char smem[];
-    float* red = (float*)smem;  // [4][2C]
+    float* red = (float*)smem;  // [4][C]
     const int l = lane_id(), w = wave_id(), nc8 = C / 8;
-    float aq[NCH][8], ak[NCH][8], wq[NCH][8], wk[NCH][8];
+    // work unit u = 2 * token + slot (0: q, 1: k); the unit stride is a multiple
+    // of 4, so each wave keeps one slot and accumulates one weight gradient
+    const int sl = w & 1;
+    const float* wt = sl ? kw : qw;
+    const float* rr = sl ? rk : rq;
+    float acc[NCH][8];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ch++) {
-        const int c8 = l + 64 * ch;
+    for (int ch = 0; ch < NCH; ch++)
 #pragma unroll
-        for (int i = 0; i < 8; i++) aq[ch][i] = ak[ch][i] = 0.f;
-        if (c8 < nc8) {
-            ld8(qw + 8 * c8, wq[ch]);
-            ld8(kw + 8 * c8, wk[ch]);
-        }
-    }
-    for (int tok = blockIdx.x * 4 + w; tok < ntok; tok += gridDim.x * 4) {
+        for (int i = 0; i < 8; i++) acc[ch][i] = 0.f;
+    const long nunit = 2L * ntok, ustep = (long)gridDim.x * 4;
+    // the next unit's rows are loaded before the current one is reduced
+    bf16x8 nx[NCH], ng[NCH];
+    auto fetch = [&](long u) {
+        const long tok = u >> 1;
+        const bf16* x = qkv + (size_t)tok * 3 * C + (size_t)sl * C;
+        const bf16* dx = dqkv + (size_t)tok * 3 * C + (size_t)sl * C;
 #pragma unroll
-        for (int sl = 0; sl < 2; sl++) {
-            const bf16* x = qkv + (size_t)tok * 3 * C + (size_t)sl * C;
-            bf16* dx = dqkv + (size_t)tok * 3 * C + (size_t)sl * C;
-            const float r = sl == 0 ? rq[tok] : rk[tok];
-            float xv[NCH][8], dy[NCH][8];
-            float corr = 0.f;
-#pragma unroll
-            for (int ch = 0; ch < NCH; ch++) {
-                const int c8 = l + 64 * ch;
-                if (c8 < nc8) {
-                    const bf16x8 a = *(const bf16x8*)(x + 8 * c8);
-                    const bf16x8 d = *(const bf16x8*)(dx + 8 * c8);
-#pragma unroll
-                    for (int i = 0; i < 8; i++) {
-                        xv[ch][i] = (float)a[i];
-                        dy[ch][i] = (float)d[i];
-                        corr += (sl == 0 ? wq[ch][i] : wk[ch][i]) * dy[ch][i] * xv[ch][i];
-                    }
-                }
+        for (int ch = 0; ch < NCH; ch++) {
+            const int c8 = l + 64 * ch;
+            if (c8 < nc8) {
+                nx[ch] = *(const bf16x8*)(x + 8 * c8);
+                ng[ch] = *(const bf16x8*)(dx + 8 * c8);
             }
-            corr = wave_sum(corr);
-            const float k3 = r * r * r / (float)C * corr;
+        }
+    };
+    long u = (long)blockIdx.x * 4 + w;
+    if (u < nunit) fetch(u);
+    for (; u < nunit; u += ustep) {
+        const long tok = u >> 1;
+        bf16* dx = dqkv + (size_t)tok * 3 * C + (size_t)sl * C;
+        bf16x8 xr[NCH], gr[NCH];
 #pragma unroll
-            for (int ch = 0; ch < NCH; ch++) {
-                const int c8 = l + 64 * ch;
-                if (c8 < nc8) {
-                    bf16x8 o;
+        for (int ch = 0; ch < NCH; ch++) xr[ch] = nx[ch], gr[ch] = ng[ch];
+        if (u + ustep < nunit) fetch(u + ustep);
+        const float r = rr[tok];
+        float corr = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 8; i++) {
-                        const float ww = sl == 0 ? wq[ch][i] : wk[ch][i];
-                        o[i] = (bf16)(r * ww * dy[ch][i] - k3 * xv[ch][i]);
-                        if (sl == 0) aq[ch][i] += dy[ch][i] * xv[ch][i] * r;
-                        else ak[ch][i] += dy[ch][i] * xv[ch][i] * r;
-                    }
-                    *(bf16x8*)(dx + 8 * c8) = o;
+        for (int ch = 0; ch < NCH; ch++) {
+            const int c8 = l + 64 * ch;
+            if (c8 < nc8) {
+                float w8[8];
+                ld8(wt + 8 * c8, w8);
+#pragma unroll
+                for (int i = 0; i < 8; i++) corr += w8[i] * (float)gr[ch][i] * (float)xr[ch][i];
+            }
+        }
+        corr = wave_sum(corr);
+        const float k3 = r * r * r / (float)C * corr;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ch++) {
+            const int c8 = l + 64 * ch;
+            if (c8 < nc8) {
+                float w8[8];
+                ld8(wt + 8 * c8, w8);
+                bf16x8 o;
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const float xa = (float)xr[ch][i], ga = (float)gr[ch][i];
+                    o[i] = (bf16)(r * w8[i] * ga - k3 * xa);
+                    acc[ch][i] += ga * xa * r;
                 }
+                *(bf16x8*)(dx + 8 * c8) = o;
             }
         }
     }
@@ -978,24 +1041,36 @@ __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restri
         const int c8 = l + 64 * ch;
         if (c8 < nc8)
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                red[w * 2 * C + 8 * c8 + i] = aq[ch][i];
-                red[w * 2 * C + C + 8 * c8 + i] = ak[ch][i];
-            }
+            for (int i = 0; i < 8; i++) red[w * C + 8 * c8 + i] = acc[ch][i];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 2 * C; i += 256)
-        wpart[(size_t)blockIdx.x * 2 * C + i] = red[i] + red[2 * C + i] + red[4 * C + i] + red[6 * C + i];
+    // waves 0, 2 hold q partials, waves 1, 3 k partials
+    for (int i = threadIdx.x; i < 2 * C; i += 256) {
+        const int slot = i / C, c = i - slot * C;
+        wpart[(size_t)blockIdx.x * 2 * C + i] = red[slot * C + c] + red[(2 + slot) * C + c];
+    }
 }
 
+// Sum of the per-block norm-weight partials: 64 channels per workgroup, the
+// partial rows split over four thread rows (loads unrolled eight deep), then
+// added in a fixed order through LDS.
 __global__ void __launch_bounds__(256) bigdn_wsum_kernel(const float* __restrict__ wpart, float* __restrict__ dqw,
-                                                   float* __restrict__ dkw, int nblk, int C) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= 2 * C) return;
+                                                         float* __restrict__ dkw, int nblk, int C) {
+    __shared__ float part[4][64];
+    const int t = threadIdx.x, cl = t & 63, rg = t >> 6;
+    const int i = blockIdx.x * 64 + cl;
     float s = 0.f;
-    for (int k = 0; k < nblk; k++) s += wpart[(size_t)k * 2 * C + i];
-    if (i < C) dqw[i] = s;
-    else dkw[i - C] = s;
+    if (i < 2 * C) {
+#pragma unroll 8
+        for (int k = rg; k < nblk; k += 4) s += wpart[(size_t)k * 2 * C + i];
+    }
+    part[rg][cl] = s;
+    __syncthreads();
+    if (rg == 0 && i < 2 * C) {
+        const float v = part[0][cl] + part[1][cl] + part[2][cl] + part[3][cl];
+        if (i < C) dqw[i] = v;
+        else dkw[i - C] = v;
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -1088,14 +1163,14 @@ static hipError_t run_abar(const Dims& d, const Inputs& in, const Outputs& out, 
 template <int NCH>
 static hipError_t run_rms_bwd(const Dims& d, const Inputs& in, const Outputs& out, const Ws& w, hipStream_t s) {
     const int C = d.H * d.D, ntok = d.B * d.F * d.S;
-    const size_t sm = (size_t)4 * 2 * C * 4;
+    const size_t sm = (size_t)4 * C * 4;
     auto k = bigdn_rms_bwd_kernel<NCH>;
     if (set_smem(k, sm) != hipSuccess) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k, dim3(w.nblk), dim3(256), sm, s, (const bf16*)in.qkv, (bf16*)out.dqkv, w.rq, w.rk, in.qw,
                        in.kw, w.wpart, ntok, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bigdn_wsum_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, w.wpart, out.dqw, out.dkw, w.nblk, C);
+    hipLaunchKernelGGL(bigdn_wsum_kernel, dim3((2 * C + 63) / 64), dim3(256), 0, s, w.wpart, out.dqw, out.dkw, w.nblk, C);
     return hipGetLastError();
 }
 
