@@ -38,7 +38,8 @@ struct Problem {
 
 // Workspace carve-up (byte offsets from the workspace base).  The segment
 // state buffers (hloc, dhloc, P, hstart, dhin: [NS][HV][K][V] fp32 each, in
-// the fp32 fragment order below) are empty when maxS == 1.
+// the fp32 fragment order below; P holds its values in the 16-bit operand
+// type, in the first half of each block) are empty when maxS == 1.
 struct WsPlan {
     size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
     size_t hloc, dhloc, P, hstart, dhin, gsum, total;

@@ -161,7 +161,10 @@ __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long uni
 }
 
 // Initial / final state forms of one scan job.
-enum StateForm { ST_NONE = 0, ST_ZERO = 0, ST_IDENT = 1, ST_NAT = 2, ST_FRAG = 3 };
+// ST_FRAG16: the fragment order with the values in the 16-bit operand type S
+// (four per lane and tile, 8 bytes), for the transfer matrices, which only
+// ever enter an MFMA as 16-bit operands.
+enum StateForm { ST_NONE = 0, ST_ZERO = 0, ST_IDENT = 1, ST_NAT = 2, ST_FRAG = 3, ST_FRAG16 = 4 };
 
 // One scan job: a run of chunks of one sequence and value head.
 struct ScanJob {
@@ -169,7 +172,7 @@ struct ScanJob {
     int c0, nc, lc0;    // first chunk (global index), chunk count, first chunk's index in the sequence
     int init_form;      // ST_ZERO, ST_IDENT (transfer matrix), ST_NAT ([K][V] fp32), ST_FRAG (fp32 fragment order)
     const float* init;  // K x V block of the initial state
-    int out_form;       // ST_NONE, ST_NAT or ST_FRAG
+    int out_form;       // ST_NONE, ST_NAT, ST_FRAG or ST_FRAG16
     float* out;         // K x V block of the final state
 };
 
@@ -497,6 +500,20 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
     }
 
     // final state
+    if constexpr (sizeof(S) == 2) {
+        if (jb.out_form == ST_FRAG16) {
+            typedef S s4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int t = 0; t < KT; t++) {
+                    s4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) x[e] = (S)St[nb][t][e];
+                    *(s4*)((S*)jb.out + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4) = x;
+                }
+        }
+    }
     if (jb.out_form == ST_FRAG) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
@@ -619,6 +636,7 @@ seg_kernel(ScanArgs a, int NS, int HV) {
     } else {
         if (v.S == 1) return;
         jb.init_form = ST_IDENT;
+        jb.out_form = ST_FRAG16;
         jb.out = a.P + sblk;
         scan_body<E, S, KD, VD, false, false, true>(a, jb, HV, smem);
     }
@@ -628,85 +646,80 @@ seg_kernel(ScanArgs a, int NS, int HV) {
 //   forward  h_start[s+1] = P_s h_start[s] + hloc_s       (h_start[0] = h0)
 //   reverse  dh_in[s-1]   = P_sᵀ dh_in[s] + dhloc_s       (dh_in[S-1] = dht)
 // writing every boundary state except the two sequence ends (which the scans
-// read from h0 / dht).  The state is kept in fp32 accumulators as in the
-// scans; P_s is staged in LDS transposed (PT[v][k] = P[k][v], operand type S)
-// and the next segment's P and hloc are prefetched into registers while the
-// current product runs.  Grid: forward jobs then reverse jobs, N*HV each.
+// read from h0 / dht).  The state columns evolve independently, so each
+// (sequence, value head, direction) job is split by columns over VD/64
+// workgroups of four waves, one 16-column block per wave, the state in fp32
+// accumulators as in the scans.  P_s (16-bit, fragment order, written by the
+// local scans) is staged in LDS transposed (PT[v][k] = P[k][v]); the P and
+// hloc blocks of the next two segments are in flight in registers while the
+// current product runs.  Grid: forward jobs then reverse jobs, N*HV*VD/64 each.
 template <class S, int KD, int VD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 combine_kernel(ScanArgs a, int nseq, int HV) {
     static_assert(KD == VD, "the transfer matrix multiplies the state from the left");
-    constexpr int KT = KD / 16, NB = VD / 64, CW = VD / 4, LK = KD + spad<S>();
-    constexpr int NP = KD * KD / (4 * 256);   // float4 chunks of P per thread
+    static_assert(sizeof(S) == 2, "transfer matrices are 16-bit");
+    constexpr int KT = KD / 16, VS = VD / 64, LK = KD + spad<S>();
+    constexpr int NP = KD * KD / (4 * 256);   // 4-element groups of P per thread
+    typedef S s4 __attribute__((ext_vector_type(4)));
     extern __shared__ __align__(16) unsigned char smem[];
     S* sPT = (S*)smem;
     using frag = typename Mma<S>::frag;
-    const int per = nseq * HV;
+    const int per = nseq * HV * VS;
     const bool rev = (int)blockIdx.x >= per;
     const int b = rev ? (int)blockIdx.x - per : (int)blockIdx.x;
-    const int n = b / HV, hv = b % HV;
+    const int vs = b % VS, n = b / VS / HV, hv = b / VS % HV;
     const int s0 = a.seq_seg0[n], S_n = a.seq_seg0[n + 1] - s0;
     if (S_n < 2 || (rev ? !a.do_rev : !a.do_fwd)) return;
     const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-    const int col0 = CW * w + r;
+    const int cb = 4 * vs + w;           // this wave's 16-column block
+    const int col = 16 * cb + r;
     const long KV = (long)KD * VD;
     auto blk = [&](float* base, int j) { return base + ((long)j * HV + hv) * KV; };
 
-    f32x4 St[NB][KT];
+    f32x4 St[KT];
     const float* init = rev ? a.dht : a.h0;
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++)
+    for (int t = 0; t < KT; t++)
 #pragma unroll
-        for (int t = 0; t < KT; t++)
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                St[nb][t][e] = init ? init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col0 + 16 * nb] : 0.f;
+        for (int e = 0; e < 4; e++)
+            St[t][e] = init ? init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col] : 0.f;
 
     // step q uses segment j(q): forward j = s0 + q (q = 0 .. S_n-2), reverse j = s0 + S_n-1-q
     const int nsteps = S_n - 1;
     auto seg_of = [&](int q) { return rev ? s0 + S_n - 1 - q : s0 + q; };
-    f32x4 pr[NP], hl[NB][KT];
-    auto prefetch = [&](int q) {
+    struct Stg {
+        s4 p[NP];
+        f32x4 h[KT];
+    };
+    auto prefetch = [&](Stg& x, int q) {
         const int j = seg_of(q);
-        const float* P = blk(a.P, j);
+        const S* P = (const S*)blk(a.P, j);
         const float* H = blk(rev ? a.dhloc : a.hloc, j);
 #pragma unroll
-        for (int i = 0; i < NP; i++) pr[i] = *(const f32x4*)(P + (threadIdx.x + 256 * i) * 4);
+        for (int i = 0; i < NP; i++) x.p[i] = *(const s4*)(P + (threadIdx.x + 256 * i) * 4);
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-            for (int t = 0; t < KT; t++) hl[nb][t] = *(const f32x4*)(H + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4);
+        for (int t = 0; t < KT; t++) x.h[t] = *(const f32x4*)(H + ((cb * KT + t) * 64 + l) * 4);
     };
-    prefetch(0);
-    for (int q = 0; q < nsteps; q++) {
+    auto step = [&](int q, const Stg& x) {
         lds_barrier();   // the previous product has read sPT
 #pragma unroll
-        for (int i = 0; i < NP; i++) {   // fragment-order tile (cb, tt), lane (g', r'): P[16tt+4g'+e][16cb+r']
+        for (int i = 0; i < NP; i++) {   // fragment-order tile (cbp, tt), lane (g', r'): P[16tt+4g'+e][16cbp+r']
             const int c = threadIdx.x + 256 * i, tile = c >> 6, ln = c & 63;
-            const int cb = tile / KT, tt = tile % KT;
-            typedef S s4 __attribute__((ext_vector_type(4)));
-            s4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; e++) v4[e] = (S)pr[i][e];
-            *(s4*)(sPT + (16 * cb + (ln & 15)) * LK + 16 * tt + 4 * (ln >> 4)) = v4;
+            const int cbp = tile / KT, tt = tile % KT;
+            *(s4*)(sPT + (16 * cbp + (ln & 15)) * LK + 16 * tt + 4 * (ln >> 4)) = x.p[i];
         }
-        f32x4 X[NB][KT];
+        f32x4 X[KT];
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-            for (int t = 0; t < KT; t++) X[nb][t] = hl[nb][t];
+        for (int t = 0; t < KT; t++) X[t] = x.h[t];
         lds_barrier();
-        if (q + 1 < nsteps) prefetch(q + 1);
-        frag Bs[NB][KD / 32];
+        frag Bs[KD / 32];
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
+        for (int s = 0; s < KD / 32; s++)
 #pragma unroll
-            for (int s = 0; s < KD / 32; s++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    Bs[nb][s][e] = (S)St[nb][2 * s][e];
-                    Bs[nb][s][4 + e] = (S)St[nb][2 * s + 1][e];
-                }
+            for (int e = 0; e < 4; e++) {
+                Bs[s][e] = (S)St[2 * s][e];
+                Bs[s][4 + e] = (S)St[2 * s + 1][e];
+            }
 #pragma unroll
         for (int t = 0; t < KT; t++)
 #pragma unroll
@@ -721,19 +734,26 @@ combine_kernel(ScanArgs a, int nseq, int HV) {
                     hi = ld_trans4<S>(sPT, LK, 16 * t, 32 * s + 16 + 4 * g);
                 }
                 i16x8 c8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const frag A = __builtin_bit_cast(frag, c8);
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) X[nb][t] = Mma<S>::run(A, Bs[nb][s], X[nb][t]);
+                X[t] = Mma<S>::run(__builtin_bit_cast(frag, c8), Bs[s], X[t]);
             }
         const int jd = rev ? seg_of(q) - 1 : seg_of(q) + 1;   // the segment whose boundary state this is
         float* out = blk(rev ? a.dhin : a.hstart, jd);
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-            for (int t = 0; t < KT; t++) {
-                St[nb][t] = X[nb][t];
-                *(f32x4*)(out + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4) = X[nb][t];
-            }
+        for (int t = 0; t < KT; t++) {
+            St[t] = X[t];
+            *(f32x4*)(out + ((cb * KT + t) * 64 + l) * 4) = X[t];
+        }
+    };
+    Stg x0, x1;
+    prefetch(x0, 0);
+    if (nsteps > 1) prefetch(x1, 1);
+    for (int q = 0; q < nsteps; q += 2) {
+        step(q, x0);
+        if (q + 2 < nsteps) prefetch(x0, q + 2);
+        if (q + 1 < nsteps) {
+            step(q + 1, x1);
+            if (q + 3 < nsteps) prefetch(x1, q + 3);
+        }
     }
 }
 
@@ -761,7 +781,8 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             constexpr int csm = KD * (KD + spad<S>()) * (int)sizeof(S);
-            hipLaunchKernelGGL((combine_kernel<S, KD, VD>), dim3(2 * nseq * p.HV), dim3(256), csm, s, a, nseq, p.HV);
+            hipLaunchKernelGGL((combine_kernel<S, KD, VD>), dim3(2 * nseq * p.HV * (VD / 64)), dim3(256), csm, s, a,
+                               nseq, p.HV);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else {
             return hipErrorInvalidValue;   // fp32 problems are planned without segments
