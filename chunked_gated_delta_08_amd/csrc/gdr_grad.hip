@@ -284,20 +284,25 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
     const E* dhT = (const E*)a.dhT;
     const E* beta = (const E*)a.beta;
 
-    {
-        RowsReg<E, KD, LK> rq, rk;
-        rq.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-        rk.load(k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-        rq.store(sQ);
-        rk.store(sK);
-    }
-
     f32x4 dq_tot[2][TNK], dk_tot[2][TNK];   // this head's dq, dk (then the group sums)
 
     {
         const int hv = GRP ? hk * G + hi : hk;
         const long unit = (long)ci * HV + hv;
-        // this head's A and first value slice: loads in flight during Pm
+        // Every load of the unit's start is issued before the first wait: the
+        // gate and β (needed first), Q and K (the first product), then this
+        // head's A and first value slice (in flight during Pm).  The waits
+        // before the first LDS stores then cover only the first two groups.
+        // (every wave loads row threadIdx.x % 64, unconditionally, so no wait
+        // is placed at a branch join)
+        const int rg = min((int)threadIdx.x & (C - 1), Cn - 1);
+        const float gg = a.gcum[(t0 + rg) * HV + hv];
+        const E bb = beta[(t0 + rg) * HV + hv];
+        __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the waits count on it
+        RowsReg<E, KD, LK> rq, rk;
+        rq.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        rk.load(k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
+        __builtin_amdgcn_sched_barrier(0);
         RowsReg<E, 64, LA> rA;
         StateReg<E, KD, LK> rH, rdH;
         RowsReg<E, 64, LS> rdO, rV;
@@ -308,11 +313,12 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
         rV.load(v + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
         if (threadIdx.x < C) {
             const int r = threadIdx.x;
-            const float gg = a.gcum[(t0 + min(r, Cn - 1)) * HV + hv];
             sG[r] = gg;
             sGam[r] = __expf(gg);
-            sB[r] = r < Cn ? (float)beta[(t0 + r) * HV + hv] : 0.f;
+            sB[r] = r < Cn ? (float)bb : 0.f;
         }
+        rq.store(sQ);
+        rk.store(sK);
         lds_barrier();
         const float gl = sG[C - 1], gC = sGam[C - 1];
 
