@@ -33,7 +33,7 @@
 
 namespace gdr {
 
-template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 8 : 4; }
+template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 16 : 4; }
 
 // Wave w owns rows 32*(w&1) .. +31 and the column block (w>>1) of every
 // output; 8 waves (two per SIMD, so one wave's element-wise work overlaps the
