@@ -62,7 +62,7 @@ struct TileMap {
     static constexpr int CPR = D / 8;            // chunks per token row
     static constexpr int NPT = ST * CPR / 512;   // chunks per thread
     static constexpr int RSTEP = 512 / CPR;      // rows between a thread's chunks
-    static constexpr int LD = D + 8;             // padded 16-bit LDS row
+    static constexpr int LD = D + 16;            // padded 16-bit LDS row
 };
 
 // RMSNorm scale, ReLU, k_scale and RoPE of one 8-channel chunk.
@@ -269,7 +269,7 @@ struct ScanArgs {
 
 template <int D>
 struct SCfg {
-    static constexpr int LD = D + 8;
+    static constexpr int LD = D + 16;
     static constexpr int NP = 512 / D;  // threads per z column
     static constexpr size_t mat = (size_t)D * LD * 2;
     static constexpr size_t smem = 2 * mat + (size_t)D * 4 + (size_t)NP * D * 4;
@@ -412,7 +412,7 @@ __global__ void __launch_bounds__(512) bigdn_scan_kernel(ScanArgs a) {
 // then dMc and dzc are stored per frame.
 template <int D>
 struct CCfg {
-    static constexpr int LD = D + 8, LDF = D + 4;
+    static constexpr int LD = D + 16, LDF = D + 4;
     static constexpr int RSTEP = TileMap<D>::RSTEP;
     static constexpr size_t mat = (size_t)D * LD * 2;
     static constexpr size_t tile = (size_t)ST * LD * 2;
@@ -646,7 +646,7 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
 //   dKn = k_scale mask (unrope(dKr) + dKu_z) -> the k slot, dV -> the v slot.
 template <int D>
 struct BCfg {
-    static constexpr int LD = D + 8;
+    static constexpr int LD = D + 16;
     static constexpr int NP = 512 / D;
     static constexpr size_t mat = (size_t)D * LD * 2;
     static constexpr size_t tile = (size_t)ST * LD * 2;
