@@ -174,15 +174,22 @@ struct ScanJob {
     const float* init;  // K x V block of the initial state
     int out_form;       // ST_NONE, ST_NAT, ST_FRAG or ST_FRAG16
     float* out;         // K x V block of the final state
+    float* out2;        // merged forward job: K x K block of the transfer matrix (ST_FRAG16)
 };
 
 // rev: reverse (dh) recursion, else forward.  EST: per-chunk states stored in
-// type E.  ZU: U is taken as zero (the transfer-matrix role).
-template <class E, class S, int KD, int VD, bool rev, bool EST, bool ZU>
+// type E.  ZU: U is taken as zero (the transfer-matrix role).  HP (forward,
+// local scans only): every wave also carries the same columns of the transfer
+// matrix P = Π (γ_C I − K̃ᵀ W) of the segment, as extra state blocks that
+// start from the identity and take U = 0 -- the same recursion as h with the
+// same W and K̃ fragments, so one workgroup yields both local results.
+template <class E, class S, int KD, int VD, bool rev, bool EST, bool ZU, bool HP = false>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, int HV, unsigned char* smem) {
     using Cf = ScanCfg<E, S, KD, VD>;
     using St_t = Stage<E, S, KD, VD, rev>;
     constexpr int KT = KD / 16, C = 64, EPV = Cf::EPV, LK = Cf::LK, LS = Cf::LS, NB = Cf::NB, CW = Cf::CW;
+    static_assert(!HP || (!rev && !ZU && !EST && sizeof(S) == 2), "merged blocks: forward local scans, 16-bit");
+    constexpr int NBT = HP ? 2 * NB : NB;   // state blocks per wave (blocks NB.. are the transfer matrix)
     constexpr int VPR = KD / EPV, XPR = VD / EPV;
     S* slot[2] = {(S*)smem, (S*)smem + Cf::slot_elems};
 
@@ -212,14 +219,17 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
         offX[i] = (idx % XPR) * EPV;
     }
 
-    // state tiles: St[nb][t][e] = state[16t + 4g + e][col0 + 16 nb]
-    f32x4 St[NB][KT];
+    // state tiles: St[nb][t][e] = state[16t + 4g + e][col0 + 16 (nb % NB)]
+    f32x4 St[NBT][KT];
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++)
+    for (int nb = 0; nb < NBT; nb++)
 #pragma unroll
         for (int t = 0; t < KT; t++) {
-            const int cb = CW * w / 16 + nb;
-            if (jb.init_form == ST_FRAG) {
+            const int cb = CW * w / 16 + nb % NB;
+            if (HP && nb >= NB) {   // transfer matrix: from the identity
+#pragma unroll
+                for (int e = 0; e < 4; e++) St[nb][t][e] = 16 * t + 4 * g + e == col0 + 16 * (nb % NB) ? 1.f : 0.f;
+            } else if (jb.init_form == ST_FRAG) {
                 St[nb][t] = *(const f32x4*)(jb.init + ((cb * KT + t) * 64 + l) * 4);
             } else {
 #pragma unroll
@@ -298,7 +308,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
         const int ci = chunk_of(i);
         const long unit = (long)ci * HV + hv;
         const float gC = __expf(gl);
-        f32x4 X[NB][4];
+        f32x4 X[NBT][4];
         if constexpr (sizeof(S) == 2) {
             // All state-independent fragments of this chunk are read from LDS
             // first; the MFMA groups then only wait on their own operands.
@@ -332,14 +342,21 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                         S uu[4];
                         __builtin_memcpy(uu, &u, 8);
 #pragma unroll
-                        for (int e = 0; e < 4; e++) X[nb][m][e] = (float)uu[e];
+                        for (int e = 0; e < 4; e++) X[nb][m][e] = HP ? -(float)uu[e] : (float)uu[e];
                     }
+#pragma unroll
+                for (int nb = NB; nb < NBT; nb++)
+#pragma unroll
+                    for (int m = 0; m < 4; m++) X[nb][m] = zero4();
             } else {
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++)
 #pragma unroll
                     for (int sidx = 0; sidx < 2; sidx++) Db[nb][sidx] = ld_trans<S>(sX, LS, CW * w + 16 * nb, 32 * sidx);
             }
+            // (merged blocks: read after the first product group instead, which
+            // keeps the wider state within the register file)
+            if constexpr (!HP) {
 #pragma unroll
             for (int t = 0; t < KT; t++)
 #pragma unroll
@@ -349,16 +366,18 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                     i16x8 c = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     At[t][sidx] = __builtin_bit_cast(frag, c);
                 }
+            }
             // state store (before the update) and B fragments of the state
 #pragma unroll
             for (int nb = 0; nb < NB; nb++)
                 store_state<E, KD, VD, EST>(St[nb], unit, col0 + 16 * nb, rev ? (E*)a.dhT : (E*)a.hT,
                                             rev ? nullptr : a.h32);
-            // fwd: X = U − W h ; rev: X = K̃ dh ; transfer role: X = W h (sign applied below)
-            const float sg = (rev || ZU) ? 1.f : -1.f;
-            frag Bs[NB][KD / 32];
+            // fwd: X = U − W h ; rev: X = K̃ dh ; transfer role: X = W h (sign applied below);
+            // merged blocks: X = W S − U, then S ← γ S − K̃ᵀ X (the same update)
+            const float sg = (rev || ZU || HP) ? 1.f : -1.f;
+            frag Bs[NBT][KD / 32];
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
+            for (int nb = 0; nb < NBT; nb++)
 #pragma unroll
                 for (int sidx = 0; sidx < KD / 32; sidx++)
 #pragma unroll
@@ -377,9 +396,20 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
                 for (int m = 0; m < 4; m++)
 #pragma unroll
-                    for (int nb = 0; nb < NB; nb++) X[nb][m] = Mma<S>::run(Ar[m][sidx], Bs[nb][sidx], X[nb][m]);
+                    for (int nb = 0; nb < NBT; nb++) X[nb][m] = Mma<S>::run(Ar[m][sidx], Bs[nb][sidx], X[nb][m]);
+            if constexpr (HP) {
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
+                for (int t = 0; t < KT; t++)
+#pragma unroll
+                    for (int sidx = 0; sidx < 2; sidx++) {
+                        i16x4 lo = ld_trans4<S>(sTr, LK, 16 * t, 32 * sidx + 4 * g);
+                        i16x4 hi = ld_trans4<S>(sTr, LK, 16 * t, 32 * sidx + 16 + 4 * g);
+                        i16x8 c = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        At[t][sidx] = __builtin_bit_cast(frag, c);
+                    }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NBT; nb++)
 #pragma unroll
                 for (int t = 0; t < KT; t++) St[nb][t] *= gC;
             if constexpr (rev) {
@@ -411,10 +441,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                         }
             }
             // fwd: + K̃ᵀ V_new ; rev: − Wᵀ (K̃ dh) ; transfer role: − K̃ᵀ (W h)
-            const float sp = (rev || ZU) ? -1.f : 1.f;
-            frag Bp[NB][2];
+            const float sp = (rev || ZU || HP) ? -1.f : 1.f;
+            frag Bp[NBT][2];
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
+            for (int nb = 0; nb < NBT; nb++)
 #pragma unroll
                 for (int sidx = 0; sidx < 2; sidx++)
 #pragma unroll
@@ -427,7 +457,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
                 for (int sidx = 0; sidx < 2; sidx++)
 #pragma unroll
-                    for (int nb = 0; nb < NB; nb++) St[nb][t] = Mma<S>::run(At[t][sidx], Bp[nb][sidx], St[nb][t]);
+                    for (int nb = 0; nb < NBT; nb++) St[nb][t] = Mma<S>::run(At[t][sidx], Bp[nb][sidx], St[nb][t]);
         } else {
             // fp32 operands (16x16x4 MFMA): K = V = 64 only (one 16-column block per wave), plain order
             static_assert(NB == 1, "fp32 scan is built for V = 64");
@@ -500,6 +530,18 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
     }
 
     // final state
+    if constexpr (HP) {   // the transfer-matrix blocks
+        typedef S s4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int nb = NB; nb < NBT; nb++)
+#pragma unroll
+            for (int t = 0; t < KT; t++) {
+                s4 x;
+#pragma unroll
+                for (int e = 0; e < 4; e++) x[e] = (S)St[nb][t][e];
+                *(s4*)((S*)jb.out2 + (((CW * w / 16 + nb - NB) * KT + t) * 64 + l) * 4) = x;
+            }
+    }
     if constexpr (sizeof(S) == 2) {
         if (jb.out_form == ST_FRAG16) {
             typedef S s4 __attribute__((ext_vector_type(4)));
@@ -585,33 +627,22 @@ scan_kernel(ScanArgs a, int nfwd, int HV) {
     }
 }
 
-// Local segment scans (16-bit operands only).  Roles, NS*HV jobs each:
-//   0: forward from zero over the segment  -> hloc  (not for a sequence's last segment)
-//   1: reverse from zero over the segment  -> dhloc (not for its first segment)
-//   2: transfer matrix P = Π (γ_C I − K̃ᵀ W) over the segment, from I -> P
-//      (only for sequences with more than one segment)
-// Roles 0 and 2 read the same W and K̃ tiles in the same order, so their jobs
-// are interleaved in groups of 8: blocks 16 j + i and 16 j + 8 + i (i < 8) are
-// the two roles of job 8 j + i -- the same XCD under round-robin dispatch and
-// started together, so the second reader finds the tiles in that XCD's L2.
-// Role 1 follows in blocks [2 * seg_pairs(per), ...).
+// Local segment scans (16-bit operands only), NS*HV jobs per role:
+//   blocks [0, NS*HV): forward from zero over the segment -> hloc (not needed
+//       for a sequence's last segment), together with the transfer matrix
+//       P = Π (γ_C I − K̃ᵀ W) of the segment, from I -> P (both read the same
+//       W and K̃ tiles, so one workgroup computes both; only for sequences
+//       with more than one segment);
+//   blocks [NS*HV, 2*NS*HV): reverse from zero over the segment -> dhloc (not
+//       for a sequence's first segment).
 // The caller passes arguments with no per-chunk outputs (hT, dhT, h32, v_new).
-__host__ __device__ constexpr int seg_pairs(int per) { return (per + 7) / 8 * 8; }
-
 template <class E, class S, int KD, int VD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 seg_kernel(ScanArgs a, int NS, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int per = NS * HV, x = (int)blockIdx.x, np = seg_pairs(per);
-    int role, b;
-    if (x < 2 * np) {
-        role = (x & 8) ? 2 : 0;
-        b = (x >> 4) * 8 + (x & 7);
-    } else {
-        role = 1;
-        b = x - 2 * np;
-    }
-    if (b >= per) return;
+    const int per = NS * HV, x = (int)blockIdx.x;
+    const bool rev = x >= per;
+    const int b = rev ? x - per : x;
     const SegView v = seg_view(a, b / HV);
     const long KV = (long)KD * VD;
     ScanJob jb;
@@ -621,24 +652,21 @@ seg_kernel(ScanArgs a, int NS, int HV) {
     jb.nc = v.si.nc;
     jb.lc0 = v.si.lc0;
     jb.init = nullptr;
-    jb.out_form = ST_FRAG;
+    jb.init_form = ST_ZERO;
+    jb.out2 = nullptr;
     const long sblk = ((long)v.j * HV + jb.hv) * KV;
-    if (role == 0) {
-        if (v.last || !a.do_fwd) return;
-        jb.init_form = ST_ZERO;
-        jb.out = a.hloc + sblk;
-        scan_body<E, S, KD, VD, false, false, false>(a, jb, HV, smem);
-    } else if (role == 1) {
+    if (rev) {
         if (v.first || !a.do_rev) return;
-        jb.init_form = ST_ZERO;
+        jb.out_form = ST_FRAG;
         jb.out = a.dhloc + sblk;
         scan_body<E, S, KD, VD, true, false, false>(a, jb, HV, smem);
     } else {
         if (v.S == 1) return;
-        jb.init_form = ST_IDENT;
-        jb.out_form = ST_FRAG16;
-        jb.out = a.P + sblk;
-        scan_body<E, S, KD, VD, false, false, true>(a, jb, HV, smem);
+        const bool want_h = !v.last && a.do_fwd;
+        jb.out_form = want_h ? ST_FRAG : ST_NONE;
+        jb.out = want_h ? a.hloc + sblk : nullptr;
+        jb.out2 = a.P + sblk;
+        scan_body<E, S, KD, VD, false, false, false, true>(a, jb, HV, smem);
     }
 }
 
@@ -777,7 +805,7 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
             if (hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) !=
                 hipSuccess)
                 return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL(k1, dim3(2 * seg_pairs(per) + per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
+            hipLaunchKernelGGL(k1, dim3(2 * per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             constexpr int csm = KD * (KD + spad<S>()) * (int)sizeof(S);
