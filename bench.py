@@ -61,6 +61,23 @@ def flop_model_fwd(C, K, V):
     return 6 * C * K * V + 6 * C * C * K + 4 * C * C * V + C ** 3 / 3.0
 
 
+# Matrix-core work each chunk-parallel backward kernel executes per (chunk, value
+# head), full 64-row tiles (C = 64): the products the kernel issues, recompute
+# included -- not the algorithmic model above.
+#   WY prep: K Kᵀ, Q Kᵀ, W = A·diag(βγ)K, Pm·W (2C²K each), U = A·diag(β)V
+#            (2C²V), the blocked triangular inverse (C³/3)
+#   gradient: K h, K dh, dO hᵀ, dV_new hᵀ, V_new dhᵀ (2CKV each); Q Kᵀ, T1 K,
+#             T1ᵀ Q, Aᵀ dW, dW Kᵀ, K Kᵀ (2C²K each), Eb K + Ebᵀ K (4C²K);
+#             Pmᵀ dO, A Z, dO V_newᵀ, dV_new Vᵀ, Aᵀ dV_new (2C²V each);
+#             Aᵀ dA_pre, M1 Aᵀ (2C³ each)
+def mfma_work_prep(K, V, C=64):
+    return 8 * C * C * K + 2 * C * C * V + C ** 3 / 3.0
+
+
+def mfma_work_grad(K, V, C=64):
+    return 10 * C * K * V + 16 * C * C * K + 10 * C * C * V + 4 * C ** 3
+
+
 def kernel_bytes_kda(H, K, V, chunks, es=2):
     """Algorithmic bytes of each stage of the full KDA backward (inputs read
     once, outputs written once)."""
@@ -291,6 +308,18 @@ def main():
         kb = kernel_bytes(cfg, chunks)
         kn = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}
     roof = _roofline(stage, kb, kn, ("fwd_" if fwd else "") + args.workload, profiling)
+    # every stage against HBM, and the chunk-parallel kernels' executed MFMA work against the bf16 peak
+    units = len(chunks) * cfg["HV"]
+    roof["stages"] = {}
+    for k in names:
+        gbs = kb[k] / (stage[k] * 1e-3) / 1e9
+        st = {"ms": round(stage[k], 4), "algorithmic_bytes": kb[k], "hbm_gbs": round(gbs, 1),
+              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        work = {"prep": mfma_work_prep, "grad": mfma_work_grad}.get(k) if not fwd else None
+        if work is not None:
+            tf = work(cfg["K"], cfg["V"]) * units / (stage[k] * 1e-3) / 1e12
+            st.update({"mfma_tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        roof["stages"][k] = st
 
     wname = cfg["name"].replace("gdn_bwd", "gdn_fwd") if fwd else cfg["name"]
     what = "fwd" if fwd else "bwd"
