@@ -62,7 +62,8 @@ struct TileMap {
     static constexpr int CPR = D / 8;            // chunks per token row
     static constexpr int NPT = ST * CPR / 512;   // chunks per thread
     static constexpr int RSTEP = 512 / CPR;      // rows between a thread's chunks
-    static constexpr int LD = D + 16;            // padded 16-bit LDS row
+    static constexpr int LD = D + 16;            // padded 16-bit LDS row: pitch = 8 dwords mod 32 banks, so
+                                                 // transposing fragment reads of 4 rows do not conflict
 };
 
 // RMSNorm scale, ReLU, k_scale and RoPE of one 8-channel chunk.

@@ -161,34 +161,33 @@ __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long uni
 }
 
 // Initial / final state forms of one scan job.
-// ST_FRAG16: the fragment order with the values in the 16-bit operand type S
-// (four per lane and tile, 8 bytes), for the transfer matrices, which only
-// ever enter an MFMA as 16-bit operands.
-enum StateForm { ST_NONE = 0, ST_ZERO = 0, ST_IDENT = 1, ST_NAT = 2, ST_FRAG = 3, ST_FRAG16 = 4 };
+enum StateForm { ST_NONE = 0, ST_ZERO = 0, ST_NAT = 2, ST_FRAG = 3 };
 
 // One scan job: a run of chunks of one sequence and value head.
 struct ScanJob {
     int n, hv;          // sequence, value head
     int c0, nc, lc0;    // first chunk (global index), chunk count, first chunk's index in the sequence
-    int init_form;      // ST_ZERO, ST_IDENT (transfer matrix), ST_NAT ([K][V] fp32), ST_FRAG (fp32 fragment order)
+    int init_form;      // ST_ZERO, ST_NAT ([K][V] fp32), ST_FRAG (fp32 fragment order)
     const float* init;  // K x V block of the initial state
-    int out_form;       // ST_NONE, ST_NAT, ST_FRAG or ST_FRAG16
+    int out_form;       // ST_NONE, ST_NAT or ST_FRAG
     float* out;         // K x V block of the final state
-    float* out2;        // merged forward job: K x K block of the transfer matrix (ST_FRAG16)
+    float* out2;        // merged forward job: K x K block of the transfer matrix, in the
+                        // fragment order with the values in the 16-bit operand type S
+                        // (four per lane and tile): it only enters MFMAs as an operand
 };
 
 // rev: reverse (dh) recursion, else forward.  EST: per-chunk states stored in
-// type E.  ZU: U is taken as zero (the transfer-matrix role).  HP (forward,
+// type E.  HP (forward,
 // local scans only): every wave also carries the same columns of the transfer
 // matrix P = Π (γ_C I − K̃ᵀ W) of the segment, as extra state blocks that
 // start from the identity and take U = 0 -- the same recursion as h with the
 // same W and K̃ fragments, so one workgroup yields both local results.
-template <class E, class S, int KD, int VD, bool rev, bool EST, bool ZU, bool HP = false>
+template <class E, class S, int KD, int VD, bool rev, bool EST, bool HP = false>
 __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, int HV, unsigned char* smem) {
     using Cf = ScanCfg<E, S, KD, VD>;
     using St_t = Stage<E, S, KD, VD, rev>;
     constexpr int KT = KD / 16, C = 64, EPV = Cf::EPV, LK = Cf::LK, LS = Cf::LS, NB = Cf::NB, CW = Cf::CW;
-    static_assert(!HP || (!rev && !ZU && !EST && sizeof(S) == 2), "merged blocks: forward local scans, 16-bit");
+    static_assert(!HP || (!rev && !EST && sizeof(S) == 2), "merged blocks: forward local scans, 16-bit");
     constexpr int NBT = HP ? 2 * NB : NB;   // state blocks per wave (blocks NB.. are the transfer matrix)
     constexpr int VPR = KD / EPV, XPR = VD / EPV;
     S* slot[2] = {(S*)smem, (S*)smem + Cf::slot_elems};
@@ -236,7 +235,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 for (int e = 0; e < 4; e++) {
                     const int row = 16 * t + 4 * g + e, col = col0 + 16 * nb;
                     St[nb][t][e] = jb.init_form == ST_NAT ? jb.init[row * VD + col]
-                                 : jb.init_form == ST_IDENT ? (row == col ? 1.f : 0.f) : 0.f;
+                                 : 0.f;
                 }
             }
         }
@@ -267,7 +266,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 // make the wave wait for the load it just issued)
                 const int rowc = min(rowX[j], Cn - 1);
                 st.x[j] = *(const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]);
-            } else if constexpr (!ZU) {
+            } else {
                 st.u[j] = *(const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]);
             }
         }
@@ -293,7 +292,6 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
                 for (int e = 0; e < EPV; e++) xv[e] = valid ? (S)(float)st.x[j][e] : (S)0.f;
             } else {
-                if constexpr (ZU) continue;
                 xv = st.u[j];
             }
             *(typename Vec16<S>::t*)(sX + rowX[j] * LS + offX[j]) = xv;
@@ -328,12 +326,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                     i16x8 c = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     Ar[m][sidx] = __builtin_bit_cast(frag, c);
                 }
-            if constexpr (!rev && ZU) {
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-                    for (int m = 0; m < 4; m++) X[nb][m] = zero4();
-            } else if constexpr (!rev) {
+            if constexpr (!rev) {
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++)
 #pragma unroll
@@ -372,9 +365,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
             for (int nb = 0; nb < NB; nb++)
                 store_state<E, KD, VD, EST>(St[nb], unit, col0 + 16 * nb, rev ? (E*)a.dhT : (E*)a.hT,
                                             rev ? nullptr : a.h32);
-            // fwd: X = U − W h ; rev: X = K̃ dh ; transfer role: X = W h (sign applied below);
+            // fwd: X = U − W h ; rev: X = K̃ dh (sign applied below);
             // merged blocks: X = W S − U, then S ← γ S − K̃ᵀ X (the same update)
-            const float sg = (rev || ZU || HP) ? 1.f : -1.f;
+            const float sg = (rev || HP) ? 1.f : -1.f;
             frag Bs[NBT][KD / 32];
 #pragma unroll
             for (int nb = 0; nb < NBT; nb++)
@@ -440,8 +433,8 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                                 ((E*)a.v_new)[((ct0 + row) * HV + hv) * VD + col0 + 16 * nb] = (E)X[nb][m][e];
                         }
             }
-            // fwd: + K̃ᵀ V_new ; rev: − Wᵀ (K̃ dh) ; transfer role: − K̃ᵀ (W h)
-            const float sp = (rev || ZU || HP) ? -1.f : 1.f;
+            // fwd: + K̃ᵀ V_new ; rev: − Wᵀ (K̃ dh) ; merged blocks: − K̃ᵀ X
+            const float sp = (rev || HP) ? -1.f : 1.f;
             frag Bp[NBT][2];
 #pragma unroll
             for (int nb = 0; nb < NBT; nb++)
@@ -542,20 +535,6 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 *(s4*)((S*)jb.out2 + (((CW * w / 16 + nb - NB) * KT + t) * 64 + l) * 4) = x;
             }
     }
-    if constexpr (sizeof(S) == 2) {
-        if (jb.out_form == ST_FRAG16) {
-            typedef S s4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-                for (int t = 0; t < KT; t++) {
-                    s4 x;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) x[e] = (S)St[nb][t][e];
-                    *(s4*)((S*)jb.out + (((CW * w / 16 + nb) * KT + t) * 64 + l) * 4) = x;
-                }
-        }
-    }
     if (jb.out_form == ST_FRAG) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
@@ -617,13 +596,13 @@ scan_kernel(ScanArgs a, int nfwd, int HV) {
         jb.init = from_end ? (a.dht ? a.dht + nblk : nullptr) : a.dhin + sblk;
         jb.out_form = v.first && a.dh0 ? ST_NAT : ST_NONE;
         jb.out = a.dh0 ? a.dh0 + nblk : nullptr;
-        scan_body<E, S, KD, VD, true, EST, false>(a, jb, HV, smem);
+        scan_body<E, S, KD, VD, true, EST>(a, jb, HV, smem);
     } else {
         jb.init_form = v.first ? (a.h0 ? ST_NAT : ST_ZERO) : ST_FRAG;
         jb.init = v.first ? (a.h0 ? a.h0 + nblk : nullptr) : a.hstart + sblk;
         jb.out_form = v.last && a.ht ? ST_NAT : ST_NONE;
         jb.out = a.ht ? a.ht + nblk : nullptr;
-        scan_body<E, S, KD, VD, false, EST, false>(a, jb, HV, smem);
+        scan_body<E, S, KD, VD, false, EST>(a, jb, HV, smem);
     }
 }
 
@@ -659,14 +638,14 @@ seg_kernel(ScanArgs a, int NS, int HV) {
         if (v.first || !a.do_rev) return;
         jb.out_form = ST_FRAG;
         jb.out = a.dhloc + sblk;
-        scan_body<E, S, KD, VD, true, false, false>(a, jb, HV, smem);
+        scan_body<E, S, KD, VD, true, false>(a, jb, HV, smem);
     } else {
         if (v.S == 1) return;
         const bool want_h = !v.last && a.do_fwd;
         jb.out_form = want_h ? ST_FRAG : ST_NONE;
         jb.out = want_h ? a.hloc + sblk : nullptr;
         jb.out2 = a.P + sblk;
-        scan_body<E, S, KD, VD, false, false, false, true>(a, jb, HV, smem);
+        scan_body<E, S, KD, VD, false, false, true>(a, jb, HV, smem);
     }
 }
 
