@@ -491,7 +491,7 @@ def bench_bigdn(args, torch, binding, profiling, workloads):
         for j, k in enumerate(names):
             stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
     Fl = flop_model_bigdn(B, F, S, H, D)
-    nblk = min(1024, (B * F * S + 3) // 4)
+    nblk = min(768, (B * F * S + 3) // 4)
     kb = kernel_bytes_bigdn(B, F, S, H, D, nblk)
     kn = {"stats": "bigdn_stats_kernel", "phase_a": "bigdn_phase_a_kernel", "scans": "bigdn_scan_kernel",
           "phase_c": "bigdn_phase_c_kernel", "gscans": "bigdn_scan_kernel", "abar": "bigdn_abar_kernel",

@@ -961,8 +961,10 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
 // --------------------------------------------------------------------------
 // RMSNorm VJP over all C channels of a token, in place on the q and k slots
 // of dqkv (which hold dQn and dKn):  dx = r w dy - r^3/C x sum(w dy x);
-// per-block partial sums of dy x r for the norm weights.  One wave per
-// (token, slot).
+// per-block partial sums of dy x r for the norm weights, accumulated in each
+// wave's own LDS row (lane-private addresses, so no synchronisation until the
+// end; in registers they would cost 8·NCH VGPRs per lane and a wave per SIMD).
+// One wave per (token, slot).
 template <int NCH>
 __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ dqkv,
                                                             const float* __restrict__ rq, const float* __restrict__ rk,
@@ -976,11 +978,15 @@ __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restri
     const int sl = w & 1;
     const float* wt = sl ? kw : qw;
     const float* rr = sl ? rk : rq;
-    float acc[NCH][8];
+    float* acc = red + w * C;   // this wave's partials; lane l owns channels 8 (l + 64 ch) .. +7
 #pragma unroll
-    for (int ch = 0; ch < NCH; ch++)
-#pragma unroll
-        for (int i = 0; i < 8; i++) acc[ch][i] = 0.f;
+    for (int ch = 0; ch < NCH; ch++) {
+        const int c8 = l + 64 * ch;
+        if (c8 < nc8) {
+            *(f32x4*)(acc + 8 * c8) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *(f32x4*)(acc + 8 * c8 + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     const long nunit = 2L * ntok, ustep = (long)gridDim.x * 4;
     // the next unit's rows are loaded before the current one is reduced
     bf16x8 nx[NCH], ng[NCH];
@@ -1024,25 +1030,21 @@ __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restri
         for (int ch = 0; ch < NCH; ch++) {
             const int c8 = l + 64 * ch;
             if (c8 < nc8) {
-                float w8[8];
+                float w8[8], a8[8];
                 ld8(wt + 8 * c8, w8);
+                ld8(acc + 8 * c8, a8);
                 bf16x8 o;
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     const float xa = (float)xr[ch][i], ga = (float)gr[ch][i];
                     o[i] = (bf16)(r * w8[i] * ga - k3 * xa);
-                    acc[ch][i] += ga * xa * r;
+                    a8[i] += ga * xa * r;
                 }
+                *(f32x4*)(acc + 8 * c8) = f32x4{a8[0], a8[1], a8[2], a8[3]};
+                *(f32x4*)(acc + 8 * c8 + 4) = f32x4{a8[4], a8[5], a8[6], a8[7]};
                 *(bf16x8*)(dx + 8 * c8) = o;
             }
         }
-    }
-#pragma unroll
-    for (int ch = 0; ch < NCH; ch++) {
-        const int c8 = l + 64 * ch;
-        if (c8 < nc8)
-#pragma unroll
-            for (int i = 0; i < 8; i++) red[w * C + 8 * c8 + i] = acc[ch][i];
     }
     __syncthreads();
     // waves 0, 2 hold q partials, waves 1, 3 k partials
@@ -1078,10 +1080,12 @@ __global__ void __launch_bounds__(256) bigdn_wsum_kernel(const float* __restrict
 // Host side
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Persistent RMSNorm-VJP workgroups: three per CU (158 VGPRs per lane, 32 KB
+// of LDS each) on 256 CUs, so the grid is resident in one round.
 static int rms_blocks(const Dims& d) {
     const long ntok = (long)d.B * d.F * d.S;
     const long nb = (ntok + 3) / 4;
-    return (int)(nb < 1024 ? nb : 1024);
+    return (int)(nb < 768 ? nb : 768);
 }
 
 size_t plan(const Dims& d, bool bwd, char* base, Ws* w) {
