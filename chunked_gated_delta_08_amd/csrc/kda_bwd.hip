@@ -68,37 +68,49 @@ __device__ __forceinline__ void kda_find_chunk(const int32_t* __restrict__ cu, i
 
 template <class T, int N> using kdv = T __attribute__((ext_vector_type(N)));
 
-// rows [0, rows) of a row-major block (row stride rs) into LDS (row pitch LD),
-// converted to E; rows at or past rows_valid are zero.  One 16-byte load and
-// one vector LDS write per step.
-template <class Ein, class E, int D, int LD>
-__device__ __forceinline__ void kda_load(E* s, const Ein* __restrict__ g, long rs, int rows_valid, int rows) {
-    constexpr int EPV = 16 / sizeof(Ein);
-    constexpr int VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < rows * VPR; idx += 512) {
-        const int r = idx / VPR, c = idx % VPR;
-        typename Vec16<Ein>::t v;
-        if (r < rows_valid) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
-        else v = typename Vec16<Ein>::t{};
-        kdv<E, EPV> y;
+// Register staging of a [64][D] row tile of a token-major tensor (row stride
+// rs elements): issue() loads 16-byte vectors (rows at or past Cn read row
+// Cn-1, a valid row), store() writes them to LDS (row pitch LD) with those
+// rows zeroed.  Splitting the two lets every load of a unit be in flight
+// before the first wait.
+template <class T, int D>
+struct KRows {
+    static constexpr int EPV = 16 / (int)sizeof(T), VPR = D / EPV, N = 64 * VPR / 512;
+    static_assert(64 * VPR % 512 == 0, "whole vectors per thread");
+    kdv<T, EPV> v[N];
+    __device__ __forceinline__ static int row(int i) { return ((int)threadIdx.x + 512 * i) / VPR; }
+    __device__ __forceinline__ static int col(int i) { return ((int)threadIdx.x + 512 * i) % VPR * EPV; }
+    __device__ __forceinline__ void issue(const T* __restrict__ g, long rs, int Cn) {
 #pragma unroll
-        for (int e = 0; e < EPV; e++) y[e] = (E)(float)v[e];
-        *(kdv<E, EPV>*)(s + r * LD + c * EPV) = y;
+        for (int i = 0; i < N; i++) v[i] = *(const kdv<T, EPV>*)(g + min(row(i), Cn - 1) * rs + col(i));
     }
-}
+    template <int LD>
+    __device__ __forceinline__ void store(T* s, int Cn) const {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            kdv<T, EPV> y = v[i];
+            if (row(i) >= Cn) y = kdv<T, EPV>{};
+            *(kdv<T, EPV>*)(s + row(i) * LD + col(i)) = y;
+        }
+    }
+};
 
-// A fp32 KD x VD state block into LDS as E (pitch LD), keeping this thread's
-// values: NS float4 per thread, element (row (tid + 512 i) / (VD/4), ...).
 template <class E, int KD, int VD, int LD>
 struct KdaStateRegs {
     static constexpr int VPR = VD / 4, NS = KD * VPR / 512;
     static_assert(KD * VPR % 512 == 0, "whole vectors per thread");
     f32x4 v[NS];
-    __device__ __forceinline__ void load(E* s, const float* __restrict__ g) {
+    __device__ __forceinline__ void issue(const float* __restrict__ g) {
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const int idx = threadIdx.x + 512 * i, r = idx / VPR, c = idx % VPR;
             v[i] = *(const f32x4*)(g + (long)r * VD + c * 4);
+        }
+    }
+    __device__ __forceinline__ void store(E* s) const {
+#pragma unroll
+        for (int i = 0; i < NS; i++) {
+            const int idx = threadIdx.x + 512 * i, r = idx / VPR, c = idx % VPR;
             kdv<E, 4> y;
 #pragma unroll
             for (int e = 0; e < 4; e++) y[e] = (E)v[i][e];
@@ -144,39 +156,70 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     const float* dhg = a.dh + unit * KD * VD;
     auto gidx = [&](int r, int c) { return ((t0 + r) * H + hh) * (long)KD + c; };   // [.,H,KD] element
 
-    // ---- stage h, dO, dv_in, A (lower triangle), β, β γ K, β V
+    // ---- every global load of the unit is issued first, in a pinned order
+    //      (β; h, dO, dv_in, A; K with its gates, V; dh, V_new), then staged
+    //      into LDS as the phases below need it
+    constexpr int EPE = 16 / (int)sizeof(E), NKV = C * KD / EPE / 512;
+    const E bb = beta[(t0 + min((int)threadIdx.x & (C - 1), Cn - 1)) * H + hh];
+    __builtin_amdgcn_sched_barrier(0);
     KdaStateRegs<E, KD, VD, LV> hreg;   // h stays in registers for rowsum_V(h ⊙ dh)
-    hreg.load(sH, hg);
-    kda_load<E, E, VD, LV>(sX, dO + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
-    kda_load<E, E, VD, LV>(sDV, dvi + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
-    for (int idx = threadIdx.x; idx < C * 64; idx += 512) {
-        const int r = idx / 64, c = idx % 64;
-        const float x = (r < Cn && c <= r) ? (float)Ain[((t0 + r) * H + hh) * 64 + c] : 0.f;
-        sA[r * LA + c] = (E)x;
+    hreg.issue(hg);
+    KRows<E, VD> rdo, rdv;
+    rdo.issue(dO + (t0 * H + hh) * VD, (long)H * VD, Cn);
+    rdv.issue(dvi + (t0 * H + hh) * VD, (long)H * VD, Cn);
+    KRows<E, 64> ra;
+    ra.issue(Ain + (t0 * H + hh) * 64, (long)H * 64, Cn);
+    __builtin_amdgcn_sched_barrier(0);
+    kdv<E, EPE> rkv[NKV];
+    f32x4 rgv[NKV][EPE / 4];
+#pragma unroll
+    for (int i = 0; i < NKV; i++) {
+        const int idx = threadIdx.x + 512 * i, r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
+        rkv[i] = *(const kdv<E, EPE>*)(k + gidx(rc, c));
+#pragma unroll
+        for (int e4 = 0; e4 < EPE; e4 += 4) rgv[i][e4 / 4] = *(const f32x4*)(a.g + gidx(rc, c + e4));
     }
-    if (threadIdx.x < C) sB[threadIdx.x] = threadIdx.x < Cn ? (float)beta[(t0 + threadIdx.x) * H + hh] : 0.f;
+    KRows<E, VD> rv;
+    rv.issue(v + (t0 * H + hh) * VD, (long)H * VD, Cn);
+    __builtin_amdgcn_sched_barrier(0);
+    KdaStateRegs<E, KD, VD, LV> dhreg;
+    dhreg.issue(dhg);
+    KRows<E, VD> rvn;
+    rvn.issue(vn + (t0 * H + hh) * VD, (long)H * VD, Cn);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- stage h, dO, dv_in, A (lower triangle), β
+    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)bb : 0.f;
+    hreg.store(sH);
+    rdo.template store<LV>(sX, Cn);
+    rdv.template store<LV>(sDV, Cn);
+#pragma unroll
+    for (int i = 0; i < KRows<E, 64>::N; i++) {
+        const int r = KRows<E, 64>::row(i), c = KRows<E, 64>::col(i);
+        kdv<E, KRows<E, 64>::EPV> y;
+#pragma unroll
+        for (int e = 0; e < KRows<E, 64>::EPV; e++) y[e] = (r < Cn && c + e <= r) ? ra.v[i][e] : (E)0.f;
+        *(kdv<E, KRows<E, 64>::EPV>*)(sA + r * LA + c) = y;
+    }
     lds_barrier();
-    {   // β γ K and β V, one 16-byte load of k / v (and the matching gates) per step
-        constexpr int EPE = 16 / (int)sizeof(E);
-        for (int idx = threadIdx.x; idx < C * KD / EPE; idx += 512) {
-            const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
-            const kdv<E, EPE> kv = *(const kdv<E, EPE>*)(k + gidx(rc, c));
+    {   // β γ K and β V
+#pragma unroll
+        for (int i = 0; i < NKV; i++) {
+            const int idx = threadIdx.x + 512 * i, r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE;
             kdv<E, EPE> y;
 #pragma unroll
-            for (int e4 = 0; e4 < EPE; e4 += 4) {
-                const f32x4 gv = *(const f32x4*)(a.g + gidx(rc, c + e4));
+            for (int e4 = 0; e4 < EPE; e4 += 4)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    y[e4 + e] = (E)(r < Cn ? sB[r] * __expf(gv[e]) * (float)kv[e4 + e] : 0.f);
-            }
+                    y[e4 + e] = (E)(r < Cn ? sB[r] * __expf(rgv[i][e4 / 4][e]) * (float)rkv[i][e4 + e] : 0.f);
             *(kdv<E, EPE>*)(sKb + r * LK + c) = y;
         }
-        for (int idx = threadIdx.x; idx < C * VD / EPE; idx += 512) {
-            const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
-            const kdv<E, EPE> vv = *(const kdv<E, EPE>*)(v + ((t0 + rc) * H + hh) * VD + c);
+#pragma unroll
+        for (int i = 0; i < KRows<E, VD>::N; i++) {
+            const int r = KRows<E, VD>::row(i), c = KRows<E, VD>::col(i);
             kdv<E, EPE> y;
 #pragma unroll
-            for (int e = 0; e < EPE; e++) y[e] = (E)(r < Cn ? sB[r] * (float)vv[e] : 0.f);
+            for (int e = 0; e < EPE; e++) y[e] = (E)(r < Cn ? sB[r] * (float)rv.v[i][e] : 0.f);
             *(kdv<E, EPE>*)(sVb + r * LV + c) = y;
         }
     }
@@ -190,8 +233,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     lds_barrier();
     // ---- swap in dh and V_new; dw -> LDS; rowsum_V(h ⊙ dh) in fp32 from the registers
     {
-        KdaStateRegs<E, KD, VD, LV> dhreg;
-        dhreg.load(sH, dhg);
+        dhreg.store(sH);
         constexpr int VPR = KdaStateRegs<E, KD, VD, LV>::VPR;   // lanes per key row (16 or 32)
 #pragma unroll
         for (int i = 0; i < KdaStateRegs<E, KD, VD, LV>::NS; i++) {
@@ -204,7 +246,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
             sHD[(threadIdx.x + 512 * i) / VPR] = x;
         }
     }
-    kda_load<E, E, VD, LV>(sX, vn + (t0 * H + hh) * VD, (long)H * VD, Cn, C);
+    rvn.template store<LV>(sX, Cn);
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
