@@ -441,29 +441,39 @@ __global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int
 }
 
 // ---------------------------------------------------------------- intra-chunk part
-// Grid (chunks, H), 256 threads.  Adds the Aqk and dL terms to the WY stage's
+// Grid (chunks, H), 512 threads.  Adds the Aqk and dL terms to the WY stage's
 // partials and writes dq, dk (input type), dg (reverse-cumsummed), dβ.
+// 71 KB of LDS; at K = V = 128 with 16-bit staging also at most 128 VGPRs, so
+// two workgroups share a CU and one's barriers and loads overlap the other's
+// products (the K = V = 64 instances need more registers and run one per CU).
 template <class S, int VD>
 struct KIntraCfg {
     static constexpr int C = 64, LV = VD + kfpad<S>(), LF = 68;
+    static constexpr int WPE = sizeof(S) == 2 && VD == 128 ? 4 : 2;    // waves per SIMD
+    static constexpr size_t szIO = (size_t)2 * C * LV * sizeof(S), szSl = (size_t)4 * C * LSL * 4;
     static constexpr size_t oDO = 0;                                   // dO [64][LV] S
     static constexpr size_t oVn = oDO + (size_t)C * LV * sizeof(S);    // V_new [64][LV] S
-    static constexpr size_t oDAq = oVn + (size_t)C * LV * sizeof(S);   // dAqk [64][LF] fp32
+    static constexpr size_t oPA = 0;                                   // 4 fp32 slices [64][LSL], over dO and V_new
+    static constexpr size_t oDAq = szIO > szSl ? szIO : szSl;          // dAqk [64][LF] fp32
     static constexpr size_t oDL = oDAq + (size_t)C * LF * 4;           // dL [64][LF] fp32
-    static constexpr size_t oDG = oDL + (size_t)C * LF * 4;            // dG slice [64][LSL] fp32
-    static constexpr size_t oB = oDG + (size_t)C * LSL * 4;            // β [64], dβ row sums [2][64]
-    static constexpr size_t oPA = oB + (size_t)3 * 64 * 4;             // 4 fp32 slices [64][LSL]
-    static constexpr size_t smem = oPA + (size_t)4 * C * LSL * 4;
-    static_assert(smem <= 160 * 1024, "LDS budget");
+    static constexpr size_t oB = oDL + (size_t)C * LF * 4;             // β [64], dβ row sums [2][64]
+    static constexpr size_t oBT = oB + (size_t)3 * 64 * 4;             // dG totals of 16-row blocks [4][KSL]
+    static constexpr size_t smem = oBT + (size_t)4 * KSL * 4;
+    static_assert(2 * smem <= 160 * 1024, "two workgroups per CU");
 };
 
 // 512 threads: wave w owns rows 16 (w & 3) .. +15 and half w >> 2 of the
-// columns of every product.
+// columns of every product.  Every global load is issued one step ahead: the
+// next slice's q, k and G rows and the next slice's per-element operands are
+// in flight during this slice's products.
 template <class E, class S, int KD, int VD>
-__global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, float scale) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(KIntraCfg<S, VD>::WPE, KIntraCfg<S, VD>::WPE)))
+kda_intra_kernel(KdaFullArgs a, int H, float scale) {
     using Cf = KIntraCfg<S, VD>;
-    constexpr int C = 64, NT = 512, LV = Cf::LV, LF = Cf::LF;
+    constexpr int C = 64, LV = Cf::LV, LF = Cf::LF;
     constexpr int EPE = 16 / (int)sizeof(E);
+    constexpr int NIO = C * VD / EPE / 512, NDA = C * C / 4 / 512;   // dO / V_new and dL vectors per thread
+    static_assert(C * VD / EPE % 512 == 0 && C * KSL / 4 == 512, "whole vectors per thread");
     extern __shared__ __align__(16) unsigned char smem[];
     S* sDO = (S*)(smem + Cf::oDO);
     S* sVn = (S*)(smem + Cf::oVn);
@@ -473,11 +483,11 @@ __global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, fl
     float* sEp = sKb + C * LSL;              // e^{G−m}
     float* sDAq = (float*)(smem + Cf::oDAq);
     float* sDL = (float*)(smem + Cf::oDL);
-    float* sDG = (float*)(smem + Cf::oDG);
     float* sB = (float*)(smem + Cf::oB);
     float* sRB = sB + 64;
+    float* sBT = (float*)(smem + Cf::oBT);
 
-    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id(), l = lane_id();
     const int m0 = 16 * (w & 3), hc = w >> 2;   // row group, column half
     const int Cn = a.info[ci].len;
     const long t0 = a.info[ci].t0;
@@ -486,25 +496,90 @@ __global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, fl
     const float* G = a.gcum;
     const int ref = (Cn - 1) / 2;
 
-    // ---- dO, V_new (rows past the chunk zero), dL, β
-    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
-        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
-        const kvec<E, EPE> xo = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + rc) * H + h) * VD + c);
-        const kvec<E, EPE> xv = *(const kvec<E, EPE>*)((const E*)a.vn + ((t0 + rc) * H + h) * VD + c);
+    // One slice vector per thread: row sr, channels sdd .. +3 of the slice.
+    const int sr = threadIdx.x / (KSL / 4), sdd = threadIdx.x % (KSL / 4) * 4;
+    const long so = ((t0 + min(sr, Cn - 1)) * H + h) * KD + sdd, mo = ((t0 + ref) * H + h) * KD + sdd;
+    f32x4 xm, xg;
+    kvec<E, 4> xk, xq;
+    auto slice_issue = [&](int s0) {
+        xm = *(const f32x4*)(G + mo + s0);
+        xg = *(const f32x4*)(G + so + s0);
+        xk = *(const kvec<E, 4>*)(k + so + s0);
+        xq = *(const kvec<E, 4>*)(q + so + s0);
+    };
+    auto slice_store = [&]() {
+        f32x4 km, qp, kb, epv;
+        const float bt = sB[sr];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float ep = sr < Cn ? __expf(xg[e] - xm[e]) : 0.f, em = sr < Cn ? __expf(xm[e] - xg[e]) : 0.f;
+            km[e] = (float)xk[e] * em;
+            qp[e] = (float)xq[e] * ep;
+            kb[e] = bt * (float)xk[e] * ep;
+            epv[e] = ep;
+        }
+        *(f32x4*)(sKm + sr * LSL + sdd) = km;
+        *(f32x4*)(sQp + sr * LSL + sdd) = qp;
+        *(f32x4*)(sKb + sr * LSL + sdd) = kb;
+        *(f32x4*)(sEp + sr * LSL + sdd) = epv;
+    };
+    // This lane's elements of q, k and the stage partials: rows m0 + 4 g + e,
+    // channel 16 hc + (l & 15) of the slice.
+    float pk[4], pq[4], pdq[4], pdk[4], pdg[4];
+    auto elem_offset = [&](int e, int s0) {
+        const int r = acc_row(m0, 0, e);
+        return ((t0 + min(r, Cn - 1)) * H + h) * KD + s0 + acc_col(16 * hc, 0);
+    };
+    auto elem_issue = [&](int s0) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const long o = elem_offset(e, s0);
+            pk[e] = (float)k[o];
+            pq[e] = (float)q[o];
+            pdq[e] = a.dqs[o];
+            pdk[e] = a.dks[o];
+            pdg[e] = a.dgs[o];
+        }
+    };
+
+    // ---- every load of the first phase, then slice 0's, in this order
+    const float bb = (float)((const E*)a.beta)[(t0 + min((int)threadIdx.x & (C - 1), Cn - 1)) * H + h];
+    __builtin_amdgcn_sched_barrier(0);
+    kvec<E, EPE> xo[NIO], xv[NIO];
+#pragma unroll
+    for (int i = 0; i < NIO; i++) {
+        const int idx = threadIdx.x + 512 * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
+        const long o = ((t0 + min(r, Cn - 1)) * H + h) * VD + c;
+        xo[i] = *(const kvec<E, EPE>*)((const E*)a.dO + o);
+        xv[i] = *(const kvec<E, EPE>*)((const E*)a.vn + o);
+    }
+    f32x4 xa[NDA];
+#pragma unroll
+    for (int i = 0; i < NDA; i++) {
+        const int idx = threadIdx.x + 512 * i, r = idx / (C / 4), c = idx % (C / 4) * 4;
+        xa[i] = *(const f32x4*)(a.dA + ((t0 + min(r, Cn - 1)) * H + h) * C + c);
+    }
+    slice_issue(0);
+    elem_issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? bb : 0.f;
+#pragma unroll
+    for (int i = 0; i < NIO; i++) {
+        const int idx = threadIdx.x + 512 * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
         kvec<S, EPE> yo, yv;
 #pragma unroll
         for (int e = 0; e < EPE; e++) {
-            yo[e] = r < Cn ? (S)(float)xo[e] : (S)0.f;
-            yv[e] = r < Cn ? (S)(float)xv[e] : (S)0.f;
+            yo[e] = r < Cn ? (S)(float)xo[i][e] : (S)0.f;
+            yv[e] = r < Cn ? (S)(float)xv[i][e] : (S)0.f;
         }
         *(kvec<S, EPE>*)(sDO + r * LV + c) = yo;
         *(kvec<S, EPE>*)(sVn + r * LV + c) = yv;
     }
-    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-        const int r = idx / C, c = idx % C;
-        sDL[r * LF + c] = r < Cn ? a.dA[((t0 + r) * H + h) * C + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NDA; i++) {
+        const int idx = threadIdx.x + 512 * i, r = idx / (C / 4), c = idx % (C / 4) * 4;
+        *(f32x4*)(sDL + r * LF + c) = r < Cn ? xa[i] : zero4();
     }
-    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)((const E*)a.beta)[(t0 + threadIdx.x) * H + h] : 0.f;
     lds_barrier();
     // ---- dAqk = lower(dO V_newᵀ)    (wave w: rows m0, columns 32 hc .. +31)
     {
@@ -520,89 +595,67 @@ __global__ void __launch_bounds__(512) kda_intra_kernel(KdaFullArgs a, int H, fl
             }
     }
     lds_barrier();   // dO and V_new are no longer read: the slices take their place
+    slice_store();
+    lds_barrier();
 
     float rbeta[4] = {0.f, 0.f, 0.f, 0.f};   // Σ_d K e^{G−m} ⊙ (dL K e^{m−G}) for rows m0 + 4g + e (this half)
+    const int g4 = l >> 4, dd = acc_col(16 * hc, 0);
 #pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
-        for (int idx = threadIdx.x; idx < C * KSL / 4; idx += NT) {   // 4 channels per step
-            const int r = idx / (KSL / 4), dd = (idx % (KSL / 4)) * 4, d = s0 + dd;
-            const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
-            const f32x4 m = *(const f32x4*)(G + ((t0 + ref) * H + h) * KD + d);
-            const f32x4 g = *(const f32x4*)(G + o);
-            const kvec<E, 4> kv = *(const kvec<E, 4>*)(k + o), qv = *(const kvec<E, 4>*)(q + o);
-            f32x4 km, qp, kb, epv;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float ep = r < Cn ? __expf(g[e] - m[e]) : 0.f, em = r < Cn ? __expf(m[e] - g[e]) : 0.f;
-                km[e] = (float)kv[e] * em;
-                qp[e] = (float)qv[e] * ep;
-                kb[e] = sB[r] * (float)kv[e] * ep;
-                epv[e] = ep;
-            }
-            *(f32x4*)(sKm + r * LSL + dd) = km;
-            *(f32x4*)(sQp + r * LSL + dd) = qp;
-            *(f32x4*)(sKb + r * LSL + dd) = kb;
-            *(f32x4*)(sEp + r * LSL + dd) = epv;
-        }
-        lds_barrier();
-        // this lane's elements of q, k and the stage partials, loaded before the products
-        float pk[1][4], pq[1][4], pdq[1][4], pdk[1][4], pdg[1][4];
-#pragma unroll
-        for (int j = 0; j < 1; j++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = acc_row(m0, 0, e), d = s0 + acc_col(16 * hc, j);
-                const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
-                pk[j][e] = (float)k[o];
-                pq[j][e] = (float)q[o];
-                pdq[j][e] = a.dqs[o];
-                pdk[j][e] = a.dks[o];
-                pdg[j][e] = a.dgs[o];
-            }
+        const int sn = min(s0 + KSL, KD - KSL);   // the next slice (the last one again at the end)
+        slice_issue(sn);
         // wave w: rows m0, channels 16 hc .. +15 of the slice
-        f32x4 p1[1][1], p2[1][1], p3[1][1], p4[1][1];
-        zero_acc(p1);
-        zero_acc(p2);
-        zero_acc(p3);
-        zero_acc(p4);
-        wgemm<float, 1, 1, 64, false, true>(p1, sDAq, LF, sKm, LSL, m0, 16 * hc);   // dAqk · K e^{m−G}
-        wgemm<float, 1, 1, 64, true, true>(p2, sDAq, LF, sQp, LSL, m0, 16 * hc);    // dAqkᵀ · Q e^{G−m}
-        wgemm<float, 1, 1, 64, false, true>(p3, sDL, LF, sKm, LSL, m0, 16 * hc);    // dL · K e^{m−G}
-        wgemm<float, 1, 1, 64, true, true>(p4, sDL, LF, sKb, LSL, m0, 16 * hc);     // dLᵀ · β K e^{G−m}
-#pragma unroll
-        for (int j = 0; j < 1; j++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = acc_row(m0, 0, e), dd = acc_col(16 * hc, j), d = s0 + dd;
-                const float ep = sEp[r * LSL + dd];
-                const float em = ep > 0.f ? 1.f / ep : 0.f;
-                const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + d;
-                const float kv = pk[j][e], qv = pq[j][e];
-                const float dqi = scale * ep * p1[0][j][e];
-                const float dkq = scale * em * p2[0][j][e];
-                const float dkr = sB[r] * ep * p3[0][j][e];
-                const float dkc = em * p4[0][j][e];
-                rbeta[e] += kv * ep * p3[0][j][e];
-                const float dG = qv * dqi - kv * dkq + kv * dkr - kv * dkc;
-                if (r < Cn) {
-                    ((E*)a.dq)[o] = (E)(pdq[j][e] + dqi);
-                    ((E*)a.dk)[o] = (E)(pdk[j][e] + dkq + dkr + dkc);
-                }
-                sDG[r * LSL + dd] = r < Cn ? pdg[j][e] + dG : 0.f;
-            }
-        lds_barrier();
-        // in-chunk reverse cumsum of dG per channel: one thread per channel, all
-        // 64 rows (rows past the chunk hold zeros)
-        if (threadIdx.x < KSL) {
-            const int dd = threadIdx.x;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int r = C - 1; r >= 0; r--) {
-                acc += sDG[r * LSL + dd];
-                if (r < Cn) a.dg[((t0 + r) * H + h) * KD + s0 + dd] = acc;
-            }
+        // p1 = dAqk · K e^{m−G}, p2 = dAqkᵀ · Q e^{G−m}, p3 = dL · K e^{m−G},
+        // p4 = dLᵀ · β K e^{G−m}: one pass over the 64 rows of the chunk, p1 and
+        // p3 sharing their K e^{m−G} operand
+        f32x4 p1 = zero4(), p2 = zero4(), p3 = zero4(), p4 = zero4();
+#pragma unroll 4
+        for (int k0 = 0; k0 < C; k0 += Mma<float>::KS) {
+            const float bkm = ld_trans<float>(sKm, LSL, 16 * hc, k0);
+            const float bqp = ld_trans<float>(sQp, LSL, 16 * hc, k0);
+            const float bkb = ld_trans<float>(sKb, LSL, 16 * hc, k0);
+            p1 = Mma<float>::run(ld_direct<float>(sDAq, LF, m0, k0), bkm, p1);
+            p3 = Mma<float>::run(ld_direct<float>(sDL, LF, m0, k0), bkm, p3);
+            p2 = Mma<float>::run(ld_trans<float>(sDAq, LF, m0, k0), bqp, p2);
+            p4 = Mma<float>::run(ld_trans<float>(sDL, LF, m0, k0), bkb, p4);
         }
-        lds_barrier();   // the next slice is built over this one
+        float dgt[4];   // this slice's dG term (stage partial included) for rows m0 + 4g + e
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int r = acc_row(m0, 0, e);
+            const float ep = sEp[r * LSL + dd];
+            const float em = ep > 0.f ? 1.f / ep : 0.f;
+            const long o = elem_offset(e, s0);
+            const float kv = pk[e], qv = pq[e];
+            const float dqi = scale * ep * p1[e];
+            const float dkq = scale * em * p2[e];
+            const float dkr = sB[r] * ep * p3[e];
+            const float dkc = em * p4[e];
+            rbeta[e] += kv * ep * p3[e];
+            const float dG = qv * dqi - kv * dkq + kv * dkr - kv * dkc;
+            if (r < Cn) {
+                ((E*)a.dq)[o] = (E)(pdq[e] + dqi);
+                ((E*)a.dk)[o] = (E)(pdk[e] + dkq + dkr + dkc);
+            }
+            dgt[e] = r < Cn ? pdg[e] + dG : 0.f;
+        }
+        elem_issue(sn);
+        // in-chunk reverse cumsum of dG per channel: within the lane's 4 rows,
+        // across the 4 lane groups of the wave, then across the 16-row blocks
+        const float t = dgt[0] + dgt[1] + dgt[2] + dgt[3];
+        const float t1 = __shfl(t, l + 16, 64), t2 = __shfl(t, l + 32, 64), t3 = __shfl(t, l + 48, 64);
+        const float later = (g4 < 3 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 1 ? t3 : 0.f);
+        if (g4 == 0) sBT[(w & 3) * KSL + dd] = t + later;
+        lds_barrier();
+        float acc = later;
+        for (int b = (w & 3) + 1; b < 4; b++) acc += sBT[b * KSL + dd];
+#pragma unroll
+        for (int e = 3; e >= 0; e--) {
+            acc += dgt[e];
+            if (acc_row(m0, 0, e) < Cn) a.dg[elem_offset(e, s0)] = acc;
+        }
+        if (s0 + KSL < KD) slice_store();   // every wave is past this slice's products
+        lds_barrier();
     }
     // ---- dβ = dβ_stage + row sums (over the 16 lanes of each row group)
 #pragma unroll
