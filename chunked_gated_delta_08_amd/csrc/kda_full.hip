@@ -602,8 +602,8 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
     const int g4 = l >> 4, dd = acc_col(16 * hc, 0);
 #pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
-        const int sn = min(s0 + KSL, KD - KSL);   // the next slice (the last one again at the end)
-        slice_issue(sn);
+        const int sn = s0 + KSL;   // the next slice
+        if (sn < KD) slice_issue(sn);
         // wave w: rows m0, channels 16 hc .. +15 of the slice
         // p1 = dAqk · K e^{m−G}, p2 = dAqkᵀ · Q e^{G−m}, p3 = dL · K e^{m−G},
         // p4 = dLᵀ · β K e^{G−m}: one pass over the 64 rows of the chunk, p1 and
@@ -639,7 +639,7 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
             }
             dgt[e] = r < Cn ? pdg[e] + dG : 0.f;
         }
-        elem_issue(sn);
+        if (sn < KD) elem_issue(sn);
         // in-chunk reverse cumsum of dG per channel: within the lane's 4 rows,
         // across the 4 lane groups of the wave, then across the 16-row blocks
         const float t = dgt[0] + dgt[1] + dgt[2] + dgt[3];
@@ -654,7 +654,7 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
             acc += dgt[e];
             if (acc_row(m0, 0, e) < Cn) a.dg[elem_offset(e, s0)] = acc;
         }
-        if (s0 + KSL < KD) slice_store();   // every wave is past this slice's products
+        if (sn < KD) slice_store();   // every wave is past this slice's products
         lds_barrier();
     }
     // ---- dβ = dβ_stage + row sums (over the 16 lanes of each row group)
