@@ -95,67 +95,93 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
     const float* G = a.gcum;
     const int ref = (Cn - 1) / 2;
 
-    // ---- stage K, Q, V (rows past the chunk zero), β, m
-    for (int idx = threadIdx.x; idx < C * KD / EPE; idx += NT) {
-        const int r = idx / (KD / EPE), c = (idx % (KD / EPE)) * EPE, rc = min(r, Cn - 1);
-        const kvec<E, EPE> xk = *(const kvec<E, EPE>*)(k + ((t0 + rc) * H + h) * KD + c);
-        const kvec<E, EPE> xq = *(const kvec<E, EPE>*)(q + ((t0 + rc) * H + h) * KD + c);
+    // ---- every load of the staging phase, then slice 0's G rows, in this order
+    constexpr int NKV = C * KD / EPE / NT, NVV = C * VD / EPE / NT;   // K / Q and V vectors per thread
+    static_assert(C * KD / EPE % NT == 0 && C * VD / EPE % NT == 0 && C * KSL / 4 == NT, "whole vectors per thread");
+    const float bb = (float)((const E*)a.beta)[(t0 + min((int)threadIdx.x & (C - 1), Cn - 1)) * H + h];
+    const float mm = G[((t0 + ref) * H + h) * KD + min((int)threadIdx.x, KD - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    kvec<E, EPE> xk[NKV], xq[NKV], xv[NVV];
+#pragma unroll
+    for (int i = 0; i < NKV; i++) {
+        const int idx = threadIdx.x + NT * i, r = idx / (KD / EPE), c = idx % (KD / EPE) * EPE;
+        const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + c;
+        xk[i] = *(const kvec<E, EPE>*)(k + o);
+        xq[i] = *(const kvec<E, EPE>*)(q + o);
+    }
+#pragma unroll
+    for (int i = 0; i < NVV; i++) {
+        const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
+        xv[i] = *(const kvec<E, EPE>*)(v + ((t0 + min(r, Cn - 1)) * H + h) * VD + c);
+    }
+    // One slice vector per thread: row sr, channels sdd .. +3 of the slice;
+    // G of that row and of the chunk's last row.
+    const int sr = threadIdx.x / (KSL / 4), sdd = threadIdx.x % (KSL / 4) * 4;
+    const long so = ((t0 + min(sr, Cn - 1)) * H + h) * KD + sdd, co = ((t0 + Cn - 1) * H + h) * KD + sdd;
+    f32x4 xg = *(const f32x4*)(G + so), xc = *(const f32x4*)(G + co);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NKV; i++) {
+        const int idx = threadIdx.x + NT * i, r = idx / (KD / EPE), c = idx % (KD / EPE) * EPE;
         kvec<S, EPE> yk, yq;
 #pragma unroll
         for (int e = 0; e < EPE; e++) {
-            yk[e] = r < Cn ? (S)(float)xk[e] : (S)0.f;
-            yq[e] = r < Cn ? (S)(float)xq[e] : (S)0.f;
+            yk[e] = r < Cn ? (S)(float)xk[i][e] : (S)0.f;
+            yq[e] = r < Cn ? (S)(float)xq[i][e] : (S)0.f;
         }
         *(kvec<S, EPE>*)(sK + r * LK + c) = yk;
         *(kvec<S, EPE>*)(sQ + r * LK + c) = yq;
     }
-    for (int idx = threadIdx.x; idx < C * VD / EPE; idx += NT) {
-        const int r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE, rc = min(r, Cn - 1);
-        const kvec<E, EPE> xv = *(const kvec<E, EPE>*)(v + ((t0 + rc) * H + h) * VD + c);
+#pragma unroll
+    for (int i = 0; i < NVV; i++) {
+        const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
         kvec<S, EPE> yv;
 #pragma unroll
-        for (int e = 0; e < EPE; e++) yv[e] = r < Cn ? (S)(float)xv[e] : (S)0.f;
+        for (int e = 0; e < EPE; e++) yv[e] = r < Cn ? (S)(float)xv[i][e] : (S)0.f;
         *(kvec<S, EPE>*)(sV + r * LV + c) = yv;
     }
-    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? (float)((const E*)a.beta)[(t0 + threadIdx.x) * H + h] : 0.f;
-    for (int d = threadIdx.x; d < KD; d += NT) sM[d] = G[((t0 + ref) * H + h) * KD + d];
+    if (threadIdx.x < C) sB[threadIdx.x] = (int)threadIdx.x < Cn ? bb : 0.f;
+    if (threadIdx.x < KD) sM[threadIdx.x] = mm;
     lds_barrier();
 
-    // ---- K̃ = K ⊙ e^{G_C − G},  Qg = scale Q ⊙ e^G   (straight to memory)
-    {
-        S* KTo = (S*)a.KT + unit * C * KD;
-        S* QGo = (S*)a.QG + unit * C * KD;
-        for (int idx = threadIdx.x; idx < C * KD; idx += NT) {
-            const int r = idx / KD, d = idx % KD;
-            const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-            const float gC = G[((t0 + Cn - 1) * H + h) * KD + d];
-            KTo[idx] = (S)((float)sK[r * LK + d] * __expf(gC - g));
-            QGo[idx] = (S)(scale * (float)sQ[r * LK + d] * __expf(g));
-        }
-    }
-
-    // ---- Akk, Aqk over 32-channel slices (fp32 MFMA)   (wave w: rows m0, columns 32 hc .. +31)
+    // ---- per 32-channel slice: the fp32 operands K e^{G−m}, K e^{m−G}, Q e^{G−m}
+    //      of Akk and Aqk; K̃ = K ⊙ e^{G_C − G} and Qg = scale Q ⊙ e^G (straight
+    //      to memory); K ⊙ γ over Q's buffer (each thread rewrites only the Q
+    //      elements it has just read).  Akk, Aqk accumulate in fp32 MFMA
+    //      (wave w: rows m0, columns 32 hc .. +31).
     f32x4 akk[1][2], aqk[1][2];
     zero_acc(akk);
     zero_acc(aqk);
+    S* KTo = (S*)a.KT + unit * C * KD + sr * KD + sdd;
+    S* QGo = (S*)a.QG + unit * C * KD + sr * KD + sdd;
 #pragma unroll 1
     for (int s0 = 0; s0 < KD; s0 += KSL) {
-        for (int idx = threadIdx.x; idx < C * KSL / 4; idx += NT) {   // 4 channels per step
-            const int r = idx / (KSL / 4), dd = (idx % (KSL / 4)) * 4, d = s0 + dd;
-            const f32x4 g = *(const f32x4*)(G + ((t0 + min(r, Cn - 1)) * H + h) * KD + d);
+        {
+            const int d = s0 + sdd;
             const f32x4 m = *(const f32x4*)(sM + d);
-            const kvec<S, 4> kv = *(const kvec<S, 4>*)(sK + r * LK + d), qv = *(const kvec<S, 4>*)(sQ + r * LK + d);
+            const kvec<S, 4> kv = *(const kvec<S, 4>*)(sK + sr * LK + d), qv = *(const kvec<S, 4>*)(sQ + sr * LK + d);
             f32x4 kp, km, qp;
+            kvec<S, 4> kt, qg, kg;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float ep = __expf(g[e] - m[e]), em = __expf(m[e] - g[e]);
+                const float ep = __expf(xg[e] - m[e]), em = __expf(m[e] - xg[e]), eg = __expf(xg[e]);
                 kp[e] = (float)kv[e] * ep;
                 km[e] = (float)kv[e] * em;
                 qp[e] = (float)qv[e] * ep;
+                kt[e] = (S)((float)kv[e] * __expf(xc[e] - xg[e]));
+                qg[e] = (S)(scale * (float)qv[e] * eg);
+                kg[e] = (S)((float)kv[e] * eg);
             }
-            *(f32x4*)(sKp + r * LSL + dd) = kp;
-            *(f32x4*)(sKm + r * LSL + dd) = km;
-            *(f32x4*)(sQp + r * LSL + dd) = qp;
+            *(f32x4*)(sKp + sr * LSL + sdd) = kp;
+            *(f32x4*)(sKm + sr * LSL + sdd) = km;
+            *(f32x4*)(sQp + sr * LSL + sdd) = qp;
+            *(kvec<S, 4>*)(sQ + sr * LK + d) = kg;
+            *(kvec<S, 4>*)(KTo + s0) = kt;
+            *(kvec<S, 4>*)(QGo + s0) = qg;
+        }
+        if (s0 + KSL < KD) {   // the next slice's G rows, in flight during the products
+            xg = *(const f32x4*)(G + so + s0 + KSL);
+            xc = *(const f32x4*)(G + co + s0 + KSL);
         }
         lds_barrier();
         wgemm<float, 1, 2, KSL, false, false>(akk, sKp, LSL, sKm, LSL, m0, 32 * hc);
@@ -177,18 +203,12 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
     lds_barrier();
     tri_inverse64<LL, NT>(sL, sAf, sT);
 
-    // ---- A diag(β) as an MFMA operand; A itself to memory (input type, [B*T, H, 64]);
-    //      K ⊙ γ over Q's buffer
+    // ---- A diag(β) as an MFMA operand; A itself to memory (input type, [B*T, H, 64])
     for (int idx = threadIdx.x; idx < C * C; idx += NT) {
         const int r = idx / C, c = idx % C;
         const float x = sAf[r * LL + c];
         sAb[r * LA + c] = (S)(x * sB[c]);
         if (r < Cn) ((E*)a.A)[((t0 + r) * H + h) * C + c] = (E)x;
-    }
-    for (int idx = threadIdx.x; idx < C * KD; idx += NT) {
-        const int r = idx / KD, d = idx % KD;
-        const float g = G[((t0 + min(r, Cn - 1)) * H + h) * KD + d];
-        sQ[r * LK + d] = (S)((float)sK[r * LK + d] * __expf(g));
     }
     lds_barrier();
     // ---- W = A diag(β) (K ⊙ γ),  U = A diag(β) V   (wave w: rows m0, column half hc)
