@@ -40,6 +40,8 @@ template <class S> constexpr int kfpad() { return sizeof(S) == 2 ? 8 : 4; }
 
 // fp32 slices of 32 channels: [64 rows][KSL + 4]
 constexpr int KSL = 32, LSL = KSL + 4;
+// value columns per state-scan workgroup
+constexpr int KVS = 32;
 
 // LDS carve-up of the KDA WY-factor kernel.
 template <class S, int KD, int VD>
@@ -245,7 +247,7 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
 }
 
 // ---------------------------------------------------------------- state scans
-// One workgroup (4 waves) per (sequence, head, 64-column value slice,
+// One workgroup (4 waves) per (sequence, head, KVS-column value slice,
 // direction); both directions run in one launch (the reverse scan needs
 // nothing the forward one writes).  The K x 64 fp32 state slice lives in MFMA
 // accumulators (wave w: state rows (KD/4) w ..), a 16-bit copy of it in LDS is
@@ -255,7 +257,7 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
 //             dV_new (input type) and dh0
 template <class S, int KD>
 struct KScanCfg {
-    static constexpr int C = 64, LK = KD + kfpad<S>(), LS = 64 + kfpad<S>(), LA = 64 + kfpad<S>();
+    static constexpr int C = 64, LK = KD + kfpad<S>(), LS = KVS + kfpad<S>(), LA = 64 + kfpad<S>();
     static constexpr size_t oW = 0;                                     // W [64][LK]
     static constexpr size_t oKT = oW + (size_t)C * LK * sizeof(S);      // K̃ [64][LK]
     static constexpr size_t oQG = oKT + (size_t)C * LK * sizeof(S);     // Qg [64][LK] (reverse)
@@ -273,6 +275,7 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
     using Cf = KScanCfg<S, KD>;
     constexpr int C = 64, NT = 256, LK = Cf::LK, LS = Cf::LS, LA = Cf::LA;
     constexpr int TMH = KD / 64;   // 16-row tiles of state rows per wave
+    constexpr int NJ = KVS / 16;   // 16-column tiles of the value slice
     constexpr int EPS = 16 / (int)sizeof(S);
     extern __shared__ __align__(16) unsigned char smem[];
     S* sW = (S*)(smem + Cf::oW);
@@ -284,23 +287,23 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
     S* sAq = (S*)(smem + Cf::oAq);
     float* sGC = (float*)(smem + Cf::oGC);
 
-    const int nvs = VD / 64;
+    const int nvs = VD / KVS;
     const int vs = job % nvs, h = (job / nvs) % H, n = job / nvs / H;
     if (n >= nseq) return;
     const int w = wave_id();
     const int m0 = (KD / 4) * w;      // this wave's state rows
-    const int vc0 = 64 * vs;          // this workgroup's value columns
+    const int vc0 = KVS * vs;         // this workgroup's value columns
     const int c_first = a.seq_chunk0[n], c_end = a.seq_chunk0[n + 1];
     const size_t KV = (size_t)KD * VD;
 
     // state slice: rows m0 + 16 i + 4 g + e, columns 16 j + r
-    f32x4 st[TMH][4];
+    f32x4 st[TMH][NJ];
     {
         const float* init = REV ? a.dht : a.h0;
 #pragma unroll
         for (int i = 0; i < TMH; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < NJ; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     st[i][j][e] = init ? init[((size_t)n * H + h) * KV + (size_t)acc_row(m0, i, e) * VD + vc0 +
@@ -312,8 +315,8 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
     // current one is computed
     constexpr int EPE = 16 / (int)sizeof(E);
     static_assert(EPE == EPS, "input and operand types share a width");
-    static_assert(C * KD / EPS % NT == 0 && C * 64 / EPS % NT == 0 && C * C / EPS % NT == 0, "whole vectors");
-    constexpr int NKW = C * KD / EPS / NT, NXS = C * 64 / EPS / NT, NAQ = C * C / EPS / NT;
+    static_assert(C * KD / EPS % NT == 0 && C * KVS / EPS % NT == 0 && C * C / EPS % NT == 0, "whole vectors");
+    constexpr int NKW = C * KD / EPS / NT, NXS = C * KVS / EPS / NT, NAQ = C * C / EPS / NT;
     kvec<S, EPS> rW[NKW], rKT[NKW], rQG[REV ? NKW : 1], rU[REV ? 1 : NXS], rAq[REV ? NAQ : 1];
     kvec<E, EPE> rO[REV ? NXS : 1];
     float rgc = 0.f;
@@ -332,7 +335,7 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
         }
 #pragma unroll
         for (int i = 0; i < NXS; i++) {
-            const int idx = threadIdx.x + NT * i, r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
+            const int idx = threadIdx.x + NT * i, r = idx / (KVS / EPS), c = (idx % (KVS / EPS)) * EPS;
             if constexpr (REV)   // dO slice; rows past the chunk read its last row (zeroed when staged)
                 rO[i] = *(const kvec<E, EPE>*)((const E*)a.dO + ((t0 + min(r, Cn - 1)) * H + h) * VD + vc0 + c);
             else
@@ -361,7 +364,7 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
         }
 #pragma unroll
         for (int i = 0; i < NXS; i++) {
-            const int idx = threadIdx.x + NT * i, r = idx / (64 / EPS), c = (idx % (64 / EPS)) * EPS;
+            const int idx = threadIdx.x + NT * i, r = idx / (KVS / EPS), c = (idx % (KVS / EPS)) * EPS;
             kvec<S, EPS> x;
             if constexpr (REV) {
 #pragma unroll
@@ -379,13 +382,13 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
             }
         }
         if (threadIdx.x < KD) sGC[threadIdx.x] = __expf(rgc);
-        // state copy as [KD][64] and the fp32 state of this chunk boundary to memory
+        // state copy as [KD][KVS] and the fp32 state of this chunk boundary to memory
         {
             float* so = (REV ? a.dhs : a.hs) + unit * KV;
 #pragma unroll
             for (int i = 0; i < TMH; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < NJ; j++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int r = acc_row(m0, i, e), c = acc_col(0, j);
@@ -395,19 +398,19 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
         }
         lds_barrier();
         if (it + 1 < nch) issue(it + 1);   // the next chunk's loads fly during this one's products
-        // ---- V_new = U − W h   or   dV_new = Aqkᵀ dO + K̃ dh      (wave w: rows 16w, 64 columns)
+        // ---- V_new = U − W h   or   dV_new = Aqkᵀ dO + K̃ dh      (wave w: rows 16w, KVS columns)
         {
-            f32x4 x[1][4];
+            f32x4 x[1][NJ];
             zero_acc(x);
             if (REV) {
-                wgemm<S, 1, 4, 64, true, true>(x, sAq, LA, sX, LS, 16 * w, 0);
-                wgemm<S, 1, 4, KD, false, true>(x, sKT, LK, sH, LS, 16 * w, 0);
+                wgemm<S, 1, NJ, 64, true, true>(x, sAq, LA, sX, LS, 16 * w, 0);
+                wgemm<S, 1, NJ, KD, false, true>(x, sKT, LK, sH, LS, 16 * w, 0);
             } else {
-                wgemm<S, 1, 4, KD, false, true>(x, sW, LK, sH, LS, 16 * w, 0);
+                wgemm<S, 1, NJ, KD, false, true>(x, sW, LK, sH, LS, 16 * w, 0);
             }
             E* out = (E*)(REV ? a.dvn : a.vn);
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < NJ; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = acc_row(16 * w, 0, e), c = acc_col(0, j);
@@ -425,19 +428,19 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
             for (int e = 0; e < 4; e++) {
                 const float gc = sGC[acc_row(m0, i, e)];
 #pragma unroll
-                for (int j = 0; j < 4; j++) st[i][j][e] *= gc;
+                for (int j = 0; j < NJ; j++) st[i][j][e] *= gc;
             }
         if (REV) {
-            wgemm<S, TMH, 4, 64, true, true>(st, sQG, LK, sX, LS, m0, 0);
-            f32x4 t[TMH][4];
+            wgemm<S, TMH, NJ, 64, true, true>(st, sQG, LK, sX, LS, m0, 0);
+            f32x4 t[TMH][NJ];
             zero_acc(t);
-            wgemm<S, TMH, 4, 64, true, true>(t, sW, LK, sVn, LS, m0, 0);
+            wgemm<S, TMH, NJ, 64, true, true>(t, sW, LK, sVn, LS, m0, 0);
 #pragma unroll
             for (int i = 0; i < TMH; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) st[i][j] -= t[i][j];
+                for (int j = 0; j < NJ; j++) st[i][j] -= t[i][j];
         } else {
-            wgemm<S, TMH, 4, 64, true, true>(st, sKT, LK, sVn, LS, m0, 0);
+            wgemm<S, TMH, NJ, 64, true, true>(st, sKT, LK, sVn, LS, m0, 0);
         }
         lds_barrier();   // the next chunk is staged over this one's LDS
     }
@@ -445,7 +448,7 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
 #pragma unroll
         for (int i = 0; i < TMH; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < NJ; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
                     a.dh0[((size_t)n * H + h) * KV + (size_t)acc_row(m0, i, e) * VD + vc0 + acc_col(0, j)] =
@@ -712,7 +715,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
     if ((e = mark(1)) != hipSuccess) return e;
     {
         const int sm = (int)KScanCfg<S, KD>::smem;
-        const int jobs = p.N * p.HV * (VD / 64);
+        const int jobs = p.N * p.HV * (VD / KVS);
         auto kern = kda_scan_kernel<E, S, KD, VD>;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
