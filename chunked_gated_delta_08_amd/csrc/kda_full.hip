@@ -456,11 +456,17 @@ __device__ __forceinline__ void kda_scan_body(const KdaFullArgs& a, int H, int n
     }
 }
 
-// blocks [0, jobs): forward scans; [jobs, 2 jobs): reverse scans
+// blocks [0, jobs): forward scans; [jobs, 2 jobs): reverse scans.  Workgroups
+// are dispatched round-robin over the 8 XCDs, so when jobs is a multiple of 8
+// block b runs job (b % 8) jobs/8 + b/8: the value slices of one head then share
+// an XCD and its L2, and read that head's W, K̃, Qg and Aqk from HBM once.
 template <class E, class S, int KD, int VD>
 __global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int nseq, int jobs) {
-    if ((int)blockIdx.x < jobs) kda_scan_body<E, S, KD, VD, false>(a, H, nseq, blockIdx.x);
-    else kda_scan_body<E, S, KD, VD, true>(a, H, nseq, (int)blockIdx.x - jobs);
+    const bool rev = (int)blockIdx.x >= jobs;
+    int b = (int)blockIdx.x - (rev ? jobs : 0);
+    if (jobs % 8 == 0) b = b % 8 * (jobs / 8) + b / 8;
+    if (!rev) kda_scan_body<E, S, KD, VD, false>(a, H, nseq, b);
+    else kda_scan_body<E, S, KD, VD, true>(a, H, nseq, b);
 }
 
 // ---------------------------------------------------------------- intra-chunk part
