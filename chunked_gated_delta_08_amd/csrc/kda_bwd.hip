@@ -254,6 +254,29 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
 #pragma unroll
             for (int e = 0; e < 4; e++) sDW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = (E)(-dwa[i][j][e]);
     lds_barrier();
+    // ---- this lane's elements of g, k, q (key tiles) and v (value tiles), issued
+    //      before the products that precede their use (rows past the chunk read
+    //      its last row and are not used)
+    constexpr int TNV = VD / 64;
+    const int n0v = (VD / 4) * (w >> 1);
+    float pg[2][TN][4], pk[2][TN][4], pq[2][TN][4], pv[2][TNV][4], pgl[TN];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int rc = min(acc_row(m0, i, e), Cn - 1);
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const long o = gidx(rc, acc_col(n0k, j));
+                pg[i][j][e] = a.g[o];
+                pk[i][j][e] = (float)k[o];
+                pq[i][j][e] = (float)q[o];
+            }
+#pragma unroll
+            for (int j = 0; j < TNV; j++) pv[i][j][e] = (float)v[((t0 + rc) * H + hh) * VD + acc_col(n0v, j)];
+        }
+#pragma unroll
+    for (int j = 0; j < TN; j++) pgl[j] = a.g[gidx(Cn - 1, acc_col(n0k, j))];
     // ---- dks_acc = V_new dhᵀ ; AdW = Aᵀ dw ; AdV = Aᵀ dv (V-tiles)
     f32x4 dka[2][TN], adw[2][TN];
     zero_acc(dka);
@@ -267,8 +290,6 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
 #pragma unroll
         for (int e = 0; e < 4; e++) dbr[i][e] = 0.f;
     {
-        constexpr int TNV = VD / 64;
-        const int n0v = (VD / 4) * (w >> 1);
         f32x4 adv[2][TNV];
         zero_acc(adv);
         wgemm<E, 2, TNV, 64, true, true>(adv, sA, LA, sDV, LV, m0, n0v);
@@ -282,7 +303,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
                     if (rr < Cn) {
                         const long o = ((t0 + rr) * H + hh) * VD + cc;
                         ((E*)a.dv_out)[o] = (E)(sB[rr] * adv[i][j][e]);
-                        dbr[i][e] += adv[i][j][e] * (float)v[o];
+                        dbr[i][e] += adv[i][j][e] * pv[i][j][e];
                     }
                 }
     }
@@ -301,9 +322,9 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
                 dgl[i][j][e] = 0.f;
                 if (rr < Cn) {
                     const long o = gidx(rr, cc);
-                    const float gg = a.g[o], gm = __expf(gg);
-                    const float glast = a.g[gidx(Cn - 1, cc)];
-                    const float kk = (float)k[o], qq = (float)q[o];
+                    const float gg = pg[i][j][e], gm = __expf(gg);
+                    const float glast = pgl[j];
+                    const float kk = pk[i][j][e], qq = pq[i][j][e];
                     const float dqv = scale * dqa[i][j][e] * gm;
                     const float dks = dka[i][j][e] * __expf(glast - gg);
                     const float bgw = sB[rr] * gm * adw[i][j][e];
@@ -332,7 +353,7 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
                 const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
                 if (rr < Cn) {
                     float x = dgl[i][j][e];
-                    if (rr == Cn - 1) x += sCS[cc] + sCS[KD + cc] + __expf(a.g[gidx(rr, cc)]) * sHD[cc];
+                    if (rr == Cn - 1) x += sCS[cc] + sCS[KD + cc] + __expf(pg[i][j][e]) * sHD[cc];
                     a.dg[gidx(rr, cc)] = x;
                 }
             }
