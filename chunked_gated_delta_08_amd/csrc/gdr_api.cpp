@@ -18,10 +18,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ceil(n / L) segments (at least one).  Without segments the scans take one
 // workgroup per (sequence, value head, direction) and as many sequential
 // steps as the longest sequence has chunks; with segments there are three
-// launches (local scans and transfer matrices: about 3 jobs per segment and
-// value head; the sequential combine: one step per segment; the scans proper:
-// 2 jobs per segment and value head).  L is chosen to minimise the estimated
-// number of sequential chunk steps with one workgroup per CU on 256 CUs.
+// launches (local scans and transfer matrices: 2 workgroups per segment and
+// value head of every sequence that has more than one segment; the sequential
+// combine: one step per segment; the scans proper: 2 workgroups per segment
+// and value head).  L is chosen to minimise the estimated time in units of one
+// chunk step of a round of workgroups (one workgroup per CU on 256 CUs); a
+// combine step counts 1.4 such units.  That weight, and counting the local
+// scans by workgroups, fit the measured call times at T = 32768 with 16 and 32
+// value heads and at the 12-sequence varlen workload (K = V = 128, bf16) over
+// L = 8 .. 128.
 void plan_segments(const gdr_problem* p, Problem* q) {
     const int nseq = q->N;
     auto nch = [&](int n) -> int64_t {
@@ -34,16 +39,16 @@ void plan_segments(const gdr_problem* p, Problem* q) {
     struct Plan { int L; int64_t NS; int maxS; double cost; };
     auto eval = [&](int64_t L) {
         Plan pl{(int)L, 0, 1, 0.0};
-        int64_t multi = 0;
+        int64_t multi = 0;   // segments of the sequences cut into more than one
         for (int n = 0; n < nseq; n++) {
             const int64_t c = nch(n), S = c > L ? (c + L - 1) / L : 1;
             pl.NS += S;
-            if (S > 1) multi += 3 * S - 2;
+            if (S > 1) multi += S;
             if (S > pl.maxS) pl.maxS = (int)S;
         }
         const double Ls = (double)(L < maxn ? L : maxn);
         pl.cost = rounds(2 * q->HV * pl.NS) * Ls;
-        if (pl.maxS > 1) pl.cost += rounds(q->HV * multi) * Ls + pl.maxS + 3.0;
+        if (pl.maxS > 1) pl.cost += rounds(2 * q->HV * multi) * Ls + 1.4 * pl.maxS;
         return pl;
     };
     Plan best = eval(maxn > 0 ? maxn : 1);   // no segments
