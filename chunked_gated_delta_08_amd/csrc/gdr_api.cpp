@@ -21,13 +21,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // launches (local scans and transfer matrices: 2 workgroups per segment and
 // value head of every sequence that has more than one segment; the sequential
 // combine: one step per segment; the scans proper: 2 workgroups per segment
-// and value head).  L is chosen to minimise the estimated time in units of one
+// and value head).  `dirs` is 2 for the backward and 1 for the forward calls,
+// which scan in one direction only (half the workgroups of each launch).  L is chosen to minimise the estimated time in units of one
 // chunk step of a round of workgroups (one workgroup per CU on 256 CUs); a
 // combine step counts 1.4 such units.  That weight, and counting the local
 // scans by workgroups, fit the measured call times at T = 32768 with 16 and 32
 // value heads and at the 12-sequence varlen workload (K = V = 128, bf16) over
 // L = 8 .. 128.
-void plan_segments(const gdr_problem* p, Problem* q) {
+void plan_segments(const gdr_problem* p, Problem* q, int dirs) {
     const int nseq = q->N;
     auto nch = [&](int n) -> int64_t {
         const int64_t len = p->cu_seqlens ? (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] : p->T;
@@ -47,8 +48,8 @@ void plan_segments(const gdr_problem* p, Problem* q) {
             if (S > pl.maxS) pl.maxS = (int)S;
         }
         const double Ls = (double)(L < maxn ? L : maxn);
-        pl.cost = rounds(2 * q->HV * pl.NS) * Ls;
-        if (pl.maxS > 1) pl.cost += rounds(2 * q->HV * multi) * Ls + 1.4 * pl.maxS;
+        pl.cost = rounds(dirs * q->HV * pl.NS) * Ls;
+        if (pl.maxS > 1) pl.cost += rounds(dirs * q->HV * multi) * Ls + 1.4 * pl.maxS;
         return pl;
     };
     Plan best = eval(maxn > 0 ? maxn : 1);   // no segments
@@ -69,7 +70,7 @@ void plan_segments(const gdr_problem* p, Problem* q) {
 size_t elem_size(int dtype) { return dtype == GDR_F32 ? 4 : 2; }
 
 // Host-side checks shared by every entry point.  Fills `q` on success.
-int check_problem(const gdr_problem* p, Problem* q) {
+int check_problem(const gdr_problem* p, Problem* q, int dirs = 2) {
     if (!p) return GDR_ERR_INVALID;
     if (p->B < 1 || p->T < 0 || p->HK < 1 || p->HV < 1 || p->K < 1 || p->V < 1 || p->BT < 1) return GDR_ERR_INVALID;
     if (p->HV % p->HK != 0) return GDR_ERR_INVALID;
@@ -96,7 +97,7 @@ int check_problem(const gdr_problem* p, Problem* q) {
     q->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
     q->dtype = p->dtype;
     q->cu = p->cu_seqlens;
-    plan_segments(p, q);
+    plan_segments(p, q, dirs);
     return GDR_OK;
 }
 
@@ -221,16 +222,18 @@ int64_t gdr_num_chunks(const gdr_problem* p) {
 }
 
 size_t gdr_workspace_size(const gdr_problem* p) {
-    Problem q;
-    if (check_problem(p, &q) != GDR_OK) return 0;
-    return gdr::plan_workspace(q).total;
+    // large enough for the segment plans of both the forward and the backward calls
+    Problem q1, q2;
+    if (check_problem(p, &q1, 1) != GDR_OK || check_problem(p, &q2, 2) != GDR_OK) return 0;
+    const size_t a = gdr::plan_workspace(q1).total, b = gdr::plan_workspace(q2).total;
+    return a > b ? a : b;
 }
 
 int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const float* g_cum, const void* beta,
                    const float* h0, float* h_out, void* v_new_out, float* ht_out, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
     Problem q;
-    int st = check_problem(p, &q);
+    int st = check_problem(p, &q, 1);
     if (st != GDR_OK) return st;
     if ((st = check_supported(q)) != GDR_OK) return st;
     if (q.NT > 0 && (!k || !v || !g_cum || !beta || !h_out)) return GDR_ERR_INVALID;
@@ -272,7 +275,7 @@ int gdr_chunk_fwd_events(const gdr_problem* p, const void* qp, const void* k, co
                          const void* beta, const float* h0, void* o, float* ht_out, void* ws, size_t ws_bytes,
                          hipStream_t stream, hipEvent_t* ev) {
     Problem q;
-    int st = check_problem(p, &q);
+    int st = check_problem(p, &q, 1);
     if (st != GDR_OK) return st;
     if ((st = check_supported(q)) != GDR_OK) return st;
     if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !o)) return GDR_ERR_INVALID;
