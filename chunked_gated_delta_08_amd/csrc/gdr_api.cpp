@@ -222,7 +222,8 @@ int64_t gdr_num_chunks(const gdr_problem* p) {
 }
 
 size_t gdr_workspace_size(const gdr_problem* p) {
-    // large enough for the segment plans of both the forward and the backward calls
+    // large enough for the segment plans of both the forward and the backward
+    // calls; every GDN entry point asks for at least this much
     Problem q1, q2;
     if (check_problem(p, &q1, 1) != GDR_OK || check_problem(p, &q2, 2) != GDR_OK) return 0;
     const size_t a = gdr::plan_workspace(q1).total, b = gdr::plan_workspace(q2).total;
@@ -238,7 +239,7 @@ int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const flo
     if ((st = check_supported(q)) != GDR_OK) return st;
     if (q.NT > 0 && (!k || !v || !g_cum || !beta || !h_out)) return GDR_ERR_INVALID;
     const WsPlan w = gdr::plan_workspace(q);
-    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    if (!ws || ws_bytes < gdr_workspace_size(p)) return GDR_ERR_WORKSPACE;
     char* base = (char*)ws;
     auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
@@ -280,7 +281,7 @@ int gdr_chunk_fwd_events(const gdr_problem* p, const void* qp, const void* k, co
     if ((st = check_supported(q)) != GDR_OK) return st;
     if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !o)) return GDR_ERR_INVALID;
     const WsPlan w = gdr::plan_workspace(q);
-    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    if (!ws || ws_bytes < gdr_workspace_size(p)) return GDR_ERR_WORKSPACE;
     char* base = (char*)ws;
     auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
@@ -330,7 +331,7 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     if (q.NT > 0 && (!qp || !k || !v || !g_cum || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
         return GDR_ERR_INVALID;
     const WsPlan w = gdr::plan_workspace(q);
-    if (!ws || ws_bytes < w.total) return GDR_ERR_WORKSPACE;
+    if (!ws || ws_bytes < gdr_workspace_size(p)) return GDR_ERR_WORKSPACE;
     char* base = (char*)ws;
     auto* info = (gdr::ChunkInfo*)(base + w.chunk_info);
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);

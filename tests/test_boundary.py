@@ -128,6 +128,17 @@ def test_fwd_validation(B):
         assert _fwd(B, p, **{missing: None}) == -1, missing
 
 
+def test_workspace_covers_both_plans(B):
+    # At T = 32768 with 16 value heads the forward and the backward calls cut the
+    # state scans into segments of different lengths; one workspace of
+    # gdr_workspace_size() serves both, and each call rejects anything smaller.
+    p = _prob(B, T=32768, HK=16, HV=16, K=128, V=128)
+    n = B.workspace_size(p)
+    assert n > 0
+    assert _bwd(B, p, ws_bytes=n - 1) == -3
+    assert _fwd(B, p, ws_bytes=n - 1) == -3
+
+
 def test_gate_cumsum_validation(B):
     p = _prob(B)
     assert B.lib.gdr_gate_cumsum(ctypes.byref(p), None, FAKE, None) == -1
