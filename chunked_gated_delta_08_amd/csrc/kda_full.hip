@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
 // ---------------------------------------------------------------- state scans
 // One workgroup (4 waves) per (sequence, head, KVS-column value slice,
 // direction); both directions run in one launch (the reverse scan needs
-// nothing the forward one writes).  The K x 64 fp32 state slice lives in MFMA
+// nothing the forward one writes).  The K x KVS fp32 state slice lives in MFMA
 // accumulators (wave w: state rows (KD/4) w ..), a 16-bit copy of it in LDS is
 // the operand of the per-chunk products.
 //   forward:  stores h[c] (fp32 [NT,H,K,V]) and V_new (input type)
