@@ -515,15 +515,15 @@ __global__ void __launch_bounds__(512) bigdn_phase_c_kernel(const bf16* __restri
             const bf16x8 raw = pQ[p];
             const float r = pR[p];
             if constexpr (BWD) rD[p] = pD[p];
-            if (ok[p]) {
-                const size_t ro = ((size_t)f * S + s) * D + 8 * c;
-                ld8(cosT + ro, cs[p]);
-                ld8(sinT + ro, sn[p]);
-            } else {
+            {   // rows past the frame read its last row (no branch around the loads)
+                const size_t ro = ((size_t)f * S + min(s, S - 1)) * D + 8 * c;
+                float tc[8], ts[8];
+                ld8(cosT + ro, tc);
+                ld8(sinT + ro, ts);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    cs[p][i] = 0.f;
-                    sn[p][i] = 0.f;
+                    cs[p][i] = ok[p] ? tc[i] : 0.f;
+                    sn[p][i] = ok[p] ? ts[i] : 0.f;
                 }
             }
             float y[8];
@@ -866,15 +866,15 @@ __global__ void __launch_bounds__(512) bigdn_abar_kernel(const bf16* __restrict_
             const bf16x8 raw = pK[p], rv = pV[p];
             const float r = pR[p], bb = pB[p];
             float cs[8], sn[8];
-            if (ok[p]) {
-                const size_t ro = ((size_t)f * S + s) * D + 8 * c;
-                ld8(cosT + ro, cs);
-                ld8(sinT + ro, sn);
-            } else {
+            {   // rows past the frame read its last row (no branch around the loads)
+                const size_t ro = ((size_t)f * S + min(s, S - 1)) * D + 8 * c;
+                float tc[8], ts[8];
+                ld8(cosT + ro, tc);
+                ld8(sinT + ro, ts);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
-                    cs[i] = 0.f;
-                    sn[i] = 0.f;
+                    cs[i] = ok[p] ? tc[i] : 0.f;
+                    sn[i] = ok[p] ? ts[i] : 0.f;
                 }
             }
             float u[8], y[8];
