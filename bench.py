@@ -18,6 +18,17 @@ scan, the output kernel), on the same inputs.  With --path kda a step is one
 kda_chunk_bwd_full call (the full KDA backward, per-channel gate) at B=1,
 T=2048, H=32, K=V=128, BT=64, fp16, dht present.
 
+With --path kda_stage a step is one kda_chunk_bwd call (the KDA WY backward
+stage alone) at B=1, T=2048, H=32, K=V=128, BT=64, fp16.
+
+Timing protocol (every path): W untimed warm-up calls, then K timed calls;
+before every call a 512 MiB scratch buffer is overwritten on the same stream
+(outside the timed region) so that no input is served from the 256 MB
+Infinity Cache; each call is bracketed by HIP events recorded by the library
+on its launch stream, and ms_per_step is the median over the K calls (p10 and
+p90 beside it).  The default bwd run also times the 32-head workload and the
+12-sequence varlen GQA workload the same way and reports them in `also`.
+
 Prints one JSON line: the headline metric (effective TFLOP/s under the FLOP
 model below, with ms per call), a roofline entry for the dominant kernel
 (timed with HIP events recorded by the library between its stages during the
@@ -154,6 +165,69 @@ def elapsed_ms(hip, a, b):
     return ms.value
 
 
+EVICT_BYTES = 512 << 20
+
+
+class Evictor:
+    """Overwrites a 512 MiB device buffer on the launch stream: run before each
+    timed call, outside its events, so the call reads its inputs from HBM."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(EVICT_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i)
+
+
+def timed_calls(torch, hip, evs, nev, call, steps, warmup, evict):
+    """W warm-ups, then K calls each preceded by the eviction write; call(i)
+    records events [nev*i, nev*i + nev) around its stages.  Returns per-call
+    ms (first to last event), per-stage ms averaged over the calls, and the
+    wall-clock ms per step of the timed loop (evictions included)."""
+    for _ in range(warmup):
+        evict()
+        call(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evict()
+        call(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per_call, stage = [], [0.0] * (nev - 1)
+    for i in range(steps):
+        e = [evs[nev * i + j] for j in range(nev)]
+        per_call.append(elapsed_ms(hip, e[0], e[-1]))
+        for j in range(nev - 1):
+            stage[j] += elapsed_ms(hip, e[j], e[j + 1]) / steps
+    return per_call, stage, wall
+
+
+def call_stats(per_call):
+    import numpy as np
+    a = np.asarray(per_call)
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4),
+            "calls": int(a.size)}
+
+
+def host_info(threads):
+    """Host cores available to this process, the CPU model, and the threads a
+    CPU leg used."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": int(threads), "host_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
     """The fp64 oracle, unchanged, on the same inputs: full passes over every
     sequence and head of the workload, repeated until at least `min_seconds`
@@ -186,9 +260,24 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
     what = {"fwd": "token recurrence (forward), OpenMP over (sequence, value head)",
             "kda": "KDA token recurrence with the hand-derived backward, OpenMP over (sequence, head)"}.get(
         path, "token recurrence with the hand-derived backward, OpenMP over (sequence, key head)")
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 {what}",
-            "seconds": round(dt, 2)}
+    res = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 {what}",
+           "seconds": round(dt, 2)}
+    res.update(host_info(threads))
+    return res
+
+
+def _traffic(kernel_name, workload, profiling):
+    """HBM bytes per launch from the committed counter summary, while the
+    kernel's sources still hash to the digest recorded there (else None)."""
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.json")
+    if not os.path.exists(tfile):
+        return None
+    with open(tfile) as fh:
+        t = json.load(fh)
+    if t.get("source_digest") != profiling.source_digest(profiling.KERNEL_SOURCES[kernel_name]):
+        return None
+    return t.get("bytes_per_launch")
 
 
 def _roofline(stage, kb, names, workload, profiling):
@@ -196,45 +285,23 @@ def _roofline(stage, kb, names, workload, profiling):
     dom = max(stage, key=stage.get)
     achieved = kb[dom] / (stage[dom] * 1e-3) / 1e9
     kernel_name = names[dom]
-    traffic = None   # HBM bytes per launch from the committed counter summary, while the sources match it
-    tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as fh:
-            t = json.load(fh)
-        if t.get("source_digest") == profiling.source_digest(profiling.KERNEL_SOURCES[kernel_name]):
-            traffic = t.get("bytes_per_launch")
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel_name,
-            "kernel_ms": round(stage[dom], 4), "algorithmic_bytes": kb[dom],
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(kernel_name, workload, profiling),
+            "kernel": kernel_name, "kernel_ms": round(stage[dom], 4), "algorithmic_bytes": kb[dom],
             "stage_ms": {k: round(v, 4) for k, v in stage.items()}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
-    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd", "kda", "bigdn"],
-                    help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward; "
-                         "kda: the full KDA backward at B=1 T=2048 H=32 K=V=128 fp16; "
-                         "bigdn: the BiGDN layer backward at B=8 F=11 S=1024 H=16 D=128 bf16")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the backward of one GPU's share); "
-              "--gpus above 1 is not supported", file=sys.stderr)
-        sys.exit(2)
+# Algorithmic matrix-core work of the gradient kernel per (chunk, value head):
+# the backward's products (12CKV + 14C^2K + 8C^2V + 4C^3 in the FLOP model)
+# minus the dh scan's 6CKV -- 18.87 MFLOP at C = 64, K = V = 128.
+def flop_grad_algorithmic(C, K, V):
+    return 6 * C * K * V + 14 * C * C * K + 8 * C * C * V + 4 * C ** 3
 
-    import torch
-    from chunked_gated_delta_08_amd import binding, profiling, workloads
 
-    if args.path == "kda":
-        return bench_kda(args, torch, binding, profiling, workloads)
-    if args.path == "bigdn":
-        return bench_bigdn(args, torch, binding, profiling, workloads)
-    fwd = args.path == "fwd"
-    cfg = dict(WORKLOADS[args.workload])
+def run_gdn(args, torch, binding, workloads, wkey, fwd, evict):
+    """Times gdr_chunk_bwd (or gate cumsum + gdr_chunk_fwd) on one workload.
+    Returns inputs, chunk lengths, per-call statistics and per-stage ms."""
+    cfg = dict(WORKLOADS[wkey])
     lengths = workloads.varlen_lengths() if cfg["lengths"] == "varlen12" else None
     inp = workloads.gdr_inputs(cfg["B"], cfg["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], dtype="bf16", seed=0,
                                lengths=lengths, dht=True)
@@ -245,8 +312,7 @@ def main():
     N = inp["N"]
     ws = torch.empty(binding.workspace_size(prob), dtype=torch.uint8, device="cuda")
     P = binding._ptr
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nev = 5 if fwd else 4
     hip, evs = hip_events(nev * args.steps)
     evsz = ctypes.sizeof(ctypes.c_void_p)
@@ -281,63 +347,128 @@ def main():
             ev = None if i is None else ctypes.byref(evs, nev * i * evsz)
             check(binding.lib.gdr_chunk_bwd_events(*args_c, ev))
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
+    per_call, st, wall = timed_calls(torch, hip, evs, nev, call, args.steps, args.warmup, evict)
     names = (["gate", "prep", "scans", "out"] if fwd else ["prep", "scans", "grad"])
-    stage = {k: 0.0 for k in names}
-    for i in range(args.steps):
-        e = [evs[nev * i + j] for j in range(nev)]
-        for j, k in enumerate(names):
-            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
+    stage = dict(zip(names, st))
     chunks = chunk_lengths(lengths, cfg["T"], cfg["B"], 64)
+    del keep, ws, out, dev
+    return {"cfg": cfg, "inp": inp, "chunks": chunks, "stats": call_stats(per_call), "stage": stage,
+            "wall_ms": wall, "T": T}
+
+
+def gdn_summary(r, fwd):
+    """Per-workload figures: median ms, effective TFLOP/s, stage times and each
+    stage's algorithmic HBM rate (and matrix-core rates for the backward's
+    chunk-parallel kernels)."""
+    cfg, chunks, stage = r["cfg"], r["chunks"], r["stage"]
     model = flop_model_fwd if fwd else flop_model
     F = sum(model(c, cfg["K"], cfg["V"]) for c in chunks) * cfg["HV"]
-    tflops = F / (ms_per_step * 1e-3) / 1e12
-    if fwd:
-        kb = kernel_bytes_fwd(cfg, chunks)
-        kn = {"gate": "gate_cumsum_kernel", "prep": "prep_kernel", "scans": "scan_kernel", "out": "fwd_out_kernel"}
-    else:
-        kb = kernel_bytes(cfg, chunks)
-        kn = {"prep": "prep_kernel", "scans": "scan_kernel", "grad": "grad_kernel"}
-    roof = _roofline(stage, kb, kn, ("fwd_" if fwd else "") + args.workload, profiling)
-    # every stage against HBM, and the chunk-parallel kernels' executed MFMA work against the bf16 peak
+    ms = r["stats"]["median_ms"]
+    kb = kernel_bytes_fwd(cfg, chunks) if fwd else kernel_bytes(cfg, chunks)
     units = len(chunks) * cfg["HV"]
-    roof["stages"] = {}
-    for k in names:
-        gbs = kb[k] / (stage[k] * 1e-3) / 1e9
-        st = {"ms": round(stage[k], 4), "algorithmic_bytes": kb[k], "hbm_gbs": round(gbs, 1),
-              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        work = {"prep": mfma_work_prep, "grad": mfma_work_grad}.get(k) if not fwd else None
-        if work is not None:
-            tf = work(cfg["K"], cfg["V"]) * units / (stage[k] * 1e-3) / 1e12
-            st.update({"mfma_tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
-        roof["stages"][k] = st
+    stages = {}
+    for k, t in stage.items():
+        gbs = kb[k] / (t * 1e-3) / 1e9
+        e = {"ms": round(t, 4), "algorithmic_bytes": kb[k], "hbm_gbs": round(gbs, 1),
+             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if not fwd and k == "prep":
+            tf = mfma_work_prep(cfg["K"], cfg["V"]) * units / (t * 1e-3) / 1e12
+            e.update({"mfma_executed_tflops": round(tf, 1), "mfma_executed_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        if not fwd and k == "grad":
+            fa = sum(flop_grad_algorithmic(c, cfg["K"], cfg["V"]) for c in chunks) * cfg["HV"]
+            tf = fa / (t * 1e-3) / 1e12
+            tx = mfma_work_grad(cfg["K"], cfg["V"]) * units / (t * 1e-3) / 1e12
+            e.update({"algorithmic_flop": fa, "mfma_tflops": round(tf, 1),
+                      "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "mfma_executed_tflops": round(tx, 1), "mfma_executed_frac": round(tx / MFMA_BF16_PEAK_TFLOPS, 4)})
+        stages[k] = e
+    return {"F": F, "tflops": F / (ms * 1e-3) / 1e12, "kb": kb, "stages": stages}
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_t32k_h16", choices=list(WORKLOADS))
+    ap.add_argument("--path", default="bwd", choices=["bwd", "fwd", "kda", "kda_stage", "bigdn"],
+                    help="bwd: the chunked backward (default); fwd: gate cumsum + chunked forward; "
+                         "kda: the full KDA backward at B=1 T=2048 H=32 K=V=128 fp16; "
+                         "kda_stage: the KDA WY backward stage alone on the same shape; "
+                         "bigdn: the BiGDN layer backward at B=8 F=11 S=1024 H=16 D=128 bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true", help="bwd: time only --workload")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the backward of one GPU's share); "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunked_gated_delta_08_amd import binding, profiling, workloads
+
+    evict = Evictor(torch)
+    if args.path == "kda":
+        return bench_kda(args, torch, binding, profiling, workloads, evict)
+    if args.path == "kda_stage":
+        return bench_kda_stage(args, torch, binding, profiling, workloads, evict)
+    if args.path == "bigdn":
+        return bench_bigdn(args, torch, binding, profiling, workloads, evict)
+    fwd = args.path == "fwd"
+    r = run_gdn(args, torch, binding, workloads, args.workload, fwd, evict)
+    sm = gdn_summary(r, fwd)
+    cfg, stage, kb = r["cfg"], r["stage"], sm["kb"]
+    if fwd:
+        kn = {"gate": "gate_cumsum_kernel", "prep": "prep_kernel", "scans": "scan_kernel", "out": "fwd_out_kernel"}
+        roof = _roofline(stage, kb, kn, "fwd_" + args.workload, profiling)
+    else:
+        # the gradient kernel against the dense bf16 MFMA peak on its algorithmic
+        # FLOPs (the backward's target), with its HBM view and executed work beside it
+        g = sm["stages"]["grad"]
+        roof = {"bound": "mfma", "achieved": g["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": g["mfma_frac"], "traffic": _traffic("grad_kernel", args.workload, profiling),
+                "kernel": "grad_kernel", "kernel_ms": g["ms"], "algorithmic_flop": g["algorithmic_flop"],
+                "hbm": {"achieved": g["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g["hbm_frac"],
+                        "algorithmic_bytes": g["algorithmic_bytes"]},
+                "executed": {"tflops": g["mfma_executed_tflops"], "frac": g["mfma_executed_frac"]},
+                "stage_ms": {k: round(v, 4) for k, v in stage.items()}}
+    roof["stages"] = sm["stages"]
+    st = r["stats"]
     wname = cfg["name"].replace("gdn_bwd", "gdn_fwd") if fwd else cfg["name"]
     what = "fwd" if fwd else "bwd"
     res = {"metric": f"GDN chunked {what} ms/call + eff. TFLOP/s at T=32k, H=16/32, K=V=128, BT=64",
-           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16", "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
-           "config": {"workload": wname, "B": cfg["B"], "T": T, "HK": cfg["HK"], "HV": cfg["HV"],
-                      "K": cfg["K"], "V": cfg["V"], "BT": 64, "global_batch": cfg["B"], "seq_len": T,
-                      "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2)},
+           "value": round(sm["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": st["median_ms"], "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+           "wall_ms_per_step_with_evict": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
+           "config": {"workload": wname, "B": cfg["B"], "T": r["T"], "HK": cfg["HK"], "HV": cfg["HV"],
+                      "K": cfg["K"], "V": cfg["V"], "BT": 64, "global_batch": cfg["B"], "seq_len": r["T"],
+                      "parallelism": "none", "flop_model_gflop": round(sm["F"] / 1e9, 2),
+                      "timing": "median of per-call HIP events, 512 MiB cache-evicting write before each call"},
            "roofline": roof}
+    if not fwd and not args.no_also:
+        also = []
+        for wk in WORKLOADS:
+            if wk == args.workload:
+                continue
+            ro = run_gdn(args, torch, binding, workloads, wk, False, evict)
+            so = gdn_summary(ro, False)
+            g = so["stages"]["grad"]
+            also.append({"workload": ro["cfg"]["name"], "ms_per_call": ro["stats"]["median_ms"],
+                         "p10_ms": ro["stats"]["p10_ms"], "p90_ms": ro["stats"]["p90_ms"],
+                         "tflops": round(so["tflops"], 2), "flop_model_gflop": round(so["F"] / 1e9, 2),
+                         "stage_ms": {k: round(v, 4) for k, v in ro["stage"].items()},
+                         "grad_mfma_frac": g["mfma_frac"], "grad_hbm_frac": g["hbm_frac"],
+                         "scans_hbm_frac": so["stages"]["scans"]["hbm_frac"]})
+            del ro
+        res["also"] = also
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path=args.path)
-    del keep
+        res["cpu_baseline"] = cpu_baseline(r["inp"], cfg, r["chunks"], path=args.path)
     print(json.dumps(res), flush=True)
 
 
-def bench_kda(args, torch, binding, profiling, workloads):
+def bench_kda(args, torch, binding, profiling, workloads, evict):
     """One step = one kda_chunk_bwd_full call at B=1, T=2048, H=32, K=V=128, fp16."""
     B, T, H, K, V = 1, 2048, 32, 128, 128
     cfg = dict(B=B, T=T, HK=H, HV=H, K=K, V=V, name="kda_bwd_T2048_h32_K128_V128_BT64_f16")
@@ -364,20 +495,10 @@ def bench_kda(args, torch, binding, profiling, workloads):
         if rc != 0:
             raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(i)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    names = ["prep", "scans", "stage", "intra"]
-    stage = {k: 0.0 for k in names}
-    for i in range(args.steps):
-        e = [evs[nev * i + j] for j in range(nev)]
-        for j, k in enumerate(names):
-            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
+    per_call, st, wall = timed_calls(torch, hip, evs, nev, call, args.steps, args.warmup, evict)
+    stats = call_stats(per_call)
+    ms_per_step = stats["median_ms"]
+    stage = dict(zip(["prep", "scans", "stage", "intra"], st))
     chunks = chunk_lengths(None, T, B, 64)
     F = sum(flop_model(c, K, V) for c in chunks) * H
     kb = kernel_bytes_kda(H, K, V, chunks)
@@ -385,16 +506,106 @@ def bench_kda(args, torch, binding, profiling, workloads):
     roof = _roofline(stage, kb, kn, "kda_t2048_h32", profiling)
     res = {"metric": "KDA chunked bwd (full, per-channel gate) ms/call + eff. TFLOP/s at T=2048, H=32, K=V=128, BT=64",
            "value": round(F / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "p10_ms": stats["p10_ms"], "p90_ms": stats["p90_ms"],
+           "wall_ms_per_step_with_evict": round(wall, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16",
            "data": "synthetic (seeded randn / logsigmoid / sigmoid, as the pages' workloads)",
            "config": {"workload": cfg["name"], "B": B, "T": T, "HK": H, "HV": H, "K": K, "V": V, "BT": 64,
-                      "global_batch": B, "seq_len": T, "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2)},
+                      "global_batch": B, "seq_len": T, "parallelism": "none", "flop_model_gflop": round(F / 1e9, 2),
+                      "timing": "median of per-call HIP events, 512 MiB cache-evicting write before each call"},
            "roofline": roof}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, cfg, chunks, path="kda")
     del keep
     print(json.dumps(res), flush=True)
+
+
+def flop_model_kda_stage(C, K, V):
+    """Products of the KDA WY backward stage per (chunk, head): dq = dO hᵀ,
+    dk_s = V_new dhᵀ, dw = -dv hᵀ (2CKV each); Aᵀ dv, Aᵀ dw (2C²V, 2C²K), dA_pre
+    (2C²V + 2C²K); the two C³ products of dA."""
+    return 6 * C * K * V + 4 * C * C * (K + V) + 4 * C ** 3
+
+
+def bench_kda_stage(args, torch, binding, profiling, workloads, evict):
+    """One step = one kda_chunk_bwd call (the WY stage alone) at B=1, T=2048,
+    H=32, K=V=128, BT=64, fp16, on the page's example inputs."""
+    B, T, H, K, V, BT = 1, 2048, 32, 128, 128, 64
+    inp = workloads.kda_inputs(B=B, T=T, H=H, K=K, V=V, BT=BT, dtype="f16", seed=0)
+    names = ("q", "k", "v", "v_new", "g", "beta", "A", "h", "dO", "dh", "dv")
+    dev = {n: inp[n].cuda() for n in names}
+    prob, keep = binding.make_problem(B, T, H, H, K, V, torch.float16, BT, None)
+    ntok = B * T
+    out = {"dq": torch.empty((ntok, H, K), dtype=torch.float32, device="cuda"),
+           "dk": torch.empty((ntok, H, K), dtype=torch.float32, device="cuda"),
+           "dv": torch.empty_like(dev["v"]),
+           "db": torch.empty((ntok, H), dtype=torch.float32, device="cuda"),
+           "dg": torch.empty((ntok, H, K), dtype=torch.float32, device="cuda"),
+           "dA": torch.empty((ntok, H, BT), dtype=torch.float32, device="cuda")}
+    P = binding._ptr
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args_c = [ctypes.byref(prob)] + [P(dev[n]) for n in names] + \
+        [P(out[n]) for n in ("dq", "dk", "dv", "db", "dg", "dA")] + [sp]
+    nev = 2
+    hip, evs = hip_events(nev * args.steps)
+
+    def call(i=None):
+        if i is not None:
+            assert hip.hipEventRecord(ctypes.c_void_p(evs[nev * i]), sp) == 0
+        rc = binding.lib.kda_chunk_bwd(*args_c)
+        if rc != 0:
+            raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
+        if i is not None:
+            assert hip.hipEventRecord(ctypes.c_void_p(evs[nev * i + 1]), sp) == 0
+
+    per_call, st, wall = timed_calls(torch, hip, evs, nev, call, args.steps, args.warmup, evict)
+    stats = call_stats(per_call)
+    ms = stats["median_ms"]
+    chunks = chunk_lengths(None, T, B, BT)
+    F = sum(flop_model_kda_stage(c, K, V) for c in chunks) * H
+    # algorithmic bytes: every input read once, every output written once
+    nbytes = sum(dev[n].numel() * dev[n].element_size() for n in names) + \
+        sum(t.numel() * t.element_size() for t in out.values())
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": _traffic("kda_kernel", "kda_stage_t2048_h32", profiling),
+            "kernel": "kda_kernel", "kernel_ms": ms, "algorithmic_bytes": nbytes,
+            "floor_us": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 1)}
+    res = {"metric": "KDA WY bwd stage (kda_chunk_bwd) ms/call + eff. TFLOP/s at T=2048, H=32, K=V=128, BT=64",
+           "value": round(F / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "p10_ms": stats["p10_ms"], "p90_ms": stats["p90_ms"],
+           "wall_ms_per_step_with_evict": round(wall, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded randn / logsigmoid / sigmoid; A lower-triangular randn), the page's example",
+           "config": {"workload": "kda_wy_stage_T2048_h32_K128_V128_BT64_f16", "B": B, "T": T, "HK": H, "HV": H,
+                      "K": K, "V": V, "BT": BT, "global_batch": B, "seq_len": T, "parallelism": "none",
+                      "flop_model_gflop": round(F / 1e9, 3),
+                      "timing": "median of per-call HIP events, 512 MiB cache-evicting write before each call"},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_kda_stage(inp, F)
+    del keep
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_kda_stage(inp, flops):
+    """The oracle's KDA stage VJP (O-K), unchanged, over every head of the
+    workload, repeated until at least 10 s have elapsed."""
+    from oracle import oracle as O
+    f = lambda n: inp[n].double().numpy()  # noqa: E731
+    p = O.Problem(inp["B"], inp["T"], inp["H"], inp["H"], inp["K"], inp["V"])
+    args = [f(n) for n in ("q", "k", "v", "v_new", "g", "beta", "A", "h", "dO", "dh", "dv")]
+    passes, dt = 0, 0.0
+    while dt < 10.0:
+        t0 = time.perf_counter()
+        O.kda_wy_bwd(p, inp["BT"], *args)
+        dt += time.perf_counter() - t0
+        passes += 1
+    res = {"value": round(passes * flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"{passes} full pass(es) over the workload ({dt:.1f} s): fp64 VJP of the stage functional, "
+                     "OpenMP over (chunk, head)", "seconds": round(dt, 2)}
+    res.update(host_info(O.num_threads()))
+    return res
 
 
 def flop_model_bigdn(B, F, S, H, D):
@@ -445,13 +656,15 @@ def cpu_baseline_bigdn(inp, flops_row):
         BO.bigdn_bwd(*args, f("dout"), inp["F"], inp["S"], k_scale=inp["k_scale"])
         dt += time.perf_counter() - t0
         passes += 1
-    return {"value": round(passes * flops_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) over batch row 0 of {inp['B']} ({dt:.1f} s): fp64 numpy forward recompute "
-                      "+ hand-derived backward, BLAS threads for the per-frame products",
-            "seconds": round(dt, 2)}
+    res = {"value": round(passes * flops_row / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+           "sample": f"{passes} pass(es) over batch row 0 of {inp['B']} ({dt:.1f} s): fp64 numpy forward recompute "
+                     "+ hand-derived backward, BLAS threads for the per-frame products",
+           "seconds": round(dt, 2)}
+    res.update(host_info(cores))
+    return res
 
 
-def bench_bigdn(args, torch, binding, profiling, workloads):
+def bench_bigdn(args, torch, binding, profiling, workloads, evict):
     """One step = one bigdn_bwd call at B=8, F=11, S=1024, H=16, D=128, bf16."""
     B, F, S, H, D = 8, 11, 1024, 16, 128
     inp = workloads.bigdn_inputs(B, F, S, H, D, seed=0)
@@ -476,20 +689,11 @@ def bench_bigdn(args, torch, binding, profiling, workloads):
         if rc != 0:
             raise binding.GdrError(rc, binding.lib.gdr_strerror(rc).decode())
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(i)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per_call, st, wall = timed_calls(torch, hip, evs, nev, call, args.steps, args.warmup, evict)
+    stats = call_stats(per_call)
+    ms_per_step = stats["median_ms"]
     names = ["stats", "phase_a", "scans", "phase_c", "gscans", "abar", "rms_bwd"]
-    stage = {k: 0.0 for k in names}
-    for i in range(args.steps):
-        e = [evs[nev * i + j] for j in range(nev)]
-        for j, k in enumerate(names):
-            stage[k] += elapsed_ms(hip, e[j], e[j + 1]) / args.steps
+    stage = dict(zip(names, st))
     Fl = flop_model_bigdn(B, F, S, H, D)
     nblk = min(768, (B * F * S + 3) // 4)
     kb = kernel_bytes_bigdn(B, F, S, H, D, nblk)
@@ -501,7 +705,8 @@ def bench_bigdn(args, torch, binding, profiling, workloads):
     roof["call_hbm_frac"] = round(sum(kb.values()) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     res = {"metric": "BiGDN chunkwise bwd ms/call + eff. TFLOP/s at B=8, F=11, S=1024, H=16, D=128",
            "value": round(Fl / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "p10_ms": stats["p10_ms"], "p90_ms": stats["p90_ms"],
+           "wall_ms_per_step_with_evict": round(wall, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded randn / sigmoid, rotary tables, as the page's layer inputs)",
            "config": {"workload": "bigdn_bwd_B8_F11_S1024_H16_D128_bf16", "B": B, "F": F, "S": S, "H": H, "D": D,

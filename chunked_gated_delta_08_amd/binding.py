@@ -1,8 +1,9 @@
 """Thin ctypes binding of libgdr.so (include/gdr.h) over torch tensors.
 
 Argument marshalling only: tensors are checked for device, dtype, shape and
-contiguity, output tensors and the workspace are allocated with torch, and the
-pointers and the current HIP stream are handed to the C ABI.  Every step of the
+contiguity (ValueError / TypeError before anything reaches the library),
+output tensors and the workspace are allocated with torch, and the pointers and
+the current HIP stream are handed to the C ABI.  Every step of the
 computation runs in the library's gfx950 kernels; if the library is missing the
 import fails (there is no fallback).
 
@@ -93,6 +94,121 @@ EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_sta
             "bigdn_fwd", "bigdn_fwd_events", "bigdn_bwd", "bigdn_bwd_events"]
 
 
+# ---------------------------------------------------------------- validation
+_FLOATS = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _need(t, name, dtype=None, shape=None, cuda=True, optional=False):
+    """Raises unless `t` is a contiguous tensor of the given dtype and shape
+    (on the GPU when `cuda`).  None passes only when `optional`."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _nseq(cu_seqlens, B, cuda):
+    if cu_seqlens is None:
+        return B
+    _need(cu_seqlens, "cu_seqlens", torch.int32, cuda=cuda)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least two entries")
+    return cu_seqlens.numel() - 1
+
+
+def check_gdr_args(q, k, v, g_cum, beta, dO=None, dht=None, h0=None, cu_seqlens=None, B=1, need_q=True,
+                   need_dO=False, cuda=True):
+    """Shapes and dtypes of the GDN entry points (include/gdr.h): q, k [B*T,HK,K];
+    v, dO [B*T,HV,V]; beta [B*T,HV] (all one dtype); g_cum [B*T,HV] fp32;
+    h0, dht [N,HV,K,V] fp32.  Returns (N, HK, HV, K, V)."""
+    _need(k, "k", cuda=cuda)
+    _need(v, "v", cuda=cuda)
+    if k.dim() != 3 or v.dim() != 3:
+        raise ValueError("k must be [B*T, HK, K] and v [B*T, HV, V]")
+    if v.dtype not in _FLOATS:
+        raise TypeError(f"v has dtype {v.dtype}; expected one of {_FLOATS}")
+    ntok, HK, K = k.shape
+    _, HV, V = v.shape
+    dt = v.dtype
+    _need(k, "k", dt, cuda=cuda)
+    _need(v, "v", dt, (ntok, HV, V), cuda=cuda)
+    if need_q:
+        _need(q, "q", dt, (ntok, HK, K), cuda=cuda)
+    _need(beta, "beta", dt, (ntok, HV), cuda=cuda)
+    _need(g_cum, "g_cum", torch.float32, (ntok, HV), cuda=cuda)
+    if need_dO:
+        _need(dO, "dO", dt, (ntok, HV, V), cuda=cuda)
+    if HK < 1 or HV % HK != 0:
+        raise ValueError(f"HV ({HV}) must be a multiple of HK ({HK})")
+    if cu_seqlens is None and ntok % B != 0:
+        raise ValueError(f"the token count {ntok} is not a multiple of B = {B}")
+    N = _nseq(cu_seqlens, B, cuda)
+    _need(h0, "h0", torch.float32, (N, HV, K, V), cuda=cuda, optional=True)
+    _need(dht, "dht", torch.float32, (N, HV, K, V), cuda=cuda, optional=True)
+    return N, HK, HV, K, V
+
+
+def check_kda_stage_args(q, k, v, v_new, g, beta, A, h, dO, dh, dv, BT=64, NT=None, cuda=True):
+    """Shapes and dtypes of kda_chunk_bwd: q, k [ntok,H,K]; v, v_new, dO, dv
+    [ntok,H,V]; beta [ntok,H]; A [ntok,H,BT] (one dtype); g [ntok,H,K] fp32;
+    h, dh [NT,H,K,V] fp32 (NT given, or taken from h)."""
+    _need(k, "k", cuda=cuda)
+    _need(v, "v", cuda=cuda)
+    if k.dim() != 3 or v.dim() != 3:
+        raise ValueError("k must be [ntok, H, K] and v [ntok, H, V]")
+    ntok, H, K = k.shape
+    V = v.shape[-1]
+    dt = k.dtype
+    if dt not in _FLOATS:
+        raise TypeError(f"k has dtype {dt}")
+    for t, n in ((q, "q"), (k, "k")):
+        _need(t, n, dt, (ntok, H, K), cuda=cuda)
+    for t, n in ((v, "v"), (v_new, "v_new"), (dO, "dO"), (dv, "dv")):
+        _need(t, n, dt, (ntok, H, V), cuda=cuda)
+    _need(beta, "beta", dt, (ntok, H), cuda=cuda)
+    _need(A, "A", dt, (ntok, H, BT), cuda=cuda)
+    _need(g, "g", torch.float32, (ntok, H, K), cuda=cuda)
+    _need(h, "h", torch.float32, cuda=cuda)
+    nt = h.shape[0] if NT is None else NT
+    _need(h, "h", torch.float32, (nt, H, K, V), cuda=cuda)
+    _need(dh, "dh", torch.float32, (nt, H, K, V), cuda=cuda)
+
+
+def check_kda_full_args(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, cuda=True):
+    """Shapes and dtypes of kda_chunk_bwd_full: q, k [ntok,H,K]; v, dO [ntok,H,V];
+    beta [ntok,H] (one dtype); g_cum [ntok,H,K] fp32; h0, dht [N,H,K,V] fp32."""
+    _need(k, "k", cuda=cuda)
+    _need(v, "v", cuda=cuda)
+    if k.dim() != 3 or v.dim() != 3:
+        raise ValueError("k must be [ntok, H, K] and v [ntok, H, V]")
+    ntok, H, K = k.shape
+    V = v.shape[-1]
+    dt = k.dtype
+    if dt not in _FLOATS:
+        raise TypeError(f"k has dtype {dt}")
+    _need(q, "q", dt, (ntok, H, K), cuda=cuda)
+    _need(v, "v", dt, (ntok, H, V), cuda=cuda)
+    _need(dO, "dO", dt, (ntok, H, V), cuda=cuda)
+    _need(beta, "beta", dt, (ntok, H), cuda=cuda)
+    _need(g_cum, "g_cum", torch.float32, (ntok, H, K), cuda=cuda)
+    if cu_seqlens is None and ntok % B != 0:
+        raise ValueError(f"the token count {ntok} is not a multiple of B = {B}")
+    N = _nseq(cu_seqlens, B, cuda)
+    _need(h0, "h0", torch.float32, (N, H, K, V), cuda=cuda, optional=True)
+    _need(dht, "dht", torch.float32, (N, H, K, V), cuda=cuda, optional=True)
+    return N
+
+
 def _check(code):
     if code != 0:
         raise GdrError(code, lib.gdr_strerror(code).decode())
@@ -115,7 +231,7 @@ def make_problem(B, T, HK, HV, K, V, dtype, BT=64, cu_seqlens=None, scale=None, 
     p = Problem(B, T, HK, HV, K, V, BT, 0, None, None, float(scale or 0.0), _DT[dtype], int(seg_chunks))
     keep = []
     if cu_seqlens is not None:
-        assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
         host = cu_seqlens.detach().to("cpu").contiguous()
         keep += [cu_seqlens, host]
         p.N = host.numel() - 1
@@ -136,7 +252,6 @@ def _dims(q_or_k, v, cu_seqlens, B):
     ntok, HK, K = q_or_k.shape
     _, HV, V = v.shape
     if cu_seqlens is None:
-        assert ntok % B == 0
         return B, ntok // B, HK, HV, K, V
     return 1, ntok, HK, HV, K, V
 
@@ -144,10 +259,8 @@ def _dims(q_or_k, v, cu_seqlens, B):
 def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, scale=None, BT=64,
                   want_dh0=True, out=None, workspace=None, stream=None, seg_chunks=0):
     """Backward of the chunkwise gated delta rule.  Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    check_gdr_args(q, k, v, g_cum, beta, dO, dht, h0, cu_seqlens, B, need_dO=True)
     B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
-    for t in (q, k, v, g_cum, beta, dO):
-        assert t.is_cuda and t.is_contiguous()
-    assert g_cum.dtype == torch.float32
     p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale, seg_chunks)
     N = B if cu_seqlens is None else p.N
     dev = v.device
@@ -169,10 +282,14 @@ def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, 
 def gdr_gate_cumsum(g, cu_seqlens=None, B=1, BT=64, out=None, stream=None):
     """In-chunk cumulative sum of the raw gate g [B*T, HV] fp32 (restarting every BT
     tokens and at every sequence start).  Returns g_cum, same shape, fp32."""
-    assert g.is_cuda and g.is_contiguous() and g.dtype == torch.float32 and g.dim() == 2
+    _need(g, "g", torch.float32)
+    if g.dim() != 2:
+        raise ValueError("g must be [B*T, HV]")
     ntok, HV = g.shape
     T = ntok // B if cu_seqlens is None else ntok
-    assert cu_seqlens is not None or ntok % B == 0
+    if cu_seqlens is None and ntok % B != 0:
+        raise ValueError(f"the token count {ntok} is not a multiple of B = {B}")
+    _nseq(cu_seqlens, B, True)
     p, keep = make_problem(B if cu_seqlens is None else 1, T, 1, HV, 1, 1, torch.float32, BT, cu_seqlens)
     if out is None:
         out = torch.empty_like(g)
@@ -185,10 +302,8 @@ def gdr_chunk_fwd(q, k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, scale=Non
                   out=None, workspace=None, stream=None, seg_chunks=0):
     """Chunked forward of the gated delta rule.  Returns dict o [B*T, HV, V] (input
     dtype) and ht [N, HV, K, V] fp32 (or None)."""
+    check_gdr_args(q, k, v, g_cum, beta, h0=h0, cu_seqlens=cu_seqlens, B=B)
     B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
-    for t in (q, k, v, g_cum, beta):
-        assert t.is_cuda and t.is_contiguous()
-    assert g_cum.dtype == torch.float32
     p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale, seg_chunks)
     N = B if cu_seqlens is None else p.N
     dev = v.device
@@ -206,6 +321,7 @@ def gdr_chunk_fwd(q, k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, scale=Non
 def gdr_fwd_states(k, v, g_cum, beta, h0=None, cu_seqlens=None, B=1, BT=64, want_v_new=True, want_ht=True,
                    workspace=None, stream=None, seg_chunks=0):
     """Per-chunk forward states h [NT, HV, K, V] fp32 (state entering each chunk), v_new, ht."""
+    check_gdr_args(None, k, v, g_cum, beta, h0=h0, cu_seqlens=cu_seqlens, B=B, need_q=False)
     B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
     p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, None, seg_chunks)
     N = B if cu_seqlens is None else p.N
@@ -228,7 +344,11 @@ def kda_chunk_bwd(q, k, v, v_new, g, beta, A, h, dO, dh, dv, scale=None, cu_seql
     ntok, H, K = k.shape
     V = v.shape[-1]
     T = ntok // B if cu_seqlens is None else ntok
+    if cu_seqlens is None and ntok % B != 0:
+        raise ValueError(f"the token count {ntok} is not a multiple of B = {B}")
+    _nseq(cu_seqlens, B, True)
     p, keep = make_problem(B if cu_seqlens is None else 1, T, H, H, K, V, v.dtype, BT, cu_seqlens, scale)
+    check_kda_stage_args(q, k, v, v_new, g, beta, A, h, dO, dh, dv, BT=BT, NT=num_chunks(p))
     dev = v.device
     if out is None:
         out = {"dq": torch.empty((ntok, H, K), dtype=torch.float32, device=dev),
@@ -249,11 +369,9 @@ def kda_chunk_bwd_full(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=N
     """Full chunked KDA backward (per-channel gate).  g_cum [B*T, H, K] fp32 in-chunk
     cumulative log-gate.  Returns dict dq, dk, dv (input dtype), dg [B*T,H,K],
     dbeta [B*T,H], dh0 [N,H,K,V] (fp32)."""
+    check_kda_full_args(q, k, v, g_cum, beta, dO, dht, h0, cu_seqlens, B)
     ntok, H, K = k.shape
     V = v.shape[-1]
-    for t in (q, k, v, g_cum, beta, dO):
-        assert t.is_cuda and t.is_contiguous()
-    assert g_cum.dtype == torch.float32 and g_cum.shape == k.shape
     T = ntok // B if cu_seqlens is None else ntok
     p, keep = make_problem(B if cu_seqlens is None else 1, T, H, H, K, V, v.dtype, BT, cu_seqlens, scale)
     N = B if cu_seqlens is None else p.N
@@ -279,18 +397,20 @@ def kda_chunk_bwd_full(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=N
 # [H*D]; rope cos/sin fp32 [N, D]; out / dout bf16 [B, N, H, D].
 
 def bigdn_problem(qkv, F, S, k_scale=1.0, norm_eps=1e-5, eps=1e-6):
+    if qkv.dim() != 5 or qkv.shape[2] != 3 or qkv.shape[1] != F * S:
+        raise ValueError(f"qkv must be [B, F*S, 3, H, D]; got {tuple(qkv.shape)} with F={F}, S={S}")
     B, N, three, H, D = qkv.shape
-    assert three == 3 and N == F * S
     return BigdnProblem(B, F, S, H, D, float(k_scale), float(norm_eps), float(eps))
 
 
 def _bigdn_inputs(qkv, beta, decay, qw, kw, cos, sin, F, S):
+    _need(qkv, "qkv", torch.bfloat16)
+    if qkv.dim() != 5 or qkv.shape[2] != 3 or qkv.shape[1] != F * S:
+        raise ValueError(f"qkv must be [B, F*S, 3, H, D]; got {tuple(qkv.shape)} with F={F}, S={S}")
     B, N, _, H, D = qkv.shape
-    assert qkv.dtype == torch.bfloat16
-    for t, shape in ((beta, (B, H, F, S)), (decay, (B, H, F)), (qw, (H * D,)), (kw, (H * D,)), (cos, (N, D)),
-                     (sin, (N, D))):
-        assert t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and tuple(t.shape) == shape
-    assert qkv.is_cuda and qkv.is_contiguous()
+    for t, n, shape in ((beta, "beta", (B, H, F, S)), (decay, "decay", (B, H, F)), (qw, "qw", (H * D,)),
+                        (kw, "kw", (H * D,)), (cos, "cos", (N, D)), (sin, "sin", (N, D))):
+        _need(t, n, torch.float32, shape)
 
 
 def bigdn_workspace_size(p, bwd):
@@ -322,8 +442,7 @@ def bigdn_bwd(qkv, beta, decay, qw, kw, cos, sin, dout, F, S, k_scale=1.0, norm_
     dqw, dkw (fp32)."""
     _bigdn_inputs(qkv, beta, decay, qw, kw, cos, sin, F, S)
     B, N, _, H, D = qkv.shape
-    assert dout.is_cuda and dout.is_contiguous() and dout.dtype == torch.bfloat16
-    assert tuple(dout.shape) == (B, N, H, D)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D))
     p = bigdn_problem(qkv, F, S, k_scale, norm_eps, eps)
     dev = qkv.device
     if out is None:

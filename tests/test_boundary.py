@@ -100,6 +100,8 @@ def test_kda_validation(B):
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2
     p = _prob(B, dtype=B.GDR_F16, BT=16)
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2
+    p = _prob(B, dtype=B.GDR_F32, K=128, V=128)   # fp32 is built at K = V = 64 only
+    assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2
     p = _prob(B, dtype=B.GDR_F16)
     f2 = list(f)
     f2[6] = None   # A

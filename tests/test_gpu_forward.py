@@ -134,16 +134,17 @@ def test_fwd_deterministic(B):
 
 
 @pytest.mark.slow
-def test_fwd_full_size_sampled_heads(B, oracle):
-    heads = [3, 12]
-    _log(f"[fwd] dense T=32768 HK=HV=16 K=V=128 bf16, sampled value heads {heads}")
+def test_fwd_full_size_all_heads(B, oracle):
+    _log("[fwd] dense T=32768 HK=HV=16 K=V=128 bf16, every head")
     inp = W.gdr_inputs(1, 32768, 16, 16, 128, 128, dtype="bf16", seed=0, dht=False)
     o, ht = _fwd_gpu(B, inp)
     assert np.isfinite(o).all() and np.isfinite(ht).all()
-    ref = _fwd_oracle(oracle, inp, heads=heads)
-    e_o, e_t = rel_l2(o[:, heads], ref["o"]), rel_l2(ht[:, heads], ref["ht"])
-    _log(f"  o rel-L2 {e_o:.2e}, ht {e_t:.2e}")
-    assert e_o <= TOL["bf16"] and e_t <= TOL["bf16"]
+    ref = _fwd_oracle(oracle, inp)
+    e_o, e_t = rel_l2(o, ref["o"]), rel_l2(ht, ref["ht"])
+    w_o = max(rel_l2(o[:, h], ref["o"][:, h]) for h in range(16))
+    w_t = max(rel_l2(ht[:, h], ref["ht"][:, h]) for h in range(16))
+    _log(f"  o rel-L2 {e_o:.2e} (worst head {w_o:.2e}), ht {e_t:.2e} (worst head {w_t:.2e})")
+    assert max(e_o, e_t, w_o, w_t) <= TOL["bf16"]
 
 
 # ------------------------------------------------------------------ autograd

@@ -100,12 +100,11 @@ def test_kda_full_deterministic(B):
 
 
 @pytest.mark.slow
-def test_kda_full_T2048_h32_sampled(B, oracle):
-    heads = [3, 17]
-    _log(f"[kda full] B=1 T=2048 H=32 K=V=128 f16, sampled heads {heads}")
+def test_kda_full_T2048_h32_all_heads(B, oracle):
+    _log("[kda full] B=1 T=2048 H=32 K=V=128 f16, every head")
     inp = W.kda_full_inputs(1, 2048, 32, 128, 128, dtype="f16", seed=0)
     got = _gpu(B, inp)
     for n, v in got.items():
         assert np.isfinite(v).all(), n
-    ref = _oracle(oracle, inp, heads=heads)
-    _compare(got, ref, "f16", heads=heads, label="T2048_h32")
+    ref = _oracle(oracle, inp)
+    _compare(got, ref, "f16", label="T2048_h32")

@@ -2,8 +2,8 @@
 
 Tolerances (relative L2 per output tensor): 2e-2 for 16-bit inputs, 1e-4 for
 fp32 inputs, and 1e-3 for dh0 in every case.  Full-size configurations are
-checked on sampled heads: every (sequence, value head) is independent, so the
-oracle runs on the sampled heads' slices of the same inputs.
+compared on every head: full-tensor rel-L2 per output, and per-head rel-L2 of
+each output against the same limit.
 """
 import numpy as np
 import pytest
@@ -197,27 +197,38 @@ def test_fwd_states(B, oracle):
 
 # ------------------------------------------------------------------ full sizes
 FULL = {
-    "dense_T32k_hk16_hv16": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None, heads=[0, 9]),
-    "dense_T32k_hk32_hv32": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None, heads=[5]),
-    "varlen12_64k_hk16_hv32": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12", heads=[6, 7]),
+    "dense_T32k_hk16_hv16": dict(B=1, T=32768, HK=16, HV=16, K=128, V=128, lengths=None),
+    "dense_T32k_hk32_hv32": dict(B=1, T=32768, HK=32, HV=32, K=128, V=128, lengths=None),
+    "varlen12_64k_hk16_hv32": dict(B=1, T=None, HK=16, HV=32, K=128, V=128, lengths="varlen12"),
 }
+
+
+def _per_head(got, ref, name):
+    """Largest per-head rel-L2 of one output: key heads for dq/dk, value heads
+    otherwise (dh0 is [N, HV, K, V], the rest token-major [ntok, H, ...])."""
+    g, r = np.asarray(got[name]), np.asarray(ref[name])
+    return max(rel_l2(g[:, h], r[:, h]) for h in range(r.shape[1]))
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled_heads(B, oracle, name):
+def test_full_size_all_heads(B, oracle, name):
     cfg = dict(FULL[name])
-    heads = cfg.pop("heads")
     if cfg["lengths"] == "varlen12":
         cfg["lengths"] = W.varlen_lengths()
-    _log(f"[parity] {name}: {cfg} sampled value heads {heads}")
+    _log(f"[parity] {name}: {cfg}, every head")
     inp = W.gdr_inputs(cfg["B"], cfg["T"], cfg["HK"], cfg["HV"], cfg["K"], cfg["V"], dtype="bf16", seed=0,
                        lengths=cfg["lengths"], dht=True)
     got = _run_gpu(B, inp)
     for nm in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
         assert np.isfinite(got[nm]).all(), nm
-    ref = _run_oracle(oracle, inp, heads=heads)
-    _compare(got, ref, "bf16", heads=heads, grp=cfg["HV"] // cfg["HK"], label=name)
+    ref = _run_oracle(oracle, inp)
+    _compare(got, ref, "bf16", label=name)
+    worst = {nm: _per_head(got, ref, nm) for nm in ("dq", "dk", "dv", "dg", "dbeta", "dh0")}
+    _log(f"  {name} worst per-head rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+    for nm, e in worst.items():
+        lim = TOL_DH0 if nm == "dh0" else TOL["bf16"]
+        assert e <= lim, (name, nm, e, lim)
 
 
 # ------------------------------------------------------------------ KDA stage
@@ -252,7 +263,7 @@ def test_kda_small(B, oracle):
 
 
 @pytest.mark.slow
-def test_kda_T2048_h32_sampled(B, oracle):
-    _log("[parity] kda B=1 T=2048 H=32 K=V=128 fp16, sampled heads")
+def test_kda_T2048_h32_all_heads(B, oracle):
+    _log("[parity] kda B=1 T=2048 H=32 K=V=128 fp16, every head")
     inp = W.kda_inputs(B=1, T=2048, H=32, K=128, V=128, BT=64, dtype="f16", seed=0)
-    _kda_compare(B, oracle, inp, heads=[0, 13, 31], label="kda_T2048_h32")
+    _kda_compare(B, oracle, inp, label="kda_T2048_h32")
