@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_F32, GDR_F16, GDR_BF16 = 0, 1, 2
 _DT = {torch.float32: GDR_F32, torch.float16: GDR_F16, torch.bfloat16: GDR_BF16}
-STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED", -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_LAUNCH"}
+STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED", -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_LAUNCH",
+          -5: "GDR_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
 
 
 class GdrError(RuntimeError):
@@ -67,6 +69,10 @@ lib.kda_chunk_bwd_full_events.restype = ctypes.c_int
 lib.kda_chunk_bwd_full_events.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp, _sz, _vp, _vp]
 lib.kda_chunk_bwd.restype = ctypes.c_int
 lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 17 + [_vp]
+lib.gdr_noalloc_init.restype = ctypes.c_int
+lib.gdr_noalloc_init.argtypes = []
+lib.gdr_chunk_bwd_noalloc.restype = ctypes.c_int
+lib.gdr_chunk_bwd_noalloc.argtypes = [ctypes.POINTER(Problem)] + [_vp] * 14 + [_vp]
 
 
 
@@ -91,7 +97,8 @@ lib.bigdn_bwd_events.argtypes = [ctypes.POINTER(BigdnProblem)] + [_vp] * 13 + [_
 EXPORTED = ["gdr_strerror", "gdr_num_chunks", "gdr_workspace_size", "gdr_fwd_states", "gdr_gate_cumsum",
             "gdr_chunk_fwd", "gdr_chunk_fwd_events", "gdr_chunk_bwd", "gdr_chunk_bwd_events", "kda_chunk_bwd",
             "kda_workspace_size", "kda_chunk_bwd_full", "kda_chunk_bwd_full_events", "bigdn_workspace_size",
-            "bigdn_fwd", "bigdn_fwd_events", "bigdn_bwd", "bigdn_bwd_events"]
+            "bigdn_fwd", "bigdn_fwd_events", "bigdn_bwd", "bigdn_bwd_events", "gdr_noalloc_init",
+            "gdr_chunk_bwd_noalloc"]
 
 
 # ---------------------------------------------------------------- validation
@@ -275,6 +282,28 @@ def gdr_chunk_bwd(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, 
                              _ptr(dO), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
+    del keep
+    return out
+
+
+def gdr_chunk_bwd_noalloc(q, k, v, g_cum, beta, dO, dht=None, h0=None, cu_seqlens=None, B=1, scale=None, BT=64,
+                          want_dh0=True, out=None, stream=None, seg_chunks=0):
+    """gdr_chunk_bwd through the entry point that takes no workspace (the
+    library's fixed per-GPU scratch array).  `out` (dict of preallocated
+    outputs) lets a caller that cannot allocate pass its own buffers."""
+    check_gdr_args(q, k, v, g_cum, beta, dO, dht, h0, cu_seqlens, B, need_dO=True)
+    B, T, HK, HV, K, V = _dims(k, v, cu_seqlens, B)
+    p, keep = make_problem(B, T, HK, HV, K, V, v.dtype, BT, cu_seqlens, scale, seg_chunks)
+    N = B if cu_seqlens is None else p.N
+    dev = v.device
+    if out is None:
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "dg": torch.empty(g_cum.shape, dtype=torch.float32, device=dev),
+               "dbeta": torch.empty(beta.shape, dtype=torch.float32, device=dev),
+               "dh0": torch.empty((N, HV, K, V), dtype=torch.float32, device=dev) if want_dh0 else None}
+    _check(lib.gdr_chunk_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g_cum), _ptr(beta), _ptr(h0),
+                                     _ptr(dO), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                     _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _stream(stream)))
     del keep
     return out
 

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_grad.hip", "kda_bwd.hip", "gdr_fwd.hip", "kda_full.hip",
-               "bigdn.hip"]
+               "bigdn.hip", "gdr_noalloc.hip"]
 # per-source device flags: the WY-factor, scan and KDA kernels keep MFMA
 # accumulators in VGPRs; the gradient and forward-output kernels are left to
 # the compiler's register-class heuristics

@@ -51,7 +51,9 @@ typedef enum {
     GDR_ERR_INVALID = -1,     /* bad shape, dtype, null required pointer, bad cu_seqlens */
     GDR_ERR_UNSUPPORTED = -2, /* valid but not built: K != V, K not in {64,128}, BT != 64 */
     GDR_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than gdr_workspace_size() */
-    GDR_ERR_LAUNCH = -4       /* a HIP error was reported at launch */
+    GDR_ERR_LAUNCH = -4,      /* a HIP error was reported at launch */
+    GDR_ERR_SCRATCH = -5      /* gdr_chunk_bwd_noalloc: the problem needs more workspace than
+                                 GDR_NOALLOC_SCRATCH_BYTES */
 } gdr_status;
 
 typedef struct gdr_problem {
@@ -248,6 +250,31 @@ int kda_chunk_bwd_full_events(const gdr_problem *p, const void *q, const void *k
                               const float *g_cum, const void *beta, const float *h0, const void *dO,
                               const float *dht, void *dq, void *dk, void *dv, float *dg, float *dbeta,
                               float *dh0, void *ws, size_t ws_bytes, hipStream_t stream, hipEvent_t *events);
+
+/*
+ * gdr_chunk_bwd_noalloc -- gdr_chunk_bwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same inputs, outputs,
+ * computation and status codes as gdr_chunk_bwd; the workspace is a fixed
+ * device array of GDR_NOALLOC_SCRATCH_BYTES inside the library (one per GPU,
+ * held until the process ends).  This call allocates nothing: it makes no
+ * hipMalloc / hipFree and calls no allocating routine.
+ * Limit: problems with gdr_workspace_size(p) > GDR_NOALLOC_SCRATCH_BYTES are
+ * rejected with GDR_ERR_SCRATCH before anything is launched (at K = V = 128 and
+ * a 16-bit dtype the workspace is about 136 KB per (chunk, value head), e.g.
+ * T = 4096 with 16 value heads fits).
+ * Concurrency: every call on one GPU uses that GPU's single array, so calls
+ * that overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller; consecutive calls on one stream are safe.
+ * No part of the array needs to start at zero: every call writes what it reads.
+ * gdr_noalloc_init() resolves the array's address on the current device (the
+ * first call on a device does it too); it returns GDR_ERR_LAUNCH if that fails.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (128u << 20)
+int gdr_noalloc_init(void);
+int gdr_chunk_bwd_noalloc(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
+                          const void *beta, const float *h0, const void *dO, const float *dht,
+                          void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0, hipStream_t stream);
 
 #ifdef __cplusplus
 }

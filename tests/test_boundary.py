@@ -109,8 +109,18 @@ def test_kda_validation(B):
 
 
 def test_strerror(B):
-    for c in (0, -1, -2, -3, -4):
+    for c in (0, -1, -2, -3, -4, -5):
         assert B.lib.gdr_strerror(c)
+
+
+def test_noalloc_host_checks(B):
+    # rejected on the host before the scratch array is touched (no GPU needed)
+    args = [FAKE] * 14 + [None]
+    big = _prob(B, T=32768, HK=16, HV=16, K=128, V=128)
+    assert B.workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    assert B.lib.gdr_chunk_bwd_noalloc(ctypes.byref(big), *args) == -5
+    assert B.lib.gdr_chunk_bwd_noalloc(ctypes.byref(_prob(B, HK=2, HV=3)), *args) == -1
+    assert B.lib.gdr_chunk_bwd_noalloc(ctypes.byref(_prob(B, BT=32)), *args) == -2
 
 
 def _fwd(B, p, ws_bytes=1 << 40, **null):
