@@ -1,6 +1,6 @@
 // gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
 //
-// One workgroup (8 waves) per (chunk, key head) and launch; with G value heads
+// One workgroup (4 waves) per (chunk, key head) and launch; with G value heads
 // per key head there are G launches, one per head of the group, that add up
 // the dq/dk group sums in a fixed order (the GQA reduction the FlashQLA
 // backward explainer, §一 step ④, does in Python).
@@ -24,105 +24,143 @@
 //         its in-chunk cumsum and its gradient is reverse-cumsummed at the end).
 // All contractions run on MFMA (16-bit operands for 16-bit inputs, fp32 for
 // fp32 inputs) with fp32 accumulation; the state-dependent products are taken
-// over V in 64-column slices so the LDS footprint stays under 150 KB.
-// Every output tile of a wave uses rows 32*(w&1) .. +31, so the per-row
-// reductions (dG, dβ) accumulate in registers and are reduced once, in a
-// fixed order (deterministic, no atomics).
+// over V in 32-column slices.
+//
+// Layout for two workgroups per CU: the four waves form a 2 x 2 grid over
+// every output (wave w owns rows 32*(w&1) .. +31 and the column half w>>1), so
+// a wave's tile is 32 x 32 of a 64 x 64 result and 32 x 64 of a 64 x 128 one
+// (six 1 KB fragment reads feed eight MFMAs); with 32-column value slices and
+// the post-loop intermediates aliased onto dead slice buffers the workgroup
+// needs under 80 KB of LDS at K = V = 128 (16-bit), so a CU runs two units at
+// once and one unit's loads and barriers overlap the other's products.  The
+// per-row reductions (dG, dβ) accumulate in registers and are reduced once,
+// in a fixed order (deterministic, no atomics).
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
 
-// Row padding of the LDS tiles.  16-bit tiles: 16 elements, so a row pitch of
-// K + 16 or 64 + 16 elements is 8 dwords modulo the 32 banks and the four rows
-// a transposing 64-bit fragment read touches fall in distinct banks (measured
-// faster than a padding of 8 for both tile widths together, slower for either
-// alone).
-template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 16 : 4; }
+// Row padding of the LDS tiles (elements): a 16-bit row pitch of D + 8 is 4
+// dwords modulo the banks, fp32 D + 4.
+template <class E> constexpr int gpad() { return sizeof(E) == 2 ? 8 : 4; }
 
-// Wave w owns rows 32*(w&1) .. +31 and the column block (w>>1) of every
-// output; 8 waves (two per SIMD, so one wave's element-wise work overlaps the
-// other's LDS and MFMA latency) measured faster than 4 at every workload.
-// Cross-lane results (DPP and permute reductions) are written by every lane
-// that holds them, never under a lane-dependent branch.
-#ifndef GDR_GRAD_WAVES
-#define GDR_GRAD_WAVES 8
-#endif
-constexpr int GNT = 64 * GDR_GRAD_WAVES;
-constexpr int GNCB = GDR_GRAD_WAVES / 2;   // column blocks (waves w and w^1 share one)
+constexpr int GNW = 4;            // waves per workgroup
+constexpr int GNT = 64 * GNW;     // threads per workgroup
 
 template <class E, int KD, int VD>
 struct GradCfg {
-    static constexpr int C = 64, VH = 64, NVH = VD / VH;
-    static constexpr int LK = KD + gpad<E>(), LA = 64 + gpad<E>(), LS = VH + gpad<E>(), LF = 68;
-    static constexpr int TNK = KD / 16 / GNCB;   // 16-col tiles per wave for [64][KD] outputs
-    static constexpr int TNS = 4 / GNCB;         // 16-col tiles per wave for [64][64] outputs
-    // byte offsets.  The V slice lives in Q's buffer during the V loop (Q is
-    // reloaded afterwards); after the loop the slice region holds dW, dA_pre,
-    // M1 and Eb.
-    static constexpr size_t oQ = 0;
-    static constexpr size_t oK = oQ + (size_t)C * LK * sizeof(E);
-    static constexpr size_t oA = oK + (size_t)C * LK * sizeof(E);
-    static constexpr size_t oPm = oA + (size_t)C * LA * sizeof(E);
-    static constexpr size_t oH = oPm + (size_t)C * LA * sizeof(E);
-    static constexpr size_t odH = oH + (size_t)VH * LK * sizeof(E);
-    static constexpr size_t odO = odH + (size_t)VH * LK * sizeof(E);
-    static constexpr size_t oVn = odO + (size_t)C * LS * sizeof(E);
-    static constexpr size_t odVn = oVn + (size_t)C * LS * sizeof(E);
-    static constexpr size_t oSm = odVn + (size_t)C * LS * sizeof(E);
-    // small arrays: G, β, γ, row partials 2x[4][64], col partials [2][64], misc [80]
-    // dv slice [64][LS] staged for coalesced stores (16-bit types; fp32 stores directly)
-    static constexpr bool DV_LDS = sizeof(E) == 2;
-    static constexpr size_t oDv = oSm + (size_t)(3 * 64 + 8 * 64 + 2 * 64 + 80) * 4;
-    // V_new of the slice gets its own [64][LS] buffer when it fits (else it
-    // overwrites Z in place, one barrier later)
-    static constexpr size_t oEnd = oDv + (DV_LDS ? (size_t)C * LS * sizeof(E) : 0);
-    static constexpr bool VN2 = oEnd + (size_t)C * LS * sizeof(E) <= 160 * 1024;
-    static constexpr size_t oVn2 = VN2 ? oEnd : oVn;
-    static constexpr size_t smem = oEnd + (VN2 ? (size_t)C * LS * sizeof(E) : 0);
-    static constexpr size_t oV = oQ;                                    // [64][LS] inside the V loop
-    static constexpr size_t odW = oH;                                   // [64][LK]
-    static constexpr size_t odA = odH;                                  // [64][LA]
-    static constexpr size_t oM1 = odO;                                  // [64][LA]
-    static constexpr size_t oEb = oVn;                                  // [64][LA]
-    static_assert(LS <= LK && LA <= LK, "alias size");
-    static_assert(LA == LS, "alias size");
+    static constexpr int C = 64, VS = 32, NVS = VD / VS;
+    static constexpr int LK = KD + gpad<E>(), LA = 64 + gpad<E>(), LS = VS + gpad<E>();
+    static constexpr int TK = KD / 32;   // 16-column tiles per wave of a [64][KD] result (its column half)
+    static constexpr size_t es = sizeof(E);
+    // byte offsets.  The Q region holds the V slice, Z and V_new of the
+    // current slice during the value loop (Q is reloaded after it).
+    static constexpr size_t szK = (size_t)C * LK * es;
+    static constexpr size_t szQ = (size_t)C * LK * es > (size_t)3 * C * LS * es + 2 * 64 * 4
+                                      ? (size_t)C * LK * es : (size_t)3 * C * LS * es + 2 * 64 * 4;
+    static constexpr size_t szA = (size_t)C * LA * es;
+    static constexpr size_t szH = (size_t)VS * LK * es;
+    static constexpr size_t szS = (size_t)C * LS * es;
+    static constexpr size_t oK = 0;
+    static constexpr size_t oQ = oK + szK;
+    static constexpr size_t oA = oQ + szQ;
+    static constexpr size_t oPm = oA + szA;
+    static constexpr size_t oH = oPm + szA;
+    static constexpr size_t odH = oH + szH;
+    static constexpr size_t odO = odH + szH;
+    static constexpr size_t odVn = odO + szS;
+    static constexpr size_t oSm = odVn + szS;              // G, γ, β: 3 x 64 floats
+    static constexpr size_t smem = oSm + 3 * 64 * 4;
+    // slice buffers inside the Q region, and behind them (during the value
+    // loop only) the loop's dβ row partials, [2 column halves][64] floats
+    static constexpr size_t oV = oQ, oZ = oQ + szS, oVn = oQ + 2 * szS, oRowL = oQ + 3 * szS;
+    static_assert(3 * szS + 2 * 64 * 4 <= szQ, "row partials behind the slice buffers");
+    // post-loop aliases: dW [64][LK] over H + dH, dA [64][LA] over dO + dV_new,
+    // M1 over dW (after dW's last use), Eb over dA (after M1), the final
+    // reductions over A (after its last use), dq staged in Q's region and dk in dW's
+    static constexpr size_t odW = oH, odA = odO, oM1 = odW, oEb = odA, oRed = oA;
+    static_assert((size_t)C * LK * es <= 2 * szH, "dW alias");
+    static_assert(szA <= 2 * szS, "dA alias");
+    static_assert(szA <= (size_t)C * LK * es, "M1 alias");
+    static_assert(400 * 4 <= szA, "reduction alias");
+    static_assert(VD % VS == 0 && KD % 32 == 0, "tile shapes");
 };
 
-template <class Ein, class E, int D, int LD>
-__device__ __forceinline__ void g_load_rows(E* s, const Ein* __restrict__ g, long rs, int C, int rows = 64) {
-    constexpr int EPV = 16 / sizeof(Ein);
-    constexpr int VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < rows * VPR; idx += GNT) {
-        const int r = idx / VPR, c = idx % VPR;
-        typename Vec16<Ein>::t v;
-        if (r < C) v = *(const typename Vec16<Ein>::t*)(g + r * rs + c * EPV);
-        else v = typename Vec16<Ein>::t{};
-        *(typename Vec16<E>::t*)(s + r * LD + c * EPV) = v;
+// The lane index, recomputed where it is used: the compiler cannot share it
+// (or the addresses derived from it) between phases, so lane-dependent LDS
+// offsets are rebuilt per product (two VALU ops) instead of being kept live
+// across the whole kernel in registers the accumulators need.
+// (the masks after the opaque step restore the value range, so index
+// arithmetic stays on 24-bit multiplies)
+__device__ __forceinline__ int lane_o() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l & 63;
+}
+__device__ __forceinline__ int tid_o() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t & (GNT - 1);
+}
+
+// Wave-level product acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD
+// (AT: A stored [k][m], else [m][k]; BT_: B stored [k][n], else [n][k]); one
+// k-step of fragments in registers at a time (the other workgroup on the CU
+// covers the LDS latency); lane offsets from a fresh lane index (see lane_o).
+template <class E, int TM, int TN, int KD, bool AT, bool BT_>
+__device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0, int n0) {
+    using M = Mma<E>;
+    using frag = typename M::frag;
+    constexpr int NS = KD / M::KS;
+    const int l = lane_o(), r = l & 15, g = l >> 4;
+    // one lane base per operand; every fragment is that base plus a constant
+    // offset (16-bit: direct rows (mn0 + r), keys 8g..8g+7; transposed reads
+    // start at row k0 + 8g + r/4, column mn0 + 4(r%4), and at 4 rows further)
+    const E* pa;
+    const E* pb;
+    if constexpr (sizeof(E) == 2) {
+        pa = AT ? A + (8 * g + (r >> 2)) * lda + m0 + 4 * (r & 3) : A + (m0 + r) * lda + 8 * g;
+        pb = BT_ ? B + (8 * g + (r >> 2)) * ldb + n0 + 4 * (r & 3) : B + (n0 + r) * ldb + 8 * g;
+    } else {
+        pa = AT ? A + g * lda + m0 + r : A + (m0 + r) * lda + g;
+        pb = BT_ ? B + g * ldb + n0 + r : B + (n0 + r) * ldb + g;
+    }
+    auto frag_at = [&](const E* base, int ld, bool tr, int mn, int k0) -> frag {
+        if constexpr (sizeof(E) == 2) {
+            if (!tr) return *(const frag*)(base + mn * ld + k0);
+            const E* q = base + k0 * ld + mn;
+            i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
+            i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * ld));
+            i16x8 c = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            return __builtin_bit_cast(frag, c);
+        } else {
+            return tr ? base[k0 * ld + mn] : base[mn * ld + k0];
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        frag fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++) fa[i] = frag_at(pa, lda, AT, 16 * i, s * M::KS);
+#pragma unroll
+        for (int j = 0; j < TN; j++) fb[j] = frag_at(pb, ldb, BT_, 16 * j, s * M::KS);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) acc[i][j] = M::run(fa[i], fb[j], acc[i][j]);
     }
 }
 
-// 64 value columns (vc0 .. vc0+63) of one K x V state block from the workspace
-// state layout into LDS as [64 columns][KD keys] (row pitch LD).  16-bit types
-// read the fragment order (one contiguous 16 B per thread, two 8 B LDS
-// writes); fp32 reads the transposed [V][K] rows.
-template <class E, int KD, int LD>
-__device__ __forceinline__ void g_load_state(E* s, const E* __restrict__ blk, int vc0) {
-    if constexpr (sizeof(E) == 2) {
-        typedef short s4 __attribute__((ext_vector_type(4)));
-        typedef short s8 __attribute__((ext_vector_type(8)));
-        const E* src = blk + (long)vc0 * KD;          // 64 columns = 4 contiguous [16 x KD] blocks
-        for (int c = threadIdx.x; c < 64 * KD / 8; c += GNT) {
-            const int ln = c & 63, sblk = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
-            const int row = 16 * cb + (ln & 15), key = 32 * sblk + 4 * (ln >> 4);
-            const s8 v = *(const s8*)(src + (long)c * 8);
-            *(s4*)(s + row * LD + key) = s4{v[0], v[1], v[2], v[3]};
-            *(s4*)(s + row * LD + key + 16) = s4{v[4], v[5], v[6], v[7]};
-        }
-    } else {
-        g_load_rows<E, E, KD, LD>(s, blk + (long)vc0 * KD, KD, 64);
-    }
-}
+// Row base and column of this lane's accumulator elements, from a fresh lane
+// index (one per element-wise phase): element e of tile (i, j) of a wave
+// block at (m0, n0) is row rb + 16 i + e, column n0 + 16 j + cb.
+#define GRAD_LANE_RC()                          \
+    const int lq_ = lane_o();                   \
+    const int rb = m0 + 4 * (lq_ >> 4);         \
+    const int cb = lq_ & 15
+
+// Two adjacent 16-bit (or fp32) elements, stored as one access.
+template <class E> struct __attribute__((aligned(2 * sizeof(E)))) E2 { E x, y; };
 
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
 // issues the 16-byte loads (rows at or past C read row C-1, a valid row),
@@ -135,21 +173,23 @@ struct RowsReg {
     int C;
     __device__ __forceinline__ void load(const E* __restrict__ g, long rs, int Cn) {
         C = Cn;
+        const int tid = tid_o();
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int idx = threadIdx.x + GNT * i;
+            const int idx = tid + GNT * i;
             if (NV % GNT == 0 || idx < NV) {
-                const int r = min(idx / VPR, Cn - 1), c = idx % VPR;
+                const int r = min((int)((unsigned)idx / VPR), Cn - 1), c = (int)((unsigned)idx % VPR);
                 v[i] = *(const typename Vec16<E>::t*)(g + r * rs + c * EPV);
             }
         }
     }
     __device__ __forceinline__ void store(E* s) const {
+        const int tid = tid_o();
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int idx = threadIdx.x + GNT * i;
+            const int idx = tid + GNT * i;
             if (NV % GNT == 0 || idx < NV) {
-                const int r = idx / VPR, c = idx % VPR;
+                const int r = (int)((unsigned)idx / VPR), c = (int)((unsigned)idx % VPR);
                 typename Vec16<E>::t x = v[i];
                 if (r >= C) x = typename Vec16<E>::t{};
                 *(typename Vec16<E>::t*)(s + r * LD + c * EPV) = x;
@@ -158,18 +198,21 @@ struct RowsReg {
     }
 };
 
-// Register staging of 64 value columns (vc0 .. vc0+63) of one K x V state
-// block from the workspace state layout, written to LDS as [64 columns][KD]
-// (see g_load_state).
-template <class E, int KD, int LD>
+// Register staging of NC value columns (vc0 .. vc0+NC-1, NC a multiple of 16)
+// of one K x V state block, written to LDS as [NC columns][KD keys] (row pitch
+// LD).  16-bit types read the workspace fragment order (one contiguous 16 B
+// per thread, two 8 B LDS writes); fp32 reads the transposed [V][K] rows.
+template <class E, int KD, int LD, int NC>
 struct StateReg {
     static constexpr bool FRAG = sizeof(E) == 2;
-    static constexpr int N = 64 * KD * (int)sizeof(E) / 16 / GNT;
+    static constexpr int N = NC * KD * (int)sizeof(E) / 16 / GNT;
+    static_assert(N * 16 * GNT == NC * KD * (int)sizeof(E), "whole vectors per thread");
     typename Vec16<E>::t v[N];
     __device__ __forceinline__ void load(const E* __restrict__ blk, int vc0) {
-        const E* src = blk + (long)vc0 * KD;   // 64 columns: contiguous in both layouts
+        const E* src = blk + (long)vc0 * KD;   // NC columns: contiguous in both layouts
+        const int tid = tid_o();
 #pragma unroll
-        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(threadIdx.x + GNT * i) * (16 / sizeof(E)));
+        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(tid + GNT * i) * (16 / sizeof(E)));
     }
     // partial <this, o> over the elements this thread holds (same layout)
     __device__ __forceinline__ float dot(const StateReg& o) const {
@@ -181,19 +224,20 @@ struct StateReg {
         return acc;
     }
     __device__ __forceinline__ void store(E* s) const {
+        const int tid = tid_o();
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const int c = threadIdx.x + GNT * i;
+            const int c = tid + GNT * i;
             if constexpr (FRAG) {
                 typedef short s4 __attribute__((ext_vector_type(4)));
                 typedef short s8 __attribute__((ext_vector_type(8)));
-                const int ln = c & 63, sblk = (c >> 6) % (KD / 32), cb = (c >> 6) / (KD / 32);
+                const unsigned ln = c & 63, sblk = ((unsigned)c >> 6) % (KD / 32), cb = ((unsigned)c >> 6) / (KD / 32);
                 const int row = 16 * cb + (ln & 15), key = 32 * sblk + 4 * (ln >> 4);
                 const s8 x = __builtin_bit_cast(s8, v[i]);
                 *(s4*)(s + row * LD + key) = s4{x[0], x[1], x[2], x[3]};
                 *(s4*)(s + row * LD + key + 16) = s4{x[4], x[5], x[6], x[7]};
             } else {
-                const int row = c / (KD / 4), col = (c % (KD / 4)) * 4;
+                const int row = (int)((unsigned)c / (KD / 4)), col = (int)((unsigned)c % (KD / 4)) * 4;
                 *(typename Vec16<E>::t*)(s + row * LD + col) = v[i];
             }
         }
@@ -205,8 +249,8 @@ struct StateReg {
 template <class E, int D, int LD>
 __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* s, int C) {
     constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV;
-    for (int idx = threadIdx.x; idx < 64 * VPR; idx += GNT) {
-        const int r = idx / VPR, c = idx % VPR;
+    for (int idx = tid_o(); idx < 64 * VPR; idx += GNT) {
+        const int r = (int)((unsigned)idx / VPR), c = (int)((unsigned)idx % VPR);
         if (r < C) *(typename Vec16<E>::t*)(g + r * rs + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
     }
 }
@@ -230,6 +274,20 @@ __device__ __forceinline__ float sum16(float x) {
 // is not deferred to a later phase (where its operands would be kept live).
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
+// Pins the per-lane partials after a phase that updated them (see pin).
+__device__ __forceinline__ void pin_rows(float (&rg)[2][4], float (&rb)[2][4], float (&cg)[2], float& z) {
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            pin(rg[i][e]);
+            pin(rb[i][e]);
+        }
+    pin(cg[0]);
+    pin(cg[1]);
+    pin(z);
+}
+
 // sum over the 4 row groups (lane bits 4..5)
 __device__ __forceinline__ float sum4g(float x) {
     x += __shfl_xor(x, 16, 64);
@@ -245,341 +303,383 @@ __device__ __forceinline__ float sum4g(float x) {
 // theirs, and the last one stores the 16-bit sums.  The order of the sum is
 // fixed, and every launch has the register footprint of a single head.
 template <class E, int KD, int VD, bool GRP>
-__global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
+__global__ void __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     using Cf = GradCfg<E, KD, VD>;
-    constexpr int C = 64, TNK = Cf::TNK, TNS = Cf::TNS, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, LF = Cf::LF;
+    constexpr int C = 64, VS = Cf::VS, NVS = Cf::NVS, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, TK = Cf::TK;
     extern __shared__ __align__(16) unsigned char smem[];
-    E* sQ = (E*)(smem + Cf::oQ);
     E* sK = (E*)(smem + Cf::oK);
+    E* sQ = (E*)(smem + Cf::oQ);
     E* sA = (E*)(smem + Cf::oA);
     E* sPm = (E*)(smem + Cf::oPm);
     E* sH = (E*)(smem + Cf::oH);
     E* sdH = (E*)(smem + Cf::odH);
     E* sdO = (E*)(smem + Cf::odO);
-    E* sV = (E*)(smem + Cf::oV);
-    E* sVn = (E*)(smem + Cf::oVn);     // Z = diag(β)(V − diag(γ) K h) of the slice
-    E* sVn2 = (E*)(smem + Cf::oVn2);   // V_new = A Z of the slice (own buffer when it fits)
     E* sdVn = (E*)(smem + Cf::odVn);
+    E* sV = (E*)(smem + Cf::oV);     // V slice
+    E* sZ = (E*)(smem + Cf::oZ);     // Z = diag(β)(V − diag(γ) K h) of the slice, then dv staging
+    E* sVn = (E*)(smem + Cf::oVn);   // V_new = A Z of the slice
     E* sdW = (E*)(smem + Cf::odW);
     E* sdA = (E*)(smem + Cf::odA);
     E* sM1 = (E*)(smem + Cf::oM1);
     E* sEb = (E*)(smem + Cf::oEb);
     float* sG = (float*)(smem + Cf::oSm);
-    float* sB = sG + 64;
-    float* sGam = sB + 64;
-    float* sRowG = sGam + 64;      // [2][64] row partials of dG per column block (4 x 64 reserved)
-    float* sRowB = sRowG + 4 * 64; // [2][64] row partials of dβ
-    float* sCol = sRowB + 4 * 64;  // [2][64] column partials of dG per row half
-    float* sMisc = sCol + 2 * 64;  // [16 + 64]
-    E* sDv = (E*)(smem + Cf::oDv);
+    float* sGam = sG + 64;
+    float* sB = sGam + 64;
+    float* sRed = (float*)(smem + Cf::oRed);   // row partials of dG, dβ [2][64] each, column partials [2][64], misc [8]
+    float* sRowL = (float*)(smem + Cf::oRowL); // the value loop's dβ row partials [2][64]
 
     const int ci = blockIdx.x, hk = blockIdx.y, G = GRP ? HV / HK : 1;
     const ChunkInfo ch = a.info[ci];
     const int Cn = ch.len;
     const long t0 = ch.t0;
-    const int w = wave_id(), l = lane_id(), r16 = l & 15, g4 = l >> 4;
-    const int m0 = 32 * (w & 1);           // every output block of this wave starts at this row
-    const int n0s = (64 / GNCB) * (w >> 1);   // column block for [64][64] outputs
-    const int n0k = (KD / GNCB) * (w >> 1);   // column block for [64][KD] outputs
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l = lane_id();
+    const int wr = w & 1, wc = w >> 1;
+    const int m0 = 32 * wr;              // every output block of this wave starts at this row
+    const int n0s = 32 * wc;             // column half of [64][64] results
+    const int n0k = (KD / 2) * wc;       // column half of [64][KD] results
+    const int n0v = 16 * wc;             // column half of [64][VS] slice results
+    const int hv = GRP ? hk * G + hi : hk;
+    const long unit = (long)ci * HV + hv;
     const E* q = (const E*)a.q;
     const E* k = (const E*)a.k;
     const E* v = (const E*)a.v;
     const E* dO = (const E*)a.dO;
-    const E* hT = (const E*)a.hT;
-    const E* dhT = (const E*)a.dhT;
+    const E* hT = (const E*)a.hT + unit * VD * KD;
+    const E* dhT = (const E*)a.dhT + unit * VD * KD;
     const E* beta = (const E*)a.beta;
+    const long qrow = t0 * HK + hk, vrow = t0 * HV + hv;
 
-    f32x4 dq_tot[2][TNK], dk_tot[2][TNK];   // this head's dq, dk (then the group sums)
+    // Every load of the unit's start is issued before the first wait: the
+    // gate and β (needed first), Q and K (the first product), then A and the
+    // first value slice (in flight during Pm).  Every wave loads row
+    // threadIdx.x % 64, unconditionally, so no wait sits at a branch join.
+    const int rg = min((int)threadIdx.x & (C - 1), Cn - 1);
+    const float gg = a.gcum[(t0 + rg) * HV + hv];
+    const E bb = beta[(t0 + rg) * HV + hv];
+    __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the waits count on it
+    RowsReg<E, KD, LK> rq, rk;
+    rq.load(q + qrow * KD, (long)HK * KD, Cn);
+    rk.load(k + qrow * KD, (long)HK * KD, Cn);
+    __builtin_amdgcn_sched_barrier(0);
+    RowsReg<E, 64, LA> rA;
+    StateReg<E, KD, LK, VS> rH, rdH;
+    RowsReg<E, VS, LS> rdO, rV;
+    rA.load((const E*)a.A + unit * C * C, C, C);
+    rH.load(hT, 0);
+    rdH.load(dhT, 0);
+    rdO.load(dO + vrow * VD, (long)HV * VD, Cn);
+    rV.load(v + vrow * VD, (long)HV * VD, Cn);
+    if (threadIdx.x < C) {
+        const int r = threadIdx.x;
+        sG[r] = gg;
+        sGam[r] = __expf(gg);
+        sB[r] = r < Cn ? (float)bb : 0.f;
+    }
+    rq.store(sQ);
+    rk.store(sK);
+    lds_barrier();
+    const float gl = sG[C - 1], gC = sGam[C - 1];
 
+    // per-lane partial row sums (rows m0 + 16i + 4g + e) and column sums
+    float rowG[2][4], rowB[2][4], colG[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) rowG[i][e] = rowB[i][e] = 0.f;
+    colG[0] = colG[1] = 0.f;
+    float hdh = 0.f;   // partial <dh, h>
+
+    // ---- Pm = scale · lower(Γ ⊙ Q Kᵀ)
     {
-        const int hv = GRP ? hk * G + hi : hk;
-        const long unit = (long)ci * HV + hv;
-        // Every load of the unit's start is issued before the first wait: the
-        // gate and β (needed first), Q and K (the first product), then this
-        // head's A and first value slice (in flight during Pm).  The waits
-        // before the first LDS stores then cover only the first two groups.
-        // (every wave loads row threadIdx.x % 64, unconditionally, so no wait
-        // is placed at a branch join)
-        const int rg = min((int)threadIdx.x & (C - 1), Cn - 1);
-        const float gg = a.gcum[(t0 + rg) * HV + hv];
-        const E bb = beta[(t0 + rg) * HV + hv];
-        __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the waits count on it
-        RowsReg<E, KD, LK> rq, rk;
-        rq.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-        rk.load(k + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-        __builtin_amdgcn_sched_barrier(0);
-        RowsReg<E, 64, LA> rA;
-        StateReg<E, KD, LK> rH, rdH;
-        RowsReg<E, 64, LS> rdO, rV;
-        rA.load((const E*)a.A + unit * C * C, C, C);
-        rH.load(hT + unit * VD * KD, 0);
-        rdH.load(dhT + unit * VD * KD, 0);
-        rdO.load(dO + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
-        rV.load(v + (t0 * HV + hv) * VD, (long)HV * VD, Cn);
-        if (threadIdx.x < C) {
-            const int r = threadIdx.x;
-            sG[r] = gg;
-            sGam[r] = __expf(gg);
-            sB[r] = r < Cn ? (float)bb : 0.f;
-        }
-        rq.store(sQ);
-        rk.store(sK);
-        lds_barrier();
-        const float gl = sG[C - 1], gC = sGam[C - 1];
-
-        // per-lane partial row sums (rows m0 + 16i + 4g4 + e) and column sums
-        float rowG[2][4], rowB[2][4], colG[TNS];
+        f32x4 aqk[2][2];
+        zero_acc(aqk);
+        gemm4<E, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
+        GRAD_LANE_RC();
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) rowG[i][e] = rowB[i][e] = 0.f;
-#pragma unroll
-        for (int j = 0; j < TNS; j++) colG[j] = 0.f;
-        float hdh = 0.f;   // partial <dh, h>
-
-        // ---- S_qk -> Pm = scale · lower(Γ ⊙ Q Kᵀ)
-        {
-            f32x4 aqk[2][TNS];
-            zero_acc(aqk);
-            wgemm<E, 2, TNS, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < TNS; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
+                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
                     const float gm = (cc <= rr) ? __expf(sG[rr] - sG[cc]) : 0.f;
                     sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][j][e] : 0.f);
                 }
+    }
+    // ---- A = (I+L)^{-1} from the prep kernel
+    rA.store(sA);
+
+    // accumulators over the value slices.  dqi ends as dq and dks as dk;
+    // dAz = dV_new Zᵀ is dA_pre (= dV_new (diag(β)V)ᵀ + dW (diag(βγ)K)ᵀ, since
+    // Z = diag(β)(V − diag(γ) K h) and dW = −dV_new hᵀ).
+    f32x4 dPm[2][2], dqi[2][TK], dWa[2][TK], dks[2][TK], dAz[2][2];
+    zero_acc(dPm);
+    zero_acc(dqi);
+    zero_acc(dWa);
+    zero_acc(dks);
+    zero_acc(dAz);
+
+    // the next slice (h, dh as rows v of [V][K]; dO, V) is loaded into
+    // registers while the current one is computed
+    StateReg<E, KD, LK, VS> nH, ndH;
+    RowsReg<E, VS, LS> ndO, nV;
+#pragma unroll
+    for (int vs = 0; vs < NVS; vs++) {
+        if (vs == 0) {
+            rH.store(sH);
+            rdH.store(sdH);
+            hdh += rH.dot(rdH);   // <dh, h> over the slice, from the registers just stored
+            rdO.store(sdO);
+            lds_barrier();        // Pm has read Q: the slice buffers may take its region
+            rV.store(sV);
+            if (threadIdx.x < 128) sRowL[threadIdx.x] = 0.f;
+        } else {
+            nH.store(sH);
+            ndH.store(sdH);
+            hdh += nH.dot(ndH);
+            ndO.store(sdO);
+            nV.store(sV);
         }
-        // ---- A = (I+L)^{-1} from the prep kernel, and the first slice
-        rA.store(sA);
-        rH.store(sH);
-        rdH.store(sdH);
-        hdh += rH.dot(rdH);   // <dh, h> over the first slice, from the registers just stored
         pin(hdh);
-        rdO.store(sdO);
-        lds_barrier();   // Pm has read Q: the V slice may take its buffer
-        rV.store(sV);
-
-        // persistent accumulators over the V slices
-        f32x4 dPm[2][TNS], dqi[2][TNK], dWa[2][TNK], dks[2][TNK], dAp[2][TNS];
-        zero_acc(dPm);
-        zero_acc(dqi);
-        zero_acc(dWa);
-        zero_acc(dks);
-        zero_acc(dAp);
-
-        // the next value slice (h, dh as rows v of [V][K]; dO, V) is loaded into
-        // registers while the current one is computed
-        StateReg<E, KD, LK> nH, ndH;
-        RowsReg<E, 64, LS> ndO, nV;
-        RowsReg<E, KD, LK> nQ;   // Q returns to its buffer (which holds V during the loop)
-#pragma unroll
-        for (int vh = 0; vh < Cf::NVH; vh++) {
-            if (vh > 0) {
-                nH.store(sH);
-                ndH.store(sdH);
-                hdh += nH.dot(ndH);   // this slice's <dh, h>, before the registers take the next one
-                pin(hdh);
-                ndO.store(sdO);
-                nV.store(sV);
-            }
-            if (vh + 1 < Cf::NVH) {
-                nH.load(hT + unit * VD * KD, (vh + 1) * 64);
-                ndH.load(dhT + unit * VD * KD, (vh + 1) * 64);
-                ndO.load(dO + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
-                nV.load(v + (t0 * HV + hv) * VD + (vh + 1) * 64, (long)HV * VD, Cn);
-            } else {
-                nQ.load(q + (t0 * HK + hk) * KD, (long)HK * KD, Cn);
-            }
-            lds_barrier();
-            // ---- Kh, K dh, Pmᵀ dO  ->  Z = diag(β)(V − diag(γ) Kh),  dV_new
-            {
-                f32x4 kh[2][TNS], kdh[2][TNS], pdo[2][TNS];
-                zero_acc(kh);
-                zero_acc(kdh);
-                zero_acc(pdo);
-                wgemm<E, 2, TNS, KD, false, false>(kh, sK, LK, sH, LK, m0, n0s);
-                wgemm<E, 2, TNS, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0s);
-                wgemm<E, 2, TNS, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0s);
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-#pragma unroll
-                    for (int j = 0; j < TNS; j++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
-                        const float z = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][j][e]);
-                        sVn[rr * LS + cc] = to_e<E>(z);
-                        sdVn[rr * LS + cc] = to_e<E>(pdo[i][j][e] + __expf(gl - sG[rr]) * kdh[i][j][e]);
-                    }
-            }
-            lds_barrier();
-            // ---- V_new = A Z
-            {
-                f32x4 vn[2][TNS];
-                zero_acc(vn);
-                wgemm<E, 2, TNS, 64, false, true>(vn, sA, LA, sVn, LS, m0, n0s);
-                if constexpr (!Cf::VN2) lds_barrier();   // V_new overwrites Z
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-#pragma unroll
-                    for (int j = 0; j < TNS; j++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) sVn2[acc_row(m0, i, e) * LS + acc_col(n0s, j)] = to_e<E>(vn[i][j][e]);
-            }
-            lds_barrier();
-            // ---- accumulate the state products and the V-separable outputs
-            wgemm<E, 2, TNS, 64, false, false>(dPm, sdO, LS, sVn2, LS, m0, n0s);    // dO V_newᵀ
-            wgemm<E, 2, TNK, 64, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);    // dO hᵀ
-            wgemm<E, 2, TNK, 64, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);   // dV_new hᵀ
-            wgemm<E, 2, TNK, 64, false, true>(dks, sVn2, LS, sdH, LK, m0, n0k);  // V_new dhᵀ
-            wgemm<E, 2, TNS, 64, false, false>(dAp, sdVn, LS, sV, LS, m0, n0s);     // dV_new Vᵀ
-            {
-                f32x4 adv[2][TNS];
-                zero_acc(adv);
-                wgemm<E, 2, TNS, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0s);    // Aᵀ dV_new
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-#pragma unroll
-                    for (int j = 0; j < TNS; j++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
-                        rowB[i][e] += adv[i][j][e] * (float)sV[rr * LS + cc];
-                        if constexpr (Cf::DV_LDS) sDv[rr * LS + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
-                        else if (rr < Cn) ((E*)a.dv)[((t0 + rr) * HV + hv) * VD + vh * 64 + cc] = to_e<E>(sB[rr] * adv[i][j][e]);
-                    }
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) pin(rowB[i][e]);
-            }
-            lds_barrier();
-            if constexpr (Cf::DV_LDS) store_rows<E, 64, LS>((E*)a.dv + (t0 * HV + hv) * VD + vh * 64, (long)HV * VD, sDv, Cn);
+        if (vs + 1 < NVS) {
+            nH.load(hT, (vs + 1) * VS);
+            ndH.load(dhT, (vs + 1) * VS);
+            ndO.load(dO + vrow * VD + (vs + 1) * VS, (long)HV * VD, Cn);
+            nV.load(v + vrow * VD + (vs + 1) * VS, (long)HV * VD, Cn);
         }
-
-        // ---- Q back into its buffer (it held the V slices)
-        nQ.store(sQ);
-        // ---- F = dPm ⊙ Pm -> dG; T1 = dPm ⊙ Γ · scale (over Pm); dW -> LDS
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        // ---- K h  ->  Z = diag(β)(V − diag(γ) K h)
+        {
+            f32x4 kh[2][1];
+            zero_acc(kh);
+            gemm4<E, 2, 1, KD, false, false>(kh, sK, LK, sH, LK, m0, n0v);
+            GRAD_LANE_RC();
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
+                    sZ[rr * LS + cc] = to_e<E>(sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]));
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- dV_new = Pmᵀ dO + diag(γ_C/γ) K dh
+        {
+            f32x4 kdh[2][1], pdo[2][1];
+            zero_acc(kdh);
+            zero_acc(pdo);
+            gemm4<E, 2, 1, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0v);
+            gemm4<E, 2, 1, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0v);
+            GRAD_LANE_RC();
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
+                    sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + __expf(gl - sG[rr]) * kdh[i][0][e]);
+                }
+        }
+        lds_barrier();
+        // ---- V_new = A Z
+        {
+            f32x4 vn[2][1];
+            zero_acc(vn);
+            gemm4<E, 2, 1, 64, false, true>(vn, sA, LA, sZ, LS, m0, n0v);
+            GRAD_LANE_RC();
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sVn[(rb + 16 * i + e) * LS + (n0v + cb)] = to_e<E>(vn[i][0][e]);
+        }
+        lds_barrier();
+        // ---- the state products and the V-separable outputs (one 32-deep
+        // step each; scheduling fences keep each product's fragments out of
+        // the others' live ranges -- the accumulators take half the registers)
+        gemm4<E, 2, 2, VS, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);    // dO V_newᵀ
+        __builtin_amdgcn_sched_barrier(0);
+        gemm4<E, 2, TK, VS, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);     // dO hᵀ
+        __builtin_amdgcn_sched_barrier(0);
+        gemm4<E, 2, TK, VS, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);    // dV_new hᵀ
+        __builtin_amdgcn_sched_barrier(0);
+        gemm4<E, 2, TK, VS, false, true>(dks, sVn, LS, sdH, LK, m0, n0k);    // V_new dhᵀ
+        __builtin_amdgcn_sched_barrier(0);
+        gemm4<E, 2, 2, VS, false, false>(dAz, sdVn, LS, sZ, LS, m0, n0s);    // dV_new Zᵀ
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            f32x4 adv[2][1];
+            zero_acc(adv);
+            gemm4<E, 2, 1, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0v);  // Aᵀ dV_new
+            // dv = diag(β) Aᵀ dV_new, stored from the accumulators: lanes r and
+            // r^1 swap two rows each so that every lane writes two adjacent
+            // columns (4 bytes) of two rows
+            GRAD_LANE_RC();
+            const int r = cb, odd = r & 1;
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                float d[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
+                    // rowsum(Aᵀ dV_new ⊙ V) of this slice into the wave's own slots
+                    // (every lane of the row group holds the sum and writes it)
+                    const float rbs = sum16(adv[i][0][e] * (float)sV[rr * LS + cc]);
+                    sRowL[wc * 64 + rr] += rbs;
+                    d[e] = sB[rr] * adv[i][0][e];
+                }
+                const float s0 = odd ? d[0] : d[2], s1 = odd ? d[1] : d[3];
+                const float p0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
+                const float p1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+                // even lanes: rows e = 0, 1 at columns (r, r+1); odd lanes: rows e = 2, 3 at (r-1, r)
+                const int e0 = odd ? 2 : 0;
+                const int c0 = n0v + r - odd;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; h2++) {
+                    const int rr = rb + 16 * i + e0 + h2;
+                    const float own = odd ? (h2 ? d[3] : d[2]) : (h2 ? d[1] : d[0]);
+                    const float oth = h2 ? p1 : p0;
+                    E2<E> pr;
+                    pr.x = to_e<E>(odd ? oth : own);
+                    pr.y = to_e<E>(odd ? own : oth);
+                    if (rr < Cn) *(E2<E>*)((E*)a.dv + (vrow + (long)rr * HV) * VD + vs * VS + c0) = pr;
+                }
+            }
+        }
+        lds_barrier();   // the slice buffers are read before the next slice overwrites them
+    }
+    // the loop's dβ partials into lane 0 of each row group (the final reduction sums the 16 lanes)
+    {
+        GRAD_LANE_RC();
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < TNS; j++)
+            for (int e = 0; e < 4; e++) rowB[i][e] = cb == 0 ? sRowL[wc * 64 + (rb + 16 * i + e)] : 0.f;
+    }
+    lds_barrier();   // every wave has read its slots before Q returns over them
+
+    // ---- Q back into its region (it held the slice buffers)
+    {
+        RowsReg<E, KD, LK> nQ;
+        nQ.load(q + qrow * KD, (long)HK * KD, Cn);
+        nQ.store(sQ);
+    }
+    // ---- F = dPm ⊙ Pm -> dG; T1 = dPm ⊙ Γ · scale (over Pm, each wave its own block); dW -> LDS
+    {
+        GRAD_LANE_RC();
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
-                const bool lo = cc <= rr;
-                const float dp = lo ? dPm[i][j][e] : 0.f;
-                const float f = dp * (float)sPm[rr * LA + cc];
-                rowG[i][e] += f;
-                colG[j] += f;
-                sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
-            }
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
+                    const bool lo = cc <= rr;
+                    const float dp = lo ? dPm[i][j][e] : 0.f;
+                    const float f = dp * (float)sPm[rr * LA + cc];
+                    rowG[i][e] += f;
+                    colG[j] += f;
+                    sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
+                }
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int e = 0; e < 4; e++) pin(rowG[i][e]);
-#pragma unroll
-        for (int j = 0; j < TNS; j++) pin(colG[j]);
+        pin(colG[0]);
+        pin(colG[1]);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < TNK; j++)
+            for (int j = 0; j < TK; j++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) sdW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = to_e<E>(-dWa[i][j][e]);
-        lds_barrier();
-        E* sT1 = sPm;
+                for (int e = 0; e < 4; e++) sdW[(rb + 16 * i + e) * LK + (n0k + 16 * j + cb)] = to_e<E>(-dWa[i][j][e]);
+        // ---- dA_pre -> LDS
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) sdA[(rb + 16 * i + e) * LA + (n0s + 16 * j + cb)] = to_e<E>(dAz[i][j][e]);
+    }
+    lds_barrier();
+    E* sT1 = sPm;
 
-        // ---- dq = scale γ dO hᵀ + T1 K ;  dG += rowsum(Q ⊙ scale γ dO hᵀ)
-        {
-            f32x4 t1k[2][TNK];
-            zero_acc(t1k);
-            wgemm<E, 2, TNK, 64, false, true>(t1k, sT1, LA, sK, LK, m0, n0k);
+    // ---- dq = scale γ dO hᵀ + T1 K ;  dG += rowsum(Q ⊙ scale γ dO hᵀ)
+    {
+    GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < TNK; j++)
+        for (int j = 0; j < TK; j++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                        const float di = scale * sGam[rr] * dqi[i][j][e];
-                        rowG[i][e] += di * (float)sQ[rr * LK + cc];
-                        dq_tot[i][j][e] = di + t1k[i][j][e];
-                    }
-        }
-        // ---- dk: T1ᵀ Q + diag(γ_C/γ) V_new dhᵀ (z terms) + diag(βγ) Aᵀ dW
-        float zsum = 0.f;
-        {
-            f32x4 acc[2][TNK];
-            zero_acc(acc);
-            wgemm<E, 2, TNK, 64, true, true>(acc, sT1, LA, sQ, LK, m0, n0k);
-            f32x4 adw[2][TNK];
-            zero_acc(adw);
-            wgemm<E, 2, TNK, 64, true, true>(adw, sA, LA, sdW, LK, m0, n0k);
+            for (int e = 0; e < 4; e++) {
+                const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
+                const float di = scale * sGam[rr] * dqi[i][j][e];
+                rowG[i][e] += di * (float)sQ[rr * LK + cc];
+                dqi[i][j][e] = di;
+            }
+    }
+    float zsum = 0.f;
+    pin_rows(rowG, rowB, colG, zsum);
+    gemm4<E, 2, TK, 64, false, true>(dqi, sT1, LA, sK, LK, m0, n0k);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dk = diag(γ_C/γ) V_new dhᵀ (z terms) + diag(βγ) Aᵀ dW + T1ᵀ Q
+    {
+        f32x4 adw[2][TK];
+        zero_acc(adw);
+        gemm4<E, 2, TK, 64, true, true>(adw, sA, LA, sdW, LK, m0, n0k);
+        GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < TNK; j++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                        const float kv = (float)sK[rr * LK + cc];
-                        const float ds = __expf(gl - sG[rr]) * dks[i][j][e];
-                        const float z = ds * kv;
-                        rowG[i][e] -= z;
-                        zsum += z;
-                        const float aw = adw[i][j][e] * kv;
-                        rowB[i][e] += sGam[rr] * aw;
-                        rowG[i][e] += sB[rr] * sGam[rr] * aw;
-                        dk_tot[i][j][e] = acc[i][j][e] + ds + sB[rr] * sGam[rr] * adw[i][j][e];
-                    }
-        }
-        // ---- dA_pre = dV_new (diag(β)V)ᵀ + dW (diag(βγ)K)ᵀ  -> LDS
-        {
-            f32x4 dwk[2][TNS];
-            zero_acc(dwk);
-            wgemm<E, 2, TNS, KD, false, false>(dwk, sdW, LK, sK, LK, m0, n0s);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < TNS; j++)
+            for (int j = 0; j < TK; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
-                    sdA[rr * LA + cc] = to_e<E>(sB[cc] * (dAp[i][j][e] + sGam[cc] * dwk[i][j][e]));
+                    const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
+                    const float kv = (float)sK[rr * LK + cc];
+                    const float ds = __expf(gl - sG[rr]) * dks[i][j][e];
+                    const float z = ds * kv;
+                    rowG[i][e] -= z;
+                    zsum += z;
+                    const float aw = adw[i][j][e] * kv;
+                    rowB[i][e] += sGam[rr] * aw;
+                    rowG[i][e] += sB[rr] * sGam[rr] * aw;
+                    dks[i][j][e] = ds + sB[rr] * sGam[rr] * adw[i][j][e];
                 }
-        }
-        lds_barrier();
-        // ---- M1 = Aᵀ dA_pre
-        {
-            f32x4 m1[2][TNS];
-            zero_acc(m1);
-            wgemm<E, 2, TNS, 64, true, true>(m1, sA, LA, sdA, LA, m0, n0s);
+        pin_rows(rowG, rowB, colG, zsum);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    gemm4<E, 2, TK, 64, true, true>(dks, sT1, LA, sQ, LK, m0, n0k);
+    // ---- M1 = Aᵀ dA_pre (over dW, last read above: after the barrier)
+    lds_barrier();
+    {
+        f32x4 m1[2][2];
+        zero_acc(m1);
+        gemm4<E, 2, 2, 64, true, true>(m1, sA, LA, sdA, LA, m0, n0s);
+        GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < TNS; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) sM1[acc_row(m0, i, e) * LA + acc_col(n0s, j)] = to_e<E>(m1[i][j][e]);
-        }
-        lds_barrier();
-        // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ
-        {
-            f32x4 dl[2][TNS], akk[2][TNS];
-            zero_acc(dl);
-            zero_acc(akk);
-            wgemm<E, 2, TNS, 64, false, false>(dl, sM1, LA, sA, LA, m0, n0s);
-            wgemm<E, 2, TNS, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
+                for (int e = 0; e < 4; e++) sM1[(rb + 16 * i + e) * LA + (n0s + 16 * j + cb)] = to_e<E>(m1[i][j][e]);
+    }
+    lds_barrier();
+    // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ (over dA, last read above)
+    {
+        f32x4 dl[2][2], akk[2][2];
+        zero_acc(dl);
+        zero_acc(akk);
+        gemm4<E, 2, 2, 64, false, false>(dl, sM1, LA, sA, LA, m0, n0s);
+        gemm4<E, 2, 2, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
+        GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < TNS; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0s, j);
+                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
                     const bool lo = cc < rr;
                     const float d = lo ? -dl[i][j][e] : 0.f;
                     const float lg = lo ? __expf(sG[rr] - sG[cc]) * akk[i][j][e] : 0.f;   // Γ ⊙ KKᵀ
@@ -589,109 +689,110 @@ __global__ void __launch_bounds__(GNT) grad_kernel(GradArgs a, int HK, int HV, f
                     colG[j] += f2;
                     sEb[rr * LA + cc] = to_e<E>(lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f);
                 }
-        }
-        lds_barrier();
-        // ---- dk += Eb K + Ebᵀ K
-        {
-            f32x4 acc[2][TNK];
-            zero_acc(acc);
-            wgemm<E, 2, TNK, 64, false, true>(acc, sEb, LA, sK, LK, m0, n0k);
-            wgemm<E, 2, TNK, 64, true, true>(acc, sEb, LA, sK, LK, m0, n0k);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < TNK; j++) dk_tot[i][j] += acc[i][j];
-        }
-
-        // ---- reductions (fixed order): rows over the 16 lanes of a group and
-        // the two column blocks; columns over the 4 row groups and 2 row halves
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float rg = sum16(rowG[i][e]);
-                const float rb = sum16(rowB[i][e]);
-                // every lane of the group holds the sum: all write the same value (no branch)
-                const int rr = acc_row(m0, i, e);
-                sRowG[(w >> 1) * 64 + rr] = rg;
-                sRowB[(w >> 1) * 64 + rr] = rb;
-            }
-#pragma unroll
-        for (int j = 0; j < TNS; j++) {   // all four row groups hold the sum and write it (no branch)
-            const float cs = sum4g(colG[j]);
-            sCol[(w & 1) * 64 + acc_col(n0s, j)] = cs;
-        }
-        {
-            float hz = hdh, zz = zsum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                hz += __shfl_xor(hz, off, 64);
-                zz += __shfl_xor(zz, off, 64);
-            }
-            sMisc[w] = hz;   // every lane holds the sum (no branch)
-            sMisc[8 + w] = zz;
-        }
-        lds_barrier();
-        if (threadIdx.x < 64) {
-            const int rr = threadIdx.x;
-            float dG = -(sCol[rr] + sCol[64 + rr]), db = 0.f;
-#pragma unroll
-            for (int cb = 0; cb < GNCB; cb++) {
-                dG += sRowG[cb * 64 + rr];
-                db += sRowB[cb * 64 + rr];
-            }
-            if (rr == C - 1) {
-                float hd = 0.f, zs = 0.f;
-                for (int i = 0; i < GNT / 64; i++) { hd += sMisc[i]; zs += sMisc[8 + i]; }
-                dG += zs + gC * hd;
-            }
-            if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
-            // in-chunk reverse cumulative sum (suffix sums over the 64 rows,
-            // one row per lane; padded rows carry the chunk-end terms)
-            float x = dG;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_down(x, off, 64);
-                x += rr + off < 64 ? y : 0.f;
-            }
-            if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
-        }
-        if constexpr (GRP) {   // group sums through the workspace block of this (chunk, key head)
-            float* st = a.gsum + ((long)ci * HK + hk) * 2 * 64 * KD;
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < TNK; j++) {
-                    const int tl = (w * 2 + i) * TNK + j;
-                    f32x4* pq = (f32x4*)(st + (tl * 64 + l) * 4);
-                    f32x4* pk = (f32x4*)(st + 64 * KD + (tl * 64 + l) * 4);
-                    if (hi > 0) {
-                        dq_tot[i][j] += *pq;
-                        dk_tot[i][j] += *pk;
-                    }
-                    if (hi + 1 < G) {
-                        *pq = dq_tot[i][j];
-                        *pk = dk_tot[i][j];
-                    }
-                }
-            if (hi + 1 < G) return;   // uniform: only the last head of the group stores dq, dk
-        }
+        pin_rows(rowG, rowB, colG, zsum);
     }
-    // ---- the group sums dq, dk for this key head, through LDS (sH and sdH were last
-    //      read before the dA_pre and M1 barriers above)
+    lds_barrier();
+    // ---- dk += Eb K + Ebᵀ K
+    gemm4<E, 2, TK, 64, false, true>(dks, sEb, LA, sK, LK, m0, n0k);
+    gemm4<E, 2, TK, 64, true, true>(dks, sEb, LA, sK, LK, m0, n0k);
+
+    // ---- reductions (fixed order), over A's region (last read by M1 Aᵀ):
+    // rows over the 16 lanes of a group and the two column halves; columns
+    // over the 4 row groups and the two row halves
+    float* sRowG = sRed;
+    float* sRowB = sRed + 128;
+    float* sCol = sRed + 256;
+    float* sMisc = sRed + 384;
+    {
+    GRAD_LANE_RC();
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < TNK; j++)
+        for (int e = 0; e < 4; e++) {
+            const float rgs = sum16(rowG[i][e]);
+            const float rbs = sum16(rowB[i][e]);
+            // every lane of the group holds the sum: all write the same value (no branch)
+            const int rr = (rb + 16 * i + e);
+            sRowG[wc * 64 + rr] = rgs;
+            sRowB[wc * 64 + rr] = rbs;
+        }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {   // all four row groups hold the sum and write it (no branch)
+        const float cs = sum4g(colG[j]);
+        sCol[wr * 64 + (n0s + 16 * j + cb)] = cs;
+    }
+    }
+    {
+        float hz = hdh, zz = zsum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            hz += __shfl_xor(hz, off, 64);
+            zz += __shfl_xor(zz, off, 64);
+        }
+        sMisc[w] = hz;   // every lane holds the sum (no branch)
+        sMisc[4 + w] = zz;
+    }
+    lds_barrier();
+    if (threadIdx.x < 64) {
+        const int rr = threadIdx.x;
+        float dG = sRowG[rr] + sRowG[64 + rr] - (sCol[rr] + sCol[64 + rr]);
+        const float db = sRowB[rr] + sRowB[64 + rr];
+        if (rr == C - 1) {
+            float hd = 0.f, zs = 0.f;
+            for (int i = 0; i < GNW; i++) { hd += sMisc[i]; zs += sMisc[4 + i]; }
+            dG += zs + gC * hd;
+        }
+        if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
+        // in-chunk reverse cumulative sum (suffix sums over the 64 rows,
+        // one row per lane; padded rows carry the chunk-end terms)
+        float x = dG;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(x, off, 64);
+            x += rr + off < 64 ? y : 0.f;
+        }
+        if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
+    }
+    if constexpr (GRP) {   // group sums through the workspace block of this (chunk, key head)
+        float* st = a.gsum + ((long)ci * HK + hk) * 2 * 64 * KD;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < TK; j++) {
+                const int tl = (w * 2 + i) * TK + j;
+                f32x4* pq = (f32x4*)(st + (tl * 64 + l) * 4);
+                f32x4* pk = (f32x4*)(st + 64 * KD + (tl * 64 + l) * 4);
+                if (hi > 0) {
+                    dqi[i][j] += *pq;
+                    dks[i][j] += *pk;
+                }
+                if (hi + 1 < G) {
+                    *pq = dqi[i][j];
+                    *pk = dks[i][j];
+                }
+            }
+        if (hi + 1 < G) return;   // uniform: only the last head of the group stores dq, dk
+    }
+    // ---- dq, dk through LDS for 16-byte stores: dq over Q's region (last read
+    //      by T1ᵀ Q), dk over dW's (M1, last read by M1 Aᵀ)
+    E* sdq = sQ;
+    E* sdk = sdW;
+    {
+    GRAD_LANE_RC();
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < TK; j++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                sH[rr * LK + cc] = to_e<E>(dq_tot[i][j][e]);
-                sdH[rr * LK + cc] = to_e<E>(dk_tot[i][j][e]);
+                const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
+                sdq[rr * LK + cc] = to_e<E>(dqi[i][j][e]);
+                sdk[rr * LK + cc] = to_e<E>(dks[i][j][e]);
             }
+    }
     lds_barrier();
-    store_rows<E, KD, LK>((E*)a.dq + (t0 * HK + hk) * KD, (long)HK * KD, sH, Cn);
-    store_rows<E, KD, LK>((E*)a.dk + (t0 * HK + hk) * KD, (long)HK * KD, sdH, Cn);
+    store_rows<E, KD, LK>((E*)a.dq + qrow * KD, (long)HK * KD, sdq, Cn);
+    store_rows<E, KD, LK>((E*)a.dk + qrow * KD, (long)HK * KD, sdk, Cn);
 }
 
 template <class E, int KD, int VD, bool GRP>
