@@ -69,8 +69,8 @@ struct GradCfg {
     static constexpr size_t odH = oH + szH;
     static constexpr size_t odO = odH + szH;
     static constexpr size_t odVn = odO + szS;
-    static constexpr size_t oSm = odVn + szS;              // G, γ, β: 3 x 64 floats
-    static constexpr size_t smem = oSm + 3 * 64 * 4;
+    static constexpr size_t oSm = odVn + szS;              // G, γ, β, e^{G_C−G}: 4 x 64 floats
+    static constexpr size_t smem = oSm + 4 * 64 * 4;
     // slice buffers inside the Q region, and behind them (during the value
     // loop only) the loop's dβ row partials, [2 column halves][64] floats
     static constexpr size_t oV = oQ, oZ = oQ + szS, oVn = oQ + 2 * szS, oRowL = oQ + 3 * szS;
@@ -162,6 +162,18 @@ __device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda,
 // Two adjacent 16-bit (or fp32) elements, stored as one access.
 template <class E> struct __attribute__((aligned(2 * sizeof(E)))) E2 { E x, y; };
 
+// base + off elements, with the byte offset formed in 32 bits: a uniform base
+// and a 32-bit per-lane offset map onto the scalar-base addressing of global
+// loads and stores (no 64-bit address arithmetic per lane).
+template <class T>
+__device__ __forceinline__ T* at32(T* base, unsigned off) {
+    return (T*)((char*)base + off * (unsigned)sizeof(T));
+}
+template <class T>
+__device__ __forceinline__ const T* at32(const T* base, unsigned off) {
+    return (const T*)((const char*)base + off * (unsigned)sizeof(T));
+}
+
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
 // issues the 16-byte loads (rows at or past C read row C-1, a valid row),
 // store() writes the block to LDS (row pitch LD) with rows past C zeroed.
@@ -174,12 +186,13 @@ struct RowsReg {
     __device__ __forceinline__ void load(const E* __restrict__ g, long rs, int Cn) {
         C = Cn;
         const int tid = tid_o();
+        const unsigned urs = (unsigned)rs;   // row strides fit in 24 bits, offsets of a 64-row block in 32
 #pragma unroll
         for (int i = 0; i < N; i++) {
             const int idx = tid + GNT * i;
             if (NV % GNT == 0 || idx < NV) {
-                const int r = min((int)((unsigned)idx / VPR), Cn - 1), c = (int)((unsigned)idx % VPR);
-                v[i] = *(const typename Vec16<E>::t*)(g + r * rs + c * EPV);
+                const unsigned r = min((unsigned)idx / VPR, (unsigned)(Cn - 1)), c = (unsigned)idx % VPR;
+                v[i] = *(const typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV);
             }
         }
     }
@@ -198,6 +211,17 @@ struct RowsReg {
     }
 };
 
+// Packed 16-bit pairs and their fp32-accumulated dot product.
+template <class E> struct Pair;
+template <> struct Pair<bf16> {
+    typedef __bf16 t __attribute__((ext_vector_type(2)));
+    __device__ __forceinline__ static float dot2(t a, t b, float c) { return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false); }
+};
+template <> struct Pair<f16> {
+    typedef _Float16 t __attribute__((ext_vector_type(2)));
+    __device__ __forceinline__ static float dot2(t a, t b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
+
 // Register staging of NC value columns (vc0 .. vc0+NC-1, NC a multiple of 16)
 // of one K x V state block, written to LDS as [NC columns][KD keys] (row pitch
 // LD).  16-bit types read the workspace fragment order (one contiguous 16 B
@@ -210,17 +234,28 @@ struct StateReg {
     typename Vec16<E>::t v[N];
     __device__ __forceinline__ void load(const E* __restrict__ blk, int vc0) {
         const E* src = blk + (long)vc0 * KD;   // NC columns: contiguous in both layouts
-        const int tid = tid_o();
+        const unsigned tid = tid_o();
 #pragma unroll
-        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)(src + (long)(tid + GNT * i) * (16 / sizeof(E)));
+        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)at32(src, (tid + GNT * i) * (16u / sizeof(E)));
     }
     // partial <this, o> over the elements this thread holds (same layout)
     __device__ __forceinline__ float dot(const StateReg& o) const {
         float acc = 0.f;
+        if constexpr (sizeof(E) == 2) {   // packed pairs: one dot2 per two elements
+            using p2 = typename Pair<E>::t;
 #pragma unroll
-        for (int i = 0; i < N; i++)
+            for (int i = 0; i < N; i++) {
+                const p2* x = (const p2*)&v[i];
+                const p2* y = (const p2*)&o.v[i];
 #pragma unroll
-            for (int e = 0; e < (int)(16 / sizeof(E)); e++) acc += (float)v[i][e] * (float)o.v[i][e];
+                for (int e = 0; e < 4; e++) acc = Pair<E>::dot2(x[e], y[e], acc);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; i++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc += v[i][e] * o.v[i][e];
+        }
         return acc;
     }
     __device__ __forceinline__ void store(E* s) const {
@@ -249,9 +284,13 @@ struct StateReg {
 template <class E, int D, int LD>
 __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* s, int C) {
     constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV;
-    for (int idx = tid_o(); idx < 64 * VPR; idx += GNT) {
-        const int r = (int)((unsigned)idx / VPR), c = (int)((unsigned)idx % VPR);
-        if (r < C) *(typename Vec16<E>::t*)(g + r * rs + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
+    const unsigned urs = (unsigned)rs;
+#pragma unroll
+    for (int it = 0; it < (64 * VPR + GNT - 1) / GNT; it++) {
+        const unsigned idx = tid_o() + GNT * it;
+        const unsigned r = idx / VPR, c = idx % VPR;
+        if ((64 * VPR % GNT == 0 || idx < 64 * VPR) && (int)r < C)
+            *(typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
     }
 }
 
@@ -326,6 +365,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     float* sG = (float*)(smem + Cf::oSm);
     float* sGam = sG + 64;
     float* sB = sGam + 64;
+    float* sEg = sB + 64;   // e^{G_C − G_r}: the factor γ_C/γ
     float* sRed = (float*)(smem + Cf::oRed);   // row partials of dG, dβ [2][64] each, column partials [2][64], misc [8]
     float* sRowL = (float*)(smem + Cf::oRowL); // the value loop's dβ row partials [2][64]
 
@@ -380,6 +420,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     rk.store(sK);
     lds_barrier();
     const float gl = sG[C - 1], gC = sGam[C - 1];
+    if (threadIdx.x < C) sEg[threadIdx.x] = __expf(gl - sG[threadIdx.x]);   // read after the next barrier
 
     // per-lane partial row sums (rows m0 + 16i + 4g + e) and column sums
     float rowG[2][4], rowB[2][4], colG[2];
@@ -478,7 +519,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0v + cb);
-                    sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + __expf(gl - sG[rr]) * kdh[i][0][e]);
+                    sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + sEg[rr] * kdh[i][0][e]);
                 }
         }
         lds_barrier();
@@ -516,6 +557,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             // columns (4 bytes) of two rows
             GRAD_LANE_RC();
             const int r = cb, odd = r & 1;
+            E* dvb = (E*)a.dv + vrow * VD + vs * VS;
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 float d[4];
@@ -542,7 +584,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
                     E2<E> pr;
                     pr.x = to_e<E>(odd ? oth : own);
                     pr.y = to_e<E>(odd ? own : oth);
-                    if (rr < Cn) *(E2<E>*)((E*)a.dv + (vrow + (long)rr * HV) * VD + vs * VS + c0) = pr;
+                    if (rr < Cn) *(E2<E>*)at32(dvb, __umul24((unsigned)rr, (unsigned)(HV * VD)) + (unsigned)c0) = pr;
                 }
             }
         }
@@ -637,7 +679,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
                     const float kv = (float)sK[rr * LK + cc];
-                    const float ds = __expf(gl - sG[rr]) * dks[i][j][e];
+                    const float ds = sEg[rr] * dks[i][j][e];
                     const float z = ds * kv;
                     rowG[i][e] -= z;
                     zsum += z;
