@@ -142,6 +142,9 @@ WsPlan plan_workspace(const Problem& p) {
     w.hstart = off; off = align256(off + segbuf);
     w.dhin = off; off = align256(off + segbuf);
     w.gsum = off; off = align256(off + (p.HV > p.HK ? (size_t)p.NT * p.HK * 2 * 64 * p.K * 4 : 0));
+    w.cmax = off; off = align256(off + (size_t)(p.NT > 0 ? p.NT : 1) * 4 * p.HV * 4);
+    w.hmax = off; off = align256(off + (size_t)p.N * p.HV * 4);
+    w.dsc = off; off = align256(off + (size_t)p.N * p.HV * 4);
     w.total = off;
     return w;
 }
@@ -355,6 +358,10 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     a.hT = base + w.h; a.dhT = base + w.dh; a.dh0 = dh0;
     a.cu = q.cu; a.T = q.T;
     a.do_fwd = q.NT > 0; a.do_rev = true;
+    if (q.dtype != GDR_F32) {   // fp16 scan operands: scale dO and the state per (sequence, head)
+        a.info = info;
+        a.cmax = (float*)(base + w.cmax); a.hmax = (float*)(base + w.hmax); a.dsc = (float*)(base + w.dsc);
+    }
     if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
     if ((st = mark(2)) != GDR_OK) return st;
     if (q.NT > 0) {
@@ -363,6 +370,7 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
         g.hT = base + w.h; g.dhT = base + w.dh; g.A = base + w.A; g.info = info;
         g.dq = dq; g.dk = dk; g.dv = dv; g.dg = dg; g.dbeta = dbeta;
         g.gsum = (float*)(base + w.gsum);
+        g.dsc = a.dsc;
         st = launch_status(gdr::launch_grad(q, g, stream));
         if (st != GDR_OK) return st;
     }

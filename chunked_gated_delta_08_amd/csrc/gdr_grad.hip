@@ -420,7 +420,10 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     rk.store(sK);
     lds_barrier();
     const float gl = sG[C - 1], gC = sGam[C - 1];
-    if (threadIdx.x < C) sEg[threadIdx.x] = __expf(gl - sG[threadIdx.x]);   // read after the next barrier
+    // dh[c] arrives scaled by dsc (a power of two); its products all pass
+    // through the factor γ_C/γ, which takes 1/dsc along (and so does <dh, h>)
+    const float idsc = a.dsc ? 1.f / a.dsc[(long)ch.seq * HV + hv] : 1.f;
+    if (threadIdx.x < C) sEg[threadIdx.x] = idsc * __expf(gl - sG[threadIdx.x]);   // read after the next barrier
 
     // per-lane partial row sums (rows m0 + 16i + 4g + e) and column sums
     float rowG[2][4], rowB[2][4], colG[2];
@@ -782,7 +785,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         if (rr == C - 1) {
             float hd = 0.f, zs = 0.f;
             for (int i = 0; i < GNW; i++) { hd += sMisc[i]; zs += sMisc[4 + i]; }
-            dG += zs + gC * hd;
+            dG += zs + gC * idsc * hd;
         }
         if (rr < Cn) a.dbeta[(t0 + rr) * HV + hv] = db;
         // in-chunk reverse cumulative sum (suffix sums over the 64 rows,

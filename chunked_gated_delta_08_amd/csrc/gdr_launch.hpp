@@ -42,7 +42,7 @@ struct Problem {
 // type, in the first half of each block) are empty when maxS == 1.
 struct WsPlan {
     size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
-    size_t hloc, dhloc, P, hstart, dhin, gsum, total;
+    size_t hloc, dhloc, P, hstart, dhin, gsum, cmax, hmax, dsc, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
@@ -95,6 +95,13 @@ struct ScanArgs {
     float* hloc; float* dhloc; float* P; float* hstart; float* dhin;   // segment buffers
     const int32_t* cu; int T;   // sequence bounds: cu_seqlens (device) or dense length T
     bool do_fwd, do_rev;
+    // reverse scans with 16-bit operands: dO and the state are scaled per
+    // (sequence, value head) by a power of two so that max(|dO|, |dht|)
+    // lands in [1/2, 1) before the fp16 narrowing (NULL: no scaling); the
+    // per-chunk states dh[c] are written in that scaled form, dh0 unscaled.
+    // cmax [NT][4][HV] and hmax [N][HV] are the per-quarter-chunk / per-sequence
+    // maxima of |dO| and |dht|, dsc [N][HV] the scales; info is the chunk table.
+    const ChunkInfo* info; float* cmax; float* hmax; float* dsc;
 };
 hipError_t launch_scans(const Problem& p, const ScanArgs& a, hipStream_t s);
 
@@ -104,6 +111,7 @@ struct GradArgs {
     const void* hT; const void* dhT; const void* A; const ChunkInfo* info;
     void* dq; void* dk; void* dv; float* dg; float* dbeta;
     float* gsum;   // HV > HK: fp32 group-sum blocks, [NT][HK][2][64*K] (fragment order)
+    const float* dsc;   // [N][HV] scale of dhT (dh[c] stored times it), or NULL (1)
 };
 hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s);
 

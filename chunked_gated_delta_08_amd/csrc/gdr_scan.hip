@@ -174,7 +174,17 @@ struct ScanJob {
     float* out2;        // merged forward job: K x K block of the transfer matrix, in the
                         // fragment order with the values in the 16-bit operand type S
                         // (four per lane and tile): it only enters MFMAs as an operand
+    float sc = 1.f;     // reverse jobs: the state and dO run scaled by sc (a power of two);
+    float isc = 1.f;    // the per-chunk states dh[c] are stored scaled (the gradient kernel
+                        // folds 1/sc into its factors), dh0 is stored times isc = 1/sc
 };
+
+// Scale of the reverse scans of (sequence n, value head hv): 1 without scaling.
+__device__ __forceinline__ void job_scale(const ScanArgs& a, ScanJob& jb, int HV) {
+    const float s = a.dsc ? a.dsc[(long)jb.n * HV + jb.hv] : 1.f;
+    jb.sc = s;
+    jb.isc = 1.f / s;   // exact: s is a power of two
+}
 
 // rev: reverse (dh) recursion, else forward.  EST: per-chunk states stored in
 // type E.  HP (forward,
@@ -195,6 +205,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
     const int hv = jb.hv, n = jb.n;
     const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
     const int col0 = CW * w + r;                // this lane's state column in block 0 (block nb: + 16 nb)
+    const float sc = rev ? jb.sc : 1.f, isc = rev ? jb.isc : 1.f;   // scaled reverse state (1 forward)
     const int c0 = jb.c0, nc = jb.nc;
     const long bos = a.cu ? a.cu[n] : (long)n * a.T;            // first token of the sequence
     const int slen = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;        // its length
@@ -234,7 +245,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int row = 16 * t + 4 * g + e, col = col0 + 16 * nb;
-                    St[nb][t][e] = jb.init_form == ST_NAT ? jb.init[row * VD + col]
+                    St[nb][t][e] = jb.init_form == ST_NAT ? sc * jb.init[row * VD + col]
                                  : 0.f;
                 }
             }
@@ -290,7 +301,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
             if constexpr (rev) {
                 const bool valid = rowX[j] < st.cn;
 #pragma unroll
-                for (int e = 0; e < EPV; e++) xv[e] = valid ? (S)(float)st.x[j][e] : (S)0.f;
+                for (int e = 0; e < EPV; e++) xv[e] = valid ? (S)(sc * (float)st.x[j][e]) : (S)0.f;
             } else {
                 xv = st.u[j];
             }
@@ -546,7 +557,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
             for (int t = 0; t < KT; t++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) jb.out[(16 * t + 4 * g + e) * VD + col0 + 16 * nb] = St[nb][t][e];
+                for (int e = 0; e < 4; e++) jb.out[(16 * t + 4 * g + e) * VD + col0 + 16 * nb] = isc * St[nb][t][e];
     }
 }
 
@@ -596,6 +607,7 @@ scan_kernel(ScanArgs a, int nfwd, int HV) {
         jb.init = from_end ? (a.dht ? a.dht + nblk : nullptr) : a.dhin + sblk;
         jb.out_form = v.first && a.dh0 ? ST_NAT : ST_NONE;
         jb.out = a.dh0 ? a.dh0 + nblk : nullptr;
+        job_scale(a, jb, HV);
         scan_body<E, S, KD, VD, true, EST>(a, jb, HV, smem);
     } else {
         jb.init_form = v.first ? (a.h0 ? ST_NAT : ST_ZERO) : ST_FRAG;
@@ -638,6 +650,7 @@ seg_kernel(ScanArgs a, int NS, int HV) {
         if (v.first || !a.do_rev) return;
         jb.out_form = ST_FRAG;
         jb.out = a.dhloc + sblk;
+        job_scale(a, jb, HV);
         scan_body<E, S, KD, VD, true, false>(a, jb, HV, smem);
     } else {
         if (v.S == 1) return;
@@ -685,11 +698,12 @@ combine_kernel(ScanArgs a, int nseq, int HV) {
 
     f32x4 St[KT];
     const float* init = rev ? a.dht : a.h0;
+    const float isc0 = rev && a.dsc ? a.dsc[(long)n * HV + hv] : 1.f;   // reverse: scaled space
 #pragma unroll
     for (int t = 0; t < KT; t++)
 #pragma unroll
         for (int e = 0; e < 4; e++)
-            St[t][e] = init ? init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col] : 0.f;
+            St[t][e] = init ? isc0 * init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col] : 0.f;
 
     // step q uses segment j(q): forward j = s0 + q (q = 0 .. S_n-2), reverse j = s0 + S_n-1-q
     const int nsteps = S_n - 1;
@@ -764,6 +778,92 @@ combine_kernel(ScanArgs a, int nseq, int HV) {
     }
 }
 
+// Scale of the reverse scans (16-bit operands).  The dh recursion is linear in
+// (dO, dht), so it runs on s·dO and s·dht with s a power of two per (sequence,
+// value head) chosen so that max(|dO|, |dht|)·s lies in [1/2, 1): gradients of
+// a loss averaged over many tokens (|dO| ~ 1e-6 .. 1e-8) would otherwise fall
+// below fp16's normal range when dO and the state are narrowed to fp16 MFMA
+// operands.  The per-chunk states and dh0 are stored times 1/s (exact).
+// dmax_kernel: blocks [0, 4·NT) take max |dO| over a quarter (16 rows) of one
+// chunk for every value head (the rows are contiguous across the heads: each
+// thread takes 16-byte vectors of one head, V/8 threads share a head), blocks
+// [4·NT, 4·NT + N·HV) max |dht| over one K x V block.
+template <class E, int VD>
+__global__ void __launch_bounds__(256) dmax_kernel(ScanArgs a, int NT, int HV, int KV) {
+    typedef E e8 __attribute__((ext_vector_type(8)));
+    constexpr int VPH = VD / 8;                      // vectors per head and row (16 at V = 128)
+    __shared__ float red[256];
+    const int b = blockIdx.x;
+    if (b < 4 * NT) {
+        const ChunkInfo ch = a.info[b >> 2];
+        const int r0 = 16 * (b & 3), r1 = min(r0 + 16, ch.len);   // rows of this quarter (may be none)
+        const E* dO = (const E*)a.dO + (long)ch.t0 * HV * VD;
+        const int vpr = HV * VPH;                    // vectors per token row
+        for (int h0 = 0; h0 < vpr; h0 += 256) {      // heads handled by this pass
+            const int vi = h0 + (int)threadIdx.x;
+            float m = 0.f;
+            if (vi < vpr && r0 < r1)
+                for (int rb = r0; rb < r1; rb += 8) {   // eight rows in flight (repeated last row: same max)
+                    e8 x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; u++) x[u] = *(const e8*)(dO + ((long)min(rb + u, r1 - 1) * vpr + vi) * 8);
+#pragma unroll
+                    for (int u = 0; u < 8; u++)
+#pragma unroll
+                        for (int e = 0; e < 8; e++) m = fmaxf(m, fabsf((float)x[u][e]));
+                }
+            // the VPH threads of a head are consecutive: reduce within the group
+#pragma unroll
+            for (int off = 1; off < VPH; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (vi < vpr && vi % VPH == 0) a.cmax[(long)b * HV + vi / VPH] = m;
+        }
+        return;
+    }
+    const int j = b - 4 * NT;
+    float m = 0.f;
+    if (a.dht) {   // eight 16-byte loads in flight per thread
+        const float* x = a.dht + (long)j * KV;
+        for (int i0 = 0; i0 < KV / 4; i0 += 8 * 256) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) v[u] = *(const f32x4*)(x + 4 * min(i0 + u * 256 + (int)threadIdx.x, KV / 4 - 1));
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) a.hmax[j] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One block per (sequence, value head): the maximum over the sequence's chunks
+// and its dht block, and the power of two s = 2^-e with max = f·2^e, f in [1/2, 1)
+// (s = 1 when the maximum is zero or not finite).
+__global__ void __launch_bounds__(256) dscale_kernel(ScanArgs a, int HV) {
+    __shared__ float red[4];
+    const int j = blockIdx.x, n = j / HV, hv = j % HV;
+    const int c0 = 4 * a.seq_chunk0[n], c1 = 4 * a.seq_chunk0[n + 1];   // chunk quarters of the sequence
+    float m = 0.f;
+    for (int c = c0 + (int)threadIdx.x; c < c1; c += 256) m = fmaxf(m, a.cmax[(long)c * HV + hv]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), a.hmax[j]);
+        float s = 1.f;
+        if (m > 0.f && isfinite(m)) {
+            int e;
+            frexpf(m, &e);
+            s = ldexpf(1.f, -e);
+        }
+        a.dsc[j] = s;
+    }
+}
+
 template <class E, class S, int KD, int VD>
 static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
     using Cf = ScanCfg<E, S, KD, VD>;
@@ -776,6 +876,18 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
     const bool none_f = !a.do_fwd || !a.hT, none_r = !a.do_rev || !a.dhT;
     if (!(est_f && est_r) && !(none_f && none_r)) return hipErrorInvalidValue;
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
+    if constexpr (sizeof(S) == 2) {
+        if (a.do_rev && a.dsc) {   // scales of the reverse scans
+            const int nseq = p.cu ? p.N : p.B;
+            static_assert(VD % 8 == 0 && 64 % (VD / 8) == 0, "a head's vectors stay inside one wave");
+            hipLaunchKernelGGL((dmax_kernel<E, VD>), dim3((unsigned)(4 * p.NT + (int64_t)nseq * p.HV)), dim3(256), 0, s,
+                               a, (int)p.NT, p.HV, KD * VD);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(dscale_kernel, dim3((unsigned)(nseq * p.HV)), dim3(256), 0, s, a, p.HV);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
     if (p.maxS > 1) {
         if constexpr (sizeof(S) == 2) {
             ScanArgs a1 = a;   // local scans write only their final states

@@ -156,6 +156,33 @@ def test_segmented_matches_unsegmented(B):
         assert e <= 5e-3, (name, e)
 
 
+# Magnitude cases for the 16-bit scan operands.  The reverse scans narrow dO and
+# the state to fp16; they run scaled per (sequence, value head) by a power of
+# two, so gradients far below fp16's normal range keep their precision.  The
+# backward is linear in (dO, dht), so the same rel-L2 limits apply.
+MAG_CASES = {
+    # name: (T, HK, HV, lengths, extra, dO/dht factor, v factor)
+    "bf16_dO_dht_1e-6": (700, 2, 2, None, {"gate_scale": 1 / 16}, 1e-6, 1.0),
+    "bf16_dO_dht_1e-9_varlen_gqa": (None, 1, 2, [300, 5, 530, 64], {"gate_scale": 1 / 16, "h0": True}, 1e-9, 1.0),
+    "bf16_v_dO_x256_slow_gate_T4096": (4096, 1, 1, None, {"gate_scale": 1 / 64}, 256.0, 256.0),
+}
+
+
+@pytest.mark.parametrize("name", list(MAG_CASES))
+def test_magnitude_parity(B, oracle, name):
+    T, HK, HV, lens, extra, fo, fv = MAG_CASES[name]
+    _log(f"[parity] {name}: T={T} HK={HK} HV={HV} lens={lens} {extra} dO,dht x{fo} v x{fv}")
+    inp = W.gdr_inputs(1, T, HK, HV, 128, 128, dtype="bf16", seed=5, lengths=lens, **extra)
+    inp["dO"] = (inp["dO"].float() * fo).to(inp["dO"].dtype)
+    inp["dht"] = inp["dht"] * fo
+    inp["v"] = (inp["v"].float() * fv).to(inp["v"].dtype)
+    got = _run_gpu(B, inp)
+    for nm in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert np.isfinite(got[nm]).all(), nm
+    ref = _run_oracle(oracle, inp)
+    _compare(got, ref, "bf16", label=name)
+
+
 def test_dht_null_equals_zero(B):
     _log("[parity] dht NULL vs explicit zeros")
     inp = W.gdr_inputs(1, 256, 2, 2, 64, 64, dtype="f32", seed=0, dht=False)
