@@ -141,7 +141,6 @@ WsPlan plan_workspace(const Problem& p) {
     w.P = off; off = align256(off + segbuf);
     w.hstart = off; off = align256(off + segbuf);
     w.dhin = off; off = align256(off + segbuf);
-    w.gsum = off; off = align256(off + (p.HV > p.HK ? (size_t)p.NT * p.HK * 2 * 64 * p.K * 4 : 0));
     w.cmax = off; off = align256(off + (size_t)(p.NT > 0 ? p.NT : 1) * 4 * p.HV * 4);
     w.hmax = off; off = align256(off + (size_t)p.N * p.HV * 4);
     w.dsc = off; off = align256(off + (size_t)p.N * p.HV * 4);
@@ -369,7 +368,6 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
         g.q = qp; g.k = k; g.v = v; g.gcum = g_cum; g.beta = beta; g.dO = dO;
         g.hT = base + w.h; g.dhT = base + w.dh; g.A = base + w.A; g.info = info;
         g.dq = dq; g.dk = dk; g.dv = dv; g.dg = dg; g.dbeta = dbeta;
-        g.gsum = (float*)(base + w.gsum);
         g.dsc = a.dsc;
         st = launch_status(gdr::launch_grad(q, g, stream));
         if (st != GDR_OK) return st;

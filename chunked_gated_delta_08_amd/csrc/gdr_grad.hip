@@ -336,11 +336,12 @@ __device__ __forceinline__ float sum4g(float x) {
 
 // One launch handles value head hv = hk * G + hi of every (chunk, key head).
 // GRP (G > 1): the launches for hi = 0 .. G-1 run in order on one stream and
-// carry the group sums of dq and dk in an fp32 workspace block per (chunk,
-// key head) (fragment order, each element read back and rewritten only by the
-// lane that owns it): the first launch writes its partials, later ones add
-// theirs, and the last one stores the 16-bit sums.  The order of the sum is
-// fixed, and every launch has the register footprint of a single head.
+// build the group sums of dq and dk in the outputs themselves: the first
+// launch stores its dq, dk; every later one loads the rows stored so far
+// (coalesced, into the LDS staging tiles), adds its own in fp32 and stores
+// the sum.  The order of the sum is fixed, the partial sums are rounded to
+// the output type between launches, no workspace round trip is needed, and
+// every launch has the register footprint of a single head.
 template <class E, int KD, int VD, bool GRP>
 __global__ void __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
@@ -741,6 +742,14 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     gemm4<E, 2, TK, 64, false, true>(dks, sEb, LA, sK, LK, m0, n0k);
     gemm4<E, 2, TK, 64, true, true>(dks, sEb, LA, sK, LK, m0, n0k);
 
+    // ---- GQA: the group's dq, dk stored by the earlier launches (rows in flight
+    //      during the reductions, staged over Q's and dW's regions with them)
+    const bool add_prev = GRP && hi > 0;
+    RowsReg<E, KD, LK> pq, pk;
+    if (add_prev) {
+        pq.load((const E*)a.dq + qrow * KD, (long)HK * KD, Cn);
+        pk.load((const E*)a.dk + qrow * KD, (long)HK * KD, Cn);
+    }
     // ---- reductions (fixed order), over A's region (last read by M1 Aᵀ):
     // rows over the 16 lanes of a group and the two column halves; columns
     // over the 4 row groups and the two row halves
@@ -777,6 +786,10 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         sMisc[w] = hz;   // every lane holds the sum (no branch)
         sMisc[4 + w] = zz;
     }
+    if (add_prev) {   // over Q (last read by T1ᵀ Q) and dW / M1 (last read by M1 Aᵀ)
+        pq.store(sQ);
+        pk.store(sdW);
+    }
     lds_barrier();
     if (threadIdx.x < 64) {
         const int rr = threadIdx.x;
@@ -798,26 +811,6 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         }
         if (rr < Cn) a.dg[(t0 + rr) * HV + hv] = x;
     }
-    if constexpr (GRP) {   // group sums through the workspace block of this (chunk, key head)
-        float* st = a.gsum + ((long)ci * HK + hk) * 2 * 64 * KD;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < TK; j++) {
-                const int tl = (w * 2 + i) * TK + j;
-                f32x4* pq = (f32x4*)(st + (tl * 64 + l) * 4);
-                f32x4* pk = (f32x4*)(st + 64 * KD + (tl * 64 + l) * 4);
-                if (hi > 0) {
-                    dqi[i][j] += *pq;
-                    dks[i][j] += *pk;
-                }
-                if (hi + 1 < G) {
-                    *pq = dqi[i][j];
-                    *pk = dks[i][j];
-                }
-            }
-        if (hi + 1 < G) return;   // uniform: only the last head of the group stores dq, dk
-    }
     // ---- dq, dk through LDS for 16-byte stores: dq over Q's region (last read
     //      by T1ᵀ Q), dk over dW's (M1, last read by M1 Aᵀ)
     E* sdq = sQ;
@@ -831,8 +824,11 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
-                sdq[rr * LK + cc] = to_e<E>(dqi[i][j][e]);
-                sdk[rr * LK + cc] = to_e<E>(dks[i][j][e]);
+                // each element is read and written by the lane that owns it
+                const float pqv = add_prev ? (float)sdq[rr * LK + cc] : 0.f;
+                const float pkv = add_prev ? (float)sdk[rr * LK + cc] : 0.f;
+                sdq[rr * LK + cc] = to_e<E>(dqi[i][j][e] + pqv);
+                sdk[rr * LK + cc] = to_e<E>(dks[i][j][e] + pkv);
             }
     }
     lds_barrier();
@@ -858,7 +854,6 @@ static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
 template <class E, int KD, int VD>
 static hipError_t grad_go(const Problem& p, const GradArgs& a, hipStream_t s) {
     if (p.HV == p.HK) return grad_go1<E, KD, VD, false>(p, a, s);
-    if (!a.gsum) return hipErrorInvalidValue;
     return grad_go1<E, KD, VD, true>(p, a, s);
 }
 

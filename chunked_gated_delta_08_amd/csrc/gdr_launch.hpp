@@ -42,7 +42,7 @@ struct Problem {
 // type, in the first half of each block) are empty when maxS == 1.
 struct WsPlan {
     size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
-    size_t hloc, dhloc, P, hstart, dhin, gsum, cmax, hmax, dsc, total;
+    size_t hloc, dhloc, P, hstart, dhin, cmax, hmax, dsc, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
@@ -110,7 +110,6 @@ struct GradArgs {
     const void* q; const void* k; const void* v; const float* gcum; const void* beta; const void* dO;
     const void* hT; const void* dhT; const void* A; const ChunkInfo* info;
     void* dq; void* dk; void* dv; float* dg; float* dbeta;
-    float* gsum;   // HV > HK: fp32 group-sum blocks, [NT][HK][2][64*K] (fragment order)
     const float* dsc;   // [N][HV] scale of dhT (dh[c] stored times it), or NULL (1)
 };
 hipError_t launch_grad(const Problem& p, const GradArgs& a, hipStream_t s);
