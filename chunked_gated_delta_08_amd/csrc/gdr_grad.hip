@@ -103,6 +103,47 @@ __device__ __forceinline__ int tid_o() {
     return t & (GNT - 1);
 }
 
+// Fragment helpers.  A lane's base pointer into an operand X at rows /
+// columns mn0 (tr: X stored [k][mn], else [mn][k]); fragment n of the k-step
+// at k0 is that base plus a constant offset (16-bit: direct rows mn0 + r,
+// keys 8g..8g+7; transposed reads start at row k0 + 8g + r/4, column
+// mn0 + 4(r%4), and at 4 rows further).
+template <class E, bool TR>
+__device__ __forceinline__ const E* frag_base(const E* X, int ld, int mn0, int l) {
+    const int r = l & 15, g = l >> 4;
+    if constexpr (sizeof(E) == 2)
+        return TR ? X + (8 * g + (r >> 2)) * ld + mn0 + 4 * (r & 3) : X + (mn0 + r) * ld + 8 * g;
+    else
+        return TR ? X + g * ld + mn0 + r : X + (mn0 + r) * ld + g;
+}
+template <class E, int N, bool TR>
+__device__ __forceinline__ void frags(typename Mma<E>::frag (&f)[N], const E* base, int ld, int k0) {
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        if constexpr (sizeof(E) == 2) {
+            if constexpr (!TR) {
+                f[n] = *(const typename Mma<E>::frag*)(base + 16 * n * ld + k0);
+            } else {
+                const E* q = base + k0 * ld + 16 * n;
+                i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
+                i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * ld));
+                i16x8 c = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                f[n] = __builtin_bit_cast(typename Mma<E>::frag, c);
+            }
+        } else {
+            f[n] = TR ? base[k0 * ld + 16 * n] : base[16 * n * ld + k0];
+        }
+    }
+}
+template <class E, int TM, int TN>
+__device__ __forceinline__ void mma_tiles(f32x4 (&acc)[TM][TN], const typename Mma<E>::frag (&fa)[TM],
+                                          const typename Mma<E>::frag (&fb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = Mma<E>::run(fa[i], fb[j], acc[i][j]);
+}
+
 // Wave-level product acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD
 // (AT: A stored [k][m], else [m][k]; BT_: B stored [k][n], else [n][k]); one
 // k-step of fragments in registers at a time (the other workgroup on the CU
@@ -110,44 +151,15 @@ __device__ __forceinline__ int tid_o() {
 template <class E, int TM, int TN, int KD, bool AT, bool BT_>
 __device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0, int n0) {
     using M = Mma<E>;
-    using frag = typename M::frag;
-    constexpr int NS = KD / M::KS;
-    const int l = lane_o(), r = l & 15, g = l >> 4;
-    // one lane base per operand; every fragment is that base plus a constant
-    // offset (16-bit: direct rows (mn0 + r), keys 8g..8g+7; transposed reads
-    // start at row k0 + 8g + r/4, column mn0 + 4(r%4), and at 4 rows further)
-    const E* pa;
-    const E* pb;
-    if constexpr (sizeof(E) == 2) {
-        pa = AT ? A + (8 * g + (r >> 2)) * lda + m0 + 4 * (r & 3) : A + (m0 + r) * lda + 8 * g;
-        pb = BT_ ? B + (8 * g + (r >> 2)) * ldb + n0 + 4 * (r & 3) : B + (n0 + r) * ldb + 8 * g;
-    } else {
-        pa = AT ? A + g * lda + m0 + r : A + (m0 + r) * lda + g;
-        pb = BT_ ? B + g * ldb + n0 + r : B + (n0 + r) * ldb + g;
-    }
-    auto frag_at = [&](const E* base, int ld, bool tr, int mn, int k0) -> frag {
-        if constexpr (sizeof(E) == 2) {
-            if (!tr) return *(const frag*)(base + mn * ld + k0);
-            const E* q = base + k0 * ld + mn;
-            i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
-            i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * ld));
-            i16x8 c = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            return __builtin_bit_cast(frag, c);
-        } else {
-            return tr ? base[k0 * ld + mn] : base[mn * ld + k0];
-        }
-    };
+    const int l = lane_o();
+    const E* pa = frag_base<E, AT>(A, lda, m0, l);
+    const E* pb = frag_base<E, BT_>(B, ldb, n0, l);
 #pragma unroll
-    for (int s = 0; s < NS; s++) {
-        frag fa[TM], fb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; i++) fa[i] = frag_at(pa, lda, AT, 16 * i, s * M::KS);
-#pragma unroll
-        for (int j = 0; j < TN; j++) fb[j] = frag_at(pb, ldb, BT_, 16 * j, s * M::KS);
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int j = 0; j < TN; j++) acc[i][j] = M::run(fa[i], fb[j], acc[i][j]);
+    for (int s = 0; s < KD / M::KS; s++) {
+        typename M::frag fa[TM], fb[TN];
+        frags<E, TM, AT>(fa, pa, lda, s * M::KS);
+        frags<E, TN, BT_>(fb, pb, ldb, s * M::KS);
+        mma_tiles<E>(acc, fa, fb);
     }
 }
 
@@ -172,6 +184,27 @@ __device__ __forceinline__ T* at32(T* base, unsigned off) {
 template <class T>
 __device__ __forceinline__ const T* at32(const T* base, unsigned off) {
     return (const T*)((const char*)base + off * (unsigned)sizeof(T));
+}
+
+// Stores this lane's four accumulator values v[e] (rows rbase + e, column col
+// of a 16-column tile, col's parity = the lane's) as pairs of adjacent
+// columns: lanes col and col^1 swap two values (DPP), so every lane writes two
+// 2-element stores and no two lanes write into the same dword (even lanes:
+// rows rbase, rbase+1; odd lanes: rows rbase+2, rbase+3).
+template <class E>
+__device__ __forceinline__ void st_pair4(E* tile, int ld, int rbase, int col, const float (&v)[4]) {
+    const bool odd = col & 1;
+    const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
+    const float p0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xf, 0xf, true));
+    const float p1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xf, 0xf, true));
+    const int r0 = rbase + (odd ? 2 : 0), c0 = col - (odd ? 1 : 0);
+    E2<E> x, y;
+    x.x = to_e<E>(odd ? p0 : v[0]);
+    x.y = to_e<E>(odd ? v[2] : p0);
+    y.x = to_e<E>(odd ? p1 : v[1]);
+    y.y = to_e<E>(odd ? v[3] : p1);
+    *(E2<E>*)(tile + r0 * ld + c0) = x;
+    *(E2<E>*)(tile + (r0 + 1) * ld + c0) = y;
 }
 
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
@@ -444,13 +477,16 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++) {
+                float sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
                     const float gm = (cc <= rr) ? __expf(sG[rr] - sG[cc]) : 0.f;
-                    sPm[rr * LA + cc] = to_e<E>((cc <= rr) ? scale * gm * aqk[i][j][e] : 0.f);
+                    sv[e] = (cc <= rr) ? scale * gm * aqk[i][j][e] : 0.f;
                 }
+                st_pair4<E>(sPm, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+            }
     }
     // ---- A = (I+L)^{-1} from the prep kernel
     rA.store(sA);
@@ -495,36 +531,54 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         }
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
-        // ---- K h  ->  Z = diag(β)(V − diag(γ) K h)
+        // ---- K h and K dh (one read of K's fragments for both);
+        //      Z = diag(β)(V − diag(γ) K h)
+        f32x4 kdh[2][1];
         {
             f32x4 kh[2][1];
             zero_acc(kh);
-            gemm4<E, 2, 1, KD, false, false>(kh, sK, LK, sH, LK, m0, n0v);
+            zero_acc(kdh);
+            {
+                const int l = lane_o();
+                const E* pk = frag_base<E, false>(sK, LK, m0, l);
+                const E* ph = frag_base<E, false>(sH, LK, n0v, l);
+                const E* pd = frag_base<E, false>(sdH, LK, n0v, l);
+#pragma unroll
+                for (int s = 0; s < KD / Mma<E>::KS; s++) {
+                    typename Mma<E>::frag fk[2], fh[1], fd[1];
+                    frags<E, 2, false>(fk, pk, LK, s * Mma<E>::KS);
+                    frags<E, 1, false>(fh, ph, LK, s * Mma<E>::KS);
+                    frags<E, 1, false>(fd, pd, LK, s * Mma<E>::KS);
+                    mma_tiles<E>(kh, fk, fh);
+                    mma_tiles<E>(kdh, fk, fd);
+                }
+            }
             GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < 2; i++) {
+                float sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0v + cb);
-                    sZ[rr * LS + cc] = to_e<E>(sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]));
+                    sv[e] = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]);
                 }
+                st_pair4<E>(sZ, LS, rb + 16 * i, n0v + cb, sv);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // ---- dV_new = Pmᵀ dO + diag(γ_C/γ) K dh
         {
-            f32x4 kdh[2][1], pdo[2][1];
-            zero_acc(kdh);
+            f32x4 pdo[2][1];
             zero_acc(pdo);
-            gemm4<E, 2, 1, KD, false, false>(kdh, sK, LK, sdH, LK, m0, n0v);
             gemm4<E, 2, 1, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0v);
             GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < 2; i++) {
+                float sv[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
-                    sdVn[rr * LS + cc] = to_e<E>(pdo[i][0][e] + sEg[rr] * kdh[i][0][e]);
-                }
+                for (int e = 0; e < 4; e++) sv[e] = pdo[i][0][e] + sEg[rb + 16 * i + e] * kdh[i][0][e];
+                st_pair4<E>(sdVn, LS, rb + 16 * i, n0v + cb, sv);
+            }
         }
         lds_barrier();
         // ---- V_new = A Z
@@ -534,24 +588,57 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             gemm4<E, 2, 1, 64, false, true>(vn, sA, LA, sZ, LS, m0, n0v);
             GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) sVn[(rb + 16 * i + e) * LS + (n0v + cb)] = to_e<E>(vn[i][0][e]);
+            for (int i = 0; i < 2; i++) {
+                const float sv[4] = {vn[i][0][0], vn[i][0][1], vn[i][0][2], vn[i][0][3]};
+                st_pair4<E>(sVn, LS, rb + 16 * i, n0v + cb, sv);
+            }
         }
         lds_barrier();
-        // ---- the state products and the V-separable outputs (one 32-deep
-        // step each; scheduling fences keep each product's fragments out of
-        // the others' live ranges -- the accumulators take half the registers)
-        gemm4<E, 2, 2, VS, false, false>(dPm, sdO, LS, sVn, LS, m0, n0s);    // dO V_newᵀ
-        __builtin_amdgcn_sched_barrier(0);
-        gemm4<E, 2, TK, VS, false, true>(dqi, sdO, LS, sH, LK, m0, n0k);     // dO hᵀ
-        __builtin_amdgcn_sched_barrier(0);
-        gemm4<E, 2, TK, VS, false, true>(dWa, sdVn, LS, sH, LK, m0, n0k);    // dV_new hᵀ
-        __builtin_amdgcn_sched_barrier(0);
-        gemm4<E, 2, TK, VS, false, true>(dks, sVn, LS, sdH, LK, m0, n0k);    // V_new dhᵀ
-        __builtin_amdgcn_sched_barrier(0);
-        gemm4<E, 2, 2, VS, false, false>(dAz, sdVn, LS, sZ, LS, m0, n0s);    // dV_new Zᵀ
-        __builtin_amdgcn_sched_barrier(0);
+        // ---- the state products and the V-separable outputs over the slice:
+        //      dqi += dO hᵀ, dWa += dV_new hᵀ (one read of h), dPm += dO V_newᵀ,
+        //      dAz += dV_new Zᵀ (the dO and dV_new fragments read once), dks +=
+        //      V_new dhᵀ; scheduling fences keep each group's fragments out of
+        //      the others' live ranges (the accumulators take half the registers)
+        {
+            using frag = typename Mma<E>::frag;
+            constexpr int KS = Mma<E>::KS;
+            const int l = lane_o();
+            const E* pO = frag_base<E, false>(sdO, LS, m0, l);
+            const E* pD = frag_base<E, false>(sdVn, LS, m0, l);
+            const E* pN = frag_base<E, false>(sVn, LS, m0, l);
+            const E* pHt = frag_base<E, true>(sH, LK, n0k, l);
+            const E* pdHt = frag_base<E, true>(sdH, LK, n0k, l);
+            const E* pNb = frag_base<E, false>(sVn, LS, n0s, l);
+            const E* pZb = frag_base<E, false>(sZ, LS, n0s, l);
+#pragma unroll
+            for (int s = 0; s < VS / KS; s++) {
+                frag fo[2], fd[2];
+                frags<E, 2, false>(fo, pO, LS, s * KS);
+                frags<E, 2, false>(fd, pD, LS, s * KS);
+                {
+                    frag fh[TK];
+                    frags<E, TK, true>(fh, pHt, LK, s * KS);
+                    mma_tiles<E>(dqi, fo, fh);
+                    mma_tiles<E>(dWa, fd, fh);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                {
+                    frag fn[2], fz[2];
+                    frags<E, 2, false>(fn, pNb, LS, s * KS);
+                    frags<E, 2, false>(fz, pZb, LS, s * KS);
+                    mma_tiles<E>(dPm, fo, fn);
+                    mma_tiles<E>(dAz, fd, fz);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                {
+                    frag fa[2], fh[TK];
+                    frags<E, 2, false>(fa, pN, LS, s * KS);
+                    frags<E, TK, true>(fh, pdHt, LK, s * KS);
+                    mma_tiles<E>(dks, fa, fh);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         {
             f32x4 adv[2][1];
             zero_acc(adv);
@@ -575,8 +662,8 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
                     d[e] = sB[rr] * adv[i][0][e];
                 }
                 const float s0 = odd ? d[0] : d[2], s1 = odd ? d[1] : d[3];
-                const float p0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
-                const float p1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+                const float p0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xf, 0xf, true));
+                const float p1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xf, 0xf, true));
                 // even lanes: rows e = 0, 1 at columns (r, r+1); odd lanes: rows e = 2, 3 at (r-1, r)
                 const int e0 = odd ? 2 : 0;
                 const int c0 = n0v + r - odd;
@@ -616,7 +703,8 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++) {
+                float sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
@@ -625,8 +713,11 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
                     const float f = dp * (float)sPm[rr * LA + cc];
                     rowG[i][e] += f;
                     colG[j] += f;
-                    sPm[rr * LA + cc] = to_e<E>(lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f);
+                    sv[e] = lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f;
                 }
+                // the tile's reads above all precede its pair stores (they feed the exchange)
+                st_pair4<E>(sPm, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+            }
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -636,16 +727,18 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < TK; j++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) sdW[(rb + 16 * i + e) * LK + (n0k + 16 * j + cb)] = to_e<E>(-dWa[i][j][e]);
+            for (int j = 0; j < TK; j++) {
+                const float sv[4] = {-dWa[i][j][0], -dWa[i][j][1], -dWa[i][j][2], -dWa[i][j][3]};
+                st_pair4<E>(sdW, LK, rb + 16 * i, n0k + 16 * j + cb, sv);
+            }
         // ---- dA_pre -> LDS
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) sdA[(rb + 16 * i + e) * LA + (n0s + 16 * j + cb)] = to_e<E>(dAz[i][j][e]);
+            for (int j = 0; j < 2; j++) {
+                const float sv[4] = {dAz[i][j][0], dAz[i][j][1], dAz[i][j][2], dAz[i][j][3]};
+                st_pair4<E>(sdA, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+            }
     }
     lds_barrier();
     E* sT1 = sPm;
@@ -706,9 +799,10 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) sM1[(rb + 16 * i + e) * LA + (n0s + 16 * j + cb)] = to_e<E>(m1[i][j][e]);
+            for (int j = 0; j < 2; j++) {
+                const float sv[4] = {m1[i][j][0], m1[i][j][1], m1[i][j][2], m1[i][j][3]};
+                st_pair4<E>(sM1, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+            }
     }
     lds_barrier();
     // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ (over dA, last read above)
@@ -722,7 +816,8 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++) {
+                float sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
@@ -733,8 +828,10 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
                     const float f2 = d * sB[rr] * lg;
                     rowG[i][e] += f2;
                     colG[j] += f2;
-                    sEb[rr * LA + cc] = to_e<E>(lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f);
+                    sv[e] = lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f;
                 }
+                st_pair4<E>(sEb, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+            }
         pin_rows(rowG, rowB, colG, zsum);
     }
     lds_barrier();
@@ -820,16 +917,19 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < TK; j++)
+        for (int j = 0; j < TK; j++) {
+            // each element is read by the lane that owns it; the pair stores
+            // consume the read values, so every read precedes the overwrite
+            float sq[4], sk[4];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
-                // each element is read and written by the lane that owns it
-                const float pqv = add_prev ? (float)sdq[rr * LK + cc] : 0.f;
-                const float pkv = add_prev ? (float)sdk[rr * LK + cc] : 0.f;
-                sdq[rr * LK + cc] = to_e<E>(dqi[i][j][e] + pqv);
-                sdk[rr * LK + cc] = to_e<E>(dks[i][j][e] + pkv);
+                sq[e] = dqi[i][j][e] + (add_prev ? (float)sdq[rr * LK + cc] : 0.f);
+                sk[e] = dks[i][j][e] + (add_prev ? (float)sdk[rr * LK + cc] : 0.f);
             }
+            st_pair4<E>(sdq, LK, rb + 16 * i, n0k + 16 * j + cb, sq);
+            st_pair4<E>(sdk, LK, rb + 16 * i, n0k + 16 * j + cb, sk);
+        }
     }
     lds_barrier();
     store_rows<E, KD, LK>((E*)a.dq + qrow * KD, (long)HK * KD, sdq, Cn);
