@@ -56,8 +56,8 @@ struct GradCfg {
     // byte offsets.  The Q region holds the V slice, Z and V_new of the
     // current slice during the value loop (Q is reloaded after it).
     static constexpr size_t szK = (size_t)C * LK * es;
-    static constexpr size_t szQ = (size_t)C * LK * es > (size_t)3 * C * LS * es + 2 * 64 * 4
-                                      ? (size_t)C * LK * es : (size_t)3 * C * LS * es + 2 * 64 * 4;
+    static constexpr size_t szQ = (size_t)C * LK * es > (size_t)3 * C * LS * es ? (size_t)C * LK * es
+                                                                                 : (size_t)3 * C * LS * es;
     static constexpr size_t szA = (size_t)C * LA * es;
     static constexpr size_t szH = (size_t)VS * LK * es;
     static constexpr size_t szS = (size_t)C * LS * es;
@@ -71,10 +71,8 @@ struct GradCfg {
     static constexpr size_t odVn = odO + szS;
     static constexpr size_t oSm = odVn + szS;              // G, γ, β, e^{G_C−G}: 4 x 64 floats
     static constexpr size_t smem = oSm + 4 * 64 * 4;
-    // slice buffers inside the Q region, and behind them (during the value
-    // loop only) the loop's dβ row partials, [2 column halves][64] floats
-    static constexpr size_t oV = oQ, oZ = oQ + szS, oVn = oQ + 2 * szS, oRowL = oQ + 3 * szS;
-    static_assert(3 * szS + 2 * 64 * 4 <= szQ, "row partials behind the slice buffers");
+    // slice buffers inside the Q region
+    static constexpr size_t oV = oQ, oZ = oQ + szS, oVn = oQ + 2 * szS;
     // post-loop aliases: dW [64][LK] over H + dH, dA [64][LA] over dO + dV_new,
     // M1 over dW (after dW's last use), Eb over dA (after M1), the final
     // reductions over A (after its last use), dq staged in Q's region and dk in dW's
@@ -135,13 +133,17 @@ __device__ __forceinline__ void frags(typename Mma<E>::frag (&f)[N], const E* ba
         }
     }
 }
+// acc[i][j] += A-tile i times B-tile j, run as (Bᵀ Aᵀ)ᵀ: the MFMA takes the B
+// fragment as its first operand, so the tile comes out in row form: lane
+// 16g + r holds row r and columns 4g .. 4g+3 of the tile (four adjacent
+// columns of one row: whole 8-byte stores, and one row per lane).
 template <class E, int TM, int TN>
 __device__ __forceinline__ void mma_tiles(f32x4 (&acc)[TM][TN], const typename Mma<E>::frag (&fa)[TM],
                                           const typename Mma<E>::frag (&fb)[TN]) {
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = Mma<E>::run(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; j++) acc[i][j] = Mma<E>::run(fb[j], fa[i], acc[i][j]);
 }
 
 // Wave-level product acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD
@@ -163,16 +165,15 @@ __device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda,
     }
 }
 
-// Row base and column of this lane's accumulator elements, from a fresh lane
-// index (one per element-wise phase): element e of tile (i, j) of a wave
-// block at (m0, n0) is row rb + 16 i + e, column n0 + 16 j + cb.
+// Row and column offset of this lane's accumulator elements, from a fresh
+// lane index (one per element-wise phase): element e of tile (i, j) of a
+// wave block at (m0, n0) is row rw + 16 i, column n0 + 16 j + cg + e.
 #define GRAD_LANE_RC()                          \
     const int lq_ = lane_o();                   \
-    const int rb = m0 + 4 * (lq_ >> 4);         \
-    const int cb = lq_ & 15
+    const int rw = m0 + (lq_ & 15);             \
+    const int cg = 4 * (lq_ >> 4)
 
 // Two adjacent 16-bit (or fp32) elements, stored as one access.
-template <class E> struct __attribute__((aligned(2 * sizeof(E)))) E2 { E x, y; };
 
 // base + off elements, with the byte offset formed in 32 bits: a uniform base
 // and a 32-bit per-lane offset map onto the scalar-base addressing of global
@@ -186,25 +187,18 @@ __device__ __forceinline__ const T* at32(const T* base, unsigned off) {
     return (const T*)((const char*)base + off * (unsigned)sizeof(T));
 }
 
-// Stores this lane's four accumulator values v[e] (rows rbase + e, column col
-// of a 16-column tile, col's parity = the lane's) as pairs of adjacent
-// columns: lanes col and col^1 swap two values (DPP), so every lane writes two
-// 2-element stores and no two lanes write into the same dword (even lanes:
-// rows rbase, rbase+1; odd lanes: rows rbase+2, rbase+3).
+// Four adjacent elements (one row of a tile in row form) as fp32.
+template <class E> struct Vec4;
+template <> struct Vec4<bf16> { typedef __bf16 t __attribute__((ext_vector_type(4))); };
+template <> struct Vec4<f16> { typedef _Float16 t __attribute__((ext_vector_type(4))); };
+template <> struct Vec4<float> { typedef float t __attribute__((ext_vector_type(4))); };
 template <class E>
-__device__ __forceinline__ void st_pair4(E* tile, int ld, int rbase, int col, const float (&v)[4]) {
-    const bool odd = col & 1;
-    const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
-    const float p0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xf, 0xf, true));
-    const float p1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xf, 0xf, true));
-    const int r0 = rbase + (odd ? 2 : 0), c0 = col - (odd ? 1 : 0);
-    E2<E> x, y;
-    x.x = to_e<E>(odd ? p0 : v[0]);
-    x.y = to_e<E>(odd ? v[2] : p0);
-    y.x = to_e<E>(odd ? p1 : v[1]);
-    y.y = to_e<E>(odd ? v[3] : p1);
-    *(E2<E>*)(tile + r0 * ld + c0) = x;
-    *(E2<E>*)(tile + (r0 + 1) * ld + c0) = y;
+__device__ __forceinline__ f32x4 ld4(const E* p) {
+    return __builtin_convertvector(*(const typename Vec4<E>::t*)p, f32x4);
+}
+template <class E>
+__device__ __forceinline__ void st4(E* p, f32x4 x) {
+    *(typename Vec4<E>::t*)p = __builtin_convertvector(x, typename Vec4<E>::t);
 }
 
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
@@ -347,16 +341,14 @@ __device__ __forceinline__ float sum16(float x) {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 // Pins the per-lane partials after a phase that updated them (see pin).
-__device__ __forceinline__ void pin_rows(float (&rg)[2][4], float (&rb)[2][4], float (&cg)[2], float& z) {
+__device__ __forceinline__ void pin_rows(float (&rg)[2], float (&rb)[2], float (&cs)[2][4], float& z) {
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        pin(rg[i]);
+        pin(rb[i]);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            pin(rg[i][e]);
-            pin(rb[i][e]);
-        }
-    pin(cg[0]);
-    pin(cg[1]);
+        for (int e = 0; e < 4; e++) pin(cs[i][e]);
+    }
     pin(z);
 }
 
@@ -401,7 +393,6 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     float* sB = sGam + 64;
     float* sEg = sB + 64;   // e^{G_C − G_r}: the factor γ_C/γ
     float* sRed = (float*)(smem + Cf::oRed);   // row partials of dG, dβ [2][64] each, column partials [2][64], misc [8]
-    float* sRowL = (float*)(smem + Cf::oRowL); // the value loop's dβ row partials [2][64]
 
     const int ci = blockIdx.x, hk = blockIdx.y, G = GRP ? HV / HK : 1;
     const ChunkInfo ch = a.info[ci];
@@ -459,13 +450,15 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     const float idsc = a.dsc ? 1.f / a.dsc[(long)ch.seq * HV + hv] : 1.f;
     if (threadIdx.x < C) sEg[threadIdx.x] = idsc * __expf(gl - sG[threadIdx.x]);   // read after the next barrier
 
-    // per-lane partial row sums (rows m0 + 16i + 4g + e) and column sums
-    float rowG[2][4], rowB[2][4], colG[2];
+    // per-lane partial row sums (rows rw + 16i) and column sums (columns
+    // n0s + 16j + cg + e of the [64][64] results)
+    float rowG[2], rowB[2], colG[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        rowG[i] = rowB[i] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; e++) rowG[i][e] = rowB[i][e] = 0.f;
-    colG[0] = colG[1] = 0.f;
+        for (int e = 0; e < 4; e++) colG[i][e] = 0.f;
+    }
     float hdh = 0.f;   // partial <dh, h>
 
     // ---- Pm = scale · lower(Γ ⊙ Q Kᵀ)
@@ -475,18 +468,19 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         gemm4<E, 2, 2, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0s);
         GRAD_LANE_RC();
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rw + 16 * i;
+            const float gr = sG[rr];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                float sv[4];
+                const int c0 = n0s + 16 * j + cg;
+                const f32x4 gc = *(const f32x4*)(sG + c0);
+                f32x4 sv;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
-                    const float gm = (cc <= rr) ? __expf(sG[rr] - sG[cc]) : 0.f;
-                    sv[e] = (cc <= rr) ? scale * gm * aqk[i][j][e] : 0.f;
-                }
-                st_pair4<E>(sPm, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+                for (int e = 0; e < 4; e++) sv[e] = (c0 + e <= rr) ? scale * __expf(gr - gc[e]) * aqk[i][j][e] : 0.f;
+                st4<E>(sPm + rr * LA + c0, sv);
             }
+        }
     }
     // ---- A = (I+L)^{-1} from the prep kernel
     rA.store(sA);
@@ -514,7 +508,6 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             rdO.store(sdO);
             lds_barrier();        // Pm has read Q: the slice buffers may take its region
             rV.store(sV);
-            if (threadIdx.x < 128) sRowL[threadIdx.x] = 0.f;
         } else {
             nH.store(sH);
             ndH.store(sdH);
@@ -556,13 +549,13 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             GRAD_LANE_RC();
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                float sv[4];
+                const int rr = rw + 16 * i, c0 = n0v + cg;
+                const f32x4 vv = ld4<E>(sV + rr * LS + c0);
+                const float br = sB[rr], gr = sGam[rr];
+                f32x4 sv;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
-                    sv[e] = sB[rr] * ((float)sV[rr * LS + cc] - sGam[rr] * kh[i][0][e]);
-                }
-                st_pair4<E>(sZ, LS, rb + 16 * i, n0v + cb, sv);
+                for (int e = 0; e < 4; e++) sv[e] = br * (vv[e] - gr * kh[i][0][e]);
+                st4<E>(sZ + rr * LS + c0, sv);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -574,10 +567,8 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             GRAD_LANE_RC();
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                float sv[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) sv[e] = pdo[i][0][e] + sEg[rb + 16 * i + e] * kdh[i][0][e];
-                st_pair4<E>(sdVn, LS, rb + 16 * i, n0v + cb, sv);
+                const int rr = rw + 16 * i;
+                st4<E>(sdVn + rr * LS + n0v + cg, pdo[i][0] + sEg[rr] * kdh[i][0]);
             }
         }
         lds_barrier();
@@ -588,10 +579,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             gemm4<E, 2, 1, 64, false, true>(vn, sA, LA, sZ, LS, m0, n0v);
             GRAD_LANE_RC();
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const float sv[4] = {vn[i][0][0], vn[i][0][1], vn[i][0][2], vn[i][0][3]};
-                st_pair4<E>(sVn, LS, rb + 16 * i, n0v + cb, sv);
-            }
+            for (int i = 0; i < 2; i++) st4<E>(sVn + (rw + 16 * i) * LS + n0v + cg, vn[i][0]);
         }
         lds_barrier();
         // ---- the state products and the V-separable outputs over the slice:
@@ -643,54 +631,26 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             f32x4 adv[2][1];
             zero_acc(adv);
             gemm4<E, 2, 1, 64, true, true>(adv, sA, LA, sdVn, LS, m0, n0v);  // Aᵀ dV_new
-            // dv = diag(β) Aᵀ dV_new, stored from the accumulators: lanes r and
-            // r^1 swap two rows each so that every lane writes two adjacent
-            // columns (4 bytes) of two rows
+            // dv = diag(β) Aᵀ dV_new, stored from the accumulators (four adjacent
+            // columns of a row per lane: one 8-byte store); the row sums of
+            // Aᵀ dV_new ⊙ V (dβ) accumulate in the lane's row partials
             GRAD_LANE_RC();
-            const int r = cb, odd = r & 1;
             E* dvb = (E*)a.dv + vrow * VD + vs * VS;
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                float d[4];
+                const int rr = rw + 16 * i, c0 = n0v + cg;
+                const f32x4 vv = ld4<E>(sV + rr * LS + c0);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0v + cb);
-                    // rowsum(Aᵀ dV_new ⊙ V) of this slice into the wave's own slots
-                    // (every lane of the row group holds the sum and writes it)
-                    const float rbs = sum16(adv[i][0][e] * (float)sV[rr * LS + cc]);
-                    sRowL[wc * 64 + rr] += rbs;
-                    d[e] = sB[rr] * adv[i][0][e];
-                }
-                const float s0 = odd ? d[0] : d[2], s1 = odd ? d[1] : d[3];
-                const float p0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xf, 0xf, true));
-                const float p1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xf, 0xf, true));
-                // even lanes: rows e = 0, 1 at columns (r, r+1); odd lanes: rows e = 2, 3 at (r-1, r)
-                const int e0 = odd ? 2 : 0;
-                const int c0 = n0v + r - odd;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; h2++) {
-                    const int rr = rb + 16 * i + e0 + h2;
-                    const float own = odd ? (h2 ? d[3] : d[2]) : (h2 ? d[1] : d[0]);
-                    const float oth = h2 ? p1 : p0;
-                    E2<E> pr;
-                    pr.x = to_e<E>(odd ? oth : own);
-                    pr.y = to_e<E>(odd ? own : oth);
-                    if (rr < Cn) *(E2<E>*)at32(dvb, __umul24((unsigned)rr, (unsigned)(HV * VD)) + (unsigned)c0) = pr;
-                }
+                for (int e = 0; e < 4; e++) rowB[i] += adv[i][0][e] * vv[e];
+                const f32x4 d = sB[rr] * adv[i][0];
+                if (rr < Cn) *(typename Vec4<E>::t*)at32(dvb, __umul24((unsigned)rr, (unsigned)(HV * VD)) + (unsigned)c0) =
+                    __builtin_convertvector(d, typename Vec4<E>::t);
             }
+            pin(rowB[0]);
+            pin(rowB[1]);
         }
         lds_barrier();   // the slice buffers are read before the next slice overwrites them
     }
-    // the loop's dβ partials into lane 0 of each row group (the final reduction sums the 16 lanes)
-    {
-        GRAD_LANE_RC();
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) rowB[i][e] = cb == 0 ? sRowL[wc * 64 + (rb + 16 * i + e)] : 0.f;
-    }
-    lds_barrier();   // every wave has read its slots before Q returns over them
-
     // ---- Q back into its region (it held the slice buffers)
     {
         RowsReg<E, KD, LK> nQ;
@@ -701,44 +661,37 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     {
         GRAD_LANE_RC();
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rw + 16 * i;
+            const float gr = sG[rr];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                float sv[4];
+                const int c0 = n0s + 16 * j + cg;
+                const f32x4 gc = *(const f32x4*)(sG + c0);
+                const f32x4 pm = ld4<E>(sPm + rr * LA + c0);
+                f32x4 sv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
-                    const bool lo = cc <= rr;
+                    const bool lo = c0 + e <= rr;
                     const float dp = lo ? dPm[i][j][e] : 0.f;
-                    const float f = dp * (float)sPm[rr * LA + cc];
-                    rowG[i][e] += f;
-                    colG[j] += f;
-                    sv[e] = lo ? dp * scale * __expf(sG[rr] - sG[cc]) : 0.f;
+                    const float f = dp * pm[e];
+                    rowG[i] += f;
+                    colG[j][e] += f;
+                    sv[e] = lo ? dp * scale * __expf(gr - gc[e]) : 0.f;
                 }
-                // the tile's reads above all precede its pair stores (they feed the exchange)
-                st_pair4<E>(sPm, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+                st4<E>(sPm + rr * LA + c0, sv);   // the lane's own elements, read just above
             }
+        }
+        pin_rows(rowG, rowB, colG, hdh);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) pin(rowG[i][e]);
-        pin(colG[0]);
-        pin(colG[1]);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < TK; j++) {
-                const float sv[4] = {-dWa[i][j][0], -dWa[i][j][1], -dWa[i][j][2], -dWa[i][j][3]};
-                st_pair4<E>(sdW, LK, rb + 16 * i, n0k + 16 * j + cb, sv);
-            }
+            for (int j = 0; j < TK; j++) st4<E>(sdW + (rw + 16 * i) * LK + n0k + 16 * j + cg, -dWa[i][j]);
         // ---- dA_pre -> LDS
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const float sv[4] = {dAz[i][j][0], dAz[i][j][1], dAz[i][j][2], dAz[i][j][3]};
-                st_pair4<E>(sdA, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
-            }
+            for (int j = 0; j < 2; j++) st4<E>(sdA + (rw + 16 * i) * LA + n0s + 16 * j + cg, dAz[i][j]);
     }
     lds_barrier();
     E* sT1 = sPm;
@@ -747,16 +700,18 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     {
     GRAD_LANE_RC();
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        const int rr = rw + 16 * i;
+        const float sg = scale * sGam[rr];
 #pragma unroll
-        for (int j = 0; j < TK; j++)
+        for (int j = 0; j < TK; j++) {
+            const f32x4 qv = ld4<E>(sQ + rr * LK + n0k + 16 * j + cg);
+            const f32x4 di = sg * dqi[i][j];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
-                const float di = scale * sGam[rr] * dqi[i][j][e];
-                rowG[i][e] += di * (float)sQ[rr * LK + cc];
-                dqi[i][j][e] = di;
-            }
+            for (int e = 0; e < 4; e++) rowG[i] += di[e] * qv[e];
+            dqi[i][j] = di;
+        }
+    }
     }
     float zsum = 0.f;
     pin_rows(rowG, rowB, colG, zsum);
@@ -769,22 +724,24 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         gemm4<E, 2, TK, 64, true, true>(adw, sA, LA, sdW, LK, m0, n0k);
         GRAD_LANE_RC();
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rw + 16 * i;
+            const float eg = sEg[rr], gr = sGam[rr], bg = sB[rr] * gr;
 #pragma unroll
-            for (int j = 0; j < TK; j++)
+            for (int j = 0; j < TK; j++) {
+                const f32x4 kv = ld4<E>(sK + rr * LK + n0k + 16 * j + cg);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
-                    const float kv = (float)sK[rr * LK + cc];
-                    const float ds = sEg[rr] * dks[i][j][e];
-                    const float z = ds * kv;
-                    rowG[i][e] -= z;
+                    const float ds = eg * dks[i][j][e];
+                    const float z = ds * kv[e];
+                    const float aw = adw[i][j][e] * kv[e];
+                    rowG[i] += bg * aw - z;
                     zsum += z;
-                    const float aw = adw[i][j][e] * kv;
-                    rowB[i][e] += sGam[rr] * aw;
-                    rowG[i][e] += sB[rr] * sGam[rr] * aw;
-                    dks[i][j][e] = ds + sB[rr] * sGam[rr] * adw[i][j][e];
+                    rowB[i] += gr * aw;
+                    dks[i][j][e] = ds + bg * adw[i][j][e];
                 }
+            }
+        }
         pin_rows(rowG, rowB, colG, zsum);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -799,10 +756,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const float sv[4] = {m1[i][j][0], m1[i][j][1], m1[i][j][2], m1[i][j][3]};
-                st_pair4<E>(sM1, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
-            }
+            for (int j = 0; j < 2; j++) st4<E>(sM1 + (rw + 16 * i) * LA + n0s + 16 * j + cg, m1[i][j]);
     }
     lds_barrier();
     // ---- dL = −strictlower(M1 Aᵀ); dβ, dG (F2); Eb = diag(β) dL ⊙ Γ (over dA, last read above)
@@ -814,24 +768,29 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         gemm4<E, 2, 2, KD, false, false>(akk, sK, LK, sK, LK, m0, n0s);   // K Kᵀ (recomputed)
         GRAD_LANE_RC();
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rw + 16 * i;
+            const float gr = sG[rr], br = sB[rr];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                float sv[4];
+                const int c0 = n0s + 16 * j + cg;
+                const f32x4 gc = *(const f32x4*)(sG + c0);
+                f32x4 sv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int rr = (rb + 16 * i + e), cc = (n0s + 16 * j + cb);
-                    const bool lo = cc < rr;
+                    const bool lo = c0 + e < rr;
                     const float d = lo ? -dl[i][j][e] : 0.f;
-                    const float lg = lo ? __expf(sG[rr] - sG[cc]) * akk[i][j][e] : 0.f;   // Γ ⊙ KKᵀ
-                    rowB[i][e] += d * lg;
-                    const float f2 = d * sB[rr] * lg;
-                    rowG[i][e] += f2;
-                    colG[j] += f2;
-                    sv[e] = lo ? sB[rr] * d * __expf(sG[rr] - sG[cc]) : 0.f;
+                    const float ex = __expf(gr - gc[e]);
+                    const float lg = lo ? ex * akk[i][j][e] : 0.f;   // Γ ⊙ KKᵀ
+                    rowB[i] += d * lg;
+                    const float f2 = d * br * lg;
+                    rowG[i] += f2;
+                    colG[j][e] += f2;
+                    sv[e] = lo ? br * d * ex : 0.f;
                 }
-                st_pair4<E>(sEb, LA, rb + 16 * i, n0s + 16 * j + cb, sv);
+                st4<E>(sEb + rr * LA + c0, sv);
             }
+        }
         pin_rows(rowG, rowB, colG, zsum);
     }
     lds_barrier();
@@ -857,21 +816,20 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     {
     GRAD_LANE_RC();
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const float rgs = sum16(rowG[i][e]);
-            const float rbs = sum16(rowB[i][e]);
-            // every lane of the group holds the sum: all write the same value (no branch)
-            const int rr = (rb + 16 * i + e);
-            sRowG[wc * 64 + rr] = rgs;
-            sRowB[wc * 64 + rr] = rbs;
-        }
-#pragma unroll
-    for (int j = 0; j < 2; j++) {   // all four row groups hold the sum and write it (no branch)
-        const float cs = sum4g(colG[j]);
-        sCol[wr * 64 + (n0s + 16 * j + cb)] = cs;
+    for (int i = 0; i < 2; i++) {
+        // every row group holds the sum: all four write the same value (no branch)
+        const float rgs = sum4g(rowG[i]);
+        const float rbs = sum4g(rowB[i]);
+        sRowG[wc * 64 + rw + 16 * i] = rgs;
+        sRowB[wc * 64 + rw + 16 * i] = rbs;
     }
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {   // all 16 lanes of the group hold the sum and write it (no branch)
+            const float cs = sum16(colG[j][e]);
+            sCol[wr * 64 + n0s + 16 * j + cg + e] = cs;
+        }
     }
     {
         float hz = hdh, zz = zsum;
@@ -918,17 +876,11 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < TK; j++) {
-            // each element is read by the lane that owns it; the pair stores
-            // consume the read values, so every read precedes the overwrite
-            float sq[4], sk[4];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = (rb + 16 * i + e), cc = (n0k + 16 * j + cb);
-                sq[e] = dqi[i][j][e] + (add_prev ? (float)sdq[rr * LK + cc] : 0.f);
-                sk[e] = dks[i][j][e] + (add_prev ? (float)sdk[rr * LK + cc] : 0.f);
-            }
-            st_pair4<E>(sdq, LK, rb + 16 * i, n0k + 16 * j + cb, sq);
-            st_pair4<E>(sdk, LK, rb + 16 * i, n0k + 16 * j + cb, sk);
+            // each element is read and written by the lane that owns it
+            const int o = (rw + 16 * i) * LK + n0k + 16 * j + cg;
+            const f32x4 zq = {0.f, 0.f, 0.f, 0.f};
+            st4<E>(sdq + o, dqi[i][j] + (add_prev ? ld4<E>(sdq + o) : zq));
+            st4<E>(sdk + o, dks[i][j] + (add_prev ? ld4<E>(sdk + o) : zq));
         }
     }
     lds_barrier();
