@@ -150,6 +150,51 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[TM][TN]) {
         for (int j = 0; j < TN; j++) acc[i][j] = zero4();
 }
 
+// Row-form wave GEMM: as wgemm, but the MFMA takes the B fragment first, so
+// each tile comes out transposed in the lanes: lane 16g + r holds row r and
+// columns 4g .. 4g+3 of tile (i, j) (four adjacent columns of one row), i.e.
+// element e at row rf_row(m0, i), column rf_col(n0, j) + e.
+template <class E, int TM, int TN, int KD, bool AT, bool BT_>
+__device__ __forceinline__ void wgemm_rf(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0,
+                                         int n0) {
+    using M = Mma<E>;
+    constexpr int NS = KD / M::KS;
+    typename M::frag a[2][TM], b[2][TN];
+    auto load = [&](int buf, int k0) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+            a[buf][i] = AT ? ld_trans<E>(A, lda, m0 + 16 * i, k0) : ld_direct<E>(A, lda, m0 + 16 * i, k0);
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+            b[buf][j] = BT_ ? ld_trans<E>(B, ldb, n0 + 16 * j, k0) : ld_direct<E>(B, ldb, n0 + 16 * j, k0);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        if (s + 1 < NS) load((s + 1) & 1, (s + 1) * M::KS);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) acc[i][j] = M::run(b[s & 1][j], a[s & 1][i], acc[i][j]);
+    }
+}
+__device__ __forceinline__ int rf_row(int m0, int i) { return m0 + 16 * i + (lane_id() & 15); }
+__device__ __forceinline__ int rf_col(int n0, int j) { return n0 + 16 * j + 4 * (lane_id() >> 4); }
+
+// Four adjacent elements (one row of a tile in row form) as fp32, and back.
+template <class E> struct Vec4;
+template <> struct Vec4<bf16> { typedef __bf16 t __attribute__((ext_vector_type(4))); };
+template <> struct Vec4<f16> { typedef _Float16 t __attribute__((ext_vector_type(4))); };
+template <> struct Vec4<float> { typedef float t __attribute__((ext_vector_type(4))); };
+template <class E>
+__device__ __forceinline__ f32x4 ld4(const E* p) {
+    return __builtin_convertvector(*(const typename Vec4<E>::t*)p, f32x4);
+}
+template <class E>
+__device__ __forceinline__ void st4(E* p, f32x4 x) {
+    *(typename Vec4<E>::t*)p = __builtin_convertvector(x, typename Vec4<E>::t);
+}
+
 // Row / column of accumulator element e of tile (i, j) for this lane.
 __device__ __forceinline__ int acc_row(int m0, int i, int e) { return m0 + 16 * i + 4 * (lane_id() >> 4) + e; }
 __device__ __forceinline__ int acc_col(int n0, int j) { return n0 + 16 * j + (lane_id() & 15); }

@@ -187,20 +187,6 @@ __device__ __forceinline__ const T* at32(const T* base, unsigned off) {
     return (const T*)((const char*)base + off * (unsigned)sizeof(T));
 }
 
-// Four adjacent elements (one row of a tile in row form) as fp32.
-template <class E> struct Vec4;
-template <> struct Vec4<bf16> { typedef __bf16 t __attribute__((ext_vector_type(4))); };
-template <> struct Vec4<f16> { typedef _Float16 t __attribute__((ext_vector_type(4))); };
-template <> struct Vec4<float> { typedef float t __attribute__((ext_vector_type(4))); };
-template <class E>
-__device__ __forceinline__ f32x4 ld4(const E* p) {
-    return __builtin_convertvector(*(const typename Vec4<E>::t*)p, f32x4);
-}
-template <class E>
-__device__ __forceinline__ void st4(E* p, f32x4 x) {
-    *(typename Vec4<E>::t*)p = __builtin_convertvector(x, typename Vec4<E>::t);
-}
-
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
 // issues the 16-byte loads (rows at or past C read row C-1, a valid row),
 // store() writes the block to LDS (row pitch LD) with rows past C zeroed.

@@ -274,34 +274,33 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
         const int n0 = (64 / NCB) * (w >> 1);
         f32x4 akk[2][TN], aqk[2][TN];
         zero_acc(akk);
-        wgemm<S, 2, TN, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
+        wgemm_rf<S, 2, TN, KD, false, false>(akk, sK, LK, sK, LK, m0, n0);
         if (WITH_R) {
             zero_acc(aqk);
-            wgemm<S, 2, TN, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+            wgemm_rf<S, 2, TN, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
         }
-        // branch-free: Γ_rc = exp(min(G_r − G_c, 0)), then masked by a select
-        float gr[2][4], br[2][4], gc[TN];
+        // row form: four adjacent columns of one row per lane (16-byte L and
+        // 8-byte Pm stores); branch-free: Γ_rc = exp(min(G_r − G_c, 0)), then
+        // masked by a select
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int r = rf_row(m0, i);
+            const float gr = sG[r], br = sB[r];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                gr[i][e] = sG[acc_row(m0, i, e)];
-                br[i][e] = sB[acc_row(m0, i, e)];
-            }
-#pragma unroll
-        for (int j = 0; j < TN; j++) gc[j] = sG[acc_col(n0, j)];
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < TN; j++)
+            for (int j = 0; j < TN; j++) {
+                const int c0 = rf_col(n0, j);
+                const f32x4 gc = *(const f32x4*)(sG + c0);
+                f32x4 lv, pv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int r = acc_row(m0, i, e), c = acc_col(n0, j);
-                    const float gm = __expf(fminf(gr[i][e] - gc[j], 0.f));
-                    const float lv = br[i][e] * gm * akk[i][j][e];
-                    sL[r * LL + c] = c < r ? lv : 0.f;
-                    if (WITH_R) sPm[r * LA + c] = to_e<S>(c <= r ? scale * gm * aqk[i][j][e] : 0.f);
+                    const float gm = __expf(fminf(gr - gc[e], 0.f));
+                    lv[e] = c0 + e < r ? br * gm * akk[i][j][e] : 0.f;
+                    pv[e] = c0 + e <= r ? scale * gm * aqk[i][j][e] : 0.f;
                 }
+                *(f32x4*)(sL + r * LL + c0) = lv;
+                if (WITH_R) st4<S>(sPm + r * LA + c0, pv);
+            }
+        }
     }
     lds_barrier();
 
@@ -335,41 +334,37 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
     f32x4 aw[2][TNK], au[2][TNV];
     zero_acc(aw);
     zero_acc(au);
-    wgemm<S, 2, TNK, 64, false, true>(aw, sAw, LA, sK, LK, m0, n0k);
-    wgemm<S, 2, TNV, 64, false, true>(au, sAu, LA, sV, LV, m0, n0v);
+    wgemm_rf<S, 2, TNK, 64, false, true>(aw, sAw, LA, sK, LK, m0, n0k);
+    wgemm_rf<S, 2, TNV, 64, false, true>(au, sAu, LA, sV, LV, m0, n0v);
     lds_barrier();   // V is overwritten by U below
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        const int r = rf_row(m0, i);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int r = acc_row(m0, i, e);
+        for (int j = 0; j < TNK; j++) st4<S>(sW + r * LK + rf_col(n0k, j), aw[i][j]);
 #pragma unroll
-            for (int j = 0; j < TNK; j++) sW[r * LK + acc_col(n0k, j)] = to_e<S>(aw[i][j][e]);
-#pragma unroll
-            for (int j = 0; j < TNV; j++) sV[r * LV + acc_col(n0v, j)] = to_e<S>(au[i][j][e]);
-        }
+        for (int j = 0; j < TNV; j++) st4<S>(sV + r * LV + rf_col(n0v, j), au[i][j]);
+    }
     lds_barrier();
 
     if (WITH_R) {
         // ---- R = scale diag(γ) Q − Pm W
         f32x4 ar[2][TNK];
         zero_acc(ar);
-        wgemm<S, 2, TNK, 64, false, true>(ar, sPm, LA, sW, LK, m0, n0k);
+        wgemm_rf<S, 2, TNK, 64, false, true>(ar, sPm, LA, sW, LK, m0, n0k);
         store_tile_dense<S, KD, LK, NTHR>(Wg + unit * C * KD, sW);
         store_tile_dense<S, VD, LV, NTHR>(Ug + unit * C * VD, sV);
         S* sR = sK;   // K is no longer read
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int r = rf_row(m0, i);
+            const float sgr = scale * __expf(sG[r]);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = acc_row(m0, i, e);
-                const float gr = __expf(sG[r]);
-#pragma unroll
-                for (int j = 0; j < TNK; j++) {
-                    const int c = acc_col(n0k, j);
-                    sR[r * LK + c] = to_e<S>(scale * gr * (float)sQ[r * LK + c] - ar[i][j][e]);
-                }
+            for (int j = 0; j < TNK; j++) {
+                const int c0 = rf_col(n0k, j);
+                st4<S>(sR + r * LK + c0, sgr * ld4<S>(sQ + r * LK + c0) - ar[i][j]);
             }
+        }
         lds_barrier();
         store_tile_dense<S, KD, LK, NTHR>(Rg + unit * C * KD, sR);
     } else {
