@@ -78,15 +78,15 @@ def flop_model_fwd(C, K, V):
 #   WY prep: K Kᵀ, Q Kᵀ, W = A·diag(βγ)K, Pm·W (2C²K each), U = A·diag(β)V
 #            (2C²V), the blocked triangular inverse (C³/3)
 #   gradient: K h, K dh, dO hᵀ, dV_new hᵀ, V_new dhᵀ (2CKV each); Q Kᵀ, T1 K,
-#             T1ᵀ Q, Aᵀ dW, dW Kᵀ, K Kᵀ (2C²K each), Eb K + Ebᵀ K (4C²K);
-#             Pmᵀ dO, A Z, dO V_newᵀ, dV_new Vᵀ, Aᵀ dV_new (2C²V each);
+#             T1ᵀ Q, Aᵀ dW, K Kᵀ (2C²K each), Eb K + Ebᵀ K (4C²K);
+#             Pmᵀ dO, A Z, dO V_newᵀ, dV_new Zᵀ, Aᵀ dV_new (2C²V each);
 #             Aᵀ dA_pre, M1 Aᵀ (2C³ each)
 def mfma_work_prep(K, V, C=64):
     return 8 * C * C * K + 2 * C * C * V + C ** 3 / 3.0
 
 
 def mfma_work_grad(K, V, C=64):
-    return 10 * C * K * V + 16 * C * C * K + 10 * C * C * V + 4 * C ** 3
+    return 10 * C * K * V + 14 * C * C * K + 10 * C * C * V + 4 * C ** 3
 
 
 def kernel_bytes_kda(H, K, V, chunks, es=2):
