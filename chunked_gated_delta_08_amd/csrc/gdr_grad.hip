@@ -485,6 +485,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     // registers while the current one is computed
     StateReg<E, KD, LK, VS> nH, ndH;
     RowsReg<E, VS, LS> ndO, nV;
+    RowsReg<E, KD, LK> nQ;
 #pragma unroll
     for (int vs = 0; vs < NVS; vs++) {
         if (vs == 0) {
@@ -545,6 +546,8 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (vs + 1 == NVS)   // Q (needed again after the loop; its LDS region holds the
+            nQ.load(q + qrow * KD, (long)HK * KD, Cn);   // slice buffers), in flight for the rest of the slice
         // ---- dV_new = Pmᵀ dO + diag(γ_C/γ) K dh
         {
             f32x4 pdo[2][1];
@@ -639,8 +642,6 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     }
     // ---- Q back into its region (it held the slice buffers)
     {
-        RowsReg<E, KD, LK> nQ;
-        nQ.load(q + qrow * KD, (long)HK * KD, Cn);
         nQ.store(sQ);
     }
     // ---- F = dPm ⊙ Pm -> dG; T1 = dPm ⊙ Γ · scale (over Pm, each wave its own block); dW -> LDS
