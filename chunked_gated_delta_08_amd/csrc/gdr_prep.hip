@@ -133,38 +133,45 @@ __device__ __forceinline__ void store_tile_dense(E* __restrict__ g, const E* s) 
 template <class E> constexpr int pad_of() { return sizeof(E) == 2 ? 8 : 4; }
 
 // ---------------------------------------------------------------- K1a
-// LDS carve-up of the WY-factor kernel (byte offsets).
+// LDS carve-up of the WY-factor kernel (byte offsets).  Regions are reused
+// along the unit's phases: L becomes A in place (the inverse), then holds V
+// (staged from registers once A is consumed) and U; the inverse's scratch and
+// later W live over the two scaled copies of A.  16-bit at K = V = 128:
+// 80,384 bytes, so two workgroups share a CU.
 template <class E, class S, int KD, int VD>
 struct PrepCfg {
     static constexpr int C = 64;
     static constexpr int LK = KD + pad_of<S>(), LV = VD + pad_of<S>(), LA = 64 + pad_of<S>(), LL = 68;
-    static constexpr size_t oK = 0;                                          // K     [64][LK] S (later R)
-    static constexpr size_t oV = oK + (size_t)C * LK * sizeof(S);            // V     [64][LV] S (later U)
-    static constexpr size_t oQ = oV + (size_t)C * LV * sizeof(S);            // Q     [64][LK] S
-    static constexpr size_t oL = oQ + (size_t)C * LK * sizeof(S);            // L     [64][LL] fp32 (later W [64][LK] S)
-    static constexpr size_t oAf = oL + (size_t)C * LL * 4;                   // A     [64][LL] fp32
-    static constexpr size_t oAw = oAf + (size_t)C * LL * 4;                  // A diag(βγ) [64][LA] S
-    static constexpr size_t oAu = oAw + (size_t)C * LA * sizeof(S);          // A diag(β)  [64][LA] S
-    static constexpr size_t oPm = oAu + (size_t)C * LA * sizeof(S);          // Pm    [64][LA] S
-    static constexpr size_t oT = oPm + (size_t)C * LA * sizeof(S);           // 4 waves x 2 blocks [16][17] fp32
-    static constexpr size_t oG = oT + (size_t)4 * 2 * 16 * 17 * 4;           // G, β [64] fp32
+    static constexpr size_t szK = (size_t)C * LK * sizeof(S), szV = (size_t)C * LV * sizeof(S);
+    static constexpr size_t szL = (size_t)C * LL * 4, szA = (size_t)C * LA * sizeof(S);
+    static constexpr size_t oK = 0;                                    // K [64][LK] S (later R)
+    static constexpr size_t oQ = oK + szK;                             // Q [64][LK] S
+    static constexpr size_t oL = oQ + szK;                             // L -> A [64][LL] fp32, then V -> U [64][LV] S
+    static constexpr size_t oPm = oL + (szL > szV ? szL : szV);        // Pm [64][LA] S
+    static constexpr size_t oAw = oPm + szA;                           // A diag(βγ) [64][LA] S (inverse scratch before, W after)
+    static constexpr size_t oAu = oAw + szA;                           // A diag(β) [64][LA] S
+    static constexpr size_t oG = oAu + szA;                            // G, β [64] fp32
     static constexpr size_t smem = oG + (size_t)2 * C * 4;
-    static_assert((size_t)C * LK * sizeof(S) <= (size_t)C * LL * 4, "W aliases L");
+    static_assert((size_t)4 * 2 * 16 * 17 * 4 <= 2 * szA, "inverse scratch over the scaled copies of A");
+    static_assert(szK <= 2 * szA, "W over the scaled copies of A");
     static_assert(smem <= 160 * 1024, "LDS budget");
 };
 
-// Waves per workgroup: 8 for 16-bit inputs (two per SIMD, so one wave's
-// element-wise and LDS work overlaps the other's), 4 for fp32 (whose fp32 MFMA
-// operands need the larger register share of one wave per SIMD).
-template <class E> constexpr int prep_waves() { return sizeof(E) == 2 ? 8 : 4; }
+// Four waves per workgroup (the in-place inverse works on four 16-row block
+// rows); 16-bit problems fit two workgroups per CU, so one workgroup's
+// barrier-bound phases (the inverse) overlap the other's loads, products and
+// stores.
+template <class E> constexpr int prep_waves() { return 4; }
 
 // Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...
-// Every 64-row product is tiled over the waves as two row halves x (waves / 2)
-// column blocks.  The next unit's K, V, Q, gate and β are loaded into registers
-// right after the current ones are staged in LDS, so those loads are in flight
-// while the current unit is computed.  E: input type; S: scan operand type.
+// Every 64-row product is tiled over the waves as two row halves x two
+// column blocks.  The next unit's K, Q, gate and β are loaded into registers
+// right after the current ones are staged in LDS, and its V right after the
+// current V is staged (after the inverse), so those loads are in flight while
+// the current unit is computed.  E: input type; S: scan operand type.
 template <class E, class S, int KD, int VD, bool WITH_R>
-__global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ void __launch_bounds__(64 * prep_waves<E>())
+__attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const float* __restrict__ gcum,
                                                    const E* __restrict__ beta, const ChunkInfo* __restrict__ info,
                                                    int HK, int HV, float scale, S* __restrict__ Wg,
@@ -177,15 +184,14 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
     constexpr int EPV = 16 / (int)sizeof(E);
     extern __shared__ __align__(16) unsigned char smem[];
     S* sK = (S*)(smem + Cf::oK);
-    S* sV = (S*)(smem + Cf::oV);
     S* sQ = (S*)(smem + Cf::oQ);
-    float* sL = (float*)(smem + Cf::oL);
-    S* sW = (S*)(smem + Cf::oL);
-    float* sAf = (float*)(smem + Cf::oAf);
+    float* sL = (float*)(smem + Cf::oL);   // L, then A in place
+    S* sV = (S*)(smem + Cf::oL);           // V, then U (after A is consumed)
     S* sAw = (S*)(smem + Cf::oAw);
     S* sAu = (S*)(smem + Cf::oAu);
+    S* sW = (S*)(smem + Cf::oAw);          // W (after the W and U products)
+    float* sT = (float*)(smem + Cf::oAw);  // the inverse's scratch
     S* sPm = (S*)(smem + Cf::oPm);
-    float* sT = (float*)(smem + Cf::oT);
     float* sG = (float*)(smem + Cf::oG);
     float* sB = sG + C;
 
@@ -197,8 +203,8 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
     float rg = 0.f;
     E rb = E(0.f);   // raw β: converted and masked when staged (a conversion here would wait for the loads)
     // issue the loads of unit u (rows past the chunk read its last row; they
-    // are zeroed when staged)
-    auto issue = [&](int u, int Cu, int tu) {
+    // are zeroed when staged): gate, β, K, Q, then V separately
+    auto issue_kq = [&](int u, int Cu, int tu) {
         const int hvu = u % HV, hku = hvu / (HV / HK);
         if (threadIdx.x < C) {   // first, so that waiting for them leaves the vectors in flight
             const int r = min((int)threadIdx.x, Cu - 1);
@@ -211,6 +217,9 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
             rk[i] = *(const typename Vec16<E>::t*)(k + ((tu + r) * HK + hku) * KD + cc * EPV);
             if constexpr (WITH_R) rq[i] = *(const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV);
         }
+    };
+    auto issue_v = [&](int u, int Cu, int tu) {
+        const int hvu = u % HV;
 #pragma unroll
         for (int i = 0; i < NVV; i++) {
             const int idx = threadIdx.x + NTHR * i, r = min(idx / (VD / EPV), Cu - 1), cc = idx % (VD / EPV);
@@ -227,7 +236,8 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
     int u = blockIdx.x;
     if (u >= nunits) return;
     int cur_len = info[u / HV].len, cur_t0 = info[u / HV].t0;
-    issue(u, cur_len, cur_t0);
+    issue_kq(u, cur_len, cur_t0);
+    issue_v(u, cur_len, cur_t0);
     for (; u < nunits; u += gridDim.x) {
     const int ci = u / HV, hv = u % HV;
     const int Cn = cur_len;
@@ -248,11 +258,6 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
         *(typename Vec16<S>::t*)(sK + r * LK + c * EPV) = to_s(rk[i], 1.f, r < Cn);
         if constexpr (WITH_R) *(typename Vec16<S>::t*)(sQ + r * LK + c * EPV) = to_s(rq[i], 1.f, r < Cn);
     }
-#pragma unroll
-    for (int i = 0; i < NVV; i++) {
-        const int idx = threadIdx.x + NTHR * i, r = idx / (VD / EPV), c = idx % (VD / EPV);
-        *(typename Vec16<S>::t*)(sV + r * LV + c * EPV) = to_s(rv[i], 1.f, r < Cn);
-    }
     lds_barrier();
 
     // ---- K̃ = diag(γ_C/γ) K straight from the registers
@@ -265,8 +270,8 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
             *(typename Vec16<S>::t*)(KTo + r * KD + c * EPV) = to_s(rk[i], __expf(gl - sG[r]), r < Cn);
         }
     }
-    // ---- the next unit's loads fly during this unit's compute
-    if (un < nunits) issue(un, nxt_len, nxt_t0);
+    // ---- the next unit's K, Q, gate and β fly during this unit's compute
+    if (un < nunits) issue_kq(un, nxt_len, nxt_t0);
 
     // ---- S_kk = K Kᵀ -> L ;  S_qk = Q Kᵀ -> Pm     (wave w: 32 rows x 64/NCB columns)
     {
@@ -304,10 +309,12 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
     }
     lds_barrier();
 
-    // ---- A = (I+L)^{-1}
-    tri_inverse64<LL, NTHR>(sL, sAf, sT);
+    // ---- A = (I+L)^{-1}, in place
+    float* sAf = sL;
+    tri_inverse64_inplace<LL>(sL, sT);
 
-    // ---- A diag(βγ), A diag(β) as MFMA operands; A itself to memory (input type)
+    // ---- A diag(βγ), A diag(β) as MFMA operands (over the inverse's scratch);
+    //      A itself to memory (input type)
     {
         E* Ao = Ag ? Ag + unit * C * C : nullptr;
         for (int idx = threadIdx.x; idx < C * C / EPV; idx += NTHR) {
@@ -326,24 +333,39 @@ __global__ void __launch_bounds__(64 * prep_waves<E>()) prep_kernel(const E* __r
             if (Ao) *(typename Vec16<E>::t*)(Ao + r * C + c0) = ao;
         }
     }
+    lds_barrier();   // A is read: V takes its region
+#pragma unroll
+    for (int i = 0; i < NVV; i++) {
+        const int idx = threadIdx.x + NTHR * i, r = idx / (VD / EPV), c = idx % (VD / EPV);
+        *(typename Vec16<S>::t*)(sV + r * LV + c * EPV) = to_s(rv[i], 1.f, r < Cn);
+    }
+    if (un < nunits) issue_v(un, nxt_len, nxt_t0);   // the next unit's V flies from here
     lds_barrier();
 
     // ---- W = A diag(βγ) K, U = A diag(β) V     (wave w: 32 rows, KD/NCB resp. VD/NCB columns)
     constexpr int TNK = KD / 16 / NCB, TNV = VD / 16 / NCB;
     const int n0k = (KD / NCB) * (w >> 1), n0v = (VD / NCB) * (w >> 1);
-    f32x4 aw[2][TNK], au[2][TNV];
-    zero_acc(aw);
-    zero_acc(au);
-    wgemm_rf<S, 2, TNK, 64, false, true>(aw, sAw, LA, sK, LK, m0, n0k);
-    wgemm_rf<S, 2, TNV, 64, false, true>(au, sAu, LA, sV, LV, m0, n0v);
-    lds_barrier();   // V is overwritten by U below
+    // (one product's accumulators live at a time: U first, stored over V,
+    // then W, stored over the copies of A)
+    {
+        f32x4 au[2][TNV];
+        zero_acc(au);
+        wgemm_rf<S, 2, TNV, 64, false, true>(au, sAu, LA, sV, LV, m0, n0v);
+        lds_barrier();   // V is read: U takes its place
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int r = rf_row(m0, i);
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < TNK; j++) st4<S>(sW + r * LK + rf_col(n0k, j), aw[i][j]);
+            for (int j = 0; j < TNV; j++) st4<S>(sV + rf_row(m0, i) * LV + rf_col(n0v, j), au[i][j]);
+    }
+    {
+        f32x4 aw[2][TNK];
+        zero_acc(aw);
+        wgemm_rf<S, 2, TNK, 64, false, true>(aw, sAw, LA, sK, LK, m0, n0k);
+        lds_barrier();   // the copies of A are read: W takes their place
 #pragma unroll
-        for (int j = 0; j < TNV; j++) st4<S>(sV + r * LV + rf_col(n0v, j), au[i][j]);
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < TNK; j++) st4<S>(sW + rf_row(m0, i) * LK + rf_col(n0k, j), aw[i][j]);
     }
     lds_barrier();
 
@@ -389,8 +411,10 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
     const size_t sm = prep_smem<E, S, KD, VD>();
     const long nunits = p.NT * p.HV;
     if (nunits > INT32_MAX) return hipErrorInvalidValue;
-    // one persistent workgroup per CU (the LDS carve-up allows one), 256 CUs
-    dim3 grid((unsigned)(nunits < 256 ? nunits : 256));
+    // persistent workgroups: as many per CU as the LDS carve-up allows (two
+    // for 16-bit problems, at most two: two waves per SIMD), 256 CUs
+    const long per_cu = sm * 2 <= 160 * 1024 ? 2 : 1, nwg = 256 * per_cu;
+    dim3 grid((unsigned)(nunits < nwg ? nunits : nwg));
     if (q) {
         auto kern = prep_kernel<E, S, KD, VD, true>;
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)

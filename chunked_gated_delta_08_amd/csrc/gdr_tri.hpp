@@ -114,4 +114,78 @@ __device__ __forceinline__ void tri_inverse64(const float* sL, float* sAf, float
     lds_barrier();
 }
 
+// In-place variant for a workgroup of exactly four waves: sLA holds L on
+// entry (strictly lower, zero on and above the diagonal, fp32, pitch LL) and
+// A = (I + L)^{-1} on exit, with the same block recursion.  Each block of A
+// is written over the block of L it replaces once no wave reads that L block
+// any more: D_w over L_ww (step 1, wave w alone); A_10, A_32 over L_10, L_32
+// (step 2, the only step reading them); Y00 = L_20 D_0 + L_21 A_10 and
+// Y10 = L_30 D_0 + L_31 A_10 go to scratch (step 3a); after a barrier
+// A_20 = −D_2 Y00, A_21 = −D_2 Y01, A_30 = −(A_32 Y00 + D_3 Y10) and
+// A_31 = −(A_32 Y01 + D_3 Y11), one block per wave (step 3b).  sT holds two
+// [16][17] scratch blocks per wave.
+template <int LL>
+__device__ __forceinline__ void tri_inverse64_inplace(float* sLA, float* sT) {
+    const int w = wave_id(), l = lane_id();
+    constexpr int LT = 17;
+    float* t0 = sT + w * 2 * 16 * LT;
+    float* t1 = t0 + 16 * LT;
+    auto Bk = [&](int i, int j) { return sLA + 16 * i * LL + 16 * j; };
+    // step 1: lane l < 16 of wave w forms column l of D_w by forward
+    // substitution, then writes the whole column (zeros above the diagonal)
+    if (l < 16) {
+        const float* L = sLA + 16 * w * LL + 16 * w;
+        float a[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float acc = r == l ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; s++) acc -= L[r * LL + s] * a[s];
+            a[r] = acc;
+        }
+        float* D = sLA + 16 * w * LL + 16 * w;
+#pragma unroll
+        for (int r = 0; r < 16; r++) D[r * LL + l] = a[r];
+    }
+    lds_barrier();
+    // step 2
+    {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (w < 2) {
+            const int i = 2 * w + 1, j = 2 * w;            // (1,0) or (3,2)
+            mm16(acc, Bk(i, j), LL, Bk(j, j), LL);
+            put16(t0, LT, acc, 1.f);
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            mm16(acc, Bk(i, i), LL, t0, LT);
+            put16(Bk(i, j), LL, acc, -1.f);
+        } else {
+            mm16(acc, Bk(w, 1), LL, Bk(1, 1), LL);         // Y01 = L_21 D_1 or Y11 = L_31 D_1
+            put16(t0, LT, acc, 1.f);
+        }
+    }
+    lds_barrier();
+    // step 3a: Y00 (wave 0) and Y10 (wave 1)
+    if (w < 2) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mm16(acc, Bk(2 + w, 0), LL, Bk(0, 0), LL);
+        mm16(acc, Bk(2 + w, 1), LL, Bk(1, 0), LL);
+        put16(t1, LT, acc, 1.f);
+    }
+    lds_barrier();
+    // step 3b: wave w -> block (i, j) = (2 + (w >> 1), w & 1):
+    // A_2j = −D_2 Y0j, A_3j = −(A_32 Y0j + D_3 Y1j), with Y00 / Y10 in the
+    // second blocks of waves 0 / 1 and Y01 / Y11 in the first blocks of
+    // waves 2 / 3 (offsets into the scratch, so no pointer is selected)
+    {
+        const int i = 2 + (w >> 1), j = w & 1;
+        const int o0 = j == 0 ? 16 * LT : 4 * 16 * LT;       // Y0j
+        const int o1 = j == 0 ? 3 * 16 * LT : 6 * 16 * LT;   // Y1j
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mm16(acc, Bk(i, 2), LL, sT + o0, LT);
+        if (i == 3) mm16(acc, Bk(3, 3), LL, sT + o1, LT);
+        put16(Bk(i, j), LL, acc, -1.f);
+    }
+    lds_barrier();
+}
+
 }  // namespace gdr
