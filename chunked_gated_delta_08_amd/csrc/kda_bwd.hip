@@ -228,8 +228,8 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
     f32x4 dqa[2][TN], dwa[2][TN];
     zero_acc(dqa);
     zero_acc(dwa);
-    wgemm<E, 2, TN, VD, false, false>(dqa, sX, LV, sH, LV, m0, n0k);
-    wgemm<E, 2, TN, VD, false, false>(dwa, sDV, LV, sH, LV, m0, n0k);
+    wgemm_rf<E, 2, TN, VD, false, false>(dqa, sX, LV, sH, LV, m0, n0k);
+    wgemm_rf<E, 2, TN, VD, false, false>(dwa, sDV, LV, sH, LV, m0, n0k);
     lds_barrier();
     // ---- swap in dh and V_new; dw -> LDS; rowsum_V(h ⊙ dh) in fp32 from the registers
     {
@@ -250,164 +250,163 @@ __global__ void __launch_bounds__(512) kda_kernel(KdaArgs a, const int32_t* __re
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) sDW[acc_row(m0, i, e) * LK + acc_col(n0k, j)] = (E)(-dwa[i][j][e]);
+        for (int j = 0; j < TN; j++) st4<E>(sDW + rf_row(m0, i) * LK + rf_col(n0k, j), -dwa[i][j]);
     lds_barrier();
     // ---- this lane's elements of g, k, q (key tiles) and v (value tiles), issued
     //      before the products that precede their use (rows past the chunk read
-    //      its last row and are not used)
+    //      its last row and are not used).  Row form: a lane's elements of a tile
+    //      are four adjacent columns of one row (one 16-byte or 8-byte load).
     constexpr int TNV = VD / 64;
     const int n0v = (VD / 4) * (w >> 1);
-    float pg[2][TN][4], pk[2][TN][4], pq[2][TN][4], pv[2][TNV][4], pgl[TN];
+    f32x4 pg[2][TN], pk[2][TN], pq[2][TN], pv[2][TNV], pgl[TN];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        const int rc = min(rf_row(m0, i), Cn - 1);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int rc = min(acc_row(m0, i, e), Cn - 1);
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const long o = gidx(rc, acc_col(n0k, j));
-                pg[i][j][e] = a.g[o];
-                pk[i][j][e] = (float)k[o];
-                pq[i][j][e] = (float)q[o];
-            }
-#pragma unroll
-            for (int j = 0; j < TNV; j++) pv[i][j][e] = (float)v[((t0 + rc) * H + hh) * VD + acc_col(n0v, j)];
+        for (int j = 0; j < TN; j++) {
+            const long o = gidx(rc, rf_col(n0k, j));
+            pg[i][j] = *(const f32x4*)(a.g + o);
+            pk[i][j] = ld4<E>(k + o);
+            pq[i][j] = ld4<E>(q + o);
         }
 #pragma unroll
-    for (int j = 0; j < TN; j++) pgl[j] = a.g[gidx(Cn - 1, acc_col(n0k, j))];
+        for (int j = 0; j < TNV; j++) pv[i][j] = ld4<E>(v + ((t0 + rc) * H + hh) * VD + rf_col(n0v, j));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; j++) pgl[j] = *(const f32x4*)(a.g + gidx(Cn - 1, rf_col(n0k, j)));
     // ---- dks_acc = V_new dhᵀ ; AdW = Aᵀ dw ; AdV = Aᵀ dv (V-tiles)
     f32x4 dka[2][TN], adw[2][TN];
     zero_acc(dka);
     zero_acc(adw);
-    wgemm<E, 2, TN, VD, false, false>(dka, sX, LV, sH, LV, m0, n0k);
-    wgemm<E, 2, TN, 64, true, true>(adw, sA, LA, sDW, LK, m0, n0k);
+    wgemm_rf<E, 2, TN, VD, false, false>(dka, sX, LV, sH, LV, m0, n0k);
+    wgemm_rf<E, 2, TN, 64, true, true>(adw, sA, LA, sDW, LK, m0, n0k);
     // dv_out = β Aᵀ dv, db part 1 = rowsum(Aᵀdv ⊙ V)
-    float dbr[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) dbr[i][e] = 0.f;
+    float dbr[2] = {0.f, 0.f};
     {
         f32x4 adv[2][TNV];
         zero_acc(adv);
-        wgemm<E, 2, TNV, 64, true, true>(adv, sA, LA, sDV, LV, m0, n0v);
+        wgemm_rf<E, 2, TNV, 64, true, true>(adv, sA, LA, sDV, LV, m0, n0v);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rf_row(m0, i);
+            if (rr < Cn) {
 #pragma unroll
-            for (int j = 0; j < TNV; j++)
+                for (int j = 0; j < TNV; j++) {
+                    st4<E>((E*)a.dv_out + ((t0 + rr) * H + hh) * VD + rf_col(n0v, j), sB[rr] * adv[i][j]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int rr = acc_row(m0, i, e), cc = acc_col(n0v, j);
-                    if (rr < Cn) {
-                        const long o = ((t0 + rr) * H + hh) * VD + cc;
-                        ((E*)a.dv_out)[o] = (E)(sB[rr] * adv[i][j][e]);
-                        dbr[i][e] += adv[i][j][e] * pv[i][j][e];
-                    }
+                    for (int e = 0; e < 4; e++) dbr[i] += adv[i][j][e] * pv[i][j][e];
                 }
+            }
+        }
     }
     // ---- per-element outputs dq, dk and dg (last-row terms after the column sums)
-    float csum[TN];
+    float csum[TN][4];
 #pragma unroll
-    for (int j = 0; j < TN; j++) csum[j] = 0.f;
-    float dgl[2][TN][4];
+    for (int j = 0; j < TN; j++)
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+        for (int e = 0; e < 4; e++) csum[j][e] = 0.f;
+    f32x4 dgl[2][TN];
 #pragma unroll
-        for (int j = 0; j < TN; j++)
+    for (int i = 0; i < 2; i++) {
+        const int rr = rf_row(m0, i);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                dgl[i][j][e] = 0.f;
-                if (rr < Cn) {
-                    const long o = gidx(rr, cc);
+        for (int j = 0; j < TN; j++) {
+            dgl[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (rr < Cn) {
+                const long o = gidx(rr, rf_col(n0k, j));
+                f32x4 dqv, dkv;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
                     const float gg = pg[i][j][e], gm = __expf(gg);
-                    const float glast = pgl[j];
                     const float kk = pk[i][j][e], qq = pq[i][j][e];
-                    const float dqv = scale * dqa[i][j][e] * gm;
-                    const float dks = dka[i][j][e] * __expf(glast - gg);
+                    dqv[e] = scale * dqa[i][j][e] * gm;
+                    const float dks = dka[i][j][e] * __expf(pgl[j][e] - gg);
                     const float bgw = sB[rr] * gm * adw[i][j][e];
-                    a.dq[o] = dqv;
-                    a.dk[o] = dks + bgw;
-                    dgl[i][j][e] = qq * dqv - kk * dks + kk * bgw;
-                    csum[j] += kk * dks;
-                    dbr[i][e] += adw[i][j][e] * gm * kk;
+                    dkv[e] = dks + bgw;
+                    dgl[i][j][e] = qq * dqv[e] - kk * dks + kk * bgw;
+                    csum[j][e] += kk * dks;
+                    dbr[i] += adw[i][j][e] * gm * kk;
                 }
+                *(f32x4*)(a.dq + o) = dqv;
+                *(f32x4*)(a.dk + o) = dkv;
             }
-    // column sums over this wave's 32 rows -> sCS[row half][key]
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-        float x = csum[j];
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
-        sCS[(w & 1) * KD + acc_col(n0k, j)] = x;   // every row group holds the sum (no branch)
+        }
     }
+    // column sums over this wave's 32 rows (the 16 lanes of a row group hold 16
+    // rows of the same four columns) -> sCS[row half][key]
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float x = csum[j][e];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+            sCS[(w & 1) * KD + rf_col(n0k, j) + e] = x;   // every lane of the group holds the sum (no branch)
+        }
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        const int rr = rf_row(m0, i);
+        if (rr < Cn) {
 #pragma unroll
-        for (int j = 0; j < TN; j++)
+            for (int j = 0; j < TN; j++) {
+                const int c0 = rf_col(n0k, j);
+                f32x4 x = dgl[i][j];
+                if (rr == Cn - 1)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0k, j);
-                if (rr < Cn) {
-                    float x = dgl[i][j][e];
-                    if (rr == Cn - 1) x += sCS[cc] + sCS[KD + cc] + __expf(pg[i][j][e]) * sHD[cc];
-                    a.dg[gidx(rr, cc)] = x;
-                }
+                    for (int e = 0; e < 4; e++)
+                        x[e] += sCS[c0 + e] + sCS[KD + c0 + e] + __expf(pg[i][j][e]) * sHD[c0 + e];
+                *(f32x4*)(a.dg + gidx(rr, c0)) = x;
             }
+        }
+    }
     // ---- dA_pre = dv (βV)ᵀ + dw (βγK)ᵀ -> LDS (B operands stored [s][.] = [n][k])
     {
         f32x4 dap[2][1];
         zero_acc(dap);
-        wgemm<E, 2, 1, VD, false, false>(dap, sDV, LV, sVb, LV, m0, n0s);
-        wgemm<E, 2, 1, KD, false, false>(dap, sDW, LK, sKb, LK, m0, n0s);
+        wgemm_rf<E, 2, 1, VD, false, false>(dap, sDV, LV, sVb, LV, m0, n0s);
+        wgemm_rf<E, 2, 1, KD, false, false>(dap, sDW, LK, sKb, LK, m0, n0s);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) sP[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = (E)dap[i][0][e];
+        for (int i = 0; i < 2; i++) st4<E>(sP + rf_row(m0, i) * LA + rf_col(n0s, 0), dap[i][0]);
     }
-    // db: reduce over the 16 lanes of each row group, then over the 4 column blocks
+    // db: reduce over the 4 row groups (lanes 16 apart hold the same row), then
+    // over the 4 column blocks
     float* sDB = sCS;   // reuse [4][64] (column sums already consumed above)
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            float x = dbr[i][e];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
-            sDB[(w >> 1) * 64 + acc_row(m0, i, e)] = x;   // every lane of the group holds the sum
-        }
+    for (int i = 0; i < 2; i++) {
+        float x = dbr[i];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        sDB[(w >> 1) * 64 + rf_row(m0, i)] = x;   // the four row groups hold the sum and write it
+    }
     // ---- M1 = Aᵀ dA_pre
     f32x4 m1[2][1];
     zero_acc(m1);
-    wgemm<E, 2, 1, 64, true, true>(m1, sA, LA, sP, LA, m0, n0s);
+    wgemm_rf<E, 2, 1, 64, true, true>(m1, sA, LA, sP, LA, m0, n0s);
     lds_barrier();
     if (threadIdx.x < Cn) {
         const int rr = threadIdx.x;
         a.db[(t0 + rr) * H + hh] = sDB[rr] + sDB[64 + rr] + sDB[128 + rr] + sDB[192 + rr];
     }
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) sP[acc_row(m0, i, e) * LA + acc_col(n0s, 0)] = (E)m1[i][0][e];
+    for (int i = 0; i < 2; i++) st4<E>(sP + rf_row(m0, i) * LA + rf_col(n0s, 0), m1[i][0]);
     lds_barrier();
     // ---- dA = −strictlower(M1 Aᵀ)   (B = Aᵀ: A stored [s][j] = [n][k])
     {
         f32x4 da[2][1];
         zero_acc(da);
-        wgemm<E, 2, 1, 64, false, false>(da, sP, LA, sA, LA, m0, n0s);
+        wgemm_rf<E, 2, 1, 64, false, false>(da, sP, LA, sA, LA, m0, n0s);
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int i = 0; i < 2; i++) {
+            const int rr = rf_row(m0, i), c0 = rf_col(n0s, 0);
+            if (rr < Cn) {
+                f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = acc_row(m0, i, e), cc = acc_col(n0s, 0);
-                if (rr < Cn) a.dA[((t0 + rr) * H + hh) * 64 + cc] = (cc < rr) ? -da[i][0][e] : 0.f;
+                for (int e = 0; e < 4; e++) x[e] = (c0 + e < rr) ? -da[i][0][e] : 0.f;
+                *(f32x4*)(a.dA + ((t0 + rr) * H + hh) * 64 + c0) = x;
             }
+        }
     }
 }
 
