@@ -345,17 +345,10 @@ __device__ __forceinline__ float sum4g(float x) {
     return x;
 }
 
-// One launch handles value head hv = hk * G + hi of every (chunk, key head).
-// GRP (G > 1): the launches for hi = 0 .. G-1 run in order on one stream and
-// build the group sums of dq and dk in the outputs themselves: the first
-// launch stores its dq, dk; every later one loads the rows stored so far
-// (coalesced, into the LDS staging tiles), adds its own in fp32 and stores
-// the sum.  The order of the sum is fixed, the partial sums are rounded to
-// the output type between launches, no workspace round trip is needed, and
-// every launch has the register footprint of a single head.
+// One (chunk, value head) unit of the gradient: value head hv = hk·G + hi of
+// key head hk = blockIdx.y, chunk blockIdx.x.
 template <class E, int KD, int VD, bool GRP>
-__global__ void __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
+__device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, float scale, int hi) {
     using Cf = GradCfg<E, KD, VD>;
     constexpr int C = 64, VS = Cf::VS, NVS = Cf::NVS, LK = Cf::LK, LA = Cf::LA, LS = Cf::LS, TK = Cf::TK;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -380,7 +373,9 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     float* sEg = sB + 64;   // e^{G_C − G_r}: the factor γ_C/γ
     float* sRed = (float*)(smem + Cf::oRed);   // row partials of dG, dβ [2][64] each, column partials [2][64], misc [8]
 
-    const int ci = blockIdx.x, hk = blockIdx.y, G = GRP ? HV / HK : 1;
+    int ci = blockIdx.x, hk = blockIdx.y;
+    const int G = GRP ? HV / HK : 1;
+    if constexpr (GRP) asm volatile("" : "+s"(ci), "+s"(hk));   // derived per unit, not kept live across units
     const ChunkInfo ch = a.info[ci];
     const int Cn = ch.len;
     const long t0 = ch.t0;
@@ -405,7 +400,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     // gate and β (needed first), Q and K (the first product), then A and the
     // first value slice (in flight during Pm).  Every wave loads row
     // threadIdx.x % 64, unconditionally, so no wait sits at a branch join.
-    const int rg = min((int)threadIdx.x & (C - 1), Cn - 1);
+    const int rg = min(tid_o() & (C - 1), Cn - 1);
     const float gg = a.gcum[(t0 + rg) * HV + hv];
     const E bb = beta[(t0 + rg) * HV + hv];
     __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the waits count on it
@@ -421,6 +416,7 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     rdH.load(dhT, 0);
     rdO.load(dO + vrow * VD, (long)HV * VD, Cn);
     rV.load(v + vrow * VD, (long)HV * VD, Cn);
+    if (GRP && hi > 0) lds_barrier();   // the previous head's last LDS reads (dq, dk rows, reductions)
     if (threadIdx.x < C) {
         const int r = threadIdx.x;
         sG[r] = gg;
@@ -780,16 +776,20 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
         }
         pin_rows(rowG, rowB, colG, zsum);
     }
+    // the previous head's dq, dk stores (every wave's) are ordered before the
+    // loads of them below: release here, the barrier, acquire before the loads
+    if (GRP && hi > 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     lds_barrier();
     // ---- dk += Eb K + Ebᵀ K
     gemm4<E, 2, TK, 64, false, true>(dks, sEb, LA, sK, LK, m0, n0k);
     gemm4<E, 2, TK, 64, true, true>(dks, sEb, LA, sK, LK, m0, n0k);
 
-    // ---- GQA: the group's dq, dk stored by the earlier launches (rows in flight
+    // ---- GQA: the group's dq, dk summed over the earlier heads (rows in flight
     //      during the reductions, staged over Q's and dW's regions with them)
     const bool add_prev = GRP && hi > 0;
     RowsReg<E, KD, LK> pq, pk;
     if (add_prev) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         pq.load((const E*)a.dq + qrow * KD, (long)HK * KD, Cn);
         pk.load((const E*)a.dk + qrow * KD, (long)HK * KD, Cn);
     }
@@ -875,6 +875,26 @@ grad_kernel(GradArgs a, int HK, int HV, float scale, int hi) {
     store_rows<E, KD, LK>((E*)a.dk + qrow * KD, (long)HK * KD, sdk, Cn);
 }
 
+// One workgroup per (chunk, key head).  GRP (G = HV/HK > 1): the workgroup
+// takes the G value heads hv = hk·G + hi of its key head one after the other
+// and builds the group sums of dq and dk in the outputs themselves: the first
+// head stores its dq, dk; every later one loads the rows stored so far (its
+// own workgroup's, one unit earlier, so mostly from cache; coalesced, into the
+// LDS staging tiles), adds its own in fp32 and stores the sum.  The order of
+// the sum is fixed and the partial sums are rounded to the output type in
+// between; no workspace is needed and every unit has the register footprint
+// of a single head.
+template <class E, int KD, int VD, bool GRP>
+__global__ void __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+grad_kernel(GradArgs a, int HK, int HV, float scale) {
+    if constexpr (!GRP) {
+        grad_unit<E, KD, VD, false>(a, HK, HV, scale, 0);
+    } else {
+        const int G = HV / HK;
+        for (int hi = 0; hi < G; hi++) grad_unit<E, KD, VD, true>(a, HK, HV, scale, hi);
+    }
+}
+
 template <class E, int KD, int VD, bool GRP>
 static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
     using Cf = GradCfg<E, KD, VD>;
@@ -882,12 +902,8 @@ static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
     auto kern = grad_kernel<E, KD, VD, GRP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem);
     if (e != hipSuccess) return e;
-    const int G = GRP ? p.HV / p.HK : 1;
-    for (int hi = 0; hi < G; hi++) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale, hi);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale);
+    return hipGetLastError();
 }
 
 template <class E, int KD, int VD>
