@@ -84,85 +84,11 @@ struct GradCfg {
     static_assert(VD % VS == 0 && KD % 32 == 0, "tile shapes");
 };
 
-// The lane index, recomputed where it is used: the compiler cannot share it
-// (or the addresses derived from it) between phases, so lane-dependent LDS
-// offsets are rebuilt per product (two VALU ops) instead of being kept live
-// across the whole kernel in registers the accumulators need.
-// (the masks after the opaque step restore the value range, so index
-// arithmetic stays on 24-bit multiplies)
-__device__ __forceinline__ int lane_o() {
-    int l = threadIdx.x & 63;
-    asm volatile("" : "+v"(l));
-    return l & 63;
-}
+// The thread index behind an opaque step (as lane_o).
 __device__ __forceinline__ int tid_o() {
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));
     return t & (GNT - 1);
-}
-
-// Fragment helpers.  A lane's base pointer into an operand X at rows /
-// columns mn0 (tr: X stored [k][mn], else [mn][k]); fragment n of the k-step
-// at k0 is that base plus a constant offset (16-bit: direct rows mn0 + r,
-// keys 8g..8g+7; transposed reads start at row k0 + 8g + r/4, column
-// mn0 + 4(r%4), and at 4 rows further).
-template <class E, bool TR>
-__device__ __forceinline__ const E* frag_base(const E* X, int ld, int mn0, int l) {
-    const int r = l & 15, g = l >> 4;
-    if constexpr (sizeof(E) == 2)
-        return TR ? X + (8 * g + (r >> 2)) * ld + mn0 + 4 * (r & 3) : X + (mn0 + r) * ld + 8 * g;
-    else
-        return TR ? X + g * ld + mn0 + r : X + (mn0 + r) * ld + g;
-}
-template <class E, int N, bool TR>
-__device__ __forceinline__ void frags(typename Mma<E>::frag (&f)[N], const E* base, int ld, int k0) {
-#pragma unroll
-    for (int n = 0; n < N; n++) {
-        if constexpr (sizeof(E) == 2) {
-            if constexpr (!TR) {
-                f[n] = *(const typename Mma<E>::frag*)(base + 16 * n * ld + k0);
-            } else {
-                const E* q = base + k0 * ld + 16 * n;
-                i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q));
-                i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, q + 4 * ld));
-                i16x8 c = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                f[n] = __builtin_bit_cast(typename Mma<E>::frag, c);
-            }
-        } else {
-            f[n] = TR ? base[k0 * ld + 16 * n] : base[16 * n * ld + k0];
-        }
-    }
-}
-// acc[i][j] += A-tile i times B-tile j, run as (Bᵀ Aᵀ)ᵀ: the MFMA takes the B
-// fragment as its first operand, so the tile comes out in row form: lane
-// 16g + r holds row r and columns 4g .. 4g+3 of the tile (four adjacent
-// columns of one row: whole 8-byte stores, and one row per lane).
-template <class E, int TM, int TN>
-__device__ __forceinline__ void mma_tiles(f32x4 (&acc)[TM][TN], const typename Mma<E>::frag (&fa)[TM],
-                                          const typename Mma<E>::frag (&fb)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = Mma<E>::run(fb[j], fa[i], acc[i][j]);
-}
-
-// Wave-level product acc[i][j] += A[m0+16i.., k] * B[k, n0+16j..] over k < KD
-// (AT: A stored [k][m], else [m][k]; BT_: B stored [k][n], else [n][k]); one
-// k-step of fragments in registers at a time (the other workgroup on the CU
-// covers the LDS latency); lane offsets from a fresh lane index (see lane_o).
-template <class E, int TM, int TN, int KD, bool AT, bool BT_>
-__device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda, const E* B, int ldb, int m0, int n0) {
-    using M = Mma<E>;
-    const int l = lane_o();
-    const E* pa = frag_base<E, AT>(A, lda, m0, l);
-    const E* pb = frag_base<E, BT_>(B, ldb, n0, l);
-#pragma unroll
-    for (int s = 0; s < KD / M::KS; s++) {
-        typename M::frag fa[TM], fb[TN];
-        frags<E, TM, AT>(fa, pa, lda, s * M::KS);
-        frags<E, TN, BT_>(fb, pb, ldb, s * M::KS);
-        mma_tiles<E>(acc, fa, fb);
-    }
 }
 
 // Row and column offset of this lane's accumulator elements, from a fresh
@@ -172,20 +98,6 @@ __device__ __forceinline__ void gemm4(f32x4 (&acc)[TM][TN], const E* A, int lda,
     const int lq_ = lane_o();                   \
     const int rw = m0 + (lq_ & 15);             \
     const int cg = 4 * (lq_ >> 4)
-
-// Two adjacent 16-bit (or fp32) elements, stored as one access.
-
-// base + off elements, with the byte offset formed in 32 bits: a uniform base
-// and a 32-bit per-lane offset map onto the scalar-base addressing of global
-// loads and stores (no 64-bit address arithmetic per lane).
-template <class T>
-__device__ __forceinline__ T* at32(T* base, unsigned off) {
-    return (T*)((char*)base + off * (unsigned)sizeof(T));
-}
-template <class T>
-__device__ __forceinline__ const T* at32(const T* base, unsigned off) {
-    return (const T*)((const char*)base + off * (unsigned)sizeof(T));
-}
 
 // Register staging of a [ROWS][D] row block (row stride rs elements): load()
 // issues the 16-byte loads (rows at or past C read row C-1, a valid row),
