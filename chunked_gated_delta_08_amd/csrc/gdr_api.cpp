@@ -341,14 +341,6 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     auto* seg = (SegInfo*)(base + w.seg_info);
     auto* ss0 = (int32_t*)(base + w.seq_seg0);
     auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
-    if ((st = mark(0)) != GDR_OK) return st;
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
-    if (q.NT > 0) {
-        st = launch_status(gdr::launch_prep(q, qp, k, v, g_cum, beta, info, base + w.W, base + w.U, base + w.R,
-                                            base + w.A, base + w.KT, stream));
-        if (st != GDR_OK) return st;
-    }
-    if ((st = mark(1)) != GDR_OK) return st;
     gdr::ScanArgs a{};
     a.dO = dO; a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
     set_seg_buffers(a, base, w);
@@ -361,6 +353,16 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
         a.info = info;
         a.cmax = (float*)(base + w.cmax); a.hmax = (float*)(base + w.hmax); a.dsc = (float*)(base + w.dsc);
     }
+    if ((st = mark(0)) != GDR_OK) return st;
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
+    // the scales first (they read dO and dht only), then the WY factors
+    if ((st = launch_status(gdr::launch_scan_scales(q, a, stream))) != GDR_OK) return st;
+    if (q.NT > 0) {
+        st = launch_status(gdr::launch_prep(q, qp, k, v, g_cum, beta, info, base + w.W, base + w.U, base + w.R,
+                                            base + w.A, base + w.KT, stream));
+        if (st != GDR_OK) return st;
+    }
+    if ((st = mark(1)) != GDR_OK) return st;
     if ((st = launch_status(gdr::launch_scans(q, a, stream))) != GDR_OK) return st;
     if ((st = mark(2)) != GDR_OK) return st;
     if (q.NT > 0) {

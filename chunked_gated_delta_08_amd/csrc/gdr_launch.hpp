@@ -104,6 +104,9 @@ struct ScanArgs {
     const ChunkInfo* info; float* cmax; float* hmax; float* dsc;
 };
 hipError_t launch_scans(const Problem& p, const ScanArgs& a, hipStream_t s);
+// dmax + dscale: the power-of-two scales the reverse scans of a 16-bit
+// problem run dO and dht under (a.dsc); launch before launch_scans
+hipError_t launch_scan_scales(const Problem& p, const ScanArgs& a, hipStream_t s);
 
 // K3 (+ the tail): per-chunk gradients.
 struct GradArgs {

@@ -876,18 +876,6 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
     const bool none_f = !a.do_fwd || !a.hT, none_r = !a.do_rev || !a.dhT;
     if (!(est_f && est_r) && !(none_f && none_r)) return hipErrorInvalidValue;
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
-    if constexpr (sizeof(S) == 2) {
-        if (a.do_rev && a.dsc) {   // scales of the reverse scans
-            const int nseq = p.cu ? p.N : p.B;
-            static_assert(VD % 8 == 0 && 64 % (VD / 8) == 0, "a head's vectors stay inside one wave");
-            hipLaunchKernelGGL((dmax_kernel<E, VD>), dim3((unsigned)(4 * p.NT + (int64_t)nseq * p.HV)), dim3(256), 0, s,
-                               a, (int)p.NT, p.HV, KD * VD);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(dscale_kernel, dim3((unsigned)(nseq * p.HV)), dim3(256), 0, s, a, p.HV);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-    }
     if (p.maxS > 1) {
         if constexpr (sizeof(S) == 2) {
             ScanArgs a1 = a;   // local scans write only their final states
@@ -912,6 +900,29 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3(nfwd + nrev), dim3(256), Cf::smem, s, a, nfwd, p.HV);
     return hipGetLastError();
+}
+
+// The reverse scans' scales (16-bit problems with a.dsc set): max |dO| per
+// quarter chunk and max |dht| per block, then one power of two per (sequence,
+// value head).  They read only dO and dht, so the call may run them before
+// the WY factors.
+template <class E, int VD>
+static hipError_t scale_go(const Problem& p, const ScanArgs& a, hipStream_t s, int KV) {
+    const int nseq = p.cu ? p.N : p.B;
+    static_assert(VD % 8 == 0 && 64 % (VD / 8) == 0, "a head's vectors stay inside one wave");
+    hipLaunchKernelGGL((dmax_kernel<E, VD>), dim3((unsigned)(4 * p.NT + (int64_t)nseq * p.HV)), dim3(256), 0, s, a,
+                       (int)p.NT, p.HV, KV);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dscale_kernel, dim3((unsigned)(nseq * p.HV)), dim3(256), 0, s, a, p.HV);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_scales(const Problem& p, const ScanArgs& a, hipStream_t s) {
+    if (!a.do_rev || !a.dsc || p.dtype == 0) return hipSuccess;
+    if (p.V == 128) return p.dtype == 2 ? scale_go<bf16, 128>(p, a, s, p.K * 128) : scale_go<f16, 128>(p, a, s, p.K * 128);
+    if (p.V == 64) return p.dtype == 2 ? scale_go<bf16, 64>(p, a, s, p.K * 64) : scale_go<f16, 64>(p, a, s, p.K * 64);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_scans(const Problem& p, const ScanArgs& a, hipStream_t s) {
