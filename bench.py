@@ -125,7 +125,8 @@ def kernel_bytes(cfg, chunks, es=2):
     st = 64 * K * es              # one [64, K] workspace tile
     state = K * V * es            # one K x V state in the workspace
     gb = ntok * HV * (4 + es)     # gate (fp32) and beta
-    # prep: q, k, v, gate, beta in; W, U, R, K~ tiles and A out
+    # prep: q, k, v, gate, beta in; W, U, R, K~ tiles and A out (the stage's time
+    # also covers the max |dO| pass of 16-bit problems, whose read of dO is not counted)
     prep = HK * (2 * tok_k) + HV * tok_v + gb + nunits * (4 * st + 64 * 64 * es)
     # forward scan: W, K~, U in, h states out; reverse scan: W, K~, R, dO in, dh states out
     scans = nunits * (3 * st) + nunits * state + nunits * (3 * st) + HV * tok_v + nunits * state

@@ -182,8 +182,9 @@ int gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void
  * gdr_chunk_bwd_events -- gdr_chunk_bwd for measurement tools.  Identical
  * computation and arguments; `events` (NULL or 4 caller-created hipEvent_t)
  * are recorded on `stream` before the first launch and after each of the three
- * stages: [0] start, [1] after the chunk table and WY-factor kernel, [2] after
- * the two chunk scans, [3] after the gradient kernel.  hipEventElapsedTime on
+ * stages: [0] start, [1] after the chunk table, the dO scale pass (16-bit
+ * problems) and the WY-factor kernel, [2] after the two chunk scans, [3] after
+ * the gradient kernel.  hipEventElapsedTime on
  * consecutive pairs gives the per-stage GPU time of this call.
  */
 int gdr_chunk_bwd_events(const gdr_problem *p, const void *q, const void *k, const void *v, const float *g_cum,
