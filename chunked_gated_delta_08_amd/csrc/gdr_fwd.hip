@@ -69,7 +69,9 @@ struct FwdCfg {
 
 // Persistent: workgroup b handles units (chunk, value head) b, b + grid, ...;
 // 512 threads (8 waves, two per SIMD); wave w computes rows 32 (w & 1) .. +31
-// and column block w >> 1 of every output.  The next unit's Q, K, W, U, h and
+// and column block w >> 1 of every output.  Products run in row form (a lane
+// holds four adjacent columns of one row of each tile), so Pm, V_new and o
+// move through LDS as 8-byte row pieces.  The next unit's Q, K, W, U, h and
 // gate are loaded into registers while the current unit is computed.
 // E: input type; S: operand type of the workspace tiles and of the MFMAs (fp16
 // for 16-bit inputs, fp32 for fp32).
@@ -184,15 +186,18 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
             const int n0 = 16 * (w >> 1);
             f32x4 aqk[2][1];
             zero_acc(aqk);
-            wgemm<S, 2, 1, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+            wgemm_rf<S, 2, 1, KD, false, false>(aqk, sQ, LK, sK, LK, m0, n0);
+            const int c0 = rf_col(n0, 0);
+            const f32x4 gc = *(const f32x4*)(sG + c0);
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < 2; i++) {
+                const int r = rf_row(m0, i);
+                const float gr = sG[r];
+                f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int r = acc_row(m0, i, e), c = acc_col(n0, 0);
-                    const float x = scale * __expf(sG[r] - sG[c]) * aqk[i][0][e];
-                    sPm[r * LA + c] = (S)(c <= r ? x : 0.f);
-                }
+                for (int e = 0; e < 4; e++) x[e] = c0 + e <= r ? scale * __expf(gr - gc[e]) * aqk[i][0][e] : 0.f;
+                st4<S>(sPm + r * LA + c0, x);
+            }
         }
         // ---- W h and Q h   (wave w: 32 rows x VD/4 columns); V_new = U − W h in place
         constexpr int TN = VD / 64;
@@ -202,32 +207,27 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
             f32x4 wh[2][TN];
             zero_acc(wh);
             zero_acc(qh);
-            wgemm<S, 2, TN, KD, false, false>(wh, sW, LK, sH, LK, m0, n0);
-            wgemm<S, 2, TN, KD, false, false>(qh, sQ, LK, sH, LK, m0, n0);
+            wgemm_rf<S, 2, TN, KD, false, false>(wh, sW, LK, sH, LK, m0, n0);
+            wgemm_rf<S, 2, TN, KD, false, false>(qh, sQ, LK, sH, LK, m0, n0);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < TN; j++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int r = acc_row(m0, i, e), c = acc_col(n0, j);
-                        sVn[r * LV + c] = (S)((float)sVn[r * LV + c] - wh[i][j][e]);
-                    }
+                for (int j = 0; j < TN; j++) {   // the lane's own elements of U
+                    S* p = sVn + rf_row(m0, i) * LV + rf_col(n0, j);
+                    st4<S>(p, ld4<S>(p) - wh[i][j]);
+                }
         }
         lds_barrier();   // Pm and V_new complete; K is no longer read
         // ---- o = scale · diag(γ) Q h + Pm V_new
         f32x4 ov[2][TN];
         zero_acc(ov);
-        wgemm<S, 2, TN, 64, false, true>(ov, sPm, LA, sVn, LV, m0, n0);
+        wgemm_rf<S, 2, TN, 64, false, true>(ov, sPm, LA, sVn, LV, m0, n0);
 #pragma unroll
         for (int i = 0; i < 2; i++) {
+            const int r = rf_row(m0, i);
+            const float gq = scale * __expf(sG[r]);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int r = acc_row(m0, i, 0) + e;
-                const float gq = scale * __expf(sG[r]);
-#pragma unroll
-                for (int j = 0; j < TN; j++) sO[r * LV + acc_col(n0, j)] = (E)(ov[i][j][e] + gq * qh[i][j][e]);
-            }
+            for (int j = 0; j < TN; j++) st4<E>(sO + r * LV + rf_col(n0, j), ov[i][j] + gq * qh[i][j]);
         }
         lds_barrier();
 #pragma unroll
