@@ -75,7 +75,7 @@ int check_problem(const gdr_problem* p, Problem* q, int dirs = 2) {
     if (p->B < 1 || p->T < 0 || p->HK < 1 || p->HV < 1 || p->K < 1 || p->V < 1 || p->BT < 1) return GDR_ERR_INVALID;
     if (p->HV % p->HK != 0) return GDR_ERR_INVALID;
     if (p->dtype != GDR_F32 && p->dtype != GDR_F16 && p->dtype != GDR_BF16) return GDR_ERR_INVALID;
-    int64_t nt = 0;
+    int64_t nt = 0, maxc = 0;
     int nseq;
     if (p->cu_seqlens) {
         if (!p->cu_seqlens_host || p->B != 1 || p->N < 1) return GDR_ERR_INVALID;
@@ -83,17 +83,20 @@ int check_problem(const gdr_problem* p, Problem* q, int dirs = 2) {
         if (cu[0] != 0) return GDR_ERR_INVALID;
         for (int n = 0; n < p->N; n++) {
             if (cu[n + 1] < cu[n]) return GDR_ERR_INVALID;
-            nt += (cu[n + 1] - cu[n] + p->BT - 1) / p->BT;
+            const int64_t c = (cu[n + 1] - cu[n] + p->BT - 1) / p->BT;
+            nt += c;
+            maxc = c > maxc ? c : maxc;
         }
         if (cu[p->N] != p->T) return GDR_ERR_INVALID;
         nseq = p->N;
     } else {
-        nt = (int64_t)p->B * ((p->T + p->BT - 1) / p->BT);
+        maxc = (p->T + p->BT - 1) / p->BT;
+        nt = (int64_t)p->B * maxc;
         nseq = p->B;
     }
     if ((int64_t)p->B * p->T > INT32_MAX / 2) return GDR_ERR_UNSUPPORTED;
     q->B = p->B; q->T = p->T; q->HK = p->HK; q->HV = p->HV; q->K = p->K; q->V = p->V; q->BT = p->BT;
-    q->N = nseq; q->NT = nt;
+    q->N = nseq; q->NT = nt; q->maxC = maxc;
     q->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->K);
     q->dtype = p->dtype;
     q->cu = p->cu_seqlens;

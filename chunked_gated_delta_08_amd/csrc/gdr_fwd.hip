@@ -12,40 +12,45 @@
 namespace gdr {
 
 // ---------------------------------------------------------------- gate cumsum
-// One thread per (token, value head): the in-chunk prefix sum of the raw gate
-// up to this token, accumulated in fp32 in token order from the chunk's first
-// token (so every element is the same sequence of fp32 additions a serial
-// in-chunk scan performs).
+// One thread per (chunk, value head): the chunk's prefix sums of the raw gate
+// in token order, each one fp32 addition after the previous, starting from the
+// chunk's first value itself (so every element is the same sequence of fp32
+// additions a serial in-chunk scan performs).  Grid x: the (chunk, head)
+// pairs of the longest sequence; grid y: the sequences (strided past 65535).
 __global__ void gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, const int32_t* __restrict__ cu,
-                                   int nseq, int T, int HV, int BT, long ntok) {
+                                   int nseq, int T, int HV, int BT, int maxC) {
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= ntok * HV) return;
-    const long t = idx / HV;
-    const int hv = (int)(idx % HV);
-    long bos;
-    if (cu) {   // sequence of token t: largest n with cu[n] <= t
-        int lo = 0, hi = nseq - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cu[mid] <= t) lo = mid;
-            else hi = mid - 1;
+    if (idx >= (long)maxC * HV) return;
+    const int c = (int)(idx / HV), hv = (int)(idx % HV);
+    for (int n = blockIdx.y; n < nseq; n += gridDim.y) {
+        const long bos = cu ? (long)cu[n] : (long)n * T, eos = cu ? (long)cu[n + 1] : bos + T;
+        const long t0 = bos + (long)c * BT;
+        if (t0 >= eos) continue;
+        const int len = (int)(eos - t0 < BT ? eos - t0 : BT);
+        const float* gp = g + t0 * HV + hv;
+        float* op = gc + t0 * HV + hv;
+        float acc = 0.f;
+        for (int s0 = 0; s0 < len; s0 += 16) {   // sixteen loads in flight, then the serial additions
+            float x[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) x[u] = gp[(long)min(s0 + u, len - 1) * HV];
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                if (s0 + u < len) {
+                    acc = s0 + u == 0 ? x[u] : acc + x[u];
+                    op[(long)(s0 + u) * HV] = acc;
+                }
+            }
         }
-        bos = cu[lo];
-    } else {
-        bos = (t / T) * (long)T;
     }
-    const long c0 = bos + ((t - bos) / BT) * BT;
-    float acc = g[c0 * HV + hv];
-    for (long s = c0 + 1; s <= t; s++) acc += g[s * HV + hv];
-    gc[idx] = acc;
 }
 
 hipError_t launch_gate_cumsum(const Problem& p, const float* g, float* gc, hipStream_t s) {
-    const long ntok = p.cu ? p.T : (long)p.B * p.T;
-    const long n = ntok * p.HV;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, gc, p.cu,
-                       p.cu ? p.N : p.B, p.T, p.HV, p.BT, ntok);
+    const long pairs = (long)p.maxC * p.HV;
+    if (pairs == 0 || p.N == 0) return hipSuccess;
+    const unsigned gy = (unsigned)(p.N < 65535 ? p.N : 65535);
+    hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)((pairs + 255) / 256), gy), dim3(256), 0, s, g, gc, p.cu,
+                       p.N, p.T, p.HV, p.BT, (int)p.maxC);
     return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct Problem {
     int L;             // scan segment length in chunks
     int NS;            // total scan segments
     int maxS;          // most segments in one sequence (1: no segmented scans)
+    int64_t maxC;      // most chunks in one sequence
 };
 
 // Workspace carve-up (byte offsets from the workspace base).  The segment
