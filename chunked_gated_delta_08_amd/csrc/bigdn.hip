@@ -93,13 +93,28 @@ __global__ void __launch_bounds__(256) bigdn_stats_kernel(const bf16* __restrict
     const bf16* q = qkv + (size_t)tok * 3 * C;
     const bf16* k = q + C;
     float sq = 0.f, sk = 0.f;
-    for (int c8 = l; c8 < C / 8; c8 += 64) {
-        const bf16x8 a = *(const bf16x8*)(q + 8 * c8);
-        const bf16x8 b = *(const bf16x8*)(k + 8 * c8);
+    const int nv = C / 8;   // 16-byte vectors per row
+    for (int c0 = 0; c0 < nv; c0 += 256) {
+        // four vectors of q and of k per lane in flight before any arithmetic
+        // (indices past the row repeat its last vector and are weighted 0)
+        bf16x8 a[4], b[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            sq += (float)a[i] * (float)a[i];
-            sk += (float)b[i] * (float)b[i];
+        for (int u = 0; u < 4; u++) {
+            const int c8 = min(c0 + l + 64 * u, nv - 1);
+            a[u] = *(const bf16x8*)(q + 8 * c8);
+            b[u] = *(const bf16x8*)(k + 8 * c8);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float wgt = c0 + l + 64 * u < nv ? 1.f : 0.f;
+            float xq = 0.f, xk = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                xq += (float)a[u][i] * (float)a[u][i];
+                xk += (float)b[u][i] * (float)b[u][i];
+            }
+            sq += wgt * xq;
+            sk += wgt * xk;
         }
     }
     sq = wave_sum(sq);
