@@ -46,9 +46,16 @@ def _oracle_problem(oracle, inp):
     return oracle.Problem(inp["B"], inp["T"], inp["HK"], inp["HV"], inp["K"], inp["V"], cu_seqlens=inp["cu"])
 
 
+# 48 sequence lengths in [0, 200) from a seeded generator, with empty and
+# one-token sequences first, in the middle and last
+MANY = [int(x) for x in np.random.default_rng(7).integers(0, 200, size=48)]
+MANY[0], MANY[24], MANY[-1] = 0, 1, 0
+
+
 # ------------------------------------------------------------------ gate cumsum
 @pytest.mark.parametrize("B_,T,HV,lens,BT", [(2, 300, 3, None, 64), (1, None, 4, [70, 5, 130, 0, 64, 1], 64),
-                                            (3, 64, 1, None, 64), (1, None, 2, [1, 200], 16)])
+                                            (3, 64, 1, None, 64), (1, None, 2, [1, 200], 16),
+                                            (1, None, 4, MANY, 64)])
 def test_gate_cumsum(B, oracle, B_, T, HV, lens, BT):
     _log(f"[fwd] gate cumsum B={B_} T={T} HV={HV} lens={lens} BT={BT}")
     inp = W.gdr_inputs(B_, T, 1, HV, 64, 64, BT=BT, dtype="f32", seed=5, lengths=lens)
@@ -75,6 +82,8 @@ FWD_CASES = {
     "bf16_k64_gqa3_batch2": (2, 100, 1, 3, 64, 64, "bf16", None, {"gate_scale": 1 / 8}, 0),
     "bf16_gqa2_varlen_seg2": (1, None, 2, 4, 128, 128, "bf16", [300, 5, 530, 0, 64, 1, 200],
                               {"gate_scale": 1 / 16, "h0": True}, 2),
+    "bf16_gqa2_many_sequences": (1, None, 2, 4, 64, 64, "bf16", MANY, {"gate_scale": 1 / 16, "h0": True}, 0),
+    "bf16_gqa2_many_sequences_seg2": (1, None, 2, 4, 64, 64, "bf16", MANY, {"gate_scale": 1 / 16, "h0": True}, 2),
 }
 
 

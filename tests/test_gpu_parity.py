@@ -168,6 +168,27 @@ MAG_CASES = {
 }
 
 
+def _many_lengths(n, seed):
+    """n sequence lengths in [0, 200) from a seeded generator, with empty and
+    one-token sequences placed first, in the middle and last."""
+    lens = [int(x) for x in np.random.default_rng(seed).integers(0, 200, size=n)]
+    lens[0], lens[n // 2], lens[-1] = 0, 1, 0
+    return lens
+
+
+@pytest.mark.parametrize("seg", [0, 2])
+def test_many_sequences(B, oracle, seg):
+    """48 short sequences (empty, one-token and ragged ones among them), GQA
+    ratio 2, h0 and dht: the chunk and segment tables, the per-sequence scans
+    and the group sums over many sequence boundaries."""
+    lens = _many_lengths(48, 7)
+    _log(f"[parity] many sequences: {len(lens)} lengths, {sum(lens)} tokens, seg_chunks={seg}")
+    inp = W.gdr_inputs(1, None, 2, 4, 64, 64, dtype="bf16", seed=9, lengths=lens, h0=True, gate_scale=1 / 16)
+    got = _run_gpu(B, inp, seg_chunks=seg)
+    ref = _run_oracle(oracle, inp)
+    _compare(got, ref, "bf16", label=f"many_sequences_seg{seg}")
+
+
 @pytest.mark.parametrize("name", list(MAG_CASES))
 def test_magnitude_parity(B, oracle, name):
     T, HK, HV, lens, extra, fo, fv = MAG_CASES[name]
