@@ -173,7 +173,8 @@ struct ScanJob {
     float* out;         // K x V block of the final state
     float* out2;        // merged forward job: K x K block of the transfer matrix, in the
                         // fragment order with the values in the 16-bit operand type S
-                        // (four per lane and tile): it only enters MFMAs as an operand
+                        // (four per lane and tile; its transpose in the same order after
+                        // it, in the block's second half): it only enters MFMAs as an operand
     float sc = 1.f;     // reverse jobs: the state and dO run scaled by sc (a power of two);
     float isc = 1.f;    // the per-chunk states dh[c] are stored scaled (the gradient kernel
                         // folds 1/sc into its factors), dh0 is stored times isc = 1/sc
@@ -543,7 +544,13 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 s4 x;
 #pragma unroll
                 for (int e = 0; e < 4; e++) x[e] = (S)St[nb][t][e];
-                *(s4*)((S*)jb.out2 + (((CW * w / 16 + nb - NB) * KT + t) * 64 + l) * 4) = x;
+                const int cb = CW * w / 16 + nb - NB;
+                *(s4*)((S*)jb.out2 + ((cb * KT + t) * 64 + l) * 4) = x;
+                // P_sᵀ in the same order in the block's second half: element
+                // P[16t + 4g + e][16cb + r] is Pᵀ's [16cb + r][16t + 4g + e]
+                S* pt = (S*)jb.out2 + KD * KD + ((t * KT + cb) * 64 + 16 * (r >> 2) + 4 * g) * 4 + (r & 3);
+#pragma unroll
+                for (int e = 0; e < 4; e++) pt[4 * e] = x[e];
             }
     }
     if (jb.out_form == ST_FRAG) {
@@ -666,108 +673,116 @@ seg_kernel(ScanArgs a, int NS, int HV) {
 //   forward  h_start[s+1] = P_s h_start[s] + hloc_s       (h_start[0] = h0)
 //   reverse  dh_in[s-1]   = P_sᵀ dh_in[s] + dhloc_s       (dh_in[S-1] = dht)
 // writing every boundary state except the two sequence ends (which the scans
-// read from h0 / dht).  The state columns evolve independently, so each
-// (sequence, value head, direction) job is split by columns over VD/64
-// workgroups of four waves, one 16-column block per wave, the state in fp32
-// accumulators as in the scans.  P_s (16-bit, fragment order, written by the
-// local scans) is staged in LDS transposed (PT[v][k] = P[k][v]); the P and
-// hloc blocks of the next two segments are in flight in registers while the
-// current product runs.  Grid: forward jobs then reverse jobs, N*HV*VD/64 each.
+// read from h0 / dht).  The state columns evolve independently: each
+// (sequence, value head, direction) job is split over VD/16 workgroups of one
+// 16-column block each, and wave w of a workgroup forms rows 32w .. 32w+31 of
+// the new state X as Xᵀ = Stᵀ Mᵀ with M = P_s (forward) or P_sᵀ (reverse).
+// The A operand Stᵀ is read from a [16][K] 16-bit copy of the state in LDS
+// (double-buffered, one barrier per step).  The B operand Mᵀ comes straight
+// from global memory: the local scans store P_s in the accumulator fragment
+// order (a lane's four values are four consecutive rows of one column, half of
+// a B fragment of P) and P_sᵀ in the same order in the block's second half, so
+// every fragment is two 8-byte loads, issued two segments ahead.  hloc enters
+// as the accumulators' initial value; X leaves in the scans' fragment order.
+// Grid: forward jobs then reverse jobs, N*HV*VD/16 each; 2*KD threads.
 template <class S, int KD, int VD>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-combine_kernel(ScanArgs a, int nseq, int HV) {
+__global__ void __launch_bounds__(2 * KD) combine_kernel(ScanArgs a, int nseq, int HV) {
     static_assert(KD == VD, "the transfer matrix multiplies the state from the left");
     static_assert(sizeof(S) == 2, "transfer matrices are 16-bit");
-    constexpr int KT = KD / 16, VS = VD / 64, LK = KD + spad<S>();
-    constexpr int NP = KD * KD / (4 * 256);   // 4-element groups of P per thread
+    constexpr int KT = KD / 16, NCB = VD / 16, NTH = 2 * KD, LKT = KD + 8, NKS = KD / 32;
+    constexpr int NI = 16 * KD / NTH;   // initial-state elements per thread
     typedef S s4 __attribute__((ext_vector_type(4)));
-    extern __shared__ __align__(16) unsigned char smem[];
-    S* sPT = (S*)smem;
     using frag = typename Mma<S>::frag;
-    const int per = nseq * HV * VS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* sT = (S*)smem;   // two [16][LKT] buffers of Stᵀ
+    const int per = nseq * HV * NCB;
     const bool rev = (int)blockIdx.x >= per;
     const int b = rev ? (int)blockIdx.x - per : (int)blockIdx.x;
-    const int vs = b % VS, n = b / VS / HV, hv = b / VS % HV;
+    const int cbw = b % NCB, hv = b / NCB % HV, n = b / NCB / HV;
     const int s0 = a.seq_seg0[n], S_n = a.seq_seg0[n + 1] - s0;
     if (S_n < 2 || (rev ? !a.do_rev : !a.do_fwd)) return;
     const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-    const int cb = 4 * vs + w;           // this wave's 16-column block
-    const int col = 16 * cb + r;
     const long KV = (long)KD * VD;
     auto blk = [&](float* base, int j) { return base + ((long)j * HV + hv) * KV; };
 
-    f32x4 St[KT];
-    const float* init = rev ? a.dht : a.h0;
-    const float isc0 = rev && a.dsc ? a.dsc[(long)n * HV + hv] : 1.f;   // reverse: scaled space
+    // the initial state's 16 columns -> Stᵀ (reverse: in the scaled space)
+    {
+        const float* init = rev ? a.dht : a.h0;
+        const float isc0 = rev && a.dsc ? a.dsc[(long)n * HV + hv] : 1.f;
 #pragma unroll
-    for (int t = 0; t < KT; t++)
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            St[t][e] = init ? isc0 * init[((long)n * HV + hv) * KV + (16 * t + 4 * g + e) * VD + col] : 0.f;
-
+        for (int i = 0; i < NI; i++) {
+            const int idx = threadIdx.x + NTH * i, k = idx / 16, c = idx % 16;
+            const float x = init ? isc0 * init[((long)n * HV + hv) * KV + (long)k * VD + 16 * cbw + c] : 0.f;
+            sT[c * LKT + k] = (S)x;
+        }
+    }
     // step q uses segment j(q): forward j = s0 + q (q = 0 .. S_n-2), reverse j = s0 + S_n-1-q
     const int nsteps = S_n - 1;
     auto seg_of = [&](int q) { return rev ? s0 + S_n - 1 - q : s0 + q; };
+    // this lane's elements of X (and of hloc, and of the output) in the scans'
+    // fragment order: X[32w + 16nt + r][16cbw + 4g + e] at float offset
+    // ((cbw KT + 2w + nt) 64 + 16 (r/4) + 4g + e) 4 + r % 4
+    auto foff = [&](int nt, int e) { return ((cbw * KT + 2 * w + nt) * 64 + 16 * (r >> 2) + 4 * g + e) * 4 + (r & 3); };
     struct Stg {
-        s4 p[NP];
-        f32x4 h[KT];
+        s4 m[NKS][2][2];   // B fragments of Mᵀ: k-step, n tile, half
+        float h[2][4];     // hloc
     };
     auto prefetch = [&](Stg& x, int q) {
         const int j = seg_of(q);
-        const S* P = (const S*)blk(a.P, j);
+        const S* M = (const S*)blk(a.P, j) + (rev ? 0 : KD * KD);
         const float* H = blk(rev ? a.dhloc : a.hloc, j);
 #pragma unroll
-        for (int i = 0; i < NP; i++) x.p[i] = *(const s4*)(P + (threadIdx.x + 256 * i) * 4);
+        for (int sk = 0; sk < NKS; sk++)
 #pragma unroll
-        for (int t = 0; t < KT; t++) x.h[t] = *(const f32x4*)(H + ((cb * KT + t) * 64 + l) * 4);
+            for (int nt = 0; nt < 2; nt++) {
+                // rows 32 sk + 8 g + {0..7} of column 32 w + 16 nt + r of Mᵀ's
+                // stored tile (column block 2w + nt, row block 2 sk + g/2)
+                const S* p = M + (((2 * w + nt) * KT + 2 * sk + (g >> 1)) * 64 + 32 * (g & 1) + r) * 4;
+                x.m[sk][nt][0] = *(const s4*)p;
+                x.m[sk][nt][1] = *(const s4*)(p + 64);
+            }
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) x.h[nt][e] = H[foff(nt, e)];
     };
     auto step = [&](int q, const Stg& x) {
-        lds_barrier();   // the previous product has read sPT
+        const S* cur = sT + (q & 1) * 16 * LKT;
+        S* nxt = sT + ((q + 1) & 1) * 16 * LKT;
+        f32x4 C[2];
 #pragma unroll
-        for (int i = 0; i < NP; i++) {   // fragment-order tile (cbp, tt), lane (g', r'): P[16tt+4g'+e][16cbp+r']
-            const int c = threadIdx.x + 256 * i, tile = c >> 6, ln = c & 63;
-            const int cbp = tile / KT, tt = tile % KT;
-            *(s4*)(sPT + (16 * cbp + (ln & 15)) * LK + 16 * tt + 4 * (ln >> 4)) = x.p[i];
-        }
-        f32x4 X[KT];
+        for (int nt = 0; nt < 2; nt++) C[nt] = f32x4{x.h[nt][0], x.h[nt][1], x.h[nt][2], x.h[nt][3]};
 #pragma unroll
-        for (int t = 0; t < KT; t++) X[t] = x.h[t];
-        lds_barrier();
-        frag Bs[KD / 32];
+        for (int sk = 0; sk < NKS; sk++) {
+            const frag fa = *(const frag*)(cur + r * LKT + 32 * sk + 8 * g);
 #pragma unroll
-        for (int s = 0; s < KD / 32; s++)
+            for (int nt = 0; nt < 2; nt++) {
+                const s4 lo = x.m[sk][nt][0], hi = x.m[sk][nt][1];
+                frag fb;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                Bs[s][e] = (S)St[2 * s][e];
-                Bs[s][4 + e] = (S)St[2 * s + 1][e];
-            }
-#pragma unroll
-        for (int t = 0; t < KT; t++)
-#pragma unroll
-            for (int s = 0; s < KD / 32; s++) {
-                i16x4 lo, hi;
-                if (rev) {   // rows of Pᵀ = rows of PT
-                    const S* p = sPT + (16 * t + r) * LK + 32 * s + 4 * g;
-                    lo = *(const i16x4*)p;
-                    hi = *(const i16x4*)(p + 16);
-                } else {     // rows of P = columns of PT
-                    lo = ld_trans4<S>(sPT, LK, 16 * t, 32 * s + 4 * g);
-                    hi = ld_trans4<S>(sPT, LK, 16 * t, 32 * s + 16 + 4 * g);
+                for (int e = 0; e < 4; e++) {
+                    fb[e] = lo[e];
+                    fb[4 + e] = hi[e];
                 }
-                i16x8 c8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                X[t] = Mma<S>::run(__builtin_bit_cast(frag, c8), Bs[s], X[t]);
+                C[nt] = Mma<S>::run(fa, fb, C[nt]);
             }
+        }
+        // C[nt][e] = X[32w + 16nt + r][16cbw + 4g + e]
         const int jd = rev ? seg_of(q) - 1 : seg_of(q) + 1;   // the segment whose boundary state this is
         float* out = blk(rev ? a.dhin : a.hstart, jd);
 #pragma unroll
-        for (int t = 0; t < KT; t++) {
-            St[t] = X[t];
-            *(f32x4*)(out + ((cb * KT + t) * 64 + l) * 4) = X[t];
-        }
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                out[foff(nt, e)] = C[nt][e];
+                nxt[(4 * g + e) * LKT + 32 * w + 16 * nt + r] = (S)C[nt][e];
+            }
+        lds_barrier();   // the next state is complete; this one is no longer read
     };
     Stg x0, x1;
     prefetch(x0, 0);
     if (nsteps > 1) prefetch(x1, 1);
+    lds_barrier();   // the initial state
     for (int q = 0; q < nsteps; q += 2) {
         step(q, x0);
         if (q + 2 < nsteps) prefetch(x0, q + 2);
@@ -887,8 +902,8 @@ static hipError_t scan_go(const Problem& p, const ScanArgs& a, hipStream_t s) {
             hipLaunchKernelGGL(k1, dim3(2 * per), dim3(256), Cf::smem, s, a1, p.NS, p.HV);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            constexpr int csm = KD * (KD + spad<S>()) * (int)sizeof(S);
-            hipLaunchKernelGGL((combine_kernel<S, KD, VD>), dim3(2 * nseq * p.HV * (VD / 64)), dim3(256), csm, s, a,
+            constexpr int csm = 2 * 16 * (KD + 8) * (int)sizeof(S);
+            hipLaunchKernelGGL((combine_kernel<S, KD, VD>), dim3(2 * nseq * p.HV * (VD / 16)), dim3(2 * KD), csm, s, a,
                                nseq, p.HV);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else {
