@@ -401,7 +401,7 @@ def main():
     ap.add_argument("--no-also", action="store_true", help="bwd: time only --workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the backward of one GPU's share); "
+        print("bench.py: measures one GPU only (the backward of one GPU's share); "
               "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
 

@@ -213,7 +213,7 @@ const char* gdr_strerror(int status) {
     switch (status) {
         case GDR_OK: return "ok";
         case GDR_ERR_INVALID: return "invalid argument (shape, dtype, null pointer or cu_seqlens)";
-        case GDR_ERR_UNSUPPORTED: return "unsupported configuration (this build handles BT=64, K=V in {64,128}; fp32 only at K=64)";
+        case GDR_ERR_UNSUPPORTED: return "unsupported configuration (the library handles BT=64, K=V in {64,128}; fp32 only at K=64)";
         case GDR_ERR_WORKSPACE: return "workspace missing or smaller than gdr_workspace_size()";
         case GDR_ERR_LAUNCH: return "HIP error at kernel launch";
         case GDR_ERR_SCRATCH: return "problem needs more workspace than the fixed scratch of gdr_chunk_bwd_noalloc";
