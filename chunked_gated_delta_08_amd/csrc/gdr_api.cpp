@@ -439,7 +439,7 @@ int kda_chunk_bwd(const gdr_problem* p, const void* qp, const void* k, const voi
     if (st != GDR_OK) return st;
     if (q.HK != q.HV) return GDR_ERR_INVALID;
     if (q.dtype == GDR_BF16) return GDR_ERR_UNSUPPORTED;
-    if (q.BT != 64 || q.K != q.V || (q.K != 64 && q.K != 128)) return GDR_ERR_UNSUPPORTED;
+    if ((q.BT != 64 && q.BT != 16) || q.K != q.V || (q.K != 64 && q.K != 128)) return GDR_ERR_UNSUPPORTED;
     if (q.dtype == GDR_F32 && q.K != 64) return GDR_ERR_UNSUPPORTED;   // fp32 tiles exceed the LDS budget at 128
     if (q.NT == 0) return GDR_OK;
     if (!qp || !k || !v || !v_new || !g || !beta || !A || !h || !dO || !dh || !dv_in || !dq || !dk || !dv_out ||

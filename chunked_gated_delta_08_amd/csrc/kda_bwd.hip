@@ -97,19 +97,22 @@ __device__ __forceinline__ int kda_tid() {
     return t & (KNT - 1);
 }
 
-// The unit's A rows [64][64] in registers (16-byte vectors, rows at or past Cn
-// read row Cn-1), stored to LDS as the lower triangle (zero above the
-// diagonal and in rows at or past Cn).
+// The unit's A rows in registers: a [64][64] tile of 16-byte vectors over the
+// chunk's rows of BT (16 or 64) entries (rows at or past Cn read row Cn-1;
+// columns past BT read the row's last vector), stored to LDS as the lower
+// triangle (zero above the diagonal and in rows at or past Cn <= BT, which
+// also clears every column past BT).
 template <class E>
 struct KdaARows {
     static constexpr int EPV = 16 / (int)sizeof(E), VPR = 64 / EPV, N = 64 * VPR / KNT;
     static_assert(64 * VPR % KNT == 0, "whole vectors per thread");
     kdv<E, EPV> v[N];
-    __device__ __forceinline__ void issue(const E* __restrict__ g, int rs, int Cn) {
+    __device__ __forceinline__ void issue(const E* __restrict__ g, int rs, int Cn, int BT) {
         const int t = kda_tid();
 #pragma unroll
         for (int i = 0; i < N; i++) {
-            const unsigned idx = t + KNT * i, r = min(idx / VPR, (unsigned)(Cn - 1)), c = idx % VPR * EPV;
+            const unsigned idx = t + KNT * i, r = min(idx / VPR, (unsigned)(Cn - 1));
+            const unsigned c = min(idx % VPR * EPV, (unsigned)(BT - EPV));
             v[i] = *(const kdv<E, EPV>*)at32(g, __umul24(r, (unsigned)rs) + c);
         }
     }
@@ -222,7 +225,7 @@ struct KdaElemOps {
 
 template <class E, int KD, int VD>
 __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, float scale) {
+kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, int BT, float scale) {
     using Cf = KdaCfg<E, KD, VD>;
     using M = Mma<E>;
     using frag = typename M::frag;
@@ -245,7 +248,7 @@ kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, float
 
     const int ci = blockIdx.x, hh = blockIdx.y;
     int t0i, Cn;
-    kda_find_chunk(cu, N, T, 64, ci, t0i, Cn);
+    kda_find_chunk(cu, N, T, BT, ci, t0i, Cn);   // chunks of BT <= 64 rows, each in a 64-row tile
     const long t0 = t0i;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int m0 = 32 * (w & 1);             // the wave's row half of every [64][.] result
@@ -269,7 +272,7 @@ kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, float
     const E bb = ((const E*)a.beta)[(t0 + min((int)threadIdx.x & (C - 1), Cn - 1)) * H + hh];
     __builtin_amdgcn_sched_barrier(0);
     KdaARows<E> ra;
-    ra.issue((const E*)a.A + (t0 * H + hh) * 64, H * 64, Cn);
+    ra.issue((const E*)a.A + (t0 * H + hh) * BT, H * BT, Cn, BT);
     using Slice = KdaSlice<E, KD, VD, VS, LS>;
     Slice sl;
     sl.issue(hg, dhg, dO0, dv0, vn0, v0, rsv, Cn);
@@ -501,18 +504,18 @@ kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, float
         zero_acc(da);
         gemm4<E, 2, 2, 64, false, false>(da, sP, LA, sA, LA, m0, n0s);
         KDA_LANE_RC();
-        float* dAb = a.dA + (t0 * H + hh) * 64;
+        float* dAb = a.dA + (t0 * H + hh) * BT;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const int rr = rw + 16 * i;
             if (rr < Cn) {
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
-                    const int c0 = n0s + 16 * j + cg;
+                    const int c0 = n0s + 16 * j + cg;   // a multiple of 4: inside the row when below BT
                     f32x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; e++) x[e] = (c0 + e < rr) ? -da[i][j][e] : 0.f;
-                    *(f32x4*)at32(dAb, __umul24((unsigned)rr, (unsigned)(H * 64)) + c0) = x;
+                    if (c0 < BT) *(f32x4*)at32(dAb, __umul24((unsigned)rr, (unsigned)(H * BT)) + c0) = x;
                 }
             }
         }
@@ -526,7 +529,9 @@ static hipError_t kda_go(const Problem& p, const KdaArgs& a, hipStream_t s) {
     static_assert(Cf::smem <= 160 * 1024, "LDS budget");
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(KNT), Cf::smem, s, a, p.cu, p.N, p.T, p.HV, p.scale);
+    if (p.BT != 16 && p.BT != 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(KNT), Cf::smem, s, a, p.cu, p.N, p.T, p.HV, p.BT,
+                       p.scale);
     return hipGetLastError();
 }
 

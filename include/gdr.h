@@ -196,7 +196,8 @@ int gdr_chunk_bwd_events(const gdr_problem *p, const void *q, const void *k, con
  * kda_chunk_bwd -- the KDA (per-channel gate) WY backward stage ([P2] 函数签名,
  * 参数说明, 实现原理).  Requires HK == HV == H; dtype F16 or F32 (the page
  * validates fp16/fp32 only; F32 is built at K = V = 64, F16 at 64 and 128;
- * anything else returns GDR_ERR_UNSUPPORTED before any launch).  Per chunk of C <= BT rows, with γ = exp(g):
+ * chunk length BT = 16 or 64, the two the page validates; anything else
+ * returns GDR_ERR_UNSUPPORTED before any launch).  Per chunk of C <= BT rows, with γ = exp(g):
  * returns the gradients of
  *   scale<dO,(Q⊙γ)h> + <dh,(K⊙γ_C/γ)ᵀV_new> + <dh,diag(γ_C)h> + <dv,A(β⊙V) - A(β⊙γ⊙K)h>
  * with respect to q, k, v, beta, g and the strictly-lower L of A = (I+L)^{-1}.

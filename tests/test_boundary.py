@@ -98,7 +98,7 @@ def test_kda_validation(B):
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -1
     p = _prob(B, dtype=B.GDR_BF16)
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2
-    p = _prob(B, dtype=B.GDR_F16, BT=16)
+    p = _prob(B, dtype=B.GDR_F16, BT=32)   # chunk lengths 16 and 64 are built
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2
     p = _prob(B, dtype=B.GDR_F32, K=128, V=128)   # fp32 is built at K = V = 64 only
     assert B.lib.kda_chunk_bwd(ctypes.byref(p), *f, None) == -2

@@ -310,6 +310,16 @@ def test_kda_small(B, oracle):
         _kda_compare(B, oracle, inp, label=f"kda_small_{dt}")
 
 
+def test_kda_small_bt16(B, oracle):
+    """Chunk length 16 (the page's other validated chunk size), with a partial
+    last chunk in each of two batch rows."""
+    for dt in ("f16", "f32"):
+        K = 128 if dt == "f16" else 64
+        _log(f"[parity] kda BT=16 {dt} K={K}")
+        inp = W.kda_inputs(B=2, T=150, H=2, K=K, V=K, BT=16, dtype=dt, seed=4)
+        _kda_compare(B, oracle, inp, label=f"kda_bt16_{dt}")
+
+
 @pytest.mark.slow
 def test_kda_T2048_h32_all_heads(B, oracle):
     _log("[parity] kda B=1 T=2048 H=32 K=V=128 fp16, every head")
