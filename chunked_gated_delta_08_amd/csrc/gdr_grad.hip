@@ -318,7 +318,8 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
     __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the waits count on it
     RowsReg<E, KD, LK> rq, rk;
     rq.load(q + qrow * KD, (long)HK * KD, Cn);
-    rk.load(k + qrow * KD, (long)HK * KD, Cn);
+    const bool need_k = !GRP || hi == 0;   // K's LDS region is not reused within a unit: later heads keep it
+    if (need_k) rk.load(k + qrow * KD, (long)HK * KD, Cn);
     __builtin_amdgcn_sched_barrier(0);
     RowsReg<E, 64, LA> rA;
     StateReg<E, KD, LK, VS> rH, rdH;
@@ -336,7 +337,7 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
         sB[r] = r < Cn ? (float)bb : 0.f;
     }
     rq.store(sQ);
-    rk.store(sK);
+    if (need_k) rk.store(sK);
     lds_barrier();
     const float gl = sG[C - 1], gC = sGam[C - 1];
     // dh[c] arrives scaled by dsc (a power of two); its products all pass
