@@ -131,6 +131,7 @@ WsPlan plan_workspace(const Problem& p) {
     w.seq_chunk0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
     w.seg_info = off; off = align256(off + (size_t)p.NS * sizeof(SegInfo));
     w.seq_seg0 = off; off = align256(off + (size_t)(p.N + 1) * 4);
+    w.seg_order = off; off = align256(off + (size_t)p.NS * 4);
     w.W = off; off = align256(off + units * 64 * p.K * es);
     w.U = off; off = align256(off + units * 64 * p.V * es);
     w.R = off; off = align256(off + units * 64 * p.K * es);
@@ -251,14 +252,15 @@ int gdr_fwd_states(const gdr_problem* p, const void* k, const void* v, const flo
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
     auto* seg = (SegInfo*)(base + w.seg_info);
     auto* ss0 = (int32_t*)(base + w.seq_seg0);
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
+    auto* sord = (int32_t*)(base + w.seg_order);
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, sord, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
                                             nullptr, base + w.KT, stream));
         if (st != GDR_OK) return st;
     }
     gdr::ScanArgs a{};
-    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0; a.seg_order = sord;
     set_seg_buffers(a, base, w);
     a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.h0 = h0;
     a.h32 = h_out; a.v_new = v_new_out; a.ht = ht_out;
@@ -293,9 +295,10 @@ int gdr_chunk_fwd_events(const gdr_problem* p, const void* qp, const void* k, co
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
     auto* seg = (SegInfo*)(base + w.seg_info);
     auto* ss0 = (int32_t*)(base + w.seq_seg0);
+    auto* sord = (int32_t*)(base + w.seg_order);
     auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
     if ((st = mark(0)) != GDR_OK) return st;
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, sord, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
         st = launch_status(gdr::launch_prep(q, nullptr, k, v, g_cum, beta, info, base + w.W, base + w.U, nullptr,
                                             nullptr, base + w.KT, stream));
@@ -303,7 +306,7 @@ int gdr_chunk_fwd_events(const gdr_problem* p, const void* qp, const void* k, co
     }
     if ((st = mark(1)) != GDR_OK) return st;
     gdr::ScanArgs a{};
-    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0; a.seg_order = sord;
     set_seg_buffers(a, base, w);
     a.W = base + w.W; a.U = base + w.U; a.KT = base + w.KT; a.h0 = h0;
     a.hT = base + w.h; a.ht = ht_out;
@@ -343,9 +346,10 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
     auto* seg = (SegInfo*)(base + w.seg_info);
     auto* ss0 = (int32_t*)(base + w.seq_seg0);
+    auto* sord = (int32_t*)(base + w.seg_order);
     auto mark = [&](int i) { return ev ? launch_status(hipEventRecord(ev[i], stream)) : GDR_OK; };
     gdr::ScanArgs a{};
-    a.dO = dO; a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0;
+    a.dO = dO; a.gcum = g_cum; a.seq_chunk0 = sc0; a.seg = seg; a.seq_seg0 = ss0; a.seg_order = sord;
     set_seg_buffers(a, base, w);
     a.W = base + w.W; a.U = base + w.U; a.R = base + w.R; a.KT = base + w.KT;
     a.h0 = h0; a.dht = dht;
@@ -357,7 +361,7 @@ int gdr_chunk_bwd_events(const gdr_problem* p, const void* qp, const void* k, co
         a.cmax = (float*)(base + w.cmax); a.hmax = (float*)(base + w.hmax); a.dsc = (float*)(base + w.dsc);
     }
     if ((st = mark(0)) != GDR_OK) return st;
-    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, stream))) != GDR_OK) return st;
+    if ((st = launch_status(gdr::launch_chunk_table(q, info, sc0, seg, ss0, sord, stream))) != GDR_OK) return st;
     // the scales first (they read dO and dht only), then the WY factors
     if ((st = launch_status(gdr::launch_scan_scales(q, a, stream))) != GDR_OK) return st;
     if (q.NT > 0) {
@@ -409,7 +413,7 @@ int kda_chunk_bwd_full_events(const gdr_problem* p, const void* qp, const void* 
     auto* sc0 = (int32_t*)(base + w.seq_chunk0);
     if (ev && (st = launch_status(hipEventRecord(ev[0], stream))) != GDR_OK) return st;
     st = launch_status(gdr::launch_chunk_table(q, info, sc0, (SegInfo*)(base + w.seg_info),
-                                               (int32_t*)(base + w.seq_seg0), stream));
+                                               (int32_t*)(base + w.seq_seg0), nullptr, stream));
     if (st != GDR_OK) return st;
     gdr::KdaFullArgs a{};
     a.q = qp; a.k = k; a.v = v; a.gcum = g_cum; a.beta = beta; a.dO = dO; a.h0 = h0; a.dht = dht;

@@ -40,15 +40,18 @@ struct Problem {
 // Workspace carve-up (byte offsets from the workspace base).  The segment
 // state buffers (hloc, dhloc, P, hstart, dhin: [NS][HV][K][V] fp32 each, in
 // the fp32 fragment order below; P holds its values in the 16-bit operand
-// type, in the first half of each block) are empty when maxS == 1.
+// type, in the first half of each block, and its transpose in the second) are
+// empty when maxS == 1.
 struct WsPlan {
-    size_t chunk_info, seq_chunk0, seg_info, seq_seg0, W, U, R, A, KT, h, dh;
+    size_t chunk_info, seq_chunk0, seg_info, seq_seg0, seg_order, W, U, R, A, KT, h, dh;
     size_t hloc, dhloc, P, hstart, dhin, cmax, hmax, dsc, total;
 };
 WsPlan plan_workspace(const Problem& p);
 
+// seg_order (NULL: not wanted): the segments ranked by descending chunk count,
+// ties by index, when there are at most 1024 of them (index order otherwise).
 hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, SegInfo* seg,
-                              int32_t* seq_seg0, hipStream_t s);
+                              int32_t* seq_seg0, int32_t* seg_order, hipStream_t s);
 
 // K1a: per-chunk WY factors.  W, U, K̃ (and R when q != NULL) in the scan
 // operand type; A = (I+L)^{-1} in the input type when A != NULL.
@@ -89,6 +92,7 @@ __host__ __device__ constexpr long state32_frag_offset(int KD, int k, int v) {
 struct ScanArgs {
     const void* dO; const float* gcum; const int32_t* seq_chunk0;
     const SegInfo* seg; const int32_t* seq_seg0;
+    const int32_t* seg_order;   // segments by descending chunk count (ties by index), or NULL: index order
     const void* W; const void* U; const void* R; const void* KT;
     const float* h0; const float* dht;
     void* hT; float* h32; void* v_new; float* ht;

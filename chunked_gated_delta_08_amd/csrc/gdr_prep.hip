@@ -35,13 +35,17 @@ __device__ __forceinline__ int last_le(const int32_t* __restrict__ a, int n, int
 // per sequence, so that an empty sequence still gets its dh0), their exclusive
 // prefix sums (seq_chunk0, seq_seg0, each with the total at [nseq]), then the
 // chunk table and the segment table filled in parallel (binary search of
-// each entry's sequence in the prefix arrays).
+// each entry's sequence in the prefix arrays).  seg_order (if wanted): the
+// segments ranked by descending chunk count, ties by index, so the scans can
+// start the longest jobs first; each rank is a count over all segments (up to
+// 1024 of them, held in LDS; beyond that, index order).
 __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* __restrict__ cu, int N, int B, int T,
                                                            int BT, int L, ChunkInfo* __restrict__ info,
                                                            int32_t* __restrict__ seq_chunk0,
                                                            SegInfo* __restrict__ seg,
-                                                           int32_t* __restrict__ seq_seg0) {
-    __shared__ int pc[1024], ps[1024];
+                                                           int32_t* __restrict__ seq_seg0,
+                                                           int32_t* __restrict__ seg_order) {
+    __shared__ int pc[1024], ps[1024], snc[1024];
     const int nseq = cu ? N : B;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int per = (nseq + nt - 1) / nt;
@@ -100,13 +104,26 @@ __global__ void __launch_bounds__(1024) chunk_table_kernel(const int32_t* __rest
         si.c0 = seq_chunk0[n] + si.lc0;
         si.nc = min(L, nc - si.lc0);
         seg[j] = si;
+        if (NS <= nt) snc[j] = si.nc;
+    }
+    if (!seg_order) return;
+    if (NS > nt) {
+        for (int j = tid; j < NS; j += nt) seg_order[j] = j;
+        return;
+    }
+    __syncthreads();
+    if (tid < NS) {
+        const int c = snc[tid];
+        int rank = 0;
+        for (int i = 0; i < NS; i++) rank += snc[i] > c || (snc[i] == c && i < tid);
+        seg_order[rank] = tid;
     }
 }
 
 hipError_t launch_chunk_table(const Problem& p, ChunkInfo* info, int32_t* seq_chunk0, SegInfo* seg,
-                              int32_t* seq_seg0, hipStream_t s) {
+                              int32_t* seq_seg0, int32_t* seg_order, hipStream_t s) {
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, s, p.cu, p.N, p.B, p.T, p.BT, p.L, info,
-                       seq_chunk0, seg, seq_seg0);
+                       seq_chunk0, seg, seq_seg0, seg_order);
     return hipGetLastError();
 }
 

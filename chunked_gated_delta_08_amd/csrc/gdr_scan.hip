@@ -586,8 +586,20 @@ __device__ __forceinline__ SegView seg_view(const ScanArgs& a, int j) {
     return v;
 }
 
+// Workgroup x of a launch of (segment, value head, direction) jobs: the
+// forward jobs first (nfwd of them, 0 or NS*HV), then the reverse ones; within
+// a direction segment by segment, in the segment order when there is one (the
+// longest segments first, so the sequences' unequal lengths even out over the
+// CUs), all heads of a segment together.
+__device__ __forceinline__ void job_of(const ScanArgs& a, int x, int nfwd, int HV, bool& rev, int& j, int& hv) {
+    rev = x >= nfwd;
+    const int b = rev ? x - nfwd : x;
+    j = a.seg_order ? a.seg_order[b / HV] : b / HV;
+    hv = b % HV;
+}
+
 // The scans proper (one job per (segment, value head, direction)): forward
-// jobs for blocks [0, nfwd), reverse jobs after.  A job starts from h0 / dht
+// jobs and reverse jobs (nfwd and gridDim - nfwd of them), placed by job_of.  A job starts from h0 / dht
 // at the sequence ends and from the combined boundary states otherwise; the
 // first reverse segment writes dh0 and the last forward one ht.
 // EST: the states are stored in type E.  It is a template parameter so the
@@ -597,13 +609,14 @@ template <class E, class S, int KD, int VD, bool EST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 scan_kernel(ScanArgs a, int nfwd, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const bool rev = (int)blockIdx.x >= nfwd;
-    const int b = rev ? (int)blockIdx.x - nfwd : (int)blockIdx.x;
-    const SegView v = seg_view(a, b / HV);
+    bool rev;
+    int j, hvj;
+    job_of(a, (int)blockIdx.x, nfwd, HV, rev, j, hvj);
+    const SegView v = seg_view(a, j);
     const long KV = (long)KD * VD;
     ScanJob jb;
     jb.n = v.si.seq;
-    jb.hv = b % HV;
+    jb.hv = hvj;
     jb.c0 = v.si.c0;
     jb.nc = v.si.nc;
     jb.lc0 = v.si.lc0;
@@ -625,27 +638,29 @@ scan_kernel(ScanArgs a, int nfwd, int HV) {
     }
 }
 
-// Local segment scans (16-bit operands only), NS*HV jobs per role:
-//   blocks [0, NS*HV): forward from zero over the segment -> hloc (not needed
+// Local segment scans (16-bit operands only), NS*HV jobs per role, placed by
+// job_of:
+//   forward: from zero over the segment -> hloc (not needed
 //       for a sequence's last segment), together with the transfer matrix
 //       P = Π (γ_C I − K̃ᵀ W) of the segment, from I -> P (both read the same
 //       W and K̃ tiles, so one workgroup computes both; only for sequences
 //       with more than one segment);
-//   blocks [NS*HV, 2*NS*HV): reverse from zero over the segment -> dhloc (not
+//   reverse: from zero over the segment -> dhloc (not
 //       for a sequence's first segment).
 // The caller passes arguments with no per-chunk outputs (hT, dhT, h32, v_new).
 template <class E, class S, int KD, int VD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 seg_kernel(ScanArgs a, int NS, int HV) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int per = NS * HV, x = (int)blockIdx.x;
-    const bool rev = x >= per;
-    const int b = rev ? x - per : x;
-    const SegView v = seg_view(a, b / HV);
+    const int per = NS * HV;
+    bool rev;
+    int j, hvj;
+    job_of(a, (int)blockIdx.x, per, HV, rev, j, hvj);
+    const SegView v = seg_view(a, j);
     const long KV = (long)KD * VD;
     ScanJob jb;
     jb.n = v.si.seq;
-    jb.hv = b % HV;
+    jb.hv = hvj;
     jb.c0 = v.si.c0;
     jb.nc = v.si.nc;
     jb.lc0 = v.si.lc0;
