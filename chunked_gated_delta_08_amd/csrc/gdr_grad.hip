@@ -1,9 +1,9 @@
 // gdr_grad.hip -- per-chunk gradients (K3) with the tail fused in.
 //
-// One workgroup (4 waves) per (chunk, key head) and launch; with G value heads
-// per key head there are G launches, one per head of the group, that add up
-// the dq/dk group sums in a fixed order (the GQA reduction the FlashQLA
-// backward explainer, §一 step ④, does in Python).
+// One workgroup (4 waves) per (chunk, key head); with G value heads per key
+// head it takes the G heads of its group in turn and adds up the dq/dk group
+// sums in a fixed order (the GQA reduction the FlashQLA backward explainer,
+// §一 step ④, does in Python).
 // Given h = h[c] (state entering the chunk) and dh = dh[c] (gradient of the
 // state leaving it) from the scans, and recomputing the chunk's WY factors:
 //   L = strictly-lower(diag(β)(K Kᵀ) ⊙ Γ),  A = (I+L)^{-1} (read from the prep kernel),

@@ -1,6 +1,7 @@
 // gdr_scan.hip -- the two sequential chunk scans (K1b forward states, K2 dh).
 //
-// The per-chunk states go to the workspace transposed ([V][K] per chunk).
+// The per-chunk states go to the workspace in the accumulators' fragment order
+// (16-bit types) or transposed, [V][K] per chunk (fp32).
 //
 // Forward (state entering chunk c is h[c]; FlashQLA backward explainer §一
 // step ②, "recompute h"):
@@ -13,8 +14,9 @@
 // (all updates multiply the state from the left), so a wave owns a K x V/4
 // column slice (V/64 blocks of 16 columns) for the whole sequence, in fp32
 // accumulator registers.  A workgroup (4 waves) covers all V columns of one
-// (sequence, value head, direction), so each operand tile is read from HBM
-// once per direction and every fragment read from LDS feeds V/64 MFMAs.
+// job, a run of chunks (a whole sequence or one of its segments) of one value
+// head and direction, so each operand tile is read from HBM once per
+// direction and pass, and every fragment read from LDS feeds V/64 MFMAs.
 // The state doubles as the MFMA B operand without any data
 // movement: the accumulator holds rows {4g..4g+3} of every 16-row tile, so two
 // tiles form one 32-deep k block in the permuted order
