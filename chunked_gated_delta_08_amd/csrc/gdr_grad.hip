@@ -392,6 +392,9 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
 
     // the next slice (h, dh as rows v of [V][K]; dO, V) is loaded into
     // registers while the current one is computed
+    // Pmᵀ's fragments (A operand of Pmᵀ dO) read once, in the first slice, and
+    // kept: Pm does not change during the value loop
+    typename Mma<E>::frag pmf[64 / Mma<E>::KS][2];
     StateReg<E, KD, LK, VS> nH, ndH;
     RowsReg<E, VS, LS> ndO, nV;
     RowsReg<E, KD, LK> nQ;
@@ -461,7 +464,22 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
         {
             f32x4 pdo[2][1];
             zero_acc(pdo);
-            gemm4<E, 2, 1, 64, true, true>(pdo, sPm, LA, sdO, LS, m0, n0v);
+            {
+                constexpr int KS = Mma<E>::KS;
+                const int l = lane_o();
+                if (vs == 0) {
+                    const E* pa = frag_base<E, true>(sPm, LA, m0, l);
+#pragma unroll
+                    for (int s = 0; s < 64 / KS; s++) frags<E, 2, true>(pmf[s], pa, LA, s * KS);
+                }
+                const E* pb = frag_base<E, true>(sdO, LS, n0v, l);
+#pragma unroll
+                for (int s = 0; s < 64 / KS; s++) {
+                    typename Mma<E>::frag fb[1];
+                    frags<E, 1, true>(fb, pb, LS, s * KS);
+                    mma_tiles<E>(pdo, pmf[s], fb);
+                }
+            }
             GRAD_LANE_RC();
 #pragma unroll
             for (int i = 0; i < 2; i++) {
