@@ -4,10 +4,10 @@
 // (16-bit types) or transposed, [V][K] per chunk (fp32).
 //
 // Forward (state entering chunk c is h[c]; FlashQLA backward explainer §一
-// step ②, "recompute h"):
+// step ②, where h is recomputed):
 //     V_new = U − W h[c],   h[c+1] = γ_C h[c] + K̃ᵀ V_new,   K̃ = diag(γ_C/γ) K
-// Reverse (dh[c] is the gradient of the state leaving chunk c; same page §二
-// "dS is walked back chunk by chunk" and §三's R-form of the recursion):
+// Reverse (dh[c] is the gradient of the state leaving chunk c; same page §二,
+// where dS goes back one chunk at a time, and §三's R-form of the recursion):
 //     dh[c−1] = γ_C dh[c] + Rᵀ dO − Wᵀ (K̃ dh[c]),   dh0 = dh[−1]
 //
 // Parallel decomposition: every column of the K x V state evolves on its own

@@ -24,7 +24,9 @@
 // (fp16 MFMA for fp16, fp32 MFMA for fp32) with fp32 accumulation; every
 // product runs in row form (a lane holds four adjacent columns of one row of
 // each 16 x 16 tile), so element-wise operands and outputs move as whole
-// 8/16-byte row pieces.
+// 8/16-byte row pieces.  Chunk length BT = 64 or 16 (the two the page
+// validates): a 16-row chunk runs in the same 64-row tile with the rows past
+// it zero, and A and dA rows hold BT entries.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 

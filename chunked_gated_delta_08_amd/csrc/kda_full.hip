@@ -2,9 +2,10 @@
 // per-channel gate), built around the WY stage of kda_bwd.hip.
 //
 // Page: "chunk_kda_bwd_wy_dqkg_fused 算子" (MindSpeed-Ops) -- 概述 places that
-// operator inside the KDA chunk backward ("wy representation gradient"); the
-// other steps of that backward are the state recomputation, the per-channel
-// dh scan and the intra-chunk attention / dL distribution written out here.
+// operator inside the KDA chunk backward as its WY-representation gradient
+// step; the other steps of that backward are the state recomputation, the
+// per-channel dh scan and the intra-chunk attention / dL distribution written
+// out here.
 //
 // Per chunk (C <= 64 rows), with G the in-chunk cumulative per-channel
 // log-gate (C x K), γ = e^G, γ_C its last row, and h the state entering it:
