@@ -15,8 +15,8 @@ Subcommands (run with ``python -m chunked_gated_delta_08_amd.profiling``):
       copy kernel's known bytes and what the same counter reads for it, and
       writes traffic_<kernel>_<workload>.json (+ one .txt for all kernels).
 
-A traffic file records a digest of the kernel's sources; readers ignore it once
-the sources have changed.
+A traffic file records a digest of the kernel's sources (their code, comments
+and layout left out); readers ignore it once that code has changed.
 """
 import argparse
 import collections
@@ -52,11 +52,20 @@ for _k in ("bigdn_stats_kernel", "bigdn_phase_a_kernel", "bigdn_scan_kernel", "b
     KERNEL_SOURCES[_k] = _BIGDN
 
 
+def _code_of(text):
+    """The text of a source file without its comments and with every run of
+    whitespace reduced to one space: a digest of it follows the code only."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"(?<!:)//[^\n]*", " ", text)   # comment to end of line
+    return " ".join(text.split())
+
+
 def source_digest(files):
+    """Digest of the code (comments and layout left out) of the given files."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_of(fh.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
