@@ -270,7 +270,8 @@ def cpu_baseline(inp, cfg, chunks, min_seconds=10.0, path="bwd"):
 
 def _traffic(kernel_name, workload, profiling):
     """HBM bytes per launch from the committed counter summary, while the
-    kernel's sources still hash to the digest recorded there (else None)."""
+    code of the kernel's sources (comments and layout left out) still hashes to
+    the digest recorded there (else None)."""
     tfile = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.json")
     if not os.path.exists(tfile):
         return None
