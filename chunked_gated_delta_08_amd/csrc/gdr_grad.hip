@@ -258,7 +258,9 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 
 // One (chunk, value head) unit of the gradient: value head hv = hk·G + hi of
-// key head hk = blockIdx.y, chunk blockIdx.x.
+// key head hk, chunk ci, with blockIdx.x = ci·HK + hk: the workgroups of one
+// chunk's heads are consecutive, so the launch walks the inputs (token rows
+// of all heads) and the per-chunk states (unit-major) in address order.
 template <class E, int KD, int VD, bool GRP>
 __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, float scale, int hi) {
     using Cf = GradCfg<E, KD, VD>;
@@ -285,7 +287,7 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
     float* sEg = sB + 64;   // e^{G_C − G_r}: the factor γ_C/γ
     float* sRed = (float*)(smem + Cf::oRed);   // row partials of dG, dβ [2][64] each, column partials [2][64], misc [8]
 
-    int ci = blockIdx.x, hk = blockIdx.y;
+    int ci = (int)blockIdx.x / HK, hk = (int)blockIdx.x % HK;
     const int G = GRP ? HV / HK : 1;
     if constexpr (GRP) asm volatile("" : "+s"(ci), "+s"(hk));   // derived per unit, not kept live across units
     const ChunkInfo ch = a.info[ci];
@@ -806,7 +808,7 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
     store_rows<E, KD, LK>((E*)a.dk + qrow * KD, (long)HK * KD, sdk, Cn);
 }
 
-// One workgroup per (chunk, key head).  GRP (G = HV/HK > 1): the workgroup
+// One workgroup per (chunk, key head), key heads fastest.  GRP (G = HV/HK > 1): the workgroup
 // takes the G value heads hv = hk·G + hi of its key head one after the other
 // and builds the group sums of dq and dk in the outputs themselves: the first
 // head stores its dq, dk; every later one loads the rows stored so far (its
@@ -833,7 +835,8 @@ static hipError_t grad_go1(const Problem& p, const GradArgs& a, hipStream_t s) {
     auto kern = grad_kernel<E, KD, VD, GRP>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HK), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale);
+    if (p.NT * p.HK > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.NT * p.HK)), dim3(GNT), Cf::smem, s, a, p.HK, p.HV, p.scale);
     return hipGetLastError();
 }
 
