@@ -248,7 +248,7 @@ kda_kernel(KdaArgs a, const int32_t* __restrict__ cu, int N, int T, int H, int B
     float* sCS = sHD + KD;           // [2][KD] column partials of K ⊙ dks, later [2][64] dβ partials
     float* sLast = sCS + Cf::NCS;    // dg of the chunk's last row before its column-sum terms
 
-    const int ci = blockIdx.x, hh = blockIdx.y;
+    const int ci = (int)blockIdx.x / H, hh = (int)blockIdx.x % H;   // heads fastest
     int t0i, Cn;
     kda_find_chunk(cu, N, T, BT, ci, t0i, Cn);   // chunks of BT <= 64 rows, each in a 64-row tile
     const long t0 = t0i;
@@ -532,7 +532,8 @@ static hipError_t kda_go(const Problem& p, const KdaArgs& a, hipStream_t s) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::smem) != hipSuccess)
         return hipErrorInvalidConfiguration;
     if (p.BT != 16 && p.BT != 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(KNT), Cf::smem, s, a, p.cu, p.N, p.T, p.HV, p.BT,
+    if (p.NT * p.HV > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.NT * p.HV)), dim3(KNT), Cf::smem, s, a, p.cu, p.N, p.T, p.HV, p.BT,
                        p.scale);
     return hipGetLastError();
 }

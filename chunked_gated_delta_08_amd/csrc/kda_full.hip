@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
     float* sB = (float*)(smem + Cf::oB);
     float* sM = sB + 64;
 
-    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id();
+    const int ci = (int)blockIdx.x / H, h = (int)blockIdx.x % H, w = wave_id();   // heads fastest
     const int m0 = 16 * (w & 3), hc = w >> 2;   // row group, column half
     const int Cn = a.info[ci].len;
     const long t0 = a.info[ci].t0;
@@ -517,7 +517,7 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
     float* sRB = sB + 64;
     float* sBT = (float*)(smem + Cf::oBT);
 
-    const int ci = blockIdx.x, h = blockIdx.y, w = wave_id(), l = lane_id();
+    const int ci = (int)blockIdx.x / H, h = (int)blockIdx.x % H, w = wave_id(), l = lane_id();   // heads fastest
     const int m0 = 16 * (w & 3), hc = w >> 2;   // row group, column half
     const int Cn = a.info[ci].len;
     const long t0 = a.info[ci].t0;
@@ -710,13 +710,14 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
 template <class E, class S, int KD, int VD>
 static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_t s, hipEvent_t* ev) {
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+    if (p.NT * p.HV > INT32_MAX) return hipErrorInvalidValue;   // one workgroup per (chunk, head), heads fastest
     hipError_t e;
     if (p.NT > 0) {
         auto kern = kda_prep_kernel<E, S, KD, VD>;
         const int sm = (int)KPrepCfg<S, KD, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(512), sm, s, a, p.HV, p.scale);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(p.NT * p.HV)), dim3(512), sm, s, a, p.HV, p.scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
@@ -743,7 +744,7 @@ static hipError_t kda_full_go(const Problem& p, const KdaFullArgs& a, hipStream_
         const int sm = (int)KIntraCfg<S, VD>::smem;
         if ((e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, sm)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)p.NT, p.HV), dim3(512), sm, s, a, p.HV, p.scale);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(p.NT * p.HV)), dim3(512), sm, s, a, p.HV, p.scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return mark(4);
