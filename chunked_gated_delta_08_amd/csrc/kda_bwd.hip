@@ -16,7 +16,8 @@
 //   dA  = −strictlower(Aᵀ dA_pre Aᵀ),  dA_pre = dv(β⊙V)ᵀ + dw(β⊙γ⊙K)ᵀ
 // The page runs this as six Ascend kernels to avoid the BT x BT post-processing
 // in one kernel; here it is one gfx950 kernel.  One workgroup of four waves per
-// (chunk, head), two workgroups per CU: the products that reduce over the
+// (chunk, head) (the heads of a chunk on consecutive workgroups), two
+// workgroups per CU: the products that reduce over the
 // value dimension (dO hᵀ, dv hᵀ, V_new dhᵀ, dv Vᵀ) accumulate over 32-column
 // value slices, so only one slice of h, dh, dO, dv, V_new and V is staged at a
 // time (about 51 KB of LDS at K = V = 128), and the next slice is loaded into

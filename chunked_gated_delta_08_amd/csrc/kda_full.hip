@@ -63,7 +63,8 @@ struct KPrepCfg {
 }  // namespace
 
 // ---------------------------------------------------------------- WY factors
-// Grid (chunks, H), 512 threads (8 waves: wave w owns rows 16 (w & 3) .. +15
+// One workgroup per (chunk, head), the heads of a chunk on consecutive
+// workgroups; 512 threads (8 waves: wave w owns rows 16 (w & 3) .. +15
 // and column half w >> 2 of every product; the triangular inverse runs on
 // waves 0..3).  Writes, per unit u = chunk * H + head:
 // W, K̃, Qg = scale (Q ⊙ γ) as [u][64][KD], U as [u][64][VD], Aqk as
@@ -471,7 +472,8 @@ __global__ void __launch_bounds__(256) kda_scan_kernel(KdaFullArgs a, int H, int
 }
 
 // ---------------------------------------------------------------- intra-chunk part
-// Grid (chunks, H), 512 threads.  Adds the Aqk and dL terms to the WY stage's
+// One workgroup per (chunk, head), the heads of a chunk on consecutive
+// workgroups; 512 threads.  Adds the Aqk and dL terms to the WY stage's
 // partials and writes dq, dk (input type), dg (reverse-cumsummed), dβ.
 // 71 KB of LDS; at K = V = 128 with 16-bit staging also at most 128 VGPRs, so
 // two workgroups share a CU and one's barriers and loads overlap the other's
