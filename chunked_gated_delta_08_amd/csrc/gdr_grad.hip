@@ -151,6 +151,9 @@ template <> struct Pair<f16> {
 // of one K x V state block, written to LDS as [NC columns][KD keys] (row pitch
 // LD).  16-bit types read the workspace fragment order (one contiguous 16 B
 // per thread, two 8 B LDS writes); fp32 reads the transposed [V][K] rows.
+// The states are read once, so the loads are non-temporal (they leave the
+// caches to the rows that are read again: Q, and the halves of the V and dO
+// lines that the next value slice reads).
 template <class E, int KD, int LD, int NC>
 struct StateReg {
     static constexpr bool FRAG = sizeof(E) == 2;
@@ -161,7 +164,8 @@ struct StateReg {
         const E* src = blk + (long)vc0 * KD;   // NC columns: contiguous in both layouts
         const unsigned tid = tid_o();
 #pragma unroll
-        for (int i = 0; i < N; i++) v[i] = *(const typename Vec16<E>::t*)at32(src, (tid + GNT * i) * (16u / sizeof(E)));
+        for (int i = 0; i < N; i++)
+            v[i] = __builtin_nontemporal_load((const typename Vec16<E>::t*)at32(src, (tid + GNT * i) * (16u / sizeof(E))));
     }
     // partial <this, o> over the elements this thread holds (same layout)
     __device__ __forceinline__ float dot(const StateReg& o) const {
