@@ -24,7 +24,10 @@
 // and the A operand (W, K, or the transposed Kᵀ/Wᵀ) is read in the same order.
 // Operand tiles (W, U, R and K̃ = diag(γ_C/γ)K from the WY-factor kernel) are
 // staged through LDS; the next-but-one chunk is prefetched into registers
-// while the current one is computed.
+// while the current one is computed.  Every tile is read once per pass and
+// every per-chunk state written once, far ahead of its reader, so the loads
+// and the state stores are non-temporal: they stream past the caches instead
+// of evicting lines that are still to be used.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -147,7 +150,7 @@ __device__ __forceinline__ void store_state(const f32x4 (&St)[KD / 16], long uni
                     v[s][4 + e] = (E)St[2 * s + 1][e];
                 }
 #pragma unroll
-            for (int s = 0; s < KD / 32; s++) *(e8*)(p + 512 * s) = v[s];
+            for (int s = 0; s < KD / 32; s++) __builtin_nontemporal_store(v[s], (e8*)(p + 512 * s));
         } else {
             E* p = hT + (unit * VD + col) * KD + 4 * g;
 #pragma unroll
@@ -268,9 +271,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
 #pragma unroll
         for (int j = 0; j < Cf::NK; j++) {
             const int idx = threadIdx.x + 256 * j, go = (idx / VPR) * KD + (idx % VPR) * EPV;
-            st.k[j] = *(const typename Vec16<S>::t*)(Kb + go);
-            st.w[j] = *(const typename Vec16<S>::t*)(Wb + go);
-            if constexpr (rev) st.r[j] = *(const typename Vec16<S>::t*)(Rb + go);
+            st.k[j] = __builtin_nontemporal_load((const typename Vec16<S>::t*)(Kb + go));
+            st.w[j] = __builtin_nontemporal_load((const typename Vec16<S>::t*)(Wb + go));
+            if constexpr (rev) st.r[j] = __builtin_nontemporal_load((const typename Vec16<S>::t*)(Rb + go));
         }
 #pragma unroll
         for (int j = 0; j < Cf::NX; j++) {
@@ -279,9 +282,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 // commit, where the data is needed anyway (a select here would
                 // make the wave wait for the load it just issued)
                 const int rowc = min(rowX[j], Cn - 1);
-                st.x[j] = *(const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]);
+                st.x[j] = __builtin_nontemporal_load((const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]));
             } else {
-                st.u[j] = *(const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]);
+                st.u[j] = __builtin_nontemporal_load((const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]));
             }
         }
         st.gl = a.gcum[(t0 + Cn - 1) * HV + hv];
