@@ -186,7 +186,17 @@ template <class E> constexpr int prep_waves() { return 4; }
 // right after the current ones are staged in LDS, and its V right after the
 // current V is staged (after the inverse), so those loads are in flight while
 // the current unit is computed.  E: input type; S: scan operand type.
-template <class E, class S, int KD, int VD, bool WITH_R>
+// A 16-byte load, non-temporal when NT (data read once by this launch).
+template <bool NT, class T>
+__device__ __forceinline__ T ld16(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// NTQK: q and k rows are read by one unit only (HK == HV), so their loads are
+// non-temporal like those of v; under GQA the value heads of a group read the
+// same rows one unit after another and the loads keep them in the caches.
+template <class E, class S, int KD, int VD, bool WITH_R, bool NTQK>
 __global__ void __launch_bounds__(64 * prep_waves<E>())
 __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) prep_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const float* __restrict__ gcum,
@@ -231,8 +241,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) prep_kernel(cons
 #pragma unroll
         for (int i = 0; i < NKV; i++) {
             const int idx = threadIdx.x + NTHR * i, r = min(idx / (KD / EPV), Cu - 1), cc = idx % (KD / EPV);
-            rk[i] = *(const typename Vec16<E>::t*)(k + ((tu + r) * HK + hku) * KD + cc * EPV);
-            if constexpr (WITH_R) rq[i] = *(const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV);
+            rk[i] = ld16<NTQK>((const typename Vec16<E>::t*)(k + ((tu + r) * HK + hku) * KD + cc * EPV));
+            if constexpr (WITH_R) rq[i] = ld16<NTQK>((const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV));
         }
     };
     auto issue_v = [&](int u, int Cu, int tu) {
@@ -240,7 +250,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) prep_kernel(cons
 #pragma unroll
         for (int i = 0; i < NVV; i++) {
             const int idx = threadIdx.x + NTHR * i, r = min(idx / (VD / EPV), Cu - 1), cc = idx % (VD / EPV);
-            rv[i] = *(const typename Vec16<E>::t*)(v + ((tu + r) * HV + hvu) * VD + cc * EPV);
+            rv[i] = ld16<true>((const typename Vec16<E>::t*)(v + ((tu + r) * HV + hvu) * VD + cc * EPV));
         }
     };
     auto to_s = [](const typename Vec16<E>::t& x, float f, bool keep) {
@@ -432,19 +442,18 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
     // for 16-bit problems, at most two: two waves per SIMD), 256 CUs
     const long per_cu = sm * 2 <= 160 * 1024 ? 2 : 1, nwg = 256 * per_cu;
     dim3 grid((unsigned)(nunits < nwg ? nunits : nwg));
-    if (q) {
-        auto kern = prep_kernel<E, S, KD, VD, true>;
+    auto go = [&](auto kern, void* R_) {
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kern, grid, dim3(64 * prep_waves<E>()), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R, (E*)A, (S*)KT, (int)nunits);
-    } else {
-        auto kern = prep_kernel<E, S, KD, VD, false>;
-        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm) != hipSuccess)
-            return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kern, grid, dim3(64 * prep_waves<E>()), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum, (const E*)beta,
-                           info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)nullptr, (E*)A, (S*)KT, (int)nunits);
-    }
+        hipLaunchKernelGGL(kern, grid, dim3(64 * prep_waves<E>()), sm, s, (const E*)q, (const E*)k, (const E*)v, gcum,
+                           (const E*)beta, info, p.HK, p.HV, p.scale, (S*)W, (S*)U, (S*)R_, (E*)A, (S*)KT, (int)nunits);
+        return hipSuccess;
+    };
+    const bool own_qk = p.HK == p.HV;
+    hipError_t e;
+    if (q) e = own_qk ? go(prep_kernel<E, S, KD, VD, true, true>, R) : go(prep_kernel<E, S, KD, VD, true, false>, R);
+    else e = own_qk ? go(prep_kernel<E, S, KD, VD, false, true>, nullptr) : go(prep_kernel<E, S, KD, VD, false, false>, nullptr);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
