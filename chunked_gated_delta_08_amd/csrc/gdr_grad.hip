@@ -108,6 +108,7 @@ struct RowsReg {
     static constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV, NV = ROWS * VPR, N = (NV + GNT - 1) / GNT;
     typename Vec16<E>::t v[N];
     int C;
+    template <bool NT = false>
     __device__ __forceinline__ void load(const E* __restrict__ g, long rs, int Cn) {
         C = Cn;
         const int tid = tid_o();
@@ -117,7 +118,9 @@ struct RowsReg {
             const int idx = tid + GNT * i;
             if (NV % GNT == 0 || idx < NV) {
                 const unsigned r = min((unsigned)idx / VPR, (unsigned)(Cn - 1)), c = (unsigned)idx % VPR;
-                v[i] = *(const typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV);
+                const auto* p = (const typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV);
+                if constexpr (NT) v[i] = __builtin_nontemporal_load(p);
+                else v[i] = *p;
             }
         }
     }
@@ -153,7 +156,9 @@ template <> struct Pair<f16> {
 // per thread, two 8 B LDS writes); fp32 reads the transposed [V][K] rows.
 // The states are read once, so the loads are non-temporal (they leave the
 // caches to the rows that are read again: Q, and the halves of the V and dO
-// lines that the next value slice reads).
+// lines that the next value slice reads); so are the loads of A and K (read
+// once per unit and key head) and, without GQA, Q's second read and the dq, dk
+// stores.
 template <class E, int KD, int LD, int NC>
 struct StateReg {
     static constexpr bool FRAG = sizeof(E) == 2;
@@ -210,7 +215,7 @@ struct StateReg {
 
 // Coalesced store of a [64][D] LDS tile (row pitch LD) to rows < C of a global
 // row block (row stride rs), 16 bytes per thread and instruction.
-template <class E, int D, int LD>
+template <class E, int D, int LD, bool NT = false>
 __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* s, int C) {
     constexpr int EPV = 16 / (int)sizeof(E), VPR = D / EPV;
     const unsigned urs = (unsigned)rs;
@@ -219,7 +224,12 @@ __device__ __forceinline__ void store_rows(E* __restrict__ g, long rs, const E* 
         const unsigned idx = tid_o() + GNT * it;
         const unsigned r = idx / VPR, c = idx % VPR;
         if ((64 * VPR % GNT == 0 || idx < 64 * VPR) && (int)r < C)
-            *(typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV) = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
+        {
+            const typename Vec16<E>::t x = *(const typename Vec16<E>::t*)(s + r * LD + c * EPV);
+            auto* p = (typename Vec16<E>::t*)at32(g, __umul24(r, urs) + c * EPV);
+            if constexpr (NT) __builtin_nontemporal_store(x, p);
+            else *p = x;
+        }
     }
 }
 
@@ -325,12 +335,12 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
     RowsReg<E, KD, LK> rq, rk;
     rq.load(q + qrow * KD, (long)HK * KD, Cn);
     const bool need_k = !GRP || hi == 0;   // K's LDS region is not reused within a unit: later heads keep it
-    if (need_k) rk.load(k + qrow * KD, (long)HK * KD, Cn);
+    if (need_k) rk.template load<true>(k + qrow * KD, (long)HK * KD, Cn);
     __builtin_amdgcn_sched_barrier(0);
     RowsReg<E, 64, LA> rA;
     StateReg<E, KD, LK, VS> rH, rdH;
     RowsReg<E, VS, LS> rdO, rV;
-    rA.load((const E*)a.A + unit * C * C, C, C);
+    rA.template load<true>((const E*)a.A + unit * C * C, C, C);
     rH.load(hT, 0);
     rdH.load(dhT, 0);
     rdO.load(dO + vrow * VD, (long)HV * VD, Cn);
@@ -465,7 +475,7 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
         }
         __builtin_amdgcn_sched_barrier(0);
         if (vs + 1 == NVS)   // Q (needed again after the loop; its LDS region holds the
-            nQ.load(q + qrow * KD, (long)HK * KD, Cn);   // slice buffers), in flight for the rest of the slice
+            nQ.template load<!GRP>(q + qrow * KD, (long)HK * KD, Cn);   // slice buffers), in flight for the rest of the slice
         // ---- dV_new = Pmᵀ dO + diag(γ_C/γ) K dh
         {
             f32x4 pdo[2][1];
@@ -808,8 +818,8 @@ __device__ __forceinline__ void grad_unit(const GradArgs& a, int HK, int HV, flo
         }
     }
     lds_barrier();
-    store_rows<E, KD, LK>((E*)a.dq + qrow * KD, (long)HK * KD, sdq, Cn);
-    store_rows<E, KD, LK>((E*)a.dk + qrow * KD, (long)HK * KD, sdk, Cn);
+    store_rows<E, KD, LK, !GRP>((E*)a.dq + qrow * KD, (long)HK * KD, sdq, Cn);
+    store_rows<E, KD, LK, !GRP>((E*)a.dk + qrow * KD, (long)HK * KD, sdk, Cn);
 }
 
 // One workgroup per (chunk, key head), key heads fastest.  GRP (G = HV/HK > 1): the workgroup
