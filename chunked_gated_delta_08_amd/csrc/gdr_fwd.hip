@@ -77,7 +77,8 @@ struct FwdCfg {
 // and column block w >> 1 of every output.  Products run in row form (a lane
 // holds four adjacent columns of one row of each tile), so Pm, V_new and o
 // move through LDS as 8-byte row pieces.  The next unit's Q, K, W, U, h and
-// gate are loaded into registers while the current unit is computed.
+// gate are loaded into registers while the current unit is computed.  W, U,
+// h and o are read or written once, with non-temporal accesses.
 // E: input type; S: operand type of the workspace tiles and of the MFMAs (fp16
 // for 16-bit inputs, fp32 for fp32).
 template <class E, class S, int KD, int VD>
@@ -120,12 +121,12 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
             const int idx = threadIdx.x + NT * i, r = min(idx / (KD / EPE), Cu - 1), c = (idx % (KD / EPE)) * EPE;
             rq[i] = *(const VE*)(q + ((tu + r) * HK + hku) * KD + c);
             rk[i] = *(const VE*)(k + ((tu + r) * HK + hku) * KD + c);
-            rw[i] = *(const VS*)(Wg + unit * C * KD + (long)idx * EPE);
+            rw[i] = __builtin_nontemporal_load((const VS*)(Wg + unit * C * KD + (long)idx * EPE));
         }
 #pragma unroll
-        for (int i = 0; i < NU; i++) ru[i] = *(const VS*)(Ug + unit * C * VD + (long)(threadIdx.x + NT * i) * EPE);
+        for (int i = 0; i < NU; i++) ru[i] = __builtin_nontemporal_load((const VS*)(Ug + unit * C * VD + (long)(threadIdx.x + NT * i) * EPE));
 #pragma unroll
-        for (int i = 0; i < NH; i++) rh[i] = *(const VE*)(hT + unit * KD * VD + (long)(threadIdx.x + NT * i) * EPE);
+        for (int i = 0; i < NH; i++) rh[i] = __builtin_nontemporal_load((const VE*)(hT + unit * KD * VD + (long)(threadIdx.x + NT * i) * EPE));
     };
 
     int u = blockIdx.x;
@@ -238,7 +239,7 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
 #pragma unroll
         for (int i = 0; i < NU; i++) {
             const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
-            if (r < Cn) *(VE*)(o + ((t0 + r) * HV + hv) * VD + c) = *(const VE*)(sO + r * LV + c);
+            if (r < Cn) __builtin_nontemporal_store(*(const VE*)(sO + r * LV + c), (VE*)(o + ((t0 + r) * HV + hv) * VD + c));
         }
         lds_barrier();   // the next unit is staged over this one's LDS
         cur_len = nxt_len;

@@ -822,7 +822,9 @@ __global__ void __launch_bounds__(2 * KD) combine_kernel(ScanArgs a, int nseq, i
 // dmax_kernel: blocks [0, 4·NT) take max |dO| over a quarter (16 rows) of one
 // chunk for every value head (the rows are contiguous across the heads: each
 // thread takes 16-byte vectors of one head, V/8 threads share a head), blocks
-// [4·NT, 4·NT + N·HV) max |dht| over one K x V block.
+// [4·NT, 4·NT + N·HV) max |dht| over one K x V block.  dO is read with
+// non-temporal loads (the next kernels stream a gigabyte before the scans
+// read it again).
 template <class E, int VD>
 __global__ void __launch_bounds__(256) dmax_kernel(ScanArgs a, int NT, int HV, int KV) {
     typedef E e8 __attribute__((ext_vector_type(8)));
@@ -841,7 +843,7 @@ __global__ void __launch_bounds__(256) dmax_kernel(ScanArgs a, int NT, int HV, i
                 for (int rb = r0; rb < r1; rb += 8) {   // eight rows in flight (repeated last row: same max)
                     e8 x[8];
 #pragma unroll
-                    for (int u = 0; u < 8; u++) x[u] = *(const e8*)(dO + ((long)min(rb + u, r1 - 1) * vpr + vi) * 8);
+                    for (int u = 0; u < 8; u++) x[u] = __builtin_nontemporal_load((const e8*)(dO + ((long)min(rb + u, r1 - 1) * vpr + vi) * 8));
 #pragma unroll
                     for (int u = 0; u < 8; u++)
 #pragma unroll
