@@ -25,7 +25,10 @@
 // (fp16 MFMA for fp16, fp32 MFMA for fp32) with fp32 accumulation; every
 // product runs in row form (a lane holds four adjacent columns of one row of
 // each 16 x 16 tile), so element-wise operands and outputs move as whole
-// 8/16-byte row pieces.  Chunk length BT = 64 or 16 (the two the page
+// 8/16-byte row pieces.  The states, A and the element-wise g, k, q rows
+// are read once, in whole cache lines, with non-temporal loads; the value
+// slices (half a line of each row per slice) keep normal loads so the next
+// slice finds the other half in the cache.  Chunk length BT = 64 or 16 (the two the page
 // validates): a 16-row chunk runs in the same 64-row tile with the rows past
 // it zero, and A and dA rows hold BT entries.
 #include "gdr_device.hpp"
@@ -116,7 +119,7 @@ struct KdaARows {
         for (int i = 0; i < N; i++) {
             const unsigned idx = t + KNT * i, r = min(idx / VPR, (unsigned)(Cn - 1));
             const unsigned c = min(idx % VPR * EPV, (unsigned)(BT - EPV));
-            v[i] = *(const kdv<E, EPV>*)at32(g, __umul24(r, (unsigned)rs) + c);
+            v[i] = __builtin_nontemporal_load((const kdv<E, EPV>*)at32(g, __umul24(r, (unsigned)rs) + c));
         }
     }
     template <int LD>
@@ -157,8 +160,8 @@ struct KdaSlice {
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const unsigned o_ = (unsigned)(hrow(t, i) * VD + hcol(t, i));
-            h[i] = *(const f32x4*)at32(hg, o_);
-            dh[i] = *(const f32x4*)at32(dhg, o_);
+            h[i] = __builtin_nontemporal_load((const f32x4*)at32(hg, o_));
+            dh[i] = __builtin_nontemporal_load((const f32x4*)at32(dhg, o_));
         }
 #pragma unroll
         for (int i = 0; i < NR; i++) {
@@ -207,9 +210,9 @@ struct KdaElemOps {
 #pragma unroll
             for (int jj = 0; jj < TH; jj++) {
                 const unsigned o = ro + n0 + 16 * jj + cg;
-                g[i][jj] = *(const f32x4*)at32(g0, o);
-                k[i][jj] = *(const typename Vec4<E>::t*)at32(k0p, o);
-                q[i][jj] = *(const typename Vec4<E>::t*)at32(q0p, o);
+                g[i][jj] = __builtin_nontemporal_load((const f32x4*)at32(g0, o));
+                k[i][jj] = __builtin_nontemporal_load((const typename Vec4<E>::t*)at32(k0p, o));
+                q[i][jj] = __builtin_nontemporal_load((const typename Vec4<E>::t*)at32(q0p, o));
             }
         }
 #pragma unroll
