@@ -110,13 +110,13 @@ __global__ void __launch_bounds__(512) kda_prep_kernel(KdaFullArgs a, int H, flo
     for (int i = 0; i < NKV; i++) {
         const int idx = threadIdx.x + NT * i, r = idx / (KD / EPE), c = idx % (KD / EPE) * EPE;
         const long o = ((t0 + min(r, Cn - 1)) * H + h) * KD + c;
-        xk[i] = *(const kvec<E, EPE>*)(k + o);
-        xq[i] = *(const kvec<E, EPE>*)(q + o);
+        xk[i] = __builtin_nontemporal_load((const kvec<E, EPE>*)(k + o));
+        xq[i] = __builtin_nontemporal_load((const kvec<E, EPE>*)(q + o));
     }
 #pragma unroll
     for (int i = 0; i < NVV; i++) {
         const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
-        xv[i] = *(const kvec<E, EPE>*)(v + ((t0 + min(r, Cn - 1)) * H + h) * VD + c);
+        xv[i] = __builtin_nontemporal_load((const kvec<E, EPE>*)(v + ((t0 + min(r, Cn - 1)) * H + h) * VD + c));
     }
     // One slice vector per thread: row sr, channels sdd .. +3 of the slice;
     // G of that row and of the chunk's last row.
@@ -582,14 +582,14 @@ kda_intra_kernel(KdaFullArgs a, int H, float scale) {
     for (int i = 0; i < NIO; i++) {
         const int idx = threadIdx.x + 512 * i, r = idx / (VD / EPE), c = idx % (VD / EPE) * EPE;
         const long o = ((t0 + min(r, Cn - 1)) * H + h) * VD + c;
-        xo[i] = *(const kvec<E, EPE>*)((const E*)a.dO + o);
-        xv[i] = *(const kvec<E, EPE>*)((const E*)a.vn + o);
+        xo[i] = __builtin_nontemporal_load((const kvec<E, EPE>*)((const E*)a.dO + o));
+        xv[i] = __builtin_nontemporal_load((const kvec<E, EPE>*)((const E*)a.vn + o));
     }
     f32x4 xa[NDA];
 #pragma unroll
     for (int i = 0; i < NDA; i++) {
         const int idx = threadIdx.x + 512 * i, r = idx / (C / 4), c = idx % (C / 4) * 4;
-        xa[i] = *(const f32x4*)(a.dA + ((t0 + min(r, Cn - 1)) * H + h) * C + c);
+        xa[i] = __builtin_nontemporal_load((const f32x4*)(a.dA + ((t0 + min(r, Cn - 1)) * H + h) * C + c));
     }
     slice_issue(0);
     elem_issue(0);
