@@ -101,8 +101,8 @@ __global__ void __launch_bounds__(256) bigdn_stats_kernel(const bf16* __restrict
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int c8 = min(c0 + l + 64 * u, nv - 1);
-            a[u] = *(const bf16x8*)(q + 8 * c8);
-            b[u] = *(const bf16x8*)(k + 8 * c8);
+            a[u] = __builtin_nontemporal_load((const bf16x8*)(q + 8 * c8));
+            b[u] = __builtin_nontemporal_load((const bf16x8*)(k + 8 * c8));
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -1013,8 +1013,8 @@ __global__ void __launch_bounds__(256) bigdn_rms_bwd_kernel(const bf16* __restri
         for (int ch = 0; ch < NCH; ch++) {
             const int c8 = l + 64 * ch;
             if (c8 < nc8) {
-                nx[ch] = *(const bf16x8*)(x + 8 * c8);
-                ng[ch] = *(const bf16x8*)(dx + 8 * c8);
+                nx[ch] = __builtin_nontemporal_load((const bf16x8*)(x + 8 * c8));
+                ng[ch] = __builtin_nontemporal_load((const bf16x8*)(dx + 8 * c8));
             }
         }
     };
