@@ -124,9 +124,11 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
             rw[i] = __builtin_nontemporal_load((const VS*)(Wg + unit * C * KD + (long)idx * EPE));
         }
 #pragma unroll
-        for (int i = 0; i < NU; i++) ru[i] = __builtin_nontemporal_load((const VS*)(Ug + unit * C * VD + (long)(threadIdx.x + NT * i) * EPE));
+        for (int i = 0; i < NU; i++)
+            ru[i] = __builtin_nontemporal_load((const VS*)(Ug + unit * C * VD + (long)(threadIdx.x + NT * i) * EPE));
 #pragma unroll
-        for (int i = 0; i < NH; i++) rh[i] = __builtin_nontemporal_load((const VE*)(hT + unit * KD * VD + (long)(threadIdx.x + NT * i) * EPE));
+        for (int i = 0; i < NH; i++)
+            rh[i] = __builtin_nontemporal_load((const VE*)(hT + unit * KD * VD + (long)(threadIdx.x + NT * i) * EPE));
     };
 
     int u = blockIdx.x;
@@ -239,7 +241,8 @@ __global__ void __launch_bounds__(512) fwd_out_kernel(const E* __restrict__ q, c
 #pragma unroll
         for (int i = 0; i < NU; i++) {
             const int idx = threadIdx.x + NT * i, r = idx / (VD / EPE), c = (idx % (VD / EPE)) * EPE;
-            if (r < Cn) __builtin_nontemporal_store(*(const VE*)(sO + r * LV + c), (VE*)(o + ((t0 + r) * HV + hv) * VD + c));
+            if (r < Cn)
+                __builtin_nontemporal_store(*(const VE*)(sO + r * LV + c), (VE*)(o + ((t0 + r) * HV + hv) * VD + c));
         }
         lds_barrier();   // the next unit is staged over this one's LDS
         cur_len = nxt_len;

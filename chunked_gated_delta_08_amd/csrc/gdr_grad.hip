@@ -170,7 +170,8 @@ struct StateReg {
         const unsigned tid = tid_o();
 #pragma unroll
         for (int i = 0; i < N; i++)
-            v[i] = __builtin_nontemporal_load((const typename Vec16<E>::t*)at32(src, (tid + GNT * i) * (16u / sizeof(E))));
+            v[i] = __builtin_nontemporal_load(
+                (const typename Vec16<E>::t*)at32(src, (tid + GNT * i) * (16u / sizeof(E))));
     }
     // partial <this, o> over the elements this thread holds (same layout)
     __device__ __forceinline__ float dot(const StateReg& o) const {

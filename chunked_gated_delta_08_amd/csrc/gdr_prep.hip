@@ -242,7 +242,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) prep_kernel(cons
         for (int i = 0; i < NKV; i++) {
             const int idx = threadIdx.x + NTHR * i, r = min(idx / (KD / EPV), Cu - 1), cc = idx % (KD / EPV);
             rk[i] = ld16<NTQK>((const typename Vec16<E>::t*)(k + ((tu + r) * HK + hku) * KD + cc * EPV));
-            if constexpr (WITH_R) rq[i] = ld16<NTQK>((const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV));
+            if constexpr (WITH_R)
+                rq[i] = ld16<NTQK>((const typename Vec16<E>::t*)(q + ((tu + r) * HK + hku) * KD + cc * EPV));
         }
     };
     auto issue_v = [&](int u, int Cu, int tu) {
@@ -452,7 +453,9 @@ static hipError_t prep_go(const Problem& p, const void* q, const void* k, const 
     const bool own_qk = p.HK == p.HV;
     hipError_t e;
     if (q) e = own_qk ? go(prep_kernel<E, S, KD, VD, true, true>, R) : go(prep_kernel<E, S, KD, VD, true, false>, R);
-    else e = own_qk ? go(prep_kernel<E, S, KD, VD, false, true>, nullptr) : go(prep_kernel<E, S, KD, VD, false, false>, nullptr);
+    else
+        e = own_qk ? go(prep_kernel<E, S, KD, VD, false, true>, nullptr)
+                   : go(prep_kernel<E, S, KD, VD, false, false>, nullptr);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

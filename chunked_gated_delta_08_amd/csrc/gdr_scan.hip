@@ -282,9 +282,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, const ScanJob& jb, 
                 // commit, where the data is needed anyway (a select here would
                 // make the wave wait for the load it just issued)
                 const int rowc = min(rowX[j], Cn - 1);
-                st.x[j] = __builtin_nontemporal_load((const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]));
+                st.x[j] = __builtin_nontemporal_load(
+                    (const typename Vec16<E>::t*)(dO + ((t0 + rowc) * HV + hv) * VD + offX[j]));
             } else {
-                st.u[j] = __builtin_nontemporal_load((const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]));
+                st.u[j] = __builtin_nontemporal_load(
+                    (const typename Vec16<S>::t*)(U + (unit * C + rowX[j]) * VD + offX[j]));
             }
         }
         st.gl = a.gcum[(t0 + Cn - 1) * HV + hv];
@@ -843,7 +845,8 @@ __global__ void __launch_bounds__(256) dmax_kernel(ScanArgs a, int NT, int HV, i
                 for (int rb = r0; rb < r1; rb += 8) {   // eight rows in flight (repeated last row: same max)
                     e8 x[8];
 #pragma unroll
-                    for (int u = 0; u < 8; u++) x[u] = __builtin_nontemporal_load((const e8*)(dO + ((long)min(rb + u, r1 - 1) * vpr + vi) * 8));
+                    for (int u = 0; u < 8; u++)
+                        x[u] = __builtin_nontemporal_load((const e8*)(dO + ((long)min(rb + u, r1 - 1) * vpr + vi) * 8));
 #pragma unroll
                     for (int u = 0; u < 8; u++)
 #pragma unroll

@@ -53,11 +53,13 @@ for _k in ("bigdn_stats_kernel", "bigdn_phase_a_kernel", "bigdn_scan_kernel", "b
 
 
 def _code_of(text):
-    """The text of a source file without its comments and with every run of
-    whitespace reduced to one space: a digest of it follows the code only."""
+    """The text of a source file without its comments and layout: whitespace
+    is kept only where it separates two identifier characters, so a digest of
+    it follows the code alone (line breaks and indentation do not count)."""
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"(?<!:)//[^\n]*", " ", text)   # comment to end of line
-    return " ".join(text.split())
+    text = " ".join(text.split())
+    return re.sub(r"(?<![A-Za-z0-9_]) | (?![A-Za-z0-9_])", "", text)
 
 
 def source_digest(files):

@@ -10,6 +10,9 @@ def test_code_digest_ignores_comments_and_layout():
     c = "int f(int x) {\n    return x + 2;   // one more\n}\n"
     assert profiling._code_of(a) == profiling._code_of(b)
     assert profiling._code_of(a) != profiling._code_of(c)
+    # a line broken inside a call is the same code; a space between two names is not dropped
+    assert profiling._code_of("x = f(g(y));") == profiling._code_of("x = f(\n    g(y));")
+    assert profiling._code_of("int x;") != profiling._code_of("intx;")
 
 
 def test_code_digest_follows_the_files(tmp_path, monkeypatch):
